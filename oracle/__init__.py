@@ -1,0 +1,253 @@
+"""CPU oracle of the MHLA forward pass (float64).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  It shares no code
+with the HIP library and does not import it.
+
+Two independent evaluations of the same definition
+(MHLA, arXiv 2601.07832; paperlayer.ai summary, section 4 "Architecture",
+"Multi-Head Mixing", "Token-Level Adaptivity"):
+
+* ``forward`` / ``summaries`` -- the blockwise O(N d^2 + M^2 d^2) form, in
+  plain C (``mhla_oracle.c``), float64, one thread per (b, h) pair;
+* ``bruteforce`` / ``attention_matrix`` -- the materialised N x N form in
+  numpy: A[n, m] = W[b(n), b(m)] * phi(q_n) . phi(k_m), each row divided by
+  its sum plus eps, then multiplied by V.  Token -> block ids come from
+  numpy's own index utilities, not from the C code.
+
+Inputs use the conventions of ``token_level_head_block_amd.synth``: q, k, v
+are [B, N, H, d] arrays of bf16 bit patterns (uint16) or float32; W is float32
+[M, M].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmhla_oracle.so")
+_SRC = os.path.join(_HERE, "mhla_oracle.c")
+
+F32 = 0
+BF16 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc (plain -O2, no tuning)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("ndim", ctypes.c_int32), ("grid", ctypes.c_int32 * 3),
+                ("block", ctypes.c_int32 * 3), ("eps", ctypes.c_double)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.POINTER(_Problem)
+        vp, dp, ip = ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)
+        fp = ctypes.POINTER(ctypes.c_float)
+        lib.mhla_oracle_phi.argtypes = [ctypes.c_double]
+        lib.mhla_oracle_phi.restype = ctypes.c_double
+        lib.mhla_oracle_num_blocks.argtypes = [P]
+        lib.mhla_oracle_num_blocks.restype = ctypes.c_int64
+        lib.mhla_oracle_token_blocks.argtypes = [P, ip]
+        lib.mhla_oracle_token_blocks.restype = ctypes.c_int
+        lib.mhla_oracle_forward.argtypes = [vp, vp, vp, fp, P, ip, ctypes.c_int32, dp,
+                                            ctypes.c_int32, ip]
+        lib.mhla_oracle_forward.restype = ctypes.c_int
+        lib.mhla_oracle_summaries.argtypes = [vp, vp, fp, P, ip, ctypes.c_int32,
+                                              dp, dp, dp, dp, ctypes.c_int32]
+        lib.mhla_oracle_summaries.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _problem(grid, block, heads, head_dim, batch, dtype, eps) -> _Problem:
+    p = _Problem()
+    p.batch, p.heads, p.head_dim, p.dtype = batch, heads, head_dim, dtype
+    p.ndim = len(grid)
+    for a in range(3):
+        p.grid[a] = grid[a] if a < len(grid) else 1
+        p.block[a] = block[a] if a < len(block) else 1
+    p.eps = eps
+    return p
+
+
+def _dtype_of(x: np.ndarray) -> int:
+    if x.dtype == np.uint16:
+        return BF16
+    if x.dtype == np.float32:
+        return F32
+    raise TypeError(f"inputs must be uint16 (bf16 bits) or float32, got {x.dtype}")
+
+
+def _ptr(x):
+    return x.ctypes.data_as(ctypes.c_void_p)
+
+
+def _prep(q, k, v, W, grid, block):
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    q = None if q is None else np.ascontiguousarray(q)
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    if k.ndim != 4:
+        raise ValueError("q/k/v must be [B, N, H, d]")
+    B, N, H, d = k.shape
+    dt = _dtype_of(k)
+    for x in (q, v):
+        if x is not None and (x.shape != k.shape or x.dtype != k.dtype):
+            raise ValueError("q, k, v must share shape and dtype")
+    if int(np.prod(grid)) != N:
+        raise ValueError("grid does not match N")
+    return q, k, v, W, B, N, H, d, dt
+
+
+def phi(x: float) -> float:
+    """The oracle's feature map, elu(x) + 1 (exported for pinning)."""
+    return _load().mhla_oracle_phi(float(x))
+
+
+def num_blocks(grid, block) -> int:
+    return int(_load().mhla_oracle_num_blocks(ctypes.byref(_problem(grid, block, 1, 1, 1, F32, 0.0))))
+
+
+def token_blocks_c(grid, block) -> np.ndarray:
+    """Block id per raster token, from the C oracle's geometry."""
+    N = int(np.prod(grid))
+    out = np.empty(N, dtype=np.int32)
+    rc = _load().mhla_oracle_token_blocks(ctypes.byref(_problem(grid, block, 1, 1, 1, F32, 0.0)),
+                                          out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    if rc != 0:
+        raise ValueError("invalid geometry")
+    return out
+
+
+def forward(q, k, v, W, grid, block, eps=1e-6, pairs=None, threads=0, return_threads=False):
+    """Blockwise float64 forward.
+
+    pairs: None for every (b, h) pair -> returns [B, N, H, d];
+           or a list of indices b*H + h -> returns [len(pairs), N, d].
+    """
+    q, k, v, W, B, N, H, d, dt = _prep(q, k, v, W, grid, block)
+    p = _problem(grid, block, H, d, B, dt, eps)
+    if pairs is None:
+        sel, nsel = None, B * H
+    else:
+        sel = np.ascontiguousarray(pairs, dtype=np.int32)
+        nsel = len(sel)
+    out = np.empty((nsel, N, d), dtype=np.float64)
+    used = ctypes.c_int32(0)
+    rc = _load().mhla_oracle_forward(
+        _ptr(q), _ptr(k), _ptr(v), W.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+        ctypes.byref(p), None if sel is None else sel.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        nsel, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), threads, ctypes.byref(used))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    if pairs is None:
+        out = out.reshape(B, H, N, d).transpose(0, 2, 1, 3)
+    return (out, used.value) if return_threads else out
+
+
+def summaries(k, v, W, grid, block, pairs=None, threads=0):
+    """Intermediates (S, z, St, zt) for the selected pairs.
+
+    Shapes: S, St [P, M, d, d] indexed [c, e]; z, zt [P, M, d]."""
+    _, k, v, W, B, N, H, d, dt = _prep(None, k, v, W, grid, block)
+    p = _problem(grid, block, H, d, B, dt, 0.0)
+    M = num_blocks(grid, block)
+    if pairs is None:
+        sel, nsel = None, B * H
+    else:
+        sel = np.ascontiguousarray(pairs, dtype=np.int32)
+        nsel = len(sel)
+    S = np.empty((nsel, M, d, d)); z = np.empty((nsel, M, d))
+    St = np.empty((nsel, M, d, d)); zt = np.empty((nsel, M, d))
+    dp = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    rc = _load().mhla_oracle_summaries(
+        _ptr(k), _ptr(v), W.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), ctypes.byref(p),
+        None if sel is None else sel.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), nsel,
+        dp(S), dp(z), dp(St), dp(zt), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return S, z, St, zt
+
+
+# ---------------------------------------------------------------------------
+# Materialised N x N form (numpy)
+# ---------------------------------------------------------------------------
+
+def decode(x: np.ndarray) -> np.ndarray:
+    """Exact float64 values of bf16 bit patterns or float32 inputs."""
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def phi_np(x: np.ndarray) -> np.ndarray:
+    """elu(x) + 1 elementwise."""
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def token_blocks(grid, block) -> np.ndarray:
+    """Block id per raster token via numpy index utilities: block coordinate =
+    token coordinate // block extent, ids row-major over the block grid."""
+    grid = tuple(int(g) for g in grid)
+    block = tuple(int(b) for b in block)
+    if any(g % b for g, b in zip(grid, block)):
+        raise ValueError("grid not divisible by block")
+    coords = np.indices(grid).reshape(len(grid), -1)
+    nb = tuple(g // b for g, b in zip(grid, block))
+    return np.ravel_multi_index(tuple(c // b for c, b in zip(coords, block)), nb)
+
+
+def attention_matrix(qh, kh, W, bid, rows=None) -> np.ndarray:
+    """Un-normalised MHLA attention for one head: A[n, m] = W[b(n), b(m)] phi(q_n).phi(k_m).
+
+    qh, kh: float64 [N, d]; bid: block id per token; rows: optional query subset."""
+    r = np.arange(qh.shape[0]) if rows is None else np.asarray(rows)
+    W = np.asarray(W, dtype=np.float64)
+    return W[np.ix_(bid[r], bid)] * (phi_np(qh[r]) @ phi_np(kh).T)
+
+
+def bruteforce_head(qh, kh, vh, W, bid, eps, rows=None) -> np.ndarray:
+    """o_n = sum_m A[n, m] v_m / (sum_m A[n, m] + eps) for one head (float64)."""
+    A = attention_matrix(qh, kh, W, bid, rows)
+    return (A @ vh) / (A.sum(axis=1) + eps)[:, None]
+
+
+def bruteforce(q, k, v, W, grid, block, eps=1e-6, pairs=None, rows=None):
+    """Brute-force forward.  pairs=None -> [B, N, H, d] (rows must be None);
+    otherwise [len(pairs), R, d] for query rows `rows` (default all)."""
+    B, N, H, d = k.shape
+    bid = token_blocks(grid, block)
+    Q, K, V = decode(q), decode(k), decode(v)
+    if pairs is None:
+        out = np.empty((B, N, H, d))
+        for b in range(B):
+            for h in range(H):
+                out[b, :, h, :] = bruteforce_head(Q[b, :, h], K[b, :, h], V[b, :, h], W, bid, eps)
+        return out
+    res = []
+    for s in pairs:
+        b, h = divmod(int(s), H)
+        res.append(bruteforce_head(Q[b, :, h], K[b, :, h], V[b, :, h], W, bid, eps, rows))
+    return np.stack(res)

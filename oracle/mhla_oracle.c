@@ -1,0 +1,238 @@
+/*
+ * mhla_oracle.c -- plain CPU reference of the MHLA forward pass, in float64.
+ *
+ * TEST INFRASTRUCTURE ONLY (see mhla_oracle.h).  Deliberately simple: scalar
+ * loops, float64 accumulation in ascending token / block order, one worker
+ * thread per (b, h) pair.  No blocking, fusion or reordering beyond the
+ * method's own blockwise reorganisation (paperlayer.ai summary of
+ * arXiv 2601.07832, section 4 "Efficiency": summaries are formed once per
+ * block and mixtures once per query block, then reused by every query).
+ */
+#include "mhla_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ---- geometry (section 4 "Architecture": M non-overlapping token blocks on
+ * a spatial / spatio-temporal grid; blocks and tokens both row-major) ---- */
+
+typedef struct {
+    int64_t N, M, T;     /* tokens, blocks, tokens per block */
+    int32_t g[3], b[3], nb[3];  /* padded to 3 axes, slowest first */
+} geom;
+
+static int make_geom(const mhla_oracle_problem* p, geom* G) {
+    if (!p || (p->ndim != 2 && p->ndim != 3)) return -1;
+    if (p->batch < 0 || p->heads < 0 || p->head_dim <= 0) return -1;
+    if (p->dtype != MHLA_ORACLE_F32 && p->dtype != MHLA_ORACLE_BF16) return -1;
+    if (!(p->eps >= 0.0)) return -1;
+    int off = 3 - p->ndim;
+    for (int a = 0; a < 3; ++a) { G->g[a] = 1; G->b[a] = 1; }
+    for (int a = 0; a < p->ndim; ++a) {
+        if (p->grid[a] <= 0 || p->block[a] <= 0) return -1;
+        if (p->grid[a] % p->block[a] != 0) return -1;
+        G->g[off + a] = p->grid[a];
+        G->b[off + a] = p->block[a];
+    }
+    G->N = 1; G->M = 1; G->T = 1;
+    for (int a = 0; a < 3; ++a) {
+        G->nb[a] = G->g[a] / G->b[a];
+        G->N *= G->g[a];
+        G->M *= G->nb[a];
+        G->T *= G->b[a];
+    }
+    return 0;
+}
+
+/* Block id of raster token n: its per-axis coordinate divided by the block
+ * extent gives the block coordinate; block ids are row-major over those. */
+static int64_t block_of(const geom* G, int64_t n) {
+    int64_t x2 = n % G->g[2];
+    int64_t x1 = (n / G->g[2]) % G->g[1];
+    int64_t x0 = n / ((int64_t)G->g[2] * G->g[1]);
+    int64_t c0 = x0 / G->b[0], c1 = x1 / G->b[1], c2 = x2 / G->b[2];
+    return (c0 * G->nb[1] + c1) * G->nb[2] + c2;
+}
+
+/* ---- element decoding and feature map ---- */
+
+static double load_elem(const void* base, int dtype, int64_t idx) {
+    if (dtype == MHLA_ORACLE_F32) {
+        float f;
+        memcpy(&f, (const char*)base + 4 * idx, 4);
+        return (double)f;
+    }
+    uint16_t h;
+    memcpy(&h, (const char*)base + 2 * idx, 2);
+    uint32_t u = (uint32_t)h << 16;   /* bfloat16 is the top half of a float32 */
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* phi(x) = elu(x) + 1 (alpha = 1): x + 1 for x > 0, exp(x) otherwise.
+ * Strictly positive, so every kernel weight phi(q).phi(k) is positive. */
+double mhla_oracle_phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+int64_t mhla_oracle_num_blocks(const mhla_oracle_problem* p) {
+    geom G;
+    if (make_geom(p, &G) != 0) return -1;
+    return G.M;
+}
+
+int mhla_oracle_token_blocks(const mhla_oracle_problem* p, int32_t* out) {
+    geom G;
+    if (make_geom(p, &G) != 0 || !out) return -1;
+    for (int64_t n = 0; n < G.N; ++n) out[n] = (int32_t)block_of(&G, n);
+    return 0;
+}
+
+/* ---- one (b, h) pair ---- */
+
+typedef struct {
+    const void *q, *k, *v;
+    const float* W;
+    const mhla_oracle_problem* p;
+    const geom* G;
+    /* outputs, each already offset to this pair (may be NULL) */
+    double *out, *S, *z, *St, *zt;
+} pair_job;
+
+static void run_pair(const pair_job* J, int32_t b, int32_t h) {
+    const geom* G = J->G;
+    const int64_t H = J->p->heads, d = J->p->head_dim, N = G->N, M = G->M;
+    const int dt = J->p->dtype;
+    const int64_t row = H * d;                      /* elements per token */
+    const int64_t base = (int64_t)b * N * row + (int64_t)h * d;
+
+    double* S = calloc((size_t)(M * d * d), sizeof(double));
+    double* z = calloc((size_t)(M * d), sizeof(double));
+    double* St = calloc((size_t)(M * d * d), sizeof(double));
+    double* zt = calloc((size_t)(M * d), sizeof(double));
+    double* fk = malloc((size_t)d * sizeof(double));
+    double* vv = malloc((size_t)d * sizeof(double));
+    if (!S || !z || !St || !zt || !fk || !vv) abort();
+
+    /* Local key-value summaries, one per block (repost section 5 item (2)):
+     * S_j += phi(k_m) v_m^T and z_j += phi(k_m) for every token m of block j. */
+    for (int64_t m = 0; m < N; ++m) {
+        int64_t j = block_of(G, m);
+        for (int64_t c = 0; c < d; ++c) fk[c] = mhla_oracle_phi(load_elem(J->k, dt, base + m * row + c));
+        for (int64_t e = 0; e < d; ++e) vv[e] = load_elem(J->v, dt, base + m * row + e);
+        double* Sj = S + j * d * d;
+        for (int64_t c = 0; c < d; ++c) {
+            z[j * d + c] += fk[c];
+            for (int64_t e = 0; e < d; ++e) Sj[c * d + e] += fk[c] * vv[e];
+        }
+    }
+
+    /* Multi-head mixing (section 4 "Multi-Head Mixing"): query block i takes
+     * the combination of all local summaries given by row i of W. */
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < M; ++j) {
+            double w = (double)J->W[i * M + j];
+            for (int64_t t = 0; t < d * d; ++t) St[i * d * d + t] += w * S[j * d * d + t];
+            for (int64_t c = 0; c < d; ++c) zt[i * d + c] += w * z[j * d + c];
+        }
+    }
+
+    /* Every query reads its own block's mixed summary:
+     * o_n = phi(q_n)^T St_i / (phi(q_n) . zt_i + eps). */
+    if (J->out) {
+        double* fq = fk;
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t i = block_of(G, n);
+            for (int64_t c = 0; c < d; ++c) fq[c] = mhla_oracle_phi(load_elem(J->q, dt, base + n * row + c));
+            double den = 0.0;
+            for (int64_t c = 0; c < d; ++c) den += fq[c] * zt[i * d + c];
+            den += J->p->eps;
+            for (int64_t e = 0; e < d; ++e) {
+                double num = 0.0;
+                for (int64_t c = 0; c < d; ++c) num += fq[c] * St[i * d * d + c * d + e];
+                J->out[n * d + e] = num / den;
+            }
+        }
+    }
+    if (J->S) memcpy(J->S, S, (size_t)(M * d * d) * sizeof(double));
+    if (J->z) memcpy(J->z, z, (size_t)(M * d) * sizeof(double));
+    if (J->St) memcpy(J->St, St, (size_t)(M * d * d) * sizeof(double));
+    if (J->zt) memcpy(J->zt, zt, (size_t)(M * d) * sizeof(double));
+    free(S); free(z); free(St); free(zt); free(fk); free(vv);
+}
+
+/* ---- thread pool over the selected pairs (static round-robin split) ---- */
+
+typedef struct {
+    const void *q, *k, *v;
+    const float* W;
+    const mhla_oracle_problem* p;
+    const geom* G;
+    const int32_t* sel;
+    int32_t nsel, nthreads, tid;
+    double *out, *S, *z, *St, *zt;
+} worker_arg;
+
+static void* worker(void* arg) {
+    const worker_arg* A = (const worker_arg*)arg;
+    const int64_t N = A->G->N, M = A->G->M, d = A->p->head_dim, H = A->p->heads;
+    for (int32_t s = A->tid; s < A->nsel; s += A->nthreads) {
+        int32_t pair = A->sel ? A->sel[s] : s;
+        pair_job J = {A->q, A->k, A->v, A->W, A->p, A->G, NULL, NULL, NULL, NULL, NULL};
+        if (A->out) J.out = A->out + (int64_t)s * N * d;
+        if (A->S) J.S = A->S + (int64_t)s * M * d * d;
+        if (A->z) J.z = A->z + (int64_t)s * M * d;
+        if (A->St) J.St = A->St + (int64_t)s * M * d * d;
+        if (A->zt) J.zt = A->zt + (int64_t)s * M * d;
+        run_pair(&J, (int32_t)(pair / H), (int32_t)(pair % H));
+    }
+    return NULL;
+}
+
+static int run_all(const void* q, const void* k, const void* v, const float* W,
+                   const mhla_oracle_problem* p, const int32_t* sel, int32_t nsel,
+                   double* out, double* S, double* z, double* St, double* zt,
+                   int32_t threads, int32_t* threads_used) {
+    geom G;
+    if (make_geom(p, &G) != 0) return -1;
+    int64_t pairs = (int64_t)p->batch * p->heads;
+    if (!sel) nsel = (int32_t)pairs;
+    if (nsel < 0) return -1;
+    for (int32_t s = 0; sel && s < nsel; ++s)
+        if (sel[s] < 0 || sel[s] >= pairs) return -1;
+    if (nsel > 0 && (!k || !v || !W || (out && !q))) return -1;
+    if (threads <= 0) threads = (int32_t)sysconf(_SC_NPROCESSORS_ONLN);
+    if (threads < 1) threads = 1;
+    if (threads > nsel) threads = nsel > 0 ? nsel : 1;
+    if (threads_used) *threads_used = threads;
+    if (nsel == 0) return 0;
+
+    pthread_t* tids = malloc(sizeof(pthread_t) * (size_t)threads);
+    worker_arg* args = malloc(sizeof(worker_arg) * (size_t)threads);
+    if (!tids || !args) abort();
+    for (int32_t t = 0; t < threads; ++t) {
+        worker_arg a = {q, k, v, W, p, &G, sel, nsel, threads, t, out, S, z, St, zt};
+        args[t] = a;
+    }
+    for (int32_t t = 1; t < threads; ++t) pthread_create(&tids[t], NULL, worker, &args[t]);
+    worker(&args[0]);
+    for (int32_t t = 1; t < threads; ++t) pthread_join(tids[t], NULL);
+    free(tids);
+    free(args);
+    return 0;
+}
+
+int mhla_oracle_forward(const void* q, const void* k, const void* v, const float* W,
+                        const mhla_oracle_problem* p, const int32_t* sel, int32_t nsel,
+                        double* out, int32_t threads, int32_t* threads_used) {
+    if (!out) return -1;
+    return run_all(q, k, v, W, p, sel, nsel, out, NULL, NULL, NULL, NULL, threads, threads_used);
+}
+
+int mhla_oracle_summaries(const void* k, const void* v, const float* W,
+                          const mhla_oracle_problem* p, const int32_t* sel, int32_t nsel,
+                          double* S, double* z, double* St, double* zt, int32_t threads) {
+    return run_all(NULL, k, v, W, p, sel, nsel, NULL, S, z, St, zt, threads, NULL);
+}
