@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Benchmark of the MHLA forward pass (libmhla) on one MI355X.
+
+One step = one full forward (block_kv_summary -> mix_summaries -> query_apply,
+or the fused path) over one batch of seeded synthetic inputs already resident
+in HBM.  Several input/output sets are rotated so that the 256 MB Infinity
+Cache cannot serve the inputs of a step from the previous one.
+
+Prints ONE JSON line: tokens/s over the timed steps, achieved algorithmic HBM
+bandwidth of the whole path, a roofline entry for the dominant kernel (its
+algorithmic bytes over its average duration, timed with HIP events on the
+launch stream), and the float64 CPU oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MHLA fwd tokens/s + achieved HBM GB/s (% peak), N=65536 H=6 d=64 bf16"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+MALL_BYTES = 256 << 20          # Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload index (2 = the metric's workload)")
+    ap.add_argument("--path", choices=["3kernel", "fused"], default="3kernel")
+    ap.add_argument("--w", choices=["gaussian", "local", "identity", "ones"], default="gaussian")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough to exceed 2x the MALL)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--out", default="", help="also write the JSON line to this file")
+    return ap.parse_args()
+
+
+def kernel_bytes(p, ws_elem):
+    """Algorithmic HBM bytes per launch of each kernel (compulsory reads + writes)."""
+    B, N, H, d, M = p.batch, p.n_tokens, p.heads, p.head_dim, p.n_blocks
+    e = p.elem_bytes
+    P = B * H
+    tensor = B * N * H * d * e
+    sz = P * M * (d * d + d) * ws_elem
+    st = P * M * d * d * ws_elem
+    zt = P * M * d * 4
+    w = M * M * 4
+    return {
+        "block_kv_summary": 2 * tensor + sz,
+        "mix_summaries": sz + w + st + zt,
+        "query_apply": tensor + st + zt + tensor,
+        "query_apply_fused": tensor + sz + w + tensor,   # every summary read at least once
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the (b, h) pairs are independent, so more GPUs would each run their own share).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import token_level_head_block_amd as mh
+    from token_level_head_block_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mh.lib()   # fail loudly if the HIP library is missing
+
+    p = synth.CONFIGS[args.config]
+    path = mh.MHLA_PATH_FUSED if args.path == "fused" else mh.MHLA_PATH_3KERNEL
+    tensor_bytes = p.batch * p.n_tokens * p.heads * p.head_dim * p.elem_bytes
+    per_set = 4 * tensor_bytes
+    sets = args.sets or max(2, int(np.ceil(2 * MALL_BYTES / per_set)))
+    dt = torch.bfloat16 if p.dtype == synth.BF16 else torch.float32
+
+    def dev(x):
+        if p.dtype == synth.BF16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    data = []
+    for s in range(sets):
+        q, k, v, W = synth.make_inputs(p, seed=(args.config, s) if s else args.config, w_kind=args.w)
+        data.append((dev(q), dev(k), dev(v), torch.from_numpy(W).cuda(), torch.empty(q.shape, dtype=dt, device="cuda")))
+        if s == 0:
+            host0 = (q, k, v, W)
+    g = mh.make_grid(p.batch, p.heads, p.head_dim, mh.MHLA_BF16 if p.dtype == synth.BF16 else mh.MHLA_F32,
+                     p.grid, p.eps)
+    b = mh.make_block(p.block)
+    ws_bytes = mh.mhla_workspace_bytes(g, b)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        q, k, v, W, out = data[i % sets]
+        st = mh.mhla_forward_ex(q, k, v, W, g, b, out, ws, ws_bytes, path, events, stream)
+        if st != mh.MHLA_OK:
+            raise mh.MhlaError(st, "mhla_forward_ex")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` forward passes
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    tokens_per_s = p.batch * p.n_tokens / (ms_step * 1e-3)
+    U = 4 * tensor_bytes + 4 * p.n_blocks ** 2
+    path_gbps = U / (ms_step * 1e-3) / 1e9
+
+    # ---- per-kernel attribution: stage events on the launch stream, same loop
+    nstage = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nstage)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(nstage):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(3)] for row in evs])
+    avg = stage_ms.mean(axis=0)
+    names = (["block_kv_summary", "mix_summaries", "query_apply"] if path == mh.MHLA_PATH_3KERNEL
+             else ["block_kv_summary", "(none)", "query_apply_fused"])
+    ws_elem = p.elem_bytes
+    kb = kernel_bytes(p, ws_elem)
+    kernels = {}
+    for j, n in enumerate(names):
+        if n == "(none)":
+            continue
+        gbps = kb[n] / (avg[j] * 1e-3) / 1e9
+        kernels[n] = {"avg_us": round(float(avg[j]) * 1e3, 2), "alg_bytes": int(kb[n]),
+                      "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": kernels[dom]["frac"], "traffic": None,
+                "avg_us": kernels[dom]["avg_us"], "alg_bytes": kernels[dom]["alg_bytes"]}
+
+    # ---- CPU baseline: the float64 oracle on the host cores
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        q, k, v, W = host0
+        ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        t = time.perf_counter()
+        _, used = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps, threads=ncpu, return_threads=True)
+        dt_cpu = time.perf_counter() - t
+        cpu = {"value": round(p.batch * p.n_tokens / dt_cpu, 1), "unit": "tokens/s", "cores": used,
+               "kind": "oracle", "seconds": round(dt_cpu, 3),
+               "sample": f"the full workload ({p.batch * p.heads} (b,h) pairs, {p.n_tokens} tokens), "
+                         f"float64 blockwise oracle, one thread per pair"}
+
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if p.dtype == synth.BF16 else "f32", "data": "synthetic",
+        "config": {"workload": f"{p.name}: B={p.batch} H={p.heads} d={p.head_dim} grid={list(p.grid)} "
+                               f"blocks={list(p.block)} N={p.n_tokens} M={p.n_blocks}",
+                   "path": args.path, "w": args.w, "input_sets": sets, "parallelism": "none (1 GPU)"},
+        "path_hbm_gbps": round(path_gbps, 1), "path_hbm_frac": round(path_gbps / HBM_PEAK_GBPS, 4),
+        "path_alg_bytes": U,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()

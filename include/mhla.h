@@ -1,0 +1,149 @@
+/*
+ * mhla.h -- libmhla: the MHLA forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * MHLA ("Restoring Expressivity of Linear Attention via Token-Level
+ * Multi-Head", arXiv 2601.07832; paperlayer.ai summary, section 4
+ * "Architecture", "Multi-Head Mixing", "Efficiency"; 171host.com repost,
+ * section 5 items (1)-(3)) splits the tokens of a 2D or 3D grid into M
+ * non-overlapping blocks and computes, for every (batch b, head h):
+ *
+ *   S_j  = sum_{m in block j} phi(k_m) v_m^T          (d x d)
+ *   z_j  = sum_{m in block j} phi(k_m)                (d)
+ *   St_i = sum_j W[i,j] S_j,   zt_i = sum_j W[i,j] z_j
+ *   o_n  = phi(q_n)^T St_i / (phi(q_n) . zt_i + eps)   for token n in block i
+ *
+ * with phi(x) = elu(x) + 1 and one M x M coefficient matrix W shared by all
+ * batches and heads.  The work runs as hand-written HIP kernels on the
+ * caller's stream; every call is asynchronous.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - q, k, v, out: device pointers to contiguous [B, N, H, d] tensors of the
+ *   grid's dtype (IEEE float32 or bfloat16), N = prod(grid extents) in raster
+ *   order over the grid (last axis fastest), channel index h*d + c.
+ * - W: device pointer to a contiguous row-major float32 [M, M] matrix;
+ *   W[i*M + j] weights source block j for query block i.  Blocks are
+ *   numbered row-major over the block grid (slowest axis first).
+ * - All pointers are owned by the caller; the library never frees or keeps
+ *   them past the call's enqueued work.  q, k, v, W and out must be 16-byte
+ *   aligned, and out must not overlap q, k, v or W.
+ * - bfloat16 path: products in bf16 MFMA with fp32 accumulation; phi is
+ *   evaluated in fp32; summaries and mixed summaries are stored in bf16,
+ *   normalisers in fp32; output rounded to nearest even.  float32 path: all
+ *   arithmetic in fp32 (fp32 MFMA), intermediates in fp32.
+ * - B = 0 or H = 0 is an empty problem: the call validates and returns
+ *   MHLA_OK without launching anything.
+ * - Validation errors are returned before any HIP call; in that case nothing
+ *   is enqueued.  Faults inside kernels surface at the caller's next
+ *   synchronisation of `stream`.
+ * - The library holds no global state and is safe to call from several
+ *   threads; calls that share a workspace must not overlap in time.
+ */
+#ifndef MHLA_H
+#define MHLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mhla_status {
+    MHLA_OK = 0,
+    MHLA_ERR_INVALID_ARG = 1,   /* null pointer, bad extents, grid % block != 0, eps < 0 or
+                                   not finite, out overlapping an input, workspace too small */
+    MHLA_ERR_UNSUPPORTED = 2,   /* head_dim not in {32, 64, 128}, unknown dtype, or a tensor
+                                   with 2^31 or more elements */
+    MHLA_ERR_MISALIGNED = 3,    /* q, k, v, W, out or workspace not 16-byte aligned */
+    MHLA_ERR_ALLOC = 4,         /* workspace allocation on the stream failed */
+    MHLA_ERR_HIP = 5            /* a HIP launch or runtime call failed */
+} mhla_status;
+
+typedef enum mhla_dtype {
+    MHLA_F32 = 0,
+    MHLA_BF16 = 1
+} mhla_dtype;
+
+/* Problem shape.  extent[0..ndim-1] are the token-grid extents, slowest
+ * axis first (2D: {Y, X}; 3D: {T, Y, X}); entries past ndim are ignored. */
+typedef struct mhla_grid {
+    int32_t batch;       /* B >= 0 */
+    int32_t heads;       /* H >= 0 */
+    int32_t head_dim;    /* d: 32, 64 or 128 */
+    int32_t dtype;       /* mhla_dtype of q, k, v and out */
+    int32_t ndim;        /* 2 or 3 */
+    int32_t extent[3];
+    float eps;           /* added once to every mixed normaliser; finite, >= 0 */
+} mhla_grid;
+
+/* Block shape in tokens, same axes and order as the grid; every grid extent
+ * must be a multiple of the matching block extent (non-overlapping blocks
+ * that tile the grid: section 4 "Architecture"). */
+typedef struct mhla_block {
+    int32_t extent[3];
+} mhla_block;
+
+/* Path selection for mhla_forward_ex. */
+enum {
+    MHLA_PATH_3KERNEL = 0,   /* block_kv_summary -> mix_summaries -> query_apply */
+    MHLA_PATH_FUSED = 1      /* block_kv_summary -> query_apply_fused (mixes per query
+                                block on the fly, skipping zero W entries) */
+};
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* mhla_status_string(mhla_status status);
+
+/* Validates grid and block alone (no pointers).  Returns MHLA_OK,
+ * MHLA_ERR_INVALID_ARG or MHLA_ERR_UNSUPPORTED.  On success and if non-NULL,
+ * *num_blocks receives M and *block_tokens receives T = N / M. */
+mhla_status mhla_check_problem(const mhla_grid* grid, const mhla_block* block,
+                               int64_t* num_blocks, int64_t* block_tokens);
+
+/* Bytes of device workspace mhla_forward_ws / mhla_forward_ex need for this
+ * problem (0 for an invalid problem or an empty one).  Layout, from the
+ * start of the workspace, for P = B*H pairs ordered (b, h):
+ *   region 0: summaries, P*M records of (d*d + d) elements of the compute
+ *             type (bf16 for a bf16 problem, fp32 for fp32): S_j transposed
+ *             ([e][c], c fastest: element (e, c) = sum phi(k)[c] v[e]),
+ *             then z_j[c];
+ *   region 1 (at a 256-byte boundary): mixed summaries St_i transposed,
+ *             P*M records of d*d compute-type elements ([e][c]);
+ *   region 2 (at a 256-byte boundary): mixed normalisers zt_i, P*M*d fp32.
+ * After a 3-kernel call completes, the regions hold these intermediates;
+ * the fused path fills region 0 only. */
+size_t mhla_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
+
+/* The MHLA forward pass: out = MHLA(q, k, v; W) for the whole problem,
+ * enqueued on `stream` (0 = the null stream).  Allocates its workspace with
+ * hipMallocAsync / hipFreeAsync on the same stream (MHLA_ERR_ALLOC if that
+ * fails).  Uses the 3-kernel path. */
+mhla_status mhla_forward(const void* q, const void* k, const void* v, const float* W,
+                         const mhla_grid* grid, const mhla_block* block, void* out,
+                         hipStream_t stream);
+
+/* As mhla_forward, with a caller-provided device workspace of ws_bytes
+ * >= mhla_workspace_bytes(grid, block) bytes (16-byte aligned).  Allocates
+ * nothing. */
+mhla_status mhla_forward_ws(const void* q, const void* k, const void* v, const float* W,
+                            const mhla_grid* grid, const mhla_block* block, void* out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* As mhla_forward_ws, with a path choice (MHLA_PATH_*) and optional stage
+ * events.  If stage_events is non-NULL it points to 4 hipEvent_t handles
+ * created by the caller; they are recorded on `stream` before the first
+ * kernel, after the summary kernel, after the mixing kernel (right after
+ * the summary kernel on the fused path) and after the last kernel, so the
+ * caller can time each kernel with hipEventElapsedTime.  ws may be NULL
+ * (with ws_bytes 0) to allocate on the stream as mhla_forward does. */
+mhla_status mhla_forward_ex(const void* q, const void* k, const void* v, const float* W,
+                            const mhla_grid* grid, const mhla_block* block, void* out,
+                            void* ws, size_t ws_bytes, int32_t path,
+                            const hipEvent_t* stage_events, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MHLA_H */

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: exports, status strings, workspace arithmetic and
+every validation error (all returned before any HIP call)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import token_level_head_block_amd as mh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mhla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return mh.lib()
+
+
+def test_every_declared_function_is_exported(L):
+    names = header_functions()
+    assert {"mhla_forward", "mhla_forward_ws", "mhla_forward_ex", "mhla_workspace_bytes",
+            "mhla_status_string", "mhla_check_problem"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(6):
+        s = mh.mhla_status_string(code)
+        assert s.startswith("MHLA_")
+    assert mh.mhla_status_string(99) == "unknown mhla_status"
+
+
+def cfg2():
+    return mh.make_grid(1, 6, 64, mh.MHLA_BF16, (256, 256), 1e-6), mh.make_block((16, 16))
+
+
+def test_workspace_bytes_layout(L):
+    g, b = cfg2()
+    st, M, T = mh.mhla_check_problem(g, b)
+    assert (st, M, T) == (mh.MHLA_OK, 256, 256)
+    recs = 6 * 256
+    up = lambda x: (x + 255) // 256 * 256
+    assert mh.mhla_workspace_bytes(g, b) == up(recs * (64 * 64 + 64) * 2) + up(recs * 64 * 64 * 2) + up(recs * 64 * 4)
+    g32 = mh.make_grid(1, 1, 32, mh.MHLA_F32, (16, 16), 1e-6)
+    assert mh.mhla_workspace_bytes(g32, mh.make_block((4, 4))) == \
+        up(16 * (32 * 32 + 32) * 4) + up(16 * 32 * 32 * 4) + up(16 * 32 * 4)
+    g3 = mh.make_grid(1, 12, 128, mh.MHLA_BF16, (16, 64, 64), 1e-6)
+    assert mh.mhla_check_problem(g3, mh.make_block((4, 8, 8)))[1:] == (256, 256)
+    assert mh.mhla_workspace_bytes(mh.make_grid(0, 6, 64, mh.MHLA_BF16, (256, 256)), b) == 0
+
+
+@pytest.mark.parametrize("mut,code", [
+    (lambda g, b: setattr(g, "head_dim", 48), mh.MHLA_ERR_UNSUPPORTED),
+    (lambda g, b: setattr(g, "dtype", 7), mh.MHLA_ERR_UNSUPPORTED),
+    (lambda g, b: setattr(g, "ndim", 4), mh.MHLA_ERR_INVALID_ARG),
+    (lambda g, b: setattr(g, "ndim", 1), mh.MHLA_ERR_INVALID_ARG),
+    (lambda g, b: setattr(g, "batch", -1), mh.MHLA_ERR_INVALID_ARG),
+    (lambda g, b: setattr(g, "eps", -1e-6), mh.MHLA_ERR_INVALID_ARG),
+    (lambda g, b: setattr(g, "eps", math.nan), mh.MHLA_ERR_INVALID_ARG),
+    (lambda g, b: setattr(g, "eps", math.inf), mh.MHLA_ERR_INVALID_ARG),
+    (lambda g, b: b.extent.__setitem__(0, 15), mh.MHLA_ERR_INVALID_ARG),      # 256 % 15 != 0
+    (lambda g, b: b.extent.__setitem__(1, 0), mh.MHLA_ERR_INVALID_ARG),
+    (lambda g, b: g.extent.__setitem__(0, -256), mh.MHLA_ERR_INVALID_ARG),
+    (lambda g, b: setattr(g, "batch", 1 << 20), mh.MHLA_ERR_UNSUPPORTED),     # >= 2^31 elements
+], ids=["d48", "dtype", "ndim4", "ndim1", "neg-batch", "neg-eps", "nan-eps", "inf-eps",
+        "not-divisible", "zero-block", "neg-extent", "too-large"])
+def test_problem_validation(L, mut, code):
+    g, b = cfg2()
+    mut(g, b)
+    assert mh.mhla_check_problem(g, b)[0] == code
+    assert mh.mhla_workspace_bytes(g, b) == 0
+    # the forward entry points return the same code before touching HIP
+    fake = 1 << 20
+    assert L.mhla_forward(fake, fake * 2, fake * 3, fake * 4, ctypes.byref(g), ctypes.byref(b),
+                          fake * 5, None) == code
+
+
+def test_null_structs(L):
+    assert L.mhla_check_problem(None, None, None, None) == mh.MHLA_ERR_INVALID_ARG
+    assert L.mhla_workspace_bytes(None, None) == 0
+
+
+BIG = 1 << 36          # fake, 16-byte aligned, far apart: never dereferenced
+
+
+def call_fwd(L, g, b, q=BIG, k=2 * BIG, v=3 * BIG, W=4 * BIG, out=5 * BIG, ws=None, ws_bytes=0, path=0,
+             entry="ex"):
+    if entry == "ex":
+        return L.mhla_forward_ex(q, k, v, W, ctypes.byref(g), ctypes.byref(b), out, ws, ws_bytes, path,
+                                 None, None)
+    return L.mhla_forward_ws(q, k, v, W, ctypes.byref(g), ctypes.byref(b), out, ws, ws_bytes, None)
+
+
+def test_pointer_validation(L):
+    g, b = cfg2()
+    need = mh.mhla_workspace_bytes(g, b)
+    ws = 6 * BIG
+    assert call_fwd(L, g, b, q=None, ws=ws, ws_bytes=need) == mh.MHLA_ERR_INVALID_ARG
+    assert call_fwd(L, g, b, W=None, ws=ws, ws_bytes=need) == mh.MHLA_ERR_INVALID_ARG
+    assert call_fwd(L, g, b, out=None, ws=ws, ws_bytes=need) == mh.MHLA_ERR_INVALID_ARG
+    assert call_fwd(L, g, b, k=2 * BIG + 8, ws=ws, ws_bytes=need) == mh.MHLA_ERR_MISALIGNED
+    assert call_fwd(L, g, b, out=5 * BIG + 2, ws=ws, ws_bytes=need) == mh.MHLA_ERR_MISALIGNED
+    assert call_fwd(L, g, b, ws=ws + 4, ws_bytes=need) == mh.MHLA_ERR_MISALIGNED
+    # out overlapping an input
+    assert call_fwd(L, g, b, out=BIG + 4096, ws=ws, ws_bytes=need) == mh.MHLA_ERR_INVALID_ARG
+    assert call_fwd(L, g, b, out=4 * BIG - 1024 * 16, ws=ws, ws_bytes=need) == mh.MHLA_ERR_INVALID_ARG
+    # workspace too small / overlapping out
+    assert call_fwd(L, g, b, ws=ws, ws_bytes=need - 16) == mh.MHLA_ERR_INVALID_ARG
+    assert call_fwd(L, g, b, ws=5 * BIG, ws_bytes=need) == mh.MHLA_ERR_INVALID_ARG
+    # unknown path
+    assert call_fwd(L, g, b, ws=ws, ws_bytes=need, path=7) == mh.MHLA_ERR_INVALID_ARG
+    # mhla_forward_ws requires a workspace
+    assert call_fwd(L, g, b, ws=None, ws_bytes=0, entry="ws") == mh.MHLA_ERR_INVALID_ARG
+    # ws NULL with nonzero size
+    assert call_fwd(L, g, b, ws=None, ws_bytes=64) == mh.MHLA_ERR_INVALID_ARG
+
+
+def test_empty_problem_is_a_no_op(L):
+    for B, H in ((0, 6), (1, 0)):
+        g = mh.make_grid(B, H, 64, mh.MHLA_BF16, (256, 256))
+        b = mh.make_block((16, 16))
+        assert call_fwd(L, g, b, q=None, k=None, v=None, W=None, out=None) == mh.MHLA_OK
+        assert call_fwd(L, g, b, q=None, k=None, v=None, W=None, out=None, entry="ws") == mh.MHLA_OK
+        assert L.mhla_forward(None, None, None, None, ctypes.byref(g), ctypes.byref(b), None, None) == mh.MHLA_OK

@@ -1,0 +1,167 @@
+"""HIP path vs the float64 CPU oracle, through the C ABI.
+
+Bar: max|d| / max|ref| <= 1e-5 for float32 problems and <= 1e-2 for bf16
+(bf16 I/O with fp32 accumulation).  Small problems are compared element by
+element over every output; the full-size workloads run in the benchmark's
+launch configuration and are compared on every output of sampled (b, h)
+pairs, which the oracle computes exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_level_head_block_amd as mh
+from token_level_head_block_amd import synth
+
+from gpu_util import TOL, Run, rel_err, say, to_host64
+
+pytestmark = pytest.mark.gpu
+
+BF, F = synth.BF16, synth.F32
+
+# name, B, H, d, grid, block, dtype, std  -- sizes the oracle finishes in seconds,
+# spanning several tiles, ragged token / block tails, 2D and 3D.
+SMALL = [
+    ("bf-d64-M24", 2, 3, 64, (32, 48), (8, 8), BF, 1.0),
+    ("bf-d32-T15", 1, 2, 32, (12, 20), (3, 5), BF, 1.0),
+    ("bf-d128-3d", 1, 2, 128, (4, 12, 12), (2, 3, 4), BF, 1.0),
+    ("bf-d64-T25-M64", 1, 2, 64, (40, 40), (5, 5), BF, 1.0),
+    ("bf-d64-M1", 1, 2, 64, (7, 9), (7, 9), BF, 1.0),
+    ("bf-d32-T1", 1, 1, 32, (6, 6), (1, 1), BF, 1.0),
+    ("bf-d32-M10", 1, 3, 32, (15, 10), (3, 5), BF, 0.5),
+    ("bf-d32-M360", 1, 1, 32, (36, 40), (2, 2), BF, 1.0),
+    ("bf-d128-T200", 1, 1, 128, (20, 40), (10, 20), BF, 1.0),
+    ("f32-d32-T15", 1, 2, 32, (12, 20), (3, 5), F, 1.0),
+    ("f32-d64-3d", 2, 1, 64, (8, 16, 8), (2, 4, 4), F, 1.0),
+    ("f32-d128", 1, 2, 128, (16, 16), (4, 8), F, 1.0),
+    ("f32-d64-M70", 1, 1, 64, (14, 20), (2, 2), F, 1.0),
+]
+
+
+def small_problem(case):
+    name, B, H, d, grid, block, dt, std = case
+    return synth.Problem(name, B, H, d, grid, block, dtype=dt, std=std)
+
+
+@pytest.mark.parametrize("path", [mh.MHLA_PATH_3KERNEL, mh.MHLA_PATH_FUSED], ids=["3kernel", "fused"])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c[0])
+def test_small_problems_all_outputs(case, path):
+    p = small_problem(case)
+    q, k, v, W = synth.make_inputs(p, seed=21)
+    ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)
+    out = to_host64(Run(p, q, k, v, W).forward(path))
+    err = rel_err(out, ref)
+    say(f"  {p.name} path={path}: max|d|/max|ref| = {err:.3e}")
+    assert np.isfinite(out).all()
+    assert err <= TOL[p.dtype]
+
+
+def test_tiny_fp32_workload_and_intermediates():
+    p = synth.CONFIGS[0]
+    q, k, v, W = synth.make_inputs(p, seed=0)
+    run = Run(p, q, k, v, W)
+    out = to_host64(run.forward())
+    ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)
+    assert rel_err(out, ref) <= 1e-5
+    S, z, St, zt = run.workspace()
+    rS, rz, rSt, rzt = oracle.summaries(k, v, W, p.grid, p.block)
+    for name, a, b in (("S", S, rS), ("z", z, rz), ("St", St, rSt), ("zt", zt, rzt)):
+        e = rel_err(a, b)
+        say(f"  {name}: {e:.2e}")
+        assert e <= 1e-5, name
+
+
+@pytest.mark.parametrize("case", [c for c in SMALL if c[6] == BF][:4], ids=lambda c: c[0])
+def test_bf16_intermediates(case):
+    """Per-kernel parity: summaries (bf16), mixed summaries (bf16) and mixed
+    normalisers (fp32) against the oracle's float64 intermediates."""
+    p = small_problem(case)
+    q, k, v, W = synth.make_inputs(p, seed=22)
+    run = Run(p, q, k, v, W)
+    run.forward()
+    S, z, St, zt = run.workspace()
+    rS, rz, rSt, rzt = oracle.summaries(k, v, W, p.grid, p.block)
+    for name, a, b in (("S", S, rS), ("z", z, rz), ("St", St, rSt), ("zt", zt, rzt)):
+        e = rel_err(a, b)
+        say(f"  {p.name} {name}: {e:.2e}")
+        assert e <= 1e-2, name
+
+
+@pytest.mark.parametrize("cfg_index", [1, 2, 3, 4])
+def test_full_workloads_sampled_pairs(cfg_index):
+    """Full-size workload, default launch configuration; every output of the
+    first and last (b, h) pair against the oracle, plus both paths agreeing."""
+    p = synth.CONFIGS[cfg_index]
+    q, k, v, W = synth.make_inputs(p, seed=cfg_index)
+    run = Run(p, q, k, v, W)
+    out = run.forward()
+    pairs = [0, p.batch * p.heads - 1]
+    ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps, pairs=pairs)
+    for s, pair in enumerate(pairs):
+        b, h = divmod(pair, p.heads)
+        got = to_host64(out[b, :, h, :])
+        err = rel_err(got, ref[s])
+        say(f"  {p.name} pair {pair}: max|d|/max|ref| = {err:.3e}")
+        assert err <= TOL[p.dtype]
+    # All outputs finite; determinism of the whole output over a second call.
+    assert torch.isfinite(out.float()).all().item()
+    out2 = run.forward()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("w_kind", ["identity", "ones", "local"])
+@pytest.mark.parametrize("path", [mh.MHLA_PATH_3KERNEL, mh.MHLA_PATH_FUSED], ids=["3kernel", "fused"])
+def test_special_coefficient_matrices(w_kind, path):
+    """W = I (per-block attention), W = 1/M (global attention), sparse local W."""
+    p = synth.Problem("special", 1, 2, 64, (64, 64), (8, 8))
+    q, k, v, W = synth.make_inputs(p, seed=23, w_kind=w_kind)
+    ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)
+    out = to_host64(Run(p, q, k, v, W).forward(path))
+    err = rel_err(out, ref)
+    say(f"  W={w_kind} path={path}: {err:.3e}")
+    assert err <= 1e-2
+
+
+def test_alloc_entry_point_matches_workspace_entry_point():
+    p = synth.CONFIGS[1].with_(batch=2)
+    q, k, v, W = synth.make_inputs(p, seed=24)
+    run = Run(p, q, k, v, W)
+    a = run.forward()
+    b = torch.empty_like(a)
+    say("  [gpu] mhla_forward (stream-ordered workspace)")
+    st = mh.mhla_forward(run.q, run.k, run.v, run.W, run.g, run.b, b)
+    assert st == mh.MHLA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_side_stream_and_stage_events():
+    p = synth.CONFIGS[2]
+    q, k, v, W = synth.make_inputs(p, seed=2)
+    run = Run(p, q, k, v, W)
+    ref = run.forward()
+    s = torch.cuda.Stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    with torch.cuda.stream(s):
+        for e in ev:
+            e.record(s)
+        out = torch.empty_like(ref)
+        say("  [gpu] mhla_forward_ex on a side stream with stage events")
+        st = mh.mhla_forward_ex(run.q, run.k, run.v, run.W, run.g, run.b, out, run.ws, run.ws_bytes,
+                                mh.MHLA_PATH_3KERNEL, ev, s)
+        assert st == mh.MHLA_OK
+    s.synchronize()
+    assert torch.equal(ref.view(torch.int16), out.view(torch.int16))
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+    say(f"  stage ms: {times}")
+    assert all(t > 0 for t in times)
+
+
+def test_empty_problem_on_gpu():
+    g = mh.make_grid(0, 6, 64, mh.MHLA_BF16, (256, 256))
+    x = torch.empty(0, 65536, 6, 64, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    st = mh.mhla_forward(x, x, x, torch.empty(256, 256, device="cuda"), g, mh.make_block((16, 16)), y)
+    torch.cuda.synchronize()
+    assert st == mh.MHLA_OK

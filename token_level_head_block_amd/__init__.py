@@ -1,1 +1,209 @@
-"""MHLA forward on MI355X (placeholder, binding follows)."""
+"""libmhla: the MHLA forward pass on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C ABI declared in ``include/mhla.h``: the
+functions below carry the C names and only marshal arguments (tensor data
+pointers, shape structs, the current HIP stream).  Every step of the forward
+pass runs in the HIP kernels of ``libmhla.so``; there is no Python or CPU
+fallback -- if the library is missing, every call raises.
+
+MHLA (arXiv 2601.07832; paperlayer.ai summary, section 4) splits the tokens of
+a 2D/3D grid into M non-overlapping blocks, summarises each block as
+S_j = phi(K_j)^T V_j and z_j = sum phi(k), mixes the summaries with a learnable
+M x M matrix W, and gives every query o = phi(q) St_i / (phi(q) . zt_i + eps).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmhla.so")
+
+MHLA_OK = 0
+MHLA_ERR_INVALID_ARG = 1
+MHLA_ERR_UNSUPPORTED = 2
+MHLA_ERR_MISALIGNED = 3
+MHLA_ERR_ALLOC = 4
+MHLA_ERR_HIP = 5
+
+MHLA_F32 = 0
+MHLA_BF16 = 1
+
+MHLA_PATH_3KERNEL = 0
+MHLA_PATH_FUSED = 1
+
+
+class mhla_grid(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("ndim", ctypes.c_int32), ("extent", ctypes.c_int32 * 3),
+                ("eps", ctypes.c_float)]
+
+
+class mhla_block(ctypes.Structure):
+    _fields_ = [("extent", ctypes.c_int32 * 3)]
+
+
+class MhlaError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {mhla_status_string(status)}" if what else mhla_status_string(status))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmhla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m token_level_head_block_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        G, Bk = ctypes.POINTER(mhla_grid), ctypes.POINTER(mhla_block)
+        vp = ctypes.c_void_p
+        L.mhla_status_string.argtypes = [ctypes.c_int]
+        L.mhla_status_string.restype = ctypes.c_char_p
+        L.mhla_check_problem.argtypes = [G, Bk, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+        L.mhla_check_problem.restype = ctypes.c_int
+        L.mhla_workspace_bytes.argtypes = [G, Bk]
+        L.mhla_workspace_bytes.restype = ctypes.c_size_t
+        L.mhla_forward.argtypes = [vp, vp, vp, vp, G, Bk, vp, vp]
+        L.mhla_forward.restype = ctypes.c_int
+        L.mhla_forward_ws.argtypes = [vp, vp, vp, vp, G, Bk, vp, vp, ctypes.c_size_t, vp]
+        L.mhla_forward_ws.restype = ctypes.c_int
+        L.mhla_forward_ex.argtypes = [vp, vp, vp, vp, G, Bk, vp, vp, ctypes.c_size_t, ctypes.c_int32,
+                                      vp, vp]
+        L.mhla_forward_ex.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------- structs
+
+def make_grid(batch: int, heads: int, head_dim: int, dtype: int, extents, eps: float = 1e-6) -> mhla_grid:
+    g = mhla_grid()
+    g.batch, g.heads, g.head_dim, g.dtype = batch, heads, head_dim, dtype
+    g.ndim = len(extents)
+    for a in range(3):
+        g.extent[a] = int(extents[a]) if a < len(extents) else 0
+    g.eps = eps
+    return g
+
+
+def make_block(extents) -> mhla_block:
+    b = mhla_block()
+    for a in range(3):
+        b.extent[a] = int(extents[a]) if a < len(extents) else 0
+    return b
+
+
+# ---------------------------------------------------------------- C entry points
+
+def mhla_status_string(status: int) -> str:
+    return lib().mhla_status_string(int(status)).decode()
+
+
+def mhla_check_problem(grid: mhla_grid, block: mhla_block):
+    """(status, M, T)."""
+    m, t = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = lib().mhla_check_problem(ctypes.byref(grid), ctypes.byref(block), ctypes.byref(m), ctypes.byref(t))
+    return st, m.value, t.value
+
+
+def mhla_workspace_bytes(grid: mhla_grid, block: mhla_block) -> int:
+    return int(lib().mhla_workspace_bytes(ctypes.byref(grid), ctypes.byref(block)))
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check_tensors(q, k, v, W, out, grid: mhla_grid, block: mhla_block):
+    """Host-side shape/dtype checks of torch tensors against the grid, so the
+    kernels never index past a buffer whose size the C ABI cannot see."""
+    import torch
+    st, M, _ = mhla_check_problem(grid, block)
+    if st != MHLA_OK:
+        return
+    N = 1
+    for a in range(grid.ndim):
+        N *= grid.extent[a]
+    want = (grid.batch, N, grid.heads, grid.head_dim)
+    tdt = torch.bfloat16 if grid.dtype == MHLA_BF16 else torch.float32
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not isinstance(t, torch.Tensor):
+            continue
+        if tuple(t.shape) != want or t.dtype != tdt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {tdt} tensor of shape {want}, "
+                             f"got {t.dtype} {tuple(t.shape)}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU")
+    if isinstance(W, torch.Tensor):
+        if tuple(W.shape) != (M, M) or W.dtype != torch.float32 or not W.is_contiguous() or not W.is_cuda:
+            raise ValueError(f"W must be a contiguous float32 GPU tensor of shape {(M, M)}")
+
+
+def mhla_forward(q, k, v, W, grid: mhla_grid, block: mhla_block, out, stream=None) -> int:
+    _check_tensors(q, k, v, W, out, grid, block)
+    return lib().mhla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(W), ctypes.byref(grid),
+                              ctypes.byref(block), _ptr(out), _stream(stream))
+
+
+def mhla_forward_ws(q, k, v, W, grid: mhla_grid, block: mhla_block, out, ws, ws_bytes: int,
+                    stream=None) -> int:
+    _check_tensors(q, k, v, W, out, grid, block)
+    return lib().mhla_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(W), ctypes.byref(grid),
+                                 ctypes.byref(block), _ptr(out), _ptr(ws), int(ws_bytes),
+                                 _stream(stream))
+
+
+def mhla_forward_ex(q, k, v, W, grid: mhla_grid, block: mhla_block, out, ws, ws_bytes: int,
+                    path: int = MHLA_PATH_3KERNEL, stage_events=None, stream=None) -> int:
+    """stage_events: None or 4 torch.cuda.Event objects (already recorded once,
+    so that their HIP handles exist)."""
+    _check_tensors(q, k, v, W, out, grid, block)
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 4:
+            raise ValueError("stage_events needs 4 events")
+        arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in stage_events])
+        if any(a is None or a == 0 for a in arr):
+            raise ValueError("stage events have no HIP handle yet; record each once first")
+        ev = ctypes.cast(arr, ctypes.c_void_p)
+    return lib().mhla_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(W), ctypes.byref(grid),
+                                 ctypes.byref(block), _ptr(out), _ptr(ws), int(ws_bytes), int(path),
+                                 ev, _stream(stream))
+
+
+# ---------------------------------------------------------------- convenience
+
+def forward(q, k, v, W, grid_extents, block_extents, eps: float = 1e-6, out=None, ws=None,
+            path: int = MHLA_PATH_3KERNEL, stream=None):
+    """Allocate `out` if needed, call mhla_forward_ex, raise MhlaError on failure."""
+    import torch
+    dt = MHLA_BF16 if q.dtype == torch.bfloat16 else MHLA_F32
+    B, N, H, d = q.shape
+    g = make_grid(B, H, d, dt, grid_extents, eps)
+    b = make_block(block_extents)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = mhla_forward_ex(q, k, v, W, g, b, out, ws, nbytes, path, None, stream)
+    if st != MHLA_OK:
+        raise MhlaError(st, "mhla_forward_ex")
+    return out

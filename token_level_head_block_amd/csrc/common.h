@@ -1,0 +1,104 @@
+// common.h -- shared device helpers and problem geometry for the libmhla kernels.
+//
+// Geometry follows the method's token-dimension partition (MHLA,
+// arXiv 2601.07832; paperlayer.ai summary, section 4 "Architecture"): the
+// token grid (up to 3 axes, slowest first, raster order) is tiled by
+// non-overlapping blocks; blocks are numbered row-major over the block grid
+// and the tokens of a block are visited row-major inside it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mhla {
+
+// ---------------------------------------------------------------- fast division
+// Quotient n / d for 0 <= n < 2^31 and d >= 1 with one multiply-high, using
+// the round-up multiplier of Granlund & Montgomery ("Division by invariant
+// integers using multiplication", PLDI 1994): with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1, n / d = (mulhi(n, m) + n) >> s.
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    f.s = s;
+    f.m = (uint32_t)((((1ull << s) - d) << 32) / d + 1);
+    return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+    return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// ---------------------------------------------------------------- geometry
+struct Geo {
+    int32_t B, H, D, N, M, T;
+    int32_t BH;           // B * H
+    int32_t E1, E2;       // grid extents of the two fastest axes
+    int32_t bk0, bk1, bk2;  // block extents (slowest first)
+    FastDiv div_bk2, div_bk12;   // in-block position -> coordinates
+    FastDiv div_nb2, div_nb12;   // block id -> block coordinates
+    FastDiv div_M, div_H;
+    float eps;
+};
+
+// Raster index of the first token of block j.
+__device__ __forceinline__ int32_t block_origin(const Geo& g, int32_t j) {
+    uint32_t j0 = fdiv((uint32_t)j, g.div_nb12);
+    uint32_t r = (uint32_t)j - j0 * g.div_nb12.d;
+    uint32_t j1 = fdiv(r, g.div_nb2);
+    uint32_t j2 = r - j1 * g.div_nb2.d;
+    return (int32_t)(((j0 * g.bk0) * g.E1 + j1 * g.bk1) * g.E2 + j2 * g.bk2);
+}
+
+// Raster offset of in-block position p (row-major inside the block).
+__device__ __forceinline__ int32_t in_block(const Geo& g, int32_t p) {
+    uint32_t p0 = fdiv((uint32_t)p, g.div_bk12);
+    uint32_t r = (uint32_t)p - p0 * g.div_bk12.d;
+    uint32_t p1 = fdiv(r, g.div_bk2);
+    uint32_t p2 = r - p1 * g.div_bk2.d;
+    return (int32_t)((p0 * g.E1 + p1) * g.E2 + p2);
+}
+
+// ---------------------------------------------------------------- vector types
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16 halves of a packed 32-bit word, widened exactly to fp32.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 values -> packed bf16 pair (a in the low half), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    bf16x2 p = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// Low halves / high halves of two words, packed (first argument -> low half).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+// Feature map phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise.
+__device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ __forceinline__ float phi_exact(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+}  // namespace mhla

@@ -1,0 +1,230 @@
+// mhla_api.cpp -- the C ABI of libmhla: validation, workspace layout and dispatch.
+//
+// The problem statement (token grid split into non-overlapping blocks, one
+// M x M coefficient matrix mixing per-block key-value summaries) follows MHLA,
+// arXiv 2601.07832 (paperlayer.ai summary, section 4 "Architecture" and
+// "Multi-Head Mixing").  Everything here runs on the host; the kernels live
+// in kernels_bf16.hip and kernels_f32.hip.
+#include <mhla.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Shape {
+    int64_t B, H, D, N, M, T;
+    int64_t g[3], b[3], nb[3];   // padded to 3 axes, slowest first
+    int dtype;
+    size_t esz;                  // bytes per element of q/k/v/out and of intermediates
+};
+
+mhla_status check(const mhla_grid* grid, const mhla_block* block, Shape* s) {
+    if (!grid || !block) return MHLA_ERR_INVALID_ARG;
+    if (grid->dtype != MHLA_F32 && grid->dtype != MHLA_BF16) return MHLA_ERR_UNSUPPORTED;
+    if (grid->head_dim != 32 && grid->head_dim != 64 && grid->head_dim != 128) return MHLA_ERR_UNSUPPORTED;
+    if (grid->batch < 0 || grid->heads < 0) return MHLA_ERR_INVALID_ARG;
+    if (grid->ndim != 2 && grid->ndim != 3) return MHLA_ERR_INVALID_ARG;
+    if (!std::isfinite(grid->eps) || grid->eps < 0.f) return MHLA_ERR_INVALID_ARG;
+    const int off = 3 - grid->ndim;
+    for (int a = 0; a < 3; ++a) { s->g[a] = 1; s->b[a] = 1; }
+    for (int a = 0; a < grid->ndim; ++a) {
+        if (grid->extent[a] <= 0 || block->extent[a] <= 0) return MHLA_ERR_INVALID_ARG;
+        if (grid->extent[a] % block->extent[a] != 0) return MHLA_ERR_INVALID_ARG;
+        s->g[off + a] = grid->extent[a];
+        s->b[off + a] = block->extent[a];
+    }
+    s->N = s->g[0] * s->g[1] * s->g[2];
+    s->T = s->b[0] * s->b[1] * s->b[2];
+    for (int a = 0; a < 3; ++a) s->nb[a] = s->g[a] / s->b[a];
+    s->M = s->nb[0] * s->nb[1] * s->nb[2];
+    s->B = grid->batch;
+    s->H = grid->heads;
+    s->D = grid->head_dim;
+    s->dtype = grid->dtype;
+    s->esz = grid->dtype == MHLA_F32 ? 4 : 2;
+    // Kernels index with 32-bit offsets: every tensor (and every workspace
+    // region, in elements) must stay below 2^31.
+    const double lim = 2147483648.0;
+    if ((double)s->B * (double)s->N * (double)s->H * (double)s->D >= lim) return MHLA_ERR_UNSUPPORTED;
+    if ((double)s->B * (double)s->H * (double)s->M * (double)(s->D * s->D + s->D) >= lim)
+        return MHLA_ERR_UNSUPPORTED;
+    return MHLA_OK;
+}
+
+struct Layout {
+    size_t sz, st, zt, total;   // byte offsets of the three regions, total size
+};
+
+Layout layout(const Shape& s) {
+    const size_t recs = (size_t)(s.B * s.H * s.M);
+    Layout L;
+    L.sz = 0;
+    L.st = align_up(recs * (size_t)(s.D * s.D + s.D) * s.esz);
+    L.zt = L.st + align_up(recs * (size_t)(s.D * s.D) * s.esz);
+    L.total = L.zt + align_up(recs * (size_t)s.D * 4);
+    return L;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return std::atoi(v);
+}
+
+mhla::Tuning choose_tuning(const Shape& s) {
+    mhla::Tuning t;
+    // Waves per block: enough token groups per wave to amortise the per-wave
+    // setup, enough waves to keep loads in flight.
+    t.summary_waves = s.T >= 192 ? 2 : (s.T >= 64 ? 2 : 1);
+    t.apply_waves = s.T >= 128 ? 2 : 1;
+    const int sw = env_int("MHLA_SUMMARY_WAVES", 0), aw = env_int("MHLA_APPLY_WAVES", 0);
+    if (sw == 1 || sw == 2 || sw == 4) t.summary_waves = sw;
+    if (aw == 1 || aw == 2 || aw == 4) t.apply_waves = aw;
+    return t;
+}
+
+mhla::Geo make_geo(const Shape& s, float eps) {
+    mhla::Geo g;
+    g.B = (int32_t)s.B; g.H = (int32_t)s.H; g.D = (int32_t)s.D;
+    g.N = (int32_t)s.N; g.M = (int32_t)s.M; g.T = (int32_t)s.T;
+    g.BH = (int32_t)(s.B * s.H);
+    g.E1 = (int32_t)s.g[1]; g.E2 = (int32_t)s.g[2];
+    g.bk0 = (int32_t)s.b[0]; g.bk1 = (int32_t)s.b[1]; g.bk2 = (int32_t)s.b[2];
+    g.div_bk2 = mhla::make_fastdiv((uint32_t)s.b[2]);
+    g.div_bk12 = mhla::make_fastdiv((uint32_t)(s.b[1] * s.b[2]));
+    g.div_nb2 = mhla::make_fastdiv((uint32_t)s.nb[2]);
+    g.div_nb12 = mhla::make_fastdiv((uint32_t)(s.nb[1] * s.nb[2]));
+    g.div_M = mhla::make_fastdiv((uint32_t)s.M);
+    g.div_H = mhla::make_fastdiv((uint32_t)(s.H > 0 ? s.H : 1));
+    g.eps = eps;
+    return g;
+}
+
+mhla_status forward_impl(const void* q, const void* k, const void* v, const float* W,
+                         const mhla_grid* grid, const mhla_block* block, void* out, void* ws,
+                         size_t ws_bytes, bool allow_alloc, int32_t path,
+                         const hipEvent_t* events, hipStream_t stream) {
+    Shape s;
+    mhla_status st = check(grid, block, &s);
+    if (st != MHLA_OK) return st;
+    if (path != MHLA_PATH_3KERNEL && path != MHLA_PATH_FUSED) return MHLA_ERR_INVALID_ARG;
+    if (s.B == 0 || s.H == 0) return MHLA_OK;
+    if (!q || !k || !v || !W || !out) return MHLA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(W) || !aligned16(out))
+        return MHLA_ERR_MISALIGNED;
+    const size_t tbytes = (size_t)(s.B * s.N * s.H * s.D) * s.esz;
+    const size_t wbytes = (size_t)(s.M * s.M) * 4;
+    if (overlaps(out, tbytes, q, tbytes) || overlaps(out, tbytes, k, tbytes) ||
+        overlaps(out, tbytes, v, tbytes) || overlaps(out, tbytes, W, wbytes))
+        return MHLA_ERR_INVALID_ARG;
+    const Layout lay = layout(s);
+    bool owned = false;
+    if (ws) {
+        if (ws_bytes < lay.total) return MHLA_ERR_INVALID_ARG;
+        if (!aligned16(ws)) return MHLA_ERR_MISALIGNED;
+        if (overlaps(ws, lay.total, out, tbytes) || overlaps(ws, lay.total, q, tbytes) ||
+            overlaps(ws, lay.total, k, tbytes) || overlaps(ws, lay.total, v, tbytes) ||
+            overlaps(ws, lay.total, W, wbytes))
+            return MHLA_ERR_INVALID_ARG;
+    } else {
+        if (!allow_alloc || ws_bytes != 0) return MHLA_ERR_INVALID_ARG;
+        if (hipMallocAsync(&ws, lay.total, stream) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return MHLA_ERR_ALLOC;
+        }
+        owned = true;
+    }
+    mhla::Launch L;
+    L.q = q; L.k = k; L.v = v; L.W = W; L.out = out;
+    char* base = static_cast<char*>(ws);
+    L.sz = base + lay.sz;
+    L.st = base + lay.st;
+    L.zt = reinterpret_cast<float*>(base + lay.zt);
+    L.g = make_geo(s, grid->eps);
+    L.tune = choose_tuning(s);
+    L.path = path;
+    L.events = events;
+    L.stream = stream;
+    const hipError_t err = s.dtype == MHLA_BF16 ? mhla::run_bf16(L) : mhla::run_f32(L);
+    if (owned) (void)hipFreeAsync(ws, stream);
+    return err == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mhla_status_string(mhla_status status) {
+    switch (status) {
+        case MHLA_OK: return "MHLA_OK";
+        case MHLA_ERR_INVALID_ARG: return "MHLA_ERR_INVALID_ARG: invalid argument";
+        case MHLA_ERR_UNSUPPORTED: return "MHLA_ERR_UNSUPPORTED: unsupported head_dim, dtype or size";
+        case MHLA_ERR_MISALIGNED: return "MHLA_ERR_MISALIGNED: pointer not 16-byte aligned";
+        case MHLA_ERR_ALLOC: return "MHLA_ERR_ALLOC: workspace allocation failed";
+        case MHLA_ERR_HIP: return "MHLA_ERR_HIP: HIP launch or runtime error";
+    }
+    return "unknown mhla_status";
+}
+
+mhla_status mhla_check_problem(const mhla_grid* grid, const mhla_block* block, int64_t* num_blocks,
+                               int64_t* block_tokens) {
+    Shape s;
+    const mhla_status st = check(grid, block, &s);
+    if (st == MHLA_OK) {
+        if (num_blocks) *num_blocks = s.M;
+        if (block_tokens) *block_tokens = s.T;
+    }
+    return st;
+}
+
+size_t mhla_workspace_bytes(const mhla_grid* grid, const mhla_block* block) {
+    Shape s;
+    if (check(grid, block, &s) != MHLA_OK || s.B == 0 || s.H == 0) return 0;
+    return layout(s).total;
+}
+
+mhla_status mhla_forward(const void* q, const void* k, const void* v, const float* W,
+                         const mhla_grid* grid, const mhla_block* block, void* out,
+                         hipStream_t stream) {
+    return forward_impl(q, k, v, W, grid, block, out, nullptr, 0, true, MHLA_PATH_3KERNEL, nullptr,
+                        stream);
+}
+
+mhla_status mhla_forward_ws(const void* q, const void* k, const void* v, const float* W,
+                            const mhla_grid* grid, const mhla_block* block, void* out, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+    if (!ws) {
+        Shape s;
+        const mhla_status st = check(grid, block, &s);
+        if (st != MHLA_OK) return st;
+        if (s.B != 0 && s.H != 0) return MHLA_ERR_INVALID_ARG;
+    }
+    return forward_impl(q, k, v, W, grid, block, out, ws, ws_bytes, false, MHLA_PATH_3KERNEL,
+                        nullptr, stream);
+}
+
+mhla_status mhla_forward_ex(const void* q, const void* k, const void* v, const float* W,
+                            const mhla_grid* grid, const mhla_block* block, void* out, void* ws,
+                            size_t ws_bytes, int32_t path, const hipEvent_t* stage_events,
+                            hipStream_t stream) {
+    return forward_impl(q, k, v, W, grid, block, out, ws, ws_bytes, true, path, stage_events,
+                        stream);
+}
+
+}  // extern "C"
