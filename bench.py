@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough to exceed 2x the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--out", default="", help="also write the JSON line to this file")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size")
+    ap.add_argument("--heads", type=int, default=0, help="override the workload's head count")
     return ap.parse_args()
 
 
@@ -80,6 +82,8 @@ def main():
     mh.lib()   # fail loudly if the HIP library is missing
 
     p = synth.CONFIGS[args.config]
+    if args.batch or args.heads:
+        p = p.with_(batch=args.batch or p.batch, heads=args.heads or p.heads)
     path = mh.MHLA_PATH_FUSED if args.path == "fused" else mh.MHLA_PATH_3KERNEL
     tensor_bytes = p.batch * p.n_tokens * p.heads * p.head_dim * p.elem_bytes
     per_set = 4 * tensor_bytes

@@ -111,7 +111,10 @@ mhla_status mhla_check_problem(const mhla_grid* grid, const mhla_block* block,
  *             then z_j[c];
  *   region 1 (at a 256-byte boundary): mixed summaries St_i transposed,
  *             P*M records of d*d compute-type elements ([e][c]);
- *   region 2 (at a 256-byte boundary): mixed normalisers zt_i, P*M*d fp32.
+ *   region 2 (at a 256-byte boundary): mixed normalisers zt_i, P*M*d fp32;
+ *   region 3 (at a 256-byte boundary, bf16 problems only): W rounded to
+ *             bf16, roundup(M, 64) rows of roundup(M, 32) elements, zero
+ *             padded.
  * After a 3-kernel call completes, the regions hold these intermediates;
  * the fused path fills region 0 only. */
 size_t mhla_workspace_bytes(const mhla_grid* grid, const mhla_block* block);

@@ -48,7 +48,8 @@ def test_workspace_bytes_layout(L):
     assert (st, M, T) == (mh.MHLA_OK, 256, 256)
     recs = 6 * 256
     up = lambda x: (x + 255) // 256 * 256
-    assert mh.mhla_workspace_bytes(g, b) == up(recs * (64 * 64 + 64) * 2) + up(recs * 64 * 64 * 2) + up(recs * 64 * 4)
+    assert mh.mhla_workspace_bytes(g, b) == up(recs * (64 * 64 + 64) * 2) + up(recs * 64 * 64 * 2) + \
+        up(recs * 64 * 4) + up(256 * 256 * 2)
     g32 = mh.make_grid(1, 1, 32, mh.MHLA_F32, (16, 16), 1e-6)
     assert mh.mhla_workspace_bytes(g32, mh.make_block((4, 4))) == \
         up(16 * (32 * 32 + 32) * 4) + up(16 * 32 * 32 * 4) + up(16 * 32 * 4)

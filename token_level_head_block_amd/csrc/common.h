@@ -44,8 +44,26 @@ struct Geo {
     FastDiv div_bk2, div_bk12;   // in-block position -> coordinates
     FastDiv div_nb2, div_nb12;   // block id -> block coordinates
     FastDiv div_M, div_H;
+    // Head grouping of the bf16 kernels: a workgroup covers G consecutive heads
+    // of one (b, block), so its waves read whole runs of each token's channels.
+    int32_t G, HG;        // heads per workgroup, head groups per (b, block)
+    FastDiv div_HG;
     float eps;
 };
+
+// Workgroup index -> (b, block, head group) for head-grouped launches:
+// blockIdx = (b * M + j) * HG + hg.
+struct WgCoord {
+    int b, j, hg;
+};
+__device__ __forceinline__ WgCoord wg_coord(const Geo& g, uint32_t wg) {
+    WgCoord c;
+    const uint32_t bj = fdiv(wg, g.div_HG);
+    c.hg = (int)(wg - bj * g.div_HG.d);
+    c.b = (int)fdiv(bj, g.div_M);
+    c.j = (int)(bj - (uint32_t)c.b * g.div_M.d);
+    return c;
+}
 
 // Raster index of the first token of block j.
 __device__ __forceinline__ int32_t block_origin(const Geo& g, int32_t j) {

@@ -25,145 +25,196 @@
 namespace mhla {
 namespace {
 
+// Loads of data read exactly once (q, k, v) may carry the non-temporal hint
+// so they do not displace the summaries in the caches.
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+// =====================================================================
+// Software pipeline: iterations first, first + step, ... < n (n >= 1), with
+// the loads of PF later iterations in flight while one is computed.  Buffers
+// rotate with compile-time indices so they stay in registers.  Every load is
+// issued unconditionally (indices past the end are clamped to the last
+// iteration and the data ignored): a load under a branch would make the
+// compiler's wait counts conservative and drain the prefetched loads too.
+// =====================================================================
+template <int PF, typename Buf, typename LoadF, typename ComputeF>
+__device__ __forceinline__ void pipelined(int first, int step, int n, LoadF&& load, ComputeF&& compute) {
+    Buf buf[PF + 1];
+    const int last = n - 1;
+#pragma unroll
+    for (int s = 0; s < PF; ++s) load(min(first + s * step, last), buf[s]);
+    for (int base = first; base < n; base += step * (PF + 1)) {
+#pragma unroll
+        for (int u = 0; u <= PF; ++u) {
+            const int it = base + u * step;
+            if (it >= n) break;
+            load(min(it + PF * step, last), buf[(u + PF) % (PF + 1)]);
+            __builtin_amdgcn_sched_barrier(0);   // issue the prefetch before computing
+            compute(buf[u]);
+        }
+    }
+}
+
+// W (fp32 [M][M]) -> bf16 [Ipad][Jpad], zero padded, for the mixing kernel's
+// B operand.  Done by extra workgroups appended to the summary launch, so the
+// summary workgroups themselves never wait on it.
+struct WConv {
+    int32_t M, Jpad, nchunks;   // nchunks = Ipad * Jpad / 8 (8 elements each); 0 = none
+    int32_t first_wg;           // workgroups [first_wg, gridDim.x) convert
+};
+
+__device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t* __restrict__ Wb,
+                                          const WConv& wc) {
+    const int cpr = wc.Jpad >> 3;   // chunks per row
+    const int nthr = (gridDim.x - wc.first_wg) * blockDim.x;
+    for (int c = (blockIdx.x - wc.first_wg) * blockDim.x + threadIdx.x; c < wc.nchunks; c += nthr) {
+        const int i = c / cpr, j0 = (c - i * cpr) * 8;
+        float x[8];
+        if (i < wc.M && (wc.M & 7) == 0 && j0 < wc.M) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(W + (size_t)i * wc.M + j0);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(W + (size_t)i * wc.M + j0 + 4);
+            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        } else {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)i * wc.M + j0 + s] : 0.f;
+        }
+        *reinterpret_cast<u32x4*>(Wb + (size_t)i * wc.Jpad + j0) =
+            u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+    }
+}
+
 // =====================================================================
 // block_kv_summary
-// Workgroup = one (b, h, j) block, NQ x NWT waves.  A wave owns a 64x64
-// (d = 128: one quadrant of S) or 32x32 (d = 32) tile of S and a 1/NWT share
-// of the block's tokens; shares are summed through LDS in fixed order.
+// Workgroup = one block j of one batch b for G consecutive heads; one wave per
+// head (d = 128: four waves per head, one quadrant of S each), so together
+// the waves read contiguous runs of every token's channels.  A wave owns a
+// 64x64 (d = 32: 32x32) tile of S over all of the block's tokens.
 // Lane (li, gq): K channels CPL*li .. +CPL-1 for rows, V channels likewise
 // for columns, tokens 32*ks + 8*gq + s (s = 0..7) as k-slots.
+// z_j = phi(K_j)^T 1 runs on the matrix cores too (one extra MFMA per row
+// tile against an all-ones operand), which keeps the vector ALUs for phi.
+// ROW8: block rows hold a multiple of 8 tokens, so the 8 tokens of a lane
+// group are consecutive in raster order (one address computation).
+// FULL: ROW8 and T a multiple of 32, so no token slot is ever padding.
 // =====================================================================
-template <int D, int NWT>
-__global__ __launch_bounds__(64 * NWT * (D == 128 ? 4 : 1)) void block_kv_summary_bf16(
-    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, uint16_t* __restrict__ SZ,
-    const Geo g) {
-    constexpr int NQ = (D == 128) ? 4 : 1;
+template <int D, int PF, bool ROW8, bool FULL, bool NTL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                           uint16_t* __restrict__ SZ, const Geo g, const float* __restrict__ W,
+                           uint16_t* __restrict__ Wb, const WConv wc) {
+    static_assert(!FULL || ROW8, "FULL implies ROW8");
     constexpr int CPL = (D == 32) ? 2 : 4;   // channels per lane
     constexpr int CW = CPL / 2;              // 32-bit words per lane per token
+    constexpr int NQ = (D == 128) ? 4 : 1;
+    if ((int)blockIdx.x >= wc.first_wg) {
+        convert_w(W, Wb, wc);
+        return;
+    }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int quad = wave % NQ, tw = wave / NQ;
+    const int quad = wave % NQ;
     const int li = lane & 15, gq = lane >> 4;
-    const int blk = blockIdx.x;
-    const int bh = (int)fdiv(blk, g.div_M);
-    const int j = blk - bh * g.M;
-    const int b = (int)fdiv(bh, g.div_H), h = bh - b * g.H;
+    const WgCoord wgc = wg_coord(g, blockIdx.x);
+    const int b = wgc.b, j = wgc.j, h = wgc.hg * g.G + wave / NQ;
+    if (h >= g.H) return;
+    const int blk = (b * g.H + h) * g.M + j;   // record index (b, h, j)
     const int rowbase = (D == 128) ? (quad >> 1) * 64 : 0;
     const int colbase = (D == 128) ? (quad & 1) * 64 : 0;
+    const bool do_z = (quad & 1) == 0;        // one wave per row range forms z
     const int row = g.H * D;
     const int origin = block_origin(g, j);
     const uint16_t* kb = K + (b * g.N * row + h * D + rowbase + CPL * li);
     const uint16_t* vb = V + (b * g.N * row + h * D + colbase + CPL * li);
+    const u32x4 ones = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
 
-    f32x4 acc[CPL][CPL];
+    f32x4 acc[CPL][CPL], accz[CPL];
 #pragma unroll
-    for (int r = 0; r < CPL; ++r)
+    for (int r = 0; r < CPL; ++r) {
+        accz[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float zacc[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) zacc[c] = 0.f;
+    }
 
     struct Raw {
         uint32_t k[8][CW], v[8][CW];
         uint32_t valid;
     };
     auto load = [&](int ks, Raw& R) {
-        R.valid = 0;
+        int offs[8];
+        if constexpr (ROW8) {
+            const int p0 = ks * 32 + gq * 8;
+            const bool ok = FULL || p0 < g.T;
+            const int off0 = (origin + in_block(g, ok ? p0 : 0)) * row;
+            R.valid = ok ? 0xffu : 0u;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) offs[s] = off0 + s * row;
+        } else {
+            R.valid = 0;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int p = ks * 32 + gq * 8 + s;
+                const bool ok = p < g.T;
+                offs[s] = (origin + in_block(g, ok ? p : g.T - 1)) * row;
+                R.valid |= (ok ? 1u : 0u) << s;
+            }
+        }
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const int p = ks * 32 + gq * 8 + s;
-            const bool ok = p < g.T;
-            const int off = (origin + in_block(g, ok ? p : g.T - 1)) * row;
-            R.valid |= (ok ? 1u : 0u) << s;
             if constexpr (CW == 2) {
-                const u32x2 a = *reinterpret_cast<const u32x2*>(kb + off);
-                const u32x2 c = *reinterpret_cast<const u32x2*>(vb + off);
+                const u32x2 a = ld<NTL>(reinterpret_cast<const u32x2*>(kb + offs[s]));
+                const u32x2 c = ld<NTL>(reinterpret_cast<const u32x2*>(vb + offs[s]));
                 R.k[s][0] = a.x; R.k[s][1] = a.y;
                 R.v[s][0] = c.x; R.v[s][1] = c.y;
             } else {
-                R.k[s][0] = *reinterpret_cast<const uint32_t*>(kb + off);
-                R.v[s][0] = *reinterpret_cast<const uint32_t*>(vb + off);
+                R.k[s][0] = ld<NTL>(reinterpret_cast<const uint32_t*>(kb + offs[s]));
+                R.v[s][0] = ld<NTL>(reinterpret_cast<const uint32_t*>(vb + offs[s]));
             }
         }
     };
     auto compute = [&](const Raw& R) {
-        u32x4 aw[CPL], bw[CPL];
+        // V operands first (pure repacking), then one K row tile at a time:
+        // phi, rounding to bf16 and that tile's MFMAs.  Padding token slots
+        // (read from a real token) are zeroed in the K operand only, which
+        // removes them from both S and z.
+        u32x4 bw[CPL];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const bool ok0 = (R.valid >> (2 * w)) & 1u, ok1 = (R.valid >> (2 * w + 1)) & 1u;
+        for (int w = 0; w < 4; ++w)
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
-                const uint32_t k0 = R.k[2 * w][c >> 1], k1 = R.k[2 * w + 1][c >> 1];
-                const float x0 = (c & 1) ? bf_hi(k0) : bf_lo(k0);
-                const float x1 = (c & 1) ? bf_hi(k1) : bf_lo(k1);
-                const uint32_t pk = pack_bf16(ok0 ? phi_fast(x0) : 0.f, ok1 ? phi_fast(x1) : 0.f);
-                aw[c][w] = pk;
-                zacc[c] += bf_lo(pk) + bf_hi(pk);
-                const uint32_t v0 = ok0 ? R.v[2 * w][c >> 1] : 0u;
-                const uint32_t v1 = ok1 ? R.v[2 * w + 1][c >> 1] : 0u;
+                const uint32_t v0 = R.v[2 * w][c >> 1], v1 = R.v[2 * w + 1][c >> 1];
                 bw[c][w] = (c & 1) ? pack_hi(v0, v1) : pack_lo(v0, v1);
             }
+#pragma unroll
+        for (int r = 0; r < CPL; ++r) {
+            u32x4 aw;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t k0 = R.k[2 * w][r >> 1], k1 = R.k[2 * w + 1][r >> 1];
+                const float x0 = (r & 1) ? bf_hi(k0) : bf_lo(k0);
+                const float x1 = (r & 1) ? bf_hi(k1) : bf_lo(k1);
+                if constexpr (FULL) {
+                    aw[w] = pack_bf16(phi_fast(x0), phi_fast(x1));
+                } else if constexpr (ROW8) {
+                    aw[w] = R.valid ? pack_bf16(phi_fast(x0), phi_fast(x1)) : 0u;
+                } else {
+                    const bool ok0 = (R.valid >> (2 * w)) & 1u, ok1 = (R.valid >> (2 * w + 1)) & 1u;
+                    aw[w] = pack_bf16(ok0 ? phi_fast(x0) : 0.f, ok1 ? phi_fast(x1) : 0.f);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[r][c] = mfma_bf16(aw, bw[c], acc[r][c]);
+            if (do_z) accz[r] = mfma_bf16(aw, ones, accz[r]);
         }
-#pragma unroll
-        for (int r = 0; r < CPL; ++r)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[r][c] = mfma_bf16(aw[r], bw[c], acc[r][c]);
     };
-
-    const int nks = (g.T + 31) >> 5;
-    Raw ra, rb;
-    int ks = tw;
-    if (ks < nks) load(ks, ra);
-    while (ks < nks) {
-        int kn = ks + NWT;
-        if (kn < nks) load(kn, rb);
-        compute(ra);
-        ks = kn;
-        if (ks >= nks) break;
-        kn = ks + NWT;
-        if (kn < nks) load(kn, ra);
-        compute(rb);
-        ks = kn;
-    }
-
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        zacc[c] += shfl_xor(zacc[c], 16);
-        zacc[c] += shfl_xor(zacc[c], 32);
-    }
-
-    if constexpr (NWT > 1) {
-        constexpr int NV = CPL * CPL * 4 + CPL;
-        __shared__ float red[(NWT - 1) * NQ][NV][64];
-        if (tw > 0) {
-            float(*dst)[64] = red[(tw - 1) * NQ + quad];
-#pragma unroll
-            for (int r = 0; r < CPL; ++r)
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) dst[(r * CPL + c) * 4 + v][lane] = acc[r][c][v];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) dst[CPL * CPL * 4 + c][lane] = zacc[c];
-        }
-        __syncthreads();
-        if (tw > 0) return;
-#pragma unroll
-        for (int t = 0; t < NWT - 1; ++t) {
-            float(*src)[64] = red[t * NQ + quad];
-#pragma unroll
-            for (int r = 0; r < CPL; ++r)
-#pragma unroll
-                for (int c = 0; c < CPL; ++c)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[r][c][v] += src[(r * CPL + c) * 4 + v][lane];
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) zacc[c] += src[CPL * CPL * 4 + c][lane];
-        }
-    }
+    pipelined<PF, Raw>(0, 1, (g.T + 31) >> 5, load, compute);
 
     // Record layout: S_j transposed ([e][c], c fastest), then z_j.
-    // Lane holds S[c][e] for c = rowbase + 4*CPL*gq + CPL*v + r, e = colbase + CPL*li + c2.
+    // Lane holds S[c][e] for c = rowbase + 4*CPL*gq + CPL*v + r, e = colbase + CPL*li + c2,
+    // and z[c] (every column of accz is the same) for the same c.
     uint16_t* rec = SZ + (size_t)blk * (D * D + D);
 #pragma unroll
     for (int c2 = 0; c2 < CPL; ++c2) {
@@ -178,119 +229,179 @@ __global__ __launch_bounds__(64 * NWT * (D == 128 ? 4 : 1)) void block_kv_summar
         *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
         if constexpr (CPL == 4) *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
     }
-    if (gq == 0 && (quad & 1) == 0) {
-        uint16_t* dst = rec + D * D + rowbase + CPL * li;
-        if constexpr (CPL == 4)
-            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(zacc[0], zacc[1]), pack_bf16(zacc[2], zacc[3])};
-        else
-            *reinterpret_cast<uint32_t*>(dst) = pack_bf16(zacc[0], zacc[1]);
+    if (do_z && li == 0) {
+        uint32_t wv[2 * CPL];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int rp = 0; rp < CPL / 2; ++rp)
+                wv[v * (CPL / 2) + rp] = pack_bf16(accz[2 * rp][v], accz[2 * rp + 1][v]);
+        uint16_t* dst = rec + D * D + rowbase + 4 * CPL * gq;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        if constexpr (CPL == 4) *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
     }
 }
 
 // =====================================================================
 // mix_summaries:  C[col'][i] = sum_j [S|z]_j[col'] W[i][j]  per (b, h).
-// A wave computes 64 columns col' of the (d*d + d)-long records for 64
-// query blocks i; k runs over source blocks j.  Lane (li, gq): record
-// elements 4*li .. +3 of 8 source blocks (rows), W row it*64 + 16*t + li
-// (columns).  Mixed S goes out as bf16, mixed z as fp32.
+// Workgroup of 8 waves = CPW column tiles (64 record elements col' each) x
+// all query blocks i.  The A operand (records of the CPW tiles, up to 256
+// source blocks per pass) is staged once in LDS, already packed as MFMA
+// operands; wave (c, it, th) computes 64 col' x 32 i (i = it*64 + 32*th + ..)
+// with all of its W operands (bf16, padded, converted by the summary kernel)
+// loaded from L2 before the staging, so their latency is paid once.
+// Lane (li, gq): A rows col' = 4*li + r, B column i = 16*t + li.
+// Mixed S tiles leave through LDS so that every store writes whole 128-byte
+// record rows; mixed z (fp32) is stored directly.
 // =====================================================================
+struct MixGeo {
+    int32_t CT, IT, CPW, CTG, Jpad;   // column tiles, i tiles, column tiles per WG, WG per bh, padded j
+    FastDiv div_CTG;
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void mix_summaries_bf16(const uint16_t* __restrict__ SZ,
-                                                          const float* __restrict__ W,
-                                                          uint16_t* __restrict__ St,
-                                                          float* __restrict__ Zt, const Geo g,
-                                                          const FastDiv div_IT, const FastDiv div_CT) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void mix_summaries_bf16(
+    const uint16_t* __restrict__ SZ, const uint16_t* __restrict__ Wb, uint16_t* __restrict__ St,
+    float* __restrict__ Zt, const Geo g, const MixGeo mg) {
     constexpr int REC = D * D + D;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    constexpr int KSP = 8;          // k-steps (32 source blocks) per staging pass
+    constexpr int OROW = 72;        // output staging row: 64 bf16 + 8 padding
+    // A operands [tile c][r][kk][lane] (cpw * nkp <= 8: 32 KB), reused for the
+    // output transpose (8 waves x 32 rows x OROW bf16 = 36 KB).
+    __shared__ u32x4 sA[8 * 32 * OROW / 8];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, gq = lane >> 4;
-    const uint32_t tile = blockIdx.x * 4u + wave;
-    const uint32_t rest = fdiv(tile, div_IT);
-    const int it = (int)(tile - rest * div_IT.d);
-    const uint32_t bh = fdiv(rest, div_CT);
-    const int ct = (int)(rest - bh * div_CT.d);
-    if ((int)bh >= g.BH) return;
+    const uint32_t wg = blockIdx.x;
+    const uint32_t bh = fdiv(wg, mg.div_CTG);
+    const int ctg = (int)(wg - bh * mg.div_CTG.d);
     const int M = g.M;
-    const int colp = ct * 64 + 4 * li;
-    const bool colok = colp < REC;
-    const uint16_t* abase = SZ + (size_t)bh * M * REC + colp;
-    const bool wvec = (M & 7) == 0;
+    const int NK = (M + 31) >> 5;
+    const int cpw = mg.CPW;
+    const int itr = mg.IT < 4 ? mg.IT : 4;   // i tiles per round
+    const uint16_t* base = SZ + (size_t)bh * M * REC;
+    const int th = wave & 1, w2 = wave >> 1;
+    const int wc = w2 / itr, wit = w2 % itr;
+    const int ct = ctg * cpw + wc;
+    const bool wave_ok = (w2 < cpw * itr) && (ct < mg.CT);
+    const int cp0 = ct * 64;   // first record element of this wave's column tile
 
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = (M + 31) >> 5;
-    for (int kk = 0; kk < nk; ++kk) {
-        u32x2 raw[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int jj = kk * 32 + gq * 8 + s;
-            raw[s] = (colok && jj < M) ? *reinterpret_cast<const u32x2*>(abase + (size_t)jj * REC)
-                                       : u32x2{0u, 0u};
-        }
-        u32x4 aw[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            aw[0][w] = pack_lo(raw[2 * w].x, raw[2 * w + 1].x);
-            aw[1][w] = pack_hi(raw[2 * w].x, raw[2 * w + 1].x);
-            aw[2][w] = pack_lo(raw[2 * w].y, raw[2 * w + 1].y);
-            aw[3][w] = pack_hi(raw[2 * w].y, raw[2 * w + 1].y);
-        }
-        const int j0 = kk * 32 + gq * 8;
-        u32x4 bw[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            int i = it * 64 + 16 * t + li;
-            i = i < M ? i : M - 1;
-            const float* wr = W + (size_t)i * M;
-            float wv[8];
-            if (wvec) {
-                f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f}, y = x;
-                if (j0 < M) {
-                    x = *reinterpret_cast<const f32x4*>(wr + j0);
-                    y = *reinterpret_cast<const f32x4*>(wr + j0 + 4);
-                }
-                wv[0] = x.x; wv[1] = x.y; wv[2] = x.z; wv[3] = x.w;
-                wv[4] = y.x; wv[5] = y.y; wv[6] = y.z; wv[7] = y.w;
-            } else {
-#pragma unroll
-                for (int s = 0; s < 8; ++s) wv[s] = (j0 + s < M) ? wr[j0 + s] : 0.f;
-            }
-#pragma unroll
-            for (int w = 0; w < 4; ++w) bw[t][w] = pack_bf16(wv[2 * w], wv[2 * w + 1]);
-        }
+    for (int iround = 0; iround * 4 < mg.IT; ++iround) {
+        const int it = iround * 4 + wit;
+        const bool active = wave_ok && it < mg.IT;
+        const int itc = it < mg.IT ? it : mg.IT - 1;   // inactive waves load a valid tile too
+        f32x4 acc[4][2];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[r][t] = mfma_bf16(aw[r], bw[t], acc[r][t]);
-    }
+            for (int t = 0; t < 2; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Lane holds C[col' = ct*64 + 16*gq + 4*v + r][i = it*64 + 16*t + li].
-    const int cp0 = ct * 64 + 16 * gq;
-    if (cp0 >= REC) return;
+        for (int k0 = 0; k0 < NK; k0 += KSP) {
+            const int nkp = min(KSP, NK - k0);
+            // W operands (B) of this pass: the first half before the staging of A,
+            // the second half after it; steps past nkp reload step nkp - 1.
+            u32x4 bw[KSP][2];
+            auto load_w = [&](int kk) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int i = it * 64 + 16 * t + li;
-        if (i >= M) continue;
-        const size_t rec = (size_t)bh * M + i;
-        if (cp0 < D * D) {
-            uint32_t wv[8];
+                for (int t = 0; t < 2; ++t)
+                    bw[kk][t] = *reinterpret_cast<const u32x4*>(
+                        Wb + (size_t)(itc * 64 + 32 * th + 16 * t + li) * mg.Jpad +
+                        (k0 + (kk < nkp ? kk : nkp - 1)) * 32 + gq * 8);
+            };
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                wv[2 * v] = pack_bf16(acc[0][t][v], acc[1][t][v]);
-                wv[2 * v + 1] = pack_bf16(acc[2][t][v], acc[3][t][v]);
+            for (int kk = 0; kk < KSP / 2; ++kk) load_w(kk);
+            __syncthreads();
+            // ---- stage A: unit (tile c, li', j-group of 8) -> 4 packed operands.
+            // cpw * nkp <= 8, so there are at most 512 units: one per thread.
+            {
+                const int units = cpw * 16 * 4 * nkp;
+                const int u = tid;
+                const int lip = u & 15;
+                const int jg = (u >> 4) % (4 * nkp);
+                const int c = (u >> 4) / (4 * nkp);
+                const int colp = (ctg * cpw + c) * 64 + 4 * lip;
+                const bool ok = u < units && colp < REC && (ctg * cpw + c) < mg.CT;
+                const int colc = ok ? colp : 0;
+                u32x2 raw[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    // Clamped address, then a mask: the load stays unconditional.
+                    const int jj = (k0 + (jg >> 2)) * 32 + (jg & 3) * 8 + s;
+                    const u32x2 t = *reinterpret_cast<const u32x2*>(base + (size_t)(jj < M ? jj : M - 1) * REC + colc);
+                    const uint32_t m = (ok && jj < M) ? 0xffffffffu : 0u;
+                    raw[s] = u32x2{t.x & m, t.y & m};
+                }
+                if (u < units) {
+                    const int kk = jg >> 2, lanep = (jg & 3) * 16 + lip;
+                    u32x4 op[4];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        op[0][w] = pack_lo(raw[2 * w].x, raw[2 * w + 1].x);
+                        op[1][w] = pack_hi(raw[2 * w].x, raw[2 * w + 1].x);
+                        op[2][w] = pack_lo(raw[2 * w].y, raw[2 * w + 1].y);
+                        op[3][w] = pack_hi(raw[2 * w].y, raw[2 * w + 1].y);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sA[((c * 4 + r) * nkp + kk) * 64 + lanep] = op[r];
+                }
             }
-            uint16_t* dst = St + rec * (D * D) + cp0;
-            *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
-        } else {
-            float* dst = Zt + rec * D + (cp0 - D * D);
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                *reinterpret_cast<f32x4*>(dst + 4 * v) = f32x4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
+            for (int kk = KSP / 2; kk < KSP; ++kk) load_w(kk);
+            __syncthreads();
+            if (active) {
+#pragma unroll
+                for (int kk = 0; kk < KSP; ++kk) {
+                    if (kk >= nkp) break;
+                    u32x4 a[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a[r] = sA[((wc * 4 + r) * nkp + kk) * 64 + lane];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) acc[r][t] = mfma_bf16(a[r], bw[kk][t], acc[r][t]);
+                }
+            }
         }
+
+        // ---- output.  Lane holds C[col' = cp0 + 16*gq + 4*v + r][i = it*64 + 32*th + 16*t + li].
+        const bool s_tile = active && cp0 < D * D;
+        uint16_t* stage = reinterpret_cast<uint16_t*>(sA) + wave * (32 * OROW);
+        __syncthreads();   // every wave is done with the A operands
+        if (s_tile) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                uint32_t wv[8];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    wv[2 * v] = pack_bf16(acc[0][t][v], acc[1][t][v]);
+                    wv[2 * v + 1] = pack_bf16(acc[2][t][v], acc[3][t][v]);
+                }
+                uint16_t* dst = stage + (16 * t + li) * OROW + 16 * gq;
+                *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+                *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+            }
+        }
+        __syncthreads();
+        if (s_tile) {
+            // 32 rows of 128 bytes: 8 lanes per row, 8 rows per instruction.
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int rl = 8 * k + (lane >> 3), chunk = lane & 7;
+                const int i = it * 64 + 32 * th + rl;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rl * OROW + chunk * 8);
+                if (i < M) *reinterpret_cast<u32x4*>(St + ((size_t)bh * M + i) * (D * D) + cp0 + chunk * 8) = x;
+            }
+        } else if (active && cp0 + 16 * gq < REC) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int i = it * 64 + 32 * th + 16 * t + li;
+                if (i >= M) continue;
+                float* dst = Zt + ((size_t)bh * M + i) * D + (cp0 + 16 * gq - D * D);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    *reinterpret_cast<f32x4*>(dst + 4 * v) = f32x4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
+            }
+        }
+        __syncthreads();   // the staging area is reused by the next round
     }
 }
 
@@ -299,27 +410,47 @@ __global__ __launch_bounds__(256) void mix_summaries_bf16(const uint16_t* __rest
 // A = St_i^T (rows e, k = c) stays in registers for the whole block; row ii of
 // row-tile r is e = 4*RT*(ii/4) + 4r + ii%4, so each lane ends with 4*RT
 // consecutive output channels of one token.  B = phi(q) of 16 tokens, loaded
-// straight from Q (8 consecutive channels per lane).  The denominator is a
-// per-lane partial dot product reduced over the 4 lane groups.
+// straight from Q (8 consecutive channels per lane).  The denominator also
+// runs on the matrix cores: two extra row tiles whose every row is zt_i
+// (split into a bf16 high part and the bf16 rounding of the remainder), so
+// every lane receives its token's phi(q) . zt_i without cross-lane sums.
 // =====================================================================
 template <int D>
 struct ApplyA {
     static constexpr int RT = D / 16, KS = D / 32;
     u32x4 a[RT][KS];
-    float zt[KS][8];
+    u32x4 zhi[KS], zlo[KS];
 };
 
-template <int D, int NWA>
+// zt (8 fp32 values of one k-slot group) -> hi/lo bf16 operand words.
+__device__ __forceinline__ void split_zt(const float* z, u32x4& hi, u32x4& lo) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t h = pack_bf16(z[2 * w], z[2 * w + 1]);
+        hi[w] = h;
+        lo[w] = pack_bf16(z[2 * w] - bf_lo(h), z[2 * w + 1] - bf_hi(h));
+    }
+}
+
+template <int D, int NWA, int PF, bool NTL, bool NTO>
 __device__ __forceinline__ void apply_tokens_bf16(const ApplyA<D>& A, const uint16_t* __restrict__ Q,
                                                   uint16_t* __restrict__ O, const Geo& g, int bh,
                                                   int i, int wave, int lane) {
     constexpr int RT = D / 16, KS = D / 32;
     const int t = lane & 15, gq = lane >> 4;
+    // bh and i are wave-uniform; say so, so that addresses and the buffer
+    // descriptor below live in scalar registers.
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    i = __builtin_amdgcn_readfirstlane(i);
     const int b = (int)fdiv(bh, g.div_H), h = bh - b * g.H;
     const int row = g.H * D;
     const int origin = block_origin(g, i);
     const uint16_t* qb = Q + (b * g.N * row + h * D + gq * 8);
-    uint16_t* ob = O + (b * g.N * row + h * D + 4 * RT * gq);
+    // Output of batch b as a raw buffer (at most 2^31 bytes: checked on the host);
+    // the descriptor is wave-uniform, per-lane parts go in the offset.
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        O + (size_t)b * g.N * row, 0, g.N * row * 2, 0x00020000);
+    const int olane = (h * D + 4 * RT * gq) * 2;
     const int nit = (g.T + 15) >> 4;
 
     struct Raw {
@@ -329,73 +460,78 @@ __device__ __forceinline__ void apply_tokens_bf16(const ApplyA<D>& A, const uint
     };
     auto load = [&](int it, Raw& R) {
         const int p = it * 16 + t;
-        R.ok = p < g.T;
+        R.ok = p < g.T;   // false for padding lanes and for groups past the end
         R.off = (origin + in_block(g, R.ok ? p : g.T - 1)) * row;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) R.q[kk] = *reinterpret_cast<const u32x4*>(qb + R.off + kk * 32);
+        for (int kk = 0; kk < KS; ++kk) R.q[kk] = ld<NTL>(reinterpret_cast<const u32x4*>(qb + R.off + kk * 32));
     };
     auto compute = [&](const Raw& R) {
         u32x4 bq[KS];
-        float den = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t pk = pack_bf16(phi_fast(bf_lo(R.q[kk][w])), phi_fast(bf_hi(R.q[kk][w])));
-                bq[kk][w] = pk;
-                den += bf_lo(pk) * A.zt[kk][2 * w] + bf_hi(pk) * A.zt[kk][2 * w + 1];
-            }
-        f32x4 acc[RT];
+            for (int w = 0; w < 4; ++w)
+                bq[kk][w] = pack_bf16(phi_fast(bf_lo(R.q[kk][w])), phi_fast(bf_hi(R.q[kk][w])));
+        f32x4 acc[RT], accd = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
+        for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
             for (int r = 0; r < RT; ++r) acc[r] = mfma_bf16(A.a[r][kk], bq[kk], acc[r]);
-        den += shfl_xor(den, 16);
-        den += shfl_xor(den, 32);
-        const float inv = 1.f / (den + g.eps);
-        if (R.ok) {
-            uint32_t wv[2 * RT];
-#pragma unroll
-            for (int r = 0; r < RT; ++r) {
-                wv[2 * r] = pack_bf16(acc[r][0] * inv, acc[r][1] * inv);
-                wv[2 * r + 1] = pack_bf16(acc[r][2] * inv, acc[r][3] * inv);
-            }
-#pragma unroll
-            for (int u = 0; u < RT / 2; ++u)
-                *reinterpret_cast<u32x4*>(ob + R.off + 8 * u) =
-                    u32x4{wv[4 * u], wv[4 * u + 1], wv[4 * u + 2], wv[4 * u + 3]};
+            accd = mfma_bf16(A.zhi[kk], bq[kk], accd);
+            accd = mfma_bf16(A.zlo[kk], bq[kk], accd);
         }
+        const float inv = 1.f / (accd[0] + g.eps);
+        uint32_t wv[2 * RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            wv[2 * r] = pack_bf16(acc[r][0] * inv, acc[r][1] * inv);
+            wv[2 * r + 1] = pack_bf16(acc[r][2] * inv, acc[r][3] * inv);
+        }
+        // Buffer stores: a lane past the block's last token gets an offset
+        // beyond the buffer's range and the hardware drops its write, so the
+        // store needs no branch.
+        const uint32_t boff = R.ok ? (uint32_t)(R.off * 2 + olane) : 0x80000000u;
+#pragma unroll
+        for (int u = 0; u < RT / 2; ++u)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{wv[4 * u], wv[4 * u + 1], wv[4 * u + 2], wv[4 * u + 3]},
+                                                   orsrc, boff + 16 * u, 0, NTO ? 2 : 0);   // 2: nt
     };
 
-    Raw ra, rb;
-    int it = wave;
-    if (it < nit) load(it, ra);
-    while (it < nit) {
-        int in = it + NWA;
-        if (in < nit) load(in, rb);
-        compute(ra);
-        it = in;
-        if (it >= nit) break;
-        in = it + NWA;
-        if (in < nit) load(in, ra);
-        compute(rb);
-        it = in;
+    // Batches of PF token groups: all loads of a batch are issued together
+    // (clamped past the end), then the groups are computed and stored.  No
+    // buffer is carried across iterations, so every wait is exact.
+    // Groups past the end load the block's last token and store nothing
+    // (their lanes are all "not ok"), so the body has no branch the compiler
+    // could sink the loads into.
+    for (int it0 = wave; it0 < nit; it0 += NWA * PF) {
+        Raw r[PF];
+#pragma unroll
+        for (int u = 0; u < PF; ++u) load(it0 + u * NWA, r[u]);
+        // Keep the scheduler from sinking the batch's loads next to their uses.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < PF; ++u) compute(r[u]);
     }
 }
 
-template <int D, int NWA>
-__global__ __launch_bounds__(64 * NWA) void query_apply_bf16(const uint16_t* __restrict__ Q,
-                                                             const uint16_t* __restrict__ St,
-                                                             const float* __restrict__ Zt,
-                                                             uint16_t* __restrict__ O, const Geo g) {
+// Workgroup = query block i of batch b for G consecutive heads x NWA waves
+// splitting the block's tokens.
+template <int D, int NWA, int PF, bool NTL, bool NTO>
+__global__ __launch_bounds__(512) void query_apply_bf16(const uint16_t* __restrict__ Q,
+                                                        const uint16_t* __restrict__ St,
+                                                        const float* __restrict__ Zt,
+                                                        uint16_t* __restrict__ O, const Geo g) {
     constexpr int RT = D / 16, KS = D / 32;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = (threadIdx.x >> 6) % NWA, lane = threadIdx.x & 63;
     const int t = lane & 15, gq = lane >> 4;
-    const int blk = blockIdx.x;
-    const int bh = (int)fdiv(blk, g.div_M);
-    const int i = blk - bh * g.M;
+    const WgCoord wgc = wg_coord(g, blockIdx.x);
+    const int h = wgc.hg * g.G + (int)(threadIdx.x >> 6) / NWA;
+    if (h >= g.H) return;
+    const int i = wgc.j;
+    const int bh = wgc.b * g.H + h;
+    const int blk = bh * g.M + i;
     ApplyA<D> A;
     const uint16_t* sb = St + (size_t)blk * (D * D);
 #pragma unroll
@@ -409,10 +545,10 @@ __global__ __launch_bounds__(64 * NWA) void query_apply_bf16(const uint16_t* __r
     for (int kk = 0; kk < KS; ++kk) {
         const f32x4 x = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8);
         const f32x4 y = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8 + 4);
-        A.zt[kk][0] = x.x; A.zt[kk][1] = x.y; A.zt[kk][2] = x.z; A.zt[kk][3] = x.w;
-        A.zt[kk][4] = y.x; A.zt[kk][5] = y.y; A.zt[kk][6] = y.z; A.zt[kk][7] = y.w;
+        const float z[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        split_zt(z, A.zhi[kk], A.zlo[kk]);
     }
-    apply_tokens_bf16<D, NWA>(A, Q, O, g, bh, i, wave, lane);
+    apply_tokens_bf16<D, NWA, PF, NTL, NTO>(A, Q, O, g, bh, i, wave, lane);
 }
 
 // =====================================================================
@@ -484,10 +620,13 @@ __global__ __launch_bounds__(256) void query_apply_fused_bf16(const uint16_t* __
         for (int kk = 0; kk < KS; ++kk) A.a[r][kk] = *reinterpret_cast<const u32x4*>(sSt + e * D + kk * 32 + gq * 8);
     }
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk)
+    for (int kk = 0; kk < KS; ++kk) {
+        float z[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) A.zt[kk][s] = sZt[kk * 32 + gq * 8 + s];
-    apply_tokens_bf16<D, 4>(A, Q, O, g, bh, i, wave, lane);
+        for (int s = 0; s < 8; ++s) z[s] = sZt[kk * 32 + gq * 8 + s];
+        split_zt(z, A.zhi[kk], A.zlo[kk]);
+    }
+    apply_tokens_bf16<D, 4, 2, false, false>(A, Q, O, g, bh, i, wave, lane);
 }
 
 // =====================================================================
@@ -495,6 +634,53 @@ __global__ __launch_bounds__(256) void query_apply_fused_bf16(const uint16_t* __
 // =====================================================================
 inline void record(const Launch& L, int k) {
     if (L.events) (void)hipEventRecord(L.events[k], L.stream);
+}
+
+// Head groups: G heads per workgroup with `per_head` waves each, at most 8 waves.
+inline Geo with_head_groups(Geo g, int per_head) {
+    g.G = g.H < 8 / per_head ? g.H : 8 / per_head;
+    g.HG = (g.H + g.G - 1) / g.G;
+    g.div_HG = make_fastdiv((uint32_t)g.HG);
+    return g;
+}
+
+template <int D, int PF, bool ROW8, bool FULL>
+void launch_summary(const Launch& L, const uint16_t* k, const uint16_t* v, uint16_t* sz,
+                    const WConv& wc) {
+    constexpr int NQ = D == 128 ? 4 : 1;
+    const Geo g = with_head_groups(L.g, NQ);
+    const int nsum = g.B * g.M * g.HG, threads = 64 * NQ * g.G;
+    WConv w = wc;
+    w.first_wg = nsum;
+    const int nconv = (wc.nchunks + threads * 4 - 1) / (threads * 4);   // up to 4 chunks per thread
+    if (L.tune.nt_loads)
+        block_kv_summary_bf16<D, PF, ROW8, FULL, true><<<nsum + nconv, threads, 0, L.stream>>>(
+            k, v, sz, g, L.W, static_cast<uint16_t*>(L.wb), w);
+    else
+        block_kv_summary_bf16<D, PF, ROW8, FULL, false><<<nsum + nconv, threads, 0, L.stream>>>(
+            k, v, sz, g, L.W, static_cast<uint16_t*>(L.wb), w);
+}
+
+template <int D, int NWA, int PF>
+void launch_apply_pf(const Launch& L, const Geo& g, const uint16_t* q, const uint16_t* st, uint16_t* o) {
+    const int grid = g.B * g.M * g.HG, block = 64 * NWA * g.G;
+    if (L.tune.nt_loads) {
+        if (L.tune.nt_stores) query_apply_bf16<D, NWA, PF, true, true><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
+        else query_apply_bf16<D, NWA, PF, true, false><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
+    } else {
+        if (L.tune.nt_stores) query_apply_bf16<D, NWA, PF, false, true><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
+        else query_apply_bf16<D, NWA, PF, false, false><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
+    }
+}
+
+template <int D, int NWA>
+void launch_apply(const Launch& L, const uint16_t* q, const uint16_t* st, uint16_t* o) {
+    const Geo g = with_head_groups(L.g, NWA);
+    switch (L.tune.apply_pf) {
+        case 1: launch_apply_pf<D, NWA, 1>(L, g, q, st, o); break;
+        case 2: launch_apply_pf<D, NWA, 2>(L, g, q, st, o); break;
+        default: launch_apply_pf<D, NWA, 4>(L, g, q, st, o); break;
+    }
 }
 
 template <int D>
@@ -507,31 +693,45 @@ hipError_t run_d(const Launch& L) {
     auto* o = static_cast<uint16_t*>(L.out);
     auto* sz = static_cast<uint16_t*>(L.sz);
     auto* st = static_cast<uint16_t*>(L.st);
+    const bool fused = L.path == MHLA_PATH_FUSED;
+    const int IT = (g.M + 63) / 64, NK = (g.M + 31) / 32;
+    WConv wc;
+    wc.M = g.M;
+    wc.Jpad = NK * 32;
+    wc.nchunks = fused ? 0 : IT * 64 * wc.Jpad / 8;
+    wc.first_wg = 0;
+    const bool row8 = (g.bk2 % 8) == 0;
 
     record(L, 0);
-    if constexpr (D == 128) {
-        block_kv_summary_bf16<D, 1><<<nblk, 256, 0, L.stream>>>(k, v, sz, g);
+    const bool full = row8 && (g.T % 32) == 0;
+    if (L.tune.summary_pf == 1) {
+        if (full) launch_summary<D, 1, true, true>(L, k, v, sz, wc);
+        else if (row8) launch_summary<D, 1, true, false>(L, k, v, sz, wc);
+        else launch_summary<D, 1, false, false>(L, k, v, sz, wc);
     } else {
-        switch (L.tune.summary_waves) {
-            case 1: block_kv_summary_bf16<D, 1><<<nblk, 64, 0, L.stream>>>(k, v, sz, g); break;
-            case 2: block_kv_summary_bf16<D, 2><<<nblk, 128, 0, L.stream>>>(k, v, sz, g); break;
-            default: block_kv_summary_bf16<D, 4><<<nblk, 256, 0, L.stream>>>(k, v, sz, g); break;
-        }
+        if (full) launch_summary<D, 2, true, true>(L, k, v, sz, wc);
+        else if (row8) launch_summary<D, 2, true, false>(L, k, v, sz, wc);
+        else launch_summary<D, 2, false, false>(L, k, v, sz, wc);
     }
     record(L, 1);
-    if (L.path == MHLA_PATH_FUSED) {
+    if (fused) {
         record(L, 2);
         query_apply_fused_bf16<D><<<nblk, 256, 0, L.stream>>>(q, sz, L.W, o, g);
     } else {
-        const int CT = (D * D + D + 63) / 64, IT = (g.M + 63) / 64;
-        const long tiles = (long)g.BH * CT * IT;
-        mix_summaries_bf16<D><<<(unsigned)((tiles + 3) / 4), 256, 0, L.stream>>>(
-            sz, L.W, st, L.zt, g, make_fastdiv(IT), make_fastdiv(CT));
+        MixGeo mg;
+        mg.CT = (D * D + D + 63) / 64;
+        mg.IT = IT;
+        mg.CPW = IT >= 4 ? 1 : 4 / IT;
+        mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
+        mg.Jpad = wc.Jpad;
+        mg.div_CTG = make_fastdiv(mg.CTG);
+        mix_summaries_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(
+            sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg);
         record(L, 2);
         switch (L.tune.apply_waves) {
-            case 1: query_apply_bf16<D, 1><<<nblk, 64, 0, L.stream>>>(q, st, L.zt, o, g); break;
-            case 2: query_apply_bf16<D, 2><<<nblk, 128, 0, L.stream>>>(q, st, L.zt, o, g); break;
-            default: query_apply_bf16<D, 4><<<nblk, 256, 0, L.stream>>>(q, st, L.zt, o, g); break;
+            case 1: launch_apply<D, 1>(L, q, st, o); break;
+            case 2: launch_apply<D, 2>(L, q, st, o); break;
+            default: launch_apply<D, 4>(L, q, st, o); break;
         }
     }
     record(L, 3);

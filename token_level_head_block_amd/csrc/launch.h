@@ -8,8 +8,12 @@
 namespace mhla {
 
 struct Tuning {
-    int summary_waves;   // waves splitting the tokens of one block in block_kv_summary (1, 2, 4)
+    int summary_waves;   // fp32 path: waves splitting the tokens of one block (1, 2, 4)
+    int summary_pf;      // bf16 path: k-steps of K/V loads in flight per wave (1, 2)
     int apply_waves;     // waves splitting the tokens of one block in query_apply (1, 2, 4)
+    int apply_pf;        // bf16 path: 16-token groups of Q loads in flight per wave (1, 2, 4)
+    int nt_loads;        // bf16 path: non-temporal hint on the loads of q, k, v
+    int nt_stores;       // bf16 path: non-temporal hint on the stores of out
 };
 
 struct Launch {
@@ -21,6 +25,7 @@ struct Launch {
     void* sz;      // summaries  [BH][M][D*D + D]   (compute type)
     void* st;      // mixed      [BH][M][D*D]       (compute type)
     float* zt;     // mixed normalisers [BH][M][D]  (fp32)
+    void* wb;      // bf16 path: W as bf16 [roundup(M,64)][roundup(M,32)], zero padded
     Geo g;
     Tuning tune;
     int path;                     // MHLA_PATH_*

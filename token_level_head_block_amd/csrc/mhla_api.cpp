@@ -57,11 +57,13 @@ mhla_status check(const mhla_grid* grid, const mhla_block* block, Shape* s) {
     if ((double)s->B * (double)s->N * (double)s->H * (double)s->D >= lim) return MHLA_ERR_UNSUPPORTED;
     if ((double)s->B * (double)s->H * (double)s->M * (double)(s->D * s->D + s->D) >= lim)
         return MHLA_ERR_UNSUPPORTED;
+    // One batch item's tensor must also fit a 2^31-byte buffer range.
+    if ((double)s->N * (double)s->H * (double)s->D * (double)s->esz >= lim) return MHLA_ERR_UNSUPPORTED;
     return MHLA_OK;
 }
 
 struct Layout {
-    size_t sz, st, zt, total;   // byte offsets of the three regions, total size
+    size_t sz, st, zt, wb, total;   // byte offsets of the regions, total size
 };
 
 Layout layout(const Shape& s) {
@@ -70,7 +72,11 @@ Layout layout(const Shape& s) {
     L.sz = 0;
     L.st = align_up(recs * (size_t)(s.D * s.D + s.D) * s.esz);
     L.zt = L.st + align_up(recs * (size_t)(s.D * s.D) * s.esz);
-    L.total = L.zt + align_up(recs * (size_t)s.D * 4);
+    L.wb = L.zt + align_up(recs * (size_t)s.D * 4);
+    // bf16 problems: W converted to bf16, rows padded to a multiple of 64 and
+    // columns to a multiple of 32 (the mixing kernel's tile sizes).
+    const size_t wb = s.dtype == MHLA_BF16 ? (size_t)((s.M + 63) / 64 * 64) * (size_t)((s.M + 31) / 32 * 32) * 2 : 0;
+    L.total = L.wb + align_up(wb);
     return L;
 }
 
@@ -91,11 +97,19 @@ mhla::Tuning choose_tuning(const Shape& s) {
     mhla::Tuning t;
     // Waves per block: enough token groups per wave to amortise the per-wave
     // setup, enough waves to keep loads in flight.
-    t.summary_waves = s.T >= 192 ? 2 : (s.T >= 64 ? 2 : 1);
-    t.apply_waves = s.T >= 128 ? 2 : 1;
+    t.summary_waves = 1;
+    t.summary_pf = 2;
+    t.apply_waves = 1;
+    t.apply_pf = s.D == 128 ? 1 : 4;   // d = 128 keeps 32 operand registers per row tile live
+    // Overrides for launch-shape sweeps.
     const int sw = env_int("MHLA_SUMMARY_WAVES", 0), aw = env_int("MHLA_APPLY_WAVES", 0);
+    const int sp = env_int("MHLA_SUMMARY_PF", 0), ap = env_int("MHLA_APPLY_PF", 0);
     if (sw == 1 || sw == 2 || sw == 4) t.summary_waves = sw;
     if (aw == 1 || aw == 2 || aw == 4) t.apply_waves = aw;
+    if (sp == 1 || sp == 2) t.summary_pf = sp;
+    if (ap == 1 || ap == 2 || ap == 4) t.apply_pf = ap;
+    t.nt_loads = env_int("MHLA_NT_LOADS", 1) != 0;
+    t.nt_stores = env_int("MHLA_NT_STORES", 0) != 0;
     return t;
 }
 
@@ -112,6 +126,9 @@ mhla::Geo make_geo(const Shape& s, float eps) {
     g.div_nb12 = mhla::make_fastdiv((uint32_t)(s.nb[1] * s.nb[2]));
     g.div_M = mhla::make_fastdiv((uint32_t)s.M);
     g.div_H = mhla::make_fastdiv((uint32_t)(s.H > 0 ? s.H : 1));
+    g.G = 1;
+    g.HG = g.H;
+    g.div_HG = mhla::make_fastdiv((uint32_t)(s.H > 0 ? s.H : 1));
     g.eps = eps;
     return g;
 }
@@ -156,6 +173,7 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
     L.sz = base + lay.sz;
     L.st = base + lay.st;
     L.zt = reinterpret_cast<float*>(base + lay.zt);
+    L.wb = base + lay.wb;
     L.g = make_geo(s, grid->eps);
     L.tune = choose_tuning(s);
     L.path = path;
