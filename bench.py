@@ -26,6 +26,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MHLA fwd tokens/s + achieved HBM GB/s (% peak), N=65536 H=6 d=64 bf16"
+KERNEL_SOURCES = ["token_level_head_block_amd/csrc/kernels_bf16.hip", "token_level_head_block_amd/csrc/common.h",
+                  "token_level_head_block_amd/csrc/mhla_api.cpp", "token_level_head_block_amd/csrc/launch.h"]
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 MALL_BYTES = 256 << 20          # Infinity Cache
 
@@ -43,7 +45,45 @@ def parse():
     ap.add_argument("--out", default="", help="also write the JSON line to this file")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size")
     ap.add_argument("--heads", type=int, default=0, help="override the workload's head count")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (10 times): the reference "
+                         "for scaling the HBM byte counters of a profiler run")
     return ap.parse_args()
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """Per-dispatch HBM bytes of each kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE, WRITE_SIZE scaled by a plain copy of known size), or {}
+    if there is none for this workload or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return {}
+    vals = {}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_sha():
+        return {}
+    fs, ws = float(vals["fetch_scale"]), float(vals["write_scale"])
+    out = {}
+    for k, v in vals.items():
+        if k.endswith(" fetch_kib"):
+            name = k[: -len(" fetch_kib")]
+            w = float(vals.get(name + " write_kib", 0.0))
+            out[name] = int(float(v) * 1024 * fs + w * 1024 * ws)
+    return out
 
 
 def kernel_bytes(p, ws_elem):
@@ -79,6 +119,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        x = torch.empty(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(10):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "dispatches": 10}), flush=True)
+        return
     mh.lib()   # fail loudly if the HIP library is missing
 
     p = synth.CONFIGS[args.config]
@@ -157,8 +206,12 @@ def main():
         kernels[n] = {"avg_us": round(float(avg[j]) * 1e3, 2), "alg_bytes": int(kb[n]),
                       "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
+    traffic = measured_traffic(p.name) if (args.path == "3kernel" and args.w == "gaussian"
+                                           and not args.batch and not args.heads) else {}
+    for n in kernels:
+        kernels[n]["traffic"] = traffic.get(n)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": kernels[dom]["frac"], "traffic": None,
+                "unit": "GB/s", "frac": kernels[dom]["frac"], "traffic": traffic.get(dom),
                 "avg_us": kernels[dom]["avg_us"], "alg_bytes": kernels[dom]["alg_bytes"]}
 
     # ---- CPU baseline: the float64 oracle on the host cores

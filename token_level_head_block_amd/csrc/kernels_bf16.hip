@@ -450,8 +450,13 @@ __device__ __forceinline__ void apply_tokens_bf16(const ApplyA<D>& A, const uint
     // the descriptor is wave-uniform, per-lane parts go in the offset.
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         O + (size_t)b * g.N * row, 0, g.N * row * 2, 0x00020000);
-    const int olane = (h * D + 4 * RT * gq) * 2;
+    const int olane = h * D * 2;
     const int nit = (g.T + 15) >> 4;
+    // Output staging: 16 tokens x D channels per wave, rows padded by 8 elements.
+    constexpr int OSTR = D + 8;
+    constexpr int CPR = D / 8;   // 16-byte chunks per token row
+    __shared__ __attribute__((aligned(16))) uint16_t sout_all[8 * 16 * OSTR];
+    uint16_t* sout = sout_all + (threadIdx.x >> 6) * (16 * OSTR);
 
     struct Raw {
         u32x4 q[KS];
@@ -489,14 +494,25 @@ __device__ __forceinline__ void apply_tokens_bf16(const ApplyA<D>& A, const uint
             wv[2 * r] = pack_bf16(acc[r][0] * inv, acc[r][1] * inv);
             wv[2 * r + 1] = pack_bf16(acc[r][2] * inv, acc[r][3] * inv);
         }
+        // The 16 x D output tile goes through this wave's LDS slice so that each
+        // store instruction writes whole rows of 2*D bytes (8 lanes x 16 bytes per
+        // 128-byte line) instead of interleaved 16-byte pieces of every row.
+        uint16_t* srow = sout + t * OSTR + 4 * RT * gq;
+#pragma unroll
+        for (int u = 0; u < RT / 2; ++u)
+            *reinterpret_cast<u32x4*>(srow + 8 * u) = u32x4{wv[4 * u], wv[4 * u + 1], wv[4 * u + 2], wv[4 * u + 3]};
         // Buffer stores: a lane past the block's last token gets an offset
         // beyond the buffer's range and the hardware drops its write, so the
         // store needs no branch.
-        const uint32_t boff = R.ok ? (uint32_t)(R.off * 2 + olane) : 0x80000000u;
 #pragma unroll
-        for (int u = 0; u < RT / 2; ++u)
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{wv[4 * u], wv[4 * u + 1], wv[4 * u + 2], wv[4 * u + 3]},
-                                                   orsrc, boff + 16 * u, 0, NTO ? 2 : 0);   // 2: nt
+        for (int k = 0; k < D / 32; ++k) {
+            const int tt = k * (64 / CPR) + lane / CPR, chunk = lane % CPR;
+            const int offk = __shfl(R.off, tt, 64);
+            const int okk = __shfl((int)R.ok, tt, 64);
+            const u32x4 x = *reinterpret_cast<const u32x4*>(sout + tt * OSTR + chunk * 8);
+            const uint32_t bo = okk ? (uint32_t)(offk * 2 + olane + chunk * 16) : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, bo, 0, NTO ? 2 : 0);   // 2: nt
+        }
     };
 
     // Batches of PF token groups: all loads of a batch are issued together
@@ -505,14 +521,25 @@ __device__ __forceinline__ void apply_tokens_bf16(const ApplyA<D>& A, const uint
     // Groups past the end load the block's last token and store nothing
     // (their lanes are all "not ok"), so the body has no branch the compiler
     // could sink the loads into.
-    for (int it0 = wave; it0 < nit; it0 += NWA * PF) {
-        Raw r[PF];
+    // Two batch buffers alternate: the next batch's loads are issued before the
+    // current batch is computed and stored.
+    const int step = NWA * PF;
+    Raw ra[PF], rb[PF];
 #pragma unroll
-        for (int u = 0; u < PF; ++u) load(it0 + u * NWA, r[u]);
+    for (int u = 0; u < PF; ++u) load(wave + u * NWA, ra[u]);
+    for (int it0 = wave; it0 < nit; it0 += 2 * step) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) load(it0 + step + u * NWA, rb[u]);
         // Keep the scheduler from sinking the batch's loads next to their uses.
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < PF; ++u) compute(r[u]);
+        for (int u = 0; u < PF; ++u) compute(ra[u]);
+        if (it0 + step >= nit) break;
+#pragma unroll
+        for (int u = 0; u < PF; ++u) load(it0 + 2 * step + u * NWA, ra[u]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < PF; ++u) compute(rb[u]);
     }
 }
 
@@ -636,10 +663,12 @@ inline void record(const Launch& L, int k) {
     if (L.events) (void)hipEventRecord(L.events[k], L.stream);
 }
 
-// Head groups: G heads per workgroup with `per_head` waves each, at most 8 waves.
+// Head groups: G heads per workgroup with `per_head` waves each, at most 8
+// waves, with the heads spread evenly over the groups.
 inline Geo with_head_groups(Geo g, int per_head) {
-    g.G = g.H < 8 / per_head ? g.H : 8 / per_head;
-    g.HG = (g.H + g.G - 1) / g.G;
+    const int gmax = 8 / per_head;
+    g.HG = (g.H + gmax - 1) / gmax;
+    g.G = (g.H + g.HG - 1) / g.HG;
     g.div_HG = make_fastdiv((uint32_t)g.HG);
     return g;
 }

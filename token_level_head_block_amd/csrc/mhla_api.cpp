@@ -99,8 +99,8 @@ mhla::Tuning choose_tuning(const Shape& s) {
     // setup, enough waves to keep loads in flight.
     t.summary_waves = 1;
     t.summary_pf = 2;
-    t.apply_waves = 1;
-    t.apply_pf = s.D == 128 ? 1 : 4;   // d = 128 keeps 32 operand registers per row tile live
+    t.apply_waves = s.T >= 128 ? 2 : 1;
+    t.apply_pf = s.D == 128 ? 1 : 2;   // d = 128 keeps 32 operand registers per row tile live
     // Overrides for launch-shape sweeps.
     const int sw = env_int("MHLA_SUMMARY_WAVES", 0), aw = env_int("MHLA_APPLY_WAVES", 0);
     const int sp = env_int("MHLA_SUMMARY_PF", 0), ap = env_int("MHLA_APPLY_PF", 0);
