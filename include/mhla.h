@@ -113,8 +113,10 @@ mhla_status mhla_check_problem(const mhla_grid* grid, const mhla_block* block,
  *             P*M records of d*d compute-type elements ([e][c]);
  *   region 2 (at a 256-byte boundary): mixed normalisers zt_i, P*M*d fp32;
  *   region 3 (at a 256-byte boundary, bf16 problems only): W rounded to
- *             bf16, roundup(M, 64) rows of roundup(M, 32) elements, zero
- *             padded.
+ *             bf16 and zero padded to roundup(M, 64) x roundup(M, 32), stored
+ *             in the mixing kernel's operand order: 8-element unit
+ *             (rt * roundup(M,32)/32 + kk) * 64 + l holds
+ *             W[16*rt + l%16][32*kk + 8*(l/16) .. +7].
  * After a 3-kernel call completes, the regions hold these intermediates;
  * the fused path fills region 0 only. */
 size_t mhla_workspace_bytes(const mhla_grid* grid, const mhla_block* block);

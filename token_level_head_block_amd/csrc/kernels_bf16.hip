@@ -59,20 +59,23 @@ __device__ __forceinline__ void pipelined(int first, int step, int n, LoadF&& lo
     }
 }
 
-// W (fp32 [M][M]) -> bf16 [Ipad][Jpad], zero padded, for the mixing kernel's
-// B operand.  Done by extra workgroups appended to the summary launch, so the
-// summary workgroups themselves never wait on it.
+// W (fp32 [M][M]) -> bf16, zero padded to [Ipad = 64 * IT][Jpad = 32 * NK] and
+// stored in the mixing kernel's B-operand order: 16-byte unit
+// (rt * NK + kk) * 64 + lane holds W[16 * rt + lane % 16][32 * kk + 8 * (lane / 16) + 0..7],
+// so each wave's operand loads are contiguous.  Done by extra workgroups
+// appended to the summary launch, so the summary workgroups never wait on it.
 struct WConv {
-    int32_t M, Jpad, nchunks;   // nchunks = Ipad * Jpad / 8 (8 elements each); 0 = none
-    int32_t first_wg;           // workgroups [first_wg, gridDim.x) convert
+    int32_t M, NK, nchunks;   // NK = Jpad / 32; nchunks = Ipad * Jpad / 8; 0 = none
+    int32_t first_wg;         // workgroups [first_wg, gridDim.x) convert
 };
 
 __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t* __restrict__ Wb,
                                           const WConv& wc) {
-    const int cpr = wc.Jpad >> 3;   // chunks per row
     const int nthr = (gridDim.x - wc.first_wg) * blockDim.x;
     for (int c = (blockIdx.x - wc.first_wg) * blockDim.x + threadIdx.x; c < wc.nchunks; c += nthr) {
-        const int i = c / cpr, j0 = (c - i * cpr) * 8;
+        const int lane = c & 63, rk = c >> 6;
+        const int rt = rk / wc.NK, kk = rk - rt * wc.NK;
+        const int i = 16 * rt + (lane & 15), j0 = 32 * kk + 8 * (lane >> 4);
         float x[8];
         if (i < wc.M && (wc.M & 7) == 0 && j0 < wc.M) {
             const f32x4 a = *reinterpret_cast<const f32x4*>(W + (size_t)i * wc.M + j0);
@@ -83,7 +86,7 @@ __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t*
 #pragma unroll
             for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)i * wc.M + j0 + s] : 0.f;
         }
-        *reinterpret_cast<u32x4*>(Wb + (size_t)i * wc.Jpad + j0) =
+        *reinterpret_cast<u32x4*>(Wb + (size_t)c * 8) =
             u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
     }
 }
@@ -248,8 +251,8 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
 // all query blocks i.  The A operand (records of the CPW tiles, up to 256
 // source blocks per pass) is staged once in LDS, already packed as MFMA
 // operands; wave (c, it, th) computes 64 col' x 32 i (i = it*64 + 32*th + ..)
-// with all of its W operands (bf16, padded, converted by the summary kernel)
-// loaded from L2 before the staging, so their latency is paid once.
+// with all of its W operands (bf16, padded and laid out in operand order by
+// the summary kernel's extra workgroups) loaded from L2 around the staging.
 // Lane (li, gq): A rows col' = 4*li + r, B column i = 16*t + li.
 // Mixed S tiles leave through LDS so that every store writes whole 128-byte
 // record rows; mixed z (fp32) is stored directly.
@@ -304,8 +307,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
                     bw[kk][t] = *reinterpret_cast<const u32x4*>(
-                        Wb + (size_t)(itc * 64 + 32 * th + 16 * t + li) * mg.Jpad +
-                        (k0 + (kk < nkp ? kk : nkp - 1)) * 32 + gq * 8);
+                        Wb + ((size_t)((itc * 4 + 2 * th + t) * NK + k0 + (kk < nkp ? kk : nkp - 1)) * 64 + lane) * 8);
             };
 #pragma unroll
             for (int kk = 0; kk < KSP / 2; ++kk) load_w(kk);
@@ -726,8 +728,8 @@ hipError_t run_d(const Launch& L) {
     const int IT = (g.M + 63) / 64, NK = (g.M + 31) / 32;
     WConv wc;
     wc.M = g.M;
-    wc.Jpad = NK * 32;
-    wc.nchunks = fused ? 0 : IT * 64 * wc.Jpad / 8;
+    wc.NK = NK;
+    wc.nchunks = fused ? 0 : IT * 64 * NK * 32 / 8;
     wc.first_wg = 0;
     const bool row8 = (g.bk2 % 8) == 0;
 
@@ -752,7 +754,7 @@ hipError_t run_d(const Launch& L) {
         mg.IT = IT;
         mg.CPW = IT >= 4 ? 1 : 4 / IT;
         mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
-        mg.Jpad = wc.Jpad;
+        mg.Jpad = NK * 32;
         mg.div_CTG = make_fastdiv(mg.CTG);
         mix_summaries_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(
             sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg);
