@@ -106,7 +106,7 @@ __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t*
 // FULL: ROW8 and T a multiple of 32, so no token slot is ever padding.
 // =====================================================================
 template <int D, int PF, bool ROW8, bool FULL, bool NTL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 && D <= 64 ? 3 : 2)))
 void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                            uint16_t* __restrict__ SZ, const Geo g, const float* __restrict__ W,
                            uint16_t* __restrict__ Wb, const WConv wc) {
@@ -217,20 +217,32 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
 
     // Record layout: S_j transposed ([e][c], c fastest), then z_j.
     // Lane holds S[c][e] for c = rowbase + 4*CPL*gq + CPL*v + r, e = colbase + CPL*li + c2,
-    // and z[c] (every column of accz is the same) for the same c.
-    uint16_t* rec = SZ + (size_t)blk * (D * D + D);
+    // and z[c] (every column of accz is the same) for the same c.  The tile
+    // goes through this wave's own LDS slice so that every store instruction
+    // writes whole record rows (8 lanes x 16 bytes per 128 bytes).
+    constexpr int TW = 16 * CPL;          // tile width: 64 (32 for d = 32)
+    constexpr int TS = TW + 8;            // padded LDS row
+    __shared__ __attribute__((aligned(16))) uint16_t stile_all[8 * TW * TS];
+    uint16_t* stile = stile_all + wave * (TW * TS);
 #pragma unroll
     for (int c2 = 0; c2 < CPL; ++c2) {
-        const int e = colbase + CPL * li + c2;
         uint32_t wv[2 * CPL];
 #pragma unroll
         for (int v = 0; v < 4; ++v)
 #pragma unroll
             for (int rp = 0; rp < CPL / 2; ++rp)
                 wv[v * (CPL / 2) + rp] = pack_bf16(acc[2 * rp][c2][v], acc[2 * rp + 1][c2][v]);
-        uint16_t* dst = rec + e * D + rowbase + 4 * CPL * gq;
+        uint16_t* dst = stile + (CPL * li + c2) * TS + 4 * CPL * gq;
         *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
         if constexpr (CPL == 4) *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+    }
+    uint16_t* rec = SZ + (size_t)blk * (D * D + D);
+    constexpr int LPR = TW / 8;           // lanes per tile row (16 bytes each)
+#pragma unroll
+    for (int k = 0; k < TW / (64 / LPR); ++k) {
+        const int er = k * (64 / LPR) + lane / LPR, chunk = lane % LPR;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(stile + er * TS + chunk * 8);
+        *reinterpret_cast<u32x4*>(rec + (colbase + er) * D + rowbase + chunk * 8) = x;
     }
     if (do_z && li == 0) {
         uint32_t wv[2 * CPL];

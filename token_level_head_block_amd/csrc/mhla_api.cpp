@@ -98,7 +98,7 @@ mhla::Tuning choose_tuning(const Shape& s) {
     // Waves per block: enough token groups per wave to amortise the per-wave
     // setup, enough waves to keep loads in flight.
     t.summary_waves = 1;
-    t.summary_pf = 2;
+    t.summary_pf = 1;
     t.apply_waves = s.T >= 128 ? 2 : 1;
     t.apply_pf = s.D == 128 ? 1 : 2;   // d = 128 keeps 32 operand registers per row tile live
     // Overrides for launch-shape sweeps.
