@@ -104,6 +104,37 @@ def kernel_bytes(p, ws_elem):
     }
 
 
+class HipEvents:
+    """HIP events created with hipEventDisableSystemFence, through the HIP runtime."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.made = []
+
+    def create(self) -> int:
+        e = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.ct.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0 or not e.value:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.made.append(e.value)
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        x = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(x), self.ct.c_void_p(a), self.ct.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(x.value)
+
+    def destroy_all(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(self.ct.c_void_p(e))
+        self.made = []
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -182,17 +213,19 @@ def main():
     U = 4 * tensor_bytes + 4 * p.n_blocks ** 2
     path_gbps = U / (ms_step * 1e-3) / 1e9
 
-    # ---- per-kernel attribution: stage events on the launch stream, same loop
+    # ---- per-kernel attribution: stage events on the launch stream, same loop.
+    # The events skip the system-scope fence (cache write-back) that a default
+    # event performs when it completes, so they cost almost nothing between
+    # kernels and agree with rocprofv3's kernel durations.
     nstage = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nstage)]
-    for row in evs:
-        for e in row:
-            e.record(stream)
+    hev = HipEvents()
+    evs = [[hev.create() for _ in range(4)] for _ in range(nstage)]
     torch.cuda.synchronize()
     for i in range(nstage):
         step(i, evs[i])
     torch.cuda.synchronize()
-    stage_ms = np.array([[row[j].elapsed_time(row[j + 1]) for j in range(3)] for row in evs])
+    stage_ms = np.array([[hev.elapsed_ms(row[j], row[j + 1]) for j in range(3)] for row in evs])
+    hev.destroy_all()
     avg = stage_ms.mean(axis=0)
     names = (["block_kv_summary", "mix_summaries", "query_apply"] if path == mh.MHLA_PATH_3KERNEL
              else ["block_kv_summary", "(none)", "query_apply_fused"])

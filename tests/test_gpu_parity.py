@@ -88,6 +88,32 @@ def test_bf16_intermediates(case):
         assert e <= 1e-2, name
 
 
+MIX_CASES = [
+    ("mix-d64-M16-units544", 4, 8, 64, (16, 16), (4, 4), BF, 1.0),     # 544 work units: several per workgroup
+    ("mix-d32-M180", 1, 3, 32, (30, 24), (2, 2), BF, 1.0),              # 3 query-block tiles, ragged
+    ("mix-d128-M96", 1, 2, 128, (24, 32), (2, 4), BF, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", MIX_CASES, ids=lambda c: c[0])
+def test_mixing_kernels(case, monkeypatch):
+    """Both bf16 mixing kernels (persistent with W in registers, and one
+    workgroup per column tile) against the oracle's mixed summaries, and the
+    whole output of each against the oracle."""
+    p = small_problem(case)
+    q, k, v, W = synth.make_inputs(p, seed=25)
+    ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)
+    _, _, rSt, rzt = oracle.summaries(k, v, W, p.grid, p.block)
+    run = Run(p, q, k, v, W)
+    for resident in ("1", "0"):
+        monkeypatch.setenv("MHLA_MIX_RESIDENT", resident)
+        out = to_host64(run.forward())
+        _, _, St, zt = run.workspace()
+        e_out, e_st, e_zt = rel_err(out, ref), rel_err(St, rSt), rel_err(zt, rzt)
+        say(f"  {p.name} resident={resident}: out {e_out:.2e} St {e_st:.2e} zt {e_zt:.2e}")
+        assert e_out <= TOL[p.dtype] and e_st <= 1e-2 and e_zt <= 1e-2
+
+
 @pytest.mark.parametrize("cfg_index", [1, 2, 3, 4])
 def test_full_workloads_sampled_pairs(cfg_index):
     """Full-size workload, default launch configuration; every output of the

@@ -174,14 +174,15 @@ def mhla_forward_ws(q, k, v, W, grid: mhla_grid, block: mhla_block, out, ws, ws_
 
 def mhla_forward_ex(q, k, v, W, grid: mhla_grid, block: mhla_block, out, ws, ws_bytes: int,
                     path: int = MHLA_PATH_3KERNEL, stage_events=None, stream=None) -> int:
-    """stage_events: None or 4 torch.cuda.Event objects (already recorded once,
-    so that their HIP handles exist)."""
+    """stage_events: None or 4 events, each a torch.cuda.Event (already
+    recorded once, so that its HIP handle exists) or a raw hipEvent_t handle
+    (int)."""
     _check_tensors(q, k, v, W, out, grid, block)
     ev = None
     if stage_events is not None:
         if len(stage_events) != 4:
             raise ValueError("stage_events needs 4 events")
-        arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in stage_events])
+        arr = (ctypes.c_void_p * 4)(*[e if isinstance(e, int) else e.cuda_event for e in stage_events])
         if any(a is None or a == 0 for a in arr):
             raise ValueError("stage events have no HIP handle yet; record each once first")
         ev = ctypes.cast(arr, ctypes.c_void_p)

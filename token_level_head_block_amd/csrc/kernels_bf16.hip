@@ -106,7 +106,7 @@ __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t*
 // FULL: ROW8 and T a multiple of 32, so no token slot is ever padding.
 // =====================================================================
 template <int D, int PF, bool ROW8, bool FULL, bool NTL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 && D <= 64 ? 3 : 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 && D <= 64 && FULL ? 3 : 2)))
 void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                            uint16_t* __restrict__ SZ, const Geo g, const float* __restrict__ W,
                            uint16_t* __restrict__ Wb, const WConv wc) {
@@ -312,14 +312,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
 
         for (int k0 = 0; k0 < NK; k0 += KSP) {
             const int nkp = min(KSP, NK - k0);
+            // Workgroups visit the pass's k-steps in rotated order (step kr(kk)
+            // at position kk), so that they do not all request the same W lines
+            // from L2 at the same moment.
+            const int rot = (int)(wg % (uint32_t)nkp);
+            auto kr = [&](int kk) {
+                const int x = kk + rot;
+                return kk >= nkp ? nkp - 1 : (x >= nkp ? x - nkp : x);
+            };
             // W operands (B) of this pass: the first half before the staging of A,
-            // the second half after it; steps past nkp reload step nkp - 1.
+            // the second half after it; positions past nkp reload a valid step.
             u32x4 bw[KSP][2];
             auto load_w = [&](int kk) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
                     bw[kk][t] = *reinterpret_cast<const u32x4*>(
-                        Wb + ((size_t)((itc * 4 + 2 * th + t) * NK + k0 + (kk < nkp ? kk : nkp - 1)) * 64 + lane) * 8);
+                        Wb + ((size_t)((itc * 4 + 2 * th + t) * NK + k0 + kr(kk)) * 64 + lane) * 8);
             };
 #pragma unroll
             for (int kk = 0; kk < KSP / 2; ++kk) load_w(kk);
@@ -367,7 +375,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
                     if (kk >= nkp) break;
                     u32x4 a[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) a[r] = sA[((wc * 4 + r) * nkp + kk) * 64 + lane];
+                    for (int r = 0; r < 4; ++r) a[r] = sA[((wc * 4 + r) * nkp + kr(kk)) * 64 + lane];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -420,6 +428,155 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
 }
 
 // =====================================================================
+// mix_resident: the same product for M <= 256 as a persistent kernel.  One
+// workgroup per compute unit; wave (c, it, th) loads its W operands (32 query
+// blocks x all source blocks: at most 16 operand registers x 4) once and keeps
+// them in registers, and the workgroup walks the work units (b*h, group of CPW
+// column tiles) with a stride of the grid size.  The A operands of the next
+// unit are loaded from memory while the current unit is multiplied and
+// stored, with two LDS buffers for the packed operands.  Lane roles, operand
+// packing and output mapping are those of mix_summaries.
+// =====================================================================
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void mix_resident_bf16(
+    const uint16_t* __restrict__ SZ, const uint16_t* __restrict__ Wb, uint16_t* __restrict__ St,
+    float* __restrict__ Zt, const Geo g, const MixGeo mg) {
+    constexpr int REC = D * D + D;
+    constexpr int KMAX = 8;         // k-steps (32 source blocks each) held in registers
+    constexpr int OROW = 72;        // output staging row: 64 bf16 + 8 padding
+    __shared__ u32x4 sA[2][8 * 4 * 64];                                          // 2 x 32 KB
+    __shared__ __attribute__((aligned(16))) uint16_t sOut[8 * 32 * OROW];       // 36 KB
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, gq = lane >> 4;
+    const int M = g.M;
+    const int NK = (M + 31) >> 5;                     // <= KMAX (checked on the host)
+    const int cpw = mg.CPW;
+    const int itr = mg.IT;                            // <= 4 (checked on the host)
+    const int th = wave & 1, w2 = wave >> 1;
+    const int wc = w2 / itr, wit = w2 % itr;
+    const bool wave_ok = w2 < cpw * itr;
+    const int U = g.BH * mg.CTG;
+
+    // ---- W operands of this wave, kept for the whole kernel.
+    u32x4 bw[KMAX][2];
+#pragma unroll
+    for (int kk = 0; kk < KMAX; ++kk)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            bw[kk][t] = *reinterpret_cast<const u32x4*>(
+                Wb + ((size_t)((wit * 4 + 2 * th + t) * NK + (kk < NK ? kk : NK - 1)) * 64 + lane) * 8);
+
+    // ---- staging roles: thread -> (tile c, li', group of 8 source blocks).
+    const int units = cpw * 16 * 4 * NK;              // <= 512
+    const int lip = tid & 15;
+    const int jg = (tid >> 4) % (4 * NK);
+    const int sc = (tid >> 4) / (4 * NK);
+    const bool srole = tid < units;
+    u32x2 raw[8];
+    auto load_a = [&](int unit) {
+        const uint32_t bh = fdiv((uint32_t)unit, mg.div_CTG);
+        const int ctg = unit - (int)(bh * mg.div_CTG.d);
+        const int ct = ctg * cpw + sc;
+        const int colp = ct * 64 + 4 * lip;
+        const bool ok = srole && colp < REC && ct < mg.CT;
+        const int colc = ok ? colp : 0;
+        const uint16_t* base = SZ + (size_t)bh * M * REC;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int jj = (jg >> 2) * 32 + (jg & 3) * 8 + s;
+            const u32x2 t = *reinterpret_cast<const u32x2*>(base + (size_t)(jj < M ? jj : M - 1) * REC + colc);
+            const uint32_t m = (ok && jj < M) ? 0xffffffffu : 0u;
+            raw[s] = u32x2{t.x & m, t.y & m};
+        }
+    };
+    auto store_a = [&](u32x4* dst) {
+        if (srole) {
+            const int kk = jg >> 2, lanep = (jg & 3) * 16 + lip;
+            u32x4 op[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                op[0][w] = pack_lo(raw[2 * w].x, raw[2 * w + 1].x);
+                op[1][w] = pack_hi(raw[2 * w].x, raw[2 * w + 1].x);
+                op[2][w] = pack_lo(raw[2 * w].y, raw[2 * w + 1].y);
+                op[3][w] = pack_hi(raw[2 * w].y, raw[2 * w + 1].y);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[((sc * 4 + r) * NK + kk) * 64 + lanep] = op[r];
+        }
+    };
+
+    uint16_t* stage = sOut + wave * (32 * OROW);
+    int unit = blockIdx.x;
+    load_a(unit);
+    for (int buf = 0; unit < U; unit += gridDim.x, buf ^= 1) {
+        u32x4* sAb = sA[buf];
+        store_a(sAb);
+        const int nxt = unit + (int)gridDim.x;
+        load_a(nxt < U ? nxt : unit);     // next unit's operands (clamped: always valid)
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();                  // sAb complete; sA[buf ^ 1] free since the last barrier
+
+        const uint32_t bh = fdiv((uint32_t)unit, mg.div_CTG);
+        const int ctg = unit - (int)(bh * mg.div_CTG.d);
+        const int ct = ctg * cpw + wc;
+        const bool active = wave_ok && ct < mg.CT;
+        if (!active) continue;
+        f32x4 acc[4][2];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KMAX; ++kk) {
+            if (kk >= NK) break;
+            u32x4 a[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = sAb[((wc * 4 + r) * NK + kk) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc[r][t] = mfma_bf16(a[r], bw[kk][t], acc[r][t]);
+        }
+
+        // ---- output.  Lane holds C[col' = cp0 + 16*gq + 4*v + r][i = it*64 + 32*th + 16*t + li].
+        const int cp0 = ct * 64;
+        const int it = wit;
+        if (cp0 < D * D) {
+            // The wave's own LDS slice: written and read back by this wave only.
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                uint32_t wv[8];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    wv[2 * v] = pack_bf16(acc[0][t][v], acc[1][t][v]);
+                    wv[2 * v + 1] = pack_bf16(acc[2][t][v], acc[3][t][v]);
+                }
+                uint16_t* dst = stage + (16 * t + li) * OROW + 16 * gq;
+                *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+                *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int rl = 8 * k + (lane >> 3), chunk = lane & 7;
+                const int i = it * 64 + 32 * th + rl;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rl * OROW + chunk * 8);
+                if (i < M) *reinterpret_cast<u32x4*>(St + ((size_t)bh * M + i) * (D * D) + cp0 + chunk * 8) = x;
+            }
+        } else if (cp0 + 16 * gq < REC) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int i = it * 64 + 32 * th + 16 * t + li;
+                if (i >= M) continue;
+                float* dst = Zt + ((size_t)bh * M + i) * D + (cp0 + 16 * gq - D * D);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    *reinterpret_cast<f32x4*>(dst + 4 * v) = f32x4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
+            }
+        }
+    }
+}
+
+// =====================================================================
 // query_apply: O^T = St_i^T phi(Q)^T per 16-token group.
 // A = St_i^T (rows e, k = c) stays in registers for the whole block; row ii of
 // row-tile r is e = 4*RT*(ii/4) + 4r + ii%4, so each lane ends with 4*RT
@@ -446,8 +603,12 @@ __device__ __forceinline__ void split_zt(const float* z, u32x4& hi, u32x4& lo) {
     }
 }
 
-template <int D, int NWA, int PF, bool NTL, bool NTO>
-__device__ __forceinline__ void apply_tokens_bf16(const ApplyA<D>& A, const uint16_t* __restrict__ Q,
+// prep_load(A) issues the loads of the block's A operands (and keeps zt raw);
+// prep_finish(A) turns raw zt into operands.  Both run after the first batch of
+// Q loads has been issued, so the latencies of St, zt and Q overlap.
+template <int D, int NWA, int PF, bool NTL, bool NTO, typename PrepLoad, typename PrepFinish>
+__device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFinish&& prep_finish,
+                                                  const uint16_t* __restrict__ Q,
                                                   uint16_t* __restrict__ O, const Geo& g, int bh,
                                                   int i, int wave, int lane) {
     constexpr int RT = D / 16, KS = D / 32;
@@ -484,7 +645,7 @@ __device__ __forceinline__ void apply_tokens_bf16(const ApplyA<D>& A, const uint
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) R.q[kk] = ld<NTL>(reinterpret_cast<const u32x4*>(qb + R.off + kk * 32));
     };
-    auto compute = [&](const Raw& R) {
+    auto compute = [&](const ApplyA<D>& A, const Raw& R) {
         u32x4 bq[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
@@ -536,24 +697,35 @@ __device__ __forceinline__ void apply_tokens_bf16(const ApplyA<D>& A, const uint
     // (their lanes are all "not ok"), so the body has no branch the compiler
     // could sink the loads into.
     // Two batch buffers alternate: the next batch's loads are issued before the
-    // current batch is computed and stored.
+    // current batch is computed and stored.  The first batch goes out before
+    // the block's St / zt operands, the second right after them.
+    if (wave >= nit) return;
     const int step = NWA * PF;
+    ApplyA<D> A;
     Raw ra[PF], rb[PF];
 #pragma unroll
     for (int u = 0; u < PF; ++u) load(wave + u * NWA, ra[u]);
-    for (int it0 = wave; it0 < nit; it0 += 2 * step) {
+    prep_load(A);
+    int it0 = wave;
 #pragma unroll
-        for (int u = 0; u < PF; ++u) load(it0 + step + u * NWA, rb[u]);
-        // Keep the scheduler from sinking the batch's loads next to their uses.
-        __builtin_amdgcn_sched_barrier(0);
+    for (int u = 0; u < PF; ++u) load(it0 + step + u * NWA, rb[u]);
+    // Keep the scheduler from sinking the batch's loads next to their uses.
+    __builtin_amdgcn_sched_barrier(0);
+    prep_finish(A);
+    for (;;) {
 #pragma unroll
-        for (int u = 0; u < PF; ++u) compute(ra[u]);
+        for (int u = 0; u < PF; ++u) compute(A, ra[u]);
         if (it0 + step >= nit) break;
 #pragma unroll
         for (int u = 0; u < PF; ++u) load(it0 + 2 * step + u * NWA, ra[u]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < PF; ++u) compute(rb[u]);
+        for (int u = 0; u < PF; ++u) compute(A, rb[u]);
+        it0 += 2 * step;
+        if (it0 >= nit) break;
+#pragma unroll
+        for (int u = 0; u < PF; ++u) load(it0 + step + u * NWA, rb[u]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -573,23 +745,31 @@ __global__ __launch_bounds__(512) void query_apply_bf16(const uint16_t* __restri
     const int i = wgc.j;
     const int bh = wgc.b * g.H + h;
     const int blk = bh * g.M + i;
-    ApplyA<D> A;
     const uint16_t* sb = St + (size_t)blk * (D * D);
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-        const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) A.a[r][kk] = *reinterpret_cast<const u32x4*>(sb + e * D + kk * 32 + gq * 8);
-    }
     const float* zb = Zt + (size_t)blk * D;
+    f32x4 zraw[KS][2];
+    auto prep_load = [&](ApplyA<D>& A) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8);
-        const f32x4 y = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8 + 4);
-        const float z[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-        split_zt(z, A.zhi[kk], A.zlo[kk]);
-    }
-    apply_tokens_bf16<D, NWA, PF, NTL, NTO>(A, Q, O, g, bh, i, wave, lane);
+        for (int r = 0; r < RT; ++r) {
+            const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) A.a[r][kk] = *reinterpret_cast<const u32x4*>(sb + e * D + kk * 32 + gq * 8);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            zraw[kk][0] = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8);
+            zraw[kk][1] = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8 + 4);
+        }
+    };
+    auto prep_finish = [&](ApplyA<D>& A) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const f32x4 x = zraw[kk][0], y = zraw[kk][1];
+            const float z[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+            split_zt(z, A.zhi[kk], A.zlo[kk]);
+        }
+    };
+    apply_tokens_bf16<D, NWA, PF, NTL, NTO>(prep_load, prep_finish, Q, O, g, bh, i, wave, lane);
 }
 
 // =====================================================================
@@ -653,21 +833,24 @@ __global__ __launch_bounds__(256) void query_apply_fused_bf16(const uint16_t* __
     __syncthreads();
 
     const int t = lane & 15, gq = lane >> 4;
-    ApplyA<D> A;
+    auto prep_load = [&](ApplyA<D>& A) {
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-        const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
+        for (int r = 0; r < RT; ++r) {
+            const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) A.a[r][kk] = *reinterpret_cast<const u32x4*>(sSt + e * D + kk * 32 + gq * 8);
-    }
+            for (int kk = 0; kk < KS; ++kk) A.a[r][kk] = *reinterpret_cast<const u32x4*>(sSt + e * D + kk * 32 + gq * 8);
+        }
+    };
+    auto prep_finish = [&](ApplyA<D>& A) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        float z[8];
+        for (int kk = 0; kk < KS; ++kk) {
+            float z[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) z[s] = sZt[kk * 32 + gq * 8 + s];
-        split_zt(z, A.zhi[kk], A.zlo[kk]);
-    }
-    apply_tokens_bf16<D, 4, 2, false, false>(A, Q, O, g, bh, i, wave, lane);
+            for (int s = 0; s < 8; ++s) z[s] = sZt[kk * 32 + gq * 8 + s];
+            split_zt(z, A.zhi[kk], A.zlo[kk]);
+        }
+    };
+    apply_tokens_bf16<D, 4, 2, false, false>(prep_load, prep_finish, Q, O, g, bh, i, wave, lane);
 }
 
 // =====================================================================
@@ -707,7 +890,7 @@ void launch_summary(const Launch& L, const uint16_t* k, const uint16_t* v, uint1
 template <int D, int NWA, int PF>
 void launch_apply_pf(const Launch& L, const Geo& g, const uint16_t* q, const uint16_t* st, uint16_t* o) {
     const int grid = g.B * g.M * g.HG, block = 64 * NWA * g.G;
-    if (L.tune.nt_loads) {
+    if (L.tune.nt_apply) {
         if (L.tune.nt_stores) query_apply_bf16<D, NWA, PF, true, true><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
         else query_apply_bf16<D, NWA, PF, true, false><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
     } else {
@@ -768,8 +951,16 @@ hipError_t run_d(const Launch& L) {
         mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
         mg.Jpad = NK * 32;
         mg.div_CTG = make_fastdiv(mg.CTG);
-        mix_summaries_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(
-            sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg);
+        if (L.tune.mix_resident && IT <= 4) {
+            // NK <= 8 follows from M <= 256.
+            const int units = g.BH * mg.CTG;
+            const int grid = units < L.tune.num_cus ? units : L.tune.num_cus;
+            mix_resident_bf16<D><<<grid, 512, 0, L.stream>>>(
+                sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg);
+        } else {
+            mix_summaries_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(
+                sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg);
+        }
         record(L, 2);
         switch (L.tune.apply_waves) {
             case 1: launch_apply<D, 1>(L, q, st, o); break;

@@ -12,8 +12,11 @@ struct Tuning {
     int summary_pf;      // bf16 path: k-steps of K/V loads in flight per wave (1, 2)
     int apply_waves;     // waves splitting the tokens of one block in query_apply (1, 2, 4)
     int apply_pf;        // bf16 path: 16-token groups of Q loads in flight per wave (1, 2, 4)
-    int nt_loads;        // bf16 path: non-temporal hint on the loads of q, k, v
+    int nt_loads;        // bf16 path: non-temporal hint on the loads of k, v (summary kernel)
+    int nt_apply;        // bf16 path: non-temporal hint on the loads of q (apply kernel)
     int nt_stores;       // bf16 path: non-temporal hint on the stores of out
+    int mix_resident;    // bf16 path, M <= 256: persistent mixing kernel with W in registers
+    int num_cus;         // compute units of the current device (persistent grid size)
 };
 
 struct Launch {

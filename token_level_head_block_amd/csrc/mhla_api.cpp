@@ -108,8 +108,13 @@ mhla::Tuning choose_tuning(const Shape& s) {
     if (aw == 1 || aw == 2 || aw == 4) t.apply_waves = aw;
     if (sp == 1 || sp == 2) t.summary_pf = sp;
     if (ap == 1 || ap == 2 || ap == 4) t.apply_pf = ap;
+    // Non-temporal loads: faster for the summary kernel's k, v stream and
+    // slower for the apply kernel's q stream (measured on MI355X).
     t.nt_loads = env_int("MHLA_NT_LOADS", 1) != 0;
+    t.nt_apply = env_int("MHLA_NT_APPLY", 0) != 0;
     t.nt_stores = env_int("MHLA_NT_STORES", 0) != 0;
+    t.mix_resident = env_int("MHLA_MIX_RESIDENT", 1) != 0;
+    t.num_cus = 256;
     return t;
 }
 
@@ -176,6 +181,14 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
     L.wb = base + lay.wb;
     L.g = make_geo(s, grid->eps);
     L.tune = choose_tuning(s);
+    {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            L.tune.num_cus = cus;
+        else
+            (void)hipGetLastError();
+    }
     L.path = path;
     L.events = events;
     L.stream = stream;
