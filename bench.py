@@ -227,8 +227,10 @@ def main():
     stage_ms = np.array([[hev.elapsed_ms(row[j], row[j + 1]) for j in range(3)] for row in evs])
     hev.destroy_all()
     avg = stage_ms.mean(axis=0)
-    names = (["block_kv_summary", "mix_summaries", "query_apply"] if path == mh.MHLA_PATH_3KERNEL
-             else ["block_kv_summary", "(none)", "query_apply_fused"])
+    st_plan, plan = mh.mhla_launch_plan(g, b, path)
+    if st_plan != mh.MHLA_OK:
+        raise mh.MhlaError(st_plan, "mhla_launch_plan")
+    names = plan if len(plan) == 3 else [plan[0], "(none)", plan[1]]
     ws_elem = p.elem_bytes
     kb = kernel_bytes(p, ws_elem)
     kernels = {}

@@ -102,6 +102,15 @@ const char* mhla_status_string(mhla_status status);
 mhla_status mhla_check_problem(const mhla_grid* grid, const mhla_block* block,
                                int64_t* num_blocks, int64_t* block_tokens);
 
+/* The kernels a call with these arguments launches, in order: *num_kernels
+ * receives 3 (MHLA_PATH_3KERNEL), 2 (MHLA_PATH_FUSED) or 0 (empty problem)
+ * and, if kernel_names is non-NULL, kernel_names[0..2] receive static names
+ * of the kernels, NULL past the count: "block_kv_summary", then
+ * "mix_summaries" and "query_apply", or "query_apply_fused".  Returns the
+ * validation status of grid, block and path; makes no HIP call. */
+mhla_status mhla_launch_plan(const mhla_grid* grid, const mhla_block* block, int32_t path,
+                             int32_t* num_kernels, const char** kernel_names);
+
 /* Bytes of device workspace mhla_forward_ws / mhla_forward_ex need for this
  * problem (0 for an invalid problem or an empty one).  Layout, from the
  * start of the workspace, for P = B*H pairs ordered (b, h):
@@ -117,8 +126,8 @@ mhla_status mhla_check_problem(const mhla_grid* grid, const mhla_block* block,
  *             in the mixing kernel's operand order: 8-element unit
  *             (rt * roundup(M,32)/32 + kk) * 64 + l holds
  *             W[16*rt + l%16][32*kk + 8*(l/16) .. +7].
- * After a 3-kernel call completes, the regions hold these intermediates;
- * the fused path fills region 0 only. */
+ * After a MHLA_PATH_3KERNEL call completes, regions 0-2 hold these
+ * intermediates; the fused path fills region 0 only. */
 size_t mhla_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
 
 /* The MHLA forward pass: out = MHLA(q, k, v; W) for the whole problem,

@@ -26,7 +26,7 @@ def L():
 def test_every_declared_function_is_exported(L):
     names = header_functions()
     assert {"mhla_forward", "mhla_forward_ws", "mhla_forward_ex", "mhla_workspace_bytes",
-            "mhla_status_string", "mhla_check_problem"} <= set(names)
+            "mhla_status_string", "mhla_check_problem", "mhla_launch_plan"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -131,3 +131,15 @@ def test_empty_problem_is_a_no_op(L):
         assert call_fwd(L, g, b, q=None, k=None, v=None, W=None, out=None) == mh.MHLA_OK
         assert call_fwd(L, g, b, q=None, k=None, v=None, W=None, out=None, entry="ws") == mh.MHLA_OK
         assert L.mhla_forward(None, None, None, None, ctypes.byref(g), ctypes.byref(b), None, None) == mh.MHLA_OK
+
+
+def test_launch_plan(L):
+    g, b = cfg2()
+    three = ["block_kv_summary", "mix_summaries", "query_apply"]
+    assert mh.mhla_launch_plan(g, b, mh.MHLA_PATH_3KERNEL) == (mh.MHLA_OK, three)
+    assert mh.mhla_launch_plan(g, b, mh.MHLA_PATH_FUSED) == (mh.MHLA_OK, ["block_kv_summary", "query_apply_fused"])
+    g32 = mh.make_grid(1, 1, 32, mh.MHLA_F32, (16, 16))
+    assert mh.mhla_launch_plan(g32, mh.make_block((4, 4)))[1] == three
+    assert mh.mhla_launch_plan(mh.make_grid(0, 6, 64, mh.MHLA_BF16, (256, 256)), b) == (mh.MHLA_OK, [])
+    assert mh.mhla_launch_plan(g, b, 7)[0] == mh.MHLA_ERR_INVALID_ARG
+    assert mh.mhla_launch_plan(g, mh.make_block((15, 16)))[0] == mh.MHLA_ERR_INVALID_ARG

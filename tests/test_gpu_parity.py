@@ -50,7 +50,8 @@ def test_small_problems_all_outputs(case, path):
     p = small_problem(case)
     q, k, v, W = synth.make_inputs(p, seed=21)
     ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)
-    out = to_host64(Run(p, q, k, v, W).forward(path))
+    run = Run(p, q, k, v, W)
+    out = to_host64(run.forward(path))
     err = rel_err(out, ref)
     say(f"  {p.name} path={path}: max|d|/max|ref| = {err:.3e}")
     assert np.isfinite(out).all()
@@ -95,6 +96,12 @@ MIX_CASES = [
 ]
 
 
+MIX_VARIANTS = {   # environment of each bf16 mixing variant
+    "resident": {},
+    "per-tile": {"MHLA_MIX_RESIDENT": "0"},
+}
+
+
 @pytest.mark.parametrize("case", MIX_CASES, ids=lambda c: c[0])
 def test_mixing_kernels(case, monkeypatch):
     """Both bf16 mixing kernels (persistent with W in registers, and one
@@ -105,12 +112,15 @@ def test_mixing_kernels(case, monkeypatch):
     ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)
     _, _, rSt, rzt = oracle.summaries(k, v, W, p.grid, p.block)
     run = Run(p, q, k, v, W)
-    for resident in ("1", "0"):
-        monkeypatch.setenv("MHLA_MIX_RESIDENT", resident)
+    for name, env in MIX_VARIANTS.items():
+        monkeypatch.delenv("MHLA_MIX_RESIDENT", raising=False)
+        for key, val in env.items():
+            monkeypatch.setenv(key, val)
+        say(f"  variant {name}: plan {mh.mhla_launch_plan(run.g, run.b)[1]}")
         out = to_host64(run.forward())
         _, _, St, zt = run.workspace()
         e_out, e_st, e_zt = rel_err(out, ref), rel_err(St, rSt), rel_err(zt, rzt)
-        say(f"  {p.name} resident={resident}: out {e_out:.2e} St {e_st:.2e} zt {e_zt:.2e}")
+        say(f"  {p.name} {name}: out {e_out:.2e} St {e_st:.2e} zt {e_zt:.2e}")
         assert e_out <= TOL[p.dtype] and e_st <= 1e-2 and e_zt <= 1e-2
 
 

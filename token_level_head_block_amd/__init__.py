@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.mhla_status_string.restype = ctypes.c_char_p
         L.mhla_check_problem.argtypes = [G, Bk, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
         L.mhla_check_problem.restype = ctypes.c_int
+        L.mhla_launch_plan.argtypes = [G, Bk, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.POINTER(ctypes.c_char_p)]
+        L.mhla_launch_plan.restype = ctypes.c_int
         L.mhla_workspace_bytes.argtypes = [G, Bk]
         L.mhla_workspace_bytes.restype = ctypes.c_size_t
         L.mhla_forward.argtypes = [vp, vp, vp, vp, G, Bk, vp, vp]
@@ -110,6 +113,14 @@ def mhla_check_problem(grid: mhla_grid, block: mhla_block):
     m, t = ctypes.c_int64(0), ctypes.c_int64(0)
     st = lib().mhla_check_problem(ctypes.byref(grid), ctypes.byref(block), ctypes.byref(m), ctypes.byref(t))
     return st, m.value, t.value
+
+
+def mhla_launch_plan(grid: mhla_grid, block: mhla_block, path: int = 0):
+    """(status, [kernel names in launch order])."""
+    n = ctypes.c_int32(0)
+    names = (ctypes.c_char_p * 3)()
+    st = lib().mhla_launch_plan(ctypes.byref(grid), ctypes.byref(block), int(path), ctypes.byref(n), names)
+    return st, [names[i].decode() for i in range(n.value)]
 
 
 def mhla_workspace_bytes(grid: mhla_grid, block: mhla_block) -> int:

@@ -606,7 +606,7 @@ __device__ __forceinline__ void split_zt(const float* z, u32x4& hi, u32x4& lo) {
 // prep_load(A) issues the loads of the block's A operands (and keeps zt raw);
 // prep_finish(A) turns raw zt into operands.  Both run after the first batch of
 // Q loads has been issued, so the latencies of St, zt and Q overlap.
-template <int D, int NWA, int PF, bool NTL, bool NTO, typename PrepLoad, typename PrepFinish>
+template <int D, int NWA, int PF, bool NTL, int MAXW, typename PrepLoad, typename PrepFinish>
 __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFinish&& prep_finish,
                                                   const uint16_t* __restrict__ Q,
                                                   uint16_t* __restrict__ O, const Geo& g, int bh,
@@ -630,7 +630,7 @@ __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFini
     // Output staging: 16 tokens x D channels per wave, rows padded by 8 elements.
     constexpr int OSTR = D + 8;
     constexpr int CPR = D / 8;   // 16-byte chunks per token row
-    __shared__ __attribute__((aligned(16))) uint16_t sout_all[8 * 16 * OSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t sout_all[MAXW * 16 * OSTR];
     uint16_t* sout = sout_all + (threadIdx.x >> 6) * (16 * OSTR);
 
     struct Raw {
@@ -686,7 +686,7 @@ __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFini
             const int okk = __shfl((int)R.ok, tt, 64);
             const u32x4 x = *reinterpret_cast<const u32x4*>(sout + tt * OSTR + chunk * 8);
             const uint32_t bo = okk ? (uint32_t)(offk * 2 + olane + chunk * 16) : 0x80000000u;
-            __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, bo, 0, NTO ? 2 : 0);   // 2: nt
+            __builtin_amdgcn_raw_buffer_store_b128(x, orsrc, bo, 0, 0);
         }
     };
 
@@ -730,9 +730,9 @@ __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFini
 }
 
 // Workgroup = query block i of batch b for G consecutive heads x NWA waves
-// splitting the block's tokens.
-template <int D, int NWA, int PF, bool NTL, bool NTO>
-__global__ __launch_bounds__(512) void query_apply_bf16(const uint16_t* __restrict__ Q,
+// splitting the block's tokens, at most MAXW waves.
+template <int D, int NWA, int PF, bool NTL, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void query_apply_bf16(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ St,
                                                         const float* __restrict__ Zt,
                                                         uint16_t* __restrict__ O, const Geo g) {
@@ -769,7 +769,7 @@ __global__ __launch_bounds__(512) void query_apply_bf16(const uint16_t* __restri
             split_zt(z, A.zhi[kk], A.zlo[kk]);
         }
     };
-    apply_tokens_bf16<D, NWA, PF, NTL, NTO>(prep_load, prep_finish, Q, O, g, bh, i, wave, lane);
+    apply_tokens_bf16<D, NWA, PF, NTL, MAXW>(prep_load, prep_finish, Q, O, g, bh, i, wave, lane);
 }
 
 // =====================================================================
@@ -850,7 +850,7 @@ __global__ __launch_bounds__(256) void query_apply_fused_bf16(const uint16_t* __
             split_zt(z, A.zhi[kk], A.zlo[kk]);
         }
     };
-    apply_tokens_bf16<D, 4, 2, false, false>(prep_load, prep_finish, Q, O, g, bh, i, wave, lane);
+    apply_tokens_bf16<D, 4, 2, false, 4>(prep_load, prep_finish, Q, O, g, bh, i, wave, lane);
 }
 
 // =====================================================================
@@ -862,8 +862,8 @@ inline void record(const Launch& L, int k) {
 
 // Head groups: G heads per workgroup with `per_head` waves each, at most 8
 // waves, with the heads spread evenly over the groups.
-inline Geo with_head_groups(Geo g, int per_head) {
-    const int gmax = 8 / per_head;
+inline Geo with_head_groups(Geo g, int per_head, int max_waves = 8) {
+    const int gmax = max_waves / per_head;
     g.HG = (g.H + gmax - 1) / gmax;
     g.G = (g.H + g.HG - 1) / g.HG;
     g.div_HG = make_fastdiv((uint32_t)g.HG);
@@ -887,25 +887,20 @@ void launch_summary(const Launch& L, const uint16_t* k, const uint16_t* v, uint1
             k, v, sz, g, L.W, static_cast<uint16_t*>(L.wb), w);
 }
 
-template <int D, int NWA, int PF>
-void launch_apply_pf(const Launch& L, const Geo& g, const uint16_t* q, const uint16_t* st, uint16_t* o) {
+template <int D, int NWA, int PF, int MAXW>
+void launch_apply_pf(const Launch& L, const uint16_t* q, const uint16_t* st, uint16_t* o) {
+    const Geo g = with_head_groups(L.g, NWA, MAXW);
     const int grid = g.B * g.M * g.HG, block = 64 * NWA * g.G;
-    if (L.tune.nt_apply) {
-        if (L.tune.nt_stores) query_apply_bf16<D, NWA, PF, true, true><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
-        else query_apply_bf16<D, NWA, PF, true, false><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
-    } else {
-        if (L.tune.nt_stores) query_apply_bf16<D, NWA, PF, false, true><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
-        else query_apply_bf16<D, NWA, PF, false, false><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
-    }
+    if (L.tune.nt_apply) query_apply_bf16<D, NWA, PF, true, MAXW><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
+    else query_apply_bf16<D, NWA, PF, false, MAXW><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
 }
 
 template <int D, int NWA>
 void launch_apply(const Launch& L, const uint16_t* q, const uint16_t* st, uint16_t* o) {
-    const Geo g = with_head_groups(L.g, NWA);
     switch (L.tune.apply_pf) {
-        case 1: launch_apply_pf<D, NWA, 1>(L, g, q, st, o); break;
-        case 2: launch_apply_pf<D, NWA, 2>(L, g, q, st, o); break;
-        default: launch_apply_pf<D, NWA, 4>(L, g, q, st, o); break;
+        case 1: launch_apply_pf<D, NWA, 1, 8>(L, q, st, o); break;
+        case 2: launch_apply_pf<D, NWA, 2, 8>(L, q, st, o); break;
+        default: launch_apply_pf<D, NWA, 4, 8>(L, q, st, o); break;
     }
 }
 

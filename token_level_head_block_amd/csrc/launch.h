@@ -14,7 +14,6 @@ struct Tuning {
     int apply_pf;        // bf16 path: 16-token groups of Q loads in flight per wave (1, 2, 4)
     int nt_loads;        // bf16 path: non-temporal hint on the loads of k, v (summary kernel)
     int nt_apply;        // bf16 path: non-temporal hint on the loads of q (apply kernel)
-    int nt_stores;       // bf16 path: non-temporal hint on the stores of out
     int mix_resident;    // bf16 path, M <= 256: persistent mixing kernel with W in registers
     int num_cus;         // compute units of the current device (persistent grid size)
 };

@@ -99,8 +99,10 @@ mhla::Tuning choose_tuning(const Shape& s) {
     // setup, enough waves to keep loads in flight.
     t.summary_waves = 1;
     t.summary_pf = 1;
-    t.apply_waves = s.T >= 128 ? 2 : 1;
-    t.apply_pf = s.D == 128 ? 1 : 2;   // d = 128 keeps 32 operand registers per row tile live
+    t.apply_waves = s.T >= 128 ? 4 : 1;
+    // d = 128 keeps 32 operand registers per row tile live; with 4 waves per
+    // block, one group in flight per wave is enough.
+    t.apply_pf = (s.D == 128 || s.T >= 128) ? 1 : 2;
     // Overrides for launch-shape sweeps.
     const int sw = env_int("MHLA_SUMMARY_WAVES", 0), aw = env_int("MHLA_APPLY_WAVES", 0);
     const int sp = env_int("MHLA_SUMMARY_PF", 0), ap = env_int("MHLA_APPLY_PF", 0);
@@ -112,7 +114,6 @@ mhla::Tuning choose_tuning(const Shape& s) {
     // slower for the apply kernel's q stream (measured on MI355X).
     t.nt_loads = env_int("MHLA_NT_LOADS", 1) != 0;
     t.nt_apply = env_int("MHLA_NT_APPLY", 0) != 0;
-    t.nt_stores = env_int("MHLA_NT_STORES", 0) != 0;
     t.mix_resident = env_int("MHLA_MIX_RESIDENT", 1) != 0;
     t.num_cus = 256;
     return t;
@@ -222,6 +223,29 @@ mhla_status mhla_check_problem(const mhla_grid* grid, const mhla_block* block, i
         if (block_tokens) *block_tokens = s.T;
     }
     return st;
+}
+
+mhla_status mhla_launch_plan(const mhla_grid* grid, const mhla_block* block, int32_t path,
+                             int32_t* num_kernels, const char** kernel_names) {
+    Shape s;
+    const mhla_status st = check(grid, block, &s);
+    if (st != MHLA_OK) return st;
+    if (path != MHLA_PATH_3KERNEL && path != MHLA_PATH_FUSED) return MHLA_ERR_INVALID_ARG;
+    const char* names[3] = {nullptr, nullptr, nullptr};
+    int n = 0;
+    if (s.B != 0 && s.H != 0) {
+        names[n++] = "block_kv_summary";
+        if (path == MHLA_PATH_FUSED) {
+            names[n++] = "query_apply_fused";
+        } else {
+            names[n++] = "mix_summaries";
+            names[n++] = "query_apply";
+        }
+    }
+    if (num_kernels) *num_kernels = n;
+    if (kernel_names)
+        for (int i = 0; i < 3; ++i) kernel_names[i] = names[i];
+    return MHLA_OK;
 }
 
 size_t mhla_workspace_bytes(const mhla_grid* grid, const mhla_block* block) {
