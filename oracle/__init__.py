@@ -1,4 +1,4 @@
-"""CPU oracle of the MHLA forward pass (float64).
+"""CPU oracle of the MHLA forward pass and its gradients (float64).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  It shares no code
@@ -77,6 +77,8 @@ def _load():
         lib.mhla_oracle_summaries.argtypes = [vp, vp, fp, P, ip, ctypes.c_int32,
                                               dp, dp, dp, dp, ctypes.c_int32]
         lib.mhla_oracle_summaries.restype = ctypes.c_int
+        lib.mhla_oracle_backward.argtypes = [vp, vp, vp, fp, vp, P, dp, dp, dp, dp, ctypes.c_int32, ip]
+        lib.mhla_oracle_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -189,6 +191,27 @@ def summaries(k, v, W, grid, block, pairs=None, threads=0):
     if rc != 0:
         raise ValueError("oracle rejected the problem")
     return S, z, St, zt
+
+
+def backward(q, k, v, W, dout, grid, block, eps=1e-6, threads=0, return_threads=False):
+    """Blockwise float64 gradients for upstream gradient dout (same dtype and
+    shape as q): (dq, dk, dv) [B, N, H, d] and dW [M, M], all float64."""
+    q, k, v, W, B, N, H, d, dt = _prep(q, k, v, W, grid, block)
+    dout = np.ascontiguousarray(dout)
+    if dout.shape != q.shape or dout.dtype != q.dtype:
+        raise ValueError("dout must match q in shape and dtype")
+    p = _problem(grid, block, H, d, B, dt, eps)
+    M = num_blocks(grid, block)
+    dq, dk, dv = (np.empty((B, N, H, d)) for _ in range(3))
+    dW = np.empty((M, M))
+    dp = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    used = ctypes.c_int32(0)
+    rc = _load().mhla_oracle_backward(
+        _ptr(q), _ptr(k), _ptr(v), W.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(dout),
+        ctypes.byref(p), dp(dq), dp(dk), dp(dv), dp(dW), threads, ctypes.byref(used))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return ((dq, dk, dv, dW), used.value) if return_threads else (dq, dk, dv, dW)
 
 
 # ---------------------------------------------------------------------------

@@ -236,3 +236,191 @@ int mhla_oracle_summaries(const void* k, const void* v, const float* W,
                           double* S, double* z, double* St, double* zt, int32_t threads) {
     return run_all(NULL, k, v, W, p, sel, nsel, NULL, S, z, St, zt, threads, NULL);
 }
+
+/* =====================================================================
+ * Backward pass (gradients of a scalar loss L with upstream gradient
+ * g_n = dL/do_n).  The coefficient matrix W is a learned parameter of the
+ * method (paperlayer.ai summary, section 4 "Multi-Head Mixing"), so the
+ * gradient covers q, k, v and W.  Each step is the chain rule applied to the
+ * forward definition above, in the forward's notation, u = phi(q), a = phi(k):
+ *
+ *   den_n = u_n . zt_i + eps,   o_n = St_i^T u_n / den_n
+ *   dnum_n = g_n / den_n,       dden_n = -(g_n . o_n) / den_n
+ *   du_n   = St_i dnum_n + zt_i dden_n,        dq_n = du_n * phi'(q_n)
+ *   dSt_i  = sum_{n in i} u_n dnum_n^T,        dzt_i = sum_{n in i} u_n dden_n
+ *   dS_j   = sum_i W[i,j] dSt_i,               dz_j  = sum_i W[i,j] dzt_i
+ *   dW[i,j] = sum over (b, h) of <dSt_i, S_j> + <dzt_i, z_j>
+ *   dv_m   = dS_j^T a_m,   da_m = dS_j v_m + dz_j,   dk_m = da_m * phi'(k_m)
+ *
+ * with phi'(x) = 1 for x > 0 and exp(x) otherwise.
+ * ===================================================================== */
+
+static double phi_grad(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+typedef struct {
+    const void *q, *k, *v, *dout;
+    const float* W;
+    const mhla_oracle_problem* p;
+    const geom* G;
+    double *dq, *dk, *dv;   /* [B][N][H][d] */
+    double* dWp;            /* this pair's share of dW, [M][M] */
+} bwd_job;
+
+static void run_pair_backward(const bwd_job* J, int32_t b, int32_t h) {
+    const geom* G = J->G;
+    const int64_t H = J->p->heads, d = J->p->head_dim, N = G->N, M = G->M;
+    const int dt = J->p->dtype;
+    const int64_t row = H * d;
+    const int64_t base = (int64_t)b * N * row + (int64_t)h * d;
+
+    double* S = calloc((size_t)(M * d * d), sizeof(double));
+    double* z = calloc((size_t)(M * d), sizeof(double));
+    double* St = calloc((size_t)(M * d * d), sizeof(double));
+    double* zt = calloc((size_t)(M * d), sizeof(double));
+    double* dSt = calloc((size_t)(M * d * d), sizeof(double));
+    double* dzt = calloc((size_t)(M * d), sizeof(double));
+    double* dS = calloc((size_t)(M * d * d), sizeof(double));
+    double* dz = calloc((size_t)(M * d), sizeof(double));
+    double* x = malloc((size_t)d * sizeof(double));    /* raw q or k of one token */
+    double* u = malloc((size_t)d * sizeof(double));    /* phi of it */
+    double* y = malloc((size_t)d * sizeof(double));    /* v or g of one token */
+    double* t1 = malloc((size_t)d * sizeof(double));
+    if (!S || !z || !St || !zt || !dSt || !dzt || !dS || !dz || !x || !u || !y || !t1) abort();
+
+    /* Forward summaries and their mixture, as in the forward pass. */
+    for (int64_t m = 0; m < N; ++m) {
+        int64_t j = block_of(G, m);
+        for (int64_t c = 0; c < d; ++c) u[c] = mhla_oracle_phi(load_elem(J->k, dt, base + m * row + c));
+        for (int64_t e = 0; e < d; ++e) y[e] = load_elem(J->v, dt, base + m * row + e);
+        for (int64_t c = 0; c < d; ++c) {
+            z[j * d + c] += u[c];
+            for (int64_t e = 0; e < d; ++e) S[j * d * d + c * d + e] += u[c] * y[e];
+        }
+    }
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < M; ++j) {
+            double w = (double)J->W[i * M + j];
+            for (int64_t t = 0; t < d * d; ++t) St[i * d * d + t] += w * S[j * d * d + t];
+            for (int64_t c = 0; c < d; ++c) zt[i * d + c] += w * z[j * d + c];
+        }
+
+    /* Query side: gradient of q, and the gradients of the mixed summaries. */
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t i = block_of(G, n);
+        const double* Sti = St + i * d * d;
+        const double* zti = zt + i * d;
+        for (int64_t c = 0; c < d; ++c) {
+            x[c] = load_elem(J->q, dt, base + n * row + c);
+            u[c] = mhla_oracle_phi(x[c]);
+        }
+        for (int64_t e = 0; e < d; ++e) y[e] = load_elem(J->dout, dt, base + n * row + e);
+        double den = J->p->eps;
+        for (int64_t c = 0; c < d; ++c) den += u[c] * zti[c];
+        double go = 0.0;   /* g . o */
+        for (int64_t e = 0; e < d; ++e) {
+            double num = 0.0;
+            for (int64_t c = 0; c < d; ++c) num += u[c] * Sti[c * d + e];
+            go += y[e] * (num / den);
+        }
+        const double dden = -go / den;
+        for (int64_t e = 0; e < d; ++e) t1[e] = y[e] / den;   /* dnum */
+        for (int64_t c = 0; c < d; ++c) {
+            double du = zti[c] * dden;
+            for (int64_t e = 0; e < d; ++e) du += Sti[c * d + e] * t1[e];
+            J->dq[base + n * row + c] = du * phi_grad(x[c]);
+            dzt[i * d + c] += u[c] * dden;
+            for (int64_t e = 0; e < d; ++e) dSt[i * d * d + c * d + e] += u[c] * t1[e];
+        }
+    }
+
+    /* Mixing, transposed: every source block collects the gradients of the
+     * query blocks that read it; dW pairs each query block's gradient with
+     * each source block's summary. */
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < M; ++j) {
+            double w = (double)J->W[i * M + j];
+            double acc = 0.0;
+            for (int64_t t = 0; t < d * d; ++t) {
+                dS[j * d * d + t] += w * dSt[i * d * d + t];
+                acc += dSt[i * d * d + t] * S[j * d * d + t];
+            }
+            for (int64_t c = 0; c < d; ++c) {
+                dz[j * d + c] += w * dzt[i * d + c];
+                acc += dzt[i * d + c] * z[j * d + c];
+            }
+            J->dWp[i * M + j] = acc;
+        }
+
+    /* Key / value side. */
+    for (int64_t m = 0; m < N; ++m) {
+        int64_t j = block_of(G, m);
+        const double* dSj = dS + j * d * d;
+        for (int64_t c = 0; c < d; ++c) {
+            x[c] = load_elem(J->k, dt, base + m * row + c);
+            u[c] = mhla_oracle_phi(x[c]);
+        }
+        for (int64_t e = 0; e < d; ++e) y[e] = load_elem(J->v, dt, base + m * row + e);
+        for (int64_t e = 0; e < d; ++e) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < d; ++c) acc += u[c] * dSj[c * d + e];
+            J->dv[base + m * row + e] = acc;
+        }
+        for (int64_t c = 0; c < d; ++c) {
+            double acc = dz[j * d + c];
+            for (int64_t e = 0; e < d; ++e) acc += dSj[c * d + e] * y[e];
+            J->dk[base + m * row + c] = acc * phi_grad(x[c]);
+        }
+    }
+    free(S); free(z); free(St); free(zt); free(dSt); free(dzt); free(dS); free(dz);
+    free(x); free(u); free(y); free(t1);
+}
+
+typedef struct {
+    bwd_job proto;
+    double* dWparts;   /* [B*H][M][M] */
+    int32_t pairs, nthreads, tid;
+} bwd_worker_arg;
+
+static void* bwd_worker(void* arg) {
+    const bwd_worker_arg* A = (const bwd_worker_arg*)arg;
+    const int64_t M = A->proto.G->M, H = A->proto.p->heads;
+    for (int32_t s = A->tid; s < A->pairs; s += A->nthreads) {
+        bwd_job J = A->proto;
+        J.dWp = A->dWparts + (int64_t)s * M * M;
+        run_pair_backward(&J, (int32_t)(s / H), (int32_t)(s % H));
+    }
+    return NULL;
+}
+
+int mhla_oracle_backward(const void* q, const void* k, const void* v, const float* W, const void* dout,
+                         const mhla_oracle_problem* p, double* dq, double* dk, double* dv, double* dW,
+                         int32_t threads, int32_t* threads_used) {
+    geom G;
+    if (make_geom(p, &G) != 0) return -1;
+    const int64_t pairs = (int64_t)p->batch * p->heads, M = G.M;
+    if (pairs > 0 && (!q || !k || !v || !W || !dout || !dq || !dk || !dv)) return -1;
+    if (!dW) return -1;
+    if (threads <= 0) threads = (int32_t)sysconf(_SC_NPROCESSORS_ONLN);
+    if (threads < 1) threads = 1;
+    if (threads > pairs) threads = pairs > 0 ? (int32_t)pairs : 1;
+    if (threads_used) *threads_used = threads;
+    for (int64_t t = 0; t < M * M; ++t) dW[t] = 0.0;
+    if (pairs == 0) return 0;
+    double* parts = malloc((size_t)(pairs * M * M) * sizeof(double));
+    pthread_t* tids = malloc(sizeof(pthread_t) * (size_t)threads);
+    bwd_worker_arg* args = malloc(sizeof(bwd_worker_arg) * (size_t)threads);
+    if (!parts || !tids || !args) abort();
+    for (int32_t t = 0; t < threads; ++t) {
+        bwd_worker_arg a = {{q, k, v, dout, W, p, &G, dq, dk, dv, NULL}, parts, (int32_t)pairs, threads, t};
+        args[t] = a;
+    }
+    for (int32_t t = 1; t < threads; ++t) pthread_create(&tids[t], NULL, bwd_worker, &args[t]);
+    bwd_worker(&args[0]);
+    for (int32_t t = 1; t < threads; ++t) pthread_join(tids[t], NULL);
+    /* Sum the pairs' shares in pair order, so the result does not depend on
+     * the thread count. */
+    for (int64_t s = 0; s < pairs; ++s)
+        for (int64_t t = 0; t < M * M; ++t) dW[t] += parts[s * M * M + t];
+    free(parts); free(tids); free(args);
+    return 0;
+}

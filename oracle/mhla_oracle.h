@@ -69,6 +69,15 @@ int mhla_oracle_summaries(const void* k, const void* v, const float* W,
                           const mhla_oracle_problem* p, const int32_t* sel, int32_t nsel,
                           double* S, double* z, double* St, double* zt, int32_t threads);
 
+/* Gradients of a scalar loss with upstream gradient dout = dL/dout ([B, N,
+ * H, d], same dtype and layout as q): dq, dk, dv [B, N, H, d] float64 and
+ * dW [M, M] float64 (summed over every (b, h) pair in pair order).  Chain rule
+ * on the forward above; W is a learned parameter of the method (section 4
+ * "Multi-Head Mixing"). */
+int mhla_oracle_backward(const void* q, const void* k, const void* v, const float* W, const void* dout,
+                         const mhla_oracle_problem* p, double* dq, double* dk, double* dv, double* dW,
+                         int32_t threads, int32_t* threads_used);
+
 #ifdef __cplusplus
 }
 #endif
