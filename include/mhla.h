@@ -157,6 +157,52 @@ mhla_status mhla_forward_ex(const void* q, const void* k, const void* v, const f
                             void* ws, size_t ws_bytes, int32_t path,
                             const hipEvent_t* stage_events, hipStream_t stream);
 
+/* ---------------------------------------------------------------- backward
+ *
+ * Gradients of a scalar loss L through the forward pass above, given the
+ * upstream gradient dout = dL/dout: dq, dk, dv (dL/dq, dL/dk, dL/dv) and dW
+ * (dL/dW).  W is a learned parameter of the method (paperlayer.ai summary,
+ * section 4 "Multi-Head Mixing").  With u = phi(q_n), a = phi(k_m), g = dout_n
+ * and the forward's S_j, z_j, St_i, zt_i:
+ *
+ *   den = u . zt_i + eps,  dnum = g / den,  dden = -(g . o_n) / den
+ *   dq_n   = (St_i dnum + zt_i dden) * phi'(q_n)
+ *   dSt_i  = sum_{n in i} u dnum^T,  dzt_i = sum_{n in i} u dden
+ *   dS_j   = sum_i W[i,j] dSt_i,     dz_j  = sum_i W[i,j] dzt_i
+ *   dW[i,j] = sum over (b, h) of <dSt_i, S_j> + <dzt_i, z_j>
+ *   dv_m   = dS_j^T a,  dk_m = (dS_j v_m + dz_j) * phi'(k_m)
+ *
+ * with phi'(x) = 1 for x > 0 and exp(x) otherwise.
+ *
+ * Supported: bfloat16 problems with head_dim 32 or 64 (MHLA_ERR_UNSUPPORTED
+ * otherwise).  q, k, v, dout, dq, dk, dv: [B, N, H, d] bfloat16 as for the
+ * forward; W: fp32 [M, M] (read); dW: fp32 [M, M], overwritten (zero for an
+ * empty problem).  All device pointers, 16-byte aligned, owned by the caller;
+ * no output may overlap an input or another output.  Products in bf16 MFMA
+ * with fp32 accumulation; the forward summaries are recomputed; gradients of
+ * the summaries are kept in bf16.  Asynchronous on `stream`. */
+
+/* Bytes of device workspace mhla_backward needs (0 for an unsupported, invalid
+ * or empty problem).  Layout from the start: the forward's regions 0-3 (see
+ * mhla_workspace_bytes), then at 256-byte boundaries: gradients of the mixed
+ * summaries as B*H*M bf16 records in the summaries' layout; gradients of the
+ * summaries, B*H*M*d*d bf16 ([e][c] order); gradients of the normalisers,
+ * B*H*M*d fp32; W^T in the mixing kernel's operand order; dW partial sums. */
+size_t mhla_backward_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
+
+/* The backward pass, enqueued on `stream`.  ws: workspace of ws_bytes >=
+ * mhla_backward_workspace_bytes (16-byte aligned), or NULL with ws_bytes 0 to
+ * allocate it on the stream (hipMallocAsync / hipFreeAsync).  stage_events:
+ * NULL or 5 caller-created events recorded before the first kernel, after the
+ * forward recompute (summary and mixing kernels), after the query-side kernel
+ * (dq and the gradients of the mixed summaries), after the transposed mixing
+ * and dW kernels, and after the key/value-side kernel (dk, dv).  Returns the
+ * same codes as mhla_forward_ex. */
+mhla_status mhla_backward(const void* q, const void* k, const void* v, const float* W, const void* dout,
+                          const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
+                          float* dW, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
+                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

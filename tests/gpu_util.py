@@ -54,6 +54,22 @@ class Run:
         torch.cuda.synchronize()
         return out
 
+    def backward(self, dout_host, stream=None, ws=True):
+        """Gradients through mhla_backward: (dq, dk, dv) device tensors like q and dW [M, M] fp32."""
+        p = self.p
+        dout = to_dev(dout_host, p.dtype)
+        dq, dk, dv = (torch.empty_like(self.q) for _ in range(3))
+        M = p.n_blocks
+        dW = torch.empty(M, M, dtype=torch.float32, device="cuda")
+        wsb = mh.mhla_backward_workspace_bytes(self.g, self.b)
+        wst = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if ws else None
+        say(f"  [gpu] mhla_backward {p.name} B{p.batch} H{p.heads} d{p.head_dim} grid{p.grid} block{p.block}")
+        st = mh.mhla_backward(self.q, self.k, self.v, self.W, dout, self.g, self.b, dq, dk, dv, dW,
+                              wst, wsb if ws else 0, None, stream)
+        assert st == mh.MHLA_OK, mh.mhla_status_string(st)
+        torch.cuda.synchronize()
+        return dq, dk, dv, dW
+
     def workspace(self):
         """Intermediates from the workspace after a 3-kernel call:
         (S [P,M,d,d] as [c][e], z [P,M,d], St [P,M,d,d] as [c][e], zt [P,M,d]) in float64."""

@@ -143,3 +143,31 @@ def test_launch_plan(L):
     assert mh.mhla_launch_plan(mh.make_grid(0, 6, 64, mh.MHLA_BF16, (256, 256)), b) == (mh.MHLA_OK, [])
     assert mh.mhla_launch_plan(g, b, 7)[0] == mh.MHLA_ERR_INVALID_ARG
     assert mh.mhla_launch_plan(g, mh.make_block((15, 16)))[0] == mh.MHLA_ERR_INVALID_ARG
+
+
+def test_backward_workspace_and_validation(L):
+    g, b = cfg2()
+    need = mh.mhla_backward_workspace_bytes(g, b)
+    assert need > mh.mhla_workspace_bytes(g, b)
+    # unsupported: d = 128, fp32
+    g128 = mh.make_grid(1, 12, 128, mh.MHLA_BF16, (16, 64, 64))
+    assert mh.mhla_backward_workspace_bytes(g128, mh.make_block((4, 8, 8))) == 0
+    g32 = mh.make_grid(1, 1, 32, mh.MHLA_F32, (16, 16))
+    assert mh.mhla_backward_workspace_bytes(g32, mh.make_block((4, 4))) == 0
+
+    def bwd(g_, b_, q=BIG, k=2 * BIG, v=3 * BIG, W=4 * BIG, dout=5 * BIG, dq=6 * BIG, dk=7 * BIG,
+            dv=8 * BIG, dW=9 * BIG, ws=10 * BIG, ws_bytes=None):
+        wsb = mh.mhla_backward_workspace_bytes(g_, b_) if ws_bytes is None else ws_bytes
+        return L.mhla_backward(q, k, v, W, dout, ctypes.byref(g_), ctypes.byref(b_), dq, dk, dv, dW, ws, wsb,
+                               None, None)
+
+    assert bwd(g128, mh.make_block((4, 8, 8)), ws_bytes=1 << 30) == mh.MHLA_ERR_UNSUPPORTED
+    assert bwd(g32, mh.make_block((4, 4)), ws_bytes=1 << 30) == mh.MHLA_ERR_UNSUPPORTED
+    assert bwd(g, b, dout=None) == mh.MHLA_ERR_INVALID_ARG
+    assert bwd(g, b, dW=None) == mh.MHLA_ERR_INVALID_ARG
+    assert bwd(g, b, dk=7 * BIG + 8) == mh.MHLA_ERR_MISALIGNED
+    assert bwd(g, b, dq=BIG + 4096) == mh.MHLA_ERR_INVALID_ARG          # dq overlaps q
+    assert bwd(g, b, dv=6 * BIG + 64) == mh.MHLA_ERR_INVALID_ARG        # dv overlaps dq
+    assert bwd(g, b, ws_bytes=need - 16) == mh.MHLA_ERR_INVALID_ARG
+    assert bwd(g, b, ws=9 * BIG) == mh.MHLA_ERR_INVALID_ARG             # workspace overlaps dW
+    assert bwd(g, mh.make_block((15, 16))) == mh.MHLA_ERR_INVALID_ARG

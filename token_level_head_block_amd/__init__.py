@@ -70,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.mhla_launch_plan.argtypes = [G, Bk, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                        ctypes.POINTER(ctypes.c_char_p)]
         L.mhla_launch_plan.restype = ctypes.c_int
+        L.mhla_backward_workspace_bytes.argtypes = [G, Bk]
+        L.mhla_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.mhla_backward.argtypes = [vp, vp, vp, vp, vp, G, Bk, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+        L.mhla_backward.restype = ctypes.c_int
         L.mhla_workspace_bytes.argtypes = [G, Bk]
         L.mhla_workspace_bytes.restype = ctypes.c_size_t
         L.mhla_forward.argtypes = [vp, vp, vp, vp, G, Bk, vp, vp]
@@ -200,6 +204,33 @@ def mhla_forward_ex(q, k, v, W, grid: mhla_grid, block: mhla_block, out, ws, ws_
     return lib().mhla_forward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(W), ctypes.byref(grid),
                                  ctypes.byref(block), _ptr(out), _ptr(ws), int(ws_bytes), int(path),
                                  ev, _stream(stream))
+
+
+def mhla_backward_workspace_bytes(grid: mhla_grid, block: mhla_block) -> int:
+    return int(lib().mhla_backward_workspace_bytes(ctypes.byref(grid), ctypes.byref(block)))
+
+
+def _events(stage_events, n):
+    if stage_events is None:
+        return None
+    if len(stage_events) != n:
+        raise ValueError(f"stage_events needs {n} events")
+    arr = (ctypes.c_void_p * n)(*[e if isinstance(e, int) else e.cuda_event for e in stage_events])
+    if any(a is None or a == 0 for a in arr):
+        raise ValueError("stage events have no HIP handle yet; record each once first")
+    return ctypes.cast(arr, ctypes.c_void_p)
+
+
+def mhla_backward(q, k, v, W, dout, grid: mhla_grid, block: mhla_block, dq, dk, dv, dW, ws=None,
+                  ws_bytes: int = 0, stage_events=None, stream=None) -> int:
+    """Gradients dq, dk, dv (bf16 tensors like q) and dW (fp32 [M, M]) for the
+    upstream gradient dout.  stage_events: None or 5 events (torch.cuda.Event
+    already recorded once, or raw hipEvent_t handles)."""
+    _check_tensors(q, k, v, W, dout, grid, block)
+    _check_tensors(dq, dk, dv, dW, None, grid, block)
+    return lib().mhla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dout), ctypes.byref(grid),
+                               ctypes.byref(block), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), _ptr(ws),
+                               int(ws_bytes), _events(stage_events, 5), _stream(stream))
 
 
 # ---------------------------------------------------------------- convenience

@@ -19,77 +19,12 @@
 // Output layout of a 16x16 MFMA tile (f32x4 per lane): lane l holds rows
 // 4*(l/16) + v, v = 0..3, of column l % 16.
 #include "launch.h"
+#include "bf16_shared.h"
 
 #include <mhla.h>
 
 namespace mhla {
 namespace {
-
-// Loads of data read exactly once (q, k, v) may carry the non-temporal hint
-// so they do not displace the summaries in the caches.
-template <bool NT, typename T>
-__device__ __forceinline__ T ld(const T* p) {
-    if constexpr (NT) return __builtin_nontemporal_load(p);
-    else return *p;
-}
-
-// =====================================================================
-// Software pipeline: iterations first, first + step, ... < n (n >= 1), with
-// the loads of PF later iterations in flight while one is computed.  Buffers
-// rotate with compile-time indices so they stay in registers.  Every load is
-// issued unconditionally (indices past the end are clamped to the last
-// iteration and the data ignored): a load under a branch would make the
-// compiler's wait counts conservative and drain the prefetched loads too.
-// =====================================================================
-template <int PF, typename Buf, typename LoadF, typename ComputeF>
-__device__ __forceinline__ void pipelined(int first, int step, int n, LoadF&& load, ComputeF&& compute) {
-    Buf buf[PF + 1];
-    const int last = n - 1;
-#pragma unroll
-    for (int s = 0; s < PF; ++s) load(min(first + s * step, last), buf[s]);
-    for (int base = first; base < n; base += step * (PF + 1)) {
-#pragma unroll
-        for (int u = 0; u <= PF; ++u) {
-            const int it = base + u * step;
-            if (it >= n) break;
-            load(min(it + PF * step, last), buf[(u + PF) % (PF + 1)]);
-            __builtin_amdgcn_sched_barrier(0);   // issue the prefetch before computing
-            compute(buf[u]);
-        }
-    }
-}
-
-// W (fp32 [M][M]) -> bf16, zero padded to [Ipad = 64 * IT][Jpad = 32 * NK] and
-// stored in the mixing kernel's B-operand order: 16-byte unit
-// (rt * NK + kk) * 64 + lane holds W[16 * rt + lane % 16][32 * kk + 8 * (lane / 16) + 0..7],
-// so each wave's operand loads are contiguous.  Done by extra workgroups
-// appended to the summary launch, so the summary workgroups never wait on it.
-struct WConv {
-    int32_t M, NK, nchunks;   // NK = Jpad / 32; nchunks = Ipad * Jpad / 8; 0 = none
-    int32_t first_wg;         // workgroups [first_wg, gridDim.x) convert
-};
-
-__device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t* __restrict__ Wb,
-                                          const WConv& wc) {
-    const int nthr = (gridDim.x - wc.first_wg) * blockDim.x;
-    for (int c = (blockIdx.x - wc.first_wg) * blockDim.x + threadIdx.x; c < wc.nchunks; c += nthr) {
-        const int lane = c & 63, rk = c >> 6;
-        const int rt = rk / wc.NK, kk = rk - rt * wc.NK;
-        const int i = 16 * rt + (lane & 15), j0 = 32 * kk + 8 * (lane >> 4);
-        float x[8];
-        if (i < wc.M && (wc.M & 7) == 0 && j0 < wc.M) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(W + (size_t)i * wc.M + j0);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(W + (size_t)i * wc.M + j0 + 4);
-            x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-            x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-        } else {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)i * wc.M + j0 + s] : 0.f;
-        }
-        *reinterpret_cast<u32x4*>(Wb + (size_t)c * 8) =
-            u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
-    }
-}
 
 // =====================================================================
 // block_kv_summary
@@ -258,173 +193,14 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
 }
 
 // =====================================================================
-// mix_summaries:  C[col'][i] = sum_j [S|z]_j[col'] W[i][j]  per (b, h).
-// Workgroup of 8 waves = CPW column tiles (64 record elements col' each) x
-// all query blocks i.  The A operand (records of the CPW tiles, up to 256
-// source blocks per pass) is staged once in LDS, already packed as MFMA
-// operands; wave (c, it, th) computes 64 col' x 32 i (i = it*64 + 32*th + ..)
-// with all of its W operands (bf16, padded and laid out in operand order by
-// the summary kernel's extra workgroups) loaded from L2 around the staging.
-// Lane (li, gq): A rows col' = 4*li + r, B column i = 16*t + li.
-// Mixed S tiles leave through LDS so that every store writes whole 128-byte
-// record rows; mixed z (fp32) is stored directly.
+// mix_summaries (one workgroup per work unit), for any M.
 // =====================================================================
-struct MixGeo {
-    int32_t CT, IT, CPW, CTG, Jpad;   // column tiles, i tiles, column tiles per WG, WG per bh, padded j
-    FastDiv div_CTG;
-};
-
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void mix_summaries_bf16(
     const uint16_t* __restrict__ SZ, const uint16_t* __restrict__ Wb, uint16_t* __restrict__ St,
     float* __restrict__ Zt, const Geo g, const MixGeo mg) {
-    constexpr int REC = D * D + D;
-    constexpr int KSP = 8;          // k-steps (32 source blocks) per staging pass
-    constexpr int OROW = 72;        // output staging row: 64 bf16 + 8 padding
-    // A operands [tile c][r][kk][lane] (cpw * nkp <= 8: 32 KB), reused for the
-    // output transpose (8 waves x 32 rows x OROW bf16 = 36 KB).
-    __shared__ u32x4 sA[8 * 32 * OROW / 8];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int li = lane & 15, gq = lane >> 4;
-    const uint32_t wg = blockIdx.x;
-    const uint32_t bh = fdiv(wg, mg.div_CTG);
-    const int ctg = (int)(wg - bh * mg.div_CTG.d);
-    const int M = g.M;
-    const int NK = (M + 31) >> 5;
-    const int cpw = mg.CPW;
-    const int itr = mg.IT < 4 ? mg.IT : 4;   // i tiles per round
-    const uint16_t* base = SZ + (size_t)bh * M * REC;
-    const int th = wave & 1, w2 = wave >> 1;
-    const int wc = w2 / itr, wit = w2 % itr;
-    const int ct = ctg * cpw + wc;
-    const bool wave_ok = (w2 < cpw * itr) && (ct < mg.CT);
-    const int cp0 = ct * 64;   // first record element of this wave's column tile
-
-    for (int iround = 0; iround * 4 < mg.IT; ++iround) {
-        const int it = iround * 4 + wit;
-        const bool active = wave_ok && it < mg.IT;
-        const int itc = it < mg.IT ? it : mg.IT - 1;   // inactive waves load a valid tile too
-        f32x4 acc[4][2];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        for (int k0 = 0; k0 < NK; k0 += KSP) {
-            const int nkp = min(KSP, NK - k0);
-            // Workgroups visit the pass's k-steps in rotated order (step kr(kk)
-            // at position kk), so that they do not all request the same W lines
-            // from L2 at the same moment.
-            const int rot = (int)(wg % (uint32_t)nkp);
-            auto kr = [&](int kk) {
-                const int x = kk + rot;
-                return kk >= nkp ? nkp - 1 : (x >= nkp ? x - nkp : x);
-            };
-            // W operands (B) of this pass: the first half before the staging of A,
-            // the second half after it; positions past nkp reload a valid step.
-            u32x4 bw[KSP][2];
-            auto load_w = [&](int kk) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    bw[kk][t] = *reinterpret_cast<const u32x4*>(
-                        Wb + ((size_t)((itc * 4 + 2 * th + t) * NK + k0 + kr(kk)) * 64 + lane) * 8);
-            };
-#pragma unroll
-            for (int kk = 0; kk < KSP / 2; ++kk) load_w(kk);
-            __syncthreads();
-            // ---- stage A: unit (tile c, li', j-group of 8) -> 4 packed operands.
-            // cpw * nkp <= 8, so there are at most 512 units: one per thread.
-            {
-                const int units = cpw * 16 * 4 * nkp;
-                const int u = tid;
-                const int lip = u & 15;
-                const int jg = (u >> 4) % (4 * nkp);
-                const int c = (u >> 4) / (4 * nkp);
-                const int colp = (ctg * cpw + c) * 64 + 4 * lip;
-                const bool ok = u < units && colp < REC && (ctg * cpw + c) < mg.CT;
-                const int colc = ok ? colp : 0;
-                u32x2 raw[8];
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    // Clamped address, then a mask: the load stays unconditional.
-                    const int jj = (k0 + (jg >> 2)) * 32 + (jg & 3) * 8 + s;
-                    const u32x2 t = *reinterpret_cast<const u32x2*>(base + (size_t)(jj < M ? jj : M - 1) * REC + colc);
-                    const uint32_t m = (ok && jj < M) ? 0xffffffffu : 0u;
-                    raw[s] = u32x2{t.x & m, t.y & m};
-                }
-                if (u < units) {
-                    const int kk = jg >> 2, lanep = (jg & 3) * 16 + lip;
-                    u32x4 op[4];
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        op[0][w] = pack_lo(raw[2 * w].x, raw[2 * w + 1].x);
-                        op[1][w] = pack_hi(raw[2 * w].x, raw[2 * w + 1].x);
-                        op[2][w] = pack_lo(raw[2 * w].y, raw[2 * w + 1].y);
-                        op[3][w] = pack_hi(raw[2 * w].y, raw[2 * w + 1].y);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sA[((c * 4 + r) * nkp + kk) * 64 + lanep] = op[r];
-                }
-            }
-#pragma unroll
-            for (int kk = KSP / 2; kk < KSP; ++kk) load_w(kk);
-            __syncthreads();
-            if (active) {
-#pragma unroll
-                for (int kk = 0; kk < KSP; ++kk) {
-                    if (kk >= nkp) break;
-                    u32x4 a[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) a[r] = sA[((wc * 4 + r) * nkp + kr(kk)) * 64 + lane];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-#pragma unroll
-                        for (int t = 0; t < 2; ++t) acc[r][t] = mfma_bf16(a[r], bw[kk][t], acc[r][t]);
-                }
-            }
-        }
-
-        // ---- output.  Lane holds C[col' = cp0 + 16*gq + 4*v + r][i = it*64 + 32*th + 16*t + li].
-        const bool s_tile = active && cp0 < D * D;
-        uint16_t* stage = reinterpret_cast<uint16_t*>(sA) + wave * (32 * OROW);
-        __syncthreads();   // every wave is done with the A operands
-        if (s_tile) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                uint32_t wv[8];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    wv[2 * v] = pack_bf16(acc[0][t][v], acc[1][t][v]);
-                    wv[2 * v + 1] = pack_bf16(acc[2][t][v], acc[3][t][v]);
-                }
-                uint16_t* dst = stage + (16 * t + li) * OROW + 16 * gq;
-                *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-                *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
-            }
-        }
-        __syncthreads();
-        if (s_tile) {
-            // 32 rows of 128 bytes: 8 lanes per row, 8 rows per instruction.
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int rl = 8 * k + (lane >> 3), chunk = lane & 7;
-                const int i = it * 64 + 32 * th + rl;
-                const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rl * OROW + chunk * 8);
-                if (i < M) *reinterpret_cast<u32x4*>(St + ((size_t)bh * M + i) * (D * D) + cp0 + chunk * 8) = x;
-            }
-        } else if (active && cp0 + 16 * gq < REC) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int i = it * 64 + 32 * th + 16 * t + li;
-                if (i >= M) continue;
-                float* dst = Zt + ((size_t)bh * M + i) * D + (cp0 + 16 * gq - D * D);
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    *reinterpret_cast<f32x4*>(dst + 4 * v) = f32x4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
-            }
-        }
-        __syncthreads();   // the staging area is reused by the next round
-    }
+    __shared__ u32x4 sA[MIX_LDS_UNITS];
+    mix_tile_bf16<D>(blockIdx.x, SZ, Wb, St, Zt, g, mg, sA);
 }
 
 // =====================================================================
@@ -586,26 +362,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
 // (split into a bf16 high part and the bf16 rounding of the remainder), so
 // every lane receives its token's phi(q) . zt_i without cross-lane sums.
 // =====================================================================
-template <int D>
-struct ApplyA {
-    static constexpr int RT = D / 16, KS = D / 32;
-    u32x4 a[RT][KS];
-    u32x4 zhi[KS], zlo[KS];
-};
-
-// zt (8 fp32 values of one k-slot group) -> hi/lo bf16 operand words.
-__device__ __forceinline__ void split_zt(const float* z, u32x4& hi, u32x4& lo) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t h = pack_bf16(z[2 * w], z[2 * w + 1]);
-        hi[w] = h;
-        lo[w] = pack_bf16(z[2 * w] - bf_lo(h), z[2 * w + 1] - bf_hi(h));
-    }
-}
-
-// prep_load(A) issues the loads of the block's A operands (and keeps zt raw);
-// prep_finish(A) turns raw zt into operands.  Both run after the first batch of
-// Q loads has been issued, so the latencies of St, zt and Q overlap.
 template <int D, int NWA, int PF, bool NTL, int MAXW, typename PrepLoad, typename PrepFinish>
 __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFinish&& prep_finish,
                                                   const uint16_t* __restrict__ Q,
@@ -921,6 +677,7 @@ hipError_t run_d(const Launch& L) {
     wc.NK = NK;
     wc.nchunks = fused ? 0 : IT * 64 * NK * 32 / 8;
     wc.first_wg = 0;
+    wc.transpose = 0;
     const bool row8 = (g.bk2 % 8) == 0;
 
     record(L, 0);
@@ -957,6 +714,7 @@ hipError_t run_d(const Launch& L) {
                 sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg);
         }
         record(L, 2);
+        if (L.summaries_only) return hipGetLastError();
         switch (L.tune.apply_waves) {
             case 1: launch_apply<D, 1>(L, q, st, o); break;
             case 2: launch_apply<D, 2>(L, q, st, o); break;
@@ -968,6 +726,14 @@ hipError_t run_d(const Launch& L) {
 }
 
 }  // namespace
+
+hipError_t run_bf16_summaries(const Launch& L) {
+    Launch S = L;
+    S.summaries_only = 1;
+    S.path = MHLA_PATH_3KERNEL;
+    S.events = nullptr;
+    return run_bf16(S);
+}
 
 hipError_t run_bf16(const Launch& L) {
     switch (L.g.D) {

@@ -1,0 +1,586 @@
+// kernels_bwd_bf16.hip -- gradients of the MHLA forward pass for bfloat16
+// inputs on gfx950 (MI355X), d = 32 or 64.
+//
+// W is a learned parameter of the method (MHLA, arXiv 2601.07832;
+// paperlayer.ai summary, section 4 "Multi-Head Mixing"), so the backward pass
+// returns dq, dk, dv and dW.  With u = phi(q), a = phi(k), g = dL/do and the
+// forward's S_j, z_j, St_i, zt_i (recomputed by the forward kernels):
+//
+//   den = u . zt_i + eps,  dnum = g / den,  dden = -(g . o) / den
+//   dq  = (St_i dnum + zt_i dden) * phi'(q)
+//   dSt_i = sum_{n in i} u dnum^T,  dzt_i = sum_{n in i} u dden        (bwd_query)
+//   dS_j = sum_i W[i,j] dSt_i,  dz_j = sum_i W[i,j] dzt_i              (mixing with W^T)
+//   dW[i,j] = sum over (b, h) of <dSt_i, S_j> + <dzt_i, z_j>          (dw_partial + dw_reduce)
+//   dv = dS_j^T a,  dk = (dS_j v + dz_j) * phi'(k)                       (bwd_kv)
+//
+// with phi'(x) = 1 for x > 0 and exp(x) otherwise.  Products run on bf16
+// MFMA with fp32 accumulation; the gradients of the summaries are kept as
+// bf16 records in the summaries' own layout ([e][c] then the normaliser part),
+// so dW is one GEMM over all (b, h) and record elements.
+#include "launch.h"
+#include "bf16_shared.h"
+
+#include <mhla.h>
+
+namespace mhla {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x16_bf16: lane l supplies row (or column) l % 16 and
+// k = 4 * (l / 16) + 0..3; output as for the 16x16x32 form.
+__device__ __forceinline__ f32x4 mfma_k16(const u32x2& a, const u32x2& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                     c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float phi_grad(float x) { return x > 0.f ? 1.f : __expf(x); }
+
+// Unpack 8 channels (one 16-byte load) into fp32.
+__device__ __forceinline__ void unpack8(const u32x4& w, float* x) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        x[2 * k] = bf_lo(w[k]);
+        x[2 * k + 1] = bf_hi(w[k]);
+    }
+}
+
+// A 16-token x D tile whose lane (t, gq) holds channels 4*RT*gq .. +4*RT-1 of
+// token t as packed bf16 pairs leaves through the wave's LDS slice and is
+// written as whole token rows by buffer stores; a token past the block's end
+// gets an out-of-range offset, so the hardware drops its write.
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* sout, const uint32_t* wv, int lane, int off, bool ok,
+                                           __amdgpu_buffer_rsrc_t rsrc, int olane) {
+    constexpr int RT = D / 16, OSTR = D + 8, CPR = D / 8;
+    const int t = lane & 15, gq = lane >> 4;
+    uint16_t* srow = sout + t * OSTR + 4 * RT * gq;
+#pragma unroll
+    for (int u = 0; u < RT / 2; ++u)
+        *reinterpret_cast<u32x4*>(srow + 8 * u) = u32x4{wv[4 * u], wv[4 * u + 1], wv[4 * u + 2], wv[4 * u + 3]};
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+        const int tt = k * (64 / CPR) + lane / CPR, chunk = lane % CPR;
+        const int offk = __shfl(off, tt, 64);
+        const int okk = __shfl((int)ok, tt, 64);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(sout + tt * OSTR + chunk * 8);
+        const uint32_t bo = okk ? (uint32_t)(offk * 2 + olane + chunk * 16) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, bo, 0, 0);
+    }
+}
+
+// A x B operand rows for a d x d matrix held as [e][c] (c fastest), the way
+// the summaries store S^T: row e, k = c (contiguous), lane (t, gq) rows in the
+// order that leaves each lane with 4*RT consecutive outputs.
+template <int D>
+__device__ __forceinline__ void rows_e_k_c(const uint16_t* __restrict__ m, int t, int gq, u32x4 (&a)[D / 16][D / 32]) {
+    constexpr int RT = D / 16, KS = D / 32;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) a[r][kk] = *reinterpret_cast<const u32x4*>(m + e * D + kk * 32 + gq * 8);
+    }
+}
+
+// The transposed operand of the same matrix: row c, k-slot s of k-step kk at
+// e = ebase(gq) + 8 * kk + s, gathered element by element (once per block).
+template <int D>
+__device__ __forceinline__ void rows_c_k_e(const uint16_t* __restrict__ m, int t, int ebase,
+                                           u32x4 (&a)[D / 16][D / 32]) {
+    constexpr int RT = D / 16, KS = D / 32;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int c = 4 * RT * (t >> 2) + 4 * rt + (t & 3);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int e0 = ebase + 8 * kk + 2 * w;
+                a[rt][kk][w] = (uint32_t)m[e0 * D + c] | ((uint32_t)m[(e0 + 1) * D + c] << 16);
+            }
+    }
+}
+
+// =====================================================================
+// bwd_query: dq and the gradients of the mixed summaries, per query block.
+// Workgroup = (b, block i, group of <= 8 heads), one wave per head over all of
+// the block's tokens, 16 tokens per step (token t = lane % 16):
+//   num = St^T u and den (as in the forward apply), then dnum, dden;
+//   du  = St dnum (MFMA; k-slots of lane group gq are its own 4*RT channels)
+//         + zt dden, dq = du * phi'(q);
+//   dSt += u dnum^T, dzt += u dden on v_mfma_f32_16x16x16_bf16 with the 16
+//   tokens as k, both operands read transposed from the wave's LDS slice.
+// =====================================================================
+template <int D>
+__global__ __launch_bounds__(512) void bwd_query_bf16(const uint16_t* __restrict__ Q,
+                                                      const uint16_t* __restrict__ dO,
+                                                      const uint16_t* __restrict__ St,
+                                                      const float* __restrict__ Zt, uint16_t* __restrict__ dQ,
+                                                      uint16_t* __restrict__ dSt, const Geo g) {
+    constexpr int RT = D / 16, KS = D / 32, REC = D * D + D;
+    constexpr int OSTR = D + 8, TS = 20;   // TS: transposed tile row, 16 tokens + 4 padding
+    constexpr int SLICE = 16 * OSTR + 2 * D * TS;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[8 * SLICE];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = lane & 15, gq = lane >> 4;
+    const WgCoord wgc = wg_coord(g, blockIdx.x);
+    const int hh = wgc.hg * g.G + wave;
+    if (hh >= g.H) return;
+    const int b = __builtin_amdgcn_readfirstlane(wgc.b);
+    const int h = __builtin_amdgcn_readfirstlane(hh);
+    const int i = __builtin_amdgcn_readfirstlane(wgc.j);
+    const int bh = b * g.H + h, blk = bh * g.M + i;
+    uint16_t* sout = lds + wave * SLICE;
+    uint16_t* dnT = sout + 16 * OSTR;   // [e][token]
+    uint16_t* uT = dnT + D * TS;        // [c][token]
+
+    // ---- operands of this block's mixed summary
+    const uint16_t* sb = St + (size_t)blk * (D * D);
+    const float* zb = Zt + (size_t)blk * D;
+    u32x4 a1[RT][KS], a2[RT][KS], zhi[KS], zlo[KS];
+    rows_e_k_c<D>(sb, t, gq, a1);
+    rows_c_k_e<D>(sb, t, 4 * RT * gq, a2);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8 + 4);
+        const float z[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        split_zt(z, zhi[kk], zlo[kk]);
+    }
+    float zc[4 * RT];   // zt at this lane's output channels 4*RT*gq + ..
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(zb + 4 * RT * gq + 4 * u);
+        zc[4 * u] = x.x; zc[4 * u + 1] = x.y; zc[4 * u + 2] = x.z; zc[4 * u + 3] = x.w;
+    }
+
+    const int row = g.H * D;
+    const int origin = block_origin(g, i);
+    const uint16_t* qb = Q + ((size_t)b * g.N * row + h * D);
+    const uint16_t* gb = dO + ((size_t)b * g.N * row + h * D);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        dQ + (size_t)b * g.N * row, 0, g.N * row * 2, 0x00020000);
+    const int olane = h * D * 2;
+
+    f32x4 dsacc[RT][RT], dzacc[RT];
+#pragma unroll
+    for (int re = 0; re < RT; ++re) {
+        dzacc[re] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rc = 0; rc < RT; ++rc) dsacc[re][rc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int nit = (g.T + 15) >> 4;
+    for (int it = 0; it < nit; ++it) {
+        const int p = it * 16 + t;
+        const bool ok = p < g.T;
+        const int off = (origin + in_block(g, ok ? p : g.T - 1)) * row;
+        u32x4 qv[KS], go[RT / 2], qo[RT / 2];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) qv[kk] = *reinterpret_cast<const u32x4*>(qb + off + kk * 32 + gq * 8);
+#pragma unroll
+        for (int u = 0; u < RT / 2; ++u) {
+            go[u] = *reinterpret_cast<const u32x4*>(gb + off + 4 * RT * gq + 8 * u);
+            qo[u] = *reinterpret_cast<const u32x4*>(qb + off + 4 * RT * gq + 8 * u);
+        }
+        // u = phi(q) as the B operand (k = channel kk*32 + gq*8 + s, column = token t)
+        u32x4 bq[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                bq[kk][w] = pack_bf16(phi_fast(bf_lo(qv[kk][w])), phi_fast(bf_hi(qv[kk][w])));
+        f32x4 acc[RT], accd = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r) acc[r] = mfma_bf16(a1[r][kk], bq[kk], acc[r]);
+            accd = mfma_bf16(zhi[kk], bq[kk], accd);
+            accd = mfma_bf16(zlo[kk], bq[kk], accd);
+        }
+        const float inv = 1.f / (accd[0] + g.eps);
+        // Upstream gradient at this lane's channels e = 4*RT*gq + 4r + v (zero past the block).
+        float gl[4 * RT];
+#pragma unroll
+        for (int u = 0; u < RT / 2; ++u) unpack8(go[u], gl + 8 * u);
+#pragma unroll
+        for (int e = 0; e < 4 * RT; ++e) gl[e] = ok ? gl[e] : 0.f;
+        float dot = 0.f;   // g . num over this lane's channels
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dot += gl[4 * r + v] * acc[r][v];
+        dot += shfl_xor(dot, 16);
+        dot += shfl_xor(dot, 32);
+        const float dden = -dot * inv * inv;
+        // dnum as the B operand of du: k-step kk, slot s <-> e = 4*RT*gq + 8*kk + s,
+        // as a bf16 high part and the bf16 rounding of the remainder (du cancels
+        // along u, so dnum's own rounding would show in dq).
+        u32x4 b2h[KS], b2l[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float x0 = gl[8 * kk + 2 * w] * inv, x1 = gl[8 * kk + 2 * w + 1] * inv;
+                const uint32_t hw = pack_bf16(x0, x1);
+                b2h[kk][w] = hw;
+                b2l[kk][w] = pack_bf16(x0 - bf_lo(hw), x1 - bf_hi(hw));
+            }
+        f32x4 du[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) du[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                du[rt] = mfma_bf16(a2[rt][kk], b2h[kk], du[rt]);
+                du[rt] = mfma_bf16(a2[rt][kk], b2l[kk], du[rt]);
+            }
+        float ql[4 * RT];
+#pragma unroll
+        for (int u = 0; u < RT / 2; ++u) unpack8(qo[u], ql + 8 * u);
+        uint32_t wv[2 * RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float x[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int cl = 4 * rt + v;
+                x[v] = (du[rt][v] + zc[cl] * dden) * phi_grad(ql[cl]);
+            }
+            wv[2 * rt] = pack_bf16(x[0], x[1]);
+            wv[2 * rt + 1] = pack_bf16(x[2], x[3]);
+        }
+        store_rows<D>(sout, wv, lane, off, ok, rsrc, olane);
+
+        // ---- dSt += u dnum^T and dzt += u dden over these 16 tokens.
+#pragma unroll
+        for (int e = 0; e < 4 * RT; ++e)
+            dnT[(4 * RT * gq + e) * TS + t] = (uint16_t)(pack_bf16(gl[e] * inv, 0.f) & 0xffffu);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int c = kk * 32 + gq * 8 + 2 * w;
+                uT[c * TS + t] = (uint16_t)(bq[kk][w] & 0xffffu);
+                uT[(c + 1) * TS + t] = (uint16_t)(bq[kk][w] >> 16);
+            }
+        float dd[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) dd[s] = __shfl(dden, 4 * gq + s, 64);
+        const uint32_t d01 = pack_bf16(dd[0], dd[1]), d23 = pack_bf16(dd[2], dd[3]);
+        const u32x2 dhi = u32x2{d01, d23};
+        const u32x2 dlo = u32x2{pack_bf16(dd[0] - bf_lo(d01), dd[1] - bf_hi(d01)),
+                                pack_bf16(dd[2] - bf_lo(d23), dd[3] - bf_hi(d23))};
+        u32x2 bu[RT];
+#pragma unroll
+        for (int rc = 0; rc < RT; ++rc) bu[rc] = *reinterpret_cast<const u32x2*>(uT + (16 * rc + t) * TS + 4 * gq);
+#pragma unroll
+        for (int re = 0; re < RT; ++re) {
+            const u32x2 an = *reinterpret_cast<const u32x2*>(dnT + (16 * re + t) * TS + 4 * gq);
+#pragma unroll
+            for (int rc = 0; rc < RT; ++rc) dsacc[re][rc] = mfma_k16(an, bu[rc], dsacc[re][rc]);
+        }
+#pragma unroll
+        for (int rc = 0; rc < RT; ++rc) {
+            dzacc[rc] = mfma_k16(dhi, bu[rc], dzacc[rc]);
+            dzacc[rc] = mfma_k16(dlo, bu[rc], dzacc[rc]);
+        }
+    }
+
+    // ---- the block's record: dSt as [e][c] (element (c, e) at e*D + c), then dzt[c].
+    uint16_t* rec = dSt + (size_t)blk * REC;
+#pragma unroll
+    for (int re = 0; re < RT; ++re)
+#pragma unroll
+        for (int rc = 0; rc < RT; ++rc)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int e = 16 * re + 4 * gq + v, c = 16 * rc + t;
+                rec[e * D + c] = (uint16_t)(pack_bf16(dsacc[re][rc][v], 0.f) & 0xffffu);
+            }
+    if (gq == 0) {
+#pragma unroll
+        for (int rc = 0; rc < RT; ++rc) rec[D * D + 16 * rc + t] = (uint16_t)(pack_bf16(dzacc[rc][0], 0.f) & 0xffffu);
+    }
+}
+
+// =====================================================================
+// bwd_kv: dv and dk per source block.  Workgroup = (b, block j, group of
+// <= 8 heads), one wave per head over the block's tokens, 16 per step:
+//   dv = dS^T a (rows e, k = c: the record's own layout),
+//   dk = (dS v + dz) * phi'(k) (rows c, k = e: the transposed operand).
+// =====================================================================
+template <int D>
+__global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                                   const uint16_t* __restrict__ dS, const float* __restrict__ dZ,
+                                                   uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                                                   const Geo g) {
+    constexpr int RT = D / 16, KS = D / 32;
+    constexpr int OSTR = D + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[8 * 16 * OSTR];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = lane & 15, gq = lane >> 4;
+    const WgCoord wgc = wg_coord(g, blockIdx.x);
+    const int hh = wgc.hg * g.G + wave;
+    if (hh >= g.H) return;
+    const int b = __builtin_amdgcn_readfirstlane(wgc.b);
+    const int h = __builtin_amdgcn_readfirstlane(hh);
+    const int j = __builtin_amdgcn_readfirstlane(wgc.j);
+    const int blk = (b * g.H + h) * g.M + j;
+    uint16_t* sout = lds + wave * (16 * OSTR);
+
+    const uint16_t* mb = dS + (size_t)blk * (D * D);
+    u32x4 a3[RT][KS], a4[RT][KS];
+    rows_e_k_c<D>(mb, t, gq, a3);
+    // a4: row c, k-slot s of k-step kk at e = kk*32 + gq*8 + s (the layout V is loaded in).
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int c = 4 * RT * (t >> 2) + 4 * rt + (t & 3);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int e0 = kk * 32 + gq * 8 + 2 * w;
+                a4[rt][kk][w] = (uint32_t)mb[e0 * D + c] | ((uint32_t)mb[(e0 + 1) * D + c] << 16);
+            }
+    }
+    float dzc[4 * RT];
+    const float* zb = dZ + (size_t)blk * D;
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(zb + 4 * RT * gq + 4 * u);
+        dzc[4 * u] = x.x; dzc[4 * u + 1] = x.y; dzc[4 * u + 2] = x.z; dzc[4 * u + 3] = x.w;
+    }
+
+    const int row = g.H * D;
+    const int origin = block_origin(g, j);
+    const size_t bbase = (size_t)b * g.N * row + h * D;
+    const uint16_t* kb = K + bbase;
+    const uint16_t* vb = V + bbase;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(dK + (size_t)b * g.N * row, 0,
+                                                                        g.N * row * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(dV + (size_t)b * g.N * row, 0,
+                                                                        g.N * row * 2, 0x00020000);
+    const int olane = h * D * 2;
+
+    const int nit = (g.T + 15) >> 4;
+    for (int it = 0; it < nit; ++it) {
+        const int p = it * 16 + t;
+        const bool ok = p < g.T;
+        const int off = (origin + in_block(g, ok ? p : g.T - 1)) * row;
+        u32x4 kv[KS], vv[KS], ko[RT / 2];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            kv[kk] = *reinterpret_cast<const u32x4*>(kb + off + kk * 32 + gq * 8);
+            vv[kk] = *reinterpret_cast<const u32x4*>(vb + off + kk * 32 + gq * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < RT / 2; ++u) ko[u] = *reinterpret_cast<const u32x4*>(kb + off + 4 * RT * gq + 8 * u);
+        u32x4 ba[KS];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                ba[kk][w] = pack_bf16(phi_fast(bf_lo(kv[kk][w])), phi_fast(bf_hi(kv[kk][w])));
+        f32x4 accv[RT], acck[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            accv[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acck[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                accv[r] = mfma_bf16(a3[r][kk], ba[kk], accv[r]);
+                acck[r] = mfma_bf16(a4[r][kk], vv[kk], acck[r]);
+            }
+        uint32_t wv[2 * RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            wv[2 * r] = pack_bf16(accv[r][0], accv[r][1]);
+            wv[2 * r + 1] = pack_bf16(accv[r][2], accv[r][3]);
+        }
+        store_rows<D>(sout, wv, lane, off, ok, rv, olane);
+        float kl[4 * RT];
+#pragma unroll
+        for (int u = 0; u < RT / 2; ++u) unpack8(ko[u], kl + 8 * u);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            float x[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int cl = 4 * r + v;
+                x[v] = (acck[r][v] + dzc[cl]) * phi_grad(kl[cl]);
+            }
+            wv[2 * r] = pack_bf16(x[0], x[1]);
+            wv[2 * r + 1] = pack_bf16(x[2], x[3]);
+        }
+        store_rows<D>(sout, wv, lane, off, ok, rk, olane);
+    }
+}
+
+// =====================================================================
+// dW = sum over (b, h) and record elements of dSt_i[x] S_j[x]: a GEMM whose
+// k runs over B*H*(d*d + d).  Workgroup = (128 x 128 tile of dW, split s of
+// the k-steps); wave (wi, wj) computes 32 i x 64 j; both operands come from
+// the bf16 records (rows i of dSt, rows j of S, 8 consecutive elements per
+// lane).  Partial sums go to part[s]; dw_reduce adds them in split order.
+// =====================================================================
+template <int D>
+__global__ __launch_bounds__(512) void dw_partial_bf16(const uint16_t* __restrict__ dSt,
+                                                       const uint16_t* __restrict__ SZ, float* __restrict__ part,
+                                                       int M, int P, int nsplit, int ntj) {
+    constexpr int REC = D * D + D, KPR = REC / 32;
+    const int tile = blockIdx.x, s = blockIdx.y;
+    const int ti = tile / ntj, tj = tile - ti * ntj;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane & 15, gq = lane >> 4;
+    const int i0 = ti * 128 + (wave >> 1) * 32, j0 = tj * 128 + (wave & 1) * 64;
+    int ri[2], rj[4];
+    uint32_t mi[2], mj[4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int i = i0 + 16 * a + li;
+        ri[a] = i < M ? i : M - 1;
+        mi[a] = i < M ? 0xffffffffu : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int jj = j0 + 16 * c + li;
+        rj[c] = jj < M ? jj : M - 1;
+        mj[c] = jj < M ? 0xffffffffu : 0u;
+    }
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int KT = P * KPR;
+    for (int ks = s; ks < KT; ks += nsplit) {
+        const int bh = ks / KPR, col = (ks - bh * KPR) * 32 + gq * 8;
+        const size_t rb = (size_t)bh * M;
+        u32x4 A[2], B[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) A[a] = *reinterpret_cast<const u32x4*>(dSt + (rb + ri[a]) * REC + col) & mi[a];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) B[c] = *reinterpret_cast<const u32x4*>(SZ + (rb + rj[c]) * REC + col) & mj[c];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(A[a], B[c], acc[a][c]);
+    }
+    float* out = part + (size_t)s * M * M;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = i0 + 16 * a + 4 * gq + v, jj = j0 + 16 * c + li;
+                if (i < M && jj < M) out[(size_t)i * M + jj] = acc[a][c][v];
+            }
+}
+
+__global__ __launch_bounds__(256) void dw_reduce(const float* __restrict__ part, float* __restrict__ dW, int MM,
+                                                 int nsplit) {
+    const int x = blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= MM) return;
+    float s = 0.f;
+    for (int k = 0; k < nsplit; ++k) s += part[(size_t)k * MM + x];
+    dW[x] = s;
+}
+
+// W^T in the mixing kernel's operand order.
+__global__ __launch_bounds__(256) void convert_wt(const float* __restrict__ W, uint16_t* __restrict__ Wb,
+                                                  const WConv wc) {
+    convert_w(W, Wb, wc);
+}
+
+// The mixing product with W^T over the gradient records.
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void mix_transposed_bf16(
+    const uint16_t* __restrict__ dSt, const uint16_t* __restrict__ WbT, uint16_t* __restrict__ dS,
+    float* __restrict__ dZ, const Geo g, const MixGeo mg) {
+    __shared__ u32x4 sA[MIX_LDS_UNITS];
+    mix_tile_bf16<D>(blockIdx.x, dSt, WbT, dS, dZ, g, mg, sA);
+}
+
+inline void rec(const BwdLaunch& B, int k) {
+    if (B.events) (void)hipEventRecord(B.events[k], B.F.stream);
+}
+
+template <int D>
+hipError_t run_bwd_d(const BwdLaunch& B) {
+    const Launch& L = B.F;
+    const Geo& g = L.g;
+    rec(B, 0);
+    // Forward summaries and mixed summaries (regions 0-3 of the workspace).
+    hipError_t err = run_bf16_summaries(L);
+    if (err != hipSuccess) return err;
+    rec(B, 1);
+    const int IT = (g.M + 63) / 64, NK = (g.M + 31) / 32;
+    WConv wc;
+    wc.M = g.M;
+    wc.NK = NK;
+    wc.nchunks = IT * 64 * NK * 32 / 8;
+    wc.first_wg = 0;
+    wc.transpose = 1;
+    convert_wt<<<(wc.nchunks + 255) / 256, 256, 0, L.stream>>>(L.W, B.wbt, wc);
+    const Geo gh = [&] {
+        Geo x = g;
+        x.HG = (g.H + 7) / 8;
+        x.G = (g.H + x.HG - 1) / x.HG;
+        x.div_HG = make_fastdiv((uint32_t)x.HG);
+        return x;
+    }();
+    const int grid_tok = gh.B * gh.M * gh.HG, block_tok = 64 * gh.G;
+    bwd_query_bf16<D><<<grid_tok, block_tok, 0, L.stream>>>(
+        static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(B.dout), static_cast<const uint16_t*>(L.st),
+        L.zt, static_cast<uint16_t*>(B.dq), B.dst, gh);
+    rec(B, 2);
+    MixGeo mg;
+    mg.CT = (D * D + D + 63) / 64;
+    mg.IT = IT;
+    mg.CPW = IT >= 4 ? 1 : 4 / IT;
+    mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
+    mg.Jpad = NK * 32;
+    mg.div_CTG = make_fastdiv(mg.CTG);
+    mix_transposed_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(B.dst, B.wbt, B.ds, B.dz, g, mg);
+    const int ntj = (g.M + 127) / 128;
+    dw_partial_bf16<D><<<dim3(ntj * ntj, B.nsplit), 512, 0, L.stream>>>(
+        B.dst, static_cast<const uint16_t*>(L.sz), B.part, g.M, g.BH, B.nsplit, ntj);
+    dw_reduce<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, B.dw, g.M * g.M, B.nsplit);
+    rec(B, 3);
+    bwd_kv_bf16<D><<<grid_tok, block_tok, 0, L.stream>>>(
+        static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v), B.ds, B.dz,
+        static_cast<uint16_t*>(B.dk), static_cast<uint16_t*>(B.dv), gh);
+    rec(B, 4);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void fill_zero(float* __restrict__ p, int n) {
+    const int x = blockIdx.x * blockDim.x + threadIdx.x;
+    if (x < n) p[x] = 0.f;
+}
+
+}  // namespace
+
+hipError_t zero_f32(float* p, int n, hipStream_t stream) {
+    if (n > 0) fill_zero<<<(n + 255) / 256, 256, 0, stream>>>(p, n);
+    return hipGetLastError();
+}
+
+hipError_t run_bwd_bf16(const BwdLaunch& B) {
+    switch (B.F.g.D) {
+        case 32: return run_bwd_d<32>(B);
+        case 64: return run_bwd_d<64>(B);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace mhla

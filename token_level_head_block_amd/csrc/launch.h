@@ -31,6 +31,7 @@ struct Launch {
     Geo g;
     Tuning tune;
     int path;                     // MHLA_PATH_*
+    int summaries_only;           // bf16: stop after the mixing kernel (backward recompute)
     const hipEvent_t* events;     // 4 events or nullptr
     hipStream_t stream;
 };
@@ -38,5 +39,30 @@ struct Launch {
 // Enqueue the whole forward pass for one dtype.  Returns the first HIP error.
 hipError_t run_bf16(const Launch& L);
 hipError_t run_f32(const Launch& L);
+
+// Backward pass (bf16, d = 32 or 64).  F holds the inputs q, k, v, W, the
+// forward workspace regions (summaries, mixed summaries, normalisers, W in
+// operand order) that the recompute fills, geometry, tuning and stream.
+struct BwdLaunch {
+    Launch F;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dw;
+    uint16_t* dst;    // gradients of the mixed summaries, records [BH][M][D*D + D] (bf16)
+    uint16_t* ds;     // gradients of the summaries [BH][M][D*D] (bf16, record order)
+    float* dz;        // gradients of the normalisers [BH][M][D]
+    uint16_t* wbt;    // W^T in the mixing kernel's operand order
+    float* part;      // dW partial sums [nsplit][M][M]
+    int nsplit;
+    const hipEvent_t* events;   // 5 events or nullptr
+};
+
+// Summary and mixing kernels of the bf16 forward only (regions of F).
+hipError_t run_bf16_summaries(const Launch& L);
+hipError_t run_bwd_bf16(const BwdLaunch& B);
+// p[0 .. n) = 0 by a kernel (safe inside a captured graph).
+hipError_t zero_f32(float* p, int n, hipStream_t stream);
 
 }  // namespace mhla

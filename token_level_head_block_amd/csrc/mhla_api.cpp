@@ -191,6 +191,7 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
             (void)hipGetLastError();
     }
     L.path = path;
+    L.summaries_only = 0;
     L.events = events;
     L.stream = stream;
     const hipError_t err = s.dtype == MHLA_BF16 ? mhla::run_bf16(L) : mhla::run_f32(L);
@@ -198,9 +199,140 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
     return err == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------- backward
+
+struct BwdLayout {
+    Layout fwd;                                  // regions of the forward recompute
+    size_t dst, ds, dz, wbt, part, total;
+    int nsplit;
+};
+
+bool bwd_supported(const Shape& s) { return s.dtype == MHLA_BF16 && (s.D == 32 || s.D == 64); }
+
+BwdLayout bwd_layout(const Shape& s) {
+    BwdLayout L;
+    L.fwd = layout(s);
+    const size_t recs = (size_t)(s.B * s.H * s.M);
+    const size_t wpad = (size_t)((s.M + 63) / 64 * 64) * (size_t)((s.M + 31) / 32 * 32) * 2;
+    L.dst = L.fwd.total;
+    L.ds = L.dst + align_up(recs * (size_t)(s.D * s.D + s.D) * 2);
+    L.dz = L.ds + align_up(recs * (size_t)(s.D * s.D) * 2);
+    L.wbt = L.dz + align_up(recs * (size_t)s.D * 4);
+    L.part = L.wbt + align_up(wpad);
+    // dW: k-steps of 32 record elements over all (b, h), split so that about
+    // 256 workgroups share them.
+    const int64_t tiles = ((s.M + 127) / 128) * ((s.M + 127) / 128);
+    const int64_t ksteps = s.B * s.H * ((s.D * s.D + s.D) / 32);
+    int64_t ns = 256 / tiles;
+    if (ns < 1) ns = 1;
+    if (ns > ksteps) ns = ksteps > 0 ? ksteps : 1;
+    L.nsplit = (int)ns;
+    L.total = L.part + align_up((size_t)ns * (size_t)(s.M * s.M) * 4);
+    return L;
+}
+
+mhla_status backward_impl(const void* q, const void* k, const void* v, const float* W, const void* dout,
+                          const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
+                          float* dW, void* ws, size_t ws_bytes, const hipEvent_t* events, hipStream_t stream) {
+    Shape s;
+    mhla_status st = check(grid, block, &s);
+    if (st != MHLA_OK) return st;
+    if (!bwd_supported(s)) return MHLA_ERR_UNSUPPORTED;
+    if (!dW) return MHLA_ERR_INVALID_ARG;
+    if (!aligned16(dW)) return MHLA_ERR_MISALIGNED;
+    const size_t wbytes = (size_t)(s.M * s.M) * 4;
+    if (s.B == 0 || s.H == 0) {
+        // No pair contributes: dW is zero.
+        return mhla::zero_f32(dW, (int)(s.M * s.M), stream) == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
+    }
+    const void* ins[5] = {q, k, v, W, dout};
+    void* outs[4] = {dq, dk, dv, dW};
+    for (const void* x : ins)
+        if (!x) return MHLA_ERR_INVALID_ARG;
+    for (const void* x : outs)
+        if (!x) return MHLA_ERR_INVALID_ARG;
+    for (const void* x : ins)
+        if (!aligned16(x)) return MHLA_ERR_MISALIGNED;
+    for (const void* x : outs)
+        if (!aligned16(x)) return MHLA_ERR_MISALIGNED;
+    const size_t tbytes = (size_t)(s.B * s.N * s.H * s.D) * s.esz;
+    const size_t insz[5] = {tbytes, tbytes, tbytes, wbytes, tbytes};
+    const size_t outsz[4] = {tbytes, tbytes, tbytes, wbytes};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = 0; b < 5; ++b)
+            if (overlaps(outs[a], outsz[a], ins[b], insz[b])) return MHLA_ERR_INVALID_ARG;
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a], outsz[a], outs[b], outsz[b])) return MHLA_ERR_INVALID_ARG;
+    }
+    const BwdLayout lay = bwd_layout(s);
+    bool owned = false;
+    if (ws) {
+        if (ws_bytes < lay.total) return MHLA_ERR_INVALID_ARG;
+        if (!aligned16(ws)) return MHLA_ERR_MISALIGNED;
+        for (int b = 0; b < 5; ++b)
+            if (overlaps(ws, lay.total, ins[b], insz[b])) return MHLA_ERR_INVALID_ARG;
+        for (int a = 0; a < 4; ++a)
+            if (overlaps(ws, lay.total, outs[a], outsz[a])) return MHLA_ERR_INVALID_ARG;
+    } else {
+        if (ws_bytes != 0) return MHLA_ERR_INVALID_ARG;
+        if (hipMallocAsync(&ws, lay.total, stream) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return MHLA_ERR_ALLOC;
+        }
+        owned = true;
+    }
+    char* base = static_cast<char*>(ws);
+    mhla::BwdLaunch B;
+    mhla::Launch& L = B.F;
+    L.q = q; L.k = k; L.v = v; L.W = W; L.out = nullptr;
+    L.sz = base + lay.fwd.sz;
+    L.st = base + lay.fwd.st;
+    L.zt = reinterpret_cast<float*>(base + lay.fwd.zt);
+    L.wb = base + lay.fwd.wb;
+    L.g = make_geo(s, grid->eps);
+    L.tune = choose_tuning(s);
+    L.path = MHLA_PATH_3KERNEL;
+    L.summaries_only = 1;
+    L.events = nullptr;
+    L.stream = stream;
+    {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            L.tune.num_cus = cus;
+        else
+            (void)hipGetLastError();
+    }
+    B.dout = dout;
+    B.dq = dq; B.dk = dk; B.dv = dv; B.dw = dW;
+    B.dst = reinterpret_cast<uint16_t*>(base + lay.dst);
+    B.ds = reinterpret_cast<uint16_t*>(base + lay.ds);
+    B.dz = reinterpret_cast<float*>(base + lay.dz);
+    B.wbt = reinterpret_cast<uint16_t*>(base + lay.wbt);
+    B.part = reinterpret_cast<float*>(base + lay.part);
+    B.nsplit = lay.nsplit;
+    B.events = events;
+    const hipError_t err = mhla::run_bwd_bf16(B);
+    if (owned) (void)hipFreeAsync(ws, stream);
+    return err == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t mhla_backward_workspace_bytes(const mhla_grid* grid, const mhla_block* block) {
+    Shape s;
+    if (check(grid, block, &s) != MHLA_OK || !bwd_supported(s) || s.B == 0 || s.H == 0) return 0;
+    return bwd_layout(s).total;
+}
+
+mhla_status mhla_backward(const void* q, const void* k, const void* v, const float* W, const void* dout,
+                          const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
+                          float* dW, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
+                          hipStream_t stream) {
+    return backward_impl(q, k, v, W, dout, grid, block, dq, dk, dv, dW, ws, ws_bytes, stage_events, stream);
+}
 
 const char* mhla_status_string(mhla_status status) {
     switch (status) {
