@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough to exceed 2x the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--out", default="", help="also write the JSON line to this file")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dq, dk, dv, dW) instead of the forward (bf16, d <= 64)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size")
     ap.add_argument("--heads", type=int, default=0, help="override the workload's head count")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -135,6 +137,121 @@ class HipEvents:
         self.made = []
 
 
+def backward_bytes(p):
+    """Algorithmic HBM bytes of each backward stage (compulsory reads + writes, bf16 records)."""
+    B, N, H, d, M = p.batch, p.n_tokens, p.heads, p.head_dim, p.n_blocks
+    tensor = B * N * H * d * p.elem_bytes
+    P = B * H
+    rec = P * M * (d * d + d) * 2      # summaries, or their gradients, as bf16 records
+    st = P * M * d * d * 2
+    zt = P * M * d * 4
+    w = M * M * 4
+    return {
+        "recompute (block_kv_summary + mix)": 2 * tensor + rec + rec + w + st + zt,
+        "bwd_query": 2 * tensor + st + zt + tensor + rec,
+        "mix_transposed + dW": rec + w + st + zt + 2 * rec + w,
+        "bwd_kv": 2 * tensor + st + zt + 2 * tensor,
+    }
+
+
+def bench_backward(args, p, torch, mh, synth):
+    """One step = one mhla_backward call (recompute of the forward summaries,
+    query side, transposed mixing and dW, key/value side) on synthetic inputs
+    and a synthetic upstream gradient resident in HBM."""
+    if p.dtype != synth.BF16 or p.head_dim not in (32, 64):
+        print("the backward pass supports bf16 problems with d = 32 or 64", file=sys.stderr)
+        sys.exit(1)
+    tensor_bytes = p.batch * p.n_tokens * p.heads * p.head_dim * p.elem_bytes
+    sets = args.sets or max(2, int(np.ceil(2 * MALL_BYTES / (7 * tensor_bytes))))
+
+    def dev(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+
+    data, host0 = [], None
+    for s in range(sets):
+        q, k, v, W = synth.make_inputs(p, seed=(args.config, s) if s else args.config, w_kind=args.w)
+        rng = np.random.default_rng(1000 + s)
+        g = synth.bf16_bits(rng.standard_normal(q.shape).astype(np.float32))
+        t = [dev(x) for x in (q, k, v, g)]
+        outs = [torch.empty_like(t[0]) for _ in range(3)]
+        dW = torch.empty(p.n_blocks, p.n_blocks, dtype=torch.float32, device="cuda")
+        data.append((t[0], t[1], t[2], torch.from_numpy(W).cuda(), t[3], outs[0], outs[1], outs[2], dW))
+        if s == 0:
+            host0 = (q, k, v, W, g)
+    gr = mh.make_grid(p.batch, p.heads, p.head_dim, mh.MHLA_BF16, p.grid, p.eps)
+    bl = mh.make_block(p.block)
+    ws_bytes = mh.mhla_backward_workspace_bytes(gr, bl)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        q, k, v, W, g, dq, dk, dv, dW = data[i % sets]
+        st = mh.mhla_backward(q, k, v, W, g, gr, bl, dq, dk, dv, dW, ws, ws_bytes, events, stream)
+        if st != mh.MHLA_OK:
+            raise mh.MhlaError(st, "mhla_backward")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    hev = HipEvents()
+    evs = [[hev.create() for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    stage_ms = np.array([[hev.elapsed_ms(r[j], r[j + 1]) for j in range(4)] for r in evs]).mean(axis=0)
+    hev.destroy_all()
+    kb = backward_bytes(p)
+    stages = {}
+    for j, (name, nbytes) in enumerate(kb.items()):
+        gbps = nbytes / (stage_ms[j] * 1e-3) / 1e9
+        stages[name] = {"avg_us": round(float(stage_ms[j]) * 1e3, 2), "alg_bytes": int(nbytes),
+                        "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    dom = max(stages, key=lambda n: stages[n]["avg_us"])
+    U = 7 * tensor_bytes + 8 * p.n_blocks ** 2      # read q, k, v, dout, W; write dq, dk, dv, dW
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        q, k, v, W, g = host0
+        ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        t = time.perf_counter()
+        _, used = oracle.backward(q, k, v, W, g, p.grid, p.block, eps=p.eps, threads=ncpu, return_threads=True)
+        dt_cpu = time.perf_counter() - t
+        cpu = {"value": round(p.batch * p.n_tokens / dt_cpu, 1), "unit": "tokens/s", "cores": used,
+               "kind": "oracle", "seconds": round(dt_cpu, 3),
+               "sample": f"the full workload ({p.batch * p.heads} (b,h) pairs), float64 blockwise gradients"}
+    line = {
+        "metric": "MHLA bwd tokens/s (dq, dk, dv, dW) + achieved HBM GB/s", "value":
+            round(p.batch * p.n_tokens / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{p.name}: B={p.batch} H={p.heads} d={p.head_dim} grid={list(p.grid)} "
+                               f"blocks={list(p.block)} N={p.n_tokens} M={p.n_blocks}",
+                   "pass": "backward", "input_sets": sets, "parallelism": "none (1 GPU)"},
+        "path_hbm_gbps": round(U / (ms_step * 1e-3) / 1e9, 1),
+        "path_hbm_frac": round(U / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "path_alg_bytes": U,
+        "kernels": stages,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": stages[dom]["gbps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": stages[dom]["frac"], "traffic": None,
+                     "avg_us": stages[dom]["avg_us"], "alg_bytes": stages[dom]["alg_bytes"]},
+        "cpu_baseline": cpu,
+    }
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(s + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -164,6 +281,9 @@ def main():
     p = synth.CONFIGS[args.config]
     if args.batch or args.heads:
         p = p.with_(batch=args.batch or p.batch, heads=args.heads or p.heads)
+    if args.backward:
+        bench_backward(args, p, torch, mh, synth)
+        return
     path = mh.MHLA_PATH_FUSED if args.path == "fused" else mh.MHLA_PATH_3KERNEL
     tensor_bytes = p.batch * p.n_tokens * p.heads * p.head_dim * p.elem_bytes
     per_set = 4 * tensor_bytes

@@ -50,18 +50,21 @@ __device__ __forceinline__ void pipelined(int first, int step, int n, LoadF&& lo
 struct WConv {
     int32_t M, NK, nchunks;   // NK = Jpad / 32; nchunks = Ipad * Jpad / 8; 0 = none
     int32_t first_wg;         // workgroups [first_wg, gridDim.x) convert
-    int32_t transpose;        // nonzero: convert W^T instead of W
+    uint16_t* wbt;            // if not null, W^T is converted to this buffer as well
 };
 
 __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t* __restrict__ Wb,
                                           const WConv& wc) {
     const int nthr = (gridDim.x - wc.first_wg) * blockDim.x;
-    for (int c = (blockIdx.x - wc.first_wg) * blockDim.x + threadIdx.x; c < wc.nchunks; c += nthr) {
+    const int total = wc.nchunks * (wc.wbt ? 2 : 1);
+    for (int c0 = (blockIdx.x - wc.first_wg) * blockDim.x + threadIdx.x; c0 < total; c0 += nthr) {
+        const bool tr = c0 >= wc.nchunks;   // the chunks of W^T follow those of W
+        const int c = tr ? c0 - wc.nchunks : c0;
         const int lane = c & 63, rk = c >> 6;
         const int rt = rk / wc.NK, kk = rk - rt * wc.NK;
         const int i = 16 * rt + (lane & 15), j0 = 32 * kk + 8 * (lane >> 4);
         float x[8];
-        if (wc.transpose) {
+        if (tr) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)(j0 + s) * wc.M + i] : 0.f;
         } else if (i < wc.M && (wc.M & 7) == 0 && j0 < wc.M) {
@@ -73,7 +76,7 @@ __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t*
 #pragma unroll
             for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)i * wc.M + j0 + s] : 0.f;
         }
-        *reinterpret_cast<u32x4*>(Wb + (size_t)c * 8) =
+        *reinterpret_cast<u32x4*>((tr ? wc.wbt : Wb) + (size_t)c * 8) =
             u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
     }
 }

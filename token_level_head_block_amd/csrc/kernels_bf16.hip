@@ -634,7 +634,8 @@ void launch_summary(const Launch& L, const uint16_t* k, const uint16_t* v, uint1
     const int nsum = g.B * g.M * g.HG, threads = 64 * NQ * g.G;
     WConv w = wc;
     w.first_wg = nsum;
-    const int nconv = (wc.nchunks + threads * 4 - 1) / (threads * 4);   // up to 4 chunks per thread
+    const int nchunks = wc.nchunks * (wc.wbt ? 2 : 1);
+    const int nconv = (nchunks + threads * 4 - 1) / (threads * 4);   // up to 4 chunks per thread
     if (L.tune.nt_loads)
         block_kv_summary_bf16<D, PF, ROW8, FULL, true><<<nsum + nconv, threads, 0, L.stream>>>(
             k, v, sz, g, L.W, static_cast<uint16_t*>(L.wb), w);
@@ -677,7 +678,7 @@ hipError_t run_d(const Launch& L) {
     wc.NK = NK;
     wc.nchunks = fused ? 0 : IT * 64 * NK * 32 / 8;
     wc.first_wg = 0;
-    wc.transpose = 0;
+    wc.wbt = static_cast<uint16_t*>(L.wbt);
     const bool row8 = (g.bk2 % 8) == 0;
 
     record(L, 0);

@@ -112,8 +112,12 @@ __device__ __forceinline__ void rows_c_k_e(const uint16_t* __restrict__ m, int t
 //   dSt += u dnum^T, dzt += u dden on v_mfma_f32_16x16x16_bf16 with the 16
 //   tokens as k, both operands read transposed from the wave's LDS slice.
 // =====================================================================
+// At d = 64 a wave keeps two operand copies of St (64 registers), the dSt
+// accumulators (64) and a token group's working set, more than 256 registers:
+// such workgroups hold 4 waves (heads) so that each wave may use the
+// accumulation registers too.
 template <int D>
-__global__ __launch_bounds__(512) void bwd_query_bf16(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint16_t* __restrict__ Q,
                                                       const uint16_t* __restrict__ dO,
                                                       const uint16_t* __restrict__ St,
                                                       const float* __restrict__ Zt, uint16_t* __restrict__ dQ,
@@ -121,7 +125,8 @@ __global__ __launch_bounds__(512) void bwd_query_bf16(const uint16_t* __restrict
     constexpr int RT = D / 16, KS = D / 32, REC = D * D + D;
     constexpr int OSTR = D + 8, TS = 20;   // TS: transposed tile row, 16 tokens + 4 padding
     constexpr int SLICE = 16 * OSTR + 2 * D * TS;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[8 * SLICE];
+    constexpr int MAXW = D == 64 ? 4 : 8;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[MAXW * SLICE];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = lane & 15, gq = lane >> 4;
     const WgCoord wgc = wg_coord(g, blockIdx.x);
@@ -172,25 +177,31 @@ __global__ __launch_bounds__(512) void bwd_query_bf16(const uint16_t* __restrict
     }
 
     const int nit = (g.T + 15) >> 4;
-    for (int it = 0; it < nit; ++it) {
-        const int p = it * 16 + t;
-        const bool ok = p < g.T;
-        const int off = (origin + in_block(g, ok ? p : g.T - 1)) * row;
+    struct Raw {
         u32x4 qv[KS], go[RT / 2], qo[RT / 2];
+        int off;
+        bool ok;
+    };
+    auto load = [&](int it, Raw& R) {
+        const int p = it * 16 + t;
+        R.ok = p < g.T;
+        R.off = (origin + in_block(g, R.ok ? p : g.T - 1)) * row;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) qv[kk] = *reinterpret_cast<const u32x4*>(qb + off + kk * 32 + gq * 8);
+        for (int kk = 0; kk < KS; ++kk) R.qv[kk] = *reinterpret_cast<const u32x4*>(qb + R.off + kk * 32 + gq * 8);
 #pragma unroll
         for (int u = 0; u < RT / 2; ++u) {
-            go[u] = *reinterpret_cast<const u32x4*>(gb + off + 4 * RT * gq + 8 * u);
-            qo[u] = *reinterpret_cast<const u32x4*>(qb + off + 4 * RT * gq + 8 * u);
+            R.go[u] = *reinterpret_cast<const u32x4*>(gb + R.off + 4 * RT * gq + 8 * u);
+            R.qo[u] = *reinterpret_cast<const u32x4*>(qb + R.off + 4 * RT * gq + 8 * u);
         }
+    };
+    auto compute = [&](const Raw& R) {
         // u = phi(q) as the B operand (k = channel kk*32 + gq*8 + s, column = token t)
         u32x4 bq[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int w = 0; w < 4; ++w)
-                bq[kk][w] = pack_bf16(phi_fast(bf_lo(qv[kk][w])), phi_fast(bf_hi(qv[kk][w])));
+                bq[kk][w] = pack_bf16(phi_fast(bf_lo(R.qv[kk][w])), phi_fast(bf_hi(R.qv[kk][w])));
         f32x4 acc[RT], accd = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -205,9 +216,9 @@ __global__ __launch_bounds__(512) void bwd_query_bf16(const uint16_t* __restrict
         // Upstream gradient at this lane's channels e = 4*RT*gq + 4r + v (zero past the block).
         float gl[4 * RT];
 #pragma unroll
-        for (int u = 0; u < RT / 2; ++u) unpack8(go[u], gl + 8 * u);
+        for (int u = 0; u < RT / 2; ++u) unpack8(R.go[u], gl + 8 * u);
 #pragma unroll
-        for (int e = 0; e < 4 * RT; ++e) gl[e] = ok ? gl[e] : 0.f;
+        for (int e = 0; e < 4 * RT; ++e) gl[e] = R.ok ? gl[e] : 0.f;
         float dot = 0.f;   // g . num over this lane's channels
 #pragma unroll
         for (int r = 0; r < RT; ++r)
@@ -241,7 +252,7 @@ __global__ __launch_bounds__(512) void bwd_query_bf16(const uint16_t* __restrict
             }
         float ql[4 * RT];
 #pragma unroll
-        for (int u = 0; u < RT / 2; ++u) unpack8(qo[u], ql + 8 * u);
+        for (int u = 0; u < RT / 2; ++u) unpack8(R.qo[u], ql + 8 * u);
         uint32_t wv[2 * RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -254,7 +265,7 @@ __global__ __launch_bounds__(512) void bwd_query_bf16(const uint16_t* __restrict
             wv[2 * rt] = pack_bf16(x[0], x[1]);
             wv[2 * rt + 1] = pack_bf16(x[2], x[3]);
         }
-        store_rows<D>(sout, wv, lane, off, ok, rsrc, olane);
+        store_rows<D>(sout, wv, lane, R.off, R.ok, rsrc, olane);
 
         // ---- dSt += u dnum^T and dzt += u dden over these 16 tokens.
 #pragma unroll
@@ -289,7 +300,9 @@ __global__ __launch_bounds__(512) void bwd_query_bf16(const uint16_t* __restrict
             dzacc[rc] = mfma_k16(dhi, bu[rc], dzacc[rc]);
             dzacc[rc] = mfma_k16(dlo, bu[rc], dzacc[rc]);
         }
-    }
+    };
+    // The next group's loads are in flight while this one is computed.
+    pipelined<1, Raw>(0, 1, nit, load, compute);
 
     // ---- the block's record: dSt as [e][c] (element (c, e) at e*D + c), then dzt[c].
     uint16_t* rec = dSt + (size_t)blk * REC;
@@ -368,24 +381,30 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
     const int olane = h * D * 2;
 
     const int nit = (g.T + 15) >> 4;
-    for (int it = 0; it < nit; ++it) {
-        const int p = it * 16 + t;
-        const bool ok = p < g.T;
-        const int off = (origin + in_block(g, ok ? p : g.T - 1)) * row;
+    struct Raw {
         u32x4 kv[KS], vv[KS], ko[RT / 2];
+        int off;
+        bool ok;
+    };
+    auto load = [&](int it, Raw& R) {
+        const int p = it * 16 + t;
+        R.ok = p < g.T;
+        R.off = (origin + in_block(g, R.ok ? p : g.T - 1)) * row;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            kv[kk] = *reinterpret_cast<const u32x4*>(kb + off + kk * 32 + gq * 8);
-            vv[kk] = *reinterpret_cast<const u32x4*>(vb + off + kk * 32 + gq * 8);
+            R.kv[kk] = *reinterpret_cast<const u32x4*>(kb + R.off + kk * 32 + gq * 8);
+            R.vv[kk] = *reinterpret_cast<const u32x4*>(vb + R.off + kk * 32 + gq * 8);
         }
 #pragma unroll
-        for (int u = 0; u < RT / 2; ++u) ko[u] = *reinterpret_cast<const u32x4*>(kb + off + 4 * RT * gq + 8 * u);
+        for (int u = 0; u < RT / 2; ++u) R.ko[u] = *reinterpret_cast<const u32x4*>(kb + R.off + 4 * RT * gq + 8 * u);
+    };
+    auto compute = [&](const Raw& R) {
         u32x4 ba[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int w = 0; w < 4; ++w)
-                ba[kk][w] = pack_bf16(phi_fast(bf_lo(kv[kk][w])), phi_fast(bf_hi(kv[kk][w])));
+                ba[kk][w] = pack_bf16(phi_fast(bf_lo(R.kv[kk][w])), phi_fast(bf_hi(R.kv[kk][w])));
         f32x4 accv[RT], acck[RT];
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
@@ -397,7 +416,7 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 accv[r] = mfma_bf16(a3[r][kk], ba[kk], accv[r]);
-                acck[r] = mfma_bf16(a4[r][kk], vv[kk], acck[r]);
+                acck[r] = mfma_bf16(a4[r][kk], R.vv[kk], acck[r]);
             }
         uint32_t wv[2 * RT];
 #pragma unroll
@@ -405,10 +424,10 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
             wv[2 * r] = pack_bf16(accv[r][0], accv[r][1]);
             wv[2 * r + 1] = pack_bf16(accv[r][2], accv[r][3]);
         }
-        store_rows<D>(sout, wv, lane, off, ok, rv, olane);
+        store_rows<D>(sout, wv, lane, R.off, R.ok, rv, olane);
         float kl[4 * RT];
 #pragma unroll
-        for (int u = 0; u < RT / 2; ++u) unpack8(ko[u], kl + 8 * u);
+        for (int u = 0; u < RT / 2; ++u) unpack8(R.ko[u], kl + 8 * u);
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             float x[4];
@@ -420,8 +439,10 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
             wv[2 * r] = pack_bf16(x[0], x[1]);
             wv[2 * r + 1] = pack_bf16(x[2], x[3]);
         }
-        store_rows<D>(sout, wv, lane, off, ok, rk, olane);
-    }
+        store_rows<D>(sout, wv, lane, R.off, R.ok, rk, olane);
+    };
+    // The next group's loads are in flight while this one is computed.
+    pipelined<1, Raw>(0, 1, nit, load, compute);
 }
 
 // =====================================================================
@@ -460,20 +481,25 @@ __global__ __launch_bounds__(512) void dw_partial_bf16(const uint16_t* __restric
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int KT = P * KPR;
-    for (int ks = s; ks < KT; ks += nsplit) {
+    struct Ops {
+        u32x4 A[2], B[4];
+    };
+    auto load = [&](int ks, Ops& o) {
         const int bh = ks / KPR, col = (ks - bh * KPR) * 32 + gq * 8;
         const size_t rb = (size_t)bh * M;
-        u32x4 A[2], B[4];
 #pragma unroll
-        for (int a = 0; a < 2; ++a) A[a] = *reinterpret_cast<const u32x4*>(dSt + (rb + ri[a]) * REC + col) & mi[a];
+        for (int a = 0; a < 2; ++a) o.A[a] = *reinterpret_cast<const u32x4*>(dSt + (rb + ri[a]) * REC + col);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) B[c] = *reinterpret_cast<const u32x4*>(SZ + (rb + rj[c]) * REC + col) & mj[c];
+        for (int c = 0; c < 4; ++c) o.B[c] = *reinterpret_cast<const u32x4*>(SZ + (rb + rj[c]) * REC + col);
+    };
+    auto compute = [&](const Ops& o) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(A[a], B[c], acc[a][c]);
-    }
+            for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(o.A[a] & mi[a], o.B[c] & mj[c], acc[a][c]);
+    };
+    // Two later k-steps in flight while one is multiplied.
+    pipelined<2, Ops>(s, nsplit, P * KPR, load, compute);
     float* out = part + (size_t)s * M * M;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -486,19 +512,22 @@ __global__ __launch_bounds__(512) void dw_partial_bf16(const uint16_t* __restric
             }
 }
 
+// dW[x] = sum over splits in split order; eight partial sums in flight per thread.
 __global__ __launch_bounds__(256) void dw_reduce(const float* __restrict__ part, float* __restrict__ dW, int MM,
                                                  int nsplit) {
     const int x = blockIdx.x * blockDim.x + threadIdx.x;
     if (x >= MM) return;
     float s = 0.f;
-    for (int k = 0; k < nsplit; ++k) s += part[(size_t)k * MM + x];
+    int k = 0;
+    for (; k + 8 <= nsplit; k += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(k + u) * MM + x];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; k < nsplit; ++k) s += part[(size_t)k * MM + x];
     dW[x] = s;
-}
-
-// W^T in the mixing kernel's operand order.
-__global__ __launch_bounds__(256) void convert_wt(const float* __restrict__ W, uint16_t* __restrict__ Wb,
-                                                  const WConv wc) {
-    convert_w(W, Wb, wc);
 }
 
 // The mixing product with W^T over the gradient records.
@@ -524,24 +553,20 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     if (err != hipSuccess) return err;
     rec(B, 1);
     const int IT = (g.M + 63) / 64, NK = (g.M + 31) / 32;
-    WConv wc;
-    wc.M = g.M;
-    wc.NK = NK;
-    wc.nchunks = IT * 64 * NK * 32 / 8;
-    wc.first_wg = 0;
-    wc.transpose = 1;
-    convert_wt<<<(wc.nchunks + 255) / 256, 256, 0, L.stream>>>(L.W, B.wbt, wc);
-    const Geo gh = [&] {
+    // Head groups: at most `maxw` heads (one wave each) per workgroup, balanced.
+    auto heads = [&](int maxw) {
         Geo x = g;
-        x.HG = (g.H + 7) / 8;
+        x.HG = (g.H + maxw - 1) / maxw;
         x.G = (g.H + x.HG - 1) / x.HG;
         x.div_HG = make_fastdiv((uint32_t)x.HG);
         return x;
-    }();
-    const int grid_tok = gh.B * gh.M * gh.HG, block_tok = 64 * gh.G;
-    bwd_query_bf16<D><<<grid_tok, block_tok, 0, L.stream>>>(
+    };
+    const Geo gq = heads(D == 64 ? 4 : 8);
+    bwd_query_bf16<D><<<gq.B * gq.M * gq.HG, 64 * gq.G, 0, L.stream>>>(
         static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(B.dout), static_cast<const uint16_t*>(L.st),
-        L.zt, static_cast<uint16_t*>(B.dq), B.dst, gh);
+        L.zt, static_cast<uint16_t*>(B.dq), B.dst, gq);
+    const Geo gh = heads(8);
+    const int grid_tok = gh.B * gh.M * gh.HG, block_tok = 64 * gh.G;
     rec(B, 2);
     MixGeo mg;
     mg.CT = (D * D + D + 63) / 64;

@@ -28,6 +28,7 @@ struct Launch {
     void* st;      // mixed      [BH][M][D*D]       (compute type)
     float* zt;     // mixed normalisers [BH][M][D]  (fp32)
     void* wb;      // bf16 path: W as bf16 [roundup(M,64)][roundup(M,32)], zero padded
+    void* wbt;     // bf16 path: W^T in the same form as well (backward), or nullptr
     Geo g;
     Tuning tune;
     int path;                     // MHLA_PATH_*

@@ -180,6 +180,7 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
     L.st = base + lay.st;
     L.zt = reinterpret_cast<float*>(base + lay.zt);
     L.wb = base + lay.wb;
+    L.wbt = nullptr;
     L.g = make_geo(s, grid->eps);
     L.tune = choose_tuning(s);
     {
@@ -289,6 +290,7 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
     L.st = base + lay.fwd.st;
     L.zt = reinterpret_cast<float*>(base + lay.fwd.zt);
     L.wb = base + lay.fwd.wb;
+    L.wbt = base + lay.wbt;
     L.g = make_geo(s, grid->eps);
     L.tune = choose_tuning(s);
     L.path = MHLA_PATH_3KERNEL;
