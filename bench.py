@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--out", default="", help="also write the JSON line to this file")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dq, dk, dv, dW) instead of the forward (bf16, d <= 64)")
+    ap.add_argument("--block", default="", help="override the block extents, e.g. 32x32 (token-level head count sweeps)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size")
     ap.add_argument("--heads", type=int, default=0, help="override the workload's head count")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -281,6 +282,8 @@ def main():
     p = synth.CONFIGS[args.config]
     if args.batch or args.heads:
         p = p.with_(batch=args.batch or p.batch, heads=args.heads or p.heads)
+    if args.block:
+        p = p.with_(block=tuple(int(x) for x in args.block.lower().split("x")))
     if args.backward:
         bench_backward(args, p, torch, mh, synth)
         return
@@ -362,7 +365,7 @@ def main():
                       "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
     traffic = measured_traffic(p.name) if (args.path == "3kernel" and args.w == "gaussian"
-                                           and not args.batch and not args.heads) else {}
+                                           and not args.batch and not args.heads and not args.block) else {}
     for n in kernels:
         kernels[n]["traffic"] = traffic.get(n)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS,

@@ -31,6 +31,7 @@ SMALL = [
     ("bf-d32-T1", 1, 1, 32, (6, 6), (1, 1), BF, 1.0),
     ("bf-d32-M10", 1, 3, 32, (15, 10), (3, 5), BF, 0.5),
     ("bf-d32-M360", 1, 1, 32, (36, 40), (2, 2), BF, 1.0),
+    ("bf-d32-M1024", 1, 2, 32, (64, 64), (2, 2), BF, 1.0),
     ("bf-d128-T200", 1, 1, 128, (20, 40), (10, 20), BF, 1.0),
     ("f32-d32-T15", 1, 2, 32, (12, 20), (3, 5), F, 1.0),
     ("f32-d64-3d", 2, 1, 64, (8, 16, 8), (2, 4, 4), F, 1.0),
@@ -148,9 +149,11 @@ def test_full_workloads_sampled_pairs(cfg_index):
 
 @pytest.mark.parametrize("w_kind", ["identity", "ones", "local"])
 @pytest.mark.parametrize("path", [mh.MHLA_PATH_3KERNEL, mh.MHLA_PATH_FUSED], ids=["3kernel", "fused"])
-def test_special_coefficient_matrices(w_kind, path):
+@pytest.mark.parametrize("shape", [((64, 64), (8, 8)), ((64, 64), (2, 2))], ids=["M64", "M1024"])
+def test_special_coefficient_matrices(w_kind, path, shape):
     """W = I (per-block attention), W = 1/M (global attention), sparse local W."""
-    p = synth.Problem("special", 1, 2, 64, (64, 64), (8, 8))
+    grid, block = shape
+    p = synth.Problem("special", 1, 2, 64 if block[0] == 8 else 32, grid, block)
     q, k, v, W = synth.make_inputs(p, seed=23, w_kind=w_kind)
     ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)
     out = to_host64(Run(p, q, k, v, W).forward(path))
