@@ -119,4 +119,34 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 
 __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// Nonzero weights of one row of W for a workgroup of 256 threads: entries
+// [base, base + 256) of the row wr (length M) are scanned, and the nonzero
+// ones are written in index order to idx[0..n) / wt[0..n) (LDS) by a wave
+// ballot and a prefix count over the four waves; n is returned to every
+// thread.  wcnt: 4 ints of LDS.  Ends with a workgroup barrier.
+__device__ __forceinline__ int compact_nonzero(const float* __restrict__ wr, int M, int base, int* idx,
+                                               float* wt, int* wcnt) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int j = base + tid;
+    const float w = j < M ? wr[j] : 0.f;
+    const bool nz = w != 0.f;
+    const unsigned long long m = __ballot(nz);
+    const int pre = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int off = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = wcnt[k];
+        off += k < wave ? c : 0;
+        total += c;
+    }
+    if (nz) {
+        idx[off + pre] = j;
+        wt[off + pre] = w;
+    }
+    __syncthreads();
+    return total;
+}
+
 }  // namespace mhla

@@ -555,22 +555,29 @@ __global__ __launch_bounds__(256) void query_apply_fused_bf16(const uint16_t* __
         for (int s = 0; s < 8; ++s) acc[u][s] = 0.f;
     const float* wr = W + (size_t)i * M;
     const uint16_t* base = SZ + (size_t)bh * M * REC;
-    for (int jj = 0; jj < M; ++jj) {
-        const float w = wr[jj];
-        if (w == 0.f) continue;
-        const uint16_t* src = base + (size_t)jj * REC;
+    __shared__ int s_idx[256], s_cnt[4];
+    __shared__ float s_w[256];
+    // Row i of W 256 entries at a time: the nonzero weights are listed first,
+    // so a sparse row costs only its nonzeros.
+    for (int j0 = 0; j0 < M; j0 += 256) {
+        const int n = compact_nonzero(wr, M, j0, s_idx, s_w, s_cnt);
+        for (int t = 0; t < n; ++t) {
+            const float w = s_w[t];
+            const uint16_t* src = base + (size_t)s_idx[t] * REC;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int ch = tid + 256 * u;
-            if (ch < NCH) {
-                const u32x4 x = *reinterpret_cast<const u32x4*>(src + ch * 8);
+            for (int u = 0; u < NU; ++u) {
+                const int ch = tid + 256 * u;
+                if (ch < NCH) {
+                    const u32x4 x = *reinterpret_cast<const u32x4*>(src + ch * 8);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    acc[u][2 * s] += w * bf_lo(x[s]);
-                    acc[u][2 * s + 1] += w * bf_hi(x[s]);
+                    for (int s = 0; s < 4; ++s) {
+                        acc[u][2 * s] += w * bf_lo(x[s]);
+                        acc[u][2 * s + 1] += w * bf_hi(x[s]);
+                    }
                 }
             }
         }
+        __syncthreads();   // the list is rebuilt by the next pass
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {

@@ -305,18 +305,24 @@ __global__ __launch_bounds__(256) void query_apply_fused_f32(const float* __rest
     for (int u = 0; u < NU; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     const float* wr = W + (size_t)i * M;
     const float* base = SZ + (size_t)bh * M * REC;
-    for (int jj = 0; jj < M; ++jj) {
-        const float w = wr[jj];
-        if (w == 0.f) continue;
-        const float* src = base + (size_t)jj * REC;
+    __shared__ int s_idx[256], s_cnt[4];
+    __shared__ float s_w[256];
+    // Row i of W 256 entries at a time, nonzero weights listed first.
+    for (int j0 = 0; j0 < M; j0 += 256) {
+        const int n = compact_nonzero(wr, M, j0, s_idx, s_w, s_cnt);
+        for (int t = 0; t < n; ++t) {
+            const float w = s_w[t];
+            const float* src = base + (size_t)s_idx[t] * REC;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int ch = tid + 256 * u;
-            if (ch < NCH) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * ch);
-                acc[u] += w * x;
+            for (int u = 0; u < NU; ++u) {
+                const int ch = tid + 256 * u;
+                if (ch < NCH) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * ch);
+                    acc[u] += w * x;
+                }
             }
         }
+        __syncthreads();
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
