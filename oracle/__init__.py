@@ -78,6 +78,10 @@ def _load():
                                               dp, dp, dp, dp, ctypes.c_int32]
         lib.mhla_oracle_summaries.restype = ctypes.c_int
         lib.mhla_oracle_backward.argtypes = [vp, vp, vp, fp, vp, P, dp, dp, dp, dp, ctypes.c_int32, ip]
+        lib.mhla_oracle_chunks_contiguous.argtypes = [P]
+        lib.mhla_oracle_chunks_contiguous.restype = ctypes.c_int
+        lib.mhla_oracle_forward_causal.argtypes = [vp, vp, vp, fp, P, ip, ctypes.c_int32, dp, ctypes.c_int32]
+        lib.mhla_oracle_forward_causal.restype = ctypes.c_int
         lib.mhla_oracle_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -214,6 +218,30 @@ def backward(q, k, v, W, dout, grid, block, eps=1e-6, threads=0, return_threads=
     return ((dq, dk, dv, dW), used.value) if return_threads else (dq, dk, dv, dW)
 
 
+def forward_causal(q, k, v, W, grid, block, eps=1e-6, pairs=None, threads=0):
+    """Causal chunkwise float64 forward (chunks contiguous in raster order).
+    Same shapes as ``forward``."""
+    q, k, v, W, B, N, H, d, dt = _prep(q, k, v, W, grid, block)
+    p = _problem(grid, block, H, d, B, dt, eps)
+    if _load().mhla_oracle_chunks_contiguous(ctypes.byref(p)) != 1:
+        raise ValueError("causal form needs blocks that are contiguous in raster order")
+    if pairs is None:
+        sel, nsel = None, B * H
+    else:
+        sel = np.ascontiguousarray(pairs, dtype=np.int32)
+        nsel = len(sel)
+    out = np.empty((nsel, N, d), dtype=np.float64)
+    rc = _load().mhla_oracle_forward_causal(
+        _ptr(q), _ptr(k), _ptr(v), W.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), ctypes.byref(p),
+        None if sel is None else sel.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), nsel,
+        out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    if pairs is None:
+        out = out.reshape(B, H, N, d).transpose(0, 2, 1, 3)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Materialised N x N form (numpy)
 # ---------------------------------------------------------------------------
@@ -274,3 +302,21 @@ def bruteforce(q, k, v, W, grid, block, eps=1e-6, pairs=None, rows=None):
         b, h = divmod(int(s), H)
         res.append(bruteforce_head(Q[b, :, h], K[b, :, h], V[b, :, h], W, bid, eps, rows))
     return np.stack(res)
+
+
+def bruteforce_causal_head(qh, kh, vh, W, bid, eps) -> np.ndarray:
+    """Causal N x N form for one head: A[n, m] as above for m <= n (raster order), else 0."""
+    A = np.tril(attention_matrix(qh, kh, W, bid))
+    return (A @ vh) / (A.sum(axis=1) + eps)[:, None]
+
+
+def bruteforce_causal(q, k, v, W, grid, block, eps=1e-6):
+    """Causal brute force for every (b, h) pair: [B, N, H, d] float64."""
+    B, N, H, d = k.shape
+    bid = token_blocks(grid, block)
+    Q, K, V = decode(q), decode(k), decode(v)
+    out = np.empty((B, N, H, d))
+    for b in range(B):
+        for h in range(H):
+            out[b, :, h, :] = bruteforce_causal_head(Q[b, :, h], K[b, :, h], V[b, :, h], W, bid, eps)
+    return out

@@ -424,3 +424,148 @@ int mhla_oracle_backward(const void* q, const void* k, const void* v, const floa
     free(parts); free(tids); free(args);
     return 0;
 }
+
+/* =====================================================================
+ * Causal chunkwise form (paperlayer.ai summary, appendix B "Causal MHLA":
+ * block-specific mixtures reused per block, causality preserved).  The
+ * attention matrix is the MHLA matrix restricted to m <= n in raster order:
+ *   A[n, m] = W[b(n), b(m)] phi(q_n) . phi(k_m)   for m <= n, else 0,
+ *   o_n = sum_m A[n, m] v_m / (sum_m A[n, m] + eps).
+ * For chunks that are contiguous in raster order this is, for query n in
+ * chunk i: the mixture of the earlier chunks' summaries, sum_{j < i} W[i,j] S_j
+ * (and z likewise), plus W[i,i] times the running summary of chunk i's own
+ * tokens up to n.
+ * ===================================================================== */
+
+typedef struct {
+    const void *q, *k, *v;
+    const float* W;
+    const mhla_oracle_problem* p;
+    const geom* G;
+    double* out;   /* this pair's [N][d] */
+} causal_job;
+
+static void run_pair_causal(const causal_job* J, int32_t b, int32_t h) {
+    const geom* G = J->G;
+    const int64_t H = J->p->heads, d = J->p->head_dim, N = G->N, M = G->M;
+    const int dt = J->p->dtype;
+    const int64_t row = H * d;
+    const int64_t base = (int64_t)b * N * row + (int64_t)h * d;
+    double* S = calloc((size_t)(M * d * d), sizeof(double));
+    double* z = calloc((size_t)(M * d), sizeof(double));
+    double* St = malloc((size_t)(d * d) * sizeof(double));   /* earlier chunks' mixture + own prefix */
+    double* zt = malloc((size_t)d * sizeof(double));
+    double* P = malloc((size_t)(d * d) * sizeof(double));    /* running summary of the own chunk */
+    double* zP = malloc((size_t)d * sizeof(double));
+    double* fk = malloc((size_t)d * sizeof(double));
+    double* vv = malloc((size_t)d * sizeof(double));
+    if (!S || !z || !St || !zt || !P || !zP || !fk || !vv) abort();
+    for (int64_t m = 0; m < N; ++m) {
+        int64_t j = block_of(G, m);
+        for (int64_t c = 0; c < d; ++c) fk[c] = mhla_oracle_phi(load_elem(J->k, dt, base + m * row + c));
+        for (int64_t e = 0; e < d; ++e) vv[e] = load_elem(J->v, dt, base + m * row + e);
+        for (int64_t c = 0; c < d; ++c) {
+            z[j * d + c] += fk[c];
+            for (int64_t e = 0; e < d; ++e) S[j * d * d + c * d + e] += fk[c] * vv[e];
+        }
+    }
+    /* Tokens in raster order; chunks are contiguous, so a chunk starts when
+     * the block id changes. */
+    int64_t cur = -1;
+    double wii = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t i = block_of(G, n);
+        if (i != cur) {
+            cur = i;
+            memset(P, 0, (size_t)(d * d) * sizeof(double));
+            memset(zP, 0, (size_t)d * sizeof(double));
+            memset(St, 0, (size_t)(d * d) * sizeof(double));
+            memset(zt, 0, (size_t)d * sizeof(double));
+            for (int64_t j = 0; j < i; ++j) {
+                const double w = (double)J->W[i * M + j];
+                for (int64_t t = 0; t < d * d; ++t) St[t] += w * S[j * d * d + t];
+                for (int64_t c = 0; c < d; ++c) zt[c] += w * z[j * d + c];
+            }
+            wii = (double)J->W[i * M + i];
+        }
+        /* the own chunk's prefix grows by token n before n reads it (m <= n) */
+        for (int64_t c = 0; c < d; ++c) fk[c] = mhla_oracle_phi(load_elem(J->k, dt, base + n * row + c));
+        for (int64_t e = 0; e < d; ++e) vv[e] = load_elem(J->v, dt, base + n * row + e);
+        for (int64_t c = 0; c < d; ++c) {
+            zP[c] += fk[c];
+            for (int64_t e = 0; e < d; ++e) P[c * d + e] += fk[c] * vv[e];
+        }
+        double* fq = fk;
+        for (int64_t c = 0; c < d; ++c) fq[c] = mhla_oracle_phi(load_elem(J->q, dt, base + n * row + c));
+        double den = J->p->eps;
+        for (int64_t c = 0; c < d; ++c) den += fq[c] * (zt[c] + wii * zP[c]);
+        for (int64_t e = 0; e < d; ++e) {
+            double num = 0.0;
+            for (int64_t c = 0; c < d; ++c) num += fq[c] * (St[c * d + e] + wii * P[c * d + e]);
+            J->out[n * d + e] = num / den;
+        }
+    }
+    free(S); free(z); free(St); free(zt); free(P); free(zP); free(fk); free(vv);
+}
+
+typedef struct {
+    causal_job proto;
+    const int32_t* sel;
+    int32_t nsel, nthreads, tid;
+} causal_worker_arg;
+
+static void* causal_worker(void* arg) {
+    const causal_worker_arg* A = (const causal_worker_arg*)arg;
+    const int64_t N = A->proto.G->N, d = A->proto.p->head_dim, H = A->proto.p->heads;
+    for (int32_t s = A->tid; s < A->nsel; s += A->nthreads) {
+        const int32_t pair = A->sel ? A->sel[s] : s;
+        causal_job J = A->proto;
+        J.out = A->proto.out + (int64_t)s * N * d;
+        run_pair_causal(&J, (int32_t)(pair / H), (int32_t)(pair % H));
+    }
+    return NULL;
+}
+
+int mhla_oracle_chunks_contiguous(const mhla_oracle_problem* p) {
+    geom G;
+    if (make_geom(p, &G) != 0) return -1;
+    /* A block is one run of raster indices iff some axis a splits it while every
+     * faster axis is covered whole and every slower axis has extent 1. */
+    for (int a = 0; a < p->ndim; ++a) {
+        int ok = 1;
+        for (int x = 0; x < a; ++x) ok &= p->block[x] == 1;
+        for (int x = a + 1; x < p->ndim; ++x) ok &= p->block[x] == p->grid[x];
+        if (ok) return 1;
+    }
+    return 0;
+}
+
+int mhla_oracle_forward_causal(const void* q, const void* k, const void* v, const float* W,
+                               const mhla_oracle_problem* p, const int32_t* sel, int32_t nsel, double* out,
+                               int32_t threads) {
+    geom G;
+    if (make_geom(p, &G) != 0 || !out) return -1;
+    if (mhla_oracle_chunks_contiguous(p) != 1) return -1;
+    const int64_t pairs = (int64_t)p->batch * p->heads;
+    if (!sel) nsel = (int32_t)pairs;
+    if (nsel < 0) return -1;
+    for (int32_t s = 0; sel && s < nsel; ++s)
+        if (sel[s] < 0 || sel[s] >= pairs) return -1;
+    if (nsel > 0 && (!q || !k || !v || !W)) return -1;
+    if (threads <= 0) threads = (int32_t)sysconf(_SC_NPROCESSORS_ONLN);
+    if (threads < 1) threads = 1;
+    if (threads > nsel) threads = nsel > 0 ? nsel : 1;
+    if (nsel == 0) return 0;
+    pthread_t* tids = malloc(sizeof(pthread_t) * (size_t)threads);
+    causal_worker_arg* args = malloc(sizeof(causal_worker_arg) * (size_t)threads);
+    if (!tids || !args) abort();
+    for (int32_t t = 0; t < threads; ++t) {
+        causal_worker_arg a = {{q, k, v, W, p, &G, out}, sel, nsel, threads, t};
+        args[t] = a;
+    }
+    for (int32_t t = 1; t < threads; ++t) pthread_create(&tids[t], NULL, causal_worker, &args[t]);
+    causal_worker(&args[0]);
+    for (int32_t t = 1; t < threads; ++t) pthread_join(tids[t], NULL);
+    free(tids); free(args);
+    return 0;
+}

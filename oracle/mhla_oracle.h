@@ -78,6 +78,18 @@ int mhla_oracle_backward(const void* q, const void* k, const void* v, const floa
                          const mhla_oracle_problem* p, double* dq, double* dk, double* dv, double* dW,
                          int32_t threads, int32_t* threads_used);
 
+/* 1 if every block is one contiguous run of raster indices (some axis is
+ * split while all faster axes are covered whole and all slower axes have
+ * block extent 1), 0 if not, -1 for an invalid problem. */
+int mhla_oracle_chunks_contiguous(const mhla_oracle_problem* p);
+
+/* Causal chunkwise forward (appendix B "Causal MHLA"): the attention matrix
+ * above restricted to m <= n in raster order.  Needs contiguous chunks.
+ * Same selection and output conventions as mhla_oracle_forward. */
+int mhla_oracle_forward_causal(const void* q, const void* k, const void* v, const float* W,
+                               const mhla_oracle_problem* p, const int32_t* sel, int32_t nsel, double* out,
+                               int32_t threads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,106 @@
+"""Pins of the oracle's causal chunkwise form (paperlayer.ai summary,
+appendix B "Causal MHLA": block-specific mixtures reused per block, causality
+preserved), against what the definition fixes:
+
+* the materialised N x N form with the causal mask m <= n (numpy);
+* one block: textbook causal linear attention, written with prefix sums;
+* the first token's closed form;
+* causality itself: the output ignores the coefficients W[i, j] with j > i
+  and the keys/values of later tokens.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from token_level_head_block_amd import synth
+
+
+def rel_err(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# name, B, H, d, grid, block, dtype: chunks contiguous in raster order
+CASES = [
+    ("seq-1d", 1, 2, 8, (1, 48), (1, 8), synth.F32),
+    ("rows-2d", 2, 1, 8, (6, 5), (2, 5), synth.BF16),
+    ("frames-3d", 1, 2, 4, (4, 3, 4), (2, 3, 4), synth.F32),
+    ("T1", 1, 1, 8, (1, 12), (1, 1), synth.BF16),
+]
+
+
+def make(case, seed, eps=1e-3):
+    name, B, H, d, grid, block, dt = case
+    p = synth.Problem(name, B, H, d, grid, block, dtype=dt, eps=eps)
+    return p, synth.make_inputs(p, seed=seed)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_causal_blockwise_equals_masked_bruteforce(oracle_lib, case):
+    p, (q, k, v, W) = make(case, seed=51)
+    got = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    ref = oracle.bruteforce_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    assert rel_err(got, ref) < 1e-12
+
+
+def test_one_block_is_causal_linear_attention(oracle_lib):
+    case = ("seq", 1, 2, 8, (1, 40), (1, 40), synth.F32)
+    p, (q, k, v, _) = make(case, seed=52)
+    W = np.array([[1.0]], dtype=np.float32)
+    got = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    Q, K, V = (oracle.decode(x) for x in (q, k, v))
+    for h in range(p.heads):
+        u, a, vv = oracle.phi_np(Q[0, :, h]), oracle.phi_np(K[0, :, h]), V[0, :, h]
+        S = np.cumsum(a[:, :, None] * vv[:, None, :], axis=0)     # sum_{m <= n} a_m v_m^T
+        z = np.cumsum(a, axis=0)
+        num = np.einsum("nc,nce->ne", u, S)
+        den = np.einsum("nc,nc->n", u, z) + p.eps
+        assert rel_err(got[0, :, h], num / den[:, None]) < 1e-12
+
+
+def test_first_token_closed_form(oracle_lib):
+    p, (q, k, v, W) = make(CASES[0], seed=53)
+    got = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    Q, K, V = (oracle.decode(x) for x in (q, k, v))
+    for h in range(p.heads):
+        s = float(W[0, 0]) * float(oracle.phi_np(Q[0, 0, h]) @ oracle.phi_np(K[0, 0, h]))
+        np.testing.assert_allclose(got[0, 0, h], s * V[0, 0, h] / (s + p.eps), rtol=1e-13)
+
+
+def test_causality(oracle_lib):
+    case = ("seq", 1, 2, 8, (1, 64), (1, 8), synth.F32)
+    p, (q, k, v, W) = make(case, seed=54)
+    base = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    # coefficients of later blocks are never read
+    W2 = W.copy()
+    W2[np.triu_indices(W.shape[0], 1)] = 7.0
+    np.testing.assert_array_equal(oracle.forward_causal(q, k, v, W2, p.grid, p.block, eps=p.eps), base)
+    # the last token's key and value reach no earlier output
+    k2, v2 = k.copy(), v.copy()
+    k2[:, -1] += 1.5
+    v2[:, -1] -= 2.0
+    out = oracle.forward_causal(q, k2, v2, W, p.grid, p.block, eps=p.eps)
+    np.testing.assert_array_equal(out[:, :-1], base[:, :-1])
+    assert rel_err(out[:, -1], base[:, -1]) > 1e-6
+    # ... while the non-causal form depends on both
+    assert rel_err(oracle.forward(q, k, v, W2, p.grid, p.block, eps=p.eps),
+                   oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)) > 1e-3
+
+
+def test_causal_rejects_chunks_not_contiguous(oracle_lib):
+    p = synth.Problem("blocks", 1, 1, 8, (8, 8), (4, 4), dtype=synth.F32)
+    q, k, v, W = synth.make_inputs(p, seed=55)
+    with pytest.raises(ValueError):
+        oracle.forward_causal(q, k, v, W, p.grid, p.block)
+
+
+def test_causal_pins_catch_planted_mistakes(oracle_lib):
+    p, (q, k, v, W) = make(CASES[0], seed=56)
+    ref = oracle.bruteforce_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    run = lambda q_, k_, v_, W_: oracle.forward_causal(q_, k_, v_, W_, p.grid, p.block, eps=p.eps)
+    planted = {
+        "transposed W": run(q, k, v, np.ascontiguousarray(W.T)),
+        "q and k swapped": run(k, q, v, W),
+        "no causal mask": oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps),
+    }
+    for name, out in planted.items():
+        assert rel_err(out, ref) > 1e-3, name
