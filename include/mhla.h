@@ -89,8 +89,17 @@ typedef struct mhla_block {
 /* Path selection for mhla_forward_ex. */
 enum {
     MHLA_PATH_3KERNEL = 0,   /* block_kv_summary -> mix_summaries -> query_apply */
-    MHLA_PATH_FUSED = 1      /* block_kv_summary -> query_apply_fused (mixes per query
+    MHLA_PATH_FUSED = 1,     /* block_kv_summary -> query_apply_fused (mixes per query
                                 block on the fly, skipping zero W entries) */
+    MHLA_PATH_CAUSAL = 2     /* causal chunkwise form (paperlayer.ai summary, appendix B
+                                "Causal MHLA"): token n attends to tokens m <= n in raster
+                                order, A[n,m] = W[b(n),b(m)] phi(q_n).phi(k_m); query block i
+                                mixes the summaries of blocks j < i and adds W[i,i] times its
+                                own block's tokens up to n.  block_kv_summary ->
+                                mix_summaries (W restricted to j < i) -> query_apply_causal.
+                                bfloat16, head_dim 32 or 64, and blocks that are contiguous
+                                runs of raster indices (e.g. 1D chunks: grid {1, N}, block
+                                {1, T}); MHLA_ERR_UNSUPPORTED otherwise. */
 };
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -103,11 +112,12 @@ mhla_status mhla_check_problem(const mhla_grid* grid, const mhla_block* block,
                                int64_t* num_blocks, int64_t* block_tokens);
 
 /* The kernels a call with these arguments launches, in order: *num_kernels
- * receives 3 (MHLA_PATH_3KERNEL), 2 (MHLA_PATH_FUSED) or 0 (empty problem)
- * and, if kernel_names is non-NULL, kernel_names[0..2] receive static names
- * of the kernels, NULL past the count: "block_kv_summary", then
- * "mix_summaries" and "query_apply", or "query_apply_fused".  Returns the
- * validation status of grid, block and path; makes no HIP call. */
+ * receives 3 (MHLA_PATH_3KERNEL, MHLA_PATH_CAUSAL), 2 (MHLA_PATH_FUSED) or 0
+ * (empty problem) and, if kernel_names is non-NULL, kernel_names[0..2]
+ * receive static names of the kernels, NULL past the count:
+ * "block_kv_summary", then "mix_summaries" and "query_apply" (or
+ * "query_apply_causal"), or "query_apply_fused".  Returns the validation
+ * status of grid, block and path; makes no HIP call. */
 mhla_status mhla_launch_plan(const mhla_grid* grid, const mhla_block* block, int32_t path,
                              int32_t* num_kernels, const char** kernel_names);
 

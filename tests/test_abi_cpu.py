@@ -171,3 +171,23 @@ def test_backward_workspace_and_validation(L):
     assert bwd(g, b, ws_bytes=need - 16) == mh.MHLA_ERR_INVALID_ARG
     assert bwd(g, b, ws=9 * BIG) == mh.MHLA_ERR_INVALID_ARG             # workspace overlaps dW
     assert bwd(g, mh.make_block((15, 16))) == mh.MHLA_ERR_INVALID_ARG
+
+
+def test_causal_path_validation(L):
+    seq = mh.make_grid(1, 6, 64, mh.MHLA_BF16, (1, 65536))
+    chunk = mh.make_block((1, 256))
+    assert mh.mhla_launch_plan(seq, chunk, mh.MHLA_PATH_CAUSAL) == (
+        mh.MHLA_OK, ["block_kv_summary", "mix_summaries", "query_apply_causal"])
+    # 2D blocks are not contiguous runs of raster indices
+    g, b = cfg2()
+    assert mh.mhla_launch_plan(g, b, mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_ERR_UNSUPPORTED
+    need = mh.mhla_workspace_bytes(g, b)
+    assert call_fwd(L, g, b, ws=6 * BIG, ws_bytes=need, path=mh.MHLA_PATH_CAUSAL) == mh.MHLA_ERR_UNSUPPORTED
+    # full rows are
+    assert mh.mhla_launch_plan(mh.make_grid(1, 2, 32, mh.MHLA_BF16, (12, 20)), mh.make_block((3, 20)),
+                               mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_OK
+    # d = 128 and fp32 are not supported
+    assert mh.mhla_launch_plan(mh.make_grid(1, 2, 128, mh.MHLA_BF16, (1, 256)), mh.make_block((1, 64)),
+                               mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_ERR_UNSUPPORTED
+    assert mh.mhla_launch_plan(mh.make_grid(1, 2, 32, mh.MHLA_F32, (1, 256)), mh.make_block((1, 64)),
+                               mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_ERR_UNSUPPORTED

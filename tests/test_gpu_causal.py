@@ -1,0 +1,102 @@
+"""The causal chunkwise path (MHLA_PATH_CAUSAL) against the float64 oracle's
+causal form, through the C ABI.  Bar: max|d| / max|ref| <= 1e-2 (bf16); where
+the signed W makes the causal denominators cancel, the bar applies to the
+well-conditioned tokens and a rounding bound scaled by the cancellation to the
+rest."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_level_head_block_amd as mh
+from token_level_head_block_amd import synth
+
+from conditioning import BF16_U, causal_denominators
+from gpu_util import Run, TOL, rel_err, say, to_host64
+
+pytestmark = pytest.mark.gpu
+
+BF = synth.BF16
+
+# name, B, H, d, grid, block, std  (blocks are contiguous runs of raster indices)
+CASES = [
+    ("causal-1d-T64", 2, 3, 64, (1, 1024), (1, 64), 1.0),
+    ("causal-1d-T256", 1, 2, 64, (1, 2048), (1, 256), 1.0),
+    ("causal-1d-T15-d32", 1, 3, 32, (1, 240), (1, 15), 1.0),
+    ("causal-1d-T1", 1, 1, 32, (1, 40), (1, 1), 1.0),
+    ("causal-1d-M1", 1, 2, 64, (1, 200), (1, 200), 1.0),
+    ("causal-rows-2d", 1, 2, 32, (12, 20), (3, 20), 0.5),
+    ("causal-frames-3d", 1, 2, 64, (4, 6, 8), (1, 6, 8), 1.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_causal_small(case):
+    name, B, H, d, grid, block, std = case
+    p = synth.Problem(name, B, H, d, grid, block, dtype=BF, std=std)
+    q, k, v, W = synth.make_inputs(p, seed=61)
+    ref = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    out = to_host64(Run(p, q, k, v, W).forward(mh.MHLA_PATH_CAUSAL))
+    err = rel_err(out, ref)
+    say(f"  {name}: max|d|/max|ref| = {err:.3e}")
+    assert np.isfinite(out).all()
+    assert err <= TOL[BF]
+
+
+def check_conditioned(p, q, k, v, W, out, ref, kappa_max=16.0):
+    """Parity with cancellation accounted for.  Tokens whose causal
+    denominator is well conditioned (kappa <= kappa_max) meet the bf16 bar;
+    every token stays within 4 u kappa (max|v| + |o_n|), the first-order
+    effect of rounding W, the block summaries and phi(q) to bf16 (u = 2^-8)."""
+    den, absden = causal_denominators(q, k, W, p.grid, p.block, p.eps)
+    kappa = absden / np.abs(den)                              # [B, N, H]
+    dev = np.abs(out - ref).max(axis=3)
+    scale = np.abs(ref).max()
+    well = kappa <= kappa_max
+    vmax = np.abs(oracle.decode(v)).max(axis=(1, 3))          # [B, H]
+    bound = 4 * BF16_U * kappa * (vmax[:, None, :] + np.abs(ref).max(axis=3))
+    say(f"  {p.name}: kappa max {kappa.max():.1f}, {well.mean():.4f} of tokens <= {kappa_max}; "
+        f"well-conditioned max|d|/max|ref| = {dev[well].max() / scale:.3e}, "
+        f"worst d / bound = {(dev / bound).max():.3f}")
+    assert np.isfinite(out).all()
+    assert well.mean() >= 0.99
+    assert dev[well].max() <= TOL[BF] * scale
+    assert (dev <= bound).all()
+
+
+def test_causal_sequence_workload():
+    """65536 tokens as one sequence in chunks of 256 (the metric workload's size),
+    every output of every pair; a second call is bitwise equal.  This signed W
+    has partial row sums that cancel up to 145-fold, hence the conditioned check."""
+    p = synth.Problem("seq-65536-chunk256", 1, 6, 64, (1, 65536), (1, 256), dtype=BF)
+    q, k, v, W = synth.make_inputs(p, seed=62)
+    ref = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    run = Run(p, q, k, v, W)
+    out = run.forward(mh.MHLA_PATH_CAUSAL)
+    check_conditioned(p, q, k, v, W, to_host64(out), ref)
+    again = run.forward(mh.MHLA_PATH_CAUSAL)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+
+
+def test_causal_sequence_workload_local_w():
+    """Same shape with the nonnegative local prior (kappa = 1): the bf16 bar on every output."""
+    p = synth.Problem("seq-65536-chunk256-local", 1, 6, 64, (1, 65536), (1, 256), dtype=BF)
+    q, k, v, W = synth.make_inputs(p, seed=64, w_kind="local")
+    ref = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    out = to_host64(Run(p, q, k, v, W).forward(mh.MHLA_PATH_CAUSAL))
+    err = rel_err(out, ref)
+    say(f"  {p.name}: max|d|/max|ref| = {err:.3e}")
+    assert err <= TOL[BF]
+
+
+def test_causal_ignores_later_coefficients_and_tokens():
+    p = synth.Problem("causal-check", 1, 2, 64, (1, 512), (1, 64), dtype=BF)
+    q, k, v, W = synth.make_inputs(p, seed=63)
+    base = Run(p, q, k, v, W).forward(mh.MHLA_PATH_CAUSAL)
+    W2 = W.copy()
+    W2[np.triu_indices(W.shape[0], 1)] = 3.0
+    k2, v2 = k.copy(), v.copy()
+    k2[:, -1] = synth.bf16_bits(np.full(k2[:, -1].shape, 2.0, dtype=np.float32))
+    v2[:, -1] = synth.bf16_bits(np.full(v2[:, -1].shape, -5.0, dtype=np.float32))
+    out = Run(p, q, k2, v2, W2).forward(mh.MHLA_PATH_CAUSAL)
+    assert torch.equal(out[:, :-1].contiguous().view(torch.int16), base[:, :-1].contiguous().view(torch.int16))

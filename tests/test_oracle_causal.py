@@ -104,3 +104,22 @@ def test_causal_pins_catch_planted_mistakes(oracle_lib):
     }
     for name, out in planted.items():
         assert rel_err(out, ref) > 1e-3, name
+
+
+def test_conditioning_helper_matches_masked_row_sums(oracle_lib):
+    """The denominators the GPU tests use to measure cancellation equal the row
+    sums of the masked N x N form plus eps, with W and with |W|."""
+    from conditioning import causal_denominators
+    for case in (("seq", 1, 2, 8, (1, 48), (1, 8), synth.F32), ("rows-2d", 2, 1, 8, (6, 5), (2, 5), synth.BF16)):
+        p, (q, k, v, W) = make(case, seed=57)
+        den, absden = causal_denominators(q, k, W, p.grid, p.block, p.eps)
+        bid = oracle.token_blocks(p.grid, p.block)
+        Q, K = oracle.decode(q), oracle.decode(k)
+        N = bid.shape[0]
+        mask = np.tril(np.ones((N, N)))
+        for b in range(p.batch):
+            for h in range(p.heads):
+                S = oracle.phi_np(Q[b, :, h]) @ oracle.phi_np(K[b, :, h]).T * mask
+                Wx = W.astype(np.float64)[bid][:, bid]
+                np.testing.assert_allclose(den[b, :, h], (Wx * S).sum(1) + p.eps, rtol=1e-12)
+                np.testing.assert_allclose(absden[b, :, h], (np.abs(Wx) * S).sum(1), rtol=1e-12)

@@ -31,6 +31,7 @@ MHLA_BF16 = 1
 
 MHLA_PATH_3KERNEL = 0
 MHLA_PATH_FUSED = 1
+MHLA_PATH_CAUSAL = 2
 
 
 class mhla_grid(ctypes.Structure):

@@ -51,6 +51,7 @@ struct WConv {
     int32_t M, NK, nchunks;   // NK = Jpad / 32; nchunks = Ipad * Jpad / 8; 0 = none
     int32_t first_wg;         // workgroups [first_wg, gridDim.x) convert
     uint16_t* wbt;            // if not null, W^T is converted to this buffer as well
+    int32_t causal;           // nonzero: keep only W[i][j] with j < i (earlier blocks)
 };
 
 __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t* __restrict__ Wb,
@@ -75,6 +76,10 @@ __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t*
         } else {
 #pragma unroll
             for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)i * wc.M + j0 + s] : 0.f;
+        }
+        if (wc.causal) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) x[s] = j0 + s < i ? x[s] : 0.f;
         }
         *reinterpret_cast<u32x4*>((tr ? wc.wbt : Wb) + (size_t)c * 8) =
             u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
@@ -284,5 +289,49 @@ __device__ __forceinline__ void split_zt(const float* z, u32x4& hi, u32x4& lo) {
 // prep_load(A) issues the loads of the block's A operands (and keeps zt raw);
 // prep_finish(A) turns raw zt into operands.  Both run after the first batch of
 // Q loads has been issued, so the latencies of St, zt and Q overlap.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x16_bf16: lane l supplies row (or column) l % 16 and
+// k = 4 * (l / 16) + 0..3; output as for the 16x16x32 form.
+__device__ __forceinline__ f32x4 mfma_k16(const u32x2& a, const u32x2& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                     c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float phi_grad(float x) { return x > 0.f ? 1.f : __expf(x); }
+
+// Unpack 8 channels (one 16-byte load) into fp32.
+__device__ __forceinline__ void unpack8(const u32x4& w, float* x) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        x[2 * k] = bf_lo(w[k]);
+        x[2 * k + 1] = bf_hi(w[k]);
+    }
+}
+
+// A 16-token x D tile whose lane (t, gq) holds channels 4*RT*gq .. +4*RT-1 of
+// token t as packed bf16 pairs leaves through the wave's LDS slice and is
+// written as whole token rows by buffer stores; a token past the block's end
+// gets an out-of-range offset, so the hardware drops its write.
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* sout, const uint32_t* wv, int lane, int off, bool ok,
+                                           __amdgpu_buffer_rsrc_t rsrc, int olane) {
+    constexpr int RT = D / 16, OSTR = D + 8, CPR = D / 8;
+    const int t = lane & 15, gq = lane >> 4;
+    uint16_t* srow = sout + t * OSTR + 4 * RT * gq;
+#pragma unroll
+    for (int u = 0; u < RT / 2; ++u)
+        *reinterpret_cast<u32x4*>(srow + 8 * u) = u32x4{wv[4 * u], wv[4 * u + 1], wv[4 * u + 2], wv[4 * u + 3]};
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+        const int tt = k * (64 / CPR) + lane / CPR, chunk = lane % CPR;
+        const int offk = __shfl(off, tt, 64);
+        const int okk = __shfl((int)ok, tt, 64);
+        const u32x4 x = *reinterpret_cast<const u32x4*>(sout + tt * OSTR + chunk * 8);
+        const uint32_t bo = okk ? (uint32_t)(offk * 2 + olane + chunk * 16) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(x, rsrc, bo, 0, 0);
+    }
+}
+
 }  // namespace
 }  // namespace mhla

@@ -686,6 +686,8 @@ hipError_t run_d(const Launch& L) {
     wc.nchunks = fused ? 0 : IT * 64 * NK * 32 / 8;
     wc.first_wg = 0;
     wc.wbt = static_cast<uint16_t*>(L.wbt);
+    const bool causal = L.path == MHLA_PATH_CAUSAL;
+    wc.causal = causal ? 1 : 0;   // mixed summaries of earlier blocks only
     const bool row8 = (g.bk2 % 8) == 0;
 
     record(L, 0);
@@ -723,6 +725,11 @@ hipError_t run_d(const Launch& L) {
         }
         record(L, 2);
         if (L.summaries_only) return hipGetLastError();
+        if (causal) {
+            const hipError_t e = launch_causal_apply_bf16(L);
+            record(L, 3);
+            return e;
+        }
         switch (L.tune.apply_waves) {
             case 1: launch_apply<D, 1>(L, q, st, o); break;
             case 2: launch_apply<D, 2>(L, q, st, o); break;

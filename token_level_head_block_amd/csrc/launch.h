@@ -63,6 +63,10 @@ struct BwdLaunch {
 // Summary and mixing kernels of the bf16 forward only (regions of F).
 hipError_t run_bf16_summaries(const Launch& L);
 hipError_t run_bwd_bf16(const BwdLaunch& B);
+// The causal chunkwise apply (bf16, d = 32 or 64) after the summary and
+// mixing kernels have run with W restricted to earlier blocks.
+hipError_t launch_causal_apply_bf16(const Launch& L);
+
 // p[0 .. n) = 0 by a kernel (safe inside a captured graph).
 hipError_t zero_f32(float* p, int n, hipStream_t stream);
 

@@ -62,6 +62,22 @@ mhla_status check(const mhla_grid* grid, const mhla_block* block, Shape* s) {
     return MHLA_OK;
 }
 
+// Blocks are single runs of raster indices: some axis is split while every
+// faster axis is covered whole and every slower axis has block extent 1.
+bool chunks_contiguous(const Shape& s) {
+    for (int a = 0; a < 3; ++a) {
+        bool ok = true;
+        for (int x = 0; x < a; ++x) ok = ok && s.b[x] == 1;
+        for (int x = a + 1; x < 3; ++x) ok = ok && s.b[x] == s.g[x];
+        if (ok) return true;
+    }
+    return false;
+}
+
+bool causal_supported(const Shape& s) {
+    return s.dtype == MHLA_BF16 && (s.D == 32 || s.D == 64) && chunks_contiguous(s);
+}
+
 struct Layout {
     size_t sz, st, zt, wb, total;   // byte offsets of the regions, total size
 };
@@ -146,7 +162,9 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
     Shape s;
     mhla_status st = check(grid, block, &s);
     if (st != MHLA_OK) return st;
-    if (path != MHLA_PATH_3KERNEL && path != MHLA_PATH_FUSED) return MHLA_ERR_INVALID_ARG;
+    if (path != MHLA_PATH_3KERNEL && path != MHLA_PATH_FUSED && path != MHLA_PATH_CAUSAL)
+        return MHLA_ERR_INVALID_ARG;
+    if (path == MHLA_PATH_CAUSAL && !causal_supported(s)) return MHLA_ERR_UNSUPPORTED;
     if (s.B == 0 || s.H == 0) return MHLA_OK;
     if (!q || !k || !v || !W || !out) return MHLA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(W) || !aligned16(out))
@@ -364,13 +382,18 @@ mhla_status mhla_launch_plan(const mhla_grid* grid, const mhla_block* block, int
     Shape s;
     const mhla_status st = check(grid, block, &s);
     if (st != MHLA_OK) return st;
-    if (path != MHLA_PATH_3KERNEL && path != MHLA_PATH_FUSED) return MHLA_ERR_INVALID_ARG;
+    if (path != MHLA_PATH_3KERNEL && path != MHLA_PATH_FUSED && path != MHLA_PATH_CAUSAL)
+        return MHLA_ERR_INVALID_ARG;
+    if (path == MHLA_PATH_CAUSAL && !causal_supported(s)) return MHLA_ERR_UNSUPPORTED;
     const char* names[3] = {nullptr, nullptr, nullptr};
     int n = 0;
     if (s.B != 0 && s.H != 0) {
         names[n++] = "block_kv_summary";
         if (path == MHLA_PATH_FUSED) {
             names[n++] = "query_apply_fused";
+        } else if (path == MHLA_PATH_CAUSAL) {
+            names[n++] = "mix_summaries";
+            names[n++] = "query_apply_causal";
         } else {
             names[n++] = "mix_summaries";
             names[n++] = "query_apply";
