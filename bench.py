@@ -26,8 +26,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MHLA fwd tokens/s + achieved HBM GB/s (% peak), N=65536 H=6 d=64 bf16"
-KERNEL_SOURCES = ["token_level_head_block_amd/csrc/kernels_bf16.hip", "token_level_head_block_amd/csrc/common.h",
-                  "token_level_head_block_amd/csrc/mhla_api.cpp", "token_level_head_block_amd/csrc/launch.h"]
+KERNEL_SOURCES = ["token_level_head_block_amd/csrc/" + f for f in (
+    "kernels_bf16.hip", "kernels_causal_bf16.hip", "bf16_shared.h", "common.h", "mhla_api.cpp", "launch.h")]
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 MALL_BYTES = 256 << 20          # Infinity Cache
 
@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload index (2 = the metric's workload)")
-    ap.add_argument("--path", choices=["3kernel", "fused"], default="3kernel")
+    ap.add_argument("--path", choices=["3kernel", "fused", "causal"], default="3kernel",
+                    help="causal: the causal chunkwise form; without --block the chunks are the grid's raster rows")
     ap.add_argument("--w", choices=["gaussian", "local", "identity", "ones"], default="gaussian")
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough to exceed 2x the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -104,6 +105,7 @@ def kernel_bytes(p, ws_elem):
         "mix_summaries": sz + w + st + zt,
         "query_apply": tensor + st + zt + tensor,
         "query_apply_fused": tensor + sz + w + tensor,   # every summary read at least once
+        "query_apply_causal": 3 * tensor + st + zt + tensor,   # q, k, v of the chunk once, mixtures, out
     }
 
 
@@ -284,10 +286,13 @@ def main():
         p = p.with_(batch=args.batch or p.batch, heads=args.heads or p.heads)
     if args.block:
         p = p.with_(block=tuple(int(x) for x in args.block.lower().split("x")))
+    elif args.path == "causal":
+        # contiguous chunks: one raster row of the grid each
+        p = p.with_(name=p.name + "-causal-rows", block=(1,) * (len(p.grid) - 1) + (p.grid[-1],))
     if args.backward:
         bench_backward(args, p, torch, mh, synth)
         return
-    path = mh.MHLA_PATH_FUSED if args.path == "fused" else mh.MHLA_PATH_3KERNEL
+    path = {"3kernel": mh.MHLA_PATH_3KERNEL, "fused": mh.MHLA_PATH_FUSED, "causal": mh.MHLA_PATH_CAUSAL}[args.path]
     tensor_bytes = p.batch * p.n_tokens * p.heads * p.head_dim * p.elem_bytes
     per_set = 4 * tensor_bytes
     sets = args.sets or max(2, int(np.ceil(2 * MALL_BYTES / per_set)))
@@ -364,7 +369,7 @@ def main():
         kernels[n] = {"avg_us": round(float(avg[j]) * 1e3, 2), "alg_bytes": int(kb[n]),
                       "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
-    traffic = measured_traffic(p.name) if (args.path == "3kernel" and args.w == "gaussian"
+    traffic = measured_traffic(p.name) if (args.path != "fused" and args.w == "gaussian"
                                            and not args.batch and not args.heads and not args.block) else {}
     for n in kernels:
         kernels[n]["traffic"] = traffic.get(n)
@@ -379,12 +384,16 @@ def main():
         q, k, v, W = host0
         ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
         t = time.perf_counter()
-        _, used = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps, threads=ncpu, return_threads=True)
+        if args.path == "causal":
+            oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps, threads=ncpu)
+            used = min(ncpu, p.batch * p.heads)   # the oracle runs one thread per (b, h) pair at most
+        else:
+            _, used = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps, threads=ncpu, return_threads=True)
         dt_cpu = time.perf_counter() - t
         cpu = {"value": round(p.batch * p.n_tokens / dt_cpu, 1), "unit": "tokens/s", "cores": used,
                "kind": "oracle", "seconds": round(dt_cpu, 3),
                "sample": f"the full workload ({p.batch * p.heads} (b,h) pairs, {p.n_tokens} tokens), "
-                         f"float64 blockwise oracle, one thread per pair"}
+                         f"float64 {'causal chunkwise' if args.path == 'causal' else 'blockwise'} oracle, one thread per pair"}
 
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
