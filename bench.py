@@ -26,8 +26,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MHLA fwd tokens/s + achieved HBM GB/s (% peak), N=65536 H=6 d=64 bf16"
-KERNEL_SOURCES = ["token_level_head_block_amd/csrc/" + f for f in (
-    "kernels_bf16.hip", "kernels_causal_bf16.hip", "bf16_shared.h", "common.h", "mhla_api.cpp", "launch.h")]
+# Sources of the forward kernels each path runs; a stored traffic summary is
+# used only while the hash over its path's sources is unchanged.
+_FWD = ("kernels_bf16.hip", "bf16_shared.h", "common.h", "mhla_api.cpp", "launch.h")
+KERNEL_SOURCES = {
+    "3kernel": _FWD,
+    "fused": _FWD,
+    "causal": _FWD + ("kernels_causal_bf16.hip",),
+}
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 MALL_BYTES = 256 << 20          # Infinity Cache
 
@@ -55,30 +61,30 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_sha():
+def kernel_source_sha(path: str = "3kernel"):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in KERNEL_SOURCES[path]:
+        with open(os.path.join(ROOT, "token_level_head_block_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, path: str = "3kernel"):
     """Per-dispatch HBM bytes of each kernel from the committed rocprofv3 counter
     summary (FETCH_SIZE, WRITE_SIZE scaled by a plain copy of known size), or {}
     if there is none for this workload or the kernel sources changed since."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
-    if not os.path.exists(path):
+    fname = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(fname):
         return {}
     vals = {}
-    for line in open(path):
+    for line in open(fname):
         line = line.strip()
         if not line or line.startswith("#") or ":" not in line:
             continue
         k, v = line.split(":", 1)
         vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != kernel_source_sha():
+    if vals.get("source_sha256") != kernel_source_sha(path):
         return {}
     fs, ws = float(vals["fetch_scale"]), float(vals["write_scale"])
     out = {}
@@ -369,7 +375,7 @@ def main():
         kernels[n] = {"avg_us": round(float(avg[j]) * 1e3, 2), "alg_bytes": int(kb[n]),
                       "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
-    traffic = measured_traffic(p.name) if (args.path != "fused" and args.w == "gaussian"
+    traffic = measured_traffic(p.name, args.path) if (args.path != "fused" and args.w == "gaussian"
                                            and not args.batch and not args.heads and not args.block) else {}
     for n in kernels:
         kernels[n]["traffic"] = traffic.get(n)
