@@ -165,3 +165,43 @@ def as_float64(x: np.ndarray, dtype: int) -> np.ndarray:
     if dtype == BF16:
         return bf16_to_f32(x).astype(np.float64)
     return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def make_layer_inputs(p: Problem, seed, qk_norm: bool = False, lepe: bool = True, bias: bool = True,
+                      w_kind: str = "gaussian"):
+    """Seeded inputs of the whole layer around the core for problem p (bf16):
+    x [B, N, C] (C = H * d) and a dict of parameters, scaled like freshly
+    initialised layers: projection weights N(0, 1/C) in bf16 laid out
+    [out features, in features]; norm weights 1 + 0.1 N(0, 1); biases
+    0.02 N(0, 1); LePE kernels N(0, 1/25) per channel.  Plus W as in
+    make_inputs.  Draw order: x, ln_w, ln_b, w_qkv, b_qkv, qn_w, kn_w, lepe_w,
+    lepe_b, w_out, b_out, then W's jitter (each drawn whether used or not)."""
+    if p.dtype != BF16:
+        raise ValueError("the layer is bf16")
+    rng = _rng(seed)
+    C = p.heads * p.head_dim
+    f32 = lambda shape, s=1.0: (rng.standard_normal(shape, dtype=np.float32) * np.float32(s))
+    x = bf16_bits(f32((p.batch, p.n_tokens, C), p.std))
+    params = {}
+    params["ln_w"] = 1.0 + f32((C,), 0.1)
+    params["ln_b"] = f32((C,), 0.1)
+    params["w_qkv"] = bf16_bits(f32((3 * C, C), 1.0 / np.sqrt(C)))
+    b_qkv = f32((3 * C,), 0.02)
+    qn_w, kn_w = 1.0 + f32((C,), 0.1), 1.0 + f32((C,), 0.1)
+    lepe_w, lepe_b = f32((C, 5, 5), 0.2), f32((C,), 0.02)
+    params["w_out"] = bf16_bits(f32((C, C), 1.0 / np.sqrt(C)))
+    b_out = f32((C,), 0.02)
+    params["b_qkv"] = b_qkv if bias else None
+    params["qn_w"] = qn_w if qk_norm else None
+    params["kn_w"] = kn_w if qk_norm else None
+    params["lepe_w"] = lepe_w if lepe else None
+    params["lepe_b"] = lepe_b if lepe and bias else None
+    params["b_out"] = b_out if bias else None
+    M = p.n_blocks
+    if w_kind == "gaussian":
+        W = distance_prior(p.blocks_per_axis, p.sigma) + p.jitter * rng.standard_normal((M, M))
+    elif w_kind == "local":
+        W = local_prior(p.blocks_per_axis)
+    else:
+        raise ValueError(f"unknown w_kind {w_kind!r}")
+    return x, params, np.ascontiguousarray(W, dtype=np.float32)
