@@ -213,6 +213,71 @@ mhla_status mhla_backward(const void* q, const void* k, const void* v, const flo
                           float* dW, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
                           hipStream_t stream);
 
+/* ---------------------------------------------------------------- layer
+ *
+ * The layer around the core, after the plug-and-play module of the
+ * 171host.com repost, section 七 (class MHLA, forward), on tokens in raster
+ * order:
+ *
+ *   xn = LayerNorm(x) (biased variance over the C channels, ln_eps)
+ *   [q | k | v] = xn w_qkv^T + b_qkv                   (w_qkv: [3C, C])
+ *   q, k = RMSNorm(q; qn_w), RMSNorm(k; kn_w)          (only if qn_w != NULL)
+ *   o = the core (mhla_forward, 3-kernel path) on q, k, v with feature map
+ *       elu(x) + 1 (MHLA_PHI_ELU1) or relu(x) + phi_eps (MHLA_PHI_RELU_EPS)
+ *   o += LePE(v): depthwise 5x5 convolution of v over the 2D token grid,
+ *       zero padding 2, plus lepe_b     (only if lepe_w != NULL; 2D grids)
+ *   y = o w_out^T + b_out                              (w_out: [C, C])
+ *
+ * C = heads * head_dim.  Dropout is the identity (inference).  Weight
+ * matrices are bfloat16 laid out [output features, input features]; norm
+ * weights, biases and the LePE kernels ([C][5][5], cross-correlation as in
+ * convolution layers) are fp32.  Biases may be NULL (zero).  x, y: [B, N, C]
+ * bfloat16.  Only bfloat16 grids (grid->dtype == MHLA_BF16). */
+
+typedef enum mhla_phi {
+    MHLA_PHI_ELU1 = 0,       /* elu(x) + 1, the core's feature map */
+    MHLA_PHI_RELU_EPS = 1    /* relu(x) + phi_eps, as in the module's code */
+} mhla_phi;
+
+typedef struct mhla_layer_params {
+    const float* ln_w;       /* [C] LayerNorm weight (required) */
+    const float* ln_b;       /* [C] LayerNorm bias (required) */
+    const void* w_qkv;       /* [3C][C] bfloat16 (required) */
+    const float* b_qkv;      /* [3C] or NULL */
+    const float* qn_w;       /* [C] q RMSNorm weight, or NULL for no q/k norm */
+    const float* kn_w;       /* [C] k RMSNorm weight (required with qn_w, else NULL) */
+    const float* lepe_w;     /* [C][5][5] or NULL for no LePE */
+    const float* lepe_b;     /* [C] or NULL */
+    const void* w_out;       /* [C][C] bfloat16 (required) */
+    const float* b_out;      /* [C] or NULL */
+    int32_t phi;             /* mhla_phi */
+    float phi_eps;           /* >= 0, used by MHLA_PHI_RELU_EPS */
+    float ln_eps;            /* > 0 */
+    float rms_eps;           /* > 0 when q/k norms are used */
+} mhla_layer_params;
+
+/* Bytes of device workspace mhla_layer_forward needs (0 for an invalid or
+ * empty problem).  Layout: q, k, v, o as [B, N, C] bfloat16, w_qkv scaled by
+ * the LayerNorm weight ([3C][C] bfloat16), its column sums and folded bias
+ * ([3C] fp32 each), then the core's workspace (mhla_workspace_bytes), each
+ * region at a 256-byte boundary. */
+size_t mhla_layer_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
+
+/* The layer forward, enqueued on `stream`.  x, y: device [B, N, C] bfloat16;
+ * W: fp32 [M, M] as for mhla_forward; params: host struct of device pointers
+ * (16-byte aligned).  ws: workspace of ws_bytes >= mhla_layer_workspace_bytes
+ * (16-byte aligned) or NULL with ws_bytes 0 to allocate it on the stream.
+ * stage_events: NULL or 5 caller-created events recorded before the first
+ * kernel, after the QKV projection (and q/k norms), after the core, after
+ * LePE and after the output projection.  y must not overlap x, W, a
+ * parameter or the workspace.  Errors: MHLA_ERR_UNSUPPORTED for fp32 grids,
+ * or LePE on a 3D grid; MHLA_ERR_INVALID_ARG for a missing required pointer,
+ * an unknown phi, a negative or non-finite eps, overlaps or a short
+ * workspace; otherwise as mhla_forward_ex. */
+mhla_status mhla_layer_forward(const void* x, const float* W, const mhla_grid* grid, const mhla_block* block,
+                               const mhla_layer_params* params, void* y, void* ws, size_t ws_bytes,
+                               const hipEvent_t* stage_events, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,16 +71,18 @@ def core(Q, K, V, W, grid, block, eps, kind, phi_eps=1e-6):
     B, N, H, d = Q.shape
     bid = token_blocks(grid, block)
     M = W.shape[0]
+    T = N // M
+    order = np.argsort(bid, kind="stable")     # the tokens of block 0, then block 1, ...
     Wd = np.asarray(W, dtype=np.float64)
     out = np.empty_like(Q)
     for b in range(B):
         for h in range(H):
             u = phi(Q[b, :, h], kind, phi_eps)
             a = phi(K[b, :, h], kind, phi_eps)
-            S = np.zeros((M, d, d))
-            z = np.zeros((M, d))
-            np.add.at(S, bid, a[:, :, None] * V[b, :, h][:, None, :])
-            np.add.at(z, bid, a)
+            ab = a[order].reshape(M, T, d)
+            vb = V[b, :, h][order].reshape(M, T, d)
+            S = np.einsum("jtc,jte->jce", ab, vb)   # S_j = sum over the block's tokens
+            z = ab.sum(axis=1)
             St = np.einsum("ij,jce->ice", Wd, S)
             zt = Wd @ z
             num = np.einsum("nc,nce->ne", u, St[bid])

@@ -97,3 +97,33 @@ class Run:
 
 def rel_err(a, b):
     return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+class LayerRun:
+    """Device inputs of one layer problem (bf16) and a call through mhla_layer_forward."""
+
+    def __init__(self, p: synth.Problem, x, params: dict, W):
+        self.p = p
+        self.x = to_dev(x, synth.BF16)
+        self.W = torch.from_numpy(W).cuda()
+        self.params = {}
+        for name, val in params.items():
+            if val is None:
+                continue
+            if name.startswith("w_"):
+                self.params[name] = to_dev(val, synth.BF16)
+            else:
+                self.params[name] = torch.from_numpy(np.ascontiguousarray(val, dtype=np.float32)).cuda()
+        self.g, self.b = grid_block(p)
+        self.ws_bytes = mh.mhla_layer_workspace_bytes(self.g, self.b)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def forward(self, phi=mh.MHLA_PHI_ELU1, ws=True, stream=None):
+        y = torch.empty_like(self.x)
+        say(f"  [gpu] mhla_layer_forward phi={phi} {self.p.name} B{self.p.batch} H{self.p.heads} "
+            f"d{self.p.head_dim} grid{self.p.grid} block{self.p.block} params={sorted(self.params)}")
+        st = mh.mhla_layer_forward(self.x, self.W, self.g, self.b, self.params, y,
+                                   self.ws if ws else None, self.ws_bytes if ws else 0, phi=phi, stream=stream)
+        assert st == mh.MHLA_OK, mh.mhla_status_string(st)
+        torch.cuda.synchronize()
+        return y

@@ -191,3 +191,52 @@ def test_causal_path_validation(L):
                                mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_ERR_UNSUPPORTED
     assert mh.mhla_launch_plan(mh.make_grid(1, 2, 32, mh.MHLA_F32, (1, 256)), mh.make_block((1, 64)),
                                mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_ERR_UNSUPPORTED
+
+
+def test_layer_workspace_and_validation(L):
+    g, b = cfg2()
+    C, R = 6 * 64, 65536
+    need = mh.mhla_layer_workspace_bytes(g, b)
+    assert need >= 4 * R * C * 2 + 3 * C * C * 2 + mh.mhla_workspace_bytes(g, b)
+    assert mh.mhla_layer_workspace_bytes(mh.make_grid(1, 6, 64, mh.MHLA_F32, (256, 256)), b) == 0
+    assert mh.mhla_layer_workspace_bytes(mh.make_grid(0, 6, 64, mh.MHLA_BF16, (256, 256)), b) == 0
+    base = dict(ln_w=20 * BIG, ln_b=21 * BIG, w_qkv=22 * BIG, b_qkv=23 * BIG, lepe_w=26 * BIG,
+                lepe_b=27 * BIG, w_out=28 * BIG, b_out=29 * BIG)
+
+    def layer(g_=g, b_=b, x=BIG, W=2 * BIG, y=3 * BIG, ws=4 * BIG, ws_bytes=None, phi=0, phi_eps=1e-6,
+              ln_eps=1e-5, rms_eps=1e-6, **kw):
+        P = mh.mhla_layer_params()
+        for k_, v_ in dict(base, **kw).items():
+            setattr(P, k_, v_)
+        P.phi, P.phi_eps, P.ln_eps, P.rms_eps = phi, phi_eps, ln_eps, rms_eps
+        wsb = need if ws_bytes is None else ws_bytes
+        return L.mhla_layer_forward(x, W, ctypes.byref(g_), ctypes.byref(b_), ctypes.byref(P), y, ws, wsb,
+                                    None, None)
+
+    assert L.mhla_layer_forward(BIG, 2 * BIG, ctypes.byref(g), ctypes.byref(b), None, 3 * BIG, 4 * BIG, need,
+                                None, None) == mh.MHLA_ERR_INVALID_ARG
+    assert layer(g_=mh.make_grid(1, 6, 64, mh.MHLA_F32, (256, 256))) == mh.MHLA_ERR_UNSUPPORTED
+    assert layer(phi=5) == mh.MHLA_ERR_INVALID_ARG
+    assert layer(phi_eps=-1.0) == mh.MHLA_ERR_INVALID_ARG
+    assert layer(ln_eps=0.0) == mh.MHLA_ERR_INVALID_ARG
+    assert layer(ln_eps=float("nan")) == mh.MHLA_ERR_INVALID_ARG
+    assert layer(qn_w=24 * BIG) == mh.MHLA_ERR_INVALID_ARG                    # q norm without k norm
+    assert layer(qn_w=24 * BIG, kn_w=25 * BIG, rms_eps=0.0) == mh.MHLA_ERR_INVALID_ARG
+    assert layer(lepe_w=None) == mh.MHLA_ERR_INVALID_ARG                      # LePE bias without kernel
+    for missing in ("ln_w", "ln_b", "w_qkv", "w_out"):
+        assert layer(**{missing: None}) == mh.MHLA_ERR_INVALID_ARG, missing
+    assert layer(x=None) == mh.MHLA_ERR_INVALID_ARG
+    assert layer(y=None) == mh.MHLA_ERR_INVALID_ARG
+    assert layer(w_qkv=22 * BIG + 8) == mh.MHLA_ERR_MISALIGNED
+    assert layer(y=3 * BIG + 2) == mh.MHLA_ERR_MISALIGNED
+    assert layer(y=BIG + 4096) == mh.MHLA_ERR_INVALID_ARG                     # y overlaps x
+    assert layer(y=28 * BIG - 64) == mh.MHLA_ERR_INVALID_ARG                  # y overlaps w_out
+    assert layer(ws_bytes=need - 16) == mh.MHLA_ERR_INVALID_ARG
+    assert layer(ws=3 * BIG) == mh.MHLA_ERR_INVALID_ARG                       # workspace overlaps y
+    assert layer(ws=None, ws_bytes=64) == mh.MHLA_ERR_INVALID_ARG
+    # LePE needs a 2D grid
+    g3, b3 = mh.make_grid(1, 12, 128, mh.MHLA_BF16, (16, 64, 64)), mh.make_block((4, 8, 8))
+    assert layer(g_=g3, b_=b3, ws_bytes=1 << 40) == mh.MHLA_ERR_UNSUPPORTED
+    # empty problem: nothing to do, no pointer needed
+    g0 = mh.make_grid(0, 6, 64, mh.MHLA_BF16, (256, 256))
+    assert layer(g_=g0, x=None, y=None, ws=None, ws_bytes=0) == mh.MHLA_OK

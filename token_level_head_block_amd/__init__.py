@@ -33,6 +33,9 @@ MHLA_PATH_3KERNEL = 0
 MHLA_PATH_FUSED = 1
 MHLA_PATH_CAUSAL = 2
 
+MHLA_PHI_ELU1 = 0
+MHLA_PHI_RELU_EPS = 1
+
 
 class mhla_grid(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
@@ -43,6 +46,14 @@ class mhla_grid(ctypes.Structure):
 
 class mhla_block(ctypes.Structure):
     _fields_ = [("extent", ctypes.c_int32 * 3)]
+
+
+class mhla_layer_params(ctypes.Structure):
+    _fields_ = [("ln_w", ctypes.c_void_p), ("ln_b", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p),
+                ("b_qkv", ctypes.c_void_p), ("qn_w", ctypes.c_void_p), ("kn_w", ctypes.c_void_p),
+                ("lepe_w", ctypes.c_void_p), ("lepe_b", ctypes.c_void_p), ("w_out", ctypes.c_void_p),
+                ("b_out", ctypes.c_void_p), ("phi", ctypes.c_int32), ("phi_eps", ctypes.c_float),
+                ("ln_eps", ctypes.c_float), ("rms_eps", ctypes.c_float)]
 
 
 class MhlaError(RuntimeError):
@@ -84,6 +95,11 @@ def lib() -> ctypes.CDLL:
         L.mhla_forward_ex.argtypes = [vp, vp, vp, vp, G, Bk, vp, vp, ctypes.c_size_t, ctypes.c_int32,
                                       vp, vp]
         L.mhla_forward_ex.restype = ctypes.c_int
+        L.mhla_layer_workspace_bytes.argtypes = [G, Bk]
+        L.mhla_layer_workspace_bytes.restype = ctypes.c_size_t
+        L.mhla_layer_forward.argtypes = [vp, vp, G, Bk, ctypes.POINTER(mhla_layer_params), vp, vp,
+                                         ctypes.c_size_t, vp, vp]
+        L.mhla_layer_forward.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -251,3 +267,53 @@ def forward(q, k, v, W, grid_extents, block_extents, eps: float = 1e-6, out=None
     if st != MHLA_OK:
         raise MhlaError(st, "mhla_forward_ex")
     return out
+
+
+# ---------------------------------------------------------------- layer
+
+LAYER_PARAM_NAMES = ("ln_w", "ln_b", "w_qkv", "b_qkv", "qn_w", "kn_w", "lepe_w", "lepe_b", "w_out", "b_out")
+
+
+def mhla_layer_workspace_bytes(grid: mhla_grid, block: mhla_block) -> int:
+    return int(lib().mhla_layer_workspace_bytes(ctypes.byref(grid), ctypes.byref(block)))
+
+
+def _check_layer_tensors(x, W, grid: mhla_grid, block: mhla_block, params: dict, y):
+    """Host-side shape/dtype checks of the layer's torch tensors (the C ABI
+    cannot see tensor sizes)."""
+    import torch
+    st, M, _ = mhla_check_problem(grid, block)
+    if st != MHLA_OK:
+        return
+    N = 1
+    for a in range(grid.ndim):
+        N *= grid.extent[a]
+    C = grid.heads * grid.head_dim
+    want = {"ln_w": ((C,), torch.float32), "ln_b": ((C,), torch.float32),
+            "w_qkv": ((3 * C, C), torch.bfloat16), "b_qkv": ((3 * C,), torch.float32),
+            "qn_w": ((C,), torch.float32), "kn_w": ((C,), torch.float32),
+            "lepe_w": ((C, 5, 5), torch.float32), "lepe_b": ((C,), torch.float32),
+            "w_out": ((C, C), torch.bfloat16), "b_out": ((C,), torch.float32)}
+    tensors = [("x", x, ((grid.batch, N, C), torch.bfloat16)), ("y", y, ((grid.batch, N, C), torch.bfloat16)),
+               ("W", W, ((M, M), torch.float32))]
+    tensors += [(k, params.get(k), want[k]) for k in LAYER_PARAM_NAMES]
+    for name, t, (shape, dt) in tensors:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or tuple(t.shape) != shape or t.dtype != dt \
+                or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous {dt} GPU tensor of shape {shape}")
+
+
+def mhla_layer_forward(x, W, grid: mhla_grid, block: mhla_block, params: dict, y, ws=None, ws_bytes: int = 0,
+                       phi: int = MHLA_PHI_ELU1, phi_eps: float = 1e-6, ln_eps: float = 1e-5,
+                       rms_eps: float = 1e-6, stage_events=None, stream=None) -> int:
+    """The layer forward through the C ABI.  params: dict with the tensors
+    named in LAYER_PARAM_NAMES (absent or None for optional ones)."""
+    _check_layer_tensors(x, W, grid, block, params, y)
+    P = mhla_layer_params()
+    for name in LAYER_PARAM_NAMES:
+        setattr(P, name, _ptr(params.get(name)))
+    P.phi, P.phi_eps, P.ln_eps, P.rms_eps = int(phi), float(phi_eps), float(ln_eps), float(rms_eps)
+    return lib().mhla_layer_forward(_ptr(x), _ptr(W), ctypes.byref(grid), ctypes.byref(block), ctypes.byref(P),
+                                    _ptr(y), _ptr(ws), int(ws_bytes), _events(stage_events, 5), _stream(stream))

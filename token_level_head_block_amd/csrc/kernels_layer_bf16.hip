@@ -1,0 +1,413 @@
+// kernels_layer_bf16.hip -- the layer around the MHLA core (171host.com
+// repost, section 七, class MHLA ``forward``): LayerNorm and QKV projection,
+// optional q/k RMSNorm, the feature map variant, LePE (depthwise 5x5
+// convolution of v over the 2D token grid) and the output projection, bf16
+// activations with fp32 accumulation, on gfx950.
+//
+// Projection out[n][c] = sum_k x[n][k] Wt[c][k]: v_mfma_f32_16x16x32_bf16 with
+// the weight rows as the A operand and the token rows as the B operand, so a
+// lane's four accumulator values are four consecutive output channels of one
+// token and leave as one 8-byte store.
+//
+// LayerNorm is folded into the QKV projection:
+//   LN(x) Wt^T + b = rstd_n (x W'^T - mu_n colsum') + b',
+//   W' = Wt * gamma (per input channel, bf16), b' = b + Wt beta, colsum'_c = sum_k W'_ck,
+// so the MFMA loop streams raw x and the epilogue applies the token's mean
+// and inverse deviation.  The products of bf16 values are exact in the fp32
+// accumulators, so the subtraction loses accuracy only when |mean| is
+// around 1e5 times the deviation.
+#include "launch.h"
+
+#include <mhla.h>
+
+namespace mhla {
+namespace {
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += shfl_xor(x, o);
+    return x;
+}
+
+// elu(y) + 1 = r for the feature map value r = relu(x) + eps > 0: the core
+// then evaluates the relu feature map through its elu + 1.
+__device__ __forceinline__ float relu_phi_preimage(float x, float eps) {
+    const float r = fmaxf(x, 0.f) + eps;
+    return r > 1.f ? r - 1.f : __logf(r);
+}
+
+// ---------------------------------------------------------------- weight folding
+// One workgroup of 64 threads per output feature c of the QKV projection:
+// W'[c][k] = bf16(Wt[c][k] gamma[k]), colsum'[c] = sum_k W'[c][k] (of the rounded
+// values), b'[c] = b[c] + sum_k Wt[c][k] beta[k].
+__global__ __launch_bounds__(64) void fold_ln_bf16(const uint16_t* __restrict__ Wt, const float* __restrict__ gamma,
+                                                   const float* __restrict__ beta, const float* __restrict__ bias,
+                                                   uint16_t* __restrict__ Wf, float* __restrict__ colsum,
+                                                   float* __restrict__ biasf, int K) {
+    const int c = blockIdx.x, lane = threadIdx.x;
+    const uint16_t* wr = Wt + (size_t)c * K;
+    uint16_t* fr = Wf + (size_t)c * K;
+    float s = 0.f, t = 0.f;
+    for (int k0 = 8 * lane; k0 < K; k0 += 512) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(wr + k0);
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + k0), g1 = *reinterpret_cast<const f32x4*>(gamma + k0 + 4);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(beta + k0), b1 = *reinterpret_cast<const f32x4*>(beta + k0 + 4);
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float be[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float w0 = bf_lo(w[j]), w1 = bf_hi(w[j]);
+            o[j] = pack_bf16(w0 * g[2 * j], w1 * g[2 * j + 1]);
+            s += bf_lo(o[j]) + bf_hi(o[j]);
+            t += w0 * be[2 * j] + w1 * be[2 * j + 1];
+        }
+        *reinterpret_cast<u32x4*>(fr + k0) = o;
+    }
+    s = wave_sum(s);
+    t = wave_sum(t);
+    if (lane == 0) {
+        colsum[c] = s;
+        biasf[c] = (bias ? bias[c] : 0.f) + t;
+    }
+}
+
+// ---------------------------------------------------------------- projection GEMM
+struct GemmArgs {
+    const uint16_t* X;     // [R][K] token rows
+    const uint16_t* Wt;    // [Nc][K] weight rows
+    const float* bias;     // [Nc] or nullptr
+    const float* colsum;   // [Nc] (LayerNorm mode)
+    float ln_eps;
+    uint16_t* dst[3];      // output column ranges [0, split), [split, 2 split), [2 split, 3 split)
+    int R, K, Nc, split;
+    int phi_cols;          // columns [0, phi_cols) leave as the relu feature map's preimage
+    float phi_eps;
+};
+
+// Workgroup: 4 waves, tile of 128 output features x 128 tokens, each wave
+// 64 x 64 (4 x 4 MFMA tiles).  K in chunks of 64 through two LDS buffers;
+// the next chunk's global loads are in flight while the current one is
+// multiplied.  Feature tiles of one token tile sit 8 workgroup ids apart, so
+// they run on the same XCD and share its L2 copy of the token rows.
+template <bool LN>
+__global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
+    constexpr int TC = 128, TN = 128, KC = 64, STR = KC + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t la[2][TC * STR];
+    __shared__ __attribute__((aligned(16))) uint16_t lb[2][TN * STR];
+    __shared__ float mean_s[TN], rstd_s[TN];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, gq = lane >> 4;
+    const int nct = (a.Nc + TC - 1) / TC;
+    const int ntt = (a.R + TN - 1) / TN;
+    // blockIdx -> (token tile, feature tile) with the feature tiles of a token
+    // tile on one XCD (ids congruent modulo 8)
+    int ct, nt;
+    {
+        const int id = blockIdx.x;
+        const int full = (ntt / 8) * 8 * nct;   // ids covered by whole groups of 8 token tiles
+        if (id < full) {
+            const int grp = id / (8 * nct), r = id % (8 * nct);
+            nt = grp * 8 + r % 8;
+            ct = r / 8;
+        } else {
+            const int r = id - full;
+            nt = (ntt / 8) * 8 + r / nct;
+            ct = r % nct;
+        }
+    }
+    const int c0 = ct * TC, n0 = nt * TN;
+    const int nk = (a.K + KC - 1) / KC;
+
+    if constexpr (LN) {
+        // token statistics, two passes over the row: thread = (token, half)
+        const int row = tid >> 1, half = tid & 1;
+        const int n = min(n0 + row, a.R - 1);
+        const uint16_t* xr = a.X + (size_t)n * a.K;
+        float s = 0.f;
+        for (int k0 = 8 * half; k0 < a.K; k0 += 16) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(xr + k0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s += bf_lo(x[j]) + bf_hi(x[j]);
+        }
+        s += shfl_xor(s, 1);
+        const float mu = s / (float)a.K;
+        float s2 = 0.f;
+        for (int k0 = 8 * half; k0 < a.K; k0 += 16) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(xr + k0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float d0 = bf_lo(x[j]) - mu, d1 = bf_hi(x[j]) - mu;
+                s2 += d0 * d0 + d1 * d1;
+            }
+        }
+        s2 += shfl_xor(s2, 1);
+        if (half == 0) {
+            mean_s[row] = mu;
+            rstd_s[row] = 1.f / sqrtf(s2 / (float)a.K + a.ln_eps);
+        }
+    }
+
+    // ---- staging: unit u = (row, 8 k) of a 128 x 64 chunk, 4 per thread and operand
+    u32x4 ra[4], rb[4];
+    auto gload = [&](int kc) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int u = tid + 256 * s;
+            const int row = u >> 3, k = kc * KC + (u & 7) * 8;
+            const bool kin = k < a.K;
+            const int kk = kin ? k : 0;
+            const int c = min(c0 + row, a.Nc - 1), n = min(n0 + row, a.R - 1);
+            const u32x4 w = *reinterpret_cast<const u32x4*>(a.Wt + (size_t)c * a.K + kk);
+            const u32x4 x = *reinterpret_cast<const u32x4*>(a.X + (size_t)n * a.K + kk);
+            const uint32_t m = kin ? 0xffffffffu : 0u;
+            ra[s] = u32x4{w[0] & m, w[1] & m, w[2] & m, w[3] & m};
+            rb[s] = u32x4{x[0] & m, x[1] & m, x[2] & m, x[3] & m};
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int u = tid + 256 * s;
+            const int off = (u >> 3) * STR + (u & 7) * 8;
+            *reinterpret_cast<u32x4*>(&la[buf][off]) = ra[s];
+            *reinterpret_cast<u32x4*>(&lb[buf][off]) = rb[s];
+        }
+    };
+
+    const int wc = wave & 1, wn = wave >> 1;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kc = 0; kc < nk; ++kc) {
+        const int buf = kc & 1;
+        if (kc + 1 < nk) gload(kc + 1);
+#pragma unroll
+        for (int ks = 0; ks < KC / 32; ++ks) {
+            u32x4 fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                fa[i] = *reinterpret_cast<const u32x4*>(&la[buf][(64 * wc + 16 * i + li) * STR + ks * 32 + gq * 8]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                fb[j] = *reinterpret_cast<const u32x4*>(&lb[buf][(64 * wn + 16 * j + li) * STR + ks * 32 + gq * 8]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+        }
+        if (kc + 1 < nk) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane (li, gq) holds features c .. c+3 of token n
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int nl = 64 * wn + 16 * j + li;
+        const int n = n0 + nl;
+        float mu = 0.f, rs = 1.f;
+        if constexpr (LN) {
+            mu = mean_s[nl];
+            rs = rstd_s[nl];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = c0 + 64 * wc + 16 * i + 4 * gq;
+            if (n >= a.R || c >= a.Nc) continue;
+            float o[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float x = acc[i][j][v];
+                if constexpr (LN) x = rs * (x - mu * a.colsum[c + v]);
+                if (a.bias) x += a.bias[c + v];
+                if (c < a.phi_cols) x = relu_phi_preimage(x, a.phi_eps);
+                o[v] = x;
+            }
+            const int which = c / a.split, cc = c - which * a.split;
+            uint16_t* d = a.dst[0];
+            if (which == 1) d = a.dst[1];
+            if (which == 2) d = a.dst[2];
+            *reinterpret_cast<u32x2*>(d + (size_t)n * a.split + cc) = u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+        }
+    }
+}
+
+// ---------------------------------------------------------------- q/k RMSNorm
+// One wave per (token, tensor) row of C channels: x / sqrt(mean(x^2) + eps) * w,
+// then the relu feature map's preimage when asked for.
+__global__ __launch_bounds__(256) void rms_qk_bf16(uint16_t* __restrict__ q, uint16_t* __restrict__ k,
+                                                   const float* __restrict__ wq, const float* __restrict__ wk,
+                                                   int R, int C, float eps, int relu_phi, float phi_eps) {
+    const int lane = threadIdx.x & 63;
+    const int rowid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (rowid >= 2 * R) return;
+    const int which = rowid & 1, n = rowid >> 1;
+    uint16_t* xr = (which ? k : q) + (size_t)n * C;
+    const float* w = which ? wk : wq;
+    float s = 0.f;
+    for (int k0 = 8 * lane; k0 < C; k0 += 512) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(xr + k0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s += bf_lo(x[j]) * bf_lo(x[j]) + bf_hi(x[j]) * bf_hi(x[j]);
+    }
+    s = wave_sum(s);
+    const float r = 1.f / sqrtf(s / (float)C + eps);
+    for (int k0 = 8 * lane; k0 < C; k0 += 512) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(xr + k0);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + k0), w1 = *reinterpret_cast<const f32x4*>(w + k0 + 4);
+        const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float y0 = bf_lo(x[j]) * r * ww[2 * j], y1 = bf_hi(x[j]) * r * ww[2 * j + 1];
+            if (relu_phi) {
+                y0 = relu_phi_preimage(y0, phi_eps);
+                y1 = relu_phi_preimage(y1, phi_eps);
+            }
+            o[j] = pack_bf16(y0, y1);
+        }
+        *reinterpret_cast<u32x4*>(xr + k0) = o;
+    }
+}
+
+// ---------------------------------------------------------------- LePE
+// o[n][c] += b[c] + sum_{dy,dx} w[c][dy][dx] v[y+dy-2][x+dx-2][c] (zero outside
+// the grid), per batch item on the Y x X grid.  Workgroup = (b, 8 rows x 32
+// columns of tokens, 32 channels): the 12 x 36 halo of v goes to LDS; thread
+// (channel pair, pair of columns) keeps its two channels' 25 weights in
+// registers and slides down the 12 input rows, feeding the 8 x 2 outputs.
+constexpr int LP_TY = 8, LP_TX = 32, LP_TCH = 32;
+
+__global__ __launch_bounds__(256) void lepe_add_bf16(const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                                                     const float* __restrict__ w, const float* __restrict__ bias,
+                                                     int Y, int X, int C) {
+    constexpr int HY = LP_TY + 4, HX = LP_TX + 4;
+    __shared__ __attribute__((aligned(16))) uint32_t vt[HY * HX * (LP_TCH / 2)];   // bf16 channel pairs
+    const int tid = threadIdx.x;
+    const int ncg = C / LP_TCH, ntx = (X + LP_TX - 1) / LP_TX, nty = (Y + LP_TY - 1) / LP_TY;
+    int id = blockIdx.x;
+    const int cg = id % ncg; id /= ncg;
+    const int tx = id % ntx; id /= ntx;
+    const int ty = id % nty;
+    const int b = id / nty;
+    const int y0 = ty * LP_TY, x0 = tx * LP_TX, ch0 = cg * LP_TCH;
+    const size_t img = (size_t)b * Y * X;
+    // halo of v: unit = (position, 8 channels)
+    for (int u = tid; u < HY * HX * (LP_TCH / 8); u += 256) {
+        const int part = u % (LP_TCH / 8), pos = u / (LP_TCH / 8);
+        const int hy = pos / HX, hx = pos % HX;
+        const int yy = y0 + hy - 2, xx = x0 + hx - 2;
+        u32x4 val = u32x4{0u, 0u, 0u, 0u};
+        if (yy >= 0 && yy < Y && xx >= 0 && xx < X)
+            val = *reinterpret_cast<const u32x4*>(V + (img + (size_t)yy * X + xx) * C + ch0 + part * 8);
+        *reinterpret_cast<u32x4*>(&vt[pos * (LP_TCH / 2) + part * 4]) = val;
+    }
+    const int p = tid & 15, xg = tid >> 4;   // channel pair, pair of output columns
+    const int c = ch0 + 2 * p;
+    float w0[25], w1[25];
+#pragma unroll
+    for (int t = 0; t < 25; ++t) {
+        w0[t] = w[(size_t)c * 25 + t];
+        w1[t] = w[(size_t)(c + 1) * 25 + t];
+    }
+    const float b0 = bias ? bias[c] : 0.f, b1 = bias ? bias[c + 1] : 0.f;
+    __syncthreads();
+    float acc[LP_TY][2][2];
+#pragma unroll
+    for (int oy = 0; oy < LP_TY; ++oy)
+#pragma unroll
+        for (int ox = 0; ox < 2; ++ox) acc[oy][ox][0] = acc[oy][ox][1] = 0.f;
+#pragma unroll
+    for (int iy = 0; iy < HY; ++iy) {
+        float in0[6], in1[6];
+#pragma unroll
+        for (int s = 0; s < 6; ++s) {
+            const uint32_t pr = vt[(iy * HX + 2 * xg + s) * (LP_TCH / 2) + p];
+            in0[s] = bf_lo(pr);
+            in1[s] = bf_hi(pr);
+        }
+#pragma unroll
+        for (int dy = 0; dy < 5; ++dy) {
+            const int oy = iy - dy;
+            if (oy < 0 || oy >= LP_TY) continue;
+#pragma unroll
+            for (int ox = 0; ox < 2; ++ox)
+#pragma unroll
+                for (int dx = 0; dx < 5; ++dx) {
+                    acc[oy][ox][0] += w0[dy * 5 + dx] * in0[ox + dx];
+                    acc[oy][ox][1] += w1[dy * 5 + dx] * in1[ox + dx];
+                }
+        }
+    }
+#pragma unroll
+    for (int oy = 0; oy < LP_TY; ++oy)
+#pragma unroll
+        for (int ox = 0; ox < 2; ++ox) {
+            const int yy = y0 + oy, xx = x0 + 2 * xg + ox;
+            if (yy >= Y || xx >= X) continue;
+            uint32_t* op = reinterpret_cast<uint32_t*>(O + (img + (size_t)yy * X + xx) * C + c);
+            const uint32_t prev = *op;
+            *op = pack_bf16(bf_lo(prev) + acc[oy][ox][0] + b0, bf_hi(prev) + acc[oy][ox][1] + b1);
+        }
+}
+
+}  // namespace
+
+hipError_t run_layer_bf16(const LayerLaunch& L) {
+    const int R = L.R, C = L.C;
+    auto rec = [&](int i) {
+        if (L.events) (void)hipEventRecord(L.events[i], L.stream);
+    };
+    rec(0);
+    // 1. LayerNorm folded into the QKV weights, then the projection
+    fold_ln_bf16<<<3 * C, 64, 0, L.stream>>>(L.w_qkv, L.ln_w, L.ln_b, L.b_qkv, L.wf, L.colsum, L.biasf, C);
+    GemmArgs a;
+    a.X = L.x;
+    a.Wt = L.wf;
+    a.bias = L.biasf;
+    a.colsum = L.colsum;
+    a.ln_eps = L.ln_eps;
+    a.dst[0] = L.q; a.dst[1] = L.k; a.dst[2] = L.v;
+    a.R = R; a.K = C; a.Nc = 3 * C; a.split = C;
+    a.phi_cols = (L.relu_phi && !L.qn_w) ? 2 * C : 0;
+    a.phi_eps = L.phi_eps;
+    const int ntt = (R + 127) / 128, nct = (3 * C + 127) / 128;
+    layer_gemm_bf16<true><<<ntt * nct, 256, 0, L.stream>>>(a);
+    if (L.qn_w)
+        rms_qk_bf16<<<(2 * R + 3) / 4, 256, 0, L.stream>>>(L.q, L.k, L.qn_w, L.kn_w, R, C, L.rms_eps, L.relu_phi,
+                                                           L.phi_eps);
+    rec(1);
+    // 2. the core on q, k, v -> o
+    hipError_t e = run_bf16(L.core);
+    if (e != hipSuccess) return e;
+    rec(2);
+    // 3. LePE added into o
+    if (L.lepe_w) {
+        const int nblk = L.B * ((L.Y + LP_TY - 1) / LP_TY) * ((L.X + LP_TX - 1) / LP_TX) * (C / LP_TCH);
+        lepe_add_bf16<<<nblk, 256, 0, L.stream>>>(L.v, L.o, L.lepe_w, L.lepe_b, L.Y, L.X, C);
+    }
+    rec(3);
+    // 4. output projection
+    GemmArgs b;
+    b.X = L.o;
+    b.Wt = L.w_out;
+    b.bias = L.b_out;
+    b.colsum = nullptr;
+    b.ln_eps = 0.f;
+    b.dst[0] = L.y; b.dst[1] = L.y; b.dst[2] = L.y;
+    b.R = R; b.K = C; b.Nc = C; b.split = C;
+    b.phi_cols = 0;
+    b.phi_eps = 0.f;
+    layer_gemm_bf16<false><<<ntt * ((C + 127) / 128), 256, 0, L.stream>>>(b);
+    rec(4);
+    return hipGetLastError();
+}
+
+}  // namespace mhla

@@ -67,6 +67,38 @@ hipError_t run_bwd_bf16(const BwdLaunch& B);
 // mixing kernels have run with W restricted to earlier blocks.
 hipError_t launch_causal_apply_bf16(const Launch& L);
 
+// The layer around the core: LayerNorm + QKV projection, optional q/k
+// RMSNorm, the feature-map variant, the core (core.q/k/v/out point at q, k,
+// v, o below), LePE added into o, output projection into y.
+struct LayerLaunch {
+    const uint16_t* x;      // [R][C] layer input
+    uint16_t* y;            // [R][C] layer output
+    uint16_t* q;            // workspace [R][C] each
+    uint16_t* k;
+    uint16_t* v;
+    uint16_t* o;
+    const uint16_t* w_qkv;  // [3C][C]
+    uint16_t* wf;           // workspace: w_qkv scaled by the LayerNorm weight [3C][C]
+    float* colsum;          // workspace [3C]
+    float* biasf;           // workspace [3C]
+    const float* ln_w;
+    const float* ln_b;
+    const float* b_qkv;     // or nullptr
+    const float* qn_w;      // or nullptr (no q/k RMSNorm)
+    const float* kn_w;
+    const float* lepe_w;    // [C][5][5] or nullptr (no LePE)
+    const float* lepe_b;    // or nullptr
+    const uint16_t* w_out;  // [C][C]
+    const float* b_out;     // or nullptr
+    float ln_eps, rms_eps, phi_eps;
+    int relu_phi;
+    int R, C, B, Y, X;      // tokens (B N), channels, batch, 2D grid extents (LePE)
+    Launch core;
+    const hipEvent_t* events;   // 5 events or nullptr
+    hipStream_t stream;
+};
+hipError_t run_layer_bf16(const LayerLaunch& L);
+
 // p[0 .. n) = 0 by a kernel (safe inside a captured graph).
 hipError_t zero_f32(float* p, int n, hipStream_t stream);
 

@@ -337,6 +337,125 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
     return err == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------- layer
+
+struct LayerLayout {
+    size_t q, k, v, o, wf, colsum, biasf, core, total;
+};
+
+LayerLayout layer_layout(const Shape& s) {
+    const size_t C = (size_t)(s.H * s.D), R = (size_t)(s.B * s.N);
+    const size_t act = align_up(R * C * 2);
+    LayerLayout L;
+    L.q = 0;
+    L.k = L.q + act;
+    L.v = L.k + act;
+    L.o = L.v + act;
+    L.wf = L.o + act;
+    L.colsum = L.wf + align_up(3 * C * C * 2);
+    L.biasf = L.colsum + align_up(3 * C * 4);
+    L.core = L.biasf + align_up(3 * C * 4);
+    L.total = L.core + layout(s).total;
+    return L;
+}
+
+mhla_status layer_impl(const void* x, const float* W, const mhla_grid* grid, const mhla_block* block,
+                       const mhla_layer_params* P, void* y, void* ws, size_t ws_bytes, const hipEvent_t* events,
+                       hipStream_t stream) {
+    Shape s;
+    mhla_status st = check(grid, block, &s);
+    if (st != MHLA_OK) return st;
+    if (s.dtype != MHLA_BF16) return MHLA_ERR_UNSUPPORTED;
+    if (!P) return MHLA_ERR_INVALID_ARG;
+    if (P->phi != MHLA_PHI_ELU1 && P->phi != MHLA_PHI_RELU_EPS) return MHLA_ERR_INVALID_ARG;
+    if (!std::isfinite(P->phi_eps) || P->phi_eps < 0.f) return MHLA_ERR_INVALID_ARG;
+    if (!std::isfinite(P->ln_eps) || P->ln_eps <= 0.f) return MHLA_ERR_INVALID_ARG;
+    if ((P->qn_w == nullptr) != (P->kn_w == nullptr)) return MHLA_ERR_INVALID_ARG;
+    if (P->qn_w && (!std::isfinite(P->rms_eps) || P->rms_eps <= 0.f)) return MHLA_ERR_INVALID_ARG;
+    if (P->lepe_w && grid->ndim != 2) return MHLA_ERR_UNSUPPORTED;
+    if (!P->lepe_w && P->lepe_b) return MHLA_ERR_INVALID_ARG;
+    const size_t C = (size_t)(s.H * s.D), R = (size_t)(s.B * s.N);
+    // the layer's [3C, C] weight and its fold must also stay below 2^31 elements
+    if ((double)(3 * C) * (double)C >= 2147483648.0) return MHLA_ERR_UNSUPPORTED;
+    if (s.B == 0 || s.H == 0) return MHLA_OK;
+    if (!x || !W || !y || !P->ln_w || !P->ln_b || !P->w_qkv || !P->w_out) return MHLA_ERR_INVALID_ARG;
+    const void* ptrs[] = {x, W, y, P->ln_w, P->ln_b, P->w_qkv, P->b_qkv, P->qn_w, P->kn_w,
+                          P->lepe_w, P->lepe_b, P->w_out, P->b_out};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MHLA_ERR_MISALIGNED;
+    const size_t tb = R * C * 2;
+    struct Span { const void* p; size_t n; } spans[] = {
+        {x, tb}, {W, (size_t)(s.M * s.M) * 4}, {P->ln_w, C * 4}, {P->ln_b, C * 4}, {P->w_qkv, 3 * C * C * 2},
+        {P->b_qkv, 3 * C * 4}, {P->qn_w, C * 4}, {P->kn_w, C * 4}, {P->lepe_w, C * 25 * 4}, {P->lepe_b, C * 4},
+        {P->w_out, C * C * 2}, {P->b_out, C * 4}};
+    for (const Span& sp : spans)
+        if (sp.p && overlaps(y, tb, sp.p, sp.n)) return MHLA_ERR_INVALID_ARG;
+    const LayerLayout lay = layer_layout(s);
+    bool owned = false;
+    if (ws) {
+        if (ws_bytes < lay.total) return MHLA_ERR_INVALID_ARG;
+        if (!aligned16(ws)) return MHLA_ERR_MISALIGNED;
+        if (overlaps(ws, lay.total, y, tb)) return MHLA_ERR_INVALID_ARG;
+        for (const Span& sp : spans)
+            if (sp.p && overlaps(ws, lay.total, sp.p, sp.n)) return MHLA_ERR_INVALID_ARG;
+    } else {
+        if (ws_bytes != 0) return MHLA_ERR_INVALID_ARG;
+        if (hipMallocAsync(&ws, lay.total, stream) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return MHLA_ERR_ALLOC;
+        }
+        owned = true;
+    }
+    char* base = static_cast<char*>(ws);
+    mhla::LayerLaunch L;
+    L.x = static_cast<const uint16_t*>(x);
+    L.y = static_cast<uint16_t*>(y);
+    L.q = reinterpret_cast<uint16_t*>(base + lay.q);
+    L.k = reinterpret_cast<uint16_t*>(base + lay.k);
+    L.v = reinterpret_cast<uint16_t*>(base + lay.v);
+    L.o = reinterpret_cast<uint16_t*>(base + lay.o);
+    L.w_qkv = static_cast<const uint16_t*>(P->w_qkv);
+    L.wf = reinterpret_cast<uint16_t*>(base + lay.wf);
+    L.colsum = reinterpret_cast<float*>(base + lay.colsum);
+    L.biasf = reinterpret_cast<float*>(base + lay.biasf);
+    L.ln_w = P->ln_w; L.ln_b = P->ln_b; L.b_qkv = P->b_qkv;
+    L.qn_w = P->qn_w; L.kn_w = P->kn_w;
+    L.lepe_w = P->lepe_w; L.lepe_b = P->lepe_b;
+    L.w_out = static_cast<const uint16_t*>(P->w_out); L.b_out = P->b_out;
+    L.ln_eps = P->ln_eps; L.rms_eps = P->rms_eps; L.phi_eps = P->phi_eps;
+    L.relu_phi = P->phi == MHLA_PHI_RELU_EPS;
+    L.R = (int)R; L.C = (int)C; L.B = (int)s.B;
+    L.Y = (int)s.g[1]; L.X = (int)s.g[2];   // 2D grids: the two fastest axes
+    mhla::Launch& F = L.core;
+    const Layout cl = layout(s);
+    char* cb = base + lay.core;
+    F.q = L.q; F.k = L.k; F.v = L.v; F.W = W; F.out = L.o;
+    F.sz = cb + cl.sz;
+    F.st = cb + cl.st;
+    F.zt = reinterpret_cast<float*>(cb + cl.zt);
+    F.wb = cb + cl.wb;
+    F.wbt = nullptr;
+    F.g = make_geo(s, grid->eps);
+    F.tune = choose_tuning(s);
+    {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            F.tune.num_cus = cus;
+        else
+            (void)hipGetLastError();
+    }
+    F.path = MHLA_PATH_3KERNEL;
+    F.summaries_only = 0;
+    F.events = nullptr;
+    F.stream = stream;
+    L.events = events;
+    L.stream = stream;
+    const hipError_t err = mhla::run_layer_bf16(L);
+    if (owned) (void)hipFreeAsync(ws, stream);
+    return err == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,6 +471,18 @@ mhla_status mhla_backward(const void* q, const void* k, const void* v, const flo
                           float* dW, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
                           hipStream_t stream) {
     return backward_impl(q, k, v, W, dout, grid, block, dq, dk, dv, dW, ws, ws_bytes, stage_events, stream);
+}
+
+size_t mhla_layer_workspace_bytes(const mhla_grid* grid, const mhla_block* block) {
+    Shape s;
+    if (check(grid, block, &s) != MHLA_OK || s.dtype != MHLA_BF16 || s.B == 0 || s.H == 0) return 0;
+    return layer_layout(s).total;
+}
+
+mhla_status mhla_layer_forward(const void* x, const float* W, const mhla_grid* grid, const mhla_block* block,
+                               const mhla_layer_params* params, void* y, void* ws, size_t ws_bytes,
+                               const hipEvent_t* stage_events, hipStream_t stream) {
+    return layer_impl(x, W, grid, block, params, y, ws, ws_bytes, stage_events, stream);
 }
 
 const char* mhla_status_string(mhla_status status) {
