@@ -52,6 +52,11 @@ def parse():
     ap.add_argument("--out", default="", help="also write the JSON line to this file")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dq, dk, dv, dW) instead of the forward (bf16, d <= 64)")
+    ap.add_argument("--layer", action="store_true",
+                    help="time the whole layer around the core (mhla_layer_forward) instead")
+    ap.add_argument("--phi", choices=["elu", "relu"], default="relu",
+                    help="--layer: feature map (relu + eps as in the module's code, or elu + 1)")
+    ap.add_argument("--qk-norm", action="store_true", help="--layer: RMSNorm on q and k")
     ap.add_argument("--block", default="", help="override the block extents, e.g. 32x32 (token-level head count sweeps)")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch size")
     ap.add_argument("--heads", type=int, default=0, help="override the workload's head count")
@@ -261,6 +266,136 @@ def bench_backward(args, p, torch, mh, synth):
             f.write(s + "\n")
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+
+
+def layer_costs(p, qk_norm: bool, lepe: bool):
+    """Algorithmic HBM bytes and flops of each stage of the layer (compulsory
+    reads + writes of that stage; bf16 activations)."""
+    R, C = p.batch * p.n_tokens, p.heads * p.head_dim
+    act = R * C * 2
+    core = sum(kernel_bytes(p, p.elem_bytes)[k] for k in ("block_kv_summary", "mix_summaries", "query_apply"))
+    return {
+        "qkv projection": (act + 3 * C * C * 2 + 3 * act + (4 * act if qk_norm else 0), 2 * R * C * 3 * C),
+        "core": (core, 0),
+        "lepe": ((3 * act + C * 26 * 4) if lepe else 0, 2 * 25 * R * C if lepe else 0),
+        "output projection": (2 * act + C * C * 2, 2 * R * C * C),
+    }
+
+
+def bench_layer(args, p, torch, mh, synth):
+    """One step = one mhla_layer_forward call (LayerNorm + QKV projection, the
+    core, LePE, output projection) on seeded inputs resident in HBM."""
+    if p.dtype != synth.BF16:
+        print("the layer is bf16", file=sys.stderr)
+        sys.exit(1)
+    lepe = len(p.grid) == 2
+    phi = mh.MHLA_PHI_RELU_EPS if args.phi == "relu" else mh.MHLA_PHI_ELU1
+    R, C = p.batch * p.n_tokens, p.heads * p.head_dim
+    sets = args.sets or max(2, int(np.ceil(2 * MALL_BYTES / (6 * R * C * 2))))
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    data, host0 = [], None
+    for s in range(sets):
+        x, P, W = synth.make_layer_inputs(p, seed=(args.config, s) if s else args.config, lepe=lepe,
+                                          qk_norm=args.qk_norm)
+        params = {}
+        for name, val in P.items():
+            if val is not None:
+                params[name] = dev(val) if name.startswith("w_") else \
+                    torch.from_numpy(np.ascontiguousarray(val, dtype=np.float32)).cuda()
+        data.append((dev(x), torch.from_numpy(W).cuda(), params, torch.empty(R, C, dtype=torch.bfloat16,
+                                                                            device="cuda").view(p.batch, p.n_tokens, C)))
+        if s == 0:
+            host0 = (x, P, W)
+    gr = mh.make_grid(p.batch, p.heads, p.head_dim, mh.MHLA_BF16, p.grid, p.eps)
+    bl = mh.make_block(p.block)
+    ws_bytes = mh.mhla_layer_workspace_bytes(gr, bl)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        x, W, params, y = data[i % sets]
+        st = mh.mhla_layer_forward(x, W, gr, bl, params, y, ws, ws_bytes, phi=phi, stage_events=events,
+                                   stream=stream)
+        if st != mh.MHLA_OK:
+            raise mh.MhlaError(st, "mhla_layer_forward")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    hev = HipEvents()
+    evs = [[hev.create() for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    stage_ms = np.array([[hev.elapsed_ms(r[j], r[j + 1]) for j in range(4)] for r in evs]).mean(axis=0)
+    hev.destroy_all()
+    stages = {}
+    for j, (name, (nbytes, flops)) in enumerate(layer_costs(p, args.qk_norm, lepe).items()):
+        t = stage_ms[j] * 1e-3
+        gbps = nbytes / t / 1e9
+        tflops = flops / t / 1e12
+        stages[name] = {"avg_us": round(float(stage_ms[j]) * 1e3, 2), "alg_bytes": int(nbytes), "flops": int(flops),
+                        "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                        "tflops": round(tflops, 1), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    dom = max(stages, key=lambda n: stages[n]["avg_us"])
+    d = stages[dom]
+    if d["mfma_frac"] > d["hbm_frac"]:
+        roof = {"bound": "mfma", "achieved": d["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": d["mfma_frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": d["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d["hbm_frac"]}
+    roof.update({"kernel": dom, "traffic": None, "avg_us": d["avg_us"], "alg_bytes": d["alg_bytes"]})
+    # compulsory bytes of the whole layer: x, y, the weights and W
+    U = 2 * R * C * 2 + 4 * C * C * 2 + p.n_blocks ** 2 * 4
+    cpu = None
+    if not args.no_cpu:
+        from oracle import layer as oracle_layer
+        x, P, W = host0
+        t = time.perf_counter()
+        oracle_layer.layer_forward(x, W, p.grid, p.block, p.heads, P, eps=p.eps,
+                                   kind=oracle_layer.PHI_RELU_EPS if args.phi == "relu" else oracle_layer.PHI_ELU1)
+        dt_cpu = time.perf_counter() - t
+        blas = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+        cpu = {"value": round(R / dt_cpu, 1), "unit": "tokens/s", "cores": blas, "kind": "oracle",
+               "seconds": round(dt_cpu, 3),
+               "sample": "the full workload, float64 numpy layer oracle (matrix products on the BLAS threads, "
+                         "the rest on one thread)"}
+    line = {
+        "metric": "MHLA layer fwd tokens/s (LayerNorm, QKV projection, core, LePE, output projection)",
+        "value": round(R / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{p.name} layer: B={p.batch} H={p.heads} d={p.head_dim} C={C} grid={list(p.grid)} "
+                               f"blocks={list(p.block)} N={p.n_tokens} M={p.n_blocks}",
+                   "phi": args.phi, "qk_norm": bool(args.qk_norm), "lepe": lepe, "input_sets": sets,
+                   "parallelism": "none (1 GPU)"},
+        "path_hbm_gbps": round(U / (ms_step * 1e-3) / 1e9, 1),
+        "path_hbm_frac": round(U / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "path_alg_bytes": U,
+        "kernels": stages,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(s + "\n")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -297,6 +432,9 @@ def main():
         p = p.with_(name=p.name + "-causal-rows", block=(1,) * (len(p.grid) - 1) + (p.grid[-1],))
     if args.backward:
         bench_backward(args, p, torch, mh, synth)
+        return
+    if args.layer:
+        bench_layer(args, p, torch, mh, synth)
         return
     path = {"3kernel": mh.MHLA_PATH_3KERNEL, "fused": mh.MHLA_PATH_FUSED, "causal": mh.MHLA_PATH_CAUSAL}[args.path]
     tensor_bytes = p.batch * p.n_tokens * p.heads * p.head_dim * p.elem_bytes

@@ -259,8 +259,9 @@ typedef struct mhla_layer_params {
 /* Bytes of device workspace mhla_layer_forward needs (0 for an invalid or
  * empty problem).  Layout: q, k, v, o as [B, N, C] bfloat16, w_qkv scaled by
  * the LayerNorm weight ([3C][C] bfloat16), its column sums and folded bias
- * ([3C] fp32 each), then the core's workspace (mhla_workspace_bytes), each
- * region at a 256-byte boundary. */
+ * ([3C] fp32 each), the token means and inverse deviations of x ([B*N] fp32
+ * each), then the core's workspace (mhla_workspace_bytes), each region at a
+ * 256-byte boundary. */
 size_t mhla_layer_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
 
 /* The layer forward, enqueued on `stream`.  x, y: device [B, N, C] bfloat16;

@@ -72,13 +72,48 @@ __global__ __launch_bounds__(64) void fold_ln_bf16(const uint16_t* __restrict__ 
     }
 }
 
+// ---------------------------------------------------------------- token statistics
+// mean and 1 / sqrt(var + eps) of each token row of x (biased variance over the
+// K channels), once per token: eight lanes per row, one pass of shifted sums
+// (x - x0, x0 the row's first element, which keeps them accurate for a large
+// mean).  Workgroup = 32 rows.
+__global__ __launch_bounds__(256) void ln_stats_bf16(const uint16_t* __restrict__ X, float* __restrict__ mean,
+                                                     float* __restrict__ rstd, int R, int K, float eps) {
+    const int tid = threadIdx.x, part = tid & 7;
+    const int n = blockIdx.x * 32 + (tid >> 3);
+    const int nc = n < R ? n : R - 1;
+    const uint16_t* xr = X + (size_t)nc * K;
+    const float x0 = bf_lo(*reinterpret_cast<const uint32_t*>(xr));
+    float s1 = 0.f, s2 = 0.f;
+    for (int k0 = 8 * part; k0 < K; k0 += 64) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(xr + k0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float d0 = bf_lo(x[j]) - x0, d1 = bf_hi(x[j]) - x0;
+            s1 += d0 + d1;
+            s2 += d0 * d0 + d1 * d1;
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+        s1 += shfl_xor(s1, o);
+        s2 += shfl_xor(s2, o);
+    }
+    if (part == 0 && n < R) {
+        const float m1 = s1 / (float)K;
+        mean[n] = x0 + m1;
+        rstd[n] = 1.f / sqrtf(fmaxf(s2 / (float)K - m1 * m1, 0.f) + eps);
+    }
+}
+
 // ---------------------------------------------------------------- projection GEMM
 struct GemmArgs {
     const uint16_t* X;     // [R][K] token rows
     const uint16_t* Wt;    // [Nc][K] weight rows
     const float* bias;     // [Nc] or nullptr
     const float* colsum;   // [Nc] (LayerNorm mode)
-    float ln_eps;
+    const float* mean;     // [R] token means (LayerNorm mode)
+    const float* rstd;     // [R] token inverse deviations (LayerNorm mode)
     uint16_t* dst[3];      // output column ranges [0, split), [split, 2 split), [2 split, 3 split)
     int R, K, Nc, split;
     int phi_cols;          // columns [0, phi_cols) leave as the relu feature map's preimage
@@ -95,7 +130,6 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
     constexpr int TC = 128, TN = 128, KC = 64, STR = KC + 8;
     __shared__ __attribute__((aligned(16))) uint16_t la[2][TC * STR];
     __shared__ __attribute__((aligned(16))) uint16_t lb[2][TN * STR];
-    __shared__ float mean_s[TN], rstd_s[TN];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, gq = lane >> 4;
@@ -120,59 +154,48 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
     const int c0 = ct * TC, n0 = nt * TN;
     const int nk = (a.K + KC - 1) / KC;
 
-    if constexpr (LN) {
-        // token statistics, two passes over the row: thread = (token, half)
-        const int row = tid >> 1, half = tid & 1;
-        const int n = min(n0 + row, a.R - 1);
-        const uint16_t* xr = a.X + (size_t)n * a.K;
-        float s = 0.f;
-        for (int k0 = 8 * half; k0 < a.K; k0 += 16) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(xr + k0);
+    // ---- staging: unit u = (row, 8 k) of a 128 x 64 chunk, 4 per thread and operand,
+    // through buffer descriptors: the lane's byte offset is fixed, the chunk's
+    // advance is a scalar offset.  Only a partial last chunk is masked, when
+    // the registers go to LDS after the MFMAs of the current chunk, so the
+    // loads of the next chunk stay in flight.
+    // Byte ranges and offsets are below 2^32 (tensors hold fewer than 2^31
+    // elements): unsigned 32-bit arithmetic, passed as the bit patterns.
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.Wt, 0, (int)((uint32_t)a.Nc * (uint32_t)a.K * 2u), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)a.X, 0, (int)((uint32_t)a.R * (uint32_t)a.K * 2u), 0x00020000);
+    int offw[4], offx[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s += bf_lo(x[j]) + bf_hi(x[j]);
-        }
-        s += shfl_xor(s, 1);
-        const float mu = s / (float)a.K;
-        float s2 = 0.f;
-        for (int k0 = 8 * half; k0 < a.K; k0 += 16) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(xr + k0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float d0 = bf_lo(x[j]) - mu, d1 = bf_hi(x[j]) - mu;
-                s2 += d0 * d0 + d1 * d1;
-            }
-        }
-        s2 += shfl_xor(s2, 1);
-        if (half == 0) {
-            mean_s[row] = mu;
-            rstd_s[row] = 1.f / sqrtf(s2 / (float)a.K + a.ln_eps);
-        }
+    for (int s = 0; s < 4; ++s) {
+        const int u = tid + 256 * s;
+        const int row = u >> 3;
+        offw[s] = (int)(((uint32_t)min(c0 + row, a.Nc - 1) * (uint32_t)a.K + (uint32_t)(u & 7) * 8u) * 2u);
+        offx[s] = (int)(((uint32_t)min(n0 + row, a.R - 1) * (uint32_t)a.K + (uint32_t)(u & 7) * 8u) * 2u);
     }
-
-    // ---- staging: unit u = (row, 8 k) of a 128 x 64 chunk, 4 per thread and operand
     u32x4 ra[4], rb[4];
     auto gload = [&](int kc) {
+        const int so = __builtin_amdgcn_readfirstlane(kc * KC * 2);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int u = tid + 256 * s;
-            const int row = u >> 3, k = kc * KC + (u & 7) * 8;
-            const bool kin = k < a.K;
-            const int kk = kin ? k : 0;
-            const int c = min(c0 + row, a.Nc - 1), n = min(n0 + row, a.R - 1);
-            const u32x4 w = *reinterpret_cast<const u32x4*>(a.Wt + (size_t)c * a.K + kk);
-            const u32x4 x = *reinterpret_cast<const u32x4*>(a.X + (size_t)n * a.K + kk);
-            const uint32_t m = kin ? 0xffffffffu : 0u;
-            ra[s] = u32x4{w[0] & m, w[1] & m, w[2] & m, w[3] & m};
-            rb[s] = u32x4{x[0] & m, x[1] & m, x[2] & m, x[3] & m};
+            ra[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, offw[s], so, 0));
+            rb[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, offx[s], so, 0));
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf, int kc) {
+        const bool partial = (kc + 1) * KC > a.K;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int u = tid + 256 * s;
             const int off = (u >> 3) * STR + (u & 7) * 8;
-            *reinterpret_cast<u32x4*>(&la[buf][off]) = ra[s];
-            *reinterpret_cast<u32x4*>(&lb[buf][off]) = rb[s];
+            u32x4 x = ra[s], y = rb[s];
+            if (partial) {
+                const uint32_t m = kc * KC + (u & 7) * 8 < a.K ? 0xffffffffu : 0u;
+                x = u32x4{x[0] & m, x[1] & m, x[2] & m, x[3] & m};
+                y = u32x4{y[0] & m, y[1] & m, y[2] & m, y[3] & m};
+            }
+            *reinterpret_cast<u32x4*>(&la[buf][off]) = x;
+            *reinterpret_cast<u32x4*>(&lb[buf][off]) = y;
         }
     };
 
@@ -183,12 +206,7 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kc = 0; kc < nk; ++kc) {
-        const int buf = kc & 1;
-        if (kc + 1 < nk) gload(kc + 1);
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < KC / 32; ++ks) {
             u32x4 fa[4], fb[4];
@@ -203,37 +221,46 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
         }
-        if (kc + 1 < nk) lstore(buf ^ 1);
+    };
+    gload(0);
+    lstore(0, 0);
+    __syncthreads();
+    for (int kc = 0; kc < nk; ++kc) {
+        const int buf = kc & 1;
+        if (kc + 1 < nk) gload(kc + 1);
+        compute(buf);
+        if (kc + 1 < nk) lstore(buf ^ 1, kc + 1);
         __syncthreads();
     }
 
     // ---- epilogue: lane (li, gq) holds features c .. c+3 of token n
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int nl = 64 * wn + 16 * j + li;
-        const int n = n0 + nl;
-        float mu = 0.f, rs = 1.f;
-        if constexpr (LN) {
-            mu = mean_s[nl];
-            rs = rstd_s[nl];
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int c = c0 + 64 * wc + 16 * i + 4 * gq;
+        if (c >= a.Nc) continue;   // Nc is a multiple of 4
+        const f32x4 bias = a.bias ? *reinterpret_cast<const f32x4*>(a.bias + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 cs = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (LN) cs = *reinterpret_cast<const f32x4*>(a.colsum + c);
+        const int which = c / a.split, cc = c - which * a.split;
+        uint16_t* d = which == 0 ? a.dst[0] : (which == 1 ? a.dst[1] : a.dst[2]);
+        const bool pre = c < a.phi_cols;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = c0 + 64 * wc + 16 * i + 4 * gq;
-            if (n >= a.R || c >= a.Nc) continue;
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + 64 * wn + 16 * j + li;
+            if (n >= a.R) continue;
+            float mu = 0.f, rs = 1.f;
+            if constexpr (LN) {
+                mu = a.mean[n];
+                rs = a.rstd[n];
+            }
             float o[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 float x = acc[i][j][v];
-                if constexpr (LN) x = rs * (x - mu * a.colsum[c + v]);
-                if (a.bias) x += a.bias[c + v];
-                if (c < a.phi_cols) x = relu_phi_preimage(x, a.phi_eps);
-                o[v] = x;
+                if constexpr (LN) x = rs * (x - mu * cs[v]);
+                x += bias[v];
+                o[v] = pre ? relu_phi_preimage(x, a.phi_eps) : x;
             }
-            const int which = c / a.split, cc = c - which * a.split;
-            uint16_t* d = a.dst[0];
-            if (which == 1) d = a.dst[1];
-            if (which == 2) d = a.dst[2];
             *reinterpret_cast<u32x2*>(d + (size_t)n * a.split + cc) = u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
         }
     }
@@ -373,7 +400,9 @@ hipError_t run_layer_bf16(const LayerLaunch& L) {
     a.Wt = L.wf;
     a.bias = L.biasf;
     a.colsum = L.colsum;
-    a.ln_eps = L.ln_eps;
+    a.mean = L.mean;
+    a.rstd = L.rstd;
+    ln_stats_bf16<<<(R + 31) / 32, 256, 0, L.stream>>>(L.x, L.mean, L.rstd, R, C, L.ln_eps);
     a.dst[0] = L.q; a.dst[1] = L.k; a.dst[2] = L.v;
     a.R = R; a.K = C; a.Nc = 3 * C; a.split = C;
     a.phi_cols = (L.relu_phi && !L.qn_w) ? 2 * C : 0;
@@ -400,7 +429,8 @@ hipError_t run_layer_bf16(const LayerLaunch& L) {
     b.Wt = L.w_out;
     b.bias = L.b_out;
     b.colsum = nullptr;
-    b.ln_eps = 0.f;
+    b.mean = nullptr;
+    b.rstd = nullptr;
     b.dst[0] = L.y; b.dst[1] = L.y; b.dst[2] = L.y;
     b.R = R; b.K = C; b.Nc = C; b.split = C;
     b.phi_cols = 0;

@@ -81,6 +81,8 @@ struct LayerLaunch {
     uint16_t* wf;           // workspace: w_qkv scaled by the LayerNorm weight [3C][C]
     float* colsum;          // workspace [3C]
     float* biasf;           // workspace [3C]
+    float* mean;            // workspace [R]: token means of x
+    float* rstd;            // workspace [R]: token inverse deviations of x
     const float* ln_w;
     const float* ln_b;
     const float* b_qkv;     // or nullptr

@@ -340,7 +340,7 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
 // ---------------------------------------------------------------- layer
 
 struct LayerLayout {
-    size_t q, k, v, o, wf, colsum, biasf, core, total;
+    size_t q, k, v, o, wf, colsum, biasf, mean, rstd, core, total;
 };
 
 LayerLayout layer_layout(const Shape& s) {
@@ -354,7 +354,9 @@ LayerLayout layer_layout(const Shape& s) {
     L.wf = L.o + act;
     L.colsum = L.wf + align_up(3 * C * C * 2);
     L.biasf = L.colsum + align_up(3 * C * 4);
-    L.core = L.biasf + align_up(3 * C * 4);
+    L.mean = L.biasf + align_up(3 * C * 4);
+    L.rstd = L.mean + align_up(R * 4);
+    L.core = L.rstd + align_up(R * 4);
     L.total = L.core + layout(s).total;
     return L;
 }
@@ -418,6 +420,8 @@ mhla_status layer_impl(const void* x, const float* W, const mhla_grid* grid, con
     L.wf = reinterpret_cast<uint16_t*>(base + lay.wf);
     L.colsum = reinterpret_cast<float*>(base + lay.colsum);
     L.biasf = reinterpret_cast<float*>(base + lay.biasf);
+    L.mean = reinterpret_cast<float*>(base + lay.mean);
+    L.rstd = reinterpret_cast<float*>(base + lay.rstd);
     L.ln_w = P->ln_w; L.ln_b = P->ln_b; L.b_qkv = P->b_qkv;
     L.qn_w = P->qn_w; L.kn_w = P->kn_w;
     L.lepe_w = P->lepe_w; L.lepe_b = P->lepe_b;
