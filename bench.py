@@ -33,6 +33,7 @@ KERNEL_SOURCES = {
     "3kernel": _FWD,
     "fused": _FWD,
     "causal": _FWD + ("kernels_causal_bf16.hip",),
+    "layer": _FWD + ("kernels_layer_bf16.hip",),
 }
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 MALL_BYTES = 256 << 20          # Infinity Cache
@@ -351,6 +352,10 @@ def bench_layer(args, p, torch, mh, synth):
         stages[name] = {"avg_us": round(float(stage_ms[j]) * 1e3, 2), "alg_bytes": int(nbytes), "flops": int(flops),
                         "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
                         "tflops": round(tflops, 1), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    traffic = measured_traffic(p.name + "-layer", "layer") if (not args.qk_norm and args.phi == "relu"
+                                                                and not args.batch and not args.heads) else {}
+    for n in stages:
+        stages[n]["traffic"] = traffic.get(n)
     dom = max(stages, key=lambda n: stages[n]["avg_us"])
     d = stages[dom]
     if d["mfma_frac"] > d["hbm_frac"]:
@@ -358,7 +363,7 @@ def bench_layer(args, p, torch, mh, synth):
                 "frac": d["mfma_frac"]}
     else:
         roof = {"bound": "hbm", "achieved": d["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": d["hbm_frac"]}
-    roof.update({"kernel": dom, "traffic": None, "avg_us": d["avg_us"], "alg_bytes": d["alg_bytes"]})
+    roof.update({"kernel": dom, "traffic": traffic.get(dom), "avg_us": d["avg_us"], "alg_bytes": d["alg_bytes"]})
     # compulsory bytes of the whole layer: x, y, the weights and W
     U = 2 * R * C * 2 + 4 * C * C * 2 + p.n_blocks ** 2 * 4
     cpu = None
