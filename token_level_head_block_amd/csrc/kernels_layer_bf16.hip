@@ -306,25 +306,27 @@ __global__ __launch_bounds__(256) void rms_qk_bf16(uint16_t* __restrict__ q, uin
 
 // ---------------------------------------------------------------- LePE
 // o[n][c] += b[c] + sum_{dy,dx} w[c][dy][dx] v[y+dy-2][x+dx-2][c] (zero outside
-// the grid), per batch item on the Y x X grid.  Workgroup = (b, 8 rows x 32
-// columns of tokens, 32 channels): the 12 x 36 halo of v goes to LDS; thread
-// (channel pair, pair of columns) keeps its two channels' 25 weights in
-// registers and slides down the 12 input rows, feeding the 8 x 2 outputs.
-constexpr int LP_TY = 8, LP_TX = 32, LP_TCH = 32;
+// the grid), per batch item on the Y x X grid.  Workgroup = (b, 8 rows x 16
+// columns of tokens, 64 channels): a token's 64 channels are one 128-byte line,
+// so v's 12 x 20 halo (in LDS) and the read-modify-write of o move whole lines.
+// Thread (channel pair, pair of columns) keeps its two channels' 25 weights in
+// registers and slides down the 12 input rows, feeding 8 x 2 outputs.
+constexpr int LP_TY = 8, LP_TX = 16, LP_TCH = 64;
 
 __global__ __launch_bounds__(256) void lepe_add_bf16(const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                                                      const float* __restrict__ w, const float* __restrict__ bias,
                                                      int Y, int X, int C) {
-    constexpr int HY = LP_TY + 4, HX = LP_TX + 4;
-    __shared__ __attribute__((aligned(16))) uint32_t vt[HY * HX * (LP_TCH / 2)];   // bf16 channel pairs
+    constexpr int HY = LP_TY + 4, HX = LP_TX + 4, PAIRS = LP_TCH / 2;
+    __shared__ __attribute__((aligned(16))) uint32_t vt[HY * HX * PAIRS];   // bf16 channel pairs
     const int tid = threadIdx.x;
-    const int ncg = C / LP_TCH, ntx = (X + LP_TX - 1) / LP_TX, nty = (Y + LP_TY - 1) / LP_TY;
+    const int ncg = (C + LP_TCH - 1) / LP_TCH, ntx = (X + LP_TX - 1) / LP_TX, nty = (Y + LP_TY - 1) / LP_TY;
     int id = blockIdx.x;
     const int cg = id % ncg; id /= ncg;
     const int tx = id % ntx; id /= ntx;
     const int ty = id % nty;
     const int b = id / nty;
     const int y0 = ty * LP_TY, x0 = tx * LP_TX, ch0 = cg * LP_TCH;
+    const int nch = min(LP_TCH, C - ch0);   // 64, or 32 for the last group when C % 64 == 32
     const size_t img = (size_t)b * Y * X;
     // halo of v: unit = (position, 8 channels)
     for (int u = tid; u < HY * HX * (LP_TCH / 8); u += 256) {
@@ -332,19 +334,21 @@ __global__ __launch_bounds__(256) void lepe_add_bf16(const uint16_t* __restrict_
         const int hy = pos / HX, hx = pos % HX;
         const int yy = y0 + hy - 2, xx = x0 + hx - 2;
         u32x4 val = u32x4{0u, 0u, 0u, 0u};
-        if (yy >= 0 && yy < Y && xx >= 0 && xx < X)
+        if (yy >= 0 && yy < Y && xx >= 0 && xx < X && part * 8 < nch)
             val = *reinterpret_cast<const u32x4*>(V + (img + (size_t)yy * X + xx) * C + ch0 + part * 8);
-        *reinterpret_cast<u32x4*>(&vt[pos * (LP_TCH / 2) + part * 4]) = val;
+        *reinterpret_cast<u32x4*>(&vt[pos * PAIRS + part * 4]) = val;
     }
-    const int p = tid & 15, xg = tid >> 4;   // channel pair, pair of output columns
+    const int p = tid & (PAIRS - 1), xg = tid / PAIRS;   // channel pair, pair of output columns
     const int c = ch0 + 2 * p;
+    const bool cok = 2 * p < nch;
+    const int cw = cok ? c : ch0;
     float w0[25], w1[25];
 #pragma unroll
     for (int t = 0; t < 25; ++t) {
-        w0[t] = w[(size_t)c * 25 + t];
-        w1[t] = w[(size_t)(c + 1) * 25 + t];
+        w0[t] = w[(size_t)cw * 25 + t];
+        w1[t] = w[(size_t)(cw + 1) * 25 + t];
     }
-    const float b0 = bias ? bias[c] : 0.f, b1 = bias ? bias[c + 1] : 0.f;
+    const float b0 = bias ? bias[cw] : 0.f, b1 = bias ? bias[cw + 1] : 0.f;
     __syncthreads();
     float acc[LP_TY][2][2];
 #pragma unroll
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(256) void lepe_add_bf16(const uint16_t* __restrict_
         float in0[6], in1[6];
 #pragma unroll
         for (int s = 0; s < 6; ++s) {
-            const uint32_t pr = vt[(iy * HX + 2 * xg + s) * (LP_TCH / 2) + p];
+            const uint32_t pr = vt[(iy * HX + 2 * xg + s) * PAIRS + p];
             in0[s] = bf_lo(pr);
             in1[s] = bf_hi(pr);
         }
@@ -373,6 +377,7 @@ __global__ __launch_bounds__(256) void lepe_add_bf16(const uint16_t* __restrict_
                 }
         }
     }
+    if (!cok) return;
 #pragma unroll
     for (int oy = 0; oy < LP_TY; ++oy)
 #pragma unroll
@@ -419,7 +424,7 @@ hipError_t run_layer_bf16(const LayerLaunch& L) {
     rec(2);
     // 3. LePE added into o
     if (L.lepe_w) {
-        const int nblk = L.B * ((L.Y + LP_TY - 1) / LP_TY) * ((L.X + LP_TX - 1) / LP_TX) * (C / LP_TCH);
+        const int nblk = L.B * ((L.Y + LP_TY - 1) / LP_TY) * ((L.X + LP_TX - 1) / LP_TX) * ((C + LP_TCH - 1) / LP_TCH);
         lepe_add_bf16<<<nblk, 256, 0, L.stream>>>(L.v, L.o, L.lepe_w, L.lepe_b, L.Y, L.X, C);
     }
     rec(3);
