@@ -27,6 +27,9 @@ CASES = [
     ("causal-1d-M1", 1, 2, 64, (1, 200), (1, 200), 1.0),
     ("causal-rows-2d", 1, 2, 32, (12, 20), (3, 20), 0.5),
     ("causal-frames-3d", 1, 2, 64, (4, 6, 8), (1, 6, 8), 1.0),
+    ("causal-d128-T256", 1, 2, 128, (1, 1024), (1, 256), 1.0),
+    ("causal-d128-T40", 2, 1, 128, (1, 200), (1, 40), 1.0),
+    ("causal-d128-M1", 1, 1, 128, (1, 300), (1, 300), 1.0),
 ]
 
 
@@ -76,6 +79,15 @@ def test_causal_sequence_workload():
     check_conditioned(p, q, k, v, W, to_host64(out), ref)
     again = run.forward(mh.MHLA_PATH_CAUSAL)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+
+
+def test_causal_sequence_d128():
+    """16384 tokens in chunks of 256 at d = 128 (four heads): every output, conditioned."""
+    p = synth.Problem("seq-16384-chunk256-d128", 1, 4, 128, (1, 16384), (1, 256), dtype=BF)
+    q, k, v, W = synth.make_inputs(p, seed=65)
+    ref = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    out = Run(p, q, k, v, W).forward(mh.MHLA_PATH_CAUSAL)
+    check_conditioned(p, q, k, v, W, to_host64(out), ref)
 
 
 def test_causal_sequence_workload_local_w():

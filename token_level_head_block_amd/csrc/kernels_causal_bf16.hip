@@ -1,6 +1,6 @@
 // kernels_causal_bf16.hip -- the causal chunkwise form of MHLA (paperlayer.ai
 // summary, appendix B "Causal MHLA": block-specific mixed summaries reused per
-// block, causality preserved), bf16 inputs, d = 32 or 64, on gfx950.
+// block, causality preserved), bf16 inputs, d = 32, 64 or 128, on gfx950.
 //
 // For chunks that are contiguous in raster order, query n of chunk i reads
 //   the mixture of the earlier chunks,  St_i< = sum_{j < i} W[i,j] S_j  (z likewise),
@@ -263,10 +263,16 @@ void launch(const Launch& L) {
 
 template <int D>
 void launch_d(const Launch& L) {
-    // Waves per workgroup: enough for two query groups each, at most 8.
+    // Waves per workgroup: enough for two query groups each, at most 8 (at
+    // most 4 at d = 128, whose 256-token tile would not fit LDS).
     const int nit = (L.g.T + 15) / 16;
-    if (nit > 8) launch<D, 8>(L);
-    else if (nit > 4) launch<D, 4>(L);
+    if constexpr (D < 128) {
+        if (nit > 8) {
+            launch<D, 8>(L);
+            return;
+        }
+    }
+    if (nit > 4) launch<D, 4>(L);
     else if (nit > 2) launch<D, 2>(L);
     else launch<D, 1>(L);
 }
@@ -277,6 +283,7 @@ hipError_t launch_causal_apply_bf16(const Launch& L) {
     switch (L.g.D) {
         case 32: launch_d<32>(L); break;
         case 64: launch_d<64>(L); break;
+        case 128: launch_d<128>(L); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

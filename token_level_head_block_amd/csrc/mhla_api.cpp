@@ -75,7 +75,7 @@ bool chunks_contiguous(const Shape& s) {
 }
 
 bool causal_supported(const Shape& s) {
-    return s.dtype == MHLA_BF16 && (s.D == 32 || s.D == 64) && chunks_contiguous(s);
+    return s.dtype == MHLA_BF16 && chunks_contiguous(s);   // head_dim 32, 64 or 128
 }
 
 struct Layout {
