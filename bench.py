@@ -173,27 +173,28 @@ def bench_backward(args, p, torch, mh, synth):
     """One step = one mhla_backward call (recompute of the forward summaries,
     query side, transposed mixing and dW, key/value side) on synthetic inputs
     and a synthetic upstream gradient resident in HBM."""
-    if p.dtype != synth.BF16 or p.head_dim not in (32, 64):
-        print("the backward pass supports bf16 problems with d = 32 or 64", file=sys.stderr)
-        sys.exit(1)
     tensor_bytes = p.batch * p.n_tokens * p.heads * p.head_dim * p.elem_bytes
     sets = args.sets or max(2, int(np.ceil(2 * MALL_BYTES / (7 * tensor_bytes))))
 
     def dev(x):
-        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        if p.dtype == synth.BF16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
 
     data, host0 = [], None
     for s in range(sets):
         q, k, v, W = synth.make_inputs(p, seed=(args.config, s) if s else args.config, w_kind=args.w)
         rng = np.random.default_rng(1000 + s)
-        g = synth.bf16_bits(rng.standard_normal(q.shape).astype(np.float32))
+        g = rng.standard_normal(q.shape).astype(np.float32)
+        g = synth.bf16_bits(g) if p.dtype == synth.BF16 else g
         t = [dev(x) for x in (q, k, v, g)]
         outs = [torch.empty_like(t[0]) for _ in range(3)]
         dW = torch.empty(p.n_blocks, p.n_blocks, dtype=torch.float32, device="cuda")
         data.append((t[0], t[1], t[2], torch.from_numpy(W).cuda(), t[3], outs[0], outs[1], outs[2], dW))
         if s == 0:
             host0 = (q, k, v, W, g)
-    gr = mh.make_grid(p.batch, p.heads, p.head_dim, mh.MHLA_BF16, p.grid, p.eps)
+    gr = mh.make_grid(p.batch, p.heads, p.head_dim, mh.MHLA_BF16 if p.dtype == synth.BF16 else mh.MHLA_F32,
+                      p.grid, p.eps)
     bl = mh.make_block(p.block)
     ws_bytes = mh.mhla_backward_workspace_bytes(gr, bl)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -248,10 +249,12 @@ def bench_backward(args, p, torch, mh, synth):
         "metric": "MHLA bwd tokens/s (dq, dk, dv, dW) + achieved HBM GB/s", "value":
             round(p.batch * p.n_tokens / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if p.dtype == synth.BF16 else "f32", "data": "synthetic",
         "config": {"workload": f"{p.name}: B={p.batch} H={p.heads} d={p.head_dim} grid={list(p.grid)} "
                                f"blocks={list(p.block)} N={p.n_tokens} M={p.n_blocks}",
-                   "pass": "backward", "input_sets": sets, "parallelism": "none (1 GPU)"},
+                   "pass": "backward", "kernels": "mfma" if p.dtype == synth.BF16 and p.head_dim <= 64 else "general",
+                   "input_sets": sets, "parallelism": "none (1 GPU)"},
         "path_hbm_gbps": round(U / (ms_step * 1e-3) / 1e9, 1),
         "path_hbm_frac": round(U / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "path_alg_bytes": U,
         "kernels": stages,

@@ -184,20 +184,25 @@ mhla_status mhla_forward_ex(const void* q, const void* k, const void* v, const f
  *
  * with phi'(x) = 1 for x > 0 and exp(x) otherwise.
  *
- * Supported: bfloat16 problems with head_dim 32 or 64 (MHLA_ERR_UNSUPPORTED
- * otherwise).  q, k, v, dout, dq, dk, dv: [B, N, H, d] bfloat16 as for the
- * forward; W: fp32 [M, M] (read); dW: fp32 [M, M], overwritten (zero for an
- * empty problem).  All device pointers, 16-byte aligned, owned by the caller;
- * no output may overlap an input or another output.  Products in bf16 MFMA
- * with fp32 accumulation; the forward summaries are recomputed; gradients of
- * the summaries are kept in bf16.  Asynchronous on `stream`. */
+ * Every problem the forward accepts: q, k, v, dout, dq, dk, dv: [B, N, H, d]
+ * in the grid's dtype as for the forward; W: fp32 [M, M] (read); dW: fp32
+ * [M, M], overwritten (zero for an empty problem).  All device pointers,
+ * 16-byte aligned, owned by the caller; no output may overlap an input or
+ * another output.  bfloat16 problems with head_dim 32 or 64: products in bf16
+ * MFMA with fp32 accumulation, gradients of the summaries kept in bf16.  Other
+ * problems (fp32, or head_dim 128): fp32 arithmetic throughout, with fp32
+ * records of the summaries and their gradients.  The forward summaries are
+ * recomputed.  Asynchronous on `stream`. */
 
-/* Bytes of device workspace mhla_backward needs (0 for an unsupported, invalid
- * or empty problem).  Layout from the start: the forward's regions 0-3 (see
- * mhla_workspace_bytes), then at 256-byte boundaries: gradients of the mixed
- * summaries as B*H*M bf16 records in the summaries' layout; gradients of the
- * summaries, B*H*M*d*d bf16 ([e][c] order); gradients of the normalisers,
- * B*H*M*d fp32; W^T in the mixing kernel's operand order; dW partial sums. */
+/* Bytes of device workspace mhla_backward needs (0 for an invalid or empty
+ * problem).  bf16 with head_dim 32 or 64, from the start: the forward's
+ * regions 0-3 (see mhla_workspace_bytes), then at 256-byte boundaries:
+ * gradients of the mixed summaries as B*H*M bf16 records in the summaries'
+ * layout; gradients of the summaries, B*H*M*d*d bf16 ([e][c] order); gradients
+ * of the normalisers, B*H*M*d fp32; W^T in the mixing kernel's operand order;
+ * dW partial sums.  Other problems: four fp32 record arrays of B*H*M*(d*d + d)
+ * values (summaries [c][e] then z, mixed summaries, their gradients, the
+ * summaries' gradients), then dW partial sums. */
 size_t mhla_backward_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
 
 /* The backward pass, enqueued on `stream`.  ws: workspace of ws_bytes >=

@@ -149,11 +149,12 @@ def test_backward_workspace_and_validation(L):
     g, b = cfg2()
     need = mh.mhla_backward_workspace_bytes(g, b)
     assert need > mh.mhla_workspace_bytes(g, b)
-    # unsupported: d = 128, fp32
-    g128 = mh.make_grid(1, 12, 128, mh.MHLA_BF16, (16, 64, 64))
-    assert mh.mhla_backward_workspace_bytes(g128, mh.make_block((4, 8, 8))) == 0
-    g32 = mh.make_grid(1, 1, 32, mh.MHLA_F32, (16, 16))
-    assert mh.mhla_backward_workspace_bytes(g32, mh.make_block((4, 4))) == 0
+    # d = 128 and fp32 take the general path: fp32 records [S | z] four times, dW partials
+    g128, b128 = mh.make_grid(1, 12, 128, mh.MHLA_BF16, (16, 64, 64)), mh.make_block((4, 8, 8))
+    rec = 12 * 256 * (128 * 128 + 128) * 4
+    assert mh.mhla_backward_workspace_bytes(g128, b128) >= 4 * rec + 256 * 256 * 4
+    g32, b32 = mh.make_grid(1, 1, 32, mh.MHLA_F32, (16, 16)), mh.make_block((4, 4))
+    assert mh.mhla_backward_workspace_bytes(g32, b32) >= 4 * 16 * (32 * 32 + 32) * 4
 
     def bwd(g_, b_, q=BIG, k=2 * BIG, v=3 * BIG, W=4 * BIG, dout=5 * BIG, dq=6 * BIG, dk=7 * BIG,
             dv=8 * BIG, dW=9 * BIG, ws=10 * BIG, ws_bytes=None):
@@ -161,8 +162,8 @@ def test_backward_workspace_and_validation(L):
         return L.mhla_backward(q, k, v, W, dout, ctypes.byref(g_), ctypes.byref(b_), dq, dk, dv, dW, ws, wsb,
                                None, None)
 
-    assert bwd(g128, mh.make_block((4, 8, 8)), ws_bytes=1 << 30) == mh.MHLA_ERR_UNSUPPORTED
-    assert bwd(g32, mh.make_block((4, 4)), ws_bytes=1 << 30) == mh.MHLA_ERR_UNSUPPORTED
+    assert bwd(g128, b128, ws_bytes=mh.mhla_backward_workspace_bytes(g128, b128) - 16) == mh.MHLA_ERR_INVALID_ARG
+    assert bwd(g32, b32, dW=None) == mh.MHLA_ERR_INVALID_ARG
     assert bwd(g, b, dout=None) == mh.MHLA_ERR_INVALID_ARG
     assert bwd(g, b, dW=None) == mh.MHLA_ERR_INVALID_ARG
     assert bwd(g, b, dk=7 * BIG + 8) == mh.MHLA_ERR_MISALIGNED

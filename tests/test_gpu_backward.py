@@ -1,10 +1,12 @@
 """Gradients from the HIP backward pass against the float64 CPU oracle's,
 through the C ABI.
 
-Bar: max|d| / max|ref| <= 1e-2 for each of dq, dk, dv and dW (bf16 inputs and
-outputs, fp32 accumulation, bf16 intermediates), the forward's bf16 bar
-applied to each gradient.  Small problems compare every element; the full
-workloads compare every element too (the oracle finishes them in seconds).
+Bar: max|d| / max|ref| <= 1e-2 for each of dq, dk, dv and dW with bf16
+inputs and outputs, the forward's bf16 bar applied to each gradient; 1e-5,
+the forward's fp32 bar, with fp32 inputs.  bf16 problems with d = 32 or 64
+run on the MFMA kernels, the others (fp32, d = 128) on the general fp32 path.
+Small problems compare every element; the full workloads compare every
+element too (the oracle finishes them in seconds).
 """
 import numpy as np
 import pytest
@@ -19,7 +21,8 @@ from gpu_util import Run, rel_err, say, to_host64
 pytestmark = pytest.mark.gpu
 
 BF = synth.BF16
-TOL = 1e-2
+F32 = synth.F32
+TOL = {BF: 1e-2, F32: 1e-5}
 
 # name, B, H, d, grid, block, std
 SMALL = [
@@ -34,10 +37,20 @@ SMALL = [
     ("bwd-d64-T256-M160", 1, 2, 64, (160, 256), (16, 16), 1.0),
 ]
 
+# the general path: name, B, H, d, grid, block, dtype
+GENERAL = [
+    ("bwd-f32-d32-M16", 1, 1, 32, (16, 16), (4, 4), F32),
+    ("bwd-f32-d64-3d", 2, 2, 64, (4, 8, 8), (2, 4, 4), F32),
+    ("bwd-f32-d128-T25", 1, 2, 128, (10, 10), (5, 5), F32),
+    ("bwd-bf16-d128-M16", 1, 2, 128, (16, 16), (4, 4), BF),
+    ("bwd-bf16-d128-T6-M42", 2, 1, 128, (14, 18), (2, 3), BF),
+    ("bwd-bf16-d128-M1", 1, 1, 128, (8, 9), (8, 9), BF),
+]
+
 
 def upstream(p, seed):
-    g = np.random.default_rng(seed).standard_normal((p.batch, p.n_tokens, p.heads, p.head_dim))
-    return synth.bf16_bits(g.astype(np.float32))
+    g = np.random.default_rng(seed).standard_normal((p.batch, p.n_tokens, p.heads, p.head_dim)).astype(np.float32)
+    return synth.bf16_bits(g) if p.dtype == BF else g
 
 
 def check(p, seed):
@@ -60,7 +73,7 @@ def check(p, seed):
         else:
             e = rel_err(a, r)
             say(f"  {p.name} {name}: max|d|/max|ref| = {e:.3e}")
-        assert e <= TOL, name
+        assert e <= TOL[p.dtype], name
     return run, g, got
 
 
@@ -70,7 +83,13 @@ def test_backward_small_problems(case):
     check(synth.Problem(name, B, H, d, grid, block, dtype=BF, std=std), seed=41)
 
 
-@pytest.mark.parametrize("cfg_index", [1, 2, 3])
+@pytest.mark.parametrize("case", GENERAL, ids=lambda c: c[0])
+def test_backward_general_path(case):
+    name, B, H, d, grid, block, dt = case
+    check(synth.Problem(name, B, H, d, grid, block, dtype=dt), seed=45)
+
+
+@pytest.mark.parametrize("cfg_index", [0, 1, 2, 3, 4])
 def test_backward_full_workloads(cfg_index):
     """Every gradient element at full size; a second call is bitwise equal."""
     p = synth.CONFIGS[cfg_index]

@@ -101,6 +101,31 @@ struct LayerLaunch {
 };
 hipError_t run_layer_bf16(const LayerLaunch& L);
 
+// Backward pass for the problems the bf16 MFMA kernels do not take (fp32
+// inputs, or head_dim 128): fp32 records [S | z] of L = d*d + d values.
+struct GenericBwd {
+    Geo g;
+    int bf16;                 // inputs and gradients in bf16 (else fp32)
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* W;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dw;
+    float* s;                 // [BH][M][L] summaries
+    float* st;                // [BH][M][L] mixed summaries
+    float* dst;               // [BH][M][L] their gradients
+    float* ds;                // [BH][M][L] gradients of the summaries
+    float* part;              // [nsplit][M][M] dW partial sums
+    int nsplit;
+    const hipEvent_t* events; // 5 events or nullptr
+    hipStream_t stream;
+};
+hipError_t run_bwd_generic(const GenericBwd& B);
+
 // p[0 .. n) = 0 by a kernel (safe inside a captured graph).
 hipError_t zero_f32(float* p, int n, hipStream_t stream);
 

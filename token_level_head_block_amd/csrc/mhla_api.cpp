@@ -250,13 +250,39 @@ BwdLayout bwd_layout(const Shape& s) {
     return L;
 }
 
+// The general backward path (fp32 inputs, or head_dim 128): fp32 records.
+struct GenLayout {
+    size_t s, st, dst, ds, part, total;
+    int nsplit;
+};
+
+GenLayout gen_layout(const Shape& s) {
+    GenLayout L;
+    const size_t rec = (size_t)(s.B * s.H * s.M) * (size_t)(s.D * s.D + s.D) * 4;
+    L.s = 0;
+    L.st = align_up(rec);
+    L.dst = L.st + align_up(rec);
+    L.ds = L.dst + align_up(rec);
+    L.part = L.ds + align_up(rec);
+    // dW: 32 x 32 tiles, the (b h, 32-value chunk) pairs shared so that about
+    // 1024 workgroups run
+    const int64_t tiles = ((s.M + 31) / 32) * ((s.M + 31) / 32);
+    const int64_t chunks = s.B * s.H * ((s.D * s.D + s.D) / 32);
+    int64_t ns = 1024 / tiles;
+    if (ns < 1) ns = 1;
+    if (ns > chunks) ns = chunks > 0 ? chunks : 1;
+    L.nsplit = (int)ns;
+    L.total = L.part + align_up((size_t)ns * (size_t)(s.M * s.M) * 4);
+    return L;
+}
+
 mhla_status backward_impl(const void* q, const void* k, const void* v, const float* W, const void* dout,
                           const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
                           float* dW, void* ws, size_t ws_bytes, const hipEvent_t* events, hipStream_t stream) {
     Shape s;
     mhla_status st = check(grid, block, &s);
     if (st != MHLA_OK) return st;
-    if (!bwd_supported(s)) return MHLA_ERR_UNSUPPORTED;
+    const bool fast = bwd_supported(s);
     if (!dW) return MHLA_ERR_INVALID_ARG;
     if (!aligned16(dW)) return MHLA_ERR_MISALIGNED;
     const size_t wbytes = (size_t)(s.M * s.M) * 4;
@@ -284,23 +310,43 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
             if (overlaps(outs[a], outsz[a], outs[b], outsz[b])) return MHLA_ERR_INVALID_ARG;
     }
     const BwdLayout lay = bwd_layout(s);
+    const GenLayout glay = gen_layout(s);
+    const size_t need = fast ? lay.total : glay.total;
     bool owned = false;
     if (ws) {
-        if (ws_bytes < lay.total) return MHLA_ERR_INVALID_ARG;
+        if (ws_bytes < need) return MHLA_ERR_INVALID_ARG;
         if (!aligned16(ws)) return MHLA_ERR_MISALIGNED;
         for (int b = 0; b < 5; ++b)
-            if (overlaps(ws, lay.total, ins[b], insz[b])) return MHLA_ERR_INVALID_ARG;
+            if (overlaps(ws, need, ins[b], insz[b])) return MHLA_ERR_INVALID_ARG;
         for (int a = 0; a < 4; ++a)
-            if (overlaps(ws, lay.total, outs[a], outsz[a])) return MHLA_ERR_INVALID_ARG;
+            if (overlaps(ws, need, outs[a], outsz[a])) return MHLA_ERR_INVALID_ARG;
     } else {
         if (ws_bytes != 0) return MHLA_ERR_INVALID_ARG;
-        if (hipMallocAsync(&ws, lay.total, stream) != hipSuccess || !ws) {
+        if (hipMallocAsync(&ws, need, stream) != hipSuccess || !ws) {
             (void)hipGetLastError();
             return MHLA_ERR_ALLOC;
         }
         owned = true;
     }
     char* base = static_cast<char*>(ws);
+    if (!fast) {
+        mhla::GenericBwd G;
+        G.g = make_geo(s, grid->eps);
+        G.bf16 = s.dtype == MHLA_BF16;
+        G.q = q; G.k = k; G.v = v; G.dout = dout; G.W = W;
+        G.dq = dq; G.dk = dk; G.dv = dv; G.dw = dW;
+        G.s = reinterpret_cast<float*>(base + glay.s);
+        G.st = reinterpret_cast<float*>(base + glay.st);
+        G.dst = reinterpret_cast<float*>(base + glay.dst);
+        G.ds = reinterpret_cast<float*>(base + glay.ds);
+        G.part = reinterpret_cast<float*>(base + glay.part);
+        G.nsplit = glay.nsplit;
+        G.events = events;
+        G.stream = stream;
+        const hipError_t err = mhla::run_bwd_generic(G);
+        if (owned) (void)hipFreeAsync(ws, stream);
+        return err == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
+    }
     mhla::BwdLaunch B;
     mhla::Launch& L = B.F;
     L.q = q; L.k = k; L.v = v; L.W = W; L.out = nullptr;
@@ -466,8 +512,8 @@ extern "C" {
 
 size_t mhla_backward_workspace_bytes(const mhla_grid* grid, const mhla_block* block) {
     Shape s;
-    if (check(grid, block, &s) != MHLA_OK || !bwd_supported(s) || s.B == 0 || s.H == 0) return 0;
-    return bwd_layout(s).total;
+    if (check(grid, block, &s) != MHLA_OK || s.B == 0 || s.H == 0) return 0;
+    return bwd_supported(s) ? bwd_layout(s).total : gen_layout(s).total;
 }
 
 mhla_status mhla_backward(const void* q, const void* k, const void* v, const float* W, const void* dout,
