@@ -407,9 +407,8 @@ def bench_layer(args, p, torch, mh, synth):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the (b, h) pairs are independent, so more GPUs would each run their own share).",
-              file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the (b, h) pairs are "
+              "independent, so more GPUs would each run their own share of them).", file=sys.stderr)
         sys.exit(2)
 
     import torch
