@@ -97,7 +97,7 @@ enum {
                                 mixes the summaries of blocks j < i and adds W[i,i] times its
                                 own block's tokens up to n.  block_kv_summary ->
                                 mix_summaries (W restricted to j < i) -> query_apply_causal.
-                                bfloat16 (any head_dim), and blocks that are contiguous
+                                bfloat16 or fp32, any head_dim, and blocks that are contiguous
                                 runs of raster indices (e.g. 1D chunks: grid {1, N}, block
                                 {1, T}); MHLA_ERR_UNSUPPORTED otherwise. */
 };

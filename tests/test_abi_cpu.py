@@ -187,11 +187,11 @@ def test_causal_path_validation(L):
     # full rows are
     assert mh.mhla_launch_plan(mh.make_grid(1, 2, 32, mh.MHLA_BF16, (12, 20)), mh.make_block((3, 20)),
                                mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_OK
-    # d = 128 is supported, fp32 is not
+    # every head_dim, bf16 and fp32
     assert mh.mhla_launch_plan(mh.make_grid(1, 2, 128, mh.MHLA_BF16, (1, 256)), mh.make_block((1, 64)),
                                mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_OK
     assert mh.mhla_launch_plan(mh.make_grid(1, 2, 32, mh.MHLA_F32, (1, 256)), mh.make_block((1, 64)),
-                               mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_ERR_UNSUPPORTED
+                               mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_OK
 
 
 def test_layer_workspace_and_validation(L):

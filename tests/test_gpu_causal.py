@@ -46,6 +46,27 @@ def test_causal_small(case):
     assert err <= TOL[BF]
 
 
+# fp32 problems (bar 1e-5): name, B, H, d, grid, block
+F32_CASES = [
+    ("causal-f32-d32-T16", 1, 2, 32, (1, 256), (1, 16)),
+    ("causal-f32-d64-T100", 2, 1, 64, (1, 400), (1, 100)),
+    ("causal-f32-d128-M1", 1, 1, 128, (1, 96), (1, 96)),
+    ("causal-f32-frames-3d", 1, 2, 64, (3, 4, 8), (1, 4, 8)),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: c[0])
+def test_causal_f32(case):
+    name, B, H, d, grid, block = case
+    p = synth.Problem(name, B, H, d, grid, block, dtype=synth.F32)
+    q, k, v, W = synth.make_inputs(p, seed=66)
+    ref = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    out = to_host64(Run(p, q, k, v, W).forward(mh.MHLA_PATH_CAUSAL))
+    err = rel_err(out, ref)
+    say(f"  {name}: max|d|/max|ref| = {err:.3e}")
+    assert err <= TOL[synth.F32]
+
+
 def check_conditioned(p, q, k, v, W, out, ref, kappa_max=16.0):
     """Parity with cancellation accounted for.  Tokens whose causal
     denominator is well conditioned (kappa <= kappa_max) meet the bf16 bar;

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void mix_summaries_f32(const float* __restrict
                                                          const float* __restrict__ W,
                                                          float* __restrict__ St, float* __restrict__ Zt,
                                                          const Geo g, const FastDiv div_IT,
-                                                         const FastDiv div_CT) {
+                                                         const FastDiv div_CT, int causal) {
     constexpr int REC = D * D + D;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, gq = lane >> 4;
@@ -195,7 +195,11 @@ __global__ __launch_bounds__(256) void mix_summaries_f32(const float* __restrict
         if (ok && colok) a = *reinterpret_cast<const f32x4*>(abase + (size_t)jj * REC);
         float bw[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bw[t] = ok ? wrow[t][jj] : 0.f;
+        for (int t = 0; t < 4; ++t) {
+            // the causal form mixes only the blocks before query block i
+            const bool keep = ok && !(causal && jj >= it * 64 + 16 * t + li);
+            bw[t] = keep ? wrow[t][jj] : 0.f;
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -337,6 +341,55 @@ inline void record(const Launch& L, int k) {
     if (L.events) (void)hipEventRecord(L.events[k], L.stream);
 }
 
+// =====================================================================
+// query_apply_causal (fp32), chunks contiguous in raster order (paperlayer.ai
+// summary, appendix B "Causal MHLA"): workgroup = (b, chunk i, head h) of D
+// threads walking the chunk's tokens in order.  Thread e keeps column e of
+// C = St_i< + W[i,i] sum_{m <= p} phi(k_m) v_m^T in registers and the mixed
+// normaliser zt_i< + W[i,i] sum phi(k_m) lives in LDS, so query p reads
+// num_e = phi(q_p) . C[:, e] and den = phi(q_p) . z + eps after its own token
+// is added.
+// =====================================================================
+template <int D>
+__global__ __launch_bounds__(D) void query_apply_causal_f32(const float* __restrict__ Q, const float* __restrict__ K,
+                                                            const float* __restrict__ V, const float* __restrict__ St,
+                                                            const float* __restrict__ Zt, const float* __restrict__ W,
+                                                            float* __restrict__ O, const Geo g) {
+    __shared__ float us[D], as[D], zs[D];
+    const int e = threadIdx.x;
+    const int blk = blockIdx.x;            // (b h) * M + i
+    const int bh = blk / g.M, i = blk - bh * g.M;
+    const int b = bh / g.H, h = bh - b * g.H;
+    const float wii = W[(size_t)i * g.M + i];
+    float col[D];
+    const float* st = St + (size_t)blk * (D * D) + (size_t)e * D;   // stored as [e][c]
+#pragma unroll
+    for (int c = 0; c < D; ++c) col[c] = st[c];
+    zs[e] = Zt[(size_t)blk * D + e];
+    const size_t base = (((size_t)b * g.N + block_origin(g, i)) * g.H + h) * D + e;
+    const size_t row = (size_t)g.H * D;
+    for (int p = 0; p < g.T; ++p) {
+        const size_t off = base + (size_t)p * row;   // contiguous chunk: raster index origin + p
+        const float ve = V[off];
+        us[e] = phi_exact(Q[off]);
+        as[e] = phi_exact(K[off]);
+        __syncthreads();
+        float num = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) {
+            col[c] += wii * as[c] * ve;
+            num += us[c] * col[c];
+        }
+        zs[e] += wii * as[e];
+        __syncthreads();
+        float den = g.eps;
+#pragma unroll 8
+        for (int c = 0; c < D; ++c) den += us[c] * zs[c];
+        O[off] = num / den;
+        __syncthreads();
+    }
+}
+
 template <int D>
 hipError_t run_d(const Launch& L) {
     const Geo& g = L.g;
@@ -365,9 +418,15 @@ hipError_t run_d(const Launch& L) {
     } else {
         const int CT = (D * D + D + 63) / 64, IT = (g.M + 63) / 64;
         const long tiles = (long)g.BH * CT * IT;
+        const bool causal = L.path == MHLA_PATH_CAUSAL;
         mix_summaries_f32<D><<<(unsigned)((tiles + 3) / 4), 256, 0, L.stream>>>(
-            sz, L.W, st, L.zt, g, make_fastdiv(IT), make_fastdiv(CT));
+            sz, L.W, st, L.zt, g, make_fastdiv(IT), make_fastdiv(CT), causal ? 1 : 0);
         record(L, 2);
+        if (causal) {
+            query_apply_causal_f32<D><<<nblk, D, 0, L.stream>>>(q, k, v, st, L.zt, L.W, o, g);
+            record(L, 3);
+            return hipGetLastError();
+        }
         switch (L.tune.apply_waves) {
             case 1: query_apply_f32<D, 1><<<nblk, 64, 0, L.stream>>>(q, st, L.zt, o, g); break;
             case 2: query_apply_f32<D, 2><<<nblk, 128, 0, L.stream>>>(q, st, L.zt, o, g); break;

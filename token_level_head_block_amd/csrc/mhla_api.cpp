@@ -75,7 +75,7 @@ bool chunks_contiguous(const Shape& s) {
 }
 
 bool causal_supported(const Shape& s) {
-    return s.dtype == MHLA_BF16 && chunks_contiguous(s);   // head_dim 32, 64 or 128
+    return chunks_contiguous(s);   // bf16 or fp32, head_dim 32, 64 or 128
 }
 
 struct Layout {
