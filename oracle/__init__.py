@@ -320,3 +320,75 @@ def bruteforce_causal(q, k, v, W, grid, block, eps=1e-6):
         for h in range(H):
             out[b, :, h, :] = bruteforce_causal_head(Q[b, :, h], K[b, :, h], V[b, :, h], W, bid, eps)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Gradients of the causal chunkwise form (numpy, float64)
+# ---------------------------------------------------------------------------
+
+def backward_causal(q, k, v, W, dout, grid, block, eps=1e-6):
+    """Gradients (dq, dk, dv, dW) of sum(dout * o) for the causal chunkwise
+    form (paperlayer.ai summary, appendix B "Causal MHLA"; chunks contiguous in
+    raster order), by the chain rule on
+        num_n = u_n^T (St_i< + W_ii P_n),  den_n = u_n . (zt_i< + W_ii zp_n) + eps,
+    P_n, zp_n the chunk's prefix sums of a_m v_m^T and a_m over m <= n,
+    St_i< = sum_{j<i} W_ij S_j.  With dnum = g / den, dden = -(g . o) / den:
+        dq_n = (C_n dnum_n + zeta_n dden_n) * phi'(q_n)
+        dSt_i< = sum_{n in i} u_n dnum_n^T,  dzt_i< likewise with dden
+        R_m = sum_{n in i, n >= m} u_n dnum_n^T,  r_m = sum_{n >= m} u_n dden_n
+        G_m = sum_{k > i} W_ki dSt_k< + W_ii R_m  (gz_m likewise)
+        dv_m = G_m^T a_m,  dk_m = (G_m v_m + gz_m) * phi'(k_m)
+        dW_ij = sum_bh <dSt_i<, S_j> + <dzt_i<, z_j>   (j < i)
+        dW_ii = sum_bh sum_m a_m^T R_m v_m + r_m . a_m
+    Inputs as for forward_causal; dq, dk, dv float64 like q, dW [M, M]."""
+    Q, K, V, G = (decode(x) for x in (q, k, v, dout))
+    B, N, H, d = Q.shape
+    Wd = np.asarray(W, dtype=np.float64)
+    M = Wd.shape[0]
+    bid = token_blocks(grid, block)
+    order = np.argsort(bid, kind="stable")
+    if not np.all(np.diff(order) == 1):
+        raise ValueError("causal form needs blocks that are contiguous in raster order")
+    T = N // M
+    lower = np.tril(Wd, -1)
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    dW = np.zeros((M, M))
+    dphi = lambda x: np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+    for b in range(B):
+        for h in range(H):
+            u = phi_np(Q[b, :, h]).reshape(M, T, d)
+            a = phi_np(K[b, :, h]).reshape(M, T, d)
+            vv = V[b, :, h].reshape(M, T, d)
+            g = G[b, :, h].reshape(M, T, d)
+            S = np.einsum("jtc,jte->jce", a, vv)
+            z = a.sum(axis=1)
+            St = np.einsum("ij,jce->ice", lower, S)                 # mixtures of earlier chunks
+            zt = lower @ z
+            wii = np.diag(Wd)
+            P = np.cumsum(a[:, :, :, None] * vv[:, :, None, :], axis=1)   # [M, T, d, d] prefix
+            zp = np.cumsum(a, axis=1)
+            C = St[:, None] + wii[:, None, None, None] * P
+            zeta = zt[:, None] + wii[:, None, None] * zp
+            num = np.einsum("itc,itce->ite", u, C)
+            den = np.einsum("itc,itc->it", u, zeta) + eps
+            o = num / den[..., None]
+            dnum = g / den[..., None]
+            dden = -np.einsum("ite,ite->it", g, o) / den
+            dq = (np.einsum("itce,ite->itc", C, dnum) + zeta * dden[..., None]) * dphi(Q[b, :, h]).reshape(M, T, d)
+            dSt = np.einsum("itc,ite->ice", u, dnum)
+            dzt = np.einsum("itc,it->ic", u, dden)
+            outer = u[:, :, :, None] * dnum[:, :, None, :]
+            R = np.cumsum(outer[:, ::-1], axis=1)[:, ::-1]            # suffix sums over n >= m
+            r = np.cumsum((u * dden[..., None])[:, ::-1], axis=1)[:, ::-1]
+            Gx = np.einsum("ki,kce->ice", lower, dSt)                # sum over later chunks k > i
+            gzx = lower.T @ dzt
+            Gm = Gx[:, None] + wii[:, None, None, None] * R
+            gz = gzx[:, None] + wii[:, None, None] * r
+            dv = np.einsum("itce,itc->ite", Gm, a)
+            dk = (np.einsum("itce,ite->itc", Gm, vv) + gz) * dphi(K[b, :, h]).reshape(M, T, d)
+            dQ[b, :, h] = dq.reshape(N, d)
+            dK[b, :, h] = dk.reshape(N, d)
+            dV[b, :, h] = dv.reshape(N, d)
+            dW += np.tril(np.einsum("ice,jce->ij", dSt, S) + dzt @ z.T, -1)
+            dW[np.arange(M), np.arange(M)] += np.einsum("itc,itce,ite->i", a, R, vv) + np.einsum("itc,itc->i", r, a)
+    return dQ, dK, dV, dW

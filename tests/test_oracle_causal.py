@@ -123,3 +123,85 @@ def test_conditioning_helper_matches_masked_row_sums(oracle_lib):
                 Wx = W.astype(np.float64)[bid][:, bid]
                 np.testing.assert_allclose(den[b, :, h], (Wx * S).sum(1) + p.eps, rtol=1e-12)
                 np.testing.assert_allclose(absden[b, :, h], (np.abs(Wx) * S).sum(1), rtol=1e-12)
+
+
+def causal_autograd(p, q, k, v, W, g, eps):
+    """Gradients of sum(g * o) by torch float64 autograd through the masked N x N form."""
+    import torch
+    bid = torch.from_numpy(oracle.token_blocks(p.grid, p.block))
+    Q, K, V, G = (torch.from_numpy(oracle.decode(x)).requires_grad_(x is not g) for x in (q, k, v, g))
+    Wt = torch.from_numpy(W.astype(np.float64)).requires_grad_(True)
+    N = bid.shape[0]
+    mask = torch.tril(torch.ones(N, N, dtype=torch.float64))
+    phi = lambda x: torch.where(x > 0, x + 1.0, torch.exp(torch.clamp(x, max=0.0)))
+    L = 0.0
+    for b in range(p.batch):
+        for h in range(p.heads):
+            A = Wt[bid][:, bid] * (phi(Q[b, :, h]) @ phi(K[b, :, h]).T) * mask
+            o = (A @ V[b, :, h]) / (A.sum(dim=1) + eps)[:, None]
+            L = L + (o * G[b, :, h]).sum()
+    L.backward()
+    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy(), Wt.grad.numpy()
+
+
+BWD_CASES = [
+    ("seq", 1, 2, 4, (1, 24), (1, 6), synth.F32),
+    ("rows-2d", 2, 1, 8, (6, 5), (2, 5), synth.BF16),
+    ("frames-3d", 1, 1, 4, (3, 2, 4), (1, 2, 4), synth.F32),
+    ("M1", 1, 2, 4, (1, 10), (1, 10), synth.F32),
+    ("T1", 1, 1, 4, (1, 7), (1, 1), synth.F32),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: c[0])
+def test_causal_gradients_match_autograd(oracle_lib, case):
+    p, (q, k, v, W) = make(case, seed=58)
+    rng = np.random.default_rng(59)
+    g = rng.standard_normal(q.shape).astype(np.float32)
+    g = synth.bf16_bits(g) if p.dtype == synth.BF16 else g
+    got = oracle.backward_causal(q, k, v, W, g, p.grid, p.block, eps=p.eps)
+    ref = causal_autograd(p, q, k, v, W, g, p.eps)
+    for name, a, b in zip(("dq", "dk", "dv", "dW"), got, ref):
+        assert rel_err(a, b) < 1e-10, name
+    # coefficients of later blocks get no gradient
+    assert np.all(got[3][np.triu_indices(W.shape[0], 1)] == 0.0)
+
+
+def test_causal_gradient_directional_difference(oracle_lib):
+    case = ("seq", 1, 1, 4, (1, 20), (1, 5), synth.F32)
+    p, (q, k, v, W) = make(case, seed=60)
+    g = np.random.default_rng(61).standard_normal(q.shape).astype(np.float32)
+    grads = oracle.backward_causal(q, k, v, W, g, p.grid, p.block, eps=p.eps)
+    X = [oracle.decode(x) for x in (q, k, v)] + [W.astype(np.float64)]
+    G = oracle.decode(g)
+    bid = oracle.token_blocks(p.grid, p.block)
+    N = bid.shape[0]
+
+    def loss(Qx, Kx, Vx, Wx):
+        A = Wx[bid][:, bid] * (oracle.phi_np(Qx[0, :, 0]) @ oracle.phi_np(Kx[0, :, 0]).T) * np.tril(np.ones((N, N)))
+        return float(np.sum((A @ Vx[0, :, 0]) / (A.sum(axis=1) + p.eps)[:, None] * G[0, :, 0]))
+
+    rng = np.random.default_rng(62)
+    for idx, gr in enumerate(grads):
+        delta = rng.standard_normal(X[idx].shape)
+        plus = [x.copy() for x in X]
+        minus = [x.copy() for x in X]
+        plus[idx] += 1e-5 * delta
+        minus[idx] -= 1e-5 * delta
+        fd = (loss(*plus) - loss(*minus)) / 2e-5
+        assert abs(fd - float(np.sum(gr * delta))) <= 1e-6 * max(abs(fd), 1.0), idx
+
+
+def test_causal_gradient_pins_catch_planted_mistakes(oracle_lib):
+    p, (q, k, v, W) = make(BWD_CASES[0], seed=63)
+    g = np.random.default_rng(64).standard_normal(q.shape).astype(np.float32)
+    ref = causal_autograd(p, q, k, v, W, g, p.eps)
+    run = lambda W_, g_, eps: oracle.backward_causal(q, k, v, W_, g_, p.grid, p.block, eps=eps)
+    planted = {
+        "transposed W": run(np.ascontiguousarray(W.T), g, p.eps),
+        "upstream gradient negated": run(W, -g, p.eps),
+        "eps dropped": run(W, g, 0.0),
+        "non-causal gradients": oracle.backward(q, k, v, W, g, p.grid, p.block, eps=p.eps),
+    }
+    for name, got in planted.items():
+        assert max(rel_err(a, b) for a, b in zip(got, ref)) > 1e-6, name
