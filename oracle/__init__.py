@@ -330,17 +330,21 @@ def backward_causal(q, k, v, W, dout, grid, block, eps=1e-6):
     """Gradients (dq, dk, dv, dW) of sum(dout * o) for the causal chunkwise
     form (paperlayer.ai summary, appendix B "Causal MHLA"; chunks contiguous in
     raster order), by the chain rule on
-        num_n = u_n^T (St_i< + W_ii P_n),  den_n = u_n . (zt_i< + W_ii zp_n) + eps,
-    P_n, zp_n the chunk's prefix sums of a_m v_m^T and a_m over m <= n,
-    St_i< = sum_{j<i} W_ij S_j.  With dnum = g / den, dden = -(g . o) / den:
-        dq_n = (C_n dnum_n + zeta_n dden_n) * phi'(q_n)
+        num_n = u_n^T St_i< + w sum_{m <= n in i} (u_n . a_m) v_m,
+        den_n = u_n . zt_i< + w sum_{m <= n in i} u_n . a_m + eps,
+    St_i< = sum_{j<i} W_ij S_j, w = W_ii.  With A[n, m] = u_n . a_m (m <= n,
+    else 0), dnum = g / den, dden = -(g . o) / den and
+    E[n, m] = dnum_n . v_m + dden_n (m <= n, else 0):
+        dq_n = (St_i< dnum_n + zt_i< dden_n + w sum_m E[n, m] a_m) * phi'(q_n)
         dSt_i< = sum_{n in i} u_n dnum_n^T,  dzt_i< likewise with dden
-        R_m = sum_{n in i, n >= m} u_n dnum_n^T,  r_m = sum_{n >= m} u_n dden_n
-        G_m = sum_{k > i} W_ki dSt_k< + W_ii R_m  (gz_m likewise)
-        dv_m = G_m^T a_m,  dk_m = (G_m v_m + gz_m) * phi'(k_m)
+        Gx_i = sum_{k > i} W_ki dSt_k<,  gzx_i likewise
+        dv_m = Gx_i^T a_m + w sum_n A[n, m] dnum_n
+        dk_m = (Gx_i v_m + gzx_i + w sum_n E[n, m] u_n) * phi'(k_m)
         dW_ij = sum_bh <dSt_i<, S_j> + <dzt_i<, z_j>   (j < i)
-        dW_ii = sum_bh sum_m a_m^T R_m v_m + r_m . a_m
-    Inputs as for forward_causal; dq, dk, dv float64 like q, dW [M, M]."""
+        dW_ii = sum_bh sum_{n, m} A[n, m] E[n, m]
+    The in-chunk sums are the prefix sums P_n = sum_{m <= n} a_m v_m^T of the
+    chunkwise recurrence written out token by token.  Inputs as for
+    forward_causal; dq, dk, dv float64 like q, dW [M, M]."""
     Q, K, V, G = (decode(x) for x in (q, k, v, dout))
     B, N, H, d = Q.shape
     Wd = np.asarray(W, dtype=np.float64)
@@ -351,6 +355,7 @@ def backward_causal(q, k, v, W, dout, grid, block, eps=1e-6):
         raise ValueError("causal form needs blocks that are contiguous in raster order")
     T = N // M
     lower = np.tril(Wd, -1)
+    mask = np.tril(np.ones((T, T)))
     dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
     dW = np.zeros((M, M))
     dphi = lambda x: np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
@@ -360,35 +365,36 @@ def backward_causal(q, k, v, W, dout, grid, block, eps=1e-6):
             a = phi_np(K[b, :, h]).reshape(M, T, d)
             vv = V[b, :, h].reshape(M, T, d)
             g = G[b, :, h].reshape(M, T, d)
+            dphq = dphi(Q[b, :, h]).reshape(M, T, d)
+            dphk = dphi(K[b, :, h]).reshape(M, T, d)
             S = np.einsum("jtc,jte->jce", a, vv)
             z = a.sum(axis=1)
             St = np.einsum("ij,jce->ice", lower, S)                 # mixtures of earlier chunks
             zt = lower @ z
-            wii = np.diag(Wd)
-            P = np.cumsum(a[:, :, :, None] * vv[:, :, None, :], axis=1)   # [M, T, d, d] prefix
-            zp = np.cumsum(a, axis=1)
-            C = St[:, None] + wii[:, None, None, None] * P
-            zeta = zt[:, None] + wii[:, None, None] * zp
-            num = np.einsum("itc,itce->ite", u, C)
-            den = np.einsum("itc,itc->it", u, zeta) + eps
-            o = num / den[..., None]
-            dnum = g / den[..., None]
-            dden = -np.einsum("ite,ite->it", g, o) / den
-            dq = (np.einsum("itce,ite->itc", C, dnum) + zeta * dden[..., None]) * dphi(Q[b, :, h]).reshape(M, T, d)
-            dSt = np.einsum("itc,ite->ice", u, dnum)
-            dzt = np.einsum("itc,it->ic", u, dden)
-            outer = u[:, :, :, None] * dnum[:, :, None, :]
-            R = np.cumsum(outer[:, ::-1], axis=1)[:, ::-1]            # suffix sums over n >= m
-            r = np.cumsum((u * dden[..., None])[:, ::-1], axis=1)[:, ::-1]
+            dSt = np.empty_like(St)
+            dzt = np.empty_like(zt)
+            Am, Em, dnum = [], [], []
+            for i in range(M):                                       # query side, one chunk at a time
+                w = Wd[i, i]
+                A = (u[i] @ a[i].T) * mask
+                num = u[i] @ St[i] + w * (A @ vv[i])
+                den = u[i] @ zt[i] + w * A.sum(axis=1) + eps
+                o = num / den[:, None]
+                dn = g[i] / den[:, None]
+                dd = -np.sum(g[i] * o, axis=1) / den
+                E = (dn @ vv[i].T + dd[:, None]) * mask
+                dQ[b, i * T:(i + 1) * T, h] = (dn @ St[i].T + dd[:, None] * zt[i] + w * (E @ a[i])) * dphq[i]
+                dSt[i] = u[i].T @ dn
+                dzt[i] = u[i].T @ dd
+                Am.append(A)
+                Em.append(E)
+                dnum.append(dn)
             Gx = np.einsum("ki,kce->ice", lower, dSt)                # sum over later chunks k > i
             gzx = lower.T @ dzt
-            Gm = Gx[:, None] + wii[:, None, None, None] * R
-            gz = gzx[:, None] + wii[:, None, None] * r
-            dv = np.einsum("itce,itc->ite", Gm, a)
-            dk = (np.einsum("itce,ite->itc", Gm, vv) + gz) * dphi(K[b, :, h]).reshape(M, T, d)
-            dQ[b, :, h] = dq.reshape(N, d)
-            dK[b, :, h] = dk.reshape(N, d)
-            dV[b, :, h] = dv.reshape(N, d)
+            for i in range(M):                                       # key/value side
+                w = Wd[i, i]
+                dV[b, i * T:(i + 1) * T, h] = a[i] @ Gx[i] + w * (Am[i].T @ dnum[i])
+                dK[b, i * T:(i + 1) * T, h] = (vv[i] @ Gx[i].T + gzx[i] + w * (Em[i].T @ u[i])) * dphk[i]
+                dW[i, i] += np.sum(Am[i] * Em[i])
             dW += np.tril(np.einsum("ice,jce->ij", dSt, S) + dzt @ z.T, -1)
-            dW[np.arange(M), np.arange(M)] += np.einsum("itc,itce,ite->i", a, R, vv) + np.einsum("itc,itc->i", r, a)
     return dQ, dK, dV, dW
