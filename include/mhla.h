@@ -218,6 +218,44 @@ mhla_status mhla_backward(const void* q, const void* k, const void* v, const flo
                           float* dW, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
                           hipStream_t stream);
 
+/* ---------------------------------------------------------------- causal backward
+ *
+ * Gradients through the causal chunkwise form (MHLA_PATH_CAUSAL; paperlayer.ai
+ * summary, appendix B "Causal MHLA"), for chunks contiguous in raster order.
+ * Token n of chunk i sees C_n = St_i< + w P_n and zeta_n = zt_i< + w zp_n,
+ * with St_i< = sum_{j<i} W[i,j] S_j, w = W[i,i] and P_n, zp_n the chunk's
+ * prefix sums of a v^T and a over m <= n.  With den, dnum, dden as above:
+ *
+ *   dq_n     = (C_n dnum + zeta_n dden) * phi'(q_n)
+ *   dSt_i<   = sum_{n in i} u dnum^T,  dzt_i< = sum_{n in i} u dden
+ *   R_m, r_m = suffix sums over n >= m in the chunk of u dnum^T and u dden
+ *   G_m      = sum_{k>i} W[k,i] dSt_k< + w R_m  (g_m likewise with dzt, r)
+ *   dv_m     = G_m^T a,  dk_m = (G_m v_m + g_m) * phi'(k_m)
+ *   dW[i,j]  = sum over (b, h) of <dSt_i<, S_j> + <dzt_i<, z_j>   (j < i)
+ *   dW[i,i]  = sum over (b, h) and m in i of a . (R_m v_m + r_m), dW[i,j] = 0 (j > i)
+ *
+ * Arguments, layouts, ownership and aliasing rules as for mhla_backward; the
+ * coefficients W[i,j] with j > i are never read.  bf16 or fp32, head_dim 32,
+ * 64 or 128, fp32 arithmetic throughout.  MHLA_ERR_UNSUPPORTED when the
+ * chunks are not contiguous in raster order (blocks spanning whole rows of
+ * the grid, or any sequence). */
+
+/* Bytes of device workspace mhla_causal_backward needs (0 for an invalid,
+ * empty or unsupported problem): the four fp32 record arrays and dW partial
+ * sums of the general backward path, then at 256-byte boundaries each token's
+ * dnum (B*N*H*d fp32), each token's dden (B*N*H fp32) and the in-chunk terms
+ * of dW's diagonal (B*H*M fp32). */
+size_t mhla_causal_backward_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
+
+/* The causal backward pass, enqueued on `stream`; ws and stage_events as for
+ * mhla_backward, except that the fourth event is recorded before the
+ * key/value-side kernel and the dW reduction follows that kernel (it supplies
+ * the diagonal). */
+mhla_status mhla_causal_backward(const void* q, const void* k, const void* v, const float* W, const void* dout,
+                                 const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
+                                 float* dW, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
+                                 hipStream_t stream);
+
 /* ---------------------------------------------------------------- layer
  *
  * The layer around the core, after the plug-and-play module of the

@@ -54,18 +54,21 @@ class Run:
         torch.cuda.synchronize()
         return out
 
-    def backward(self, dout_host, stream=None, ws=True):
-        """Gradients through mhla_backward: (dq, dk, dv) device tensors like q and dW [M, M] fp32."""
+    def backward(self, dout_host, stream=None, ws=True, causal=False):
+        """Gradients through mhla_backward (mhla_causal_backward if causal):
+        (dq, dk, dv) device tensors like q and dW [M, M] fp32."""
         p = self.p
         dout = to_dev(dout_host, p.dtype)
         dq, dk, dv = (torch.empty_like(self.q) for _ in range(3))
         M = p.n_blocks
         dW = torch.empty(M, M, dtype=torch.float32, device="cuda")
-        wsb = mh.mhla_backward_workspace_bytes(self.g, self.b)
+        wsize = mh.mhla_causal_backward_workspace_bytes if causal else mh.mhla_backward_workspace_bytes
+        call = mh.mhla_causal_backward if causal else mh.mhla_backward
+        wsb = wsize(self.g, self.b)
         wst = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if ws else None
-        say(f"  [gpu] mhla_backward {p.name} B{p.batch} H{p.heads} d{p.head_dim} grid{p.grid} block{p.block}")
-        st = mh.mhla_backward(self.q, self.k, self.v, self.W, dout, self.g, self.b, dq, dk, dv, dW,
-                              wst, wsb if ws else 0, None, stream)
+        say(f"  [gpu] {call.__name__} {p.name} B{p.batch} H{p.heads} d{p.head_dim} grid{p.grid} block{p.block}")
+        st = call(self.q, self.k, self.v, self.W, dout, self.g, self.b, dq, dk, dv, dW,
+                  wst, wsb if ws else 0, None, stream)
         assert st == mh.MHLA_OK, mh.mhla_status_string(st)
         torch.cuda.synchronize()
         return dq, dk, dv, dW

@@ -194,6 +194,32 @@ def test_causal_path_validation(L):
                                mh.MHLA_PATH_CAUSAL)[0] == mh.MHLA_OK
 
 
+
+def test_causal_backward_workspace_and_validation(L):
+    seq = mh.make_grid(1, 6, 64, mh.MHLA_BF16, (1, 65536))
+    chunk = mh.make_block((1, 256))
+    need = mh.mhla_causal_backward_workspace_bytes(seq, chunk)
+    rec = 6 * 256 * (64 * 64 + 64) * 4
+    toks = 65536 * 6
+    assert need >= 4 * rec + toks * 64 * 4 + toks * 4 + 6 * 256 * 4
+    # 2D blocks are not contiguous runs of raster indices: no workspace, and the call says so
+    g, b = cfg2()
+    assert mh.mhla_causal_backward_workspace_bytes(g, b) == 0
+
+    def bwd(g_, b_, ws_bytes, q=BIG, dW=9 * BIG):
+        return L.mhla_causal_backward(q, 2 * BIG, 3 * BIG, 4 * BIG, 5 * BIG, ctypes.byref(g_), ctypes.byref(b_),
+                                      6 * BIG, 7 * BIG, 8 * BIG, dW, 10 * BIG, ws_bytes, None, None)
+
+    assert bwd(g, b, 1 << 30) == mh.MHLA_ERR_UNSUPPORTED
+    assert bwd(seq, chunk, need - 16) == mh.MHLA_ERR_INVALID_ARG
+    assert bwd(seq, chunk, need, dW=None) == mh.MHLA_ERR_INVALID_ARG
+    assert bwd(seq, chunk, need, q=BIG + 8) == mh.MHLA_ERR_MISALIGNED
+    assert bwd(seq, mh.make_block((1, 255)), need) == mh.MHLA_ERR_INVALID_ARG
+    # fp32 and d = 128 too
+    f32 = mh.make_grid(2, 1, 128, mh.MHLA_F32, (1, 400))
+    assert mh.mhla_causal_backward_workspace_bytes(f32, mh.make_block((1, 100))) > 0
+
+
 def test_layer_workspace_and_validation(L):
     g, b = cfg2()
     C, R = 6 * 64, 65536

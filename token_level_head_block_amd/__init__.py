@@ -86,6 +86,10 @@ def lib() -> ctypes.CDLL:
         L.mhla_backward_workspace_bytes.restype = ctypes.c_size_t
         L.mhla_backward.argtypes = [vp, vp, vp, vp, vp, G, Bk, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
         L.mhla_backward.restype = ctypes.c_int
+        L.mhla_causal_backward_workspace_bytes.argtypes = [G, Bk]
+        L.mhla_causal_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.mhla_causal_backward.argtypes = [vp, vp, vp, vp, vp, G, Bk, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
+        L.mhla_causal_backward.restype = ctypes.c_int
         L.mhla_workspace_bytes.argtypes = [G, Bk]
         L.mhla_workspace_bytes.restype = ctypes.c_size_t
         L.mhla_forward.argtypes = [vp, vp, vp, vp, G, Bk, vp, vp]
@@ -248,6 +252,20 @@ def mhla_backward(q, k, v, W, dout, grid: mhla_grid, block: mhla_block, dq, dk, 
     return lib().mhla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dout), ctypes.byref(grid),
                                ctypes.byref(block), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), _ptr(ws),
                                int(ws_bytes), _events(stage_events, 5), _stream(stream))
+
+
+def mhla_causal_backward_workspace_bytes(grid: mhla_grid, block: mhla_block) -> int:
+    return int(lib().mhla_causal_backward_workspace_bytes(ctypes.byref(grid), ctypes.byref(block)))
+
+
+def mhla_causal_backward(q, k, v, W, dout, grid: mhla_grid, block: mhla_block, dq, dk, dv, dW, ws=None,
+                         ws_bytes: int = 0, stage_events=None, stream=None) -> int:
+    """Gradients through the causal chunkwise form; arguments as mhla_backward."""
+    _check_tensors(q, k, v, W, dout, grid, block)
+    _check_tensors(dq, dk, dv, dW, None, grid, block)
+    return lib().mhla_causal_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dout), ctypes.byref(grid),
+                                      ctypes.byref(block), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), _ptr(ws),
+                                      int(ws_bytes), _events(stage_events, 5), _stream(stream))
 
 
 # ---------------------------------------------------------------- convenience

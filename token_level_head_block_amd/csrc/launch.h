@@ -102,7 +102,8 @@ struct LayerLaunch {
 hipError_t run_layer_bf16(const LayerLaunch& L);
 
 // Backward pass for the problems the bf16 MFMA kernels do not take (fp32
-// inputs, or head_dim 128): fp32 records [S | z] of L = d*d + d values.
+// inputs, or head_dim 128) and for the causal form: fp32 records [S | z] of
+// L = d*d + d values.
 struct GenericBwd {
     Geo g;
     int bf16;                 // inputs and gradients in bf16 (else fp32)
@@ -121,6 +122,10 @@ struct GenericBwd {
     float* ds;                // [BH][M][L] gradients of the summaries
     float* part;              // [nsplit][M][M] dW partial sums
     int nsplit;
+    int causal;               // causal chunkwise form (chunks contiguous in raster order)
+    float* dnum;              // causal: [B][N][H][d] per-token g / den
+    float* dden;              // causal: [B][N][H] per-token -(g . o) / den
+    float* diag;              // causal: [BH][M] in-chunk terms of dW[i][i]
     const hipEvent_t* events; // 5 events or nullptr
     hipStream_t stream;
 };

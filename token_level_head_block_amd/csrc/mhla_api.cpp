@@ -252,11 +252,11 @@ BwdLayout bwd_layout(const Shape& s) {
 
 // The general backward path (fp32 inputs, or head_dim 128): fp32 records.
 struct GenLayout {
-    size_t s, st, dst, ds, part, total;
+    size_t s, st, dst, ds, part, dnum, dden, diag, total;
     int nsplit;
 };
 
-GenLayout gen_layout(const Shape& s) {
+GenLayout gen_layout(const Shape& s, bool causal = false) {
     GenLayout L;
     const size_t rec = (size_t)(s.B * s.H * s.M) * (size_t)(s.D * s.D + s.D) * 4;
     L.s = 0;
@@ -273,16 +273,27 @@ GenLayout gen_layout(const Shape& s) {
     if (ns > chunks) ns = chunks > 0 ? chunks : 1;
     L.nsplit = (int)ns;
     L.total = L.part + align_up((size_t)ns * (size_t)(s.M * s.M) * 4);
+    L.dnum = L.dden = L.diag = L.total;
+    if (causal) {
+        // per-token dnum and dden from the query side, per-chunk diagonal terms of dW
+        const size_t toks = (size_t)s.B * (size_t)s.N * (size_t)s.H;
+        L.dnum = L.total;
+        L.dden = L.dnum + align_up(toks * (size_t)s.D * 4);
+        L.diag = L.dden + align_up(toks * 4);
+        L.total = L.diag + align_up((size_t)(s.B * s.H * s.M) * 4);
+    }
     return L;
 }
 
 mhla_status backward_impl(const void* q, const void* k, const void* v, const float* W, const void* dout,
                           const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
-                          float* dW, void* ws, size_t ws_bytes, const hipEvent_t* events, hipStream_t stream) {
+                          float* dW, void* ws, size_t ws_bytes, const hipEvent_t* events, hipStream_t stream,
+                          bool causal) {
     Shape s;
     mhla_status st = check(grid, block, &s);
     if (st != MHLA_OK) return st;
-    const bool fast = bwd_supported(s);
+    if (causal && !causal_supported(s)) return MHLA_ERR_UNSUPPORTED;
+    const bool fast = !causal && bwd_supported(s);
     if (!dW) return MHLA_ERR_INVALID_ARG;
     if (!aligned16(dW)) return MHLA_ERR_MISALIGNED;
     const size_t wbytes = (size_t)(s.M * s.M) * 4;
@@ -310,7 +321,7 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
             if (overlaps(outs[a], outsz[a], outs[b], outsz[b])) return MHLA_ERR_INVALID_ARG;
     }
     const BwdLayout lay = bwd_layout(s);
-    const GenLayout glay = gen_layout(s);
+    const GenLayout glay = gen_layout(s, causal);
     const size_t need = fast ? lay.total : glay.total;
     bool owned = false;
     if (ws) {
@@ -341,6 +352,10 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
         G.ds = reinterpret_cast<float*>(base + glay.ds);
         G.part = reinterpret_cast<float*>(base + glay.part);
         G.nsplit = glay.nsplit;
+        G.causal = causal ? 1 : 0;
+        G.dnum = reinterpret_cast<float*>(base + glay.dnum);
+        G.dden = reinterpret_cast<float*>(base + glay.dden);
+        G.diag = reinterpret_cast<float*>(base + glay.diag);
         G.events = events;
         G.stream = stream;
         const hipError_t err = mhla::run_bwd_generic(G);
@@ -520,7 +535,22 @@ mhla_status mhla_backward(const void* q, const void* k, const void* v, const flo
                           const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
                           float* dW, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
                           hipStream_t stream) {
-    return backward_impl(q, k, v, W, dout, grid, block, dq, dk, dv, dW, ws, ws_bytes, stage_events, stream);
+    return backward_impl(q, k, v, W, dout, grid, block, dq, dk, dv, dW, ws, ws_bytes, stage_events, stream,
+                         false);
+}
+
+size_t mhla_causal_backward_workspace_bytes(const mhla_grid* grid, const mhla_block* block) {
+    Shape s;
+    if (check(grid, block, &s) != MHLA_OK || s.B == 0 || s.H == 0 || !causal_supported(s)) return 0;
+    return gen_layout(s, true).total;
+}
+
+mhla_status mhla_causal_backward(const void* q, const void* k, const void* v, const float* W, const void* dout,
+                                 const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
+                                 float* dW, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
+                                 hipStream_t stream) {
+    return backward_impl(q, k, v, W, dout, grid, block, dq, dk, dv, dW, ws, ws_bytes, stage_events, stream,
+                         true);
 }
 
 size_t mhla_layer_workspace_bytes(const mhla_grid* grid, const mhla_block* block) {
