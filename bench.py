@@ -152,15 +152,29 @@ class HipEvents:
         self.made = []
 
 
-def backward_bytes(p):
-    """Algorithmic HBM bytes of each backward stage (compulsory reads + writes, bf16 records)."""
+def backward_bytes(p, general=False, causal=False):
+    """Algorithmic HBM bytes of each backward stage (compulsory reads + writes).
+    The MFMA path keeps the summaries and their gradients as bf16 records; the
+    general path (and the causal one) as fp32 records of d*d + d values, and the
+    causal path also passes each token's dnum (d fp32) and dden (fp32) from the
+    query side to the key/value side."""
     B, N, H, d, M = p.batch, p.n_tokens, p.heads, p.head_dim, p.n_blocks
     tensor = B * N * H * d * p.elem_bytes
     P = B * H
+    w = M * M * 4
+    if general or causal:
+        rec = P * M * (d * d + d) * 4
+        tok = B * N * H * (d + 1) * 4 if causal else 0
+        return {
+            "recompute (summary + mix)": 2 * tensor + rec + rec + w + rec,
+            "query side": (4 if causal else 2) * tensor + rec + tensor + rec + tok,
+            "mix_transposed + dW partials": rec + w + rec + 2 * rec,
+            ("key/value side + dW reduce" if causal else "key/value side"):
+                (3 if causal else 2) * tensor + rec + 2 * tensor + tok + (P * M * 4 + w if causal else 0),
+        }
     rec = P * M * (d * d + d) * 2      # summaries, or their gradients, as bf16 records
     st = P * M * d * d * 2
     zt = P * M * d * 4
-    w = M * M * 4
     return {
         "recompute (block_kv_summary + mix)": 2 * tensor + rec + rec + w + st + zt,
         "bwd_query": 2 * tensor + st + zt + tensor + rec,
@@ -196,15 +210,19 @@ def bench_backward(args, p, torch, mh, synth):
     gr = mh.make_grid(p.batch, p.heads, p.head_dim, mh.MHLA_BF16 if p.dtype == synth.BF16 else mh.MHLA_F32,
                       p.grid, p.eps)
     bl = mh.make_block(p.block)
-    ws_bytes = mh.mhla_backward_workspace_bytes(gr, bl)
+    causal = args.path == "causal"
+    general = causal or not (p.dtype == synth.BF16 and p.head_dim <= 64)
+    wsize = mh.mhla_causal_backward_workspace_bytes if causal else mh.mhla_backward_workspace_bytes
+    call = mh.mhla_causal_backward if causal else mh.mhla_backward
+    ws_bytes = wsize(gr, bl)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(i, events=None):
         q, k, v, W, g, dq, dk, dv, dW = data[i % sets]
-        st = mh.mhla_backward(q, k, v, W, g, gr, bl, dq, dk, dv, dW, ws, ws_bytes, events, stream)
+        st = call(q, k, v, W, g, gr, bl, dq, dk, dv, dW, ws, ws_bytes, events, stream)
         if st != mh.MHLA_OK:
-            raise mh.MhlaError(st, "mhla_backward")
+            raise mh.MhlaError(st, call.__name__)
 
     for i in range(args.warmup):
         step(i)
@@ -226,7 +244,7 @@ def bench_backward(args, p, torch, mh, synth):
     torch.cuda.synchronize()
     stage_ms = np.array([[hev.elapsed_ms(r[j], r[j + 1]) for j in range(4)] for r in evs]).mean(axis=0)
     hev.destroy_all()
-    kb = backward_bytes(p)
+    kb = backward_bytes(p, general, causal)
     stages = {}
     for j, (name, nbytes) in enumerate(kb.items()):
         gbps = nbytes / (stage_ms[j] * 1e-3) / 1e9
@@ -240,20 +258,28 @@ def bench_backward(args, p, torch, mh, synth):
         q, k, v, W, g = host0
         ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
         t = time.perf_counter()
-        _, used = oracle.backward(q, k, v, W, g, p.grid, p.block, eps=p.eps, threads=ncpu, return_threads=True)
+        if causal:
+            oracle.backward_causal(q, k, v, W, g, p.grid, p.block, eps=p.eps)
+            used = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+            what = ("float64 causal chunkwise gradients in numpy (matrix products on the BLAS threads, "
+                    "the rest on one thread)")
+        else:
+            _, used = oracle.backward(q, k, v, W, g, p.grid, p.block, eps=p.eps, threads=ncpu,
+                                      return_threads=True)
+            what = "float64 blockwise gradients, one thread per pair"
         dt_cpu = time.perf_counter() - t
         cpu = {"value": round(p.batch * p.n_tokens / dt_cpu, 1), "unit": "tokens/s", "cores": used,
                "kind": "oracle", "seconds": round(dt_cpu, 3),
-               "sample": f"the full workload ({p.batch * p.heads} (b,h) pairs), float64 blockwise gradients"}
+               "sample": f"the full workload ({p.batch * p.heads} (b,h) pairs), {what}"}
     line = {
-        "metric": "MHLA bwd tokens/s (dq, dk, dv, dW) + achieved HBM GB/s", "value":
+        "metric": f"MHLA {'causal ' if causal else ''}bwd tokens/s (dq, dk, dv, dW) + achieved HBM GB/s", "value":
             round(p.batch * p.n_tokens / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if p.dtype == synth.BF16 else "f32", "data": "synthetic",
         "config": {"workload": f"{p.name}: B={p.batch} H={p.heads} d={p.head_dim} grid={list(p.grid)} "
                                f"blocks={list(p.block)} N={p.n_tokens} M={p.n_blocks}",
-                   "pass": "backward", "kernels": "mfma" if p.dtype == synth.BF16 and p.head_dim <= 64 else "general",
+                   "pass": "causal backward" if causal else "backward", "kernels": "general" if general else "mfma",
                    "input_sets": sets, "parallelism": "none (1 GPU)"},
         "path_hbm_gbps": round(U / (ms_step * 1e-3) / 1e9, 1),
         "path_hbm_frac": round(U / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "path_alg_bytes": U,

@@ -168,6 +168,7 @@ __global__ __launch_bounds__(256) void g_query(const T* __restrict__ Q, const T*
                 const int e = lane + 64 * k;
                 float num = 0.f;
                 if (e < D) {
+#pragma unroll 8
                     for (int c = 0; c < D; ++c) num += ub[w][c] * s[c * DP + e];
                     ge[k] = ld1(G + off + e);
                 } else {
@@ -189,6 +190,7 @@ __global__ __launch_bounds__(256) void g_query(const T* __restrict__ Q, const T*
                 const int c = lane + 64 * k;
                 if (c >= D) continue;
                 float t = zt[c] * dden;
+#pragma unroll 8
                 for (int e = 0; e < D; ++e) t += s[c * DP + e] * dn[w][e];
                 st1(dQ + off + c, t * dphi(xq[k]));
             }
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(256) void g_dw_reduce(const float* __restrict__ par
 // chunk, as in the non-causal case) and each token's dnum and dden for the
 // key side.
 template <int D, typename T>
-__global__ __launch_bounds__(256) void g_query_causal(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g_query_causal(const T* __restrict__ Q, const T* __restrict__ K,
                                                       const T* __restrict__ V, const T* __restrict__ G,
                                                       const float* __restrict__ strec, const float* __restrict__ W,
                                                       T* __restrict__ dQ, float* __restrict__ dstrec,
@@ -407,6 +409,7 @@ __global__ __launch_bounds__(256) void g_query_causal(const T* __restrict__ Q, c
                 ge[k] = 0.f;
                 if (e >= D) continue;
                 float num = 0.f, corr = 0.f;
+#pragma unroll 8
                 for (int c = 0; c < D; ++c) num += ub[w][c] * s[c * DP + e];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) corr += ua[x] * vb[x][e];
@@ -452,6 +455,7 @@ __global__ __launch_bounds__(256) void g_query_causal(const T* __restrict__ Q, c
                         corr += ab[x][c] * vd[x];
                     }
                 float t = zc * ddv + wii * corr;
+#pragma unroll 8
                 for (int e = 0; e < D; ++e) t += s[c * DP + e] * dn[w][e];
                 st1(dQ + off + c, t * dphi(xq[k]));
             }
@@ -567,6 +571,7 @@ __global__ __launch_bounds__(256) void g_kv_causal(const T* __restrict__ Q, cons
                 const int x = lane + 64 * k;
                 if (x >= D) continue;
                 float dvx = 0.f, dvr = 0.f, dkx = gz[x], tr = rz[x];
+#pragma unroll 8
                 for (int y = 0; y < D; ++y) {
                     dvx += gx[y * DP + x] * ab[w][y];
                     dvr += rr[y * DP + x] * ab[w][y];
