@@ -233,21 +233,24 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
         __syncthreads();
     }
 
-    // ---- epilogue: lane (li, gq) holds features c .. c+3 of token n
+    // ---- epilogue: lane (li, gq) holds features c .. c+3 of token n.  The
+    // finished values go to LDS as [token][feature] (the staging buffers are
+    // free after the last barrier), then every lane stores 16 bytes so that
+    // eight lanes write one token's 128 features as whole 128-byte lines.
+    constexpr int ESTR = TC + 8;   // 272-byte rows: the 16 tokens x 4 feature groups of a store hit distinct banks
+    static_assert(TN * ESTR <= 2 * TC * STR, "epilogue tile must fit the staging buffers");
+    uint16_t* et = la[0];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int c = c0 + 64 * wc + 16 * i + 4 * gq;
-        if (c >= a.Nc) continue;   // Nc is a multiple of 4
-        const f32x4 bias = a.bias ? *reinterpret_cast<const f32x4*>(a.bias + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int cl = 64 * wc + 16 * i + 4 * gq, c = c0 + cl;
+        const int cb = c < a.Nc ? c : a.Nc - 4;   // Nc is a multiple of 4; columns past it are never stored
+        const f32x4 bias = a.bias ? *reinterpret_cast<const f32x4*>(a.bias + cb) : f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 cs = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (LN) cs = *reinterpret_cast<const f32x4*>(a.colsum + c);
-        const int which = c / a.split, cc = c - which * a.split;
-        uint16_t* d = which == 0 ? a.dst[0] : (which == 1 ? a.dst[1] : a.dst[2]);
+        if constexpr (LN) cs = *reinterpret_cast<const f32x4*>(a.colsum + cb);
         const bool pre = c < a.phi_cols;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int n = n0 + 64 * wn + 16 * j + li;
-            if (n >= a.R) continue;
+            const int nl = 64 * wn + 16 * j + li, n = min(n0 + nl, a.R - 1);
             float mu = 0.f, rs = 1.f;
             if constexpr (LN) {
                 mu = a.mean[n];
@@ -261,8 +264,19 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
                 x += bias[v];
                 o[v] = pre ? relu_phi_preimage(x, a.phi_eps) : x;
             }
-            *reinterpret_cast<u32x2*>(d + (size_t)n * a.split + cc) = u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+            *reinterpret_cast<u32x2*>(&et[nl * ESTR + cl]) = u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
         }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < TN * TC / 8 / 256; ++s) {
+        const int u = tid + 256 * s;
+        const int nl = u >> 4, cl = (u & 15) * 8;   // 16 lanes of 8 features per token
+        const int n = n0 + nl, c = c0 + cl;
+        if (n >= a.R || c >= a.Nc) continue;          // Nc is a multiple of 8
+        const int which = c / a.split, cc = c - which * a.split;   // split is a multiple of 8
+        uint16_t* d = which == 0 ? a.dst[0] : (which == 1 ? a.dst[1] : a.dst[2]);
+        *reinterpret_cast<u32x4*>(d + (size_t)n * a.split + cc) = *reinterpret_cast<const u32x4*>(&et[nl * ESTR + cl]);
     }
 }
 
