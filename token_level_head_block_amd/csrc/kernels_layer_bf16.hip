@@ -121,15 +121,17 @@ struct GemmArgs {
 };
 
 // Workgroup: 4 waves, tile of 128 output features x 128 tokens, each wave
-// 64 x 64 (4 x 4 MFMA tiles).  K in chunks of 64 through two LDS buffers;
-// the next chunk's global loads are in flight while the current one is
-// multiplied.  Feature tiles of one token tile sit 8 workgroup ids apart, so
+// 64 x 64 (4 x 4 MFMA tiles).  K in chunks of 64 through one LDS buffer per
+// operand; the next chunk's global loads are in flight while the current one
+// is multiplied.  36 KB of LDS and 128 registers let four workgroups share a
+// compute unit, which hides more of the load latency than a second buffer.  Feature tiles of one token tile sit 8 workgroup ids apart, so
 // they run on the same XCD and share its L2 copy of the token rows.
-template <bool LN>
-__global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
+template <bool LN, bool WHOLE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WHOLE ? 4 : 3))) void layer_gemm_bf16(const GemmArgs a) {
     constexpr int TC = 128, TN = 128, KC = 64, STR = KC + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t la[2][TC * STR];
-    __shared__ __attribute__((aligned(16))) uint16_t lb[2][TN * STR];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[TC * STR + TN * STR];   // 36 KB: four workgroups per CU
+    uint16_t* const la = lds;
+    uint16_t* const lb = lds + TC * STR;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, gq = lane >> 4;
@@ -155,8 +157,10 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
     const int nk = (a.K + KC - 1) / KC;
 
     // ---- staging: unit u = (row, 8 k) of a 128 x 64 chunk, 4 per thread and operand,
-    // through buffer descriptors: the lane's byte offset is fixed, the chunk's
-    // advance is a scalar offset.  Only a partial last chunk is masked, when
+    // through buffer descriptors.  WHOLE (Nc and R multiples of 128, K of 64:
+    // every tile is whole): one lane offset, advanced by scalar offsets.
+    // Otherwise the row and the k of every load are clamped so that each
+    // address stays inside its tensor, and the values past K are zeroed when
     // the registers go to LDS after the MFMAs of the current chunk, so the
     // loads of the next chunk stay in flight.
     // Byte ranges and offsets are below 2^32 (tensors hold fewer than 2^31
@@ -165,25 +169,30 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
         (void*)a.Wt, 0, (int)((uint32_t)a.Nc * (uint32_t)a.K * 2u), 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.X, 0, (int)((uint32_t)a.R * (uint32_t)a.K * 2u), 0x00020000);
-    int offw[4], offx[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int u = tid + 256 * s;
-        const int row = u >> 3;
-        offw[s] = (int)(((uint32_t)min(c0 + row, a.Nc - 1) * (uint32_t)a.K + (uint32_t)(u & 7) * 8u) * 2u);
-        offx[s] = (int)(((uint32_t)min(n0 + row, a.R - 1) * (uint32_t)a.K + (uint32_t)(u & 7) * 8u) * 2u);
-    }
+    const int r8 = tid >> 3, k8 = (tid & 7) * 8;
+    const int offw = (int)(((uint32_t)(c0 + r8) * (uint32_t)a.K + (uint32_t)k8) * 2u);
+    const int offx = (int)(((uint32_t)(n0 + r8) * (uint32_t)a.K + (uint32_t)k8) * 2u);
     u32x4 ra[4], rb[4];
     auto gload = [&](int kc) {
-        const int so = __builtin_amdgcn_readfirstlane(kc * KC * 2);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            ra[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, offw[s], so, 0));
-            rb[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, offx[s], so, 0));
+            if constexpr (WHOLE) {
+                const int so = __builtin_amdgcn_readfirstlane((kc * KC + s * 32 * a.K) * 2);
+                ra[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, offw, so, 0));
+                rb[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, offx, so, 0));
+            } else {
+                const uint32_t kk = (uint32_t)min(kc * KC + k8, a.K - 8);   // K is a multiple of 8
+                const uint32_t cw = (uint32_t)min(c0 + r8 + 32 * s, a.Nc - 1);
+                const uint32_t cx = (uint32_t)min(n0 + r8 + 32 * s, a.R - 1);
+                ra[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rw, (int)((cw * (uint32_t)a.K + kk) * 2u), 0, 0));
+                rb[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rx, (int)((cx * (uint32_t)a.K + kk) * 2u), 0, 0));
+            }
         }
     };
-    auto lstore = [&](int buf, int kc) {
-        const bool partial = (kc + 1) * KC > a.K;
+    auto lstore = [&](int kc) {
+        const bool partial = !WHOLE && (kc + 1) * KC > a.K;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int u = tid + 256 * s;
@@ -194,8 +203,8 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
                 x = u32x4{x[0] & m, x[1] & m, x[2] & m, x[3] & m};
                 y = u32x4{y[0] & m, y[1] & m, y[2] & m, y[3] & m};
             }
-            *reinterpret_cast<u32x4*>(&la[buf][off]) = x;
-            *reinterpret_cast<u32x4*>(&lb[buf][off]) = y;
+            *reinterpret_cast<u32x4*>(&la[off]) = x;
+            *reinterpret_cast<u32x4*>(&lb[off]) = y;
         }
     };
 
@@ -206,31 +215,35 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int buf) {
+    auto compute = [&]() {
 #pragma unroll
         for (int ks = 0; ks < KC / 32; ++ks) {
             u32x4 fa[4], fb[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                fa[i] = *reinterpret_cast<const u32x4*>(&la[buf][(64 * wc + 16 * i + li) * STR + ks * 32 + gq * 8]);
+                fa[i] = *reinterpret_cast<const u32x4*>(&la[(64 * wc + 16 * i + li) * STR + ks * 32 + gq * 8]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                fb[j] = *reinterpret_cast<const u32x4*>(&lb[buf][(64 * wn + 16 * j + li) * STR + ks * 32 + gq * 8]);
+                fb[j] = *reinterpret_cast<const u32x4*>(&lb[(64 * wn + 16 * j + li) * STR + ks * 32 + gq * 8]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
         }
     };
+    // One LDS buffer: the next chunk waits in registers while the current one
+    // is multiplied, then replaces it between two barriers.
     gload(0);
-    lstore(0, 0);
+    lstore(0);
     __syncthreads();
     for (int kc = 0; kc < nk; ++kc) {
-        const int buf = kc & 1;
         if (kc + 1 < nk) gload(kc + 1);
-        compute(buf);
-        if (kc + 1 < nk) lstore(buf ^ 1, kc + 1);
+        compute();
         __syncthreads();
+        if (kc + 1 < nk) {
+            lstore(kc + 1);
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: lane (li, gq) holds features c .. c+3 of token n.  The
@@ -238,8 +251,8 @@ __global__ __launch_bounds__(256) void layer_gemm_bf16(const GemmArgs a) {
     // free after the last barrier), then every lane stores 16 bytes so that
     // eight lanes write one token's 128 features as whole 128-byte lines.
     constexpr int ESTR = TC + 8;   // 272-byte rows: the 16 tokens x 4 feature groups of a store hit distinct banks
-    static_assert(TN * ESTR <= 2 * TC * STR, "epilogue tile must fit the staging buffers");
-    uint16_t* et = la[0];
+    static_assert(TN * ESTR <= TC * STR + TN * STR, "epilogue tile must fit the staging buffers");
+    uint16_t* et = lds;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int cl = 64 * wc + 16 * i + 4 * gq, c = c0 + cl;
@@ -427,7 +440,10 @@ hipError_t run_layer_bf16(const LayerLaunch& L) {
     a.phi_cols = (L.relu_phi && !L.qn_w) ? 2 * C : 0;
     a.phi_eps = L.phi_eps;
     const int ntt = (R + 127) / 128, nct = (3 * C + 127) / 128;
-    layer_gemm_bf16<true><<<ntt * nct, 256, 0, L.stream>>>(a);
+    if (a.Nc % 128 == 0 && R % 128 == 0 && C % 64 == 0)
+        layer_gemm_bf16<true, true><<<ntt * nct, 256, 0, L.stream>>>(a);
+    else
+        layer_gemm_bf16<true, false><<<ntt * nct, 256, 0, L.stream>>>(a);
     if (L.qn_w)
         rms_qk_bf16<<<(2 * R + 3) / 4, 256, 0, L.stream>>>(L.q, L.k, L.qn_w, L.kn_w, R, C, L.rms_eps, L.relu_phi,
                                                            L.phi_eps);
@@ -454,7 +470,10 @@ hipError_t run_layer_bf16(const LayerLaunch& L) {
     b.R = R; b.K = C; b.Nc = C; b.split = C;
     b.phi_cols = 0;
     b.phi_eps = 0.f;
-    layer_gemm_bf16<false><<<ntt * ((C + 127) / 128), 256, 0, L.stream>>>(b);
+    if (C % 128 == 0 && R % 128 == 0)
+        layer_gemm_bf16<false, true><<<ntt * ((C + 127) / 128), 256, 0, L.stream>>>(b);
+    else
+        layer_gemm_bf16<false, false><<<ntt * ((C + 127) / 128), 256, 0, L.stream>>>(b);
     rec(4);
     return hipGetLastError();
 }
