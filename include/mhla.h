@@ -256,6 +256,53 @@ mhla_status mhla_causal_backward(const void* q, const void* k, const void* v, co
                                  float* dW, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
                                  hipStream_t stream);
 
+/* ---------------------------------------------------------------- causal streaming
+ *
+ * Stateful execution of the causal chunkwise form (the method keeps O(N) cost
+ * and supports streaming or stateful execution: paperlayer.ai summary, key
+ * points; appendix B "Causal MHLA").  A sequence arrives as calls of whole
+ * chunks; a state of fp32 chunk summaries carries what later chunks need.
+ * A call's grid and block describe its new tokens (chunks contiguous in
+ * raster order, as for MHLA_PATH_CAUSAL); its chunks get the global indices
+ * i = n_past .. n_past + M - 1.  For each new chunk i, with u = phi(q_n):
+ *
+ *   state[i] = [S_i | z_i] = [sum_{m in i} phi(k_m) v_m^T | sum_{m in i} phi(k_m)]
+ *   o_n = u^T (St_i< + W[i,i] P_n) / (u . (zt_i< + W[i,i] zp_n) + eps)
+ *   St_i< = sum_{j<i} W[i,j] S_j  (zt_i< likewise, over the state's slots j < i)
+ *
+ * P_n, zp_n the chunk's sums of phi(k_m) v_m^T and phi(k_m) over m <= n.  A
+ * sequence streamed in any split into calls gives the outputs of one
+ * MHLA_PATH_CAUSAL call on the whole sequence (chunk lengths may differ
+ * between calls; the math is per chunk).
+ *
+ * state: fp32 [B*H][max_chunks][d*d + d] (pair b*H + h; per slot S as
+ * [c][e], key channel c slowest, then z), device memory owned by the
+ * caller; slots 0 .. n_past-1 must hold the summaries written by earlier
+ * calls (or by the caller), slots n_past .. n_past + M - 1 are overwritten.
+ * W: fp32 [w_dim][w_dim] row-major; only W[i][j] with j <= i for the new
+ * rows i is read.  q, k, v, out: [B, N_new, H, d] in the grid's dtype.  fp32
+ * arithmetic.  Errors: MHLA_ERR_UNSUPPORTED for chunks that are not
+ * contiguous; MHLA_ERR_INVALID_ARG for n_past < 0, n_past + M beyond
+ * max_chunks or w_dim, null pointers, or overlaps between out, state, the
+ * inputs and the workspace; MHLA_ERR_MISALIGNED for pointers not 16-byte
+ * aligned.  An empty problem (B or H zero) does nothing. */
+
+/* Bytes of the state for max_chunks chunks (0 for an invalid problem). */
+size_t mhla_causal_state_bytes(const mhla_grid* grid, const mhla_block* block, int32_t max_chunks);
+
+/* Bytes of workspace a call needs: the new chunks' mixtures, B*H*M records of
+ * d*d + d fp32 (0 for an invalid, empty or unsupported problem). */
+size_t mhla_causal_stream_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
+
+/* One call of the stream, enqueued on `stream`: summaries of the new chunks
+ * into the state, their mixtures over earlier chunks, their outputs.  ws: at
+ * least mhla_causal_stream_workspace_bytes (16-byte aligned), or NULL with
+ * ws_bytes 0 to allocate it on the stream.  Calls on one state must be
+ * ordered (same stream, or synchronised). */
+mhla_status mhla_causal_stream(const void* q, const void* k, const void* v, const float* W, int32_t w_dim,
+                               const mhla_grid* grid, const mhla_block* block, int32_t n_past, float* state,
+                               int32_t max_chunks, void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- layer
  *
  * The layer around the core, after the plug-and-play module of the

@@ -220,6 +220,38 @@ def test_causal_backward_workspace_and_validation(L):
     assert mh.mhla_causal_backward_workspace_bytes(f32, mh.make_block((1, 100))) > 0
 
 
+
+def test_causal_stream_state_and_validation(L):
+    new = mh.make_grid(2, 3, 64, mh.MHLA_BF16, (1, 256))
+    chunk = mh.make_block((1, 64))
+    L_ = 64 * 64 + 64
+    assert mh.mhla_causal_state_bytes(new, chunk, 10) == 2 * 3 * 10 * L_ * 4
+    assert mh.mhla_causal_state_bytes(new, chunk, 0) == 0
+    assert mh.mhla_causal_stream_workspace_bytes(new, chunk) == 2 * 3 * 4 * L_ * 4
+    g2d, b2d = cfg2()
+    assert mh.mhla_causal_stream_workspace_bytes(g2d, b2d) == 0          # 2D tiles are not chunks
+    sb = mh.mhla_causal_state_bytes(new, chunk, 10)
+
+    def call(g=new, b=chunk, n_past=0, max_chunks=10, w_dim=10, q=BIG, state=6 * BIG, out=7 * BIG,
+             ws=8 * BIG, ws_bytes=1 << 30):
+        return L.mhla_causal_stream(q, 2 * BIG, 3 * BIG, 4 * BIG, w_dim, ctypes.byref(g), ctypes.byref(b), n_past,
+                                    state, max_chunks, out, ws, ws_bytes, None)
+
+    assert call(g=g2d, b=b2d) == mh.MHLA_ERR_UNSUPPORTED
+    assert call(n_past=-1) == mh.MHLA_ERR_INVALID_ARG
+    assert call(n_past=7) == mh.MHLA_ERR_INVALID_ARG                       # 7 + 4 chunks > max_chunks 10
+    assert call(n_past=6, max_chunks=12, w_dim=9) == mh.MHLA_ERR_INVALID_ARG   # row 9 is past w_dim
+    assert call(state=None) == mh.MHLA_ERR_INVALID_ARG
+    assert call(out=6 * BIG + sb - 16) == mh.MHLA_ERR_INVALID_ARG          # out overlaps the state
+    assert call(out=BIG + 64) == mh.MHLA_ERR_INVALID_ARG                   # out overlaps q
+    assert call(ws_bytes=16) == mh.MHLA_ERR_INVALID_ARG
+    assert call(q=BIG + 4) == mh.MHLA_ERR_MISALIGNED
+    assert call(state=6 * BIG + 8) == mh.MHLA_ERR_MISALIGNED
+    assert call(b=mh.make_block((1, 60))) == mh.MHLA_ERR_INVALID_ARG       # 256 is not a multiple of 60
+    empty = mh.make_grid(0, 3, 64, mh.MHLA_BF16, (1, 256))
+    assert call(g=empty, q=None, state=None, out=None) == mh.MHLA_OK        # nothing to do
+
+
 def test_layer_workspace_and_validation(L):
     g, b = cfg2()
     C, R = 6 * 64, 65536

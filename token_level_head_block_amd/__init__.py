@@ -90,6 +90,13 @@ def lib() -> ctypes.CDLL:
         L.mhla_causal_backward_workspace_bytes.restype = ctypes.c_size_t
         L.mhla_causal_backward.argtypes = [vp, vp, vp, vp, vp, G, Bk, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
         L.mhla_causal_backward.restype = ctypes.c_int
+        L.mhla_causal_state_bytes.argtypes = [G, Bk, ctypes.c_int32]
+        L.mhla_causal_state_bytes.restype = ctypes.c_size_t
+        L.mhla_causal_stream_workspace_bytes.argtypes = [G, Bk]
+        L.mhla_causal_stream_workspace_bytes.restype = ctypes.c_size_t
+        L.mhla_causal_stream.argtypes = [vp, vp, vp, vp, ctypes.c_int32, G, Bk, ctypes.c_int32, vp, ctypes.c_int32,
+                                         vp, vp, ctypes.c_size_t, vp]
+        L.mhla_causal_stream.restype = ctypes.c_int
         L.mhla_workspace_bytes.argtypes = [G, Bk]
         L.mhla_workspace_bytes.restype = ctypes.c_size_t
         L.mhla_forward.argtypes = [vp, vp, vp, vp, G, Bk, vp, vp]
@@ -266,6 +273,32 @@ def mhla_causal_backward(q, k, v, W, dout, grid: mhla_grid, block: mhla_block, d
     return lib().mhla_causal_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dout), ctypes.byref(grid),
                                       ctypes.byref(block), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), _ptr(ws),
                                       int(ws_bytes), _events(stage_events, 5), _stream(stream))
+
+
+def mhla_causal_state_bytes(grid: mhla_grid, block: mhla_block, max_chunks: int) -> int:
+    return int(lib().mhla_causal_state_bytes(ctypes.byref(grid), ctypes.byref(block), int(max_chunks)))
+
+
+def mhla_causal_stream_workspace_bytes(grid: mhla_grid, block: mhla_block) -> int:
+    return int(lib().mhla_causal_stream_workspace_bytes(ctypes.byref(grid), ctypes.byref(block)))
+
+
+def mhla_causal_stream(q, k, v, W, grid: mhla_grid, block: mhla_block, n_past: int, state, max_chunks: int, out,
+                       ws=None, ws_bytes: int = 0, stream=None) -> int:
+    """One call of a causal stream: q, k, v, out [B, N_new, H, d] (the new
+    chunks), W fp32 [w_dim, w_dim] (w_dim from W's shape), state fp32 with
+    mhla_causal_state_bytes(grid, block, max_chunks) bytes."""
+    for t in (q, k, v, out):
+        if t is None or not t.is_contiguous():
+            raise ValueError("q, k, v and out must be contiguous device tensors")
+    if W.dim() != 2 or W.shape[0] != W.shape[1] or not W.is_contiguous():
+        raise ValueError("W must be a contiguous square fp32 matrix")
+    if not state.is_contiguous() or state.numel() * state.element_size() < mhla_causal_state_bytes(grid, block,
+                                                                                                  max_chunks):
+        raise ValueError("state is smaller than mhla_causal_state_bytes")
+    return lib().mhla_causal_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(W), int(W.shape[0]), ctypes.byref(grid),
+                                    ctypes.byref(block), int(n_past), _ptr(state), int(max_chunks), _ptr(out),
+                                    _ptr(ws), int(ws_bytes), _stream(stream))
 
 
 # ---------------------------------------------------------------- convenience

@@ -131,6 +131,25 @@ struct GenericBwd {
 };
 hipError_t run_bwd_generic(const GenericBwd& B);
 
+// Stateful causal execution: the new chunks of a sequence (Geo describes
+// them), fp32 state records of every chunk [B*H][max_chunks][d*d + d].
+struct StreamLaunch {
+    Geo g;
+    int bf16;                 // q, k, v, out in bf16 (else fp32)
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* W;           // [w_dim][w_dim]
+    int w_dim;
+    int n_past;               // chunks already in the state
+    float* state;
+    int max_chunks;
+    float* mixed;             // [B*H][M][d*d + d] workspace
+    void* out;
+    hipStream_t stream;
+};
+hipError_t run_causal_stream(const StreamLaunch& S);
+
 // p[0 .. n) = 0 by a kernel (safe inside a captured graph).
 hipError_t zero_f32(float* p, int n, hipStream_t stream);
 

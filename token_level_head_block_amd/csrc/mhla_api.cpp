@@ -521,6 +521,70 @@ mhla_status layer_impl(const void* x, const float* W, const mhla_grid* grid, con
     return err == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
 }
 
+// ---- stateful causal execution
+size_t stream_state_bytes(const Shape& s, int64_t max_chunks) {
+    return (size_t)(s.B * s.H) * (size_t)max_chunks * (size_t)(s.D * s.D + s.D) * 4;
+}
+
+size_t stream_ws_bytes(const Shape& s) { return (size_t)(s.B * s.H * s.M) * (size_t)(s.D * s.D + s.D) * 4; }
+
+mhla_status stream_impl(const void* q, const void* k, const void* v, const float* W, int32_t w_dim,
+                        const mhla_grid* grid, const mhla_block* block, int32_t n_past, float* state,
+                        int32_t max_chunks, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    Shape s;
+    mhla_status st = check(grid, block, &s);
+    if (st != MHLA_OK) return st;
+    if (!chunks_contiguous(s)) return MHLA_ERR_UNSUPPORTED;
+    if (n_past < 0 || max_chunks <= 0 || w_dim <= 0) return MHLA_ERR_INVALID_ARG;
+    if ((int64_t)n_past + s.M > (int64_t)max_chunks || (int64_t)n_past + s.M > (int64_t)w_dim)
+        return MHLA_ERR_INVALID_ARG;
+    if (s.B == 0 || s.H == 0) return MHLA_OK;   // no pair: nothing to read or write
+    const void* ins[4] = {q, k, v, W};
+    for (const void* x : ins)
+        if (!x) return MHLA_ERR_INVALID_ARG;
+    if (!state || !out) return MHLA_ERR_INVALID_ARG;
+    for (const void* x : ins)
+        if (!aligned16(x)) return MHLA_ERR_MISALIGNED;
+    if (!aligned16(state) || !aligned16(out)) return MHLA_ERR_MISALIGNED;
+    const size_t tbytes = (size_t)(s.B * s.N * s.H * s.D) * s.esz;
+    const size_t wbytes = (size_t)w_dim * (size_t)w_dim * 4;
+    const size_t sbytes = stream_state_bytes(s, max_chunks);
+    const size_t insz[4] = {tbytes, tbytes, tbytes, wbytes};
+    for (int b = 0; b < 4; ++b)
+        if (overlaps(out, tbytes, ins[b], insz[b]) || overlaps(state, sbytes, ins[b], insz[b]))
+            return MHLA_ERR_INVALID_ARG;
+    if (overlaps(out, tbytes, state, sbytes)) return MHLA_ERR_INVALID_ARG;
+    const size_t need = stream_ws_bytes(s);
+    bool owned = false;
+    if (ws) {
+        if (ws_bytes < need) return MHLA_ERR_INVALID_ARG;
+        if (!aligned16(ws)) return MHLA_ERR_MISALIGNED;
+        for (int b = 0; b < 4; ++b)
+            if (overlaps(ws, need, ins[b], insz[b])) return MHLA_ERR_INVALID_ARG;
+        if (overlaps(ws, need, out, tbytes) || overlaps(ws, need, state, sbytes)) return MHLA_ERR_INVALID_ARG;
+    } else {
+        if (ws_bytes != 0) return MHLA_ERR_INVALID_ARG;
+        if (hipMallocAsync(&ws, need, stream) != hipSuccess || !ws) {
+            (void)hipGetLastError();
+            return MHLA_ERR_ALLOC;
+        }
+        owned = true;
+    }
+    mhla::StreamLaunch S;
+    S.g = make_geo(s, grid->eps);
+    S.bf16 = s.dtype == MHLA_BF16;
+    S.q = q; S.k = k; S.v = v; S.W = W; S.w_dim = w_dim;
+    S.n_past = n_past;
+    S.state = state;
+    S.max_chunks = max_chunks;
+    S.mixed = static_cast<float*>(ws);
+    S.out = out;
+    S.stream = stream;
+    const hipError_t err = mhla::run_causal_stream(S);
+    if (owned) (void)hipFreeAsync(ws, stream);
+    return err == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -648,6 +712,24 @@ mhla_status mhla_forward_ex(const void* q, const void* k, const void* v, const f
                             hipStream_t stream) {
     return forward_impl(q, k, v, W, grid, block, out, ws, ws_bytes, true, path, stage_events,
                         stream);
+}
+
+size_t mhla_causal_state_bytes(const mhla_grid* grid, const mhla_block* block, int32_t max_chunks) {
+    Shape s;
+    if (check(grid, block, &s) != MHLA_OK || max_chunks <= 0) return 0;
+    return stream_state_bytes(s, max_chunks);
+}
+
+size_t mhla_causal_stream_workspace_bytes(const mhla_grid* grid, const mhla_block* block) {
+    Shape s;
+    if (check(grid, block, &s) != MHLA_OK || s.B == 0 || s.H == 0 || !chunks_contiguous(s)) return 0;
+    return stream_ws_bytes(s);
+}
+
+mhla_status mhla_causal_stream(const void* q, const void* k, const void* v, const float* W, int32_t w_dim,
+                               const mhla_grid* grid, const mhla_block* block, int32_t n_past, float* state,
+                               int32_t max_chunks, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return stream_impl(q, k, v, W, w_dim, grid, block, n_past, state, max_chunks, out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"
