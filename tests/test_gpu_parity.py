@@ -125,6 +125,39 @@ def test_mixing_kernels(case, monkeypatch):
         assert e_out <= TOL[p.dtype] and e_st <= 1e-2 and e_zt <= 1e-2
 
 
+PAIR_CASES = [
+    ("pair-d32-full-B2", 2, 4, 32, (32, 32), (8, 8), BF, 0.5),   # whole 32-token groups, two batch items
+    ("pair-d32-row8", 1, 6, 32, (24, 16), (3, 8), BF, 1.0),      # rows of 8 tokens, T = 24
+    ("pair-d32-ragged", 1, 2, 32, (12, 20), (3, 5), BF, 1.0),    # rows of 5 tokens
+    ("pair-d32-odd-H", 1, 3, 32, (16, 16), (4, 4), BF, 1.0),     # odd head count: one head per wave
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=lambda c: c[0])
+def test_d32_head_pairs(case, monkeypatch):
+    """head_dim 32 with an even head count: the summary kernel reads head
+    pairs as 64-channel heads and keeps the diagonal blocks.  Summaries and
+    outputs of the paired and the one-head-per-wave launch, each against the
+    oracle; the two launches agree bit for bit (same products, same order)."""
+    p = small_problem(case)
+    q, k, v, W = synth.make_inputs(p, seed=26)
+    ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)
+    rS, rz, _, _ = oracle.summaries(k, v, W, p.grid, p.block)
+    run = Run(p, q, k, v, W)
+    got = {}
+    for flag in ("1", "0"):
+        monkeypatch.setenv("MHLA_PAIR_HEADS", flag)
+        out = to_host64(run.forward())
+        S, z, _, _ = run.workspace()
+        e_out, e_s, e_z = rel_err(out, ref), rel_err(S, rS), rel_err(z, rz)
+        say(f"  {p.name} pair={flag}: out {e_out:.2e} S {e_s:.2e} z {e_z:.2e}")
+        assert np.isfinite(out).all()
+        assert e_out <= TOL[p.dtype] and e_s <= 1e-2 and e_z <= 1e-2
+        got[flag] = (out, S, z)
+    for a, b in zip(got["1"], got["0"]):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("cfg_index", [1, 2, 3, 4])
 def test_full_workloads_sampled_pairs(cfg_index):
     """Full-size workload, default launch configuration; every output of the

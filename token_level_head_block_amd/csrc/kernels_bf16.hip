@@ -39,13 +39,19 @@ namespace {
 // ROW8: block rows hold a multiple of 8 tokens, so the 8 tokens of a lane
 // group are consecutive in raster order (one address computation).
 // FULL: ROW8 and T a multiple of 32, so no token slot is ever padding.
+// PAIR (D = 64 only): the problem has head_dim 32 and an even head count; a
+// wave reads the 64 channels of heads 2p and 2p + 1 exactly as one head of
+// 64 (whole 128-byte rows per lane group) and forms the 64 x 64 product,
+// whose two diagonal 32 x 32 blocks are the two heads' S (the off-diagonal
+// blocks are discarded); the records written are those of head_dim 32.
 // =====================================================================
-template <int D, int PF, bool ROW8, bool FULL, bool NTL>
+template <int D, int PF, bool ROW8, bool FULL, bool NTL, bool PAIR = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 && D <= 64 && FULL ? 3 : 2)))
 void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                            uint16_t* __restrict__ SZ, const Geo g, const float* __restrict__ W,
                            uint16_t* __restrict__ Wb, const WConv wc) {
     static_assert(!FULL || ROW8, "FULL implies ROW8");
+    static_assert(!PAIR || D == 64, "paired heads run the 64-channel layout");
     constexpr int CPL = (D == 32) ? 2 : 4;   // channels per lane
     constexpr int CW = CPL / 2;              // 32-bit words per lane per token
     constexpr int NQ = (D == 128) ? 4 : 1;
@@ -170,6 +176,33 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
         uint16_t* dst = stile + (CPL * li + c2) * TS + 4 * CPL * gq;
         *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
         if constexpr (CPL == 4) *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+    }
+    if constexpr (PAIR) {
+        // Head 2h + s owns rows e and columns c in [32 s, 32 s + 32) of the
+        // tile: each record row is 64 bytes, four lanes x 16 bytes.
+        constexpr int DH = 32, RECH = DH * DH + DH;
+        const int Hr = 2 * g.H;
+#pragma unroll
+        for (int k = 0; k < TW / 16; ++k) {
+            const int er = k * 16 + (lane >> 2), chunk = lane & 3;
+            const int s = er >> 5;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(stile + er * TS + DH * s + chunk * 8);
+            uint16_t* rech = SZ + ((size_t)(b * Hr + 2 * h + s) * g.M + j) * RECH;
+            *reinterpret_cast<u32x4*>(rech + (er - DH * s) * DH + chunk * 8) = x;
+        }
+        if (li == 0) {
+            // Lane group gq holds z for channels 16 gq .. 16 gq + 15 of the pair.
+            uint32_t wv[8];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int rp = 0; rp < 2; ++rp) wv[v * 2 + rp] = pack_bf16(accz[2 * rp][v], accz[2 * rp + 1][v]);
+            const int s = gq >> 1;
+            uint16_t* dst = SZ + ((size_t)(b * Hr + 2 * h + s) * g.M + j) * RECH + DH * DH + 16 * (gq & 1);
+            *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+        }
+        return;
     }
     uint16_t* rec = SZ + (size_t)blk * (D * D + D);
     constexpr int LPR = TW / 8;           // lanes per tile row (16 bytes each)
@@ -633,22 +666,40 @@ inline Geo with_head_groups(Geo g, int per_head, int max_waves = 8) {
     return g;
 }
 
-template <int D, int PF, bool ROW8, bool FULL>
+template <int D, int PF, bool ROW8, bool FULL, bool PAIR = false>
 void launch_summary(const Launch& L, const uint16_t* k, const uint16_t* v, uint16_t* sz,
                     const WConv& wc) {
     constexpr int NQ = D == 128 ? 4 : 1;
-    const Geo g = with_head_groups(L.g, NQ);
+    Geo gp = L.g;
+    if (PAIR) {   // head pairs of 32 channels read as heads of 64
+        gp.H /= 2;
+        gp.D = 64;
+        gp.BH = gp.B * gp.H;
+    }
+    const Geo g = with_head_groups(gp, NQ);
     const int nsum = g.B * g.M * g.HG, threads = 64 * NQ * g.G;
     WConv w = wc;
     w.first_wg = nsum;
     const int nchunks = wc.nchunks * (wc.wbt ? 2 : 1);
     const int nconv = (nchunks + threads * 4 - 1) / (threads * 4);   // up to 4 chunks per thread
     if (L.tune.nt_loads)
-        block_kv_summary_bf16<D, PF, ROW8, FULL, true><<<nsum + nconv, threads, 0, L.stream>>>(
+        block_kv_summary_bf16<D, PF, ROW8, FULL, true, PAIR><<<nsum + nconv, threads, 0, L.stream>>>(
             k, v, sz, g, L.W, static_cast<uint16_t*>(L.wb), w);
     else
-        block_kv_summary_bf16<D, PF, ROW8, FULL, false><<<nsum + nconv, threads, 0, L.stream>>>(
+        block_kv_summary_bf16<D, PF, ROW8, FULL, false, PAIR><<<nsum + nconv, threads, 0, L.stream>>>(
             k, v, sz, g, L.W, static_cast<uint16_t*>(L.wb), w);
+}
+
+// head_dim 32 with an even head count runs as head pairs of 64 channels.
+template <int D, int PF, bool ROW8, bool FULL>
+void launch_summary_any(const Launch& L, const uint16_t* k, const uint16_t* v, uint16_t* sz, const WConv& wc) {
+    if constexpr (D == 32) {
+        if (L.g.H % 2 == 0 && L.tune.pair_heads) {
+            launch_summary<64, PF, ROW8, FULL, true>(L, k, v, sz, wc);
+            return;
+        }
+    }
+    launch_summary<D, PF, ROW8, FULL>(L, k, v, sz, wc);
 }
 
 template <int D, int NWA, int PF, int MAXW>
@@ -661,6 +712,11 @@ void launch_apply_pf(const Launch& L, const uint16_t* q, const uint16_t* st, uin
 
 template <int D, int NWA>
 void launch_apply(const Launch& L, const uint16_t* q, const uint16_t* st, uint16_t* o) {
+    if (L.tune.apply_maxw == 4) {
+        if (L.tune.apply_pf == 1) launch_apply_pf<D, NWA, 1, 4>(L, q, st, o);
+        else launch_apply_pf<D, NWA, 2, 4>(L, q, st, o);
+        return;
+    }
     switch (L.tune.apply_pf) {
         case 1: launch_apply_pf<D, NWA, 1, 8>(L, q, st, o); break;
         case 2: launch_apply_pf<D, NWA, 2, 8>(L, q, st, o); break;
@@ -693,13 +749,13 @@ hipError_t run_d(const Launch& L) {
     record(L, 0);
     const bool full = row8 && (g.T % 32) == 0;
     if (L.tune.summary_pf == 1) {
-        if (full) launch_summary<D, 1, true, true>(L, k, v, sz, wc);
-        else if (row8) launch_summary<D, 1, true, false>(L, k, v, sz, wc);
-        else launch_summary<D, 1, false, false>(L, k, v, sz, wc);
+        if (full) launch_summary_any<D, 1, true, true>(L, k, v, sz, wc);
+        else if (row8) launch_summary_any<D, 1, true, false>(L, k, v, sz, wc);
+        else launch_summary_any<D, 1, false, false>(L, k, v, sz, wc);
     } else {
-        if (full) launch_summary<D, 2, true, true>(L, k, v, sz, wc);
-        else if (row8) launch_summary<D, 2, true, false>(L, k, v, sz, wc);
-        else launch_summary<D, 2, false, false>(L, k, v, sz, wc);
+        if (full) launch_summary_any<D, 2, true, true>(L, k, v, sz, wc);
+        else if (row8) launch_summary_any<D, 2, true, false>(L, k, v, sz, wc);
+        else launch_summary_any<D, 2, false, false>(L, k, v, sz, wc);
     }
     record(L, 1);
     if (fused) {

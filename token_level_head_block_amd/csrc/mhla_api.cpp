@@ -126,10 +126,16 @@ mhla::Tuning choose_tuning(const Shape& s) {
     if (aw == 1 || aw == 2 || aw == 4) t.apply_waves = aw;
     if (sp == 1 || sp == 2) t.summary_pf = sp;
     if (ap == 1 || ap == 2 || ap == 4) t.apply_pf = ap;
-    // Non-temporal loads: faster for the summary kernel's k, v stream and
-    // slower for the apply kernel's q stream (measured on MI355X).
+    t.pair_heads = env_int("MHLA_PAIR_HEADS", 1) != 0;
+    t.apply_maxw = 8;
+    const int am = env_int("MHLA_APPLY_MAXW", 0);
+    if (am == 4 || am == 8) t.apply_maxw = am;
+    // Non-temporal loads: faster for the summary kernel's k, v stream.  On
+    // the apply kernel's q stream they cost the apply about 1 us at d <= 64
+    // but the following summary launch runs 2-5 us faster, so a repeated
+    // forward gains; at d = 128 the apply loses 6 us (measured on MI355X).
     t.nt_loads = env_int("MHLA_NT_LOADS", 1) != 0;
-    t.nt_apply = env_int("MHLA_NT_APPLY", 0) != 0;
+    t.nt_apply = env_int("MHLA_NT_APPLY", s.D <= 64 ? 1 : 0) != 0;
     t.mix_resident = env_int("MHLA_MIX_RESIDENT", 1) != 0;
     t.num_cus = 256;
     return t;
