@@ -245,8 +245,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void m
 // unit are loaded from memory while the current unit is multiplied and
 // stored, with two LDS buffers for the packed operands.  Lane roles, operand
 // packing and output mapping are those of mix_summaries.
+// NT bit 0: summary records loaded with the non-temporal hint; bit 1: mixed
+// summaries stored with it (they are read once, by the apply kernel).
 // =====================================================================
-template <int D>
+template <int D, int NT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void mix_resident_bf16(
     const uint16_t* __restrict__ SZ, const uint16_t* __restrict__ Wb, uint16_t* __restrict__ St,
     float* __restrict__ Zt, const Geo g, const MixGeo mg) {
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int jj = (jg >> 2) * 32 + (jg & 3) * 8 + s;
-            const u32x2 t = *reinterpret_cast<const u32x2*>(base + (size_t)(jj < M ? jj : M - 1) * REC + colc);
+            const u32x2 t = ld<(NT & 1) != 0>(reinterpret_cast<const u32x2*>(base + (size_t)(jj < M ? jj : M - 1) * REC + colc));
             const uint32_t m = (ok && jj < M) ? 0xffffffffu : 0u;
             raw[s] = u32x2{t.x & m, t.y & m};
         }
@@ -369,7 +371,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
                 const int rl = 8 * k + (lane >> 3), chunk = lane & 7;
                 const int i = it * 64 + 32 * th + rl;
                 const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rl * OROW + chunk * 8);
-                if (i < M) *reinterpret_cast<u32x4*>(St + ((size_t)bh * M + i) * (D * D) + cp0 + chunk * 8) = x;
+                u32x4* dst = reinterpret_cast<u32x4*>(St + ((size_t)bh * M + i) * (D * D) + cp0 + chunk * 8);
+                if (i < M) {
+                    if constexpr ((NT & 2) != 0) __builtin_nontemporal_store(x, dst);
+                    else *dst = x;
+                }
             }
         } else if (cp0 + 16 * gq < REC) {
 #pragma unroll
@@ -773,8 +779,12 @@ hipError_t run_d(const Launch& L) {
             // NK <= 8 follows from M <= 256.
             const int units = g.BH * mg.CTG;
             const int grid = units < L.tune.num_cus ? units : L.tune.num_cus;
-            mix_resident_bf16<D><<<grid, 512, 0, L.stream>>>(
-                sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg);
+            switch (L.tune.nt_mix) {
+                case 1: mix_resident_bf16<D, 1><<<grid, 512, 0, L.stream>>>(sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg); break;
+                case 2: mix_resident_bf16<D, 2><<<grid, 512, 0, L.stream>>>(sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg); break;
+                case 3: mix_resident_bf16<D, 3><<<grid, 512, 0, L.stream>>>(sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg); break;
+                default: mix_resident_bf16<D, 0><<<grid, 512, 0, L.stream>>>(sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg); break;
+            }
         } else {
             mix_summaries_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(
                 sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg);

@@ -16,6 +16,7 @@ struct Tuning {
     int apply_maxw;      // bf16 path: waves per query_apply workgroup (4 or 8; heads grouped up to it)
     int nt_loads;        // bf16 path: non-temporal hint on the loads of k, v (summary kernel)
     int nt_apply;        // bf16 path: non-temporal hint on the loads of q (apply kernel)
+    int nt_mix;          // bf16 persistent mixing kernel: 1 = non-temporal summary loads, 2 = non-temporal stores of St
     int mix_resident;    // bf16 path, M <= 256: persistent mixing kernel with W in registers
     int num_cus;         // compute units of the current device (persistent grid size)
 };

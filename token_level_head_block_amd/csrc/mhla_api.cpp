@@ -137,6 +137,13 @@ mhla::Tuning choose_tuning(const Shape& s) {
     t.nt_loads = env_int("MHLA_NT_LOADS", 1) != 0;
     t.nt_apply = env_int("MHLA_NT_APPLY", s.D <= 64 ? 1 : 0) != 0;
     t.mix_resident = env_int("MHLA_MIX_RESIDENT", 1) != 0;
+    // Non-temporal stores of the mixed summaries: mixing 12.7 -> 11.7 us at
+    // dit-s2-256x256 (T = 256, the apply unchanged), video-16x64x64 307 us
+    // per step against 308; at T = 64 the apply waits longer for St (one
+    // wave per block and head reads all of St_i for 64 tokens): dit-s2-64x64
+    // 153 -> 159 us, sana-128x128 201 -> 216 us.  Non-temporal summary
+    // loads: 0.4 us slower at dit-s2-256x256.
+    t.nt_mix = env_int("MHLA_NT_MIX", s.T >= 128 ? 2 : 0) & 3;
     t.num_cus = 256;
     return t;
 }
