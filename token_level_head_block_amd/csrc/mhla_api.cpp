@@ -115,7 +115,10 @@ mhla::Tuning choose_tuning(const Shape& s) {
     // setup, enough waves to keep loads in flight.
     t.summary_waves = 1;
     t.summary_pf = 1;
-    t.apply_waves = s.T >= 128 ? 4 : 1;
+    // d = 128: every wave of a block holds all of St_i (32 KB of operands),
+    // so two waves per head load it half as often as four (video-16x64x64
+    // apply 118 -> 100 us; one wave per head 104 us).
+    t.apply_waves = s.T >= 128 ? (s.D == 128 ? 2 : 4) : 1;
     // d = 128 keeps 32 operand registers per row tile live; with 4 waves per
     // block, one group in flight per wave is enough.
     t.apply_pf = (s.D == 128 || s.T >= 128) ? 1 : 2;
