@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (2 = the metric's workload)")
     ap.add_argument("--path", choices=["3kernel", "fused", "causal"], default="3kernel",
                     help="causal: the causal chunkwise form; without --block the chunks are the grid's raster rows")
+    ap.add_argument("--stream-chunks", type=int, default=0,
+                    help="with --path causal: stream the sequence through mhla_causal_stream in calls of this "
+                         "many chunks (one step = the whole sequence)")
     ap.add_argument("--w", choices=["gaussian", "local", "identity", "ones"], default="gaussian")
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough to exceed 2x the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -430,6 +433,85 @@ def bench_layer(args, p, torch, mh, synth):
             f.write(s + "\n")
 
 
+def bench_stream(args, p, torch, mh, synth):
+    """Stateful causal execution: one step streams the whole sequence (chunks =
+    the grid's raster rows) through mhla_causal_stream in calls of
+    --stream-chunks chunks, carrying the fp32 state of chunk summaries."""
+    C = args.stream_chunks
+    rows = p.grid[0] if len(p.grid) == 2 else None
+    if len(p.grid) != 2 or p.block != (1, p.grid[1]) or rows % C:
+        raise SystemExit("--stream-chunks needs a 2D grid with raster-row chunks and a row count divisible by it")
+    ncall = rows // C
+    T = p.grid[1]
+    dt = mh.MHLA_BF16 if p.dtype == synth.BF16 else mh.MHLA_F32
+
+    def dev(x):
+        if p.dtype == synth.BF16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    q, k, v, W = synth.make_inputs(p, seed=args.config, w_kind=args.w)
+    n = C * T
+    # per-call inputs and outputs, contiguous, resident before the timed region
+    calls = []
+    for c in range(ncall):
+        sl = slice(c * n, (c + 1) * n)
+        qs, ks, vs = (dev(np.ascontiguousarray(x[:, sl])) for x in (q, k, v))
+        calls.append((qs, ks, vs, torch.empty_like(qs)))
+    Wd = torch.from_numpy(W).cuda()
+    g = mh.make_grid(p.batch, p.heads, p.head_dim, dt, (C, T), p.eps)
+    b = mh.make_block((1, T))
+    g_all = mh.make_grid(p.batch, p.heads, p.head_dim, dt, p.grid, p.eps)
+    state = torch.empty(mh.mhla_causal_state_bytes(g_all, b, rows) // 4, dtype=torch.float32, device="cuda")
+    wsb = mh.mhla_causal_stream_workspace_bytes(g, b)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    def step():
+        for c, (qs, ks, vs, out) in enumerate(calls):
+            st = mh.mhla_causal_stream(qs, ks, vs, Wd, g, b, c * C, state, rows, out, ws, wsb)
+            if st != mh.MHLA_OK:
+                raise mh.MhlaError(st, "mhla_causal_stream")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    tensor_bytes = p.batch * p.n_tokens * p.heads * p.head_dim * p.elem_bytes
+    U = 4 * tensor_bytes + 4 * p.n_blocks ** 2
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        t = time.perf_counter()
+        oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps, threads=ncpu)
+        dt_cpu = time.perf_counter() - t
+        cpu = {"value": round(p.batch * p.n_tokens / dt_cpu, 1), "unit": "tokens/s",
+               "cores": min(ncpu, p.batch * p.heads), "kind": "oracle", "seconds": round(dt_cpu, 3),
+               "sample": f"the full workload in one call ({p.batch * p.heads} (b,h) pairs, {p.n_tokens} tokens), "
+                         "float64 causal chunkwise oracle, one thread per pair"}
+    line = {
+        "metric": "MHLA causal streaming tokens/s", "value": round(p.batch * p.n_tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if p.dtype == synth.BF16 else "f32", "data": "synthetic",
+        "config": {"workload": f"{p.name}: B={p.batch} H={p.heads} d={p.head_dim} N={p.n_tokens}, "
+                               f"{rows} chunks of {T} tokens streamed in {ncall} calls of {C} chunks",
+                   "path": "causal stream", "w": args.w, "parallelism": "none (1 GPU)"},
+        "path_hbm_gbps": round(U / (ms_step * 1e-3) / 1e9, 1), "path_alg_bytes": U,
+        "ms_per_call": round(ms_step / ncall, 5),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -468,6 +550,11 @@ def main():
         return
     if args.layer:
         bench_layer(args, p, torch, mh, synth)
+        return
+    if args.stream_chunks:
+        if args.path != "causal":
+            raise SystemExit("--stream-chunks streams the causal form: add --path causal")
+        bench_stream(args, p, torch, mh, synth)
         return
     path = {"3kernel": mh.MHLA_PATH_3KERNEL, "fused": mh.MHLA_PATH_FUSED, "causal": mh.MHLA_PATH_CAUSAL}[args.path]
     tensor_bytes = p.batch * p.n_tokens * p.heads * p.head_dim * p.elem_bytes

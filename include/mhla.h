@@ -280,8 +280,11 @@ mhla_status mhla_causal_backward(const void* q, const void* k, const void* v, co
  * caller; slots 0 .. n_past-1 must hold the summaries written by earlier
  * calls (or by the caller), slots n_past .. n_past + M - 1 are overwritten.
  * W: fp32 [w_dim][w_dim] row-major; only W[i][j] with j <= i for the new
- * rows i is read.  q, k, v, out: [B, N_new, H, d] in the grid's dtype.  fp32
- * arithmetic.  Errors: MHLA_ERR_UNSUPPORTED for chunks that are not
+ * rows i is read.  q, k, v, out: [B, N_new, H, d] in the grid's dtype.
+ * Summaries and mixtures are formed in fp32; fp32 problems compute the
+ * outputs in fp32 token by token, bf16 problems round the mixtures to bf16
+ * operands and run the one-shot causal form's matrix-core apply (the
+ * forward's bf16 accuracy).  Errors: MHLA_ERR_UNSUPPORTED for chunks that are not
  * contiguous; MHLA_ERR_INVALID_ARG for n_past < 0, n_past + M beyond
  * max_chunks or w_dim, null pointers, or overlaps between out, state, the
  * inputs and the workspace; MHLA_ERR_MISALIGNED for pointers not 16-byte
@@ -290,8 +293,10 @@ mhla_status mhla_causal_backward(const void* q, const void* k, const void* v, co
 /* Bytes of the state for max_chunks chunks (0 for an invalid problem). */
 size_t mhla_causal_state_bytes(const mhla_grid* grid, const mhla_block* block, int32_t max_chunks);
 
-/* Bytes of workspace a call needs: the new chunks' mixtures, B*H*M records of
- * d*d + d fp32 (0 for an invalid, empty or unsupported problem). */
+/* Bytes of workspace a call needs for the new chunks' mixtures: B*H*M
+ * records of d*d + d fp32 for fp32 problems; for bf16 problems B*H*M*d*d
+ * bf16 (the mixed S, rounded) and B*H*M*d fp32 (the mixed z).  0 for an
+ * invalid, empty or unsupported problem. */
 size_t mhla_causal_stream_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
 
 /* One call of the stream, enqueued on `stream`: summaries of the new chunks

@@ -139,3 +139,20 @@ def test_stream_rows_of_an_image():
     err = rel_err(got, ref)
     say(f"  stream-rows: max|d|/max|ref| = {err:.3e}")
     assert err <= TOL[BF]
+
+
+def test_stream_long_sequence_bf16():
+    """16384 tokens in 64 chunks of 256 (six heads, d = 64), streamed in four
+    calls of 16 chunks through the matrix-core apply, against the oracle's
+    one-shot causal outputs: every output.  The nonnegative local W keeps
+    every partial row sum of W positive, so no denominator cancels."""
+    T, splits = 256, (16, 16, 16, 16)
+    M = sum(splits)
+    p = synth.Problem("stream-long", 1, 6, 64, (1, M * T), (1, T), dtype=BF)
+    q, k, v, W = synth.make_inputs(p, seed=85, w_kind="local")
+    got, state = stream_calls(p, q, k, v, W, splits, T)
+    ref = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    err = rel_err(got, ref)
+    say(f"  stream-long: max|d|/max|ref| = {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL[BF]

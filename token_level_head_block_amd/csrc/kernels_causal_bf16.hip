@@ -38,7 +38,7 @@ template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) void query_apply_causal_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ St, const float* __restrict__ Zt, const float* __restrict__ W,
-    uint16_t* __restrict__ O, const Geo g) {
+    uint16_t* __restrict__ O, const Geo g, const int wld) {
     constexpr int RT = D / 16, KS = D / 32;
     constexpr int NT = 64 * NW;        // threads
     constexpr int KT = 32 * NW;        // tokens per query tile and per key tile
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     const int h = __builtin_amdgcn_readfirstlane(wgc.hg);
     const int i = __builtin_amdgcn_readfirstlane(wgc.j);
     const int blk = (b * g.H + h) * g.M + i;
-    const float wii = W[(size_t)i * g.M + i];
+    const float wii = W[(size_t)i * wld + i];   // W[i][i], leading dimension wld
 
     // Chunks are contiguous in raster order: position p of chunk i is raster
     // index origin + p.  Offsets fit in 32 bits: tensors hold fewer than 2^31
@@ -251,39 +251,40 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
 }
 
 template <int D, int NW>
-void launch(const Launch& L) {
+void launch(const Launch& L, int wld) {
     Geo g = L.g;
     g.HG = g.H;
     g.G = 1;
     g.div_HG = make_fastdiv((uint32_t)g.HG);
     query_apply_causal_bf16<D, NW><<<g.B * g.M * g.H, 64 * NW, 0, L.stream>>>(
         static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v),
-        static_cast<const uint16_t*>(L.st), L.zt, L.W, static_cast<uint16_t*>(L.out), g);
+        static_cast<const uint16_t*>(L.st), L.zt, L.W, static_cast<uint16_t*>(L.out), g, wld);
 }
 
 template <int D>
-void launch_d(const Launch& L) {
+void launch_d(const Launch& L, int wld) {
     // Waves per workgroup: enough for two query groups each, at most 8 (at
     // most 4 at d = 128, whose 256-token tile would not fit LDS).
     const int nit = (L.g.T + 15) / 16;
     if constexpr (D < 128) {
         if (nit > 8) {
-            launch<D, 8>(L);
+            launch<D, 8>(L, wld);
             return;
         }
     }
-    if (nit > 4) launch<D, 4>(L);
-    else if (nit > 2) launch<D, 2>(L);
-    else launch<D, 1>(L);
+    if (nit > 4) launch<D, 4>(L, wld);
+    else if (nit > 2) launch<D, 2>(L, wld);
+    else launch<D, 1>(L, wld);
 }
 
 }  // namespace
 
-hipError_t launch_causal_apply_bf16(const Launch& L) {
+hipError_t launch_causal_apply_bf16(const Launch& L, int wld) {
+    if (wld <= 0) wld = L.g.M;
     switch (L.g.D) {
-        case 32: launch_d<32>(L); break;
-        case 64: launch_d<64>(L); break;
-        case 128: launch_d<128>(L); break;
+        case 32: launch_d<32>(L, wld); break;
+        case 64: launch_d<64>(L, wld); break;
+        case 128: launch_d<128>(L, wld); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

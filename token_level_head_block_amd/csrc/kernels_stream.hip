@@ -8,13 +8,19 @@
 // j < n_past, and coefficients W[i][j] (row-major, leading dimension w_dim):
 //   1. the new chunks' summaries go to the state at slots n_past + r;
 //   2. their mixtures over earlier chunks, St_i< = sum_{j<i} W[i][j] S_j and
-//      zt_i< likewise, go to the workspace;
+//      zt_i< likewise, go to the workspace (fp32 records, or for bf16
+//      problems St_i<^T rounded to bf16 and zt_i< in fp32);
 //   3. token n at position p of chunk i gets
 //        o_n = u^T (St_i< + w P_p) / (u . (zt_i< + w zp_p) + eps),
 //      u = phi(q_n), w = W[i][i], P_p, zp_p the chunk's sums of phi(k_m) v_m^T
 //      and phi(k_m) over m <= p.
-// fp32 arithmetic; q, k, v and o in bf16 or fp32.
+// fp32 arithmetic for the summaries and mixtures; q, k, v and o in bf16 or
+// fp32.  fp32 problems run step 3 token by token in fp32 (stream_apply);
+// bf16 problems run the causal apply kernel of the one-shot form on the
+// mixtures' bf16 operands.
 #include "launch.h"
+
+#include <mhla.h>
 
 namespace mhla {
 namespace {
@@ -30,74 +36,133 @@ __device__ __forceinline__ size_t tok_off(const Geo& g, int b, int h, int r, int
     return (((size_t)b * g.N + n) * g.H + h) * g.D;
 }
 
-// ---- summaries of the new chunks into the state: workgroup = (b h, chunk r),
-// each thread owns d*d/256 entries of S; tokens in batches of 16 through LDS.
-template <int D, typename T>
-__global__ __launch_bounds__(256) void stream_summary(const T* __restrict__ K, const T* __restrict__ V,
-                                                      float* __restrict__ state, int n_past, int max_chunks,
-                                                      const Geo g) {
-    constexpr int E = D * D / 256, TB = 16, L = D * D + D;
-    __shared__ float ka[TB][D], va[TB][D];
-    const int tid = threadIdx.x, blk = blockIdx.x;
+// ---- summaries of the new chunks into the state: workgroup = (b h, chunk r)
+// of NG groups of 256 threads.  Group gi takes the chunk's 32-token batches
+// gi, gi + NG, ... (the next one's raw loads in flight, in registers, while
+// the current one is multiplied from the group's LDS slice); thread t of a
+// group owns the TS x TS tile of S at rows TS (t / 16), columns TS (t % 16)
+// (TS = d / 16), so each token costs it 2 TS LDS reads for TS^2 products.
+// The groups' partial tiles are then added in group order (deterministic).
+template <int D, int NG, typename T>
+__global__ __launch_bounds__(256 * NG) void stream_summary(const T* __restrict__ K, const T* __restrict__ V,
+                                                           float* __restrict__ state, int n_past, int max_chunks,
+                                                           const Geo g) {
+    constexpr int TS = D / 16, TB = 32, L = D * D + D, NU = TB * D / 256;
+    // staging of every group's batch, reused for the partial sums of groups 1 .. NG-1
+    constexpr int NSTAGE = NG * 2 * TB * D, NPART = (NG - 1) * L;
+    __shared__ __attribute__((aligned(16))) float lds[NSTAGE > NPART ? NSTAGE : NPART];
+    const int tid = threadIdx.x & 255, gi = threadIdx.x >> 8, blk = blockIdx.x;
+    float* ka = lds + gi * (2 * TB * D);   // [TB][D] phi(K), then [TB][D] V
+    float* va = ka + TB * D;
     const int bh = blk / g.M, r = blk - bh * g.M;
     const int b = bh / g.H, h = bh - b * g.H;
-    float acc[E], zacc = 0.f;
+    const int c0 = TS * (tid >> 4), e0 = TS * (tid & 15);
+    float acc[TS][TS], zacc = 0.f;
 #pragma unroll
-    for (int x = 0; x < E; ++x) acc[x] = 0.f;
-    for (int t0 = 0; t0 < g.T; t0 += TB) {
-        __syncthreads();
-        for (int u = tid; u < TB * D; u += 256) {
-            const int tt = u / D, c = u - tt * D, p = t0 + tt;
-            float kv = 0.f, vv = 0.f;   // tokens past the chunk contribute nothing
-            if (p < g.T) {
-                const size_t off = tok_off(g, b, h, r, p) + c;
-                kv = phi_exact(ld1(K + off));
-                vv = ld1(V + off);
-            }
-            ka[tt][c] = kv;
-            va[tt][c] = vv;
+    for (int a = 0; a < TS; ++a)
+#pragma unroll
+        for (int x = 0; x < TS; ++x) acc[a][x] = 0.f;
+    T kr[NU], vr[NU];
+    auto load = [&](int t0) {
+#pragma unroll
+        for (int s = 0; s < NU; ++s) {
+            const int u = tid + 256 * s, tt = u / D, c = u - tt * D;
+            const int p = min(t0 + tt, g.T - 1);   // clamped; tokens past the chunk are zeroed below
+            const size_t off = tok_off(g, b, h, r, p) + c;
+            kr[s] = K[off];
+            vr[s] = V[off];
+        }
+    };
+    // every group runs the same number of rounds (barriers are workgroup-wide)
+    const int rounds = ((g.T + TB - 1) / TB + NG - 1) / NG;
+    load(TB * gi);
+    for (int it = 0; it < rounds; ++it) {
+        const int t0 = TB * (gi + NG * it);
+        __syncthreads();   // the previous batch's readers are done
+#pragma unroll
+        for (int s = 0; s < NU; ++s) {
+            const int u = tid + 256 * s, tt = u / D, c = u - tt * D;
+            const bool ok = t0 + tt < g.T;   // tokens past the chunk contribute nothing
+            ka[tt * D + c] = ok ? phi_exact(ld1(&kr[s])) : 0.f;
+            va[tt * D + c] = ok ? ld1(&vr[s]) : 0.f;
         }
         __syncthreads();
-#pragma unroll 4
+        if (it + 1 < rounds) load(t0 + TB * NG);
+#pragma unroll 2
         for (int tt = 0; tt < TB; ++tt) {
+            float kv[TS], vv[TS];
 #pragma unroll
-            for (int x = 0; x < E; ++x) {
-                const int idx = tid + 256 * x, c = idx / D, e = idx - c * D;
-                acc[x] += ka[tt][c] * va[tt][e];
+            for (int a = 0; a < TS; ++a) {
+                kv[a] = ka[tt * D + c0 + a];
+                vv[a] = va[tt * D + e0 + a];
             }
-            if (tid < D) zacc += ka[tt][tid];
+#pragma unroll
+            for (int a = 0; a < TS; ++a)
+#pragma unroll
+                for (int x = 0; x < TS; ++x) acc[a][x] += kv[a] * vv[x];
+            if (tid < D) zacc += ka[tt * D + tid];
         }
+    }
+    // groups 1 .. NG-1 leave their tiles (and z) in LDS; group 0 adds them in order
+    __syncthreads();
+    if (gi > 0) {
+        float* part = lds + (gi - 1) * (D * D + D);
+#pragma unroll
+        for (int a = 0; a < TS; ++a)
+#pragma unroll
+            for (int x = 0; x < TS; ++x) part[(c0 + a) * D + e0 + x] = acc[a][x];
+        if (tid < D) part[D * D + tid] = zacc;
+    }
+    __syncthreads();
+    if (gi > 0) return;
+    for (int q = 0; q < NG - 1; ++q) {
+        const float* part = lds + q * (D * D + D);
+#pragma unroll
+        for (int a = 0; a < TS; ++a)
+#pragma unroll
+            for (int x = 0; x < TS; ++x) acc[a][x] += part[(c0 + a) * D + e0 + x];
+        if (tid < D) zacc += part[D * D + tid];
     }
     float* out = state + ((size_t)bh * max_chunks + n_past + r) * L;
 #pragma unroll
-    for (int x = 0; x < E; ++x) out[tid + 256 * x] = acc[x];
+    for (int a = 0; a < TS; ++a)
+#pragma unroll
+        for (int x = 0; x < TS; ++x) out[(c0 + a) * D + e0 + x] = acc[a][x];
     if (tid < D) out[D * D + tid] = zacc;
 }
 
 // ---- mixtures over earlier chunks: mixed[bh][r][x] = sum_{j < n_past + r}
-// W[n_past + r][j] state[bh][j][x].  Workgroup = (b h, 16 new chunks, 256
-// record values); W rows go through LDS in pieces of 256 source chunks.
+// W[n_past + r][j] state[bh][j][x].  Workgroup = (b h, 16 new chunks, 64
+// record values); its four waves take every fourth earlier chunk, each lane
+// one record value, eight chunks' loads in flight at a time; the four partial
+// sums are added in wave order through LDS (deterministic).  W rows go
+// through LDS in pieces of 256 source chunks.  With St non-null (bf16
+// problems) the mixtures leave as the causal apply kernel's operands instead:
+// St^T [bh][r][e][c] in bf16 (round to nearest even) and zt [bh][r][d] fp32.
 __global__ __launch_bounds__(256) void stream_mix(const float* __restrict__ W, int w_dim,
                                                   const float* __restrict__ state, int max_chunks, int n_past,
-                                                  int m_new, float* __restrict__ mixed, int L) {
-    __shared__ float wt[16][257];
-    const int tid = threadIdx.x;
-    const int nxc = (L + 255) / 256, nrt = (m_new + 15) / 16;
+                                                  int m_new, float* __restrict__ mixed, int L, int D,
+                                                  uint16_t* __restrict__ St, float* __restrict__ Zt) {
+    constexpr int XW = 64, RB = 16, UN = 16;
+    __shared__ float wt[RB][257];
+    __shared__ float part[4][RB][XW];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nxc = (L + XW - 1) / XW, nrt = (m_new + RB - 1) / RB;
     int id = blockIdx.x;
     const int xc = id % nxc;
     id /= nxc;
     const int rt = id % nrt;
     const int bh = id / nrt;
-    const int x = xc * 256 + tid, r0 = rt * 16;
+    const int x = xc * XW + lane, r0 = rt * RB;
     const bool xok = x < L;
     const float* src = state + (size_t)bh * max_chunks * L + (xok ? x : 0);
-    const int jend = n_past + min(r0 + 16, m_new) - 1;   // the last row's earlier chunks end here
-    float acc[16];
+    const int jend = n_past + min(r0 + RB, m_new) - 1;   // the last row's earlier chunks end here
+    float acc[RB];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) acc[rr] = 0.f;
+    for (int rr = 0; rr < RB; ++rr) acc[rr] = 0.f;
     for (int j0 = 0; j0 < jend; j0 += 256) {
         __syncthreads();
-        for (int u = tid; u < 16 * 256; u += 256) {
+        for (int u = tid; u < RB * 256; u += 256) {
             const int rr = u >> 8, jj = u & 255, r = r0 + rr, j = j0 + jj;
             float wv = 0.f;
             if (r < m_new && j < n_past + r) wv = W[(size_t)(n_past + r) * w_dim + j];
@@ -105,16 +170,41 @@ __global__ __launch_bounds__(256) void stream_mix(const float* __restrict__ W, i
         }
         __syncthreads();
         const int jn = min(256, jend - j0);
-        for (int jj = 0; jj < jn; ++jj) {
-            const float v = src[(size_t)(j0 + jj) * L];
+        // chunks jj = wave, wave + 4, ...: UN loads issued before their products
+        for (int jb = wave; jb < jn; jb += 4 * UN) {
+            float v[UN];
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) acc[rr] += wt[rr][jj] * v;
+            for (int t = 0; t < UN; ++t) {
+                const int jj = jb + 4 * t;
+                v[t] = src[(size_t)(j0 + (jj < jn ? jj : jn - 1)) * L];
+            }
+#pragma unroll
+            for (int t = 0; t < UN; ++t) {
+                const int jj = jb + 4 * t;
+                if (jj < jn) {
+#pragma unroll
+                    for (int rr = 0; rr < RB; ++rr) acc[rr] += wt[rr][jj] * v[t];
+                }
+            }
         }
     }
-    if (!xok) return;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-        if (r0 + rr < m_new) mixed[((size_t)bh * m_new + r0 + rr) * L + x] = acc[rr];
+    for (int rr = 0; rr < RB; ++rr) part[wave][rr][lane] = acc[rr];
+    __syncthreads();
+    // thread (rr, lane) for rr = wave, wave + 4, ...: sum of the four waves in order
+    for (int rr = wave; rr < RB; rr += 4) {
+        const float sum = ((part[0][rr][lane] + part[1][rr][lane]) + part[2][rr][lane]) + part[3][rr][lane];
+        if (!xok || r0 + rr >= m_new) continue;
+        const size_t rec = (size_t)bh * m_new + r0 + rr;
+        if (!St) {
+            mixed[rec * L + x] = sum;
+        } else if (x < D * D) {
+            const int c = x / D, e = x - c * D;
+            St[rec * (D * D) + e * D + c] = (uint16_t)(pack_bf16(sum, 0.f) & 0xffffu);
+        } else {
+            Zt[rec * D + (x - D * D)] = sum;
+        }
+    }
 }
 
 // ---- outputs of the new chunks: workgroup = (b h, chunk r) of D threads;
@@ -166,12 +256,33 @@ hipError_t run_stream(const StreamLaunch& S) {
     const T* q = static_cast<const T*>(S.q);
     const T* k = static_cast<const T*>(S.k);
     const T* v = static_cast<const T*>(S.v);
-    stream_summary<D, T><<<nblk, 256, 0, S.stream>>>(k, v, S.state, S.n_past, S.max_chunks, g);
-    const int nxc = (L + 255) / 256, nrt = (g.M + 15) / 16;
+    constexpr int NG = D == 128 ? 2 : 4;   // token groups per chunk (LDS: 64 KB)
+    stream_summary<D, NG, T><<<nblk, 256 * NG, 0, S.stream>>>(k, v, S.state, S.n_past, S.max_chunks, g);
+    const int nxc = (L + 63) / 64, nrt = (g.M + 15) / 16;
+    constexpr bool BF = sizeof(T) == 2;
     stream_mix<<<g.BH * nrt * nxc, 256, 0, S.stream>>>(S.W, S.w_dim, S.state, S.max_chunks, S.n_past, g.M, S.mixed,
-                                                        L);
-    stream_apply<D, T><<<nblk, D, 0, S.stream>>>(q, k, v, S.mixed, S.W, S.w_dim, S.n_past, static_cast<T*>(S.out), g);
-    return hipGetLastError();
+                                                        L, D, BF ? S.st : nullptr, BF ? S.zt : nullptr);
+    if constexpr (sizeof(T) == 2) {
+        // bf16: the causal apply kernel of the one-shot form (matrix cores,
+        // whole chunks through LDS) on the mixtures, which stream_mix wrote
+        // as bf16 operands; W[i][i]
+        // of global chunk n_past + r is W0[r * w_dim + r], W0 = W + n_past (w_dim + 1).
+        Launch L{};
+        L.q = q; L.k = k; L.v = v;
+        L.W = S.W + (size_t)S.n_past * (S.w_dim + 1);
+        L.out = S.out;
+        L.st = S.st;
+        L.zt = S.zt;
+        L.g = g;
+        L.stream = S.stream;
+        L.path = MHLA_PATH_CAUSAL;
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_causal_apply_bf16(L, S.w_dim);
+    } else {
+        stream_apply<D, T><<<nblk, D, 0, S.stream>>>(q, k, v, S.mixed, S.W, S.w_dim, S.n_past, static_cast<T*>(S.out), g);
+        return hipGetLastError();
+    }
 }
 
 }  // namespace

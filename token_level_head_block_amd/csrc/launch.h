@@ -68,7 +68,9 @@ hipError_t run_bf16_summaries(const Launch& L);
 hipError_t run_bwd_bf16(const BwdLaunch& B);
 // The causal chunkwise apply (bf16, d = 32 or 64) after the summary and
 // mixing kernels have run with W restricted to earlier blocks.
-hipError_t launch_causal_apply_bf16(const Launch& L);
+// The causal apply kernel on the workspace's St, zt; W[i][i] is read as
+// L.W[i * wld + i] (wld <= 0: g.M, the one-shot form's square W).
+hipError_t launch_causal_apply_bf16(const Launch& L, int wld = 0);
 
 // The layer around the core: LayerNorm + QKV projection, optional q/k
 // RMSNorm, the feature-map variant, the core (core.q/k/v/out point at q, k,
@@ -147,7 +149,9 @@ struct StreamLaunch {
     int n_past;               // chunks already in the state
     float* state;
     int max_chunks;
-    float* mixed;             // [B*H][M][d*d + d] workspace
+    float* mixed;             // fp32 problems: mixtures [B*H][M][d*d + d] (workspace), else null
+    uint16_t* st;             // bf16 problems: mixed St^T [B*H][M][d][d] (bf16, workspace), else null
+    float* zt;                // bf16 problems: mixed zt [B*H][M][d] (fp32, workspace)
     void* out;
     hipStream_t stream;
 };

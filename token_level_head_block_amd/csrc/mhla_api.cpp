@@ -542,7 +542,22 @@ size_t stream_state_bytes(const Shape& s, int64_t max_chunks) {
     return (size_t)(s.B * s.H) * (size_t)max_chunks * (size_t)(s.D * s.D + s.D) * 4;
 }
 
-size_t stream_ws_bytes(const Shape& s) { return (size_t)(s.B * s.H * s.M) * (size_t)(s.D * s.D + s.D) * 4; }
+// Stream workspace: fp32 problems, the mixtures [B*H][M][d*d + d] fp32;
+// bf16 problems, the apply kernel's operands St^T [B*H][M][d*d] bf16, then
+// zt [B*H][M][d] fp32 (256-byte aligned).
+struct StreamLayout {
+    size_t st, zt, total;
+};
+StreamLayout stream_layout(const Shape& s) {
+    const size_t recs = (size_t)(s.B * s.H * s.M);
+    StreamLayout L;
+    L.st = 0;
+    L.zt = align_up(recs * (size_t)(s.D * s.D) * 2);
+    L.total = s.dtype == MHLA_BF16 ? L.zt + align_up(recs * (size_t)s.D * 4)
+                                   : recs * (size_t)(s.D * s.D + s.D) * 4;
+    return L;
+}
+size_t stream_ws_bytes(const Shape& s) { return stream_layout(s).total; }
 
 mhla_status stream_impl(const void* q, const void* k, const void* v, const float* W, int32_t w_dim,
                         const mhla_grid* grid, const mhla_block* block, int32_t n_past, float* state,
@@ -593,7 +608,10 @@ mhla_status stream_impl(const void* q, const void* k, const void* v, const float
     S.n_past = n_past;
     S.state = state;
     S.max_chunks = max_chunks;
-    S.mixed = static_cast<float*>(ws);
+    S.mixed = S.bf16 ? nullptr : static_cast<float*>(ws);
+    const StreamLayout SL = stream_layout(s);
+    S.st = S.bf16 ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + SL.st) : nullptr;
+    S.zt = S.bf16 ? reinterpret_cast<float*>(static_cast<char*>(ws) + SL.zt) : nullptr;
     S.out = out;
     S.stream = stream;
     const hipError_t err = mhla::run_causal_stream(S);
