@@ -227,7 +227,12 @@ def test_causal_stream_state_and_validation(L):
     L_ = 64 * 64 + 64
     assert mh.mhla_causal_state_bytes(new, chunk, 10) == 2 * 3 * 10 * L_ * 4
     assert mh.mhla_causal_state_bytes(new, chunk, 0) == 0
-    assert mh.mhla_causal_stream_workspace_bytes(new, chunk) == 2 * 3 * 4 * L_ * 4
+    # bf16: the mixed S of the 2*3*4 new records as bf16, then their mixed z in fp32 (256-byte aligned)
+    up = lambda x: (x + 255) // 256 * 256
+    assert mh.mhla_causal_stream_workspace_bytes(new, chunk) == up(2 * 3 * 4 * 64 * 64 * 2) + up(2 * 3 * 4 * 64 * 4)
+    # fp32: the mixtures as fp32 records
+    new32 = mh.make_grid(2, 3, 64, mh.MHLA_F32, (1, 256))
+    assert mh.mhla_causal_stream_workspace_bytes(new32, chunk) == 2 * 3 * 4 * L_ * 4
     g2d, b2d = cfg2()
     assert mh.mhla_causal_stream_workspace_bytes(g2d, b2d) == 0          # 2D tiles are not chunks
     sb = mh.mhla_causal_state_bytes(new, chunk, 10)
