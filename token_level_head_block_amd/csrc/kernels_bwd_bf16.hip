@@ -403,8 +403,12 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
 
 // =====================================================================
 // dW = sum over (b, h) and record elements of dSt_i[x] S_j[x]: a GEMM whose
-// k runs over B*H*(d*d + d).  Workgroup = (128 x 128 tile of dW, split s of
-// the k-steps); wave (wi, wj) computes 32 i x 64 j; both operands come from
+// k runs over B*H*(d*d + d).  Workgroup = (split s of the k-steps, 128 x 128
+// tile of dW); split s is a contiguous run of k-steps, so consecutive steps
+// read consecutive 64-byte pieces of each record row (whole cache lines over
+// two steps), and blockIdx.x = s puts every tile of one split on the same XCD
+// (workgroups are dealt to the XCDs by linear index), where they share the
+// records in L2.  Wave (wi, wj) computes 32 i x 64 j; both operands come from
 // the bf16 records (rows i of dSt, rows j of S, 8 consecutive elements per
 // lane).  Partial sums go to part[s]; dw_reduce adds them in split order.
 // =====================================================================
@@ -413,7 +417,7 @@ __global__ __launch_bounds__(512) void dw_partial_bf16(const uint16_t* __restric
                                                        const uint16_t* __restrict__ SZ, float* __restrict__ part,
                                                        int M, int P, int nsplit, int ntj) {
     constexpr int REC = D * D + D, KPR = REC / 32;
-    const int tile = blockIdx.x, s = blockIdx.y;
+    const int s = blockIdx.x, tile = blockIdx.y;
     const int ti = tile / ntj, tj = tile - ti * ntj;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, gq = lane >> 4;
@@ -454,8 +458,10 @@ __global__ __launch_bounds__(512) void dw_partial_bf16(const uint16_t* __restric
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(o.A[a] & mi[a], o.B[c] & mj[c], acc[a][c]);
     };
-    // Two later k-steps in flight while one is multiplied.
-    pipelined<2, Ops>(s, nsplit, P * KPR, load, compute);
+    // Steps [k0, k1) of this split; two later ones in flight while one is multiplied.
+    const int nks = P * KPR, per = (nks + nsplit - 1) / nsplit;
+    const int k0 = s * per, k1 = min(nks, k0 + per);
+    if (k0 < k1) pipelined<2, Ops>(k0, 1, k1, load, compute);
     float* out = part + (size_t)s * M * M;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -517,7 +523,13 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
         x.div_HG = make_fastdiv((uint32_t)x.HG);
         return x;
     };
-    const Geo gq = heads(D == 64 ? 4 : 8);
+    // d = 64: one wave per SIMD.  With many (b, block, head) tasks, workgroups
+    // of 2 waves keep every SIMD of a compute unit busy where groups of 3 idle
+    // one (dit-s2-64x64, 12288 tasks: 188 -> 159 us); with few tasks the
+    // larger groups' shared token rows win (dit-s2-256x256, 1536 tasks:
+    // groups of 3 heads 73.6 us, of 2 heads 75-78 us).
+    const int bq_max = D == 64 ? (g.H % 4 == 0 || g.B * g.M * g.H < 4096 ? 4 : 2) : 8;
+    const Geo gq = heads(L.tune.bwdq_heads > 0 ? L.tune.bwdq_heads : bq_max);
     bwd_query_bf16<D><<<gq.B * gq.M * gq.HG, 64 * gq.G, 0, L.stream>>>(
         static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(B.dout), static_cast<const uint16_t*>(L.st),
         L.zt, static_cast<uint16_t*>(B.dq), B.dst, gq);
@@ -533,7 +545,7 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     mg.div_CTG = make_fastdiv(mg.CTG);
     mix_transposed_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(B.dst, B.wbt, B.ds, B.dz, g, mg);
     const int ntj = (g.M + 127) / 128;
-    dw_partial_bf16<D><<<dim3(ntj * ntj, B.nsplit), 512, 0, L.stream>>>(
+    dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, L.stream>>>(
         B.dst, static_cast<const uint16_t*>(L.sz), B.part, g.M, g.BH, B.nsplit, ntj);
     dw_reduce<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, B.dw, g.M * g.M, B.nsplit);
     rec(B, 3);

@@ -13,6 +13,7 @@ struct Tuning {
     int apply_waves;     // waves splitting the tokens of one block in query_apply (1, 2, 4)
     int apply_pf;        // bf16 path: 16-token groups of Q loads in flight per wave (1, 2, 4)
     int pair_heads;      // bf16 path, head_dim 32 with an even head count: summaries of head pairs
+    int bwdq_heads;      // bf16 backward: heads per bwd_query workgroup (0: the kernel's maximum)
     int apply_maxw;      // bf16 path: waves per query_apply workgroup (4 or 8; heads grouped up to it)
     int nt_loads;        // bf16 path: non-temporal hint on the loads of k, v (summary kernel)
     int nt_apply;        // bf16 path: non-temporal hint on the loads of q (apply kernel)

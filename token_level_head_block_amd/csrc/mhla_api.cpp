@@ -131,6 +131,8 @@ mhla::Tuning choose_tuning(const Shape& s) {
     if (ap == 1 || ap == 2 || ap == 4) t.apply_pf = ap;
     t.pair_heads = env_int("MHLA_PAIR_HEADS", 1) != 0;
     t.apply_maxw = 8;
+    t.bwdq_heads = env_int("MHLA_BWDQ_HEADS", 0);
+    if (t.bwdq_heads < 0 || t.bwdq_heads > 4) t.bwdq_heads = 0;
     const int am = env_int("MHLA_APPLY_MAXW", 0);
     if (am == 4 || am == 8) t.apply_maxw = am;
     // Non-temporal loads: faster for the summary kernel's k, v stream.  On
