@@ -277,6 +277,86 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
     }
 }
 
+// dW for M <= 64: one 64 x 64 tile; the workgroup's eight waves are four
+// k-groups x two row halves (wave w: rows 32 (w & 1) .., all 64 columns,
+// k-steps k0 + (w >> 1), k0 + (w >> 1) + 4, ... of the split's run), and the
+// four k-groups' partial tiles are added in k-group order through LDS.
+template <int D>
+__global__ __launch_bounds__(512) void dw_partial_small_bf16(const uint16_t* __restrict__ dSt,
+                                                             const uint16_t* __restrict__ SZ, float* __restrict__ part,
+                                                             int M, int P, int nsplit) {
+    constexpr int REC = D * D + D, KPR = REC / 32;
+    __shared__ f32x4 red[3][2][2][4][64];   // k-groups 1..3 x row half x acc[2][4] x lane: 48 KB
+    const int s = blockIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane & 15, gq = lane >> 4;
+    const int half = wave & 1, kg = wave >> 1;
+    const int i0 = 32 * half;
+    int ri[2], rj[4];
+    uint32_t mi[2], mj[4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int i = i0 + 16 * a + li;
+        ri[a] = i < M ? i : M - 1;
+        mi[a] = i < M ? 0xffffffffu : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int jj = 16 * c + li;
+        rj[c] = jj < M ? jj : M - 1;
+        mj[c] = jj < M ? 0xffffffffu : 0u;
+    }
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    struct Ops {
+        u32x4 A[2], B[4];
+    };
+    auto load = [&](int ks, Ops& o) {
+        const int bh = ks / KPR, col = (ks - bh * KPR) * 32 + gq * 8;
+        const size_t rb = (size_t)bh * M;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) o.A[a] = *reinterpret_cast<const u32x4*>(dSt + (rb + ri[a]) * REC + col);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o.B[c] = *reinterpret_cast<const u32x4*>(SZ + (rb + rj[c]) * REC + col);
+    };
+    auto compute = [&](const Ops& o) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(o.A[a] & mi[a], o.B[c] & mj[c], acc[a][c]);
+    };
+    const int nks = P * KPR, per = (nks + nsplit - 1) / nsplit;
+    const int k0 = s * per, k1 = min(nks, k0 + per);
+    if (k0 + kg < k1) pipelined<2, Ops>(k0 + kg, 4, k1, load, compute);
+    if (kg > 0) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) red[kg - 1][half][a][c][lane] = acc[a][c];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[a][c] += red[q][half][a][c][lane];
+    float* out = part + (size_t)s * M * M;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = i0 + 16 * a + 4 * gq + v, jj = 16 * c + li;
+                if (i < M && jj < M) out[(size_t)i * M + jj] = acc[a][c][v];
+            }
+}
+
 // =====================================================================
 // bwd_kv: dv and dk per source block.  Workgroup = (b, block j, group of
 // <= 8 heads), one wave per head over the block's tokens, 16 per step:
@@ -545,8 +625,12 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     mg.div_CTG = make_fastdiv(mg.CTG);
     mix_transposed_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(B.dst, B.wbt, B.ds, B.dz, g, mg);
     const int ntj = (g.M + 127) / 128;
-    dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, L.stream>>>(
-        B.dst, static_cast<const uint16_t*>(L.sz), B.part, g.M, g.BH, B.nsplit, ntj);
+    if (g.M <= 64)
+        dw_partial_small_bf16<D><<<B.nsplit, 512, 0, L.stream>>>(B.dst, static_cast<const uint16_t*>(L.sz), B.part,
+                                                                 g.M, g.BH, B.nsplit);
+    else
+        dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, L.stream>>>(
+            B.dst, static_cast<const uint16_t*>(L.sz), B.part, g.M, g.BH, B.nsplit, ntj);
     dw_reduce<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, B.dw, g.M * g.M, B.nsplit);
     rec(B, 3);
     bwd_kv_bf16<D><<<grid_tok, block_tok, 0, L.stream>>>(
