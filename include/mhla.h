@@ -137,7 +137,15 @@ mhla_status mhla_launch_plan(const mhla_grid* grid, const mhla_block* block, int
  *             (rt * roundup(M,32)/32 + kk) * 64 + l holds
  *             W[16*rt + l%16][32*kk + 8*(l/16) .. +7].
  * After a MHLA_PATH_3KERNEL call completes, regions 0-2 hold these
- * intermediates; the fused path fills region 0 only. */
+ * intermediates; the fused path fills region 0 only.
+ * Token parts (bf16 problems with few blocks): let tasks = B*H*M and T the
+ * tokens per block; tp starts at 1 and doubles while tasks*tp < 1536,
+ * M*2*tp <= 256 and 2*tp*64 <= T.  With tp > 1 a MHLA_PATH_3KERNEL call
+ * splits each block's 32-token steps into tp contiguous runs: region 0 then
+ * holds P*M*tp records, record (pair, j*tp + t) summing part t of block j
+ * (S_j and z_j are the sums over t), and region 3 holds W with each column
+ * repeated tp times (roundup(M*tp, 32) columns).  Regions are sized for tp;
+ * the fused and causal paths always write tp = 1 records. */
 size_t mhla_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
 
 /* The MHLA forward pass: out = MHLA(q, k, v; W) for the whole problem,

@@ -158,6 +158,59 @@ def test_d32_head_pairs(case, monkeypatch):
         assert np.array_equal(a, b)
 
 
+def token_parts(B, H, M, T, limit_sources):
+    """Token parts of the bf16 3-kernel forward (the rule documented with
+    mhla_workspace_bytes): doubled while B*M*H*parts < 1536, parts of at least
+    64 tokens and, for the summaries, M*parts <= 256."""
+    p = 1
+    while B * M * H * p < 1536 and (not limit_sources or M * p * 2 <= 256) and p * 2 * 64 <= T:
+        p *= 2
+    return p
+
+
+PART_CASES = [
+    ("parts-d64-M16", 1, 6, 64, (128, 128), (32, 32), BF, 1.0),      # 16 parts of 64 tokens
+    ("parts-d32-M4-3d", 1, 3, 32, (4, 32, 32), (4, 16, 16), BF, 1.0),  # odd H (no head pairs), 3D blocks
+    ("parts-d128-M1", 1, 2, 128, (20, 40), (20, 40), BF, 1.0),       # one block, 25 token steps in 4 parts
+    ("parts-d64-ragged", 1, 2, 64, (50, 60), (25, 30), BF, 1.0),     # rows of 30 tokens, ragged last step
+]
+
+
+@pytest.mark.parametrize("case", PART_CASES, ids=lambda c: c[0])
+def test_token_parts(case):
+    """Few blocks: the summary kernel sums each block's tokens in parts (one
+    partial record per part), the mixing kernel contracts the partial records
+    with W's columns repeated, the apply kernel splits each block's tokens.
+    Every output against the oracle; the partial records of each block summed
+    against the oracle's S and z."""
+    p = small_problem(case)
+    B, H, d, M, T = p.batch, p.heads, p.head_dim, p.n_blocks, p.n_tokens // p.n_blocks
+    tp = token_parts(B, H, M, T, True)
+    assert tp > 1
+    q, k, v, W = synth.make_inputs(p, seed=27)
+    ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)
+    run = Run(p, q, k, v, W)
+    out_t = run.forward()
+    out = to_host64(out_t)
+    err = rel_err(out, ref)
+    say(f"  {p.name} (summary parts {tp}, apply parts {token_parts(B, H, M, T, False)}): max|d|/max|ref| = {err:.3e}")
+    assert np.isfinite(out).all()
+    assert err <= TOL[p.dtype]
+    rec = d * d + d
+    raw = run.ws.cpu().numpy()[: 2 * B * H * M * tp * rec].view(np.uint16)
+    parts = synth.bf16_to_f32(raw).astype(np.float64).reshape(B * H, M, tp, rec).sum(axis=2)
+    S = parts[:, :, : d * d].reshape(B * H, M, d, d).transpose(0, 1, 3, 2)
+    z = parts[:, :, d * d:]
+    rS, rz, _, _ = oracle.summaries(k, v, W, p.grid, p.block)
+    es, ez = rel_err(S, rS), rel_err(z, rz)
+    say(f"  {p.name} summed partial records: S {es:.2e} z {ez:.2e}")
+    assert es <= 1e-2 and ez <= 1e-2
+    # deterministic: a second call is bitwise equal
+    first = out_t.clone()
+    out2 = run.forward()
+    assert torch.equal(out2.view(torch.int16), first.view(torch.int16))
+
+
 @pytest.mark.parametrize("cfg_index", [1, 2, 3, 4])
 def test_full_workloads_sampled_pairs(cfg_index):
     """Full-size workload, default launch configuration; every output of the

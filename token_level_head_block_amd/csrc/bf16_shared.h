@@ -52,6 +52,7 @@ struct WConv {
     int32_t first_wg;         // workgroups [first_wg, gridDim.x) convert
     uint16_t* wbt;            // if not null, W^T is converted to this buffer as well
     int32_t causal;           // nonzero: keep only W[i][j] with j < i (earlier blocks)
+    int32_t TP;               // token parts: column j' of the operand is W[i][j' / TP] (j' < M TP)
 };
 
 __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t* __restrict__ Wb,
@@ -68,6 +69,13 @@ __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t*
         if (tr) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)(j0 + s) * wc.M + i] : 0.f;
+        } else if (wc.TP > 1) {
+            // source record j' = j TP + t holds part t of block j
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int jp = j0 + s;
+                x[s] = (i < wc.M && jp < wc.M * wc.TP) ? W[(size_t)i * wc.M + jp / wc.TP] : 0.f;
+            }
         } else if (i < wc.M && (wc.M & 7) == 0 && j0 < wc.M) {
             const f32x4 a = *reinterpret_cast<const f32x4*>(W + (size_t)i * wc.M + j0);
             const f32x4 b = *reinterpret_cast<const f32x4*>(W + (size_t)i * wc.M + j0 + 4);
@@ -131,11 +139,12 @@ __device__ __forceinline__ void mix_tile_bf16(uint32_t wg, const RecT* __restric
     const int li = lane & 15, gq = lane >> 4;
     const uint32_t bh = fdiv(wg, mg.div_CTG);
     const int ctg = (int)(wg - bh * mg.div_CTG.d);
-    const int M = g.M;
-    const int NK = (M + 31) >> 5;
+    const int M = g.M;                 // query blocks
+    const int MS = g.M * g.TP;         // source records (partial records of TP parts)
+    const int NK = (MS + 31) >> 5;
     const int cpw = mg.CPW;
     const int itr = mg.IT < 4 ? mg.IT : 4;   // i tiles per round
-    const RecT* base = SZ + (size_t)bh * M * REC;
+    const RecT* base = SZ + (size_t)bh * MS * REC;
     const int th = wave & 1, w2 = wave >> 1;
     const int wc = w2 / itr, wit = w2 % itr;
     const int ct = ctg * cpw + wc;
@@ -190,8 +199,8 @@ __device__ __forceinline__ void mix_tile_bf16(uint32_t wg, const RecT* __restric
                 for (int s = 0; s < 8; ++s) {
                     // Clamped address, then a mask: the load stays unconditional.
                     const int jj = (k0 + (jg >> 2)) * 32 + (jg & 3) * 8 + s;
-                    const u32x2 t = load4_bf16(base + (size_t)(jj < M ? jj : M - 1) * REC + colc);
-                    const uint32_t m = (ok && jj < M) ? 0xffffffffu : 0u;
+                    const u32x2 t = load4_bf16(base + (size_t)(jj < MS ? jj : MS - 1) * REC + colc);
+                    const uint32_t m = (ok && jj < MS) ? 0xffffffffu : 0u;
                     raw[s] = u32x2{t.x & m, t.y & m};
                 }
                 if (u < units) {

@@ -48,6 +48,12 @@ struct Geo {
     // of one (b, block), so its waves read whole runs of each token's channels.
     int32_t G, HG;        // heads per workgroup, head groups per (b, block)
     FastDiv div_HG;
+    // Token parts (bf16 3-kernel forward with few blocks): the summary kernel
+    // sums each block's tokens in TP contiguous runs into TP partial records
+    // (record (b h, j TP + t)), which the mixing kernel contracts as M TP source
+    // records; the apply kernel splits each block's tokens into AP runs.
+    int32_t TP, AP;
+    FastDiv div_TP, div_AP;
     float eps;
 };
 
@@ -60,6 +66,22 @@ __device__ __forceinline__ WgCoord wg_coord(const Geo& g, uint32_t wg) {
     WgCoord c;
     const uint32_t bj = fdiv(wg, g.div_HG);
     c.hg = (int)(wg - bj * g.div_HG.d);
+    c.b = (int)fdiv(bj, g.div_M);
+    c.j = (int)(bj - (uint32_t)c.b * g.div_M.d);
+    return c;
+}
+
+// Workgroup index -> (b, block, part, head group) for launches that also split
+// each block's tokens into parts: blockIdx = ((b * M + j) * parts + t) * HG + hg.
+struct WgCoordP {
+    int b, j, t, hg;
+};
+__device__ __forceinline__ WgCoordP wg_coord_parts(const Geo& g, uint32_t wg, const FastDiv& div_parts) {
+    WgCoordP c;
+    const uint32_t bjt = fdiv(wg, g.div_HG);
+    c.hg = (int)(wg - bjt * g.div_HG.d);
+    const uint32_t bj = fdiv(bjt, div_parts);
+    c.t = (int)(bjt - bj * div_parts.d);
     c.b = (int)fdiv(bj, g.div_M);
     c.j = (int)(bj - (uint32_t)c.b * g.div_M.d);
     return c;

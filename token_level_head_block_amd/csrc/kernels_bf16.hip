@@ -62,10 +62,10 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int quad = wave % NQ;
     const int li = lane & 15, gq = lane >> 4;
-    const WgCoord wgc = wg_coord(g, blockIdx.x);
+    const WgCoordP wgc = wg_coord_parts(g, blockIdx.x, g.div_TP);
     const int b = wgc.b, j = wgc.j, h = wgc.hg * g.G + wave / NQ;
     if (h >= g.H) return;
-    const int blk = (b * g.H + h) * g.M + j;   // record index (b, h, j)
+    const int blk = ((b * g.H + h) * g.M + j) * g.TP + wgc.t;   // record index (b, h, j, part)
     const int rowbase = (D == 128) ? (quad >> 1) * 64 : 0;
     const int colbase = (D == 128) ? (quad & 1) * 64 : 0;
     const bool do_z = (quad & 1) == 0;        // one wave per row range forms z
@@ -154,7 +154,10 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
             if (do_z) accz[r] = mfma_bf16(aw, ones, accz[r]);
         }
     };
-    pipelined<PF, Raw>(0, 1, (g.T + 31) >> 5, load, compute);
+    // This part's run of the block's 32-token steps (all of them when TP = 1).
+    const int nks = (g.T + 31) >> 5, per = (nks + g.TP - 1) / g.TP;
+    const int ks0 = wgc.t * per, ks1 = min(nks, ks0 + per);
+    if (ks0 < ks1) pipelined<PF, Raw>(ks0, 1, ks1, load, compute);
 
     // Record layout: S_j transposed ([e][c], c fastest), then z_j.
     // Lane holds S[c][e] for c = rowbase + 4*CPL*gq + CPL*v + r, e = colbase + CPL*li + c2,
@@ -187,7 +190,7 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
             const int er = k * 16 + (lane >> 2), chunk = lane & 3;
             const int s = er >> 5;
             const u32x4 x = *reinterpret_cast<const u32x4*>(stile + er * TS + DH * s + chunk * 8);
-            uint16_t* rech = SZ + ((size_t)(b * Hr + 2 * h + s) * g.M + j) * RECH;
+            uint16_t* rech = SZ + (((size_t)(b * Hr + 2 * h + s) * g.M + j) * g.TP + wgc.t) * RECH;
             *reinterpret_cast<u32x4*>(rech + (er - DH * s) * DH + chunk * 8) = x;
         }
         if (li == 0) {
@@ -198,7 +201,7 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
 #pragma unroll
                 for (int rp = 0; rp < 2; ++rp) wv[v * 2 + rp] = pack_bf16(accz[2 * rp][v], accz[2 * rp + 1][v]);
             const int s = gq >> 1;
-            uint16_t* dst = SZ + ((size_t)(b * Hr + 2 * h + s) * g.M + j) * RECH + DH * DH + 16 * (gq & 1);
+            uint16_t* dst = SZ + (((size_t)(b * Hr + 2 * h + s) * g.M + j) * g.TP + wgc.t) * RECH + DH * DH + 16 * (gq & 1);
             *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
             *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
         }
@@ -259,8 +262,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
     __shared__ __attribute__((aligned(16))) uint16_t sOut[8 * 32 * OROW];       // 36 KB
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, gq = lane >> 4;
-    const int M = g.M;
-    const int NK = (M + 31) >> 5;                     // <= KMAX (checked on the host)
+    const int M = g.M;                                // query blocks
+    const int MS = g.M * g.TP;                        // source records (partial records of TP parts)
+    const int NK = (MS + 31) >> 5;                    // <= KMAX (checked on the host)
     const int cpw = mg.CPW;
     const int itr = mg.IT;                            // <= 4 (checked on the host)
     const int th = wave & 1, w2 = wave >> 1;
@@ -291,12 +295,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
         const int colp = ct * 64 + 4 * lip;
         const bool ok = srole && colp < REC && ct < mg.CT;
         const int colc = ok ? colp : 0;
-        const uint16_t* base = SZ + (size_t)bh * M * REC;
+        const uint16_t* base = SZ + (size_t)bh * MS * REC;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int jj = (jg >> 2) * 32 + (jg & 3) * 8 + s;
-            const u32x2 t = ld<(NT & 1) != 0>(reinterpret_cast<const u32x2*>(base + (size_t)(jj < M ? jj : M - 1) * REC + colc));
-            const uint32_t m = (ok && jj < M) ? 0xffffffffu : 0u;
+            const u32x2 t = ld<(NT & 1) != 0>(reinterpret_cast<const u32x2*>(base + (size_t)(jj < MS ? jj : MS - 1) * REC + colc));
+            const uint32_t m = (ok && jj < MS) ? 0xffffffffu : 0u;
             raw[s] = u32x2{t.x & m, t.y & m};
         }
     };
@@ -405,7 +409,9 @@ template <int D, int NWA, int PF, bool NTL, int MAXW, typename PrepLoad, typenam
 __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFinish&& prep_finish,
                                                   const uint16_t* __restrict__ Q,
                                                   uint16_t* __restrict__ O, const Geo& g, int bh,
-                                                  int i, int wave, int lane) {
+                                                  int i, int wave, int lane, int p0 = 0, int p1 = -1) {
+    // Tokens [p0, p1) of block i (p1 < 0: to the block's end).
+    if (p1 < 0) p1 = g.T;
     constexpr int RT = D / 16, KS = D / 32;
     const int t = lane & 15, gq = lane >> 4;
     // bh and i are wave-uniform; say so, so that addresses and the buffer
@@ -421,7 +427,7 @@ __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFini
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         O + (size_t)b * g.N * row, 0, g.N * row * 2, 0x00020000);
     const int olane = h * D * 2;
-    const int nit = (g.T + 15) >> 4;
+    const int nit = (p1 - p0 + 15) >> 4;
     // Output staging: 16 tokens x D channels per wave, rows padded by 8 elements.
     constexpr int OSTR = D + 8;
     constexpr int CPR = D / 8;   // 16-byte chunks per token row
@@ -434,9 +440,9 @@ __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFini
         bool ok;
     };
     auto load = [&](int it, Raw& R) {
-        const int p = it * 16 + t;
-        R.ok = p < g.T;   // false for padding lanes and for groups past the end
-        R.off = (origin + in_block(g, R.ok ? p : g.T - 1)) * row;
+        const int p = p0 + it * 16 + t;
+        R.ok = p < p1;   // false for padding lanes and for groups past the end
+        R.off = (origin + in_block(g, R.ok ? p : p1 - 1)) * row;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) R.q[kk] = ld<NTL>(reinterpret_cast<const u32x4*>(qb + R.off + kk * 32));
     };
@@ -534,10 +540,14 @@ __global__ __launch_bounds__(64 * MAXW) void query_apply_bf16(const uint16_t* __
     constexpr int RT = D / 16, KS = D / 32;
     const int wave = (threadIdx.x >> 6) % NWA, lane = threadIdx.x & 63;
     const int t = lane & 15, gq = lane >> 4;
-    const WgCoord wgc = wg_coord(g, blockIdx.x);
+    const WgCoordP wgc = wg_coord_parts(g, blockIdx.x, g.div_AP);
     const int h = wgc.hg * g.G + (int)(threadIdx.x >> 6) / NWA;
     if (h >= g.H) return;
     const int i = wgc.j;
+    // Part t of AP contiguous runs of the block's 16-token groups.
+    const int ngr = (g.T + 15) >> 4, gper = (ngr + g.AP - 1) / g.AP;
+    const int p0 = min(g.T, 16 * gper * wgc.t), p1 = min(g.T, p0 + 16 * gper);
+    if (p0 >= p1) return;
     const int bh = wgc.b * g.H + h;
     const int blk = bh * g.M + i;
     const uint16_t* sb = St + (size_t)blk * (D * D);
@@ -564,7 +574,7 @@ __global__ __launch_bounds__(64 * MAXW) void query_apply_bf16(const uint16_t* __
             split_zt(z, A.zhi[kk], A.zlo[kk]);
         }
     };
-    apply_tokens_bf16<D, NWA, PF, NTL, MAXW>(prep_load, prep_finish, Q, O, g, bh, i, wave, lane);
+    apply_tokens_bf16<D, NWA, PF, NTL, MAXW>(prep_load, prep_finish, Q, O, g, bh, i, wave, lane, p0, p1);
 }
 
 // =====================================================================
@@ -683,7 +693,7 @@ void launch_summary(const Launch& L, const uint16_t* k, const uint16_t* v, uint1
         gp.BH = gp.B * gp.H;
     }
     const Geo g = with_head_groups(gp, NQ);
-    const int nsum = g.B * g.M * g.HG, threads = 64 * NQ * g.G;
+    const int nsum = g.B * g.M * g.TP * g.HG, threads = 64 * NQ * g.G;
     WConv w = wc;
     w.first_wg = nsum;
     const int nchunks = wc.nchunks * (wc.wbt ? 2 : 1);
@@ -711,7 +721,7 @@ void launch_summary_any(const Launch& L, const uint16_t* k, const uint16_t* v, u
 template <int D, int NWA, int PF, int MAXW>
 void launch_apply_pf(const Launch& L, const uint16_t* q, const uint16_t* st, uint16_t* o) {
     const Geo g = with_head_groups(L.g, NWA, MAXW);
-    const int grid = g.B * g.M * g.HG, block = 64 * NWA * g.G;
+    const int grid = g.B * g.M * g.AP * g.HG, block = 64 * NWA * g.G;
     if (L.tune.nt_apply) query_apply_bf16<D, NWA, PF, true, MAXW><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
     else query_apply_bf16<D, NWA, PF, false, MAXW><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
 }
@@ -731,7 +741,14 @@ void launch_apply(const Launch& L, const uint16_t* q, const uint16_t* st, uint16
 }
 
 template <int D>
-hipError_t run_d(const Launch& L) {
+hipError_t run_d(const Launch& L0) {
+    // Token parts apply to the whole 3-kernel forward only: the fused and
+    // causal paths and the backward's recompute read one record per block.
+    Launch L = L0;
+    if (L.path != MHLA_PATH_3KERNEL || L.summaries_only || L.g.TP < 1 || L.g.AP < 1) {
+        L.g.TP = L.g.AP = 1;
+        L.g.div_TP = L.g.div_AP = make_fastdiv(1u);
+    }
     const Geo& g = L.g;
     const int nblk = g.BH * g.M;
     const auto* q = static_cast<const uint16_t*>(L.q);
@@ -741,9 +758,12 @@ hipError_t run_d(const Launch& L) {
     auto* sz = static_cast<uint16_t*>(L.sz);
     auto* st = static_cast<uint16_t*>(L.st);
     const bool fused = L.path == MHLA_PATH_FUSED;
-    const int IT = (g.M + 63) / 64, NK = (g.M + 31) / 32;
+    // IT: 64-block tiles of query blocks; NK: 32-record k-steps over the
+    // M * TP source records.
+    const int IT = (g.M + 63) / 64, NK = (g.M * g.TP + 31) / 32;
     WConv wc;
     wc.M = g.M;
+    wc.TP = g.TP;
     wc.NK = NK;
     wc.nchunks = fused ? 0 : IT * 64 * NK * 32 / 8;
     wc.first_wg = 0;
@@ -771,12 +791,16 @@ hipError_t run_d(const Launch& L) {
         MixGeo mg;
         mg.CT = (D * D + D + 63) / 64;
         mg.IT = IT;
+        // Column tiles per workgroup: its 8 waves cover CPW tiles x IT query
+        // tiles x 2, and the A staging (one unit per thread) needs CPW * min(NK, 8) <= 8.
+        const int nkp = NK < 8 ? NK : 8;
         mg.CPW = IT >= 4 ? 1 : 4 / IT;
+        if (mg.CPW * nkp > 8) mg.CPW = 8 / nkp;
         mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
         mg.Jpad = NK * 32;
         mg.div_CTG = make_fastdiv(mg.CTG);
-        if (L.tune.mix_resident && IT <= 4) {
-            // NK <= 8 follows from M <= 256.
+        if (L.tune.mix_resident && IT <= 4 && NK <= 8) {
+            // NK <= 8: at most 256 source records (M <= 256, M * TP <= 256).
             const int units = g.BH * mg.CTG;
             const int grid = units < L.tune.num_cus ? units : L.tune.num_cus;
             switch (L.tune.nt_mix) {

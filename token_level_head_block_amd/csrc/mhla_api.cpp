@@ -78,20 +78,40 @@ bool causal_supported(const Shape& s) {
     return chunks_contiguous(s);   // bf16 or fp32, head_dim 32, 64 or 128
 }
 
+// Token parts of the bf16 3-kernel forward when the problem has few
+// (b, block, head) tasks: each part is a contiguous run of at least 64 of a
+// block's tokens, doubled until about 1536 tasks (six per compute unit) or
+// the limits (the mixing kernel contracts at most 256 source records, so
+// M * summary parts <= 256).
+int summary_parts(const Shape& s) {
+    if (s.dtype != MHLA_BF16) return 1;
+    int64_t p = 1;
+    while (s.B * s.M * s.H * p < 1536 && s.M * p * 2 <= 256 && p * 2 * 64 <= s.T) p *= 2;
+    return (int)p;
+}
+int apply_parts(const Shape& s) {
+    if (s.dtype != MHLA_BF16) return 1;
+    int64_t p = 1;
+    while (s.B * s.M * s.H * p < 1536 && p * 2 * 64 <= s.T) p *= 2;
+    return (int)p;
+}
+
 struct Layout {
     size_t sz, st, zt, wb, total;   // byte offsets of the regions, total size
 };
 
 Layout layout(const Shape& s) {
     const size_t recs = (size_t)(s.B * s.H * s.M);
+    const int tp = summary_parts(s);
     Layout L;
     L.sz = 0;
-    L.st = align_up(recs * (size_t)(s.D * s.D + s.D) * s.esz);
+    L.st = align_up(recs * (size_t)tp * (size_t)(s.D * s.D + s.D) * s.esz);
     L.zt = L.st + align_up(recs * (size_t)(s.D * s.D) * s.esz);
     L.wb = L.zt + align_up(recs * (size_t)s.D * 4);
     // bf16 problems: W converted to bf16, rows padded to a multiple of 64 and
     // columns to a multiple of 32 (the mixing kernel's tile sizes).
-    const size_t wb = s.dtype == MHLA_BF16 ? (size_t)((s.M + 63) / 64 * 64) * (size_t)((s.M + 31) / 32 * 32) * 2 : 0;
+    const size_t wb = s.dtype == MHLA_BF16
+                          ? (size_t)((s.M + 63) / 64 * 64) * (size_t)((s.M * tp + 31) / 32 * 32) * 2 : 0;
     L.total = L.wb + align_up(wb);
     return L;
 }
@@ -169,6 +189,8 @@ mhla::Geo make_geo(const Shape& s, float eps) {
     g.G = 1;
     g.HG = g.H;
     g.div_HG = mhla::make_fastdiv((uint32_t)(s.H > 0 ? s.H : 1));
+    g.TP = g.AP = 1;
+    g.div_TP = g.div_AP = mhla::make_fastdiv(1u);
     g.eps = eps;
     return g;
 }
@@ -218,6 +240,12 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
     L.wb = base + lay.wb;
     L.wbt = nullptr;
     L.g = make_geo(s, grid->eps);
+    if (path == MHLA_PATH_3KERNEL) {
+        L.g.TP = summary_parts(s);
+        L.g.AP = apply_parts(s);
+        L.g.div_TP = mhla::make_fastdiv((uint32_t)L.g.TP);
+        L.g.div_AP = mhla::make_fastdiv((uint32_t)L.g.AP);
+    }
     L.tune = choose_tuning(s);
     {
         int dev = 0, cus = 0;
