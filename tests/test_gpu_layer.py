@@ -23,6 +23,8 @@ CASES = [
     ("layer-3d-no-lepe", 1, 2, 64, (4, 8, 8), (2, 4, 4), False, False, False, mh.MHLA_PHI_ELU1),
     ("layer-d128", 1, 2, 128, (16, 16), (8, 8), False, True, True, mh.MHLA_PHI_RELU_EPS),
     ("layer-c384-rows", 2, 6, 64, (40, 36), (8, 12), True, True, False, mh.MHLA_PHI_ELU1),
+    # 4 blocks of 256 tokens: the core runs with token parts (4 summary and 4 apply parts)
+    ("layer-c64-token-parts", 1, 2, 32, (32, 32), (16, 16), False, True, True, mh.MHLA_PHI_ELU1),
 ]
 
 

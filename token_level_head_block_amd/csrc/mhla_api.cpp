@@ -96,6 +96,14 @@ int apply_parts(const Shape& s) {
     return (int)p;
 }
 
+// The 3-kernel forward's token parts in its geometry.
+void set_token_parts(mhla::Geo& g, const Shape& s) {
+    g.TP = summary_parts(s);
+    g.AP = apply_parts(s);
+    g.div_TP = mhla::make_fastdiv((uint32_t)g.TP);
+    g.div_AP = mhla::make_fastdiv((uint32_t)g.AP);
+}
+
 struct Layout {
     size_t sz, st, zt, wb, total;   // byte offsets of the regions, total size
 };
@@ -240,12 +248,7 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
     L.wb = base + lay.wb;
     L.wbt = nullptr;
     L.g = make_geo(s, grid->eps);
-    if (path == MHLA_PATH_3KERNEL) {
-        L.g.TP = summary_parts(s);
-        L.g.AP = apply_parts(s);
-        L.g.div_TP = mhla::make_fastdiv((uint32_t)L.g.TP);
-        L.g.div_AP = mhla::make_fastdiv((uint32_t)L.g.AP);
-    }
+    if (path == MHLA_PATH_3KERNEL) set_token_parts(L.g, s);
     L.tune = choose_tuning(s);
     {
         int dev = 0, cus = 0;
@@ -547,6 +550,7 @@ mhla_status layer_impl(const void* x, const float* W, const mhla_grid* grid, con
     F.wb = cb + cl.wb;
     F.wbt = nullptr;
     F.g = make_geo(s, grid->eps);
+    set_token_parts(F.g, s);   // the core's workspace regions are sized for them
     F.tune = choose_tuning(s);
     {
         int dev = 0, cus = 0;
