@@ -373,12 +373,19 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
     __shared__ __attribute__((aligned(16))) uint16_t lds[8 * 16 * OSTR];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = lane & 15, gq = lane >> 4;
-    const WgCoord wgc = wg_coord(g, blockIdx.x);
+    // Workgroup = (b, block j, token part, head group): part t takes a
+    // contiguous run of the block's 16-token groups (g.AP runs; one when the
+    // problem has blocks enough).
+    const WgCoordP wgc = wg_coord_parts(g, blockIdx.x, g.div_AP);
     const int hh = wgc.hg * g.G + wave;
     if (hh >= g.H) return;
     const int b = __builtin_amdgcn_readfirstlane(wgc.b);
     const int h = __builtin_amdgcn_readfirstlane(hh);
     const int j = __builtin_amdgcn_readfirstlane(wgc.j);
+    const int ngr = (g.T + 15) >> 4, gper = (ngr + g.AP - 1) / g.AP;
+    const int gr0 = __builtin_amdgcn_readfirstlane(min(ngr, gper * wgc.t));
+    const int gr1 = min(ngr, gr0 + gper);
+    if (gr0 >= gr1) return;
     const int blk = (b * g.H + h) * g.M + j;
     uint16_t* sout = lds + wave * (16 * OSTR);
 
@@ -416,7 +423,6 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
                                                                         g.N * row * 2, 0x00020000);
     const int olane = h * D * 2;
 
-    const int nit = (g.T + 15) >> 4;
     struct Raw {
         u32x4 kv[KS], vv[KS], ko[RT / 2];
         int off;
@@ -478,7 +484,7 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
         store_rows<D>(sout, wv, lane, R.off, R.ok, rk, olane);
     };
     // The next group's loads are in flight while this one is computed.
-    pipelined<1, Raw>(0, 1, nit, load, compute);
+    pipelined<1, Raw>(gr0, 1, gr1, load, compute);
 }
 
 // =====================================================================
@@ -613,8 +619,12 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     bwd_query_bf16<D><<<gq.B * gq.M * gq.HG, 64 * gq.G, 0, L.stream>>>(
         static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(B.dout), static_cast<const uint16_t*>(L.st),
         L.zt, static_cast<uint16_t*>(B.dq), B.dst, gq);
-    const Geo gh = heads(8);
-    const int grid_tok = gh.B * gh.M * gh.HG, block_tok = 64 * gh.G;
+    Geo gh = heads(8);
+    // bwd_kv: each block's tokens in token parts (dk, dv of a token depend only
+    // on its block's dS, dz), as many as the forward's apply uses.
+    gh.AP = B.kv_parts > 0 ? B.kv_parts : 1;
+    gh.div_AP = make_fastdiv((uint32_t)gh.AP);
+    const int grid_tok = gh.B * gh.M * gh.AP * gh.HG, block_tok = 64 * gh.G;
     rec(B, 2);
     MixGeo mg;
     mg.CT = (D * D + D + 63) / 64;

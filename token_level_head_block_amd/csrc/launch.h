@@ -61,6 +61,7 @@ struct BwdLaunch {
     uint16_t* wbt;    // W^T in the mixing kernel's operand order
     float* part;      // dW partial sums [nsplit][M][M]
     int nsplit;
+    int kv_parts;     // token parts of bwd_kv (1: one workgroup per block and head group)
     const hipEvent_t* events;   // 5 events or nullptr
 };
 

@@ -441,6 +441,7 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
     B.wbt = reinterpret_cast<uint16_t*>(base + lay.wbt);
     B.part = reinterpret_cast<float*>(base + lay.part);
     B.nsplit = lay.nsplit;
+    B.kv_parts = apply_parts(s);
     B.events = events;
     const hipError_t err = mhla::run_bwd_bf16(B);
     if (owned) (void)hipFreeAsync(ws, stream);
