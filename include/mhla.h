@@ -208,7 +208,10 @@ mhla_status mhla_forward_ex(const void* q, const void* k, const void* v, const f
  * gradients of the mixed summaries as B*H*M bf16 records in the summaries'
  * layout; gradients of the summaries, B*H*M*d*d bf16 ([e][c] order); gradients
  * of the normalisers, B*H*M*d fp32; W^T in the mixing kernel's operand order;
- * dW partial sums.  Other problems: four fp32 record arrays of B*H*M*(d*d + d)
+ * dW partial sums; and when tokens are split into parts (ap > 1, where ap
+ * starts at 1 and doubles while B*H*M*ap < 1536 and 2*ap*64 <= T), the query
+ * side's fp32 partial records of the mixed summaries' gradients, B*H*M*ap
+ * records of d*d + d values.  Other problems: four fp32 record arrays of B*H*M*(d*d + d)
  * values (summaries [c][e] then z, mixed summaries, their gradients, the
  * summaries' gradients), then dW partial sums. */
 size_t mhla_backward_workspace_bytes(const mhla_grid* grid, const mhla_block* block);

@@ -77,7 +77,8 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
                                                       const uint16_t* __restrict__ dO,
                                                       const uint16_t* __restrict__ St,
                                                       const float* __restrict__ Zt, uint16_t* __restrict__ dQ,
-                                                      uint16_t* __restrict__ dSt, const Geo g) {
+                                                      uint16_t* __restrict__ dSt, float* __restrict__ dpart,
+                                                      const Geo g) {
     constexpr int RT = D / 16, KS = D / 32, REC = D * D + D;
     constexpr int OSTR = D + 8, TS = 20;   // TS: transposed tile row, 16 tokens + 4 padding
     constexpr int SLICE = 16 * OSTR + 2 * D * TS;
@@ -85,12 +86,18 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
     __shared__ __attribute__((aligned(16))) uint16_t lds[MAXW * SLICE];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = lane & 15, gq = lane >> 4;
-    const WgCoord wgc = wg_coord(g, blockIdx.x);
+    // Workgroup = (b, block i, token part, head group); with g.AP > 1 part t
+    // takes a contiguous run of the block's 16-token groups and leaves its
+    // share of dSt, dzt as an fp32 partial record (fold_parts adds them).
+    const WgCoordP wgc = wg_coord_parts(g, blockIdx.x, g.div_AP);
     const int hh = wgc.hg * g.G + wave;
     if (hh >= g.H) return;
     const int b = __builtin_amdgcn_readfirstlane(wgc.b);
     const int h = __builtin_amdgcn_readfirstlane(hh);
     const int i = __builtin_amdgcn_readfirstlane(wgc.j);
+    const int ngr = (g.T + 15) >> 4, gper = (ngr + g.AP - 1) / g.AP;
+    const int gr0 = __builtin_amdgcn_readfirstlane(min(ngr, gper * wgc.t));
+    const int gr1 = min(ngr, gr0 + gper);
     const int bh = b * g.H + h, blk = bh * g.M + i;
     uint16_t* sout = lds + wave * SLICE;
     uint16_t* dnT = sout + 16 * OSTR;   // [e][token]
@@ -132,7 +139,6 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
         for (int rc = 0; rc < RT; ++rc) dsacc[re][rc] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int nit = (g.T + 15) >> 4;
     struct Raw {
         u32x4 qv[KS], go[RT / 2], qo[RT / 2];
         int off;
@@ -258,8 +264,23 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
         }
     };
     // The next group's loads are in flight while this one is computed.
-    pipelined<1, Raw>(0, 1, nit, load, compute);
+    if (gr0 < gr1) pipelined<1, Raw>(gr0, 1, gr1, load, compute);
 
+    if (g.AP > 1) {
+        // ---- this part's fp32 partial record (zeros for an empty part)
+        float* recf = dpart + ((size_t)blk * g.AP + wgc.t) * REC;
+#pragma unroll
+        for (int re = 0; re < RT; ++re)
+#pragma unroll
+            for (int rc = 0; rc < RT; ++rc)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) recf[(16 * re + 4 * gq + v) * D + 16 * rc + t] = dsacc[re][rc][v];
+        if (gq == 0) {
+#pragma unroll
+            for (int rc = 0; rc < RT; ++rc) recf[D * D + 16 * rc + t] = dzacc[rc][0];
+        }
+        return;
+    }
     // ---- the block's record: dSt as [e][c] (element (c, e) at e*D + c), then dzt[c].
     uint16_t* rec = dSt + (size_t)blk * REC;
 #pragma unroll
@@ -355,6 +376,19 @@ __global__ __launch_bounds__(512) void dw_partial_small_bf16(const uint16_t* __r
                 const int i = i0 + 16 * a + 4 * gq + v, jj = 16 * c + li;
                 if (i < M && jj < M) out[(size_t)i * M + jj] = acc[a][c][v];
             }
+}
+
+// The token parts' fp32 partial records [nrec][parts][rec] added in part order
+// and rounded to bf16 records [nrec][rec].
+__global__ __launch_bounds__(256) void fold_parts_bf16(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                       int nrec, int parts, int rec) {
+    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= (size_t)nrec * rec) return;
+    const size_t r = x / rec, e = x - r * rec;
+    const float* src = part + r * parts * rec + e;
+    float sum = 0.f;
+    for (int t = 0; t < parts; ++t) sum += src[(size_t)t * rec];
+    out[x] = (uint16_t)(pack_bf16(sum, 0.f) & 0xffffu);
 }
 
 // =====================================================================
@@ -615,10 +649,16 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     // larger groups' shared token rows win (dit-s2-256x256, 1536 tasks:
     // groups of 3 heads 73.6 us, of 2 heads 75-78 us).
     const int bq_max = D == 64 ? (g.H % 4 == 0 || g.B * g.M * g.H < 4096 ? 4 : 2) : 8;
-    const Geo gq = heads(L.tune.bwdq_heads > 0 ? L.tune.bwdq_heads : bq_max);
-    bwd_query_bf16<D><<<gq.B * gq.M * gq.HG, 64 * gq.G, 0, L.stream>>>(
+    Geo gq = heads(L.tune.bwdq_heads > 0 ? L.tune.bwdq_heads : bq_max);
+    gq.AP = B.q_parts > 1 && B.dpart ? B.q_parts : 1;
+    gq.div_AP = make_fastdiv((uint32_t)gq.AP);
+    bwd_query_bf16<D><<<gq.B * gq.M * gq.AP * gq.HG, 64 * gq.G, 0, L.stream>>>(
         static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(B.dout), static_cast<const uint16_t*>(L.st),
-        L.zt, static_cast<uint16_t*>(B.dq), B.dst, gq);
+        L.zt, static_cast<uint16_t*>(B.dq), B.dst, B.dpart, gq);
+    if (gq.AP > 1) {
+        const size_t n = (size_t)g.BH * g.M * (D * D + D);
+        fold_parts_bf16<<<(unsigned)((n + 255) / 256), 256, 0, L.stream>>>(B.dpart, B.dst, g.BH * g.M, gq.AP, D * D + D);
+    }
     Geo gh = heads(8);
     // bwd_kv: each block's tokens in token parts (dk, dv of a token depend only
     // on its block's dS, dz), as many as the forward's apply uses.

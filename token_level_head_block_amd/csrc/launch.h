@@ -62,6 +62,8 @@ struct BwdLaunch {
     float* part;      // dW partial sums [nsplit][M][M]
     int nsplit;
     int kv_parts;     // token parts of bwd_kv (1: one workgroup per block and head group)
+    int q_parts;      // token parts of bwd_query (1: as above)
+    float* dpart;     // q_parts > 1: fp32 partial records of dSt [BH][M][q_parts][D*D + D]
     const hipEvent_t* events;   // 5 events or nullptr
 };
 

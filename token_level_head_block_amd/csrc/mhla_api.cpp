@@ -271,8 +271,8 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
 
 struct BwdLayout {
     Layout fwd;                                  // regions of the forward recompute
-    size_t dst, ds, dz, wbt, part, total;
-    int nsplit;
+    size_t dst, ds, dz, wbt, part, dpart, total;
+    int nsplit, q_parts;
 };
 
 bool bwd_supported(const Shape& s) { return s.dtype == MHLA_BF16 && (s.D == 32 || s.D == 64); }
@@ -295,7 +295,10 @@ BwdLayout bwd_layout(const Shape& s) {
     if (ns < 1) ns = 1;
     if (ns > ksteps) ns = ksteps > 0 ? ksteps : 1;
     L.nsplit = (int)ns;
-    L.total = L.part + align_up((size_t)ns * (size_t)(s.M * s.M) * 4);
+    // bwd_query's token parts: fp32 partial records of the mixed summaries' gradients.
+    L.q_parts = apply_parts(s);
+    L.dpart = L.part + align_up((size_t)ns * (size_t)(s.M * s.M) * 4);
+    L.total = L.dpart + (L.q_parts > 1 ? align_up(recs * (size_t)L.q_parts * (size_t)(s.D * s.D + s.D) * 4) : 0);
     return L;
 }
 
@@ -442,6 +445,8 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
     B.part = reinterpret_cast<float*>(base + lay.part);
     B.nsplit = lay.nsplit;
     B.kv_parts = apply_parts(s);
+    B.q_parts = lay.q_parts;
+    B.dpart = lay.q_parts > 1 ? reinterpret_cast<float*>(base + lay.dpart) : nullptr;
     B.events = events;
     const hipError_t err = mhla::run_bwd_bf16(B);
     if (owned) (void)hipFreeAsync(ws, stream);
