@@ -53,17 +53,19 @@ struct WConv {
     uint16_t* wbt;            // if not null, W^T is converted to this buffer as well
     int32_t causal;           // nonzero: keep only W[i][j] with j < i (earlier blocks)
     int32_t TP;               // token parts: column j' of the operand is W[i][j' / TP] (j' < M TP)
+    int32_t NKt, nchunks_t;   // W^T (no token parts): NKt = roundup(M, 32) / 32, its 16-byte units
 };
 
 __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t* __restrict__ Wb,
                                           const WConv& wc) {
     const int nthr = (gridDim.x - wc.first_wg) * blockDim.x;
-    const int total = wc.nchunks * (wc.wbt ? 2 : 1);
+    const int total = wc.nchunks + (wc.wbt ? wc.nchunks_t : 0);
     for (int c0 = (blockIdx.x - wc.first_wg) * blockDim.x + threadIdx.x; c0 < total; c0 += nthr) {
         const bool tr = c0 >= wc.nchunks;   // the chunks of W^T follow those of W
         const int c = tr ? c0 - wc.nchunks : c0;
         const int lane = c & 63, rk = c >> 6;
-        const int rt = rk / wc.NK, kk = rk - rt * wc.NK;
+        const int nk = tr ? wc.NKt : wc.NK;
+        const int rt = rk / nk, kk = rk - rt * nk;
         const int i = 16 * rt + (lane & 15), j0 = 32 * kk + 8 * (lane >> 4);
         float x[8];
         if (tr) {

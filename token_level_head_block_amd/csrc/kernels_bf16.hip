@@ -696,7 +696,7 @@ void launch_summary(const Launch& L, const uint16_t* k, const uint16_t* v, uint1
     const int nsum = g.B * g.M * g.TP * g.HG, threads = 64 * NQ * g.G;
     WConv w = wc;
     w.first_wg = nsum;
-    const int nchunks = wc.nchunks * (wc.wbt ? 2 : 1);
+    const int nchunks = wc.nchunks + (wc.wbt ? wc.nchunks_t : 0);
     const int nconv = (nchunks + threads * 4 - 1) / (threads * 4);   // up to 4 chunks per thread
     if (L.tune.nt_loads)
         block_kv_summary_bf16<D, PF, ROW8, FULL, true, PAIR><<<nsum + nconv, threads, 0, L.stream>>>(
@@ -742,10 +742,11 @@ void launch_apply(const Launch& L, const uint16_t* q, const uint16_t* st, uint16
 
 template <int D>
 hipError_t run_d(const Launch& L0) {
-    // Token parts apply to the whole 3-kernel forward only: the fused and
-    // causal paths and the backward's recompute read one record per block.
+    // Token parts apply to the 3-kernel forward and the backward's recompute
+    // (which folds the partial records itself); the fused and causal paths
+    // read one record per block.
     Launch L = L0;
-    if (L.path != MHLA_PATH_3KERNEL || L.summaries_only || L.g.TP < 1 || L.g.AP < 1) {
+    if (L.path != MHLA_PATH_3KERNEL || L.g.TP < 1 || L.g.AP < 1) {
         L.g.TP = L.g.AP = 1;
         L.g.div_TP = L.g.div_AP = make_fastdiv(1u);
     }
@@ -766,6 +767,8 @@ hipError_t run_d(const Launch& L0) {
     wc.TP = g.TP;
     wc.NK = NK;
     wc.nchunks = fused ? 0 : IT * 64 * NK * 32 / 8;
+    wc.NKt = (g.M + 31) / 32;
+    wc.nchunks_t = IT * 64 * wc.NKt * 32 / 8;
     wc.first_wg = 0;
     wc.wbt = static_cast<uint16_t*>(L.wbt);
     const bool causal = L.path == MHLA_PATH_CAUSAL;

@@ -378,16 +378,19 @@ __global__ __launch_bounds__(512) void dw_partial_small_bf16(const uint16_t* __r
             }
 }
 
-// The token parts' fp32 partial records [nrec][parts][rec] added in part order
-// and rounded to bf16 records [nrec][rec].
-__global__ __launch_bounds__(256) void fold_parts_bf16(const float* __restrict__ part, uint16_t* __restrict__ out,
+// The token parts' partial records [nrec][parts][rec] (fp32 or bf16) added in
+// part order in fp32 and rounded to bf16 records [nrec][rec].
+__device__ __forceinline__ float as_f32(float x) { return x; }
+__device__ __forceinline__ float as_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+template <typename T>
+__global__ __launch_bounds__(256) void fold_parts_bf16(const T* __restrict__ part, uint16_t* __restrict__ out,
                                                        int nrec, int parts, int rec) {
     const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (x >= (size_t)nrec * rec) return;
     const size_t r = x / rec, e = x - r * rec;
-    const float* src = part + r * parts * rec + e;
+    const T* src = part + r * parts * rec + e;
     float sum = 0.f;
-    for (int t = 0; t < parts; ++t) sum += src[(size_t)t * rec];
+    for (int t = 0; t < parts; ++t) sum += as_f32(src[(size_t)t * rec]);
     out[x] = (uint16_t)(pack_bf16(sum, 0.f) & 0xffffu);
 }
 
@@ -628,11 +631,24 @@ inline void rec(const BwdLaunch& B, int k) {
 template <int D>
 hipError_t run_bwd_d(const BwdLaunch& B) {
     const Launch& L = B.F;
-    const Geo& g = L.g;
+    const int tp = L.g.TP;   // the recompute's token parts
+    // The gradient kernels see one record per block (token parts of the
+    // query and key/value sides are set on their own launches below).
+    Geo g = L.g;
+    g.TP = g.AP = 1;
+    g.div_TP = g.div_AP = make_fastdiv(1u);
     rec(B, 0);
     // Forward summaries and mixed summaries (regions 0-3 of the workspace).
     hipError_t err = run_bf16_summaries(L);
     if (err != hipSuccess) return err;
+    // In token parts the summaries are partial records; dW reads them folded.
+    const uint16_t* srec = static_cast<const uint16_t*>(L.sz);
+    if (tp > 1 && B.sfold) {
+        const size_t n = (size_t)g.BH * g.M * (D * D + D);
+        fold_parts_bf16<uint16_t><<<(unsigned)((n + 255) / 256), 256, 0, L.stream>>>(
+            static_cast<const uint16_t*>(L.sz), B.sfold, g.BH * g.M, tp, D * D + D);
+        srec = B.sfold;
+    }
     rec(B, 1);
     const int IT = (g.M + 63) / 64, NK = (g.M + 31) / 32;
     // Head groups: at most `maxw` heads (one wave each) per workgroup, balanced.
@@ -657,7 +673,8 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
         L.zt, static_cast<uint16_t*>(B.dq), B.dst, B.dpart, gq);
     if (gq.AP > 1) {
         const size_t n = (size_t)g.BH * g.M * (D * D + D);
-        fold_parts_bf16<<<(unsigned)((n + 255) / 256), 256, 0, L.stream>>>(B.dpart, B.dst, g.BH * g.M, gq.AP, D * D + D);
+        fold_parts_bf16<float><<<(unsigned)((n + 255) / 256), 256, 0, L.stream>>>(B.dpart, B.dst, g.BH * g.M, gq.AP,
+                                                                                  D * D + D);
     }
     Geo gh = heads(8);
     // bwd_kv: each block's tokens in token parts (dk, dv of a token depend only
@@ -676,11 +693,10 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     mix_transposed_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(B.dst, B.wbt, B.ds, B.dz, g, mg);
     const int ntj = (g.M + 127) / 128;
     if (g.M <= 64)
-        dw_partial_small_bf16<D><<<B.nsplit, 512, 0, L.stream>>>(B.dst, static_cast<const uint16_t*>(L.sz), B.part,
-                                                                 g.M, g.BH, B.nsplit);
+        dw_partial_small_bf16<D><<<B.nsplit, 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH, B.nsplit);
     else
-        dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, L.stream>>>(
-            B.dst, static_cast<const uint16_t*>(L.sz), B.part, g.M, g.BH, B.nsplit, ntj);
+        dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH,
+                                                                            B.nsplit, ntj);
     dw_reduce<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, B.dw, g.M * g.M, B.nsplit);
     rec(B, 3);
     bwd_kv_bf16<D><<<grid_tok, block_tok, 0, L.stream>>>(

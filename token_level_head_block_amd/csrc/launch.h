@@ -64,6 +64,7 @@ struct BwdLaunch {
     int kv_parts;     // token parts of bwd_kv (1: one workgroup per block and head group)
     int q_parts;      // token parts of bwd_query (1: as above)
     float* dpart;     // q_parts > 1: fp32 partial records of dSt [BH][M][q_parts][D*D + D]
+    uint16_t* sfold;  // recompute in token parts (F.g.TP > 1): S records folded to [BH][M][D*D + D]
     const hipEvent_t* events;   // 5 events or nullptr
 };
 

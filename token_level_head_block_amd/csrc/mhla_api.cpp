@@ -271,8 +271,8 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
 
 struct BwdLayout {
     Layout fwd;                                  // regions of the forward recompute
-    size_t dst, ds, dz, wbt, part, dpart, total;
-    int nsplit, q_parts;
+    size_t dst, ds, dz, wbt, part, dpart, sfold, total;
+    int nsplit, q_parts, s_parts;
 };
 
 bool bwd_supported(const Shape& s) { return s.dtype == MHLA_BF16 && (s.D == 32 || s.D == 64); }
@@ -298,7 +298,11 @@ BwdLayout bwd_layout(const Shape& s) {
     // bwd_query's token parts: fp32 partial records of the mixed summaries' gradients.
     L.q_parts = apply_parts(s);
     L.dpart = L.part + align_up((size_t)ns * (size_t)(s.M * s.M) * 4);
-    L.total = L.dpart + (L.q_parts > 1 ? align_up(recs * (size_t)L.q_parts * (size_t)(s.D * s.D + s.D) * 4) : 0);
+    L.sfold = L.dpart + (L.q_parts > 1 ? align_up(recs * (size_t)L.q_parts * (size_t)(s.D * s.D + s.D) * 4) : 0);
+    // The recompute's summaries in token parts, folded into one bf16 record per
+    // block for the dW product.
+    L.s_parts = summary_parts(s);
+    L.total = L.sfold + (L.s_parts > 1 ? align_up(recs * (size_t)(s.D * s.D + s.D) * 2) : 0);
     return L;
 }
 
@@ -423,6 +427,7 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
     L.wb = base + lay.fwd.wb;
     L.wbt = base + lay.wbt;
     L.g = make_geo(s, grid->eps);
+    set_token_parts(L.g, s);   // the recompute's summaries in token parts (regions sized for them)
     L.tune = choose_tuning(s);
     L.path = MHLA_PATH_3KERNEL;
     L.summaries_only = 1;
@@ -447,6 +452,7 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
     B.kv_parts = apply_parts(s);
     B.q_parts = lay.q_parts;
     B.dpart = lay.q_parts > 1 ? reinterpret_cast<float*>(base + lay.dpart) : nullptr;
+    B.sfold = lay.s_parts > 1 ? reinterpret_cast<uint16_t*>(base + lay.sfold) : nullptr;
     B.events = events;
     const hipError_t err = mhla::run_bwd_bf16(B);
     if (owned) (void)hipFreeAsync(ws, stream);
