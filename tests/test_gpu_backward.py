@@ -38,6 +38,7 @@ SMALL = [
     # few blocks of many tokens: the key/value side runs in token parts
     ("bwd-d64-M4-parts", 1, 2, 64, (32, 32), (16, 16), 1.0),
     ("bwd-d32-M4-parts", 1, 4, 32, (32, 48), (16, 24), 1.0),
+    ("bwd-d64-B2-parts", 2, 3, 64, (64, 64), (32, 32), 1.0),
 ]
 
 # the general path: name, B, H, d, grid, block, dtype

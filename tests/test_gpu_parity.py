@@ -173,6 +173,7 @@ PART_CASES = [
     ("parts-d32-M4-3d", 1, 3, 32, (4, 32, 32), (4, 16, 16), BF, 1.0),  # odd H (no head pairs), 3D blocks
     ("parts-d128-M1", 1, 2, 128, (20, 40), (20, 40), BF, 1.0),       # one block, 25 token steps in 4 parts
     ("parts-d64-ragged", 1, 2, 64, (50, 60), (25, 30), BF, 1.0),     # rows of 30 tokens, ragged last step
+    ("parts-d64-B2", 2, 3, 64, (64, 64), (32, 32), BF, 1.0),          # two batch items, 16 parts
 ]
 
 
