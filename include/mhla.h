@@ -144,8 +144,16 @@ mhla_status mhla_launch_plan(const mhla_grid* grid, const mhla_block* block, int
  * splits each block's 32-token steps into tp contiguous runs: region 0 then
  * holds P*M*tp records, record (pair, j*tp + t) summing part t of block j
  * (S_j and z_j are the sums over t), and region 3 holds W with each column
- * repeated tp times (roundup(M*tp, 32) columns).  Regions are sized for tp;
- * the fused and causal paths always write tp = 1 records. */
+ * repeated tp times (roundup(M*tp, 32) columns).  The fused path writes
+ * tp = 1 records.
+ * Causal sub-chunks (bf16 problems with contiguous chunks): cp starts at 1
+ * and doubles while the chunk's slowest axis of extent > 1 divides by 2*cp,
+ * T/(2*cp) >= 256 and M*2*cp <= 256.  With cp > 1 a MHLA_PATH_CAUSAL call
+ * runs the causal form on the M*cp sub-chunks (W between sub-chunks a and b
+ * is W[a/cp][b/cp]), so its records in regions 0-2 are per sub-chunk and
+ * region 3 holds that sub-chunk coefficient matrix.
+ * Sizes: region 0 holds P*M*max(tp, cp) records, regions 1 and 2 P*M*cp,
+ * region 3 roundup(M*cp, 64) x roundup(M*max(tp, cp), 32) bf16 values. */
 size_t mhla_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
 
 /* The MHLA forward pass: out = MHLA(q, k, v; W) for the whole problem,

@@ -30,6 +30,12 @@ CASES = [
     ("causal-d128-T256", 1, 2, 128, (1, 1024), (1, 256), 1.0),
     ("causal-d128-T40", 2, 1, 128, (1, 200), (1, 40), 1.0),
     ("causal-d128-M1", 1, 1, 128, (1, 300), (1, 300), 1.0),
+    # long chunks run on sub-chunks of >= 256 tokens (W between sub-chunks from their chunks)
+    ("causal-1d-T2048-sub", 1, 2, 64, (1, 8192), (1, 2048), 1.0),
+    ("causal-rows-2d-sub", 1, 2, 32, (64, 64), (16, 64), 1.0),
+    ("causal-frames-3d-sub", 1, 2, 64, (4, 32, 32), (1, 32, 32), 1.0),
+    ("causal-d128-sub", 1, 2, 128, (1, 2048), (1, 1024), 1.0),
+    ("causal-1d-T1000-sub", 1, 1, 64, (1, 3000), (1, 1000), 1.0),
 ]
 
 

@@ -54,6 +54,7 @@ struct WConv {
     int32_t causal;           // nonzero: keep only W[i][j] with j < i (earlier blocks)
     int32_t TP;               // token parts: column j' of the operand is W[i][j' / TP] (j' < M TP)
     int32_t NKt, nchunks_t;   // W^T (no token parts): NKt = roundup(M, 32) / 32, its 16-byte units
+    int32_t WD, WM;           // causal sub-chunks: entry (i, j) is W[i / WD][j / WD], W is WM x WM
 };
 
 __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t* __restrict__ Wb,
@@ -71,12 +72,14 @@ __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t*
         if (tr) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)(j0 + s) * wc.M + i] : 0.f;
-        } else if (wc.TP > 1) {
-            // source record j' = j TP + t holds part t of block j
+        } else if (wc.TP > 1 || wc.WD > 1) {
+            // token parts: source record j' = j TP + t holds part t of block j;
+            // causal sub-chunks: row and column indices are sub-chunks, WD per block of W
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const int jp = j0 + s;
-                x[s] = (i < wc.M && jp < wc.M * wc.TP) ? W[(size_t)i * wc.M + jp / wc.TP] : 0.f;
+                x[s] = (i < wc.M && jp < wc.M * wc.TP)
+                           ? W[(size_t)(i / wc.WD) * wc.WM + jp / (wc.TP * wc.WD)] : 0.f;
             }
         } else if (i < wc.M && (wc.M & 7) == 0 && j0 < wc.M) {
             const f32x4 a = *reinterpret_cast<const f32x4*>(W + (size_t)i * wc.M + j0);

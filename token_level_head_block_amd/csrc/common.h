@@ -54,6 +54,10 @@ struct Geo {
     // records; the apply kernel splits each block's tokens into AP runs.
     int32_t TP, AP;
     FastDiv div_TP, div_AP;
+    // W's index for this geometry's block i is i / WD (WD > 1: the bf16 causal
+    // form run on sub-chunks, WD of them per chunk of the caller's problem);
+    // WM is W's dimension (the caller's block count).
+    int32_t WD, WM;
     float eps;
 };
 

@@ -769,6 +769,8 @@ hipError_t run_d(const Launch& L0) {
     wc.nchunks = fused ? 0 : IT * 64 * NK * 32 / 8;
     wc.NKt = (g.M + 31) / 32;
     wc.nchunks_t = IT * 64 * wc.NKt * 32 / 8;
+    wc.WD = g.WD;
+    wc.WM = g.WM;
     wc.first_wg = 0;
     wc.wbt = static_cast<uint16_t*>(L.wbt);
     const bool causal = L.path == MHLA_PATH_CAUSAL;

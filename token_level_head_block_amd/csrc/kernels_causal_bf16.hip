@@ -60,7 +60,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     const int h = __builtin_amdgcn_readfirstlane(wgc.hg);
     const int i = __builtin_amdgcn_readfirstlane(wgc.j);
     const int blk = (b * g.H + h) * g.M + i;
-    const float wii = W[(size_t)i * wld + i];   // W[i][i], leading dimension wld
+    const int iw = i / g.WD;                     // W's index of this block (sub-chunks: WD per chunk)
+    const float wii = W[(size_t)iw * wld + iw];  // W[iw][iw], leading dimension wld
 
     // Chunks are contiguous in raster order: position p of chunk i is raster
     // index origin + p.  Offsets fit in 32 bits: tensors hold fewer than 2^31
@@ -280,7 +281,7 @@ void launch_d(const Launch& L, int wld) {
 }  // namespace
 
 hipError_t launch_causal_apply_bf16(const Launch& L, int wld) {
-    if (wld <= 0) wld = L.g.M;
+    if (wld <= 0) wld = L.g.WM;
     switch (L.g.D) {
         case 32: launch_d<32>(L, wld); break;
         case 64: launch_d<64>(L, wld); break;

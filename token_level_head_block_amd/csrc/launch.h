@@ -73,8 +73,9 @@ hipError_t run_bf16_summaries(const Launch& L);
 hipError_t run_bwd_bf16(const BwdLaunch& B);
 // The causal chunkwise apply (bf16, d = 32 or 64) after the summary and
 // mixing kernels have run with W restricted to earlier blocks.
-// The causal apply kernel on the workspace's St, zt; W[i][i] is read as
-// L.W[i * wld + i] (wld <= 0: g.M, the one-shot form's square W).
+// The causal apply kernel on the workspace's St, zt; W's diagonal entry of
+// block i is read as L.W[iw * wld + iw], iw = i / g.WD (wld <= 0: g.WM, the
+// one-shot form's square W).
 hipError_t launch_causal_apply_bf16(const Launch& L, int wld = 0);
 
 // The layer around the core: LayerNorm + QKV projection, optional q/k

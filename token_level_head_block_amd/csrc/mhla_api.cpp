@@ -89,6 +89,35 @@ int summary_parts(const Shape& s) {
     while (s.B * s.M * s.H * p < 1536 && s.M * p * 2 <= 256 && p * 2 * 64 <= s.T) p *= 2;
     return (int)p;
 }
+// The bf16 causal form on long chunks runs on sub-chunks: a chunk (a run of
+// raster order) is split along its slowest axis of extent > 1 into cp runs of
+// at least 256 tokens (at most 256 sub-chunks in all).  The causal form over
+// chunks with W equals the causal form over sub-chunks with coefficient
+// W[a / cp][b / cp] between sub-chunks a and b: every pair of tokens keeps
+// the weight of its chunks and the mask m <= n.
+int causal_split_axis(const Shape& s) {
+    for (int a = 0; a < 3; ++a)
+        if (s.b[a] > 1) return a;
+    return -1;
+}
+int causal_parts(const Shape& s) {
+    if (s.dtype != MHLA_BF16 || !chunks_contiguous(s)) return 1;
+    const int a = causal_split_axis(s);
+    if (a < 0) return 1;
+    int64_t cp = 1;
+    while (s.b[a] % (cp * 2) == 0 && s.T / (cp * 2) >= 256 && s.M * cp * 2 <= 256) cp *= 2;
+    return (int)cp;
+}
+Shape subchunk_shape(const Shape& s, int cp) {
+    Shape t = s;
+    const int a = causal_split_axis(s);
+    t.b[a] = s.b[a] / cp;
+    t.nb[a] = s.nb[a] * cp;
+    t.M = s.M * cp;
+    t.T = s.T / cp;
+    return t;
+}
+
 int apply_parts(const Shape& s) {
     if (s.dtype != MHLA_BF16) return 1;
     int64_t p = 1;
@@ -110,16 +139,19 @@ struct Layout {
 
 Layout layout(const Shape& s) {
     const size_t recs = (size_t)(s.B * s.H * s.M);
-    const int tp = summary_parts(s);
+    const int tp = summary_parts(s), cp = causal_parts(s);
+    const size_t r0 = recs * (size_t)(tp > cp ? tp : cp);   // summary records (parts or sub-chunks)
+    const size_t r12 = recs * (size_t)cp;                     // mixed records (sub-chunks)
     Layout L;
     L.sz = 0;
-    L.st = align_up(recs * (size_t)tp * (size_t)(s.D * s.D + s.D) * s.esz);
-    L.zt = L.st + align_up(recs * (size_t)(s.D * s.D) * s.esz);
-    L.wb = L.zt + align_up(recs * (size_t)s.D * 4);
+    L.st = align_up(r0 * (size_t)(s.D * s.D + s.D) * s.esz);
+    L.zt = L.st + align_up(r12 * (size_t)(s.D * s.D) * s.esz);
+    L.wb = L.zt + align_up(r12 * (size_t)s.D * 4);
     // bf16 problems: W converted to bf16, rows padded to a multiple of 64 and
     // columns to a multiple of 32 (the mixing kernel's tile sizes).
     const size_t wb = s.dtype == MHLA_BF16
-                          ? (size_t)((s.M + 63) / 64 * 64) * (size_t)((s.M * tp + 31) / 32 * 32) * 2 : 0;
+                          ? (size_t)((s.M * cp + 63) / 64 * 64) * (size_t)((s.M * (tp > cp ? tp : cp) + 31) / 32 * 32) * 2
+                          : 0;
     L.total = L.wb + align_up(wb);
     return L;
 }
@@ -199,6 +231,8 @@ mhla::Geo make_geo(const Shape& s, float eps) {
     g.div_HG = mhla::make_fastdiv((uint32_t)(s.H > 0 ? s.H : 1));
     g.TP = g.AP = 1;
     g.div_TP = g.div_AP = mhla::make_fastdiv(1u);
+    g.WD = 1;
+    g.WM = g.M;
     g.eps = eps;
     return g;
 }
@@ -249,6 +283,14 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
     L.wbt = nullptr;
     L.g = make_geo(s, grid->eps);
     if (path == MHLA_PATH_3KERNEL) set_token_parts(L.g, s);
+    if (path == MHLA_PATH_CAUSAL && s.dtype == MHLA_BF16) {
+        const int cp = causal_parts(s);
+        if (cp > 1) {
+            L.g = make_geo(subchunk_shape(s, cp), grid->eps);
+            L.g.WD = cp;
+            L.g.WM = (int32_t)s.M;
+        }
+    }
     L.tune = choose_tuning(s);
     {
         int dev = 0, cus = 0;
