@@ -438,11 +438,14 @@ def bench_stream(args, p, torch, mh, synth):
     the grid's raster rows) through mhla_causal_stream in calls of
     --stream-chunks chunks, carrying the fp32 state of chunk summaries."""
     C = args.stream_chunks
-    rows = p.grid[0] if len(p.grid) == 2 else None
-    if len(p.grid) != 2 or p.block != (1, p.grid[1]) or rows % C:
-        raise SystemExit("--stream-chunks needs a 2D grid with raster-row chunks and a row count divisible by it")
+    if len(p.grid) != 2 or p.block[1] != p.grid[1]:
+        raise SystemExit("--stream-chunks needs a 2D grid whose chunks are whole raster rows")
+    R = p.block[0]                    # raster rows per chunk
+    rows = p.grid[0] // R             # chunks in the sequence
+    if rows % C:
+        raise SystemExit("--stream-chunks must divide the number of chunks")
     ncall = rows // C
-    T = p.grid[1]
+    T = R * p.grid[1]                 # tokens per chunk
     dt = mh.MHLA_BF16 if p.dtype == synth.BF16 else mh.MHLA_F32
 
     def dev(x):
@@ -459,8 +462,8 @@ def bench_stream(args, p, torch, mh, synth):
         qs, ks, vs = (dev(np.ascontiguousarray(x[:, sl])) for x in (q, k, v))
         calls.append((qs, ks, vs, torch.empty_like(qs)))
     Wd = torch.from_numpy(W).cuda()
-    g = mh.make_grid(p.batch, p.heads, p.head_dim, dt, (C, T), p.eps)
-    b = mh.make_block((1, T))
+    g = mh.make_grid(p.batch, p.heads, p.head_dim, dt, (C * R, p.grid[1]), p.eps)
+    b = mh.make_block((R, p.grid[1]))
     g_all = mh.make_grid(p.batch, p.heads, p.head_dim, dt, p.grid, p.eps)
     state = torch.empty(mh.mhla_causal_state_bytes(g_all, b, rows) // 4, dtype=torch.float32, device="cuda")
     wsb = mh.mhla_causal_stream_workspace_bytes(g, b)

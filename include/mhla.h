@@ -313,9 +313,12 @@ mhla_status mhla_causal_backward(const void* q, const void* k, const void* v, co
 size_t mhla_causal_state_bytes(const mhla_grid* grid, const mhla_block* block, int32_t max_chunks);
 
 /* Bytes of workspace a call needs for the new chunks' mixtures: B*H*M
- * records of d*d + d fp32 for fp32 problems; for bf16 problems B*H*M*d*d
- * bf16 (the mixed S, rounded) and B*H*M*d fp32 (the mixed z).  0 for an
- * invalid, empty or unsupported problem. */
+ * records of d*d + d fp32 for fp32 problems; for bf16 problems B*H*M*cp*d*d
+ * bf16 (the mixed S, rounded) and B*H*M*cp*d fp32 (the mixed z), where cp is
+ * the sub-chunk count of mhla_workspace_bytes' causal rule (long chunks run
+ * as cp sub-chunks each), and with cp > 1 also B*H*M records of d*d + d fp32
+ * (the chunks' mixtures) and B*H*M*cp such records (the sub-chunks'
+ * summaries).  0 for an invalid, empty or unsupported problem. */
 size_t mhla_causal_stream_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
 
 /* One call of the stream, enqueued on `stream`: summaries of the new chunks

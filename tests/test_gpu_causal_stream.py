@@ -73,6 +73,10 @@ CASES = [
     ("stream-f32-d64", 1, 2, 64, 20, (2, 1, 3), F32, "local"),
     ("stream-f32-d128", 1, 1, 128, 16, (1, 4), F32, "local"),
     ("stream-f32-d32-T1", 2, 1, 32, 1, (5, 1, 10), F32, "local"),
+    # long chunks: each call runs its chunks as sub-chunks of >= 256 tokens
+    ("stream-long-chunks", 1, 2, 64, 1024, (1, 2, 1), BF, "gaussian"),
+    ("stream-d128-long", 1, 1, 128, 512, (2, 1), BF, "gaussian"),
+    ("stream-d32-long-B2", 2, 3, 32, 768, (1, 1), BF, "local"),
 ]
 
 

@@ -47,6 +47,8 @@ template <int D, int NG, typename T>
 __global__ __launch_bounds__(256 * NG) void stream_summary(const T* __restrict__ K, const T* __restrict__ V,
                                                            float* __restrict__ state, int n_past, int max_chunks,
                                                            const Geo g) {
+    // Record of block r: state[(b h) max_chunks + n_past + r] (for sub-chunks:
+    // the workspace with max_chunks = the call's sub-chunks and n_past = 0).
     constexpr int TS = D / 16, TB = 32, L = D * D + D, NU = TB * D / 256;
     // staging of every group's batch, reused for the partial sums of groups 1 .. NG-1
     constexpr int NSTAGE = NG * 2 * TB * D, NPART = (NG - 1) * L;
@@ -249,6 +251,52 @@ __global__ __launch_bounds__(D) void stream_apply(const T* __restrict__ Q, const
     }
 }
 
+// ---- long chunks in sub-chunks (bf16 problems): a chunk's state record is
+// the sum of its cp sub-chunk summaries (added in sub-chunk order); sub-chunk
+// t of new chunk r gets the operands of
+//   St< = mixed[r] + W[i][i] sum_{t' < t} Ssub[r cp + t'],  i = n_past + r
+// (zt< likewise), as St<^T in bf16 and zt< in fp32.
+__global__ __launch_bounds__(256) void stream_fold(const float* __restrict__ ssub, float* __restrict__ state,
+                                                   int m_new, int cp, int max_chunks, int n_past, int L, int nbh) {
+    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= (size_t)nbh * m_new * L) return;
+    const size_t rec = x / L, e = x - rec * L;
+    const int bh = (int)(rec / m_new), r = (int)(rec - (size_t)bh * m_new);
+    const float* src = ssub + ((size_t)bh * m_new * cp + (size_t)r * cp) * L + e;
+    float sum = 0.f;
+    for (int t = 0; t < cp; ++t) sum += src[(size_t)t * L];
+    state[((size_t)bh * max_chunks + n_past + r) * L + e] = sum;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void stream_sub_operands(const float* __restrict__ mixed,
+                                                           const float* __restrict__ ssub, const float* __restrict__ W,
+                                                           int w_dim, int n_past, int m_new, int cp,
+                                                           uint16_t* __restrict__ St, float* __restrict__ Zt) {
+    constexpr int L = D * D + D;
+    const int blk = blockIdx.x;                   // (b h, sub-chunk a) of the call, a = r cp + t
+    const int bh = blk / (m_new * cp), a = blk - bh * (m_new * cp);
+    const int r = a / cp, t = a - r * cp;
+    const float w = W[(size_t)(n_past + r) * (w_dim + 1)];
+    const float* mrec = mixed + ((size_t)bh * m_new + r) * L;
+    const float* sb = ssub + ((size_t)bh * m_new * cp + (size_t)r * cp) * L;
+    auto value = [&](int x) {
+        float acc = 0.f;
+        for (int u = 0; u < t; ++u) acc += sb[(size_t)u * L + x];
+        return mrec[x] + w * acc;
+    };
+    uint16_t* st = St + (size_t)blk * (D * D);
+    for (int u = threadIdx.x; u < D * D / 8; u += 256) {
+        const int e = u % D, c0 = (u / D) * 8;
+        float xv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) xv[q] = value((c0 + q) * D + e);
+        *reinterpret_cast<u32x4*>(st + e * D + c0) =
+            u32x4{pack_bf16(xv[0], xv[1]), pack_bf16(xv[2], xv[3]), pack_bf16(xv[4], xv[5]), pack_bf16(xv[6], xv[7])};
+    }
+    if (threadIdx.x < D) Zt[(size_t)blk * D + threadIdx.x] = value(D * D + threadIdx.x);
+}
+
 template <int D, typename T>
 hipError_t run_stream(const StreamLaunch& S) {
     const Geo& g = S.g;
@@ -257,6 +305,36 @@ hipError_t run_stream(const StreamLaunch& S) {
     const T* k = static_cast<const T*>(S.k);
     const T* v = static_cast<const T*>(S.v);
     constexpr int NG = D == 128 ? 2 : 4;   // token groups per chunk (LDS: 64 KB)
+    if constexpr (sizeof(T) == 2) {
+        if (S.cp > 1) {
+            // Long chunks: summaries per sub-chunk, folded into the state; the
+            // chunks' mixtures over earlier chunks in fp32; operands per
+            // sub-chunk; the causal apply on the sub-chunks.
+            const Geo& gs = S.gs;
+            const int nsub = gs.BH * gs.M;
+            stream_summary<D, NG, T><<<nsub, 256 * NG, 0, S.stream>>>(k, v, S.ssub, 0, gs.M, gs);
+            const size_t nf = (size_t)g.BH * g.M * L;
+            stream_fold<<<(unsigned)((nf + 255) / 256), 256, 0, S.stream>>>(S.ssub, S.state, g.M, S.cp, S.max_chunks,
+                                                                           S.n_past, L, g.BH);
+            const int nxc = (L + 63) / 64, nrt = (g.M + 15) / 16;
+            stream_mix<<<g.BH * nrt * nxc, 256, 0, S.stream>>>(S.W, S.w_dim, S.state, S.max_chunks, S.n_past, g.M,
+                                                                S.mixed, L, D, nullptr, nullptr);
+            stream_sub_operands<D><<<nsub, 256, 0, S.stream>>>(S.mixed, S.ssub, S.W, S.w_dim, S.n_past, g.M, S.cp,
+                                                               S.st, S.zt);
+            Launch La{};
+            La.q = q; La.k = k; La.v = v;
+            La.W = S.W + (size_t)S.n_past * (S.w_dim + 1);
+            La.out = S.out;
+            La.st = S.st;
+            La.zt = S.zt;
+            La.g = gs;   // WD = cp: sub-chunk a reads W's diagonal of its chunk a / cp
+            La.stream = S.stream;
+            La.path = MHLA_PATH_CAUSAL;
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            return launch_causal_apply_bf16(La, S.w_dim);
+        }
+    }
     stream_summary<D, NG, T><<<nblk, 256 * NG, 0, S.stream>>>(k, v, S.state, S.n_past, S.max_chunks, g);
     const int nxc = (L + 63) / 64, nrt = (g.M + 15) / 16;
     constexpr bool BF = sizeof(T) == 2;

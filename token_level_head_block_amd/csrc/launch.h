@@ -158,6 +158,12 @@ struct StreamLaunch {
     float* mixed;             // fp32 problems: mixtures [B*H][M][d*d + d] (workspace), else null
     uint16_t* st;             // bf16 problems: mixed St^T [B*H][M][d][d] (bf16, workspace), else null
     float* zt;                // bf16 problems: mixed zt [B*H][M][d] (fp32, workspace)
+    // bf16 problems with long chunks: cp sub-chunks per chunk, their geometry
+    // (WD = cp), their fp32 summaries [B*H][M*cp][d*d + d]; `mixed` then holds
+    // the chunks' fp32 mixtures and st, zt the sub-chunks' operands.
+    int cp;
+    Geo gs;
+    float* ssub;
     void* out;
     hipStream_t stream;
 };

@@ -631,18 +631,26 @@ size_t stream_state_bytes(const Shape& s, int64_t max_chunks) {
 }
 
 // Stream workspace: fp32 problems, the mixtures [B*H][M][d*d + d] fp32;
-// bf16 problems, the apply kernel's operands St^T [B*H][M][d*d] bf16, then
-// zt [B*H][M][d] fp32 (256-byte aligned).
+// bf16 problems, the apply kernel's operands St^T [B*H][M*cp][d*d] bf16, then
+// zt [B*H][M*cp][d] fp32, and with long chunks (cp > 1 sub-chunks per chunk,
+// as for the one-shot causal form) the chunks' fp32 mixtures [B*H][M][d*d + d]
+// and the sub-chunks' fp32 summaries [B*H][M*cp][d*d + d] (256-byte aligned).
 struct StreamLayout {
-    size_t st, zt, total;
+    size_t st, zt, mixed, ssub, total;
+    int cp;
 };
 StreamLayout stream_layout(const Shape& s) {
-    const size_t recs = (size_t)(s.B * s.H * s.M);
+    const size_t recs = (size_t)(s.B * s.H * s.M), L1 = (size_t)(s.D * s.D + s.D);
     StreamLayout L;
+    L.cp = s.dtype == MHLA_BF16 ? causal_parts(s) : 1;
+    const size_t sub = recs * (size_t)L.cp;
     L.st = 0;
-    L.zt = align_up(recs * (size_t)(s.D * s.D) * 2);
-    L.total = s.dtype == MHLA_BF16 ? L.zt + align_up(recs * (size_t)s.D * 4)
-                                   : recs * (size_t)(s.D * s.D + s.D) * 4;
+    L.zt = align_up(sub * (size_t)(s.D * s.D) * 2);
+    L.mixed = L.zt + align_up(sub * (size_t)s.D * 4);
+    L.ssub = L.mixed + align_up(recs * L1 * 4);
+    if (s.dtype != MHLA_BF16) L.total = recs * L1 * 4;
+    else if (L.cp == 1) L.total = L.mixed;
+    else L.total = L.ssub + align_up(sub * L1 * 4);
     return L;
 }
 size_t stream_ws_bytes(const Shape& s) { return stream_layout(s).total; }
@@ -696,10 +704,18 @@ mhla_status stream_impl(const void* q, const void* k, const void* v, const float
     S.n_past = n_past;
     S.state = state;
     S.max_chunks = max_chunks;
-    S.mixed = S.bf16 ? nullptr : static_cast<float*>(ws);
     const StreamLayout SL = stream_layout(s);
-    S.st = S.bf16 ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + SL.st) : nullptr;
-    S.zt = S.bf16 ? reinterpret_cast<float*>(static_cast<char*>(ws) + SL.zt) : nullptr;
+    char* wsb = static_cast<char*>(ws);
+    S.cp = SL.cp;
+    S.mixed = !S.bf16 ? static_cast<float*>(ws) : SL.cp > 1 ? reinterpret_cast<float*>(wsb + SL.mixed) : nullptr;
+    S.st = S.bf16 ? reinterpret_cast<uint16_t*>(wsb + SL.st) : nullptr;
+    S.zt = S.bf16 ? reinterpret_cast<float*>(wsb + SL.zt) : nullptr;
+    S.ssub = SL.cp > 1 ? reinterpret_cast<float*>(wsb + SL.ssub) : nullptr;
+    if (SL.cp > 1) {
+        S.gs = make_geo(subchunk_shape(s, SL.cp), grid->eps);
+        S.gs.WD = SL.cp;
+        S.gs.WM = (int32_t)s.M;
+    }
     S.out = out;
     S.stream = stream;
     const hipError_t err = mhla::run_causal_stream(S);
