@@ -268,33 +268,30 @@ __global__ __launch_bounds__(256) void stream_fold(const float* __restrict__ ssu
     state[((size_t)bh * max_chunks + n_past + r) * L + e] = sum;
 }
 
+// Workgroup = (b h, chunk r, 256 record elements x); each thread walks the
+// chunk's sub-chunks in order with the running prefix sum of their summaries.
 template <int D>
 __global__ __launch_bounds__(256) void stream_sub_operands(const float* __restrict__ mixed,
                                                            const float* __restrict__ ssub, const float* __restrict__ W,
                                                            int w_dim, int n_past, int m_new, int cp,
                                                            uint16_t* __restrict__ St, float* __restrict__ Zt) {
-    constexpr int L = D * D + D;
-    const int blk = blockIdx.x;                   // (b h, sub-chunk a) of the call, a = r cp + t
-    const int bh = blk / (m_new * cp), a = blk - bh * (m_new * cp);
-    const int r = a / cp, t = a - r * cp;
+    constexpr int L = D * D + D, NXC = (L + 255) / 256;
+    const int xc = blockIdx.x % NXC, br = blockIdx.x / NXC;   // br = (b h) m_new + r
+    const int bh = br / m_new, r = br - bh * m_new;
+    const int x = xc * 256 + threadIdx.x;
+    if (x >= L) return;
     const float w = W[(size_t)(n_past + r) * (w_dim + 1)];
-    const float* mrec = mixed + ((size_t)bh * m_new + r) * L;
-    const float* sb = ssub + ((size_t)bh * m_new * cp + (size_t)r * cp) * L;
-    auto value = [&](int x) {
-        float acc = 0.f;
-        for (int u = 0; u < t; ++u) acc += sb[(size_t)u * L + x];
-        return mrec[x] + w * acc;
-    };
-    uint16_t* st = St + (size_t)blk * (D * D);
-    for (int u = threadIdx.x; u < D * D / 8; u += 256) {
-        const int e = u % D, c0 = (u / D) * 8;
-        float xv[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) xv[q] = value((c0 + q) * D + e);
-        *reinterpret_cast<u32x4*>(st + e * D + c0) =
-            u32x4{pack_bf16(xv[0], xv[1]), pack_bf16(xv[2], xv[3]), pack_bf16(xv[4], xv[5]), pack_bf16(xv[6], xv[7])};
+    const float m = mixed[(size_t)br * L + x];
+    const float* sb = ssub + (size_t)br * cp * L + x;        // sub-chunk records r cp + t
+    const int c = x / D, e = x - c * D;                       // S element (c, e) for x < D*D
+    float prefix = 0.f;
+    for (int t = 0; t < cp; ++t) {
+        const size_t blk = (size_t)br * cp + t;               // (b h) (m_new cp) + r cp + t
+        const float val = m + w * prefix;
+        if (x < D * D) St[blk * (D * D) + e * D + c] = (uint16_t)(pack_bf16(val, 0.f) & 0xffffu);
+        else Zt[blk * D + (x - D * D)] = val;
+        prefix += sb[(size_t)t * L];
     }
-    if (threadIdx.x < D) Zt[(size_t)blk * D + threadIdx.x] = value(D * D + threadIdx.x);
 }
 
 template <int D, typename T>
@@ -319,8 +316,8 @@ hipError_t run_stream(const StreamLaunch& S) {
             const int nxc = (L + 63) / 64, nrt = (g.M + 15) / 16;
             stream_mix<<<g.BH * nrt * nxc, 256, 0, S.stream>>>(S.W, S.w_dim, S.state, S.max_chunks, S.n_past, g.M,
                                                                 S.mixed, L, D, nullptr, nullptr);
-            stream_sub_operands<D><<<nsub, 256, 0, S.stream>>>(S.mixed, S.ssub, S.W, S.w_dim, S.n_past, g.M, S.cp,
-                                                               S.st, S.zt);
+            stream_sub_operands<D><<<g.BH * g.M * ((L + 255) / 256), 256, 0, S.stream>>>(
+                S.mixed, S.ssub, S.W, S.w_dim, S.n_past, g.M, S.cp, S.st, S.zt);
             Launch La{};
             La.q = q; La.k = k; La.v = v;
             La.W = S.W + (size_t)S.n_past * (S.w_dim + 1);
