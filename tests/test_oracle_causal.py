@@ -42,6 +42,34 @@ def test_causal_blockwise_equals_masked_bruteforce(oracle_lib, case):
     assert rel_err(got, ref) < 1e-12
 
 
+# chunks split along their slowest axis of extent > 1 into cp sub-chunks
+SUBCHUNK_CASES = [
+    ("seq-1d", 1, 2, 8, (1, 64), (1, 16), synth.F32, (1, 4), 4),
+    ("rows-2d", 2, 1, 8, (8, 5), (4, 5), synth.BF16, (2, 5), 2),
+    ("frames-3d", 1, 2, 4, (3, 4, 6), (1, 4, 6), synth.F32, (1, 1, 6), 4),
+]
+
+
+@pytest.mark.parametrize("case", SUBCHUNK_CASES, ids=lambda c: c[0])
+def test_causal_form_over_subchunks_with_repeated_coefficients(oracle_lib, case):
+    """The causal form over chunks with W equals the causal form over
+    sub-chunks (each chunk split into cp contiguous runs) whose coefficient
+    between sub-chunks a and b is W[a // cp][b // cp]: every pair of tokens
+    keeps the weight of its chunks and the mask m <= n.  The library runs
+    long chunks this way."""
+    name, B, H, d, grid, block, dt, sub, cp = case
+    p, (q, k, v, W) = make(case[:7], seed=55)
+    ref = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    Wsub = W[np.arange(W.shape[0] * cp)[:, None] // cp, np.arange(W.shape[0] * cp)[None, :] // cp]
+    got = oracle.forward_causal(q, k, v, np.ascontiguousarray(Wsub, dtype=np.float32), p.grid, sub, eps=p.eps)
+    assert rel_err(got, ref) < 1e-12
+    # and a W that differs between sub-chunks of one chunk changes the result
+    Wbad = Wsub.copy()
+    Wbad[1, 0] += 0.5
+    bad = oracle.forward_causal(q, k, v, np.ascontiguousarray(Wbad, dtype=np.float32), p.grid, sub, eps=p.eps)
+    assert rel_err(bad, ref) > 1e-6
+
+
 def test_one_block_is_causal_linear_attention(oracle_lib):
     case = ("seq", 1, 2, 8, (1, 40), (1, 40), synth.F32)
     p, (q, k, v, _) = make(case, seed=52)
