@@ -87,6 +87,26 @@ def test_backward_small_problems(case):
     check(synth.Problem(name, B, H, d, grid, block, dtype=BF, std=std), seed=41)
 
 
+@pytest.mark.parametrize("case", [("bwd-pairs-d32", 2, 4, 32, (16, 24), (4, 6), 1.0),
+                                  ("bwd-pairs-d32-parts", 1, 6, 32, (32, 32), (16, 16), 0.5)],
+                         ids=lambda c: c[0])
+def test_backward_d32_head_pairs(case, monkeypatch):
+    """head_dim 32 with an even head count: the key/value side reads head pairs
+    as heads of 64 channels with block-diagonal dS.  Each launch against the
+    oracle, and the paired and one-head-per-wave launches bit for bit (the
+    zero blocks add exact zeros to the same products)."""
+    name, B, H, d, grid, block, std = case
+    p = synth.Problem(name, B, H, d, grid, block, dtype=BF, std=std)
+    outs = {}
+    for flag in ("1", "0"):
+        monkeypatch.setenv("MHLA_PAIR_HEADS", flag)
+        run, g, got = check(p, seed=46)
+        outs[flag] = got
+    for a, b in zip(outs["1"], outs["0"]):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
 @pytest.mark.parametrize("case", GENERAL, ids=lambda c: c[0])
 def test_backward_general_path(case):
     name, B, H, d, grid, block, dt = case

@@ -401,7 +401,11 @@ __global__ __launch_bounds__(256) void fold_parts_bf16(const T* __restrict__ par
 //   dv = dS^T a (rows e, k = c: the record's own layout),
 //   dk = (dS v + dz) * phi'(k) (rows c, k = e: the transposed operand).
 // =====================================================================
-template <int D>
+// PAIR (D = 64 only): the problem has head_dim 32 and an even head count; a
+// wave takes heads 2p and 2p + 1 as one head of 64 channels whose dS is the
+// block-diagonal matrix of the two heads' dS (zeros between the heads) and
+// whose dz is the two heads' dz, which gives each head's dk and dv exactly.
+template <int D, bool PAIR = false>
 __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                    const uint16_t* __restrict__ dS, const float* __restrict__ dZ,
                                                    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
@@ -427,8 +431,57 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
     const int blk = (b * g.H + h) * g.M + j;
     uint16_t* sout = lds + wave * (16 * OSTR);
 
+    static_assert(!PAIR || D == 64, "paired heads run the 64-channel layout");
     const uint16_t* mb = dS + (size_t)blk * (D * D);
     u32x4 a3[RT][KS], a4[RT][KS];
+    float dzc[4 * RT];
+    if constexpr (PAIR) {
+        // Records of the two heads (head_dim 32); channel x of the pair is
+        // channel x % 32 of head x / 32.
+        constexpr int DH = 32;
+        const int Hr = 2 * g.H;
+        const uint16_t* mp[2];
+        const float* zp[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const size_t rec = (size_t)(b * Hr + 2 * h + s2) * g.M + j;
+            mp[s2] = dS + rec * (DH * DH);
+            zp[s2] = dZ + rec * DH;
+        }
+        // a3: row e, k = c (8 consecutive c of head kk per lane group)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const u32x4 x = *reinterpret_cast<const u32x4*>(mp[kk] + (e & 31) * DH + gq * 8);
+                const uint32_t m = (e >> 5) == kk ? 0xffffffffu : 0u;
+                a3[r][kk] = u32x4{x[0] & m, x[1] & m, x[2] & m, x[3] & m};
+            }
+        }
+        // a4: row c, k-slot s of k-step kk at e = kk*32 + gq*8 + s (head kk)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int c = 4 * RT * (t >> 2) + 4 * rt + (t & 3);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const bool same = (c >> 5) == kk;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int e0 = gq * 8 + 2 * w;   // within head kk
+                    const uint32_t lo = mp[kk][e0 * DH + (c & 31)], hi = mp[kk][(e0 + 1) * DH + (c & 31)];
+                    a4[rt][kk][w] = same ? (lo | (hi << 16)) : 0u;
+                }
+            }
+        }
+        // dz of channels 4*RT*gq .. +4*RT-1 (all in head gq / 2)
+        const float* zb = zp[gq >> 1] + 4 * RT * (gq & 1);
+#pragma unroll
+        for (int u = 0; u < RT; ++u) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(zb + 4 * u);
+            dzc[4 * u] = x.x; dzc[4 * u + 1] = x.y; dzc[4 * u + 2] = x.z; dzc[4 * u + 3] = x.w;
+        }
+    } else {
     rows_e_k_c<D>(mb, t, gq, a3);
     // a4: row c, k-slot s of k-step kk at e = kk*32 + gq*8 + s (the layout V is loaded in).
 #pragma unroll
@@ -442,12 +495,12 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
                 a4[rt][kk][w] = (uint32_t)mb[e0 * D + c] | ((uint32_t)mb[(e0 + 1) * D + c] << 16);
             }
     }
-    float dzc[4 * RT];
     const float* zb = dZ + (size_t)blk * D;
 #pragma unroll
     for (int u = 0; u < RT; ++u) {
         const f32x4 x = *reinterpret_cast<const f32x4*>(zb + 4 * RT * gq + 4 * u);
         dzc[4 * u] = x.x; dzc[4 * u + 1] = x.y; dzc[4 * u + 2] = x.z; dzc[4 * u + 3] = x.w;
+    }
     }
 
     const int row = g.H * D;
@@ -700,9 +753,29 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
                                                                             B.nsplit, ntj);
     dw_reduce<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, B.dw, g.M * g.M, B.nsplit);
     rec(B, 3);
-    bwd_kv_bf16<D><<<grid_tok, block_tok, 0, L.stream>>>(
-        static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v), B.ds, B.dz,
-        static_cast<uint16_t*>(B.dk), static_cast<uint16_t*>(B.dv), gh);
+    bool paired = false;
+    if constexpr (D == 32) {
+        if (g.H % 2 == 0 && L.tune.pair_heads) {
+            // head pairs read as heads of 64 channels (whole 128-byte rows per lane group)
+            Geo gp = g;
+            gp.H = g.H / 2;
+            gp.D = 64;
+            gp.BH = g.B * gp.H;
+            gp.HG = (gp.H + 7) / 8;
+            gp.G = (gp.H + gp.HG - 1) / gp.HG;
+            gp.div_HG = make_fastdiv((uint32_t)gp.HG);
+            gp.AP = gh.AP;
+            gp.div_AP = gh.div_AP;
+            bwd_kv_bf16<64, true><<<gp.B * gp.M * gp.AP * gp.HG, 64 * gp.G, 0, L.stream>>>(
+                static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v), B.ds, B.dz,
+                static_cast<uint16_t*>(B.dk), static_cast<uint16_t*>(B.dv), gp);
+            paired = true;
+        }
+    }
+    if (!paired)
+        bwd_kv_bf16<D><<<grid_tok, block_tok, 0, L.stream>>>(
+            static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v), B.ds, B.dz,
+            static_cast<uint16_t*>(B.dk), static_cast<uint16_t*>(B.dv), gh);
     rec(B, 4);
     return hipGetLastError();
 }
