@@ -2,12 +2,14 @@
  * mhla_oracle.c -- plain CPU reference of the MHLA forward pass, in float64.
  *
  * TEST INFRASTRUCTURE ONLY (see mhla_oracle.h).  Deliberately simple: scalar
- * loops, float64 accumulation in ascending token / block order, one worker
- * thread per (b, h) pair.  No blocking, fusion or reordering beyond the
+ * loops, float64 accumulation in ascending token / block order; the forward
+ * runs its blocks and (b, h) pairs on worker threads, each element summed in
+ * the same order whatever the thread count.  No blocking, fusion or reordering beyond the
  * method's own blockwise reorganisation (paperlayer.ai summary of
  * arXiv 2601.07832, section 4 "Efficiency": summaries are formed once per
  * block and mixtures once per query block, then reused by every query).
  */
+#define _POSIX_C_SOURCE 200809L
 #include "mhla_oracle.h"
 
 #include <math.h>
@@ -90,104 +92,129 @@ int mhla_oracle_token_blocks(const mhla_oracle_problem* p, int32_t* out) {
     return 0;
 }
 
-/* ---- one (b, h) pair ---- */
+/* ---- the blockwise form in three phases over (pair, block) units ----
+ *
+ * Pairs are taken in batches; within a batch every thread takes units
+ * u = tid, tid + threads, ... of each phase, with a barrier between phases:
+ *   phase 1, unit (s, j): S_j, z_j of pair s from block j's tokens, in
+ *            ascending raster order;
+ *   phase 2, unit (s, i): St_i, zt_i = sum_j W[i,j] S_j (z likewise), j ascending;
+ *   phase 3, unit (s, i): outputs of the tokens of block i.
+ * Every element is summed in the same order whatever the thread count. */
 
 typedef struct {
     const void *q, *k, *v;
     const float* W;
     const mhla_oracle_problem* p;
     const geom* G;
-    /* outputs, each already offset to this pair (may be NULL) */
-    double *out, *S, *z, *St, *zt;
-} pair_job;
+    const int64_t* tok;     /* block j's tokens, ascending: tok[j*T .. j*T + T) */
+    const int32_t* sel;     /* selected pairs (NULL: all, in order) */
+    int32_t nsel, PB;       /* selected pairs, pairs per batch */
+    double *out, *S_out, *z_out, *St_out, *zt_out;   /* caller's outputs (each may be NULL) */
+    double *S, *z, *St, *zt;                         /* batch scratch, [PB][M][...] */
+    int32_t nthreads;
+    pthread_barrier_t* bar;
+} fwd_shared;
 
-static void run_pair(const pair_job* J, int32_t b, int32_t h) {
-    const geom* G = J->G;
-    const int64_t H = J->p->heads, d = J->p->head_dim, N = G->N, M = G->M;
-    const int dt = J->p->dtype;
-    const int64_t row = H * d;                      /* elements per token */
-    const int64_t base = (int64_t)b * N * row + (int64_t)h * d;
+typedef struct {
+    const fwd_shared* F;
+    int32_t tid;
+} fwd_arg;
 
-    double* S = calloc((size_t)(M * d * d), sizeof(double));
-    double* z = calloc((size_t)(M * d), sizeof(double));
-    double* St = calloc((size_t)(M * d * d), sizeof(double));
-    double* zt = calloc((size_t)(M * d), sizeof(double));
-    double* fk = malloc((size_t)d * sizeof(double));
-    double* vv = malloc((size_t)d * sizeof(double));
-    if (!S || !z || !St || !zt || !fk || !vv) abort();
-
-    /* Local key-value summaries, one per block (repost section 5 item (2)):
-     * S_j += phi(k_m) v_m^T and z_j += phi(k_m) for every token m of block j. */
-    for (int64_t m = 0; m < N; ++m) {
-        int64_t j = block_of(G, m);
-        for (int64_t c = 0; c < d; ++c) fk[c] = mhla_oracle_phi(load_elem(J->k, dt, base + m * row + c));
-        for (int64_t e = 0; e < d; ++e) vv[e] = load_elem(J->v, dt, base + m * row + e);
-        double* Sj = S + j * d * d;
+/* Local key-value summary of block j (repost section 5 item (2)):
+ * S_j = sum phi(k_m) v_m^T and z_j = sum phi(k_m) over the block's tokens. */
+static void summary_unit(const fwd_shared* F, int64_t base, int64_t j, double* S, double* z,
+                         double* fk, double* vv) {
+    const int64_t d = F->p->head_dim, row = (int64_t)F->p->heads * d, T = F->G->T;
+    const int dt = F->p->dtype;
+    double* Sj = S + j * d * d;
+    double* zj = z + j * d;
+    memset(Sj, 0, (size_t)(d * d) * sizeof(double));
+    memset(zj, 0, (size_t)d * sizeof(double));
+    for (int64_t r = 0; r < T; ++r) {
+        const int64_t m = F->tok[j * T + r];
+        for (int64_t c = 0; c < d; ++c) fk[c] = mhla_oracle_phi(load_elem(F->k, dt, base + m * row + c));
+        for (int64_t e = 0; e < d; ++e) vv[e] = load_elem(F->v, dt, base + m * row + e);
         for (int64_t c = 0; c < d; ++c) {
-            z[j * d + c] += fk[c];
+            zj[c] += fk[c];
             for (int64_t e = 0; e < d; ++e) Sj[c * d + e] += fk[c] * vv[e];
         }
     }
-
-    /* Multi-head mixing (section 4 "Multi-Head Mixing"): query block i takes
-     * the combination of all local summaries given by row i of W. */
-    for (int64_t i = 0; i < M; ++i) {
-        for (int64_t j = 0; j < M; ++j) {
-            double w = (double)J->W[i * M + j];
-            for (int64_t t = 0; t < d * d; ++t) St[i * d * d + t] += w * S[j * d * d + t];
-            for (int64_t c = 0; c < d; ++c) zt[i * d + c] += w * z[j * d + c];
-        }
-    }
-
-    /* Every query reads its own block's mixed summary:
-     * o_n = phi(q_n)^T St_i / (phi(q_n) . zt_i + eps). */
-    if (J->out) {
-        double* fq = fk;
-        for (int64_t n = 0; n < N; ++n) {
-            int64_t i = block_of(G, n);
-            for (int64_t c = 0; c < d; ++c) fq[c] = mhla_oracle_phi(load_elem(J->q, dt, base + n * row + c));
-            double den = 0.0;
-            for (int64_t c = 0; c < d; ++c) den += fq[c] * zt[i * d + c];
-            den += J->p->eps;
-            for (int64_t e = 0; e < d; ++e) {
-                double num = 0.0;
-                for (int64_t c = 0; c < d; ++c) num += fq[c] * St[i * d * d + c * d + e];
-                J->out[n * d + e] = num / den;
-            }
-        }
-    }
-    if (J->S) memcpy(J->S, S, (size_t)(M * d * d) * sizeof(double));
-    if (J->z) memcpy(J->z, z, (size_t)(M * d) * sizeof(double));
-    if (J->St) memcpy(J->St, St, (size_t)(M * d * d) * sizeof(double));
-    if (J->zt) memcpy(J->zt, zt, (size_t)(M * d) * sizeof(double));
-    free(S); free(z); free(St); free(zt); free(fk); free(vv);
 }
 
-/* ---- thread pool over the selected pairs (static round-robin split) ---- */
-
-typedef struct {
-    const void *q, *k, *v;
-    const float* W;
-    const mhla_oracle_problem* p;
-    const geom* G;
-    const int32_t* sel;
-    int32_t nsel, nthreads, tid;
-    double *out, *S, *z, *St, *zt;
-} worker_arg;
-
-static void* worker(void* arg) {
-    const worker_arg* A = (const worker_arg*)arg;
-    const int64_t N = A->G->N, M = A->G->M, d = A->p->head_dim, H = A->p->heads;
-    for (int32_t s = A->tid; s < A->nsel; s += A->nthreads) {
-        int32_t pair = A->sel ? A->sel[s] : s;
-        pair_job J = {A->q, A->k, A->v, A->W, A->p, A->G, NULL, NULL, NULL, NULL, NULL};
-        if (A->out) J.out = A->out + (int64_t)s * N * d;
-        if (A->S) J.S = A->S + (int64_t)s * M * d * d;
-        if (A->z) J.z = A->z + (int64_t)s * M * d;
-        if (A->St) J.St = A->St + (int64_t)s * M * d * d;
-        if (A->zt) J.zt = A->zt + (int64_t)s * M * d;
-        run_pair(&J, (int32_t)(pair / H), (int32_t)(pair % H));
+/* Multi-head mixing (section 4 "Multi-Head Mixing"): query block i takes the
+ * combination of all local summaries given by row i of W. */
+static void mix_unit(const fwd_shared* F, int64_t i, const double* S, const double* z, double* St, double* zt) {
+    const int64_t d = F->p->head_dim, M = F->G->M;
+    double* Sti = St + i * d * d;
+    double* zti = zt + i * d;
+    memset(Sti, 0, (size_t)(d * d) * sizeof(double));
+    memset(zti, 0, (size_t)d * sizeof(double));
+    for (int64_t j = 0; j < M; ++j) {
+        const double w = (double)F->W[i * M + j];
+        for (int64_t t = 0; t < d * d; ++t) Sti[t] += w * S[j * d * d + t];
+        for (int64_t c = 0; c < d; ++c) zti[c] += w * z[j * d + c];
     }
+}
+
+/* Every query of block i reads its block's mixed summary:
+ * o_n = phi(q_n)^T St_i / (phi(q_n) . zt_i + eps). */
+static void apply_unit(const fwd_shared* F, int64_t base, int64_t i, const double* St, const double* zt,
+                       double* out, double* fq) {
+    const int64_t d = F->p->head_dim, row = (int64_t)F->p->heads * d, T = F->G->T;
+    const int dt = F->p->dtype;
+    const double* Sti = St + i * d * d;
+    const double* zti = zt + i * d;
+    for (int64_t r = 0; r < T; ++r) {
+        const int64_t n = F->tok[i * T + r];
+        for (int64_t c = 0; c < d; ++c) fq[c] = mhla_oracle_phi(load_elem(F->q, dt, base + n * row + c));
+        double den = 0.0;
+        for (int64_t c = 0; c < d; ++c) den += fq[c] * zti[c];
+        den += F->p->eps;
+        for (int64_t e = 0; e < d; ++e) {
+            double num = 0.0;
+            for (int64_t c = 0; c < d; ++c) num += fq[c] * Sti[c * d + e];
+            out[n * d + e] = num / den;
+        }
+    }
+}
+
+static void* fwd_worker(void* arg) {
+    const fwd_arg* A = (const fwd_arg*)arg;
+    const fwd_shared* F = A->F;
+    const int64_t H = F->p->heads, d = F->p->head_dim, N = F->G->N, M = F->G->M;
+    const int64_t rec = M * d * d, zrec = M * d;
+    double* fk = malloc((size_t)d * sizeof(double));
+    double* vv = malloc((size_t)d * sizeof(double));
+    if (!fk || !vv) abort();
+    for (int32_t s0 = 0; s0 < F->nsel; s0 += F->PB) {
+        const int64_t npb = F->nsel - s0 < F->PB ? F->nsel - s0 : F->PB;
+        const int64_t units = npb * M;
+        for (int64_t u = A->tid; u < units; u += F->nthreads) {
+            const int64_t sb = u / M, j = u % M, s = s0 + sb;
+            const int64_t pair = F->sel ? F->sel[s] : s;
+            const int64_t base = (pair / H) * N * H * d + (pair % H) * d;
+            summary_unit(F, base, j, F->S + sb * rec, F->z + sb * zrec, fk, vv);
+        }
+        pthread_barrier_wait(F->bar);
+        for (int64_t u = A->tid; u < units; u += F->nthreads) {
+            const int64_t sb = u / M, i = u % M;
+            mix_unit(F, i, F->S + sb * rec, F->z + sb * zrec, F->St + sb * rec, F->zt + sb * zrec);
+        }
+        pthread_barrier_wait(F->bar);
+        for (int64_t u = A->tid; u < units; u += F->nthreads) {
+            const int64_t sb = u / M, i = u % M, s = s0 + sb;
+            const int64_t pair = F->sel ? F->sel[s] : s;
+            const int64_t base = (pair / H) * N * H * d + (pair % H) * d;
+            if (F->out) apply_unit(F, base, i, F->St + sb * rec, F->zt + sb * zrec, F->out + s * N * d, fk);
+            if (F->S_out) memcpy(F->S_out + s * rec + i * d * d, F->S + sb * rec + i * d * d, (size_t)(d * d) * sizeof(double));
+            if (F->z_out) memcpy(F->z_out + s * zrec + i * d, F->z + sb * zrec + i * d, (size_t)d * sizeof(double));
+            if (F->St_out) memcpy(F->St_out + s * rec + i * d * d, F->St + sb * rec + i * d * d, (size_t)(d * d) * sizeof(double));
+            if (F->zt_out) memcpy(F->zt_out + s * zrec + i * d, F->zt + sb * zrec + i * d, (size_t)d * sizeof(double));
+        }
+        pthread_barrier_wait(F->bar);   /* the batch scratch is reused by the next batch */
+    }
+    free(fk); free(vv);
     return NULL;
 }
 
@@ -205,22 +232,41 @@ static int run_all(const void* q, const void* k, const void* v, const float* W,
     if (nsel > 0 && (!k || !v || !W || (out && !q))) return -1;
     if (threads <= 0) threads = (int32_t)sysconf(_SC_NPROCESSORS_ONLN);
     if (threads < 1) threads = 1;
-    if (threads > nsel) threads = nsel > 0 ? nsel : 1;
+    /* Pairs per batch: enough (pair, block) units for every thread, at most all. */
+    int64_t PB = (8 * (int64_t)threads + G.M - 1) / G.M;
+    if (PB > nsel) PB = nsel > 0 ? nsel : 1;
+    if (threads > PB * G.M) threads = (int32_t)(PB * G.M);
     if (threads_used) *threads_used = threads;
     if (nsel == 0) return 0;
 
+    const int64_t d = p->head_dim, M = G.M, T = G.T;
+    int64_t* tok = malloc((size_t)G.N * sizeof(int64_t));
+    int64_t* fill = calloc((size_t)M, sizeof(int64_t));
+    double* sS = malloc((size_t)(PB * M * d * d) * sizeof(double));
+    double* sz = malloc((size_t)(PB * M * d) * sizeof(double));
+    double* sSt = malloc((size_t)(PB * M * d * d) * sizeof(double));
+    double* szt = malloc((size_t)(PB * M * d) * sizeof(double));
     pthread_t* tids = malloc(sizeof(pthread_t) * (size_t)threads);
-    worker_arg* args = malloc(sizeof(worker_arg) * (size_t)threads);
-    if (!tids || !args) abort();
-    for (int32_t t = 0; t < threads; ++t) {
-        worker_arg a = {q, k, v, W, p, &G, sel, nsel, threads, t, out, S, z, St, zt};
-        args[t] = a;
+    fwd_arg* args = malloc(sizeof(fwd_arg) * (size_t)threads);
+    if (!tok || !fill || !sS || !sz || !sSt || !szt || !tids || !args) abort();
+    /* Token lists: a scan in raster order leaves every block's list ascending. */
+    for (int64_t n = 0; n < G.N; ++n) {
+        const int64_t j = block_of(&G, n);
+        tok[j * T + fill[j]++] = n;
     }
-    for (int32_t t = 1; t < threads; ++t) pthread_create(&tids[t], NULL, worker, &args[t]);
-    worker(&args[0]);
+    pthread_barrier_t bar;
+    pthread_barrier_init(&bar, NULL, (unsigned)threads);
+    fwd_shared F = {q, k, v, W, p, &G, tok, sel, nsel, (int32_t)PB, out, S, z, St, zt,
+                    sS, sz, sSt, szt, threads, &bar};
+    for (int32_t t = 0; t < threads; ++t) {
+        args[t].F = &F;
+        args[t].tid = t;
+    }
+    for (int32_t t = 1; t < threads; ++t) pthread_create(&tids[t], NULL, fwd_worker, &args[t]);
+    fwd_worker(&args[0]);
     for (int32_t t = 1; t < threads; ++t) pthread_join(tids[t], NULL);
-    free(tids);
-    free(args);
+    pthread_barrier_destroy(&bar);
+    free(tok); free(fill); free(sS); free(sz); free(sSt); free(szt); free(tids); free(args);
     return 0;
 }
 

@@ -282,10 +282,19 @@ def test_pair_selection_and_threads(oracle_lib):
     full = oracle.forward(q, k, v, W, p.grid, p.block, threads=1)
     sub, used = oracle.forward(q, k, v, W, p.grid, p.block, pairs=[5, 0, 3], threads=8,
                                return_threads=True)
-    assert used == 3
+    assert used == 8      # 3 pairs x 16 blocks: every thread has (pair, block) units
     for s, pair in enumerate([5, 0, 3]):
         b, h = divmod(pair, 3)
         np.testing.assert_array_equal(sub[s], full[b, :, h])
+    # each element is summed in the same order whatever the thread count
+    for t in (2, 5, 64):
+        np.testing.assert_array_equal(oracle.forward(q, k, v, W, p.grid, p.block, threads=t), full)
+    # one block: 6 (pair, block) units at most, so 6 threads
+    p1 = p.with_(block=p.grid)
+    q1, k1, v1, W1 = synth.make_inputs(p1, seed=14)
+    _, used1 = oracle.forward(q1, k1, v1, W1, p1.grid, p1.block, threads=8, return_threads=True)
+    assert used1 == 6
+
 
 
 # ---------------------------------------------------------------- planted mistakes
