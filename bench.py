@@ -155,6 +155,63 @@ class HipEvents:
         self.made = []
 
 
+def host_cpu():
+    """Host cores this process may run on, and the CPU model from /proc/cpuinfo."""
+    ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return ncpu, model
+
+
+def time_cpu(fn, max_runs=3, single_over_s=10.0):
+    """Best wall time of up to max_runs calls (one call if it takes longer than single_over_s)."""
+    best, runs = None, 0
+    while runs < max_runs:
+        t = time.perf_counter()
+        r = fn()
+        dt = time.perf_counter() - t
+        runs += 1
+        best = dt if best is None else min(best, dt)
+        if dt > single_over_s:
+            break
+    return best, runs, r
+
+
+def measure_copy(torch, nbytes, reps=20):
+    """A plain device-to-device copy of nbytes (read nbytes, write nbytes) on
+    the current stream, rotating over enough buffer pairs that the Infinity
+    Cache cannot serve a copy's source from an earlier one.  Returns
+    (microseconds per copy, GB/s of bytes read plus written)."""
+    sets = max(2, int(np.ceil(2 * MALL_BYTES / (2 * nbytes))) + 1)
+    bufs = [(torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+             torch.empty(nbytes, dtype=torch.uint8, device="cuda")) for _ in range(sets)]
+    for src, _ in bufs:
+        src.fill_(1)
+    stream = torch.cuda.current_stream()
+    for i in range(3):
+        bufs[i % sets][1].copy_(bufs[i % sets][0])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(reps):
+        dst, src = bufs[i % sets][1], bufs[i % sets][0]
+        dst.copy_(src)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / reps
+    del bufs
+    torch.cuda.empty_cache()
+    return us, 2 * nbytes / (us * 1e-6) / 1e9
+
+
 def backward_bytes(p, general=False, causal=False):
     """Algorithmic HBM bytes of each backward stage (compulsory reads + writes).
     The MFMA path keeps the summaries and their gradients as bf16 records; the
@@ -644,23 +701,29 @@ def main():
                 "unit": "GB/s", "frac": kernels[dom]["frac"], "traffic": traffic.get(dom),
                 "avg_us": kernels[dom]["avg_us"], "alg_bytes": kernels[dom]["alg_bytes"]}
 
+    # ---- a plain device copy of the path's compulsory bytes, in the same run
+    copy_us, copy_gbps = measure_copy(torch, U)
+
     # ---- CPU baseline: the float64 oracle on the host cores
     cpu = None
     if not args.no_cpu:
         import oracle
         q, k, v, W = host0
-        ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-        t = time.perf_counter()
+        ncpu, model = host_cpu()
         if args.path == "causal":
-            oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps, threads=ncpu)
-            used = min(ncpu, p.batch * p.heads)   # the oracle runs one thread per (b, h) pair at most
+            dt_cpu, runs, _ = time_cpu(lambda: oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps,
+                                                                     threads=ncpu))
+            used = min(ncpu, p.batch * p.heads)   # the causal oracle runs one thread per (b, h) pair at most
+            how = "causal chunkwise oracle, one thread per (b, h) pair"
         else:
-            _, used = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps, threads=ncpu, return_threads=True)
-        dt_cpu = time.perf_counter() - t
+            dt_cpu, runs, r = time_cpu(lambda: oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps,
+                                                              threads=ncpu, return_threads=True))
+            used = r[1]
+            how = "blockwise oracle, threads over (pair, block) units"
         cpu = {"value": round(p.batch * p.n_tokens / dt_cpu, 1), "unit": "tokens/s", "cores": used,
-               "kind": "oracle", "seconds": round(dt_cpu, 3),
+               "kind": "oracle", "seconds": round(dt_cpu, 3), "host_cores": ncpu, "cpu_model": model,
                "sample": f"the full workload ({p.batch * p.heads} (b,h) pairs, {p.n_tokens} tokens), "
-                         f"float64 {'causal chunkwise' if args.path == 'causal' else 'blockwise'} oracle, one thread per pair"}
+                         f"float64 {how}, best of {runs} runs"}
 
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -672,6 +735,11 @@ def main():
                    "path": args.path, "w": args.w, "input_sets": sets, "parallelism": "none (1 GPU)"},
         "path_hbm_gbps": round(path_gbps, 1), "path_hbm_frac": round(path_gbps / HBM_PEAK_GBPS, 4),
         "path_alg_bytes": U,
+        "copy": {"bytes": U, "us": round(copy_us, 2), "gbps": round(copy_gbps, 1),
+                 "frac_of_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
+                 "what": "device-to-device copy of the path's compulsory byte count (read and written), "
+                         "rotating buffers, same process"},
+        "copy_gbps": round(copy_gbps, 1), "frac_of_copy": round(path_gbps / copy_gbps, 4),
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
