@@ -55,8 +55,8 @@ typedef enum mhla_status {
     MHLA_OK = 0,
     MHLA_ERR_INVALID_ARG = 1,   /* null pointer, bad extents, grid % block != 0, eps < 0 or
                                    not finite, out overlapping an input, workspace too small */
-    MHLA_ERR_UNSUPPORTED = 2,   /* head_dim not in {32, 64, 128}, unknown dtype, or a tensor
-                                   with 2^31 or more elements */
+    MHLA_ERR_UNSUPPORTED = 2,   /* head_dim not in {32, 64, 128}, unknown dtype, a tensor
+                                   with 2^31 or more elements, or M * M >= 2^31 */
     MHLA_ERR_MISALIGNED = 3,    /* q, k, v, W, out or workspace not 16-byte aligned */
     MHLA_ERR_ALLOC = 4,         /* workspace allocation on the stream failed */
     MHLA_ERR_HIP = 5            /* a HIP launch or runtime call failed */
@@ -100,6 +100,20 @@ enum {
                                 bfloat16 or fp32, any head_dim, and blocks that are contiguous
                                 runs of raster indices (e.g. 1D chunks: grid {1, N}, block
                                 {1, T}); MHLA_ERR_UNSUPPORTED otherwise. */
+};
+
+/* Kernel-variant flags, OR-ed into the path argument of mhla_forward_ex and
+ * mhla_launch_plan.  They choose among kernels that compute the same result
+ * (for tests and comparisons); problems a variant does not apply to ignore
+ * it.  An unknown flag, or both mixing flags, gives MHLA_ERR_INVALID_ARG.
+ * Without flags the library picks the variant for the problem. */
+enum {
+    MHLA_VARIANT_MIX_RESIDENT = 1 << 8,   /* bf16, at most 256 source records: persistent mixing
+                                             kernel, one workgroup per compute unit, W in registers */
+    MHLA_VARIANT_MIX_TILED = 1 << 9,      /* bf16: mixing with one workgroup per column tile of
+                                             every query block (any M) */
+    MHLA_VARIANT_NO_PAIR_HEADS = 1 << 10  /* bf16, head_dim 32, even head count: one head per wave
+                                             in the summary kernel instead of head pairs */
 };
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -171,7 +185,8 @@ mhla_status mhla_forward_ws(const void* q, const void* k, const void* v, const f
                             const mhla_grid* grid, const mhla_block* block, void* out,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* As mhla_forward_ws, with a path choice (MHLA_PATH_*) and optional stage
+/* As mhla_forward_ws, with a path choice (MHLA_PATH_*, optionally OR-ed with
+ * MHLA_VARIANT_* flags) and optional stage
  * events.  If stage_events is non-NULL it points to 4 hipEvent_t handles
  * created by the caller; they are recorded on `stream` before the first
  * kernel, after the summary kernel, after the mixing kernel (right after
@@ -236,6 +251,15 @@ mhla_status mhla_backward(const void* q, const void* k, const void* v, const flo
                           const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
                           float* dW, void* ws, size_t ws_bytes, const hipEvent_t* stage_events,
                           hipStream_t stream);
+
+/* As mhla_backward, with kernel-variant flags: 0 or MHLA_VARIANT_NO_PAIR_HEADS
+ * (head_dim 32, even head count: the key/value-side kernel takes one head per
+ * wave instead of head pairs; same result).  Other flags give
+ * MHLA_ERR_INVALID_ARG. */
+mhla_status mhla_backward_ex(const void* q, const void* k, const void* v, const float* W, const void* dout,
+                             const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
+                             float* dW, void* ws, size_t ws_bytes, int32_t variant,
+                             const hipEvent_t* stage_events, hipStream_t stream);
 
 /* ---------------------------------------------------------------- causal backward
  *

@@ -54,7 +54,7 @@ class Run:
         torch.cuda.synchronize()
         return out
 
-    def backward(self, dout_host, stream=None, ws=True, causal=False):
+    def backward(self, dout_host, stream=None, ws=True, causal=False, variant=0):
         """Gradients through mhla_backward (mhla_causal_backward if causal):
         (dq, dk, dv) device tensors like q and dW [M, M] fp32."""
         p = self.p
@@ -67,8 +67,13 @@ class Run:
         wsb = wsize(self.g, self.b)
         wst = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda") if ws else None
         say(f"  [gpu] {call.__name__} {p.name} B{p.batch} H{p.heads} d{p.head_dim} grid{p.grid} block{p.block}")
-        st = call(self.q, self.k, self.v, self.W, dout, self.g, self.b, dq, dk, dv, dW,
-                  wst, wsb if ws else 0, None, stream)
+        if variant:
+            say(f"  [gpu] mhla_backward_ex variant={variant:#x}")
+            st = mh.mhla_backward_ex(self.q, self.k, self.v, self.W, dout, self.g, self.b, dq, dk, dv, dW,
+                                     wst, wsb if ws else 0, variant, None, stream)
+        else:
+            st = call(self.q, self.k, self.v, self.W, dout, self.g, self.b, dq, dk, dv, dW,
+                      wst, wsb if ws else 0, None, stream)
         assert st == mh.MHLA_OK, mh.mhla_status_string(st)
         torch.cuda.synchronize()
         return dq, dk, dv, dW

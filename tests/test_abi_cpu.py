@@ -71,8 +71,10 @@ def test_workspace_bytes_layout(L):
     (lambda g, b: b.extent.__setitem__(1, 0), mh.MHLA_ERR_INVALID_ARG),
     (lambda g, b: g.extent.__setitem__(0, -256), mh.MHLA_ERR_INVALID_ARG),
     (lambda g, b: setattr(g, "batch", 1 << 20), mh.MHLA_ERR_UNSUPPORTED),     # >= 2^31 elements
+    (lambda g, b: (b.extent.__setitem__(0, 1), b.extent.__setitem__(1, 1)),  # M = 65536: M * M >= 2^31
+     mh.MHLA_ERR_UNSUPPORTED),
 ], ids=["d48", "dtype", "ndim4", "ndim1", "neg-batch", "neg-eps", "nan-eps", "inf-eps",
-        "not-divisible", "zero-block", "neg-extent", "too-large"])
+        "not-divisible", "zero-block", "neg-extent", "too-large", "M-squared"])
 def test_problem_validation(L, mut, code):
     g, b = cfg2()
     mut(g, b)
@@ -131,6 +133,26 @@ def test_empty_problem_is_a_no_op(L):
         assert call_fwd(L, g, b, q=None, k=None, v=None, W=None, out=None) == mh.MHLA_OK
         assert call_fwd(L, g, b, q=None, k=None, v=None, W=None, out=None, entry="ws") == mh.MHLA_OK
         assert L.mhla_forward(None, None, None, None, ctypes.byref(g), ctypes.byref(b), None, None) == mh.MHLA_OK
+
+
+def test_variant_flags(L):
+    """Kernel-variant flags ride in the path argument; unknown bits and both
+    mixing flags at once are rejected before any HIP call."""
+    g, b = cfg2()
+    three = ["block_kv_summary", "mix_summaries", "query_apply"]
+    for flag in (mh.MHLA_VARIANT_MIX_RESIDENT, mh.MHLA_VARIANT_MIX_TILED, mh.MHLA_VARIANT_NO_PAIR_HEADS):
+        assert mh.mhla_launch_plan(g, b, mh.MHLA_PATH_3KERNEL | flag) == (mh.MHLA_OK, three)
+    both = mh.MHLA_VARIANT_MIX_RESIDENT | mh.MHLA_VARIANT_MIX_TILED
+    need = mh.mhla_workspace_bytes(g, b)
+    for bad in (1 << 12, 1 << 30, both):
+        assert mh.mhla_launch_plan(g, b, bad)[0] == mh.MHLA_ERR_INVALID_ARG
+        assert call_fwd(L, g, b, ws=6 * BIG, ws_bytes=need, path=bad) == mh.MHLA_ERR_INVALID_ARG
+    # the backward takes only the head-pair flag
+    bneed = mh.mhla_backward_workspace_bytes(g, b)
+    for bad in (mh.MHLA_VARIANT_MIX_TILED, 1 << 12):
+        assert L.mhla_backward_ex(BIG, 2 * BIG, 3 * BIG, 4 * BIG, 5 * BIG, ctypes.byref(g), ctypes.byref(b),
+                                  6 * BIG, 7 * BIG, 8 * BIG, 9 * BIG, 10 * BIG, bneed, bad, None,
+                                  None) == mh.MHLA_ERR_INVALID_ARG
 
 
 def test_launch_plan(L):

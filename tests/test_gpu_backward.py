@@ -57,12 +57,12 @@ def upstream(p, seed):
     return synth.bf16_bits(g) if p.dtype == BF else g
 
 
-def check(p, seed):
+def check(p, seed, variant=0):
     q, k, v, W = synth.make_inputs(p, seed=seed)
     g = upstream(p, seed + 1000)
     ref = oracle.backward(q, k, v, W, g, p.grid, p.block, eps=p.eps)
     run = Run(p, q, k, v, W)
-    got = run.backward(g)
+    got = run.backward(g, variant=variant)
     for name, a, r in zip(("dq", "dk", "dv", "dW"), got, ref):
         a = to_host64(a)
         assert np.isfinite(a).all(), name
@@ -90,7 +90,7 @@ def test_backward_small_problems(case):
 @pytest.mark.parametrize("case", [("bwd-pairs-d32", 2, 4, 32, (16, 24), (4, 6), 1.0),
                                   ("bwd-pairs-d32-parts", 1, 6, 32, (32, 32), (16, 16), 0.5)],
                          ids=lambda c: c[0])
-def test_backward_d32_head_pairs(case, monkeypatch):
+def test_backward_d32_head_pairs(case):
     """head_dim 32 with an even head count: the key/value side reads head pairs
     as heads of 64 channels with block-diagonal dS.  Each launch against the
     oracle, and the paired and one-head-per-wave launches bit for bit (the
@@ -99,8 +99,7 @@ def test_backward_d32_head_pairs(case, monkeypatch):
     p = synth.Problem(name, B, H, d, grid, block, dtype=BF, std=std)
     outs = {}
     for flag in ("1", "0"):
-        monkeypatch.setenv("MHLA_PAIR_HEADS", flag)
-        run, g, got = check(p, seed=46)
+        run, g, got = check(p, seed=46, variant=0 if flag == "1" else mh.MHLA_VARIANT_NO_PAIR_HEADS)
         outs[flag] = got
     for a, b in zip(outs["1"], outs["0"]):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,

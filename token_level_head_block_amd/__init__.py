@@ -33,6 +33,10 @@ MHLA_PATH_3KERNEL = 0
 MHLA_PATH_FUSED = 1
 MHLA_PATH_CAUSAL = 2
 
+MHLA_VARIANT_MIX_RESIDENT = 1 << 8
+MHLA_VARIANT_MIX_TILED = 1 << 9
+MHLA_VARIANT_NO_PAIR_HEADS = 1 << 10
+
 MHLA_PHI_ELU1 = 0
 MHLA_PHI_RELU_EPS = 1
 
@@ -86,6 +90,9 @@ def lib() -> ctypes.CDLL:
         L.mhla_backward_workspace_bytes.restype = ctypes.c_size_t
         L.mhla_backward.argtypes = [vp, vp, vp, vp, vp, G, Bk, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
         L.mhla_backward.restype = ctypes.c_int
+        L.mhla_backward_ex.argtypes = [vp, vp, vp, vp, vp, G, Bk, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                       ctypes.c_int32, vp, vp]
+        L.mhla_backward_ex.restype = ctypes.c_int
         L.mhla_causal_backward_workspace_bytes.argtypes = [G, Bk]
         L.mhla_causal_backward_workspace_bytes.restype = ctypes.c_size_t
         L.mhla_causal_backward.argtypes = [vp, vp, vp, vp, vp, G, Bk, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
@@ -259,6 +266,16 @@ def mhla_backward(q, k, v, W, dout, grid: mhla_grid, block: mhla_block, dq, dk, 
     return lib().mhla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dout), ctypes.byref(grid),
                                ctypes.byref(block), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), _ptr(ws),
                                int(ws_bytes), _events(stage_events, 5), _stream(stream))
+
+
+def mhla_backward_ex(q, k, v, W, dout, grid: mhla_grid, block: mhla_block, dq, dk, dv, dW, ws=None,
+                     ws_bytes: int = 0, variant: int = 0, stage_events=None, stream=None) -> int:
+    """As mhla_backward, with MHLA_VARIANT_* flags (MHLA_VARIANT_NO_PAIR_HEADS)."""
+    _check_tensors(q, k, v, W, dout, grid, block)
+    _check_tensors(dq, dk, dv, dW, None, grid, block)
+    return lib().mhla_backward_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(W), _ptr(dout), ctypes.byref(grid),
+                                  ctypes.byref(block), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dW), _ptr(ws),
+                                  int(ws_bytes), int(variant), _events(stage_events, 5), _stream(stream))
 
 
 def mhla_causal_backward_workspace_bytes(grid: mhla_grid, block: mhla_block) -> int:

@@ -45,11 +45,14 @@ __device__ __forceinline__ void pipelined(int first, int step, int n, LoadF&& lo
 // W (fp32 [M][M]) -> bf16, zero padded to [Ipad = 64 * IT][Jpad = 32 * NK] and
 // stored in the mixing kernel's B-operand order: 16-byte unit
 // (rt * NK + kk) * 64 + lane holds W[16 * rt + lane % 16][32 * kk + 8 * (lane / 16) + 0..7],
-// so each wave's operand loads are contiguous.  Done by extra workgroups
-// appended to the summary launch, so the summary workgroups never wait on it.
+// so each wave's operand loads are contiguous.  Done by extra workgroups at
+// the end of the summary launch, one 16-byte unit per thread, so they start on
+// the compute units the first summary workgroups leave and finish before the
+// last ones (placed first, they would hold compute units that summary
+// workgroups wait for).
 struct WConv {
     int32_t M, NK, nchunks;   // NK = Jpad / 32; nchunks = Ipad * Jpad / 8; 0 = none
-    int32_t first_wg;         // workgroups [first_wg, gridDim.x) convert
+    int32_t first_wg, nconv;  // workgroups [first_wg, first_wg + nconv) of the launch convert
     uint16_t* wbt;            // if not null, W^T is converted to this buffer as well
     int32_t causal;           // nonzero: keep only W[i][j] with j < i (earlier blocks)
     int32_t TP;               // token parts: column j' of the operand is W[i][j' / TP] (j' < M TP)
@@ -59,7 +62,7 @@ struct WConv {
 
 __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t* __restrict__ Wb,
                                           const WConv& wc) {
-    const int nthr = (gridDim.x - wc.first_wg) * blockDim.x;
+    const int nthr = wc.nconv * blockDim.x;
     const int total = wc.nchunks + (wc.wbt ? wc.nchunks_t : 0);
     for (int c0 = (blockIdx.x - wc.first_wg) * blockDim.x + threadIdx.x; c0 < total; c0 += nthr) {
         const bool tr = c0 >= wc.nchunks;   // the chunks of W^T follow those of W

@@ -396,6 +396,159 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
 }
 
 // =====================================================================
+// mix_split: the same product with one workgroup of 4 waves per (pair,
+// column tile of 64 record elements, tile of 64*TR query blocks), so that
+// several workgroups share a compute unit and their load latencies overlap.
+// Wave w computes query blocks 16*TR*w .. 16*TR*w + 16*TR - 1 of the tile
+// with its W operands for every k-step held in registers; the A operand (the
+// column tile of every source record) is staged once per workgroup in LDS,
+// already packed as MFMA operands.  Workgroups are dealt to the XCDs
+// round-robin, so tiles are numbered such that the query-block tiles of one
+// column tile run back to back on one XCD and all but the first read the
+// column tile from that XCD's L2.  Lane roles, operand packing and output
+// mapping are those of mix_summaries.  At most 256 source records (NK <= 8).
+// NT bit 1: mixed summaries stored with the non-temporal hint.
+// =====================================================================
+struct SplitGeo {
+    int32_t CT;          // column tiles of 64 record elements per pair
+    int32_t NC;          // column tiles over all pairs (BH * CT)
+    FastDiv div_CT, div_NI;   // NI: query-block tiles per column tile
+};
+
+template <int D, int TR, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void mix_split_bf16(const uint16_t* __restrict__ SZ,
+                                                      const uint16_t* __restrict__ Wb,
+                                                      uint16_t* __restrict__ St, float* __restrict__ Zt,
+                                                      const Geo g, const SplitGeo sg) {
+    constexpr int REC = D * D + D;
+    constexpr int KMAX = 8;            // k-steps (32 source records each)
+    constexpr int OROW = MIX_OROW;
+    constexpr int ROWS = 16 * TR;      // query blocks per wave
+    __shared__ u32x4 sA[4 * KMAX * 64];   // A operands [r][kk][lane], 32 KB; then output staging
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, gq = lane >> 4;
+    const uint32_t slot = blockIdx.x >> 3;
+    const uint32_t cslot = fdiv(slot, sg.div_NI);
+    const int itile = (int)(slot - cslot * sg.div_NI.d);
+    const uint32_t c = cslot * 8u + (blockIdx.x & 7u);
+    if (c >= (uint32_t)sg.NC) return;
+    const uint32_t bh = fdiv(c, sg.div_CT);
+    const int cp0 = (int)(c - bh * sg.div_CT.d) * 64;   // first record element of the tile
+    const int M = g.M, MS = g.M * g.TP, NK = (MS + 31) >> 5;
+    const int i0 = itile * (4 * ROWS) + wave * ROWS;    // first query block of this wave
+    const bool active = i0 < M;                         // then i0 + ROWS <= roundup(M, 32): inside Wb's rows
+    const int rt0 = active ? i0 >> 4 : 0;
+
+    // ---- W operands (B) of every k-step; positions past NK reload a valid step.
+    u32x4 bw[KMAX][TR];
+#pragma unroll
+    for (int kk = 0; kk < KMAX; ++kk)
+#pragma unroll
+        for (int t = 0; t < TR; ++t)
+            bw[kk][t] = *reinterpret_cast<const u32x4*>(
+                Wb + ((size_t)((rt0 + t) * NK + (kk < NK ? kk : NK - 1)) * 64 + lane) * 8);
+
+    // ---- stage A: unit (li', group of 8 source records) -> 4 packed operands.
+    const int units = 16 * 4 * NK;                      // <= 512: at most two per thread
+    const uint16_t* base = SZ + (size_t)bh * MS * REC;
+    u32x2 raw[2][8];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int u = tid + 256 * p;
+        const int colp = cp0 + 4 * (u & 15);
+        const bool ok = u < units && colp < REC;
+        const int colc = ok ? colp : 0;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            // Clamped address, then a mask: the load stays unconditional.
+            const int jj = 8 * (u >> 4) + s;
+            const u32x2 t = *reinterpret_cast<const u32x2*>(base + (size_t)(jj < MS ? jj : MS - 1) * REC + colc);
+            const uint32_t m = (ok && jj < MS) ? 0xffffffffu : 0u;
+            raw[p][s] = u32x2{t.x & m, t.y & m};
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int u = tid + 256 * p;
+        if (u < units) {
+            const int jg = u >> 4, kk = jg >> 2, lanep = (jg & 3) * 16 + (u & 15);
+            u32x4 op[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                op[0][w] = pack_lo(raw[p][2 * w].x, raw[p][2 * w + 1].x);
+                op[1][w] = pack_hi(raw[p][2 * w].x, raw[p][2 * w + 1].x);
+                op[2][w] = pack_lo(raw[p][2 * w].y, raw[p][2 * w + 1].y);
+                op[3][w] = pack_hi(raw[p][2 * w].y, raw[p][2 * w + 1].y);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sA[(r * NK + kk) * 64 + lanep] = op[r];
+        }
+    }
+    __syncthreads();
+
+    f32x4 acc[4][TR];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < TR; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (active) {
+#pragma unroll
+        for (int kk = 0; kk < KMAX; ++kk) {
+            if (kk >= NK) break;
+            u32x4 a[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = sA[(r * NK + kk) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < TR; ++t) acc[r][t] = mfma_bf16(a[r], bw[kk][t], acc[r][t]);
+        }
+    }
+    __syncthreads();   // every wave is done with the A operands
+    if (!active) return;
+
+    // ---- output.  Lane holds C[col' = cp0 + 16*gq + 4*v + r][i = i0 + 16*t + li].
+    if (cp0 < D * D) {
+        // The wave's own LDS slice: written and read back by this wave only.
+        uint16_t* stage = reinterpret_cast<uint16_t*>(sA) + wave * (ROWS * OROW);
+#pragma unroll
+        for (int t = 0; t < TR; ++t) {
+            uint32_t wv[8];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                wv[2 * v] = pack_bf16(acc[0][t][v], acc[1][t][v]);
+                wv[2 * v + 1] = pack_bf16(acc[2][t][v], acc[3][t][v]);
+            }
+            uint16_t* dst = stage + (16 * t + li) * OROW + 16 * gq;
+            *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+        }
+        // ROWS rows of 128 bytes: 8 lanes per row, 8 rows per instruction.
+#pragma unroll
+        for (int k = 0; k < ROWS / 8; ++k) {
+            const int rl = 8 * k + (lane >> 3), chunk = lane & 7;
+            const int i = i0 + rl;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rl * OROW + chunk * 8);
+            u32x4* dst = reinterpret_cast<u32x4*>(St + ((size_t)bh * M + i) * (D * D) + cp0 + chunk * 8);
+            if (i < M) {
+                if constexpr ((NT & 2) != 0) __builtin_nontemporal_store(x, dst);
+                else *dst = x;
+            }
+        }
+    } else if (cp0 + 16 * gq < REC) {
+#pragma unroll
+        for (int t = 0; t < TR; ++t) {
+            const int i = i0 + 16 * t + li;
+            if (i >= M) continue;
+            float* dst = Zt + ((size_t)bh * M + i) * D + (cp0 + 16 * gq - D * D);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                *reinterpret_cast<f32x4*>(dst + 4 * v) = f32x4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
+        }
+    }
+}
+
+// =====================================================================
 // query_apply: O^T = St_i^T phi(Q)^T per 16-token group.
 // A = St_i^T (rows e, k = c) stays in registers for the whole block; row ii of
 // row-tile r is e = 4*RT*(ii/4) + 4r + ii%4, so each lane ends with 4*RT
@@ -695,9 +848,10 @@ void launch_summary(const Launch& L, const uint16_t* k, const uint16_t* v, uint1
     const Geo g = with_head_groups(gp, NQ);
     const int nsum = g.B * g.M * g.TP * g.HG, threads = 64 * NQ * g.G;
     WConv w = wc;
-    w.first_wg = nsum;
     const int nchunks = wc.nchunks + (wc.wbt ? wc.nchunks_t : 0);
-    const int nconv = (nchunks + threads * 4 - 1) / (threads * 4);   // up to 4 chunks per thread
+    const int nconv = (nchunks + threads - 1) / threads;   // one chunk per thread
+    w.first_wg = nsum;
+    w.nconv = nconv;
     if (L.tune.nt_loads)
         block_kv_summary_bf16<D, PF, ROW8, FULL, true, PAIR><<<nsum + nconv, threads, 0, L.stream>>>(
             k, v, sz, g, L.W, static_cast<uint16_t*>(L.wb), w);
@@ -728,6 +882,14 @@ void launch_apply_pf(const Launch& L, const uint16_t* q, const uint16_t* st, uin
 
 template <int D, int NWA>
 void launch_apply(const Launch& L, const uint16_t* q, const uint16_t* st, uint16_t* o) {
+    if constexpr (NWA <= 2) {
+        if (L.tune.apply_maxw == 2) {
+            if (L.tune.apply_pf == 1) launch_apply_pf<D, NWA, 1, 2>(L, q, st, o);
+            else if (L.tune.apply_pf == 2) launch_apply_pf<D, NWA, 2, 2>(L, q, st, o);
+            else launch_apply_pf<D, NWA, 4, 2>(L, q, st, o);
+            return;
+        }
+    }
     if (L.tune.apply_maxw == 4) {
         if (L.tune.apply_pf == 1) launch_apply_pf<D, NWA, 1, 4>(L, q, st, o);
         else launch_apply_pf<D, NWA, 2, 4>(L, q, st, o);
@@ -772,6 +934,7 @@ hipError_t run_d(const Launch& L0) {
     wc.WD = g.WD;
     wc.WM = g.WM;
     wc.first_wg = 0;
+    wc.nconv = 0;
     wc.wbt = static_cast<uint16_t*>(L.wbt);
     const bool causal = L.path == MHLA_PATH_CAUSAL;
     wc.causal = causal ? 1 : 0;   // mixed summaries of earlier blocks only
@@ -804,7 +967,25 @@ hipError_t run_d(const Launch& L0) {
         mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
         mg.Jpad = NK * 32;
         mg.div_CTG = make_fastdiv(mg.CTG);
-        if (L.tune.mix_resident && IT <= 4 && NK <= 8) {
+        if (L.tune.mix_kind == 2 && NK <= 8) {
+            SplitGeo sg;
+            sg.CT = mg.CT;
+            sg.NC = g.BH * mg.CT;
+            sg.div_CT = make_fastdiv((uint32_t)mg.CT);
+            const int tr = (g.M <= 64 || L.tune.mix_rows == 1) ? 1 : 2;
+            const int ni = (g.M + 64 * tr - 1) / (64 * tr);
+            sg.div_NI = make_fastdiv((uint32_t)ni);
+            const int grid = 8 * ni * ((sg.NC + 7) / 8);
+            const auto* wbp = static_cast<const uint16_t*>(L.wb);
+            const bool nt = (L.tune.nt_mix & 2) != 0;
+            if (tr == 1) {
+                if (nt) mix_split_bf16<D, 1, 2><<<grid, 256, 0, L.stream>>>(sz, wbp, st, L.zt, g, sg);
+                else mix_split_bf16<D, 1, 0><<<grid, 256, 0, L.stream>>>(sz, wbp, st, L.zt, g, sg);
+            } else {
+                if (nt) mix_split_bf16<D, 2, 2><<<grid, 256, 0, L.stream>>>(sz, wbp, st, L.zt, g, sg);
+                else mix_split_bf16<D, 2, 0><<<grid, 256, 0, L.stream>>>(sz, wbp, st, L.zt, g, sg);
+            }
+        } else if (L.tune.mix_kind == 1 && IT <= 4 && NK <= 8) {
             // NK <= 8: at most 256 source records (M <= 256, M * TP <= 256).
             const int units = g.BH * mg.CTG;
             const int grid = units < L.tune.num_cus ? units : L.tune.num_cus;

@@ -18,7 +18,9 @@ struct Tuning {
     int nt_loads;        // bf16 path: non-temporal hint on the loads of k, v (summary kernel)
     int nt_apply;        // bf16 path: non-temporal hint on the loads of q (apply kernel)
     int nt_mix;          // bf16 persistent mixing kernel: 1 = non-temporal summary loads, 2 = non-temporal stores of St
-    int mix_resident;    // bf16 path, M <= 256: persistent mixing kernel with W in registers
+    int mix_kind;        // bf16 path, M <= 256: 2 = mix_split (workgroup per tile), 1 = persistent
+                         // mix_resident with W in registers, 0 = mix_summaries (any M)
+    int mix_rows;        // mix_split: query blocks per wave / 16 (1 or 2; 0 = by M)
     int num_cus;         // compute units of the current device (persistent grid size)
 };
 

@@ -57,6 +57,8 @@ mhla_status check(const mhla_grid* grid, const mhla_block* block, Shape* s) {
     if ((double)s->B * (double)s->N * (double)s->H * (double)s->D >= lim) return MHLA_ERR_UNSUPPORTED;
     if ((double)s->B * (double)s->H * (double)s->M * (double)(s->D * s->D + s->D) >= lim)
         return MHLA_ERR_UNSUPPORTED;
+    // W and dW hold M * M values, counted in 32-bit integers by the kernels.
+    if ((double)s->M * (double)s->M >= lim) return MHLA_ERR_UNSUPPORTED;
     // One batch item's tensor must also fit a 2^31-byte buffer range.
     if ((double)s->N * (double)s->H * (double)s->D * (double)s->esz >= lim) return MHLA_ERR_UNSUPPORTED;
     return MHLA_OK;
@@ -194,14 +196,19 @@ mhla::Tuning choose_tuning(const Shape& s) {
     t.bwdq_heads = env_int("MHLA_BWDQ_HEADS", 0);
     if (t.bwdq_heads < 0 || t.bwdq_heads > 4) t.bwdq_heads = 0;
     const int am = env_int("MHLA_APPLY_MAXW", 0);
-    if (am == 4 || am == 8) t.apply_maxw = am;
+    if (am == 4 || am == 8 || (am == 2 && t.apply_waves <= 2)) t.apply_maxw = am;
     // Non-temporal loads: faster for the summary kernel's k, v stream.  On
     // the apply kernel's q stream they cost the apply about 1 us at d <= 64
     // but the following summary launch runs 2-5 us faster, so a repeated
     // forward gains; at d = 128 the apply loses 6 us (measured on MI355X).
     t.nt_loads = env_int("MHLA_NT_LOADS", 1) != 0;
     t.nt_apply = env_int("MHLA_NT_APPLY", s.D <= 64 ? 1 : 0) != 0;
-    t.mix_resident = env_int("MHLA_MIX_RESIDENT", 1) != 0;
+    // Mixing kernel: one workgroup per (pair, column tile, query-block tile)
+    // by default; MHLA_MIX selects another for sweeps (flags of
+    // mhla_forward_ex select one per call).
+    t.mix_kind = env_int("MHLA_MIX", 2);
+    if (t.mix_kind < 0 || t.mix_kind > 2) t.mix_kind = 2;
+    t.mix_rows = env_int("MHLA_MIX_ROWS", 0);
     // Non-temporal stores of the mixed summaries: mixing 12.7 -> 11.7 us at
     // dit-s2-256x256 (T = 256, the apply unchanged), video-16x64x64 307 us
     // per step against 308; at T = 64 the apply waits longer for St (one
@@ -237,15 +244,33 @@ mhla::Geo make_geo(const Shape& s, float eps) {
     return g;
 }
 
+// The path argument of mhla_forward_ex: a MHLA_PATH_* value in the low 8 bits
+// and MHLA_VARIANT_* flags above them.
+constexpr int32_t kVariantMask = MHLA_VARIANT_MIX_RESIDENT | MHLA_VARIANT_MIX_TILED | MHLA_VARIANT_NO_PAIR_HEADS;
+
+bool split_path(int32_t arg, int32_t* path, int32_t* variant) {
+    *path = arg & 0xff;
+    *variant = arg & ~0xff;
+    if (*variant & ~kVariantMask) return false;
+    if ((*variant & MHLA_VARIANT_MIX_RESIDENT) && (*variant & MHLA_VARIANT_MIX_TILED)) return false;
+    return *path == MHLA_PATH_3KERNEL || *path == MHLA_PATH_FUSED || *path == MHLA_PATH_CAUSAL;
+}
+
+void apply_variant(mhla::Tuning& t, int32_t variant) {
+    if (variant & MHLA_VARIANT_MIX_RESIDENT) t.mix_kind = 1;
+    if (variant & MHLA_VARIANT_MIX_TILED) t.mix_kind = 0;
+    if (variant & MHLA_VARIANT_NO_PAIR_HEADS) t.pair_heads = 0;
+}
+
 mhla_status forward_impl(const void* q, const void* k, const void* v, const float* W,
                          const mhla_grid* grid, const mhla_block* block, void* out, void* ws,
-                         size_t ws_bytes, bool allow_alloc, int32_t path,
+                         size_t ws_bytes, bool allow_alloc, int32_t path_arg,
                          const hipEvent_t* events, hipStream_t stream) {
     Shape s;
     mhla_status st = check(grid, block, &s);
     if (st != MHLA_OK) return st;
-    if (path != MHLA_PATH_3KERNEL && path != MHLA_PATH_FUSED && path != MHLA_PATH_CAUSAL)
-        return MHLA_ERR_INVALID_ARG;
+    int32_t path = 0, variant = 0;
+    if (!split_path(path_arg, &path, &variant)) return MHLA_ERR_INVALID_ARG;
     if (path == MHLA_PATH_CAUSAL && !causal_supported(s)) return MHLA_ERR_UNSUPPORTED;
     if (s.B == 0 || s.H == 0) return MHLA_OK;
     if (!q || !k || !v || !W || !out) return MHLA_ERR_INVALID_ARG;
@@ -292,6 +317,7 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
         }
     }
     L.tune = choose_tuning(s);
+    apply_variant(L.tune, variant);
     {
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
@@ -386,10 +412,11 @@ GenLayout gen_layout(const Shape& s, bool causal = false) {
 mhla_status backward_impl(const void* q, const void* k, const void* v, const float* W, const void* dout,
                           const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
                           float* dW, void* ws, size_t ws_bytes, const hipEvent_t* events, hipStream_t stream,
-                          bool causal) {
+                          bool causal, int32_t variant = 0) {
     Shape s;
     mhla_status st = check(grid, block, &s);
     if (st != MHLA_OK) return st;
+    if (variant & ~MHLA_VARIANT_NO_PAIR_HEADS) return MHLA_ERR_INVALID_ARG;
     if (causal && !causal_supported(s)) return MHLA_ERR_UNSUPPORTED;
     const bool fast = !causal && bwd_supported(s);
     if (!dW) return MHLA_ERR_INVALID_ARG;
@@ -471,6 +498,7 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
     L.g = make_geo(s, grid->eps);
     set_token_parts(L.g, s);   // the recompute's summaries in token parts (regions sized for them)
     L.tune = choose_tuning(s);
+    apply_variant(L.tune, variant);
     L.path = MHLA_PATH_3KERNEL;
     L.summaries_only = 1;
     L.events = nullptr;
@@ -741,6 +769,14 @@ mhla_status mhla_backward(const void* q, const void* k, const void* v, const flo
                          false);
 }
 
+mhla_status mhla_backward_ex(const void* q, const void* k, const void* v, const float* W, const void* dout,
+                             const mhla_grid* grid, const mhla_block* block, void* dq, void* dk, void* dv,
+                             float* dW, void* ws, size_t ws_bytes, int32_t variant,
+                             const hipEvent_t* stage_events, hipStream_t stream) {
+    return backward_impl(q, k, v, W, dout, grid, block, dq, dk, dv, dW, ws, ws_bytes, stage_events, stream,
+                         false, variant);
+}
+
 size_t mhla_causal_backward_workspace_bytes(const mhla_grid* grid, const mhla_block* block) {
     Shape s;
     if (check(grid, block, &s) != MHLA_OK || s.B == 0 || s.H == 0 || !causal_supported(s)) return 0;
@@ -790,13 +826,13 @@ mhla_status mhla_check_problem(const mhla_grid* grid, const mhla_block* block, i
     return st;
 }
 
-mhla_status mhla_launch_plan(const mhla_grid* grid, const mhla_block* block, int32_t path,
+mhla_status mhla_launch_plan(const mhla_grid* grid, const mhla_block* block, int32_t path_arg,
                              int32_t* num_kernels, const char** kernel_names) {
     Shape s;
     const mhla_status st = check(grid, block, &s);
     if (st != MHLA_OK) return st;
-    if (path != MHLA_PATH_3KERNEL && path != MHLA_PATH_FUSED && path != MHLA_PATH_CAUSAL)
-        return MHLA_ERR_INVALID_ARG;
+    int32_t path = 0, variant = 0;
+    if (!split_path(path_arg, &path, &variant)) return MHLA_ERR_INVALID_ARG;
     if (path == MHLA_PATH_CAUSAL && !causal_supported(s)) return MHLA_ERR_UNSUPPORTED;
     const char* names[3] = {nullptr, nullptr, nullptr};
     int n = 0;
