@@ -198,6 +198,33 @@ mhla_status mhla_forward_ex(const void* q, const void* k, const void* v, const f
                             void* ws, size_t ws_bytes, int32_t path,
                             const hipEvent_t* stage_events, hipStream_t stream);
 
+/* ---------------------------------------------------------------- no allocation
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * mhla_forward_noalloc is mhla_forward (3-kernel path, same kernels, same
+ * results) with its workspace taken from a fixed scratch array of
+ * MHLA_NOALLOC_SCRATCH_BYTES bytes of device memory built into the library:
+ * every GPU the library runs on holds its own copy from the first call on
+ * that GPU until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipMallocAsync, hipFree or allocating library routine); the caller still
+ * passes q, k, v, W and out as for mhla_forward.
+ * - Problems whose workspace (mhla_workspace_bytes) exceeds
+ *   MHLA_NOALLOC_SCRATCH_BYTES return MHLA_ERR_UNSUPPORTED before any HIP call
+ *   (the metric workload, 256 x 256 tokens, H = 6, d = 64 bf16, needs 26 MB).
+ * - `stream` (0 = the null stream) must belong to the current device, whose
+ *   scratch is used (MHLA_ERR_INVALID_ARG otherwise).
+ * - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *   call's contents (no part of it needs to start at zero).  Calls that
+ *   overlap in time on one GPU (other threads, or other streams not ordered
+ *   with this one) race on the scratch and give undefined results.
+ * Other errors as for mhla_forward. */
+#define MHLA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+mhla_status mhla_forward_noalloc(const void* q, const void* k, const void* v, const float* W,
+                                 const mhla_grid* grid, const mhla_block* block, void* out,
+                                 hipStream_t stream);
+
 /* ---------------------------------------------------------------- backward
  *
  * Gradients of a scalar loss L through the forward pass above, given the

@@ -155,6 +155,28 @@ def test_variant_flags(L):
                                   None) == mh.MHLA_ERR_INVALID_ARG
 
 
+def test_noalloc_validation(L):
+    """mhla_forward_noalloc: the scratch size in the header and the binding
+    agree; problems whose workspace exceeds it, invalid problems and empty
+    problems return before any HIP call."""
+    text = open(os.path.join(ROOT, "include", "mhla.h")).read()
+    m = re.search(r"#define MHLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == mh.MHLA_NOALLOC_SCRATCH_BYTES
+    g, b = cfg2()
+    assert mh.mhla_workspace_bytes(g, b) <= mh.MHLA_NOALLOC_SCRATCH_BYTES
+    call = lambda g_, b_: L.mhla_forward_noalloc(BIG, 2 * BIG, 3 * BIG, 4 * BIG, ctypes.byref(g_),
+                                                 ctypes.byref(b_), 5 * BIG, None)
+    g1 = mh.make_grid(32, 6, 64, mh.MHLA_BF16, (64, 64), 1e-6)      # 32 x 6 pairs, 64 blocks: ~205 MB
+    b1 = mh.make_block((8, 8))
+    assert mh.mhla_workspace_bytes(g1, b1) > mh.MHLA_NOALLOC_SCRATCH_BYTES
+    assert call(g1, b1) == mh.MHLA_ERR_UNSUPPORTED
+    bad = mh.make_block((15, 16))
+    assert call(g, bad) == mh.MHLA_ERR_INVALID_ARG
+    g0 = mh.make_grid(0, 6, 64, mh.MHLA_BF16, (256, 256))
+    assert L.mhla_forward_noalloc(None, None, None, None, ctypes.byref(g0), ctypes.byref(b), None,
+                                  None) == mh.MHLA_OK
+
+
 def test_launch_plan(L):
     g, b = cfg2()
     three = ["block_kv_summary", "mix_summaries", "query_apply"]

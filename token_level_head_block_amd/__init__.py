@@ -113,6 +113,8 @@ def lib() -> ctypes.CDLL:
         L.mhla_forward_ex.argtypes = [vp, vp, vp, vp, G, Bk, vp, vp, ctypes.c_size_t, ctypes.c_int32,
                                       vp, vp]
         L.mhla_forward_ex.restype = ctypes.c_int
+        L.mhla_forward_noalloc.argtypes = [vp, vp, vp, vp, G, Bk, vp, vp]
+        L.mhla_forward_noalloc.restype = ctypes.c_int
         L.mhla_layer_workspace_bytes.argtypes = [G, Bk]
         L.mhla_layer_workspace_bytes.restype = ctypes.c_size_t
         L.mhla_layer_forward.argtypes = [vp, vp, G, Bk, ctypes.POINTER(mhla_layer_params), vp, vp,
@@ -220,6 +222,16 @@ def mhla_forward_ws(q, k, v, W, grid: mhla_grid, block: mhla_block, out, ws, ws_
     return lib().mhla_forward_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(W), ctypes.byref(grid),
                                  ctypes.byref(block), _ptr(out), _ptr(ws), int(ws_bytes),
                                  _stream(stream))
+
+
+MHLA_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def mhla_forward_noalloc(q, k, v, W, grid: mhla_grid, block: mhla_block, out, stream=None) -> int:
+    """mhla_forward with the library's fixed per-GPU scratch as workspace (allocates nothing)."""
+    _check_tensors(q, k, v, W, out, grid, block)
+    return lib().mhla_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(W), ctypes.byref(grid),
+                                      ctypes.byref(block), _ptr(out), _stream(stream))
 
 
 def mhla_forward_ex(q, k, v, W, grid: mhla_grid, block: mhla_block, out, ws, ws_bytes: int,

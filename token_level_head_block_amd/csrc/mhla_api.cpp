@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 
@@ -751,6 +752,71 @@ mhla_status stream_impl(const void* q, const void* k, const void* v, const float
     return err == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------- no-alloc entry point
+//
+// mhla_forward_noalloc takes its workspace from `scratch`, a fixed array of
+// device memory of which every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in;
+// its device address on the current GPU comes from hipGetSymbolAddress, taken
+// once per device and kept in scratch_dev[].
+constexpr size_t kScratchBytes = MHLA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch (looked up on the first call on
+// that GPU, with it current).
+mhla_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return MHLA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return MHLA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return MHLA_ERR_HIP;
+        }
+        scratch_dev[dev] = p;
+    }
+    *out = scratch_dev[dev];
+    return MHLA_OK;
+}
+
+mhla_status forward_noalloc_impl(const void* q, const void* k, const void* v, const float* W,
+                                 const mhla_grid* grid, const mhla_block* block, void* out,
+                                 hipStream_t stream) {
+    Shape s;
+    const mhla_status st = check(grid, block, &s);
+    if (st != MHLA_OK) return st;
+    if (s.B == 0 || s.H == 0) return MHLA_OK;
+    if (layout(s).total > kScratchBytes) return MHLA_ERR_UNSUPPORTED;
+    if (stream) {
+        // the scratch used is the current GPU's: the stream must run there
+        int cur = -1, sdev = -1;
+        if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+            (void)hipGetLastError();
+            return MHLA_ERR_HIP;
+        }
+        if (sdev != cur) return MHLA_ERR_INVALID_ARG;
+    }
+    void* ws = nullptr;
+    const mhla_status sp = scratch_on_current_device(&ws);
+    if (sp != MHLA_OK) return sp;
+    return forward_impl(q, k, v, W, grid, block, out, ws, kScratchBytes, false, MHLA_PATH_3KERNEL, nullptr,
+                        stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -886,6 +952,12 @@ mhla_status mhla_forward_ex(const void* q, const void* k, const void* v, const f
                             hipStream_t stream) {
     return forward_impl(q, k, v, W, grid, block, out, ws, ws_bytes, true, path, stage_events,
                         stream);
+}
+
+mhla_status mhla_forward_noalloc(const void* q, const void* k, const void* v, const float* W,
+                                 const mhla_grid* grid, const mhla_block* block, void* out,
+                                 hipStream_t stream) {
+    return forward_noalloc_impl(q, k, v, W, grid, block, out, stream);
 }
 
 size_t mhla_causal_state_bytes(const mhla_grid* grid, const mhla_block* block, int32_t max_chunks) {
