@@ -32,6 +32,8 @@ SMALL = [
     ("bf-d32-M360", 1, 1, 32, (36, 40), (2, 2), BF, 1.0),
     ("bf-d32-M1024", 1, 2, 32, (64, 64), (2, 2), BF, 1.0),
     ("bf-d128-T200", 1, 1, 128, (20, 40), (10, 20), BF, 1.0),
+    ("bf-d128-H3-full", 2, 3, 128, (16, 32), (8, 8), BF, 1.0),   # odd head count: a half-empty head group
+    ("bf-d128-row8", 1, 2, 128, (24, 16), (3, 8), BF, 1.0),     # rows of 8 tokens, T = 24: ragged last step
     ("f32-d32-T15", 1, 2, 32, (12, 20), (3, 5), F, 1.0),
     ("f32-d64-3d", 2, 1, 64, (8, 16, 8), (2, 4, 4), F, 1.0),
     ("f32-d128", 1, 2, 128, (16, 16), (4, 8), F, 1.0),

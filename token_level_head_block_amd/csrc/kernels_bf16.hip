@@ -229,6 +229,174 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
 }
 
 // =====================================================================
+// block_kv_summary at head_dim 128: four waves per head that share the
+// step's operands through LDS, so every K and V element is read from memory
+// once and phi is evaluated once.  Per 32-token step, wave q of a head loads
+// one 64-channel half of one tensor (q = 0, 1: K channels 64q ..; q = 2, 3:
+// V channels 64(q-2) ..), packs it into MFMA operands (phi for K) and writes
+// them to one of two LDS buffers; after a workgroup barrier, wave q reads
+// the K half q/2 and the V half q%2 and accumulates that 64 x 64 quadrant of
+// S (and z for q%2 == 0).  Lane roles, operand packing, the output mapping
+// and the record stores are those of block_kv_summary with rowbase = 64(q/2)
+// and colbase = 64(q%2).  Waves of a head past H (odd head counts) load a
+// valid head and take part in every barrier but store nothing.
+// =====================================================================
+template <int PF, bool ROW8, bool FULL, bool NTL, int HPW>
+__global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(2)))
+void block_kv_summary_d128_bf16(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                uint16_t* __restrict__ SZ, const Geo g, const float* __restrict__ W,
+                                uint16_t* __restrict__ Wb, const WConv wc) {
+    static_assert(!FULL || ROW8, "FULL implies ROW8");
+    constexpr int D = 128, CPL = 4;
+    constexpr int TW = 64, TS = TW + 8;                 // record tile width, padded LDS row
+    constexpr int OPS = 4 * 64;                         // u32x4 operands of one (tensor, half): [r][lane]
+    constexpr int HEADOPS = 4 * OPS;                    // one head: K halves 0, 1, V halves 0, 1
+    constexpr int LDS_OPS = 2 * HPW * HEADOPS * 16;     // bytes: two buffers x HPW heads
+    constexpr int LDS_TILE = 4 * HPW * TW * TS * 2;     // bytes: record tiles of the 4 HPW waves
+    __shared__ u32x4 lds_raw[(LDS_OPS > LDS_TILE ? LDS_OPS : LDS_TILE) / 16];
+    if ((int)blockIdx.x >= wc.first_wg) {
+        convert_w(W, Wb, wc);
+        return;
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int quad = wave & 3, hl = wave >> 2;           // quadrant, head within the workgroup
+    const int li = lane & 15, gq = lane >> 4;
+    const WgCoordP wgc = wg_coord_parts(g, blockIdx.x, g.div_TP);
+    const int b = wgc.b, j = wgc.j, h = wgc.hg * g.G + hl;
+    const bool active = h < g.H;
+    const int hv = active ? h : g.H - 1;                // inactive waves load a valid head
+    const int rowbase = (quad >> 1) * 64, colbase = (quad & 1) * 64;
+    const bool is_v = quad >= 2;                        // loader role: V half (quad - 2), else K half quad
+    const bool do_z = (quad & 1) == 0;
+    const int row = g.H * D;
+    const int origin = block_origin(g, j);
+    const uint16_t* src = (is_v ? V : K) + (b * g.N * row + hv * D + (quad & 1) * 64 + CPL * li);
+    const u32x4 ones = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
+
+    f32x4 acc[CPL][CPL], accz[CPL];
+#pragma unroll
+    for (int r = 0; r < CPL; ++r) {
+        accz[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    struct Raw {
+        uint32_t x[8][2];
+        uint32_t valid;
+        int ks;
+    };
+    auto load = [&](int ks, Raw& R) {
+        R.ks = ks;
+        int offs[8];
+        if constexpr (ROW8) {
+            const int p0 = ks * 32 + gq * 8;
+            const bool ok = FULL || p0 < g.T;
+            const int off0 = (origin + in_block(g, ok ? p0 : 0)) * row;
+            R.valid = ok ? 0xffu : 0u;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) offs[s] = off0 + s * row;
+        } else {
+            R.valid = 0;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int p = ks * 32 + gq * 8 + s;
+                const bool ok = p < g.T;
+                offs[s] = (origin + in_block(g, ok ? p : g.T - 1)) * row;
+                R.valid |= (ok ? 1u : 0u) << s;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const u32x2 a = ld<NTL>(reinterpret_cast<const u32x2*>(src + offs[s]));
+            R.x[s][0] = a.x;
+            R.x[s][1] = a.y;
+        }
+    };
+    u32x4* ops_head = lds_raw + hl * HEADOPS;           // + buffer * HPW * HEADOPS
+    auto compute = [&](const Raw& R) {
+        u32x4* buf = ops_head + (R.ks & 1) * (HPW * HEADOPS);
+        // Pack this wave's half into operands: K (phi, padding slots zeroed) or V.
+        u32x4 op[CPL];
+#pragma unroll
+        for (int r = 0; r < CPL; ++r)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t a0 = R.x[2 * w][r >> 1], a1 = R.x[2 * w + 1][r >> 1];
+                if (is_v) {
+                    op[r][w] = (r & 1) ? pack_hi(a0, a1) : pack_lo(a0, a1);
+                } else {
+                    const float x0 = (r & 1) ? bf_hi(a0) : bf_lo(a0);
+                    const float x1 = (r & 1) ? bf_hi(a1) : bf_lo(a1);
+                    if constexpr (FULL) {
+                        op[r][w] = pack_bf16(phi_fast(x0), phi_fast(x1));
+                    } else if constexpr (ROW8) {
+                        op[r][w] = R.valid ? pack_bf16(phi_fast(x0), phi_fast(x1)) : 0u;
+                    } else {
+                        const bool ok0 = (R.valid >> (2 * w)) & 1u, ok1 = (R.valid >> (2 * w + 1)) & 1u;
+                        op[r][w] = pack_bf16(ok0 ? phi_fast(x0) : 0.f, ok1 ? phi_fast(x1) : 0.f);
+                    }
+                }
+            }
+#pragma unroll
+        for (int r = 0; r < CPL; ++r) buf[(quad * CPL + r) * 64 + lane] = op[r];
+        __syncthreads();
+        // This wave's quadrant: K half quad/2 (slots 0, 1) and V half quad%2 (slots 2, 3).
+        u32x4 bw[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) bw[c] = buf[((2 + (quad & 1)) * CPL + c) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < CPL; ++r) {
+            const u32x4 aw = buf[((quad >> 1) * CPL + r) * 64 + lane];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[r][c] = mfma_bf16(aw, bw[c], acc[r][c]);
+            if (do_z) accz[r] = mfma_bf16(aw, ones, accz[r]);
+        }
+    };
+    // This part's run of the block's 32-token steps (all of them when TP = 1).
+    const int nks = (g.T + 31) >> 5, per = (nks + g.TP - 1) / g.TP;
+    const int ks0 = wgc.t * per, ks1 = min(nks, ks0 + per);
+    if (ks0 < ks1) pipelined<PF, Raw>(ks0, 1, ks1, load, compute);
+    __syncthreads();   // every wave is done with the operand buffers; the LDS now holds record tiles
+
+    // Record layout and stores as in block_kv_summary (S_j transposed, then z_j).
+    uint16_t* stile = reinterpret_cast<uint16_t*>(lds_raw) + wave * (TW * TS);
+#pragma unroll
+    for (int c2 = 0; c2 < CPL; ++c2) {
+        uint32_t wv[2 * CPL];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int rp = 0; rp < CPL / 2; ++rp)
+                wv[v * (CPL / 2) + rp] = pack_bf16(acc[2 * rp][c2][v], acc[2 * rp + 1][c2][v]);
+        uint16_t* dst = stile + (CPL * li + c2) * TS + 4 * CPL * gq;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+    }
+    if (!active) return;
+    const int blk = ((b * g.H + h) * g.M + j) * g.TP + wgc.t;   // record index (b, h, j, part)
+    uint16_t* rec = SZ + (size_t)blk * (D * D + D);
+    constexpr int LPR = TW / 8;           // lanes per tile row (16 bytes each)
+#pragma unroll
+    for (int k = 0; k < TW / (64 / LPR); ++k) {
+        const int er = k * (64 / LPR) + lane / LPR, chunk = lane % LPR;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(stile + er * TS + chunk * 8);
+        *reinterpret_cast<u32x4*>(rec + (colbase + er) * D + rowbase + chunk * 8) = x;
+    }
+    if (do_z && li == 0) {
+        uint32_t wv[2 * CPL];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int rp = 0; rp < CPL / 2; ++rp)
+                wv[v * (CPL / 2) + rp] = pack_bf16(accz[2 * rp][v], accz[2 * rp + 1][v]);
+        uint16_t* dst = rec + D * D + rowbase + 4 * CPL * gq;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+        *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+    }
+}
+
+// =====================================================================
 // mix_summaries (one workgroup per work unit), for any M.
 // =====================================================================
 template <int D>
@@ -852,6 +1020,29 @@ void launch_summary(const Launch& L, const uint16_t* k, const uint16_t* v, uint1
     const int nconv = (nchunks + threads - 1) / threads;   // one chunk per thread
     w.first_wg = nsum;
     w.nconv = nconv;
+    if constexpr (D == 128) {
+        if (L.tune.d128_shared) {
+            // HPW heads (4 waves each) per workgroup
+            const Geo g1 = with_head_groups(gp, NQ, 4 * L.tune.d128_shared);
+            const int ns1 = g1.B * g1.M * g1.TP * g1.HG, th1 = 64 * NQ * g1.G;
+            WConv w1 = wc;
+            w1.first_wg = ns1;
+            w1.nconv = (nchunks + th1 - 1) / th1;
+            auto* wbp = static_cast<uint16_t*>(L.wb);
+            if (L.tune.d128_shared == 1) {
+                if (L.tune.nt_loads)
+                    block_kv_summary_d128_bf16<PF, ROW8, FULL, true, 1><<<ns1 + w1.nconv, th1, 0, L.stream>>>(k, v, sz, g1, L.W, wbp, w1);
+                else
+                    block_kv_summary_d128_bf16<PF, ROW8, FULL, false, 1><<<ns1 + w1.nconv, th1, 0, L.stream>>>(k, v, sz, g1, L.W, wbp, w1);
+            } else {
+                if (L.tune.nt_loads)
+                    block_kv_summary_d128_bf16<PF, ROW8, FULL, true, 2><<<ns1 + w1.nconv, th1, 0, L.stream>>>(k, v, sz, g1, L.W, wbp, w1);
+                else
+                    block_kv_summary_d128_bf16<PF, ROW8, FULL, false, 2><<<ns1 + w1.nconv, th1, 0, L.stream>>>(k, v, sz, g1, L.W, wbp, w1);
+            }
+            return;
+        }
+    }
     if (L.tune.nt_loads)
         block_kv_summary_bf16<D, PF, ROW8, FULL, true, PAIR><<<nsum + nconv, threads, 0, L.stream>>>(
             k, v, sz, g, L.W, static_cast<uint16_t*>(L.wb), w);

@@ -10,6 +10,8 @@ namespace mhla {
 struct Tuning {
     int summary_waves;   // fp32 path: waves splitting the tokens of one block (1, 2, 4)
     int summary_pf;      // bf16 path: k-steps of K/V loads in flight per wave (1, 2)
+    int d128_shared;     // bf16 path, head_dim 128: summary waves share K/V operands through LDS,
+                         // this many heads (1, 2) per workgroup; 0 = quadrant waves loading their own
     int apply_waves;     // waves splitting the tokens of one block in query_apply (1, 2, 4)
     int apply_pf;        // bf16 path: 16-token groups of Q loads in flight per wave (1, 2, 4)
     int pair_heads;      // bf16 path, head_dim 32 with an even head count: summaries of head pairs

@@ -193,6 +193,11 @@ mhla::Tuning choose_tuning(const Shape& s) {
     if (sp == 1 || sp == 2) t.summary_pf = sp;
     if (ap == 1 || ap == 2 || ap == 4) t.apply_pf = ap;
     t.pair_heads = env_int("MHLA_PAIR_HEADS", 1) != 0;
+    // head_dim 128: the summary kernel whose four waves per head share K/V
+    // operands through LDS, one head per workgroup (video-16x64x64 summary
+    // 136 -> 103 us; two heads per workgroup 122 us).
+    t.d128_shared = env_int("MHLA_D128_SHARED", 1);
+    if (t.d128_shared < 0 || t.d128_shared > 2) t.d128_shared = 1;
     t.apply_maxw = 8;
     t.bwdq_heads = env_int("MHLA_BWDQ_HEADS", 0);
     if (t.bwdq_heads < 0 || t.bwdq_heads > 4) t.bwdq_heads = 0;
