@@ -105,15 +105,17 @@ enum {
 /* Kernel-variant flags, OR-ed into the path argument of mhla_forward_ex and
  * mhla_launch_plan.  They choose among kernels that compute the same result
  * (for tests and comparisons); problems a variant does not apply to ignore
- * it.  An unknown flag, or both mixing flags, gives MHLA_ERR_INVALID_ARG.
+ * it.  An unknown flag, or more than one mixing flag, gives MHLA_ERR_INVALID_ARG.
  * Without flags the library picks the variant for the problem. */
 enum {
     MHLA_VARIANT_MIX_RESIDENT = 1 << 8,   /* bf16, at most 256 source records: persistent mixing
                                              kernel, one workgroup per compute unit, W in registers */
     MHLA_VARIANT_MIX_TILED = 1 << 9,      /* bf16: mixing with one workgroup per column tile of
                                              every query block (any M) */
-    MHLA_VARIANT_NO_PAIR_HEADS = 1 << 10  /* bf16, head_dim 32, even head count: one head per wave
+    MHLA_VARIANT_NO_PAIR_HEADS = 1 << 10, /* bf16, head_dim 32, even head count: one head per wave
                                              in the summary kernel instead of head pairs */
+    MHLA_VARIANT_MIX_SPLIT = 1 << 11      /* bf16, at most 256 source records: mixing with one
+                                             workgroup per (pair, column tile, query-block tile) */
 };
 
 /* Human-readable name of a status code (static storage, never NULL). */

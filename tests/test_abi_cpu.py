@@ -140,11 +140,12 @@ def test_variant_flags(L):
     mixing flags at once are rejected before any HIP call."""
     g, b = cfg2()
     three = ["block_kv_summary", "mix_summaries", "query_apply"]
-    for flag in (mh.MHLA_VARIANT_MIX_RESIDENT, mh.MHLA_VARIANT_MIX_TILED, mh.MHLA_VARIANT_NO_PAIR_HEADS):
+    for flag in (mh.MHLA_VARIANT_MIX_RESIDENT, mh.MHLA_VARIANT_MIX_TILED, mh.MHLA_VARIANT_MIX_SPLIT,
+                 mh.MHLA_VARIANT_NO_PAIR_HEADS, mh.MHLA_VARIANT_MIX_SPLIT | mh.MHLA_VARIANT_NO_PAIR_HEADS):
         assert mh.mhla_launch_plan(g, b, mh.MHLA_PATH_3KERNEL | flag) == (mh.MHLA_OK, three)
-    both = mh.MHLA_VARIANT_MIX_RESIDENT | mh.MHLA_VARIANT_MIX_TILED
     need = mh.mhla_workspace_bytes(g, b)
-    for bad in (1 << 12, 1 << 30, both):
+    for bad in (1 << 12, 1 << 30, mh.MHLA_VARIANT_MIX_RESIDENT | mh.MHLA_VARIANT_MIX_TILED,
+                mh.MHLA_VARIANT_MIX_SPLIT | mh.MHLA_VARIANT_MIX_TILED):
         assert mh.mhla_launch_plan(g, b, bad)[0] == mh.MHLA_ERR_INVALID_ARG
         assert call_fwd(L, g, b, ws=6 * BIG, ws_bytes=need, path=bad) == mh.MHLA_ERR_INVALID_ARG
     # the backward takes only the head-pair flag

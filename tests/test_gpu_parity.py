@@ -99,7 +99,8 @@ MIX_CASES = [
 
 
 MIX_VARIANTS = {   # path flags of each bf16 mixing variant
-    "split": 0,
+    "default": 0,
+    "split": mh.MHLA_VARIANT_MIX_SPLIT,
     "resident": mh.MHLA_VARIANT_MIX_RESIDENT,
     "per-tile": mh.MHLA_VARIANT_MIX_TILED,
 }

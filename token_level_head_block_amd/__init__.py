@@ -36,6 +36,7 @@ MHLA_PATH_CAUSAL = 2
 MHLA_VARIANT_MIX_RESIDENT = 1 << 8
 MHLA_VARIANT_MIX_TILED = 1 << 9
 MHLA_VARIANT_NO_PAIR_HEADS = 1 << 10
+MHLA_VARIANT_MIX_SPLIT = 1 << 11
 
 MHLA_PHI_ELU1 = 0
 MHLA_PHI_RELU_EPS = 1

@@ -212,8 +212,12 @@ mhla::Tuning choose_tuning(const Shape& s) {
     // Mixing kernel: one workgroup per (pair, column tile, query-block tile)
     // by default; MHLA_MIX selects another for sweeps (flags of
     // mhla_forward_ex select one per call).
-    t.mix_kind = env_int("MHLA_MIX", 2);
-    if (t.mix_kind < 0 || t.mix_kind > 2) t.mix_kind = 2;
+    // With at most 64 query blocks the per-tile workgroups are small (8 KB
+    // of W and 8 KB of records each) and the persistent kernel, which loads W
+    // once per compute unit, is faster (dit-s2-64x64 mixing 38.2 -> 33.7 us).
+    const int mix_default = s.M <= 64 ? 1 : 2;
+    t.mix_kind = env_int("MHLA_MIX", mix_default);
+    if (t.mix_kind < 0 || t.mix_kind > 2) t.mix_kind = mix_default;
     t.mix_rows = env_int("MHLA_MIX_ROWS", 0);
     // Non-temporal stores of the mixed summaries: mixing 12.7 -> 11.7 us at
     // dit-s2-256x256 (T = 256, the apply unchanged), video-16x64x64 307 us
@@ -252,19 +256,22 @@ mhla::Geo make_geo(const Shape& s, float eps) {
 
 // The path argument of mhla_forward_ex: a MHLA_PATH_* value in the low 8 bits
 // and MHLA_VARIANT_* flags above them.
-constexpr int32_t kVariantMask = MHLA_VARIANT_MIX_RESIDENT | MHLA_VARIANT_MIX_TILED | MHLA_VARIANT_NO_PAIR_HEADS;
+constexpr int32_t kMixFlags = MHLA_VARIANT_MIX_RESIDENT | MHLA_VARIANT_MIX_TILED | MHLA_VARIANT_MIX_SPLIT;
+constexpr int32_t kVariantMask = kMixFlags | MHLA_VARIANT_NO_PAIR_HEADS;
 
 bool split_path(int32_t arg, int32_t* path, int32_t* variant) {
     *path = arg & 0xff;
     *variant = arg & ~0xff;
     if (*variant & ~kVariantMask) return false;
-    if ((*variant & MHLA_VARIANT_MIX_RESIDENT) && (*variant & MHLA_VARIANT_MIX_TILED)) return false;
+    const int32_t mix = *variant & kMixFlags;
+    if (mix & (mix - 1)) return false;   // at most one mixing kernel
     return *path == MHLA_PATH_3KERNEL || *path == MHLA_PATH_FUSED || *path == MHLA_PATH_CAUSAL;
 }
 
 void apply_variant(mhla::Tuning& t, int32_t variant) {
     if (variant & MHLA_VARIANT_MIX_RESIDENT) t.mix_kind = 1;
     if (variant & MHLA_VARIANT_MIX_TILED) t.mix_kind = 0;
+    if (variant & MHLA_VARIANT_MIX_SPLIT) t.mix_kind = 2;
     if (variant & MHLA_VARIANT_NO_PAIR_HEADS) t.pair_heads = 0;
 }
 
