@@ -36,6 +36,7 @@ KERNEL_SOURCES = {
     "layer": _FWD + ("kernels_layer_bf16.hip",),
 }
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+MFMA_PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 MALL_BYTES = 256 << 20          # Infinity Cache
 
 
@@ -103,6 +104,23 @@ def measured_traffic(workload: str, path: str = "3kernel"):
             w = float(vals.get(name + " write_kib", 0.0))
             out[name] = int(float(v) * 1024 * fs + w * 1024 * ws)
     return out
+
+
+def measured_mfma(workload: str, path: str = "3kernel"):
+    """MFMA flops per dispatch of each kernel (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) from the
+    committed rocprofv3 counter summary, or {} (as measured_traffic)."""
+    fname = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(fname):
+        return {}
+    vals = {}
+    for line in open(fname):
+        line = line.strip()
+        if line and not line.startswith("#") and ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_sha(path):
+        return {}
+    return {k[: -len(" mfma_flops")]: float(v) for k, v in vals.items() if k.endswith(" mfma_flops")}
 
 
 def kernel_bytes(p, ws_elem):
@@ -695,8 +713,16 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"])
     traffic = measured_traffic(p.name, args.path) if (args.path != "fused" and args.w == "gaussian"
                                            and not args.batch and not args.heads and not args.block) else {}
+    mfma = measured_mfma(p.name, args.path) if (args.path != "fused" and args.w == "gaussian"
+                                                 and not args.batch and not args.heads and not args.block) else {}
     for n in kernels:
         kernels[n]["traffic"] = traffic.get(n)
+        # matrix-core use: counter flops of one dispatch over its event-timed duration, against
+        # the dense bf16 peak
+        f = mfma.get(n)
+        tf = f / (kernels[n]["avg_us"] * 1e-6) / 1e12 if f else None
+        kernels[n]["mfma_tflops"] = round(tf, 1) if tf else None
+        kernels[n]["mfma_util"] = round(tf / MFMA_PEAK_BF16_TFLOPS, 4) if tf else None
     roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["gbps"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": kernels[dom]["frac"], "traffic": traffic.get(dom),
                 "avg_us": kernels[dom]["avg_us"], "alg_bytes": kernels[dom]["alg_bytes"]}
