@@ -168,8 +168,14 @@ mhla_status mhla_launch_plan(const mhla_grid* grid, const mhla_block* block, int
  * runs the causal form on the M*cp sub-chunks (W between sub-chunks a and b
  * is W[a/cp][b/cp]), so its records in regions 0-2 are per sub-chunk and
  * region 3 holds that sub-chunk coefficient matrix.
+ * Causal W parts (bf16 problems whose blocks are contiguous runs of raster
+ * order): a MHLA_PATH_CAUSAL call takes W into its mixing as a bf16 high part
+ * bf16(w) and a bf16 low part bf16(w - bf16(w)), so that the mixtures see W
+ * to about 16 significant bits; region 3 then holds 2 columns per summary
+ * record, the high part first.
  * Sizes: region 0 holds P*M*max(tp, cp) records, regions 1 and 2 P*M*cp,
- * region 3 roundup(M*cp, 64) x roundup(M*max(tp, cp), 32) bf16 values. */
+ * region 3 roundup(M*cp, 64) x roundup(M*max(tp, k), 32) bf16 values, with
+ * k = 2*cp when the blocks are contiguous runs of raster order, else k = cp. */
 size_t mhla_workspace_bytes(const mhla_grid* grid, const mhla_block* block);
 
 /* The MHLA forward pass: out = MHLA(q, k, v; W) for the whole problem,

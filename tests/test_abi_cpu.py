@@ -354,10 +354,12 @@ def test_layer_workspace_and_validation(L):
 def test_workspace_sizes_with_token_parts(L):
     """The forward's workspace with token parts, by the rule the header states:
     tp doubles while B*H*M*tp < 1536, M*2*tp <= 256 and 2*tp*64 <= T; region 0
-    holds P*M*tp records, region 3 W with roundup(M*tp, 32) columns."""
+    holds P*M*tp records, region 3 W with roundup(M*max(tp, k), 32) columns, k = 2*cp
+    where the blocks are contiguous runs of raster order (the causal form's W
+    high and low parts) and cp otherwise."""
     up = lambda x: (x + 255) // 256 * 256
 
-    def expected(B, H, d, M, T, split=None, bf16=True):
+    def expected(B, H, d, M, T, split=None, bf16=True, contiguous=False):
         """split: extent of the chunk's slowest axis > 1 when chunks are contiguous."""
         tp = cp = 1
         if bf16:
@@ -370,21 +372,22 @@ def test_workspace_sizes_with_token_parts(L):
         r0 = P * M * max(tp, cp)
         n = up(r0 * (d * d + d) * e) + up(P * M * cp * d * d * e) + up(P * M * cp * d * 4)
         if bf16:
-            n += up((M * cp + 63) // 64 * 64 * ((M * max(tp, cp) + 31) // 32 * 32) * 2)
+            k = 2 * cp if contiguous else cp
+            n += up((M * cp + 63) // 64 * 64 * ((M * max(tp, k) + 31) // 32 * 32) * 2)
         return n, tp, cp
 
-    for (B, H, d, grid, block, split) in [
-            (1, 6, 64, (256, 256), (64, 64), None),     # M = 16, T = 4096: tp = 16 (tiles: no sub-chunks)
-            (1, 6, 64, (256, 256), (32, 32), None),     # M = 64: tp = 4
-            (1, 6, 64, (256, 256), (16, 16), None),     # M = 256: tp = 1
-            (2, 3, 32, (64, 64), (32, 32), None),       # M = 4, T = 1024: tp = 16
-            (1, 2, 128, (20, 40), (20, 40), 20),        # M = 1, T = 800: tp = 4, cp = 2 (20 rows of 40)
-            (1, 6, 64, (256, 256), (16, 256), 16),      # chunks of 16 rows: tp = 16, cp = 16
-            (1, 6, 64, (256, 256), (1, 256), None)]:    # chunks of one row: tp = cp = 1
+    for (B, H, d, grid, block, split, contiguous) in [
+            (1, 6, 64, (256, 256), (64, 64), None, False),     # M = 16, T = 4096: tp = 16 (tiles: no sub-chunks)
+            (1, 6, 64, (256, 256), (32, 32), None, False),     # M = 64: tp = 4
+            (1, 6, 64, (256, 256), (16, 16), None, False),     # M = 256: tp = 1
+            (2, 3, 32, (64, 64), (32, 32), None, False),       # M = 4, T = 1024: tp = 16
+            (1, 2, 128, (20, 40), (20, 40), 20, True),         # M = 1, T = 800: tp = 4, cp = 2 (20 rows of 40)
+            (1, 6, 64, (256, 256), (16, 256), 16, True),       # chunks of 16 rows: tp = 16, cp = 16
+            (1, 6, 64, (256, 256), (1, 256), None, True)]:     # chunks of one row: tp = cp = 1
         g, b = mh.make_grid(B, H, d, mh.MHLA_BF16, grid), mh.make_block(block)
         M = (grid[0] // block[0]) * (grid[1] // block[1])
         T = block[0] * block[1]
-        n, tp, cp = expected(B, H, d, M, T, split)
+        n, tp, cp = expected(B, H, d, M, T, split, contiguous=contiguous)
         assert mh.mhla_workspace_bytes(g, b) == n, (grid, block, tp, cp)
     # fp32 problems never split
     g, b = mh.make_grid(1, 6, 64, mh.MHLA_F32, (256, 256)), mh.make_block((64, 64))

@@ -1,8 +1,8 @@
 """The causal chunkwise path (MHLA_PATH_CAUSAL) against the float64 oracle's
-causal form, through the C ABI.  Bar: max|d| / max|ref| <= 1e-2 (bf16); where
-the signed W makes the causal denominators cancel, the bar applies to the
-well-conditioned tokens and a rounding bound scaled by the cancellation to the
-rest."""
+causal form, through the C ABI.  Bar: max|d| / max|ref| <= 1e-2 (bf16) on
+every output, including sequences whose signed W makes the partial row sums
+over earlier chunks cancel (the cancellation factor of each query's
+denominator is printed as a diagnostic)."""
 import numpy as np
 import pytest
 import torch
@@ -73,48 +73,59 @@ def test_causal_f32(case):
     assert err <= TOL[synth.F32]
 
 
-def check_conditioned(p, q, k, v, W, out, ref, kappa_max=16.0):
-    """Parity with cancellation accounted for.  Tokens whose causal
-    denominator is well conditioned (kappa <= kappa_max) meet the bf16 bar;
-    every token stays within 4 u kappa (max|v| + |o_n|), the first-order
-    effect of rounding W, the block summaries and phi(q) to bf16 (u = 2^-8)."""
+def check_every_output(p, q, k, v, W, out, ref, kappa_max=16.0):
+    """The bf16 bar on every output.  Diagnostic: the cancellation factor
+    kappa of each query's causal denominator, and the error of the tokens above
+    kappa_max against a rounding bound scaled by it (4 u kappa (max|v| + |o_n|),
+    u = 2^-8), which the bar no longer needs."""
     den, absden = causal_denominators(q, k, W, p.grid, p.block, p.eps)
     kappa = absden / np.abs(den)                              # [B, N, H]
     dev = np.abs(out - ref).max(axis=3)
     scale = np.abs(ref).max()
-    well = kappa <= kappa_max
+    ill = kappa > kappa_max
     vmax = np.abs(oracle.decode(v)).max(axis=(1, 3))          # [B, H]
     bound = 4 * BF16_U * kappa * (vmax[:, None, :] + np.abs(ref).max(axis=3))
-    say(f"  {p.name}: kappa max {kappa.max():.1f}, {well.mean():.4f} of tokens <= {kappa_max}; "
-        f"well-conditioned max|d|/max|ref| = {dev[well].max() / scale:.3e}, "
+    err = dev.max() / scale
+    say(f"  {p.name}: max|d|/max|ref| = {err:.3e}; kappa max {kappa.max():.1f}, {ill.mean():.4f} of tokens "
+        f"above {kappa_max} (their max|d|/max|ref| {dev[ill].max() / scale if ill.any() else 0.0:.3e}), "
         f"worst d / bound = {(dev / bound).max():.3f}")
     assert np.isfinite(out).all()
-    assert well.mean() >= 0.99
-    assert dev[well].max() <= TOL[BF] * scale
-    assert (dev <= bound).all()
+    assert err <= TOL[BF]
 
 
 def test_causal_sequence_workload():
     """65536 tokens as one sequence in chunks of 256 (the metric workload's size),
-    every output of every pair; a second call is bitwise equal.  This signed W
-    has partial row sums that cancel up to 145-fold, hence the conditioned check."""
+    every output of every pair against the bf16 bar; a second call is bitwise
+    equal.  This signed W has partial row sums that cancel up to 145-fold; the
+    mixing takes W as a bf16 high and low part, so the bar holds everywhere."""
     p = synth.Problem("seq-65536-chunk256", 1, 6, 64, (1, 65536), (1, 256), dtype=BF)
     q, k, v, W = synth.make_inputs(p, seed=62)
     ref = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
     run = Run(p, q, k, v, W)
     out = run.forward(mh.MHLA_PATH_CAUSAL)
-    check_conditioned(p, q, k, v, W, to_host64(out), ref)
+    check_every_output(p, q, k, v, W, to_host64(out), ref)
     again = run.forward(mh.MHLA_PATH_CAUSAL)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))
 
 
 def test_causal_sequence_d128():
-    """16384 tokens in chunks of 256 at d = 128 (four heads): every output, conditioned."""
+    """16384 tokens in chunks of 256 at d = 128 (four heads): every output against the bf16 bar."""
     p = synth.Problem("seq-16384-chunk256-d128", 1, 4, 128, (1, 16384), (1, 256), dtype=BF)
     q, k, v, W = synth.make_inputs(p, seed=65)
     ref = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
     out = Run(p, q, k, v, W).forward(mh.MHLA_PATH_CAUSAL)
-    check_conditioned(p, q, k, v, W, to_host64(out), ref)
+    check_every_output(p, q, k, v, W, to_host64(out), ref)
+
+
+def test_causal_sequence_long_chunks_signed_w():
+    """65536 tokens in 16 chunks of 4096 (the rows of a 256 x 256 grid, 16 per
+    chunk), run as sub-chunks whose coefficients come from their chunks: every
+    output against the bf16 bar with the jittered W."""
+    p = synth.Problem("rows-65536-chunk4096", 1, 6, 64, (256, 256), (16, 256), dtype=BF)
+    q, k, v, W = synth.make_inputs(p, seed=67)
+    ref = oracle.forward_causal(q, k, v, W, p.grid, p.block, eps=p.eps)
+    out = Run(p, q, k, v, W).forward(mh.MHLA_PATH_CAUSAL)
+    check_every_output(p, q, k, v, W, to_host64(out), ref)
 
 
 def test_causal_sequence_workload_local_w():

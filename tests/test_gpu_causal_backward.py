@@ -17,6 +17,7 @@ import oracle
 import token_level_head_block_amd as mh
 from token_level_head_block_amd import synth
 
+from conditioning import causal_denominators
 from gpu_util import Run, rel_err, say, to_host64
 
 pytestmark = pytest.mark.gpu
@@ -91,6 +92,25 @@ def test_causal_backward_sequence_workload():
     for a, b in zip(got, again):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def test_causal_backward_f32_signed_w():
+    """fp32 gradients with a signed W (the distance prior plus a jitter of
+    standard deviation 0.15, so that some coefficients are negative) whose
+    partial row sums over earlier chunks stay away from zero: every element
+    against the fp32 bar; the denominators' cancellation factor is printed."""
+    p = synth.Problem("cbwd-f32-signed", 1, 2, 64, (1, 640), (1, 80), dtype=F32)
+    q, k, v, _ = synth.make_inputs(p, seed=77)
+    M = p.n_blocks
+    nb = [gx // bx for gx, bx in zip(p.grid, p.block)]
+    W = (synth.distance_prior(nb, 3.0) + 0.15 * np.random.default_rng(78).standard_normal((M, M))).astype(np.float32)
+    assert (np.tril(W) < 0).any()
+    den, absden = causal_denominators(q, k, W, p.grid, p.block, p.eps)
+    kappa = absden / np.abs(den)
+    say(f"  {p.name}: {int((np.tril(W) < 0).sum())} negative coefficients on or below the diagonal, "
+        f"kappa max {kappa.max():.2f}")
+    assert kappa.max() < 4.0
+    check(p, q, k, v, W, seed=79)
 
 
 def test_causal_backward_ignores_later_coefficients():

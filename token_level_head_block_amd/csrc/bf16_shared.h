@@ -58,6 +58,8 @@ struct WConv {
     int32_t TP;               // token parts: column j' of the operand is W[i][j' / TP] (j' < M TP)
     int32_t NKt, nchunks_t;   // W^T (no token parts): NKt = roundup(M, 32) / 32, its 16-byte units
     int32_t WD, WM;           // causal sub-chunks: entry (i, j) is W[i / WD][j / WD], W is WM x WM
+    int32_t RD;               // k-slots per source record: column j' is record j' / RD; with RD = 2
+                              // the even slot takes bf16(w), the odd one bf16(w - bf16(w))
 };
 
 __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t* __restrict__ Wb,
@@ -75,14 +77,21 @@ __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t*
         if (tr) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)(j0 + s) * wc.M + i] : 0.f;
-        } else if (wc.TP > 1 || wc.WD > 1) {
-            // token parts: source record j' = j TP + t holds part t of block j;
-            // causal sub-chunks: row and column indices are sub-chunks, WD per block of W
+        } else if (wc.TP > 1 || wc.WD > 1 || wc.RD > 1) {
+            // token parts: source record r = j TP + t holds part t of block j;
+            // causal sub-chunks: row and column indices are sub-chunks, WD per block of W;
+            // RD k-slots per record: slot j' reads record j' / RD
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const int jp = j0 + s;
-                x[s] = (i < wc.M && jp < wc.M * wc.TP)
-                           ? W[(size_t)(i / wc.WD) * wc.WM + jp / (wc.TP * wc.WD)] : 0.f;
+                const int jp = j0 + s, jr = jp / wc.RD;
+                float w = (i < wc.M && jr < wc.M * wc.TP)
+                              ? W[(size_t)(i / wc.WD) * wc.WM + jr / (wc.TP * wc.WD)] : 0.f;
+                if (wc.causal && jr / wc.TP >= i) w = 0.f;   // earlier blocks only
+                if (wc.RD > 1) {
+                    const float hi = bf_lo(pack_bf16(w, 0.f));
+                    w = (jp % wc.RD == 0) ? hi : w - hi;
+                }
+                x[s] = w;
             }
         } else if (i < wc.M && (wc.M & 7) == 0 && j0 < wc.M) {
             const f32x4 a = *reinterpret_cast<const f32x4*>(W + (size_t)i * wc.M + j0);
@@ -93,7 +102,7 @@ __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t*
 #pragma unroll
             for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)i * wc.M + j0 + s] : 0.f;
         }
-        if (wc.causal) {
+        if (wc.causal && !tr && wc.TP == 1 && wc.WD == 1 && wc.RD == 1) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) x[s] = j0 + s < i ? x[s] : 0.f;
         }
@@ -148,11 +157,12 @@ __device__ __forceinline__ void mix_tile_bf16(uint32_t wg, const RecT* __restric
     const uint32_t bh = fdiv(wg, mg.div_CTG);
     const int ctg = (int)(wg - bh * mg.div_CTG.d);
     const int M = g.M;                 // query blocks
-    const int MS = g.M * g.TP;         // source records (partial records of TP parts)
+    const int NR = g.M * g.TP;         // source records (partial records of TP parts)
+    const int MS = NR * g.RD;          // k-slots: each record feeds RD of them
     const int NK = (MS + 31) >> 5;
     const int cpw = mg.CPW;
     const int itr = mg.IT < 4 ? mg.IT : 4;   // i tiles per round
-    const RecT* base = SZ + (size_t)bh * MS * REC;
+    const RecT* base = SZ + (size_t)bh * NR * REC;
     const int th = wave & 1, w2 = wave >> 1;
     const int wc = w2 / itr, wit = w2 % itr;
     const int ct = ctg * cpw + wc;
@@ -207,7 +217,7 @@ __device__ __forceinline__ void mix_tile_bf16(uint32_t wg, const RecT* __restric
                 for (int s = 0; s < 8; ++s) {
                     // Clamped address, then a mask: the load stays unconditional.
                     const int jj = (k0 + (jg >> 2)) * 32 + (jg & 3) * 8 + s;
-                    const u32x2 t = load4_bf16(base + (size_t)(jj < MS ? jj : MS - 1) * REC + colc);
+                    const u32x2 t = load4_bf16(base + (size_t)((jj < MS ? jj : MS - 1) / g.RD) * REC + colc);
                     const uint32_t m = (ok && jj < MS) ? 0xffffffffu : 0u;
                     raw[s] = u32x2{t.x & m, t.y & m};
                 }

@@ -58,6 +58,10 @@ struct Geo {
     // form run on sub-chunks, WD of them per chunk of the caller's problem);
     // WM is W's dimension (the caller's block count).
     int32_t WD, WM;
+    // Every source record feeds RD consecutive k-slots of the mixing product
+    // (RD = 2: the slots take W's bf16 high and low parts, so the mixture
+    // sees W to about 16 significant bits; the bf16 causal form uses it).
+    int32_t RD;
     float eps;
 };
 

@@ -431,7 +431,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, gq = lane >> 4;
     const int M = g.M;                                // query blocks
-    const int MS = g.M * g.TP;                        // source records (partial records of TP parts)
+    const int NR = g.M * g.TP;                        // source records (partial records of TP parts)
+    const int MS = NR * g.RD;                         // k-slots: each record feeds RD of them
     const int NK = (MS + 31) >> 5;                    // <= KMAX (checked on the host)
     const int cpw = mg.CPW;
     const int itr = mg.IT;                            // <= 4 (checked on the host)
@@ -463,11 +464,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
         const int colp = ct * 64 + 4 * lip;
         const bool ok = srole && colp < REC && ct < mg.CT;
         const int colc = ok ? colp : 0;
-        const uint16_t* base = SZ + (size_t)bh * MS * REC;
+        const uint16_t* base = SZ + (size_t)bh * NR * REC;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int jj = (jg >> 2) * 32 + (jg & 3) * 8 + s;
-            const u32x2 t = ld<(NT & 1) != 0>(reinterpret_cast<const u32x2*>(base + (size_t)(jj < MS ? jj : MS - 1) * REC + colc));
+            const u32x2 t = ld<(NT & 1) != 0>(
+                reinterpret_cast<const u32x2*>(base + (size_t)((jj < MS ? jj : MS - 1) / g.RD) * REC + colc));
             const uint32_t m = (ok && jj < MS) ? 0xffffffffu : 0u;
             raw[s] = u32x2{t.x & m, t.y & m};
         }
@@ -602,7 +604,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void m
     if (c >= (uint32_t)sg.NC) return;
     const uint32_t bh = fdiv(c, sg.div_CT);
     const int cp0 = (int)(c - bh * sg.div_CT.d) * 64;   // first record element of the tile
-    const int M = g.M, MS = g.M * g.TP, NK = (MS + 31) >> 5;
+    const int M = g.M, NR = g.M * g.TP, MS = NR * g.RD, NK = (MS + 31) >> 5;
     const int i0 = itile * (4 * ROWS) + wave * ROWS;    // first query block of this wave
     const bool active = i0 < M;                         // then i0 + ROWS <= roundup(M, 32): inside Wb's rows
     const int rt0 = active ? i0 >> 4 : 0;
@@ -618,7 +620,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void m
 
     // ---- stage A: unit (li', group of 8 source records) -> 4 packed operands.
     const int units = 16 * 4 * NK;                      // <= 512: at most two per thread
-    const uint16_t* base = SZ + (size_t)bh * MS * REC;
+    const uint16_t* base = SZ + (size_t)bh * NR * REC;
     u32x2 raw[2][8];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void m
         for (int s = 0; s < 8; ++s) {
             // Clamped address, then a mask: the load stays unconditional.
             const int jj = 8 * (u >> 4) + s;
-            const u32x2 t = *reinterpret_cast<const u32x2*>(base + (size_t)(jj < MS ? jj : MS - 1) * REC + colc);
+            const u32x2 t = *reinterpret_cast<const u32x2*>(base + (size_t)((jj < MS ? jj : MS - 1) / g.RD) * REC + colc);
             const uint32_t m = (ok && jj < MS) ? 0xffffffffu : 0u;
             raw[p][s] = u32x2{t.x & m, t.y & m};
         }
@@ -1114,7 +1116,7 @@ hipError_t run_d(const Launch& L0) {
     const bool fused = L.path == MHLA_PATH_FUSED;
     // IT: 64-block tiles of query blocks; NK: 32-record k-steps over the
     // M * TP source records.
-    const int IT = (g.M + 63) / 64, NK = (g.M * g.TP + 31) / 32;
+    const int IT = (g.M + 63) / 64, NK = (g.M * g.TP * g.RD + 31) / 32;
     WConv wc;
     wc.M = g.M;
     wc.TP = g.TP;
@@ -1124,6 +1126,7 @@ hipError_t run_d(const Launch& L0) {
     wc.nchunks_t = IT * 64 * wc.NKt * 32 / 8;
     wc.WD = g.WD;
     wc.WM = g.WM;
+    wc.RD = g.RD;
     wc.first_wg = 0;
     wc.nconv = 0;
     wc.wbt = static_cast<uint16_t*>(L.wbt);

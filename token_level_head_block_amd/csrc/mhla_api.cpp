@@ -136,6 +136,10 @@ void set_token_parts(mhla::Geo& g, const Shape& s) {
     g.div_AP = mhla::make_fastdiv((uint32_t)g.AP);
 }
 
+// k-slots per summary record in the bf16 causal form's mixing: W's bf16
+// high and low parts.
+constexpr int kCausalWParts = 2;
+
 struct Layout {
     size_t sz, st, zt, wb, total;   // byte offsets of the regions, total size
 };
@@ -152,8 +156,12 @@ Layout layout(const Shape& s) {
     L.wb = L.zt + align_up(r12 * (size_t)s.D * 4);
     // bf16 problems: W converted to bf16, rows padded to a multiple of 64 and
     // columns to a multiple of 32 (the mixing kernel's tile sizes).
+    // columns: one per k-slot of the mixing product (token parts, or the causal
+    // form's sub-chunks with W's high and low parts)
+    const int64_t kslots = chunks_contiguous(s) ? (int64_t)cp * kCausalWParts : cp;
     const size_t wb = s.dtype == MHLA_BF16
-                          ? (size_t)((s.M * cp + 63) / 64 * 64) * (size_t)((s.M * (tp > cp ? tp : cp) + 31) / 32 * 32) * 2
+                          ? (size_t)((s.M * cp + 63) / 64 * 64) *
+                                (size_t)((s.M * (tp > kslots ? tp : kslots) + 31) / 32 * 32) * 2
                           : 0;
     L.total = L.wb + align_up(wb);
     return L;
@@ -250,6 +258,7 @@ mhla::Geo make_geo(const Shape& s, float eps) {
     g.div_TP = g.div_AP = mhla::make_fastdiv(1u);
     g.WD = 1;
     g.WM = g.M;
+    g.RD = 1;
     g.eps = eps;
     return g;
 }
@@ -328,6 +337,10 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
             L.g.WD = cp;
             L.g.WM = (int32_t)s.M;
         }
+        // The causal mixtures take W as a bf16 high and low part: signed W can
+        // make the partial row sums over earlier blocks cancel, and W rounded
+        // to bf16 would then dominate the error.
+        L.g.RD = kCausalWParts;
     }
     L.tune = choose_tuning(s);
     apply_variant(L.tune, variant);
