@@ -36,8 +36,12 @@
  * - Validation errors are returned before any HIP call; in that case nothing
  *   is enqueued.  Faults inside kernels surface at the caller's next
  *   synchronisation of `stream`.
- * - The library holds no global state and is safe to call from several
- *   threads; calls that share a workspace must not overlap in time.
+ * - The library holds no global state (apart from mhla_forward_noalloc's
+ *   scratch) and is safe to call from several threads; calls that share a
+ *   workspace must not overlap in time.
+ * - Fault injection for tests: with MHLA_FAIL_ALLOC=1 in the environment,
+ *   every stream-ordered workspace allocation fails, so the entry points that
+ *   allocate return MHLA_ERR_ALLOC without enqueueing anything.
  */
 #ifndef MHLA_H
 #define MHLA_H

@@ -178,6 +178,32 @@ def test_noalloc_validation(L):
                                   None) == mh.MHLA_OK
 
 
+def test_injected_allocation_failure(L, monkeypatch):
+    """MHLA_FAIL_ALLOC=1 makes every entry point that allocates its workspace
+    on the stream return MHLA_ERR_ALLOC before any HIP call (nothing is
+    enqueued); entry points given a workspace do not allocate."""
+    monkeypatch.setenv("MHLA_FAIL_ALLOC", "1")
+    g, b = cfg2()
+    assert L.mhla_forward(BIG, 2 * BIG, 3 * BIG, 4 * BIG, ctypes.byref(g), ctypes.byref(b), 5 * BIG,
+                          None) == mh.MHLA_ERR_ALLOC
+    assert call_fwd(L, g, b, ws=None, ws_bytes=0) == mh.MHLA_ERR_ALLOC
+    for fn in (L.mhla_backward, L.mhla_causal_backward):
+        gg, bb = (g, b) if fn is L.mhla_backward else (mh.make_grid(1, 6, 64, mh.MHLA_BF16, (1, 4096)),
+                                                     mh.make_block((1, 256)))
+        assert fn(BIG, 2 * BIG, 3 * BIG, 4 * BIG, 5 * BIG, ctypes.byref(gg), ctypes.byref(bb), 6 * BIG, 7 * BIG,
+                  8 * BIG, 9 * BIG, None, 0, None, None) == mh.MHLA_ERR_ALLOC
+    gs, bs = mh.make_grid(2, 3, 64, mh.MHLA_BF16, (1, 256)), mh.make_block((1, 64))
+    assert L.mhla_causal_stream(BIG, 2 * BIG, 3 * BIG, 4 * BIG, 10, ctypes.byref(gs), ctypes.byref(bs), 0,
+                                6 * BIG, 10, 7 * BIG, None, 0, None) == mh.MHLA_ERR_ALLOC
+    # validation still comes first, and a caller workspace needs no allocation
+    assert call_fwd(L, g, mh.make_block((15, 16)), ws=None, ws_bytes=0) == mh.MHLA_ERR_INVALID_ARG
+    assert call_fwd(L, g, b, q=None, ws=None, ws_bytes=0) == mh.MHLA_ERR_INVALID_ARG
+    # mhla_forward_noalloc allocates nothing: its rejection of a large problem is unchanged
+    g1 = mh.make_grid(32, 6, 64, mh.MHLA_BF16, (64, 64), 1e-6)
+    assert L.mhla_forward_noalloc(BIG, 2 * BIG, 3 * BIG, 4 * BIG, ctypes.byref(g1), ctypes.byref(mh.make_block((8, 8))),
+                                  5 * BIG, None) == mh.MHLA_ERR_UNSUPPORTED
+
+
 def test_launch_plan(L):
     g, b = cfg2()
     three = ["block_kv_summary", "mix_summaries", "query_apply"]

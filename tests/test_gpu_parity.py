@@ -290,6 +290,24 @@ def test_side_stream_and_stage_events():
     assert all(t > 0 for t in times)
 
 
+def test_injected_allocation_failure_enqueues_nothing(monkeypatch):
+    """MHLA_FAIL_ALLOC=1: mhla_forward returns MHLA_ERR_ALLOC and the output
+    keeps its contents (nothing ran); without it the same call succeeds."""
+    p = synth.Problem("fail-alloc", 1, 2, 64, (32, 32), (8, 8))
+    q, k, v, W = synth.make_inputs(p, seed=28)
+    run = Run(p, q, k, v, W)
+    out = torch.full_like(run.q, 7.0)
+    monkeypatch.setenv("MHLA_FAIL_ALLOC", "1")
+    say("  [gpu] mhla_forward with MHLA_FAIL_ALLOC=1")
+    assert mh.mhla_forward(run.q, run.k, run.v, run.W, run.g, run.b, out) == mh.MHLA_ERR_ALLOC
+    torch.cuda.synchronize()
+    assert (out == 7.0).all().item()
+    monkeypatch.delenv("MHLA_FAIL_ALLOC")
+    assert mh.mhla_forward(run.q, run.k, run.v, run.W, run.g, run.b, out) == mh.MHLA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), run.forward().view(torch.int16))
+
+
 def test_empty_problem_on_gpu():
     g = mh.make_grid(0, 6, 64, mh.MHLA_BF16, (256, 256))
     x = torch.empty(0, 65536, 6, 64, dtype=torch.bfloat16, device="cuda")

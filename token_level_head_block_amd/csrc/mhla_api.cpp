@@ -174,6 +174,20 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// Stream-ordered workspace allocation of the entry points that allocate.
+// MHLA_FAIL_ALLOC=1 in the environment makes it fail without calling HIP (a
+// fault-injection hook for testing the error path: the call then returns
+// MHLA_ERR_ALLOC and enqueues nothing).
+mhla_status alloc_workspace(void** ws, size_t bytes, hipStream_t stream) {
+    const char* f = std::getenv("MHLA_FAIL_ALLOC");
+    if (f && f[0] == '1' && f[1] == 0) return MHLA_ERR_ALLOC;
+    if (hipMallocAsync(ws, bytes, stream) != hipSuccess || !*ws) {
+        (void)hipGetLastError();
+        return MHLA_ERR_ALLOC;
+    }
+    return MHLA_OK;
+}
+
 int env_int(const char* name, int dflt) {
     const char* v = std::getenv(name);
     if (!v || !*v) return dflt;
@@ -314,10 +328,8 @@ mhla_status forward_impl(const void* q, const void* k, const void* v, const floa
             return MHLA_ERR_INVALID_ARG;
     } else {
         if (!allow_alloc || ws_bytes != 0) return MHLA_ERR_INVALID_ARG;
-        if (hipMallocAsync(&ws, lay.total, stream) != hipSuccess || !ws) {
-            (void)hipGetLastError();
-            return MHLA_ERR_ALLOC;
-        }
+        const mhla_status as = alloc_workspace(&ws, lay.total, stream);
+        if (as != MHLA_OK) return as;
         owned = true;
     }
     mhla::Launch L;
@@ -484,10 +496,8 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
             if (overlaps(ws, need, outs[a], outsz[a])) return MHLA_ERR_INVALID_ARG;
     } else {
         if (ws_bytes != 0) return MHLA_ERR_INVALID_ARG;
-        if (hipMallocAsync(&ws, need, stream) != hipSuccess || !ws) {
-            (void)hipGetLastError();
-            return MHLA_ERR_ALLOC;
-        }
+        const mhla_status as = alloc_workspace(&ws, need, stream);
+        if (as != MHLA_OK) return as;
         owned = true;
     }
     char* base = static_cast<char*>(ws);
@@ -620,10 +630,8 @@ mhla_status layer_impl(const void* x, const float* W, const mhla_grid* grid, con
             if (sp.p && overlaps(ws, lay.total, sp.p, sp.n)) return MHLA_ERR_INVALID_ARG;
     } else {
         if (ws_bytes != 0) return MHLA_ERR_INVALID_ARG;
-        if (hipMallocAsync(&ws, lay.total, stream) != hipSuccess || !ws) {
-            (void)hipGetLastError();
-            return MHLA_ERR_ALLOC;
-        }
+        const mhla_status as = alloc_workspace(&ws, lay.total, stream);
+        if (as != MHLA_OK) return as;
         owned = true;
     }
     char* base = static_cast<char*>(ws);
@@ -745,10 +753,8 @@ mhla_status stream_impl(const void* q, const void* k, const void* v, const float
         if (overlaps(ws, need, out, tbytes) || overlaps(ws, need, state, sbytes)) return MHLA_ERR_INVALID_ARG;
     } else {
         if (ws_bytes != 0) return MHLA_ERR_INVALID_ARG;
-        if (hipMallocAsync(&ws, need, stream) != hipSuccess || !ws) {
-            (void)hipGetLastError();
-            return MHLA_ERR_ALLOC;
-        }
+        const mhla_status as = alloc_workspace(&ws, need, stream);
+        if (as != MHLA_OK) return as;
         owned = true;
     }
     mhla::StreamLaunch S;
@@ -895,7 +901,11 @@ mhla_status mhla_layer_forward(const void* x, const float* W, const mhla_grid* g
 }
 
 const char* mhla_status_string(mhla_status status) {
-    switch (status) {
+    // C callers may pass any int: read it as one.
+    static_assert(sizeof(mhla_status) == sizeof(int), "mhla_status is an int-sized enum");
+    int code = 0;
+    std::memcpy(&code, &status, sizeof(code));
+    switch (code) {
         case MHLA_OK: return "MHLA_OK";
         case MHLA_ERR_INVALID_ARG: return "MHLA_ERR_INVALID_ARG: invalid argument";
         case MHLA_ERR_UNSUPPORTED: return "MHLA_ERR_UNSUPPORTED: unsupported head_dim, dtype or size";
