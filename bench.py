@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--stream-chunks", type=int, default=0,
                     help="with --path causal: stream the sequence through mhla_causal_stream in calls of this "
                          "many chunks (one step = the whole sequence)")
-    ap.add_argument("--w", choices=["gaussian", "local", "identity", "ones"], default="gaussian")
+    ap.add_argument("--w", choices=["gaussian", "local", "identity", "ones", "linear", "cos", "exp", "gaussian-dmax"],
+                    default="gaussian")
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough to exceed 2x the MALL)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--out", default="", help="also write the JSON line to this file")

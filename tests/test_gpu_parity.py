@@ -240,11 +240,12 @@ def test_full_workloads_all_outputs(cfg_index):
     assert np.isfinite(got_f).all() and err_f <= TOL[p.dtype]
 
 
-@pytest.mark.parametrize("w_kind", ["identity", "ones", "local"])
+@pytest.mark.parametrize("w_kind", ["identity", "ones", "local", "linear", "cos", "exp", "gaussian-dmax"])
 @pytest.mark.parametrize("path", [mh.MHLA_PATH_3KERNEL, mh.MHLA_PATH_FUSED], ids=["3kernel", "fused"])
 @pytest.mark.parametrize("shape", [((64, 64), (8, 8)), ((64, 64), (2, 2))], ids=["M64", "M1024"])
 def test_special_coefficient_matrices(w_kind, path, shape):
-    """W = I (per-block attention), W = 1/M (global attention), sparse local W."""
+    """W = I (per-block attention), W = 1/M (global attention), sparse local W,
+    and the module's linear, cos, exp and max-distance Gaussian transforms."""
     grid, block = shape
     p = synth.Problem("special", 1, 2, 64 if block[0] == 8 else 32, grid, block)
     q, k, v, W = synth.make_inputs(p, seed=23, w_kind=w_kind)

@@ -53,3 +53,30 @@ def test_jittered_w_row_sums_stay_positive():
     for p in synth.CONFIGS:
         W = synth.make_inputs(p.with_(batch=1, heads=1), seed=0)[3].astype(np.float64)
         assert W.sum(1).min() > 0.4
+
+
+def test_transform_priors():
+    """The module's other distance transforms on a 2x2 block grid (distances
+    0, 1, 1, sqrt 2 from block 0; max distance sqrt 2), by hand, rows sum to 1."""
+    r2 = np.sqrt(2.0)
+    d = np.array([0.0, 1.0, 1.0, r2])
+    expect = {
+        "linear": 1.0 - d / r2,
+        "cos": np.cos(d / r2 * np.pi / 4),
+        "exp": np.exp(-d / 3.0),
+        "gaussian-dmax": np.exp(-d * d / (2 * (r2 / 3) ** 2)),
+    }
+    for kind, g in expect.items():
+        W = synth.transform_prior((2, 2), kind)
+        np.testing.assert_allclose(W[0], g / g.sum(), rtol=1e-14)
+        np.testing.assert_allclose(W.sum(1), 1.0, rtol=1e-14)
+    # the linear transform gives the farthest block no weight; the separable
+    # Gaussian equals the distance prior
+    assert synth.transform_prior((2, 2), "linear")[0, 3] == 0.0
+    sep = np.exp(-(np.subtract.outer(np.arange(3), np.arange(3)) ** 2) / 18.0)
+    K = np.kron(sep, sep)
+    np.testing.assert_allclose(K / K.sum(1, keepdims=True), synth.distance_prior((3, 3), 3.0), rtol=1e-14)
+    p = synth.Problem("t", 1, 1, 32, (16, 16), (4, 4), dtype=synth.F32)
+    for kind in synth.TRANSFORMS:
+        W = synth.make_inputs(p, seed=0, w_kind=kind)[3]
+        assert W.shape == (16, 16) and (W >= 0).all()

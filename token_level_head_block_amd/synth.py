@@ -122,6 +122,36 @@ def local_prior(blocks_per_axis, thres: float = 1.5) -> np.ndarray:
     return g / g.sum(axis=1, keepdims=True)
 
 
+def transform_prior(blocks_per_axis, kind: str, exp_sigma: float = 3.0) -> np.ndarray:
+    """The module's distance transforms of the block-centre distance D
+    (Euclidean, block units; 171host.com repost, section 七, BlockDistanceConv),
+    each row scaled to sum to 1:
+      "linear":      1 - D / max D
+      "cos":         cos(D / max D * pi / 4)
+      "exp":         exp(-D / exp_sigma)
+      "gaussian-dmax": exp(-D^2 / (2 s^2)) with s = max D / 3
+    A Gaussian of the Euclidean distance is separable, exp(-dy^2/2s^2) exp(-dx^2/2s^2),
+    so the per-axis (separable) Gaussian is the same matrix as distance_prior."""
+    c = block_centres(blocks_per_axis)
+    D = np.sqrt(((c[:, None, :] - c[None, :, :]) ** 2).sum(-1))
+    dmax = D.max() if D.max() > 0 else 1.0
+    if kind == "linear":
+        g = 1.0 - D / dmax
+    elif kind == "cos":
+        g = np.cos(D / dmax * np.pi / 4)
+    elif kind == "exp":
+        g = np.exp(-D / exp_sigma)
+    elif kind == "gaussian-dmax":
+        s = dmax / 3.0
+        g = np.exp(-D * D / (2.0 * s * s))
+    else:
+        raise ValueError(f"unknown transform {kind!r}")
+    return g / g.sum(axis=1, keepdims=True)
+
+
+TRANSFORMS = ("linear", "cos", "exp", "gaussian-dmax")
+
+
 def _rng(seed) -> np.random.Generator:
     return np.random.default_rng(seed)
 
@@ -138,7 +168,8 @@ def make_inputs(p: Problem, seed, w_kind: str = "gaussian"):
 
     q, k, v: [B, N, H, d] (uint16 bf16 bits or float32); W: float32 [M, M].
     w_kind: "gaussian" (distance prior + jitter), "identity", "ones" (1/M),
-    or "local" (sparse local prior, no jitter).
+    "local" (sparse local prior, no jitter), or one of TRANSFORMS (the
+    module's other distance transforms, row-normalised, no jitter).
     """
     rng = _rng(seed)
     shape = (p.batch, p.n_tokens, p.heads, p.head_dim)
@@ -155,6 +186,8 @@ def make_inputs(p: Problem, seed, w_kind: str = "gaussian"):
         W = np.full((M, M), 1.0 / M)
     elif w_kind == "local":
         W = local_prior(p.blocks_per_axis)
+    elif w_kind in TRANSFORMS:
+        W = transform_prior(p.blocks_per_axis, w_kind)
     else:
         raise ValueError(f"unknown w_kind {w_kind!r}")
     return q, k, v, np.ascontiguousarray(W, dtype=np.float32)
