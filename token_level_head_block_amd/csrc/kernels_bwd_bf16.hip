@@ -68,12 +68,17 @@ __device__ __forceinline__ void rows_c_k_e(const uint16_t* __restrict__ m, int t
 //   dSt += u dnum^T, dzt += u dden on v_mfma_f32_16x16x16_bf16 with the 16
 //   tokens as k, both operands read transposed from the wave's LDS slice.
 // =====================================================================
-// At d = 64 a wave keeps two operand copies of St (64 registers), the dSt
-// accumulators (64) and a token group's working set, more than 256 registers:
-// such workgroups hold 4 waves (heads) so that each wave may use the
-// accumulation registers too.
-template <int D>
-__global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint16_t* __restrict__ Q,
+// LOP = false: a wave keeps two operand copies of St in registers (at d = 64:
+// 64 registers), zt's operand words and zt itself, and with the dSt
+// accumulators (64) and a token group's working set that is more than 256
+// registers at d = 64: one wave per SIMD.
+// LOP = true (d = 64, blocks of >= 128 tokens): the transposed copy of St
+// (rows c, k = e), zt's operand words and zt live in the wave's LDS slice and
+// are read where used, so a wave fits in 256 registers: two waves per SIMD
+// (dit-s2-256x256 bwd_query 73.5 -> 64.3 us; with 64-token blocks the extra
+// staging per block costs more than it saves).
+template <int D, bool LOP>
+__global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_per_eu(LOP ? 2 : 1))) void bwd_query_bf16(const uint16_t* __restrict__ Q,
                                                       const uint16_t* __restrict__ dO,
                                                       const uint16_t* __restrict__ St,
                                                       const float* __restrict__ Zt, uint16_t* __restrict__ dQ,
@@ -81,7 +86,9 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
                                                       const Geo g) {
     constexpr int RT = D / 16, KS = D / 32, REC = D * D + D;
     constexpr int OSTR = D + 8, TS = 20;   // TS: transposed tile row, 16 tokens + 4 padding
-    constexpr int SLICE = 16 * OSTR + 2 * D * TS;
+    constexpr int A2U = LOP ? RT * KS * 64 * 8 : 0;   // bf16 values of the transposed operand copy
+    constexpr int ZU = LOP ? 2 * KS * 64 * 8 : 0;     // bf16 values of zt's high and low operand words
+    constexpr int SLICE = 16 * OSTR + 2 * D * TS + A2U + ZU + (LOP ? 2 * D : 0);   // + zt (fp32)
     constexpr int MAXW = D == 64 ? 4 : 8;
     __shared__ __attribute__((aligned(16))) uint16_t lds[MAXW * SLICE];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -102,25 +109,48 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
     uint16_t* sout = lds + wave * SLICE;
     uint16_t* dnT = sout + 16 * OSTR;   // [e][token]
     uint16_t* uT = dnT + D * TS;        // [c][token]
+    u32x4* a2l = reinterpret_cast<u32x4*>(uT + D * TS);   // [rt][kk][lane] operand words
 
     // ---- operands of this block's mixed summary
     const uint16_t* sb = St + (size_t)blk * (D * D);
     const float* zb = Zt + (size_t)blk * D;
-    u32x4 a1[RT][KS], a2[RT][KS], zhi[KS], zlo[KS];
+    u32x4 a1[RT][KS], a2r[LOP ? 1 : RT][LOP ? 1 : KS], zhi[LOP ? 1 : KS], zlo[LOP ? 1 : KS];
     rows_e_k_c<D>(sb, t, gq, a1);
-    rows_c_k_e<D>(sb, t, 4 * RT * gq, a2);
+    u32x4* zl2 = a2l + A2U / 8;   // [hi/lo][kk][lane] operand words of zt
+    float* zl = reinterpret_cast<float*>(zl2 + ZU / 8);   // zt
+    float zc[LOP ? 1 : 4 * RT];   // zt at this lane's output channels 4*RT*gq + ..
+    if constexpr (LOP) {
+        u32x4 a2[RT][KS];
+        rows_c_k_e<D>(sb, t, 4 * RT * gq, a2);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) a2l[(rt * KS + kk) * 64 + lane] = a2[rt][kk];
+    } else {
+        rows_c_k_e<D>(sb, t, 4 * RT * gq, a2r);
+    }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
         const f32x4 x = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8);
         const f32x4 y = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8 + 4);
         const float z[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-        split_zt(z, zhi[kk], zlo[kk]);
+        if constexpr (LOP) {
+            u32x4 hi, lo;
+            split_zt(z, hi, lo);
+            zl2[kk * 64 + lane] = hi;
+            zl2[(KS + kk) * 64 + lane] = lo;
+        } else {
+            split_zt(z, zhi[kk], zlo[kk]);
+        }
     }
-    float zc[4 * RT];   // zt at this lane's output channels 4*RT*gq + ..
+    if constexpr (LOP) {
+        if (lane < D / 4) *reinterpret_cast<f32x4*>(zl + 4 * lane) = *reinterpret_cast<const f32x4*>(zb + 4 * lane);
+    } else {
 #pragma unroll
-    for (int u = 0; u < RT; ++u) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(zb + 4 * RT * gq + 4 * u);
-        zc[4 * u] = x.x; zc[4 * u + 1] = x.y; zc[4 * u + 2] = x.z; zc[4 * u + 3] = x.w;
+        for (int u = 0; u < RT; ++u) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(zb + 4 * RT * gq + 4 * u);
+            zc[4 * u] = x.x; zc[4 * u + 1] = x.y; zc[4 * u + 2] = x.z; zc[4 * u + 3] = x.w;
+        }
     }
 
     const int row = g.H * D;
@@ -140,7 +170,7 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
     }
 
     struct Raw {
-        u32x4 qv[KS], go[RT / 2], qo[RT / 2];
+        u32x4 qv[KS], go[RT / 2], qo[LOP ? 1 : RT / 2];
         int off;
         bool ok;
     };
@@ -153,10 +183,16 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
 #pragma unroll
         for (int u = 0; u < RT / 2; ++u) {
             R.go[u] = *reinterpret_cast<const u32x4*>(gb + R.off + 4 * RT * gq + 8 * u);
-            R.qo[u] = *reinterpret_cast<const u32x4*>(qb + R.off + 4 * RT * gq + 8 * u);
+            if constexpr (!LOP) R.qo[u] = *reinterpret_cast<const u32x4*>(qb + R.off + 4 * RT * gq + 8 * u);
         }
     };
     auto compute = [&](const Raw& R) {
+        // q at this lane's output channels (for phi'); with LOP loaded here, from
+        // the lines qv already brought in
+        u32x4 qo[RT / 2];
+#pragma unroll
+        for (int u = 0; u < RT / 2; ++u)
+            qo[u] = LOP ? *reinterpret_cast<const u32x4*>(qb + R.off + 4 * RT * gq + 8 * u) : R.qo[LOP ? 0 : u];
         // u = phi(q) as the B operand (k = channel kk*32 + gq*8 + s, column = token t)
         u32x4 bq[KS];
 #pragma unroll
@@ -171,8 +207,8 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
         for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
             for (int r = 0; r < RT; ++r) acc[r] = mfma_bf16(a1[r][kk], bq[kk], acc[r]);
-            accd = mfma_bf16(zhi[kk], bq[kk], accd);
-            accd = mfma_bf16(zlo[kk], bq[kk], accd);
+            accd = mfma_bf16(LOP ? zl2[kk * 64 + lane] : zhi[LOP ? 0 : kk], bq[kk], accd);
+            accd = mfma_bf16(LOP ? zl2[(KS + kk) * 64 + lane] : zlo[LOP ? 0 : kk], bq[kk], accd);
         }
         const float inv = 1.f / (accd[0] + g.eps);
         // Upstream gradient at this lane's channels e = 4*RT*gq + 4r + v (zero past the block).
@@ -209,12 +245,13 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                du[rt] = mfma_bf16(a2[rt][kk], b2h[kk], du[rt]);
-                du[rt] = mfma_bf16(a2[rt][kk], b2l[kk], du[rt]);
+                const u32x4 a2 = LOP ? a2l[(rt * KS + kk) * 64 + lane] : a2r[LOP ? 0 : rt][LOP ? 0 : kk];
+                du[rt] = mfma_bf16(a2, b2h[kk], du[rt]);
+                du[rt] = mfma_bf16(a2, b2l[kk], du[rt]);
             }
         float ql[4 * RT];
 #pragma unroll
-        for (int u = 0; u < RT / 2; ++u) unpack8(R.qo[u], ql + 8 * u);
+        for (int u = 0; u < RT / 2; ++u) unpack8(qo[u], ql + 8 * u);
         uint32_t wv[2 * RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -222,7 +259,7 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) void bwd_query_bf16(const uint
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int cl = 4 * rt + v;
-                x[v] = (du[rt][v] + zc[cl] * dden) * phi_grad(ql[cl]);
+                x[v] = (du[rt][v] + (LOP ? zl[4 * RT * gq + cl] : zc[LOP ? 0 : cl]) * dden) * phi_grad(ql[cl]);
             }
             wv[2 * rt] = pack_bf16(x[0], x[1]);
             wv[2 * rt + 1] = pack_bf16(x[2], x[3]);
@@ -722,9 +759,14 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     Geo gq = heads(L.tune.bwdq_heads > 0 ? L.tune.bwdq_heads : bq_max);
     gq.AP = B.q_parts > 1 && B.dpart ? B.q_parts : 1;
     gq.div_AP = make_fastdiv((uint32_t)gq.AP);
-    bwd_query_bf16<D><<<gq.B * gq.M * gq.AP * gq.HG, 64 * gq.G, 0, L.stream>>>(
-        static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(B.dout), static_cast<const uint16_t*>(L.st),
-        L.zt, static_cast<uint16_t*>(B.dq), B.dst, B.dpart, gq);
+    if (D == 64 && g.T >= 128)
+        bwd_query_bf16<D, true><<<gq.B * gq.M * gq.AP * gq.HG, 64 * gq.G, 0, L.stream>>>(
+            static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(B.dout), static_cast<const uint16_t*>(L.st),
+            L.zt, static_cast<uint16_t*>(B.dq), B.dst, B.dpart, gq);
+    else
+        bwd_query_bf16<D, false><<<gq.B * gq.M * gq.AP * gq.HG, 64 * gq.G, 0, L.stream>>>(
+            static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(B.dout), static_cast<const uint16_t*>(L.st),
+            L.zt, static_cast<uint16_t*>(B.dq), B.dst, B.dpart, gq);
     if (gq.AP > 1) {
         const size_t n = (size_t)g.BH * g.M * (D * D + D);
         fold_parts_bf16<float><<<(unsigned)((n + 255) / 256), 256, 0, L.stream>>>(B.dpart, B.dst, g.BH * g.M, gq.AP,
