@@ -233,14 +233,26 @@ def measure_copy(torch, nbytes, reps=20):
 
 def backward_bytes(p, general=False, causal=False):
     """Algorithmic HBM bytes of each backward stage (compulsory reads + writes).
-    The MFMA path keeps the summaries and their gradients as bf16 records; the
-    general path (and the causal one) as fp32 records of d*d + d values, and the
-    causal path also passes each token's dnum (d fp32) and dden (fp32) from the
-    query side to the key/value side."""
+    The MFMA paths keep the summaries and their gradients as bf16 records (the
+    causal one also passes each token's 1 / den and dden, two fp32 values, from
+    the query side to the key/value side, and each pair's in-chunk dW[i, i]
+    terms); the general kernels use fp32 records of d*d + d values, and their
+    causal form passes each token's dnum (d fp32) and dden (fp32)."""
     B, N, H, d, M = p.batch, p.n_tokens, p.heads, p.head_dim, p.n_blocks
     tensor = B * N * H * d * p.elem_bytes
     P = B * H
     w = M * M * 4
+    if causal and not general:
+        rec = P * M * (d * d + d) * 2
+        st = P * M * d * d * 2
+        zt = P * M * d * 4
+        tok = B * N * H * 8
+        return {
+            "recompute (summary + causal mix)": 2 * tensor + rec + rec + w + st + zt,
+            "query side": 4 * tensor + st + zt + tensor + rec + tok + P * M * 4,
+            "mix_transposed + dW": rec + w + st + zt + 2 * rec + P * M * 4 + w,
+            "key/value side": 4 * tensor + tok + st + zt + 2 * tensor,
+        }
     if general or causal:
         rec = P * M * (d * d + d) * 4
         tok = B * N * H * (d + 1) * 4 if causal else 0
@@ -290,7 +302,12 @@ def bench_backward(args, p, torch, mh, synth):
                       p.grid, p.eps)
     bl = mh.make_block(p.block)
     causal = args.path == "causal"
-    general = causal or not (p.dtype == synth.BF16 and p.head_dim <= 64)
+    # matrix-core kernels: bf16 with d <= 64 (causal: chunks whole, i.e. at most
+    # one sub-chunk per chunk in the forward)
+    general = not (p.dtype == synth.BF16 and p.head_dim <= 64)
+    if causal and not general:
+        split = next((b for b in p.block if b > 1), 1)   # the axis sub-chunks would split
+        general = split % 2 == 0 and p.block_tokens >= 512 and p.n_blocks * 2 <= 256
     wsize = mh.mhla_causal_backward_workspace_bytes if causal else mh.mhla_backward_workspace_bytes
     call = mh.mhla_causal_backward if causal else mh.mhla_backward
     ws_bytes = wsize(gr, bl)

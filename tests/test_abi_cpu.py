@@ -270,9 +270,14 @@ def test_causal_backward_workspace_and_validation(L):
     seq = mh.make_grid(1, 6, 64, mh.MHLA_BF16, (1, 65536))
     chunk = mh.make_block((1, 256))
     need = mh.mhla_causal_backward_workspace_bytes(seq, chunk)
-    rec = 6 * 256 * (64 * 64 + 64) * 4
     toks = 65536 * 6
-    assert need >= 4 * rec + toks * 64 * 4 + toks * 4 + 6 * 256 * 4
+    # bf16, d = 64, whole chunks: the matrix-core backward's regions plus per-token
+    # 1 / den and dden (fp32 pairs) and the per-pair dW[i, i] terms
+    assert need == mh.mhla_backward_workspace_bytes(seq, chunk) + toks * 8 + 6 * 256 * 4
+    # d = 128: the general kernels' fp32 records (four kinds) and per-token dnum (fp32), dden
+    s128 = mh.make_grid(1, 6, 128, mh.MHLA_BF16, (1, 65536))
+    rec = 6 * 256 * (128 * 128 + 128) * 4
+    assert mh.mhla_causal_backward_workspace_bytes(s128, chunk) >= 4 * rec + toks * 128 * 4 + toks * 4 + 6 * 256 * 4
     # 2D blocks are not contiguous runs of raster indices: no workspace, and the call says so
     g, b = cfg2()
     assert mh.mhla_causal_backward_workspace_bytes(g, b) == 0

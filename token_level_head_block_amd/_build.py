@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmhla.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["mhla_api.cpp", "kernels_bf16.hip", "kernels_bwd_bf16.hip", "kernels_bwd_generic.hip", "kernels_causal_bf16.hip", "kernels_layer_bf16.hip", "kernels_f32.hip", "kernels_stream.hip"]
+SOURCES = ["mhla_api.cpp", "kernels_bf16.hip", "kernels_bwd_bf16.hip", "kernels_bwd_generic.hip", "kernels_causal_bf16.hip", "kernels_causal_bwd_bf16.hip", "kernels_layer_bf16.hip", "kernels_f32.hip", "kernels_stream.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
 ARCH = os.environ.get("PYTORCH_ROCM_ARCH", "gfx950")

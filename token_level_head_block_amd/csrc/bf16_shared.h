@@ -54,7 +54,7 @@ struct WConv {
     int32_t M, NK, nchunks;   // NK = Jpad / 32; nchunks = Ipad * Jpad / 8; 0 = none
     int32_t first_wg, nconv;  // workgroups [first_wg, first_wg + nconv) of the launch convert
     uint16_t* wbt;            // if not null, W^T is converted to this buffer as well
-    int32_t causal;           // nonzero: keep only W[i][j] with j < i (earlier blocks)
+    int32_t causal;           // nonzero: keep only W[i][j] with j < i (earlier blocks; in W^T, later ones)
     int32_t TP;               // token parts: column j' of the operand is W[i][j' / TP] (j' < M TP)
     int32_t NKt, nchunks_t;   // W^T (no token parts): NKt = roundup(M, 32) / 32, its 16-byte units
     int32_t WD, WM;           // causal sub-chunks: entry (i, j) is W[i / WD][j / WD], W is WM x WM
@@ -75,8 +75,10 @@ __device__ __forceinline__ void convert_w(const float* __restrict__ W, uint16_t*
         const int i = 16 * rt + (lane & 15), j0 = 32 * kk + 8 * (lane >> 4);
         float x[8];
         if (tr) {
+            // W^T; causal: later blocks only (source j0 + s > i)
 #pragma unroll
-            for (int s = 0; s < 8; ++s) x[s] = (i < wc.M && j0 + s < wc.M) ? W[(size_t)(j0 + s) * wc.M + i] : 0.f;
+            for (int s = 0; s < 8; ++s)
+                x[s] = (i < wc.M && j0 + s < wc.M && (!wc.causal || j0 + s > i)) ? W[(size_t)(j0 + s) * wc.M + i] : 0.f;
         } else if (wc.TP > 1 || wc.WD > 1 || wc.RD > 1) {
             // token parts: source record r = j TP + t holds part t of block j;
             // causal sub-chunks: row and column indices are sub-chunks, WD per block of W;

@@ -22,6 +22,8 @@
 
 #include <mhla.h>
 
+#include <type_traits>
+
 namespace mhla {
 namespace {
 
@@ -828,6 +830,43 @@ __global__ __launch_bounds__(256) void fill_zero(float* __restrict__ p, int n) {
 }
 
 }  // namespace
+
+hipError_t launch_mix_transposed_bf16(const BwdLaunch& B, const Geo& g) {
+    const int IT = (g.M + 63) / 64, NK = (g.M + 31) / 32;
+    MixGeo mg;
+    mg.CT = (g.D * g.D + g.D + 63) / 64;
+    mg.IT = IT;
+    mg.CPW = IT >= 4 ? 1 : 4 / IT;
+    mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
+    mg.Jpad = NK * 32;
+    mg.div_CTG = make_fastdiv(mg.CTG);
+    const hipStream_t st = B.F.stream;
+    switch (g.D) {
+        case 32: mix_transposed_bf16<32><<<g.BH * mg.CTG, 512, 0, st>>>(B.dst, B.wbt, B.ds, B.dz, g, mg); break;
+        case 64: mix_transposed_bf16<64><<<g.BH * mg.CTG, 512, 0, st>>>(B.dst, B.wbt, B.ds, B.dz, g, mg); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dw_partial_bf16(const BwdLaunch& B, const Geo& g, const uint16_t* srec) {
+    const int ntj = (g.M + 127) / 128;
+    const hipStream_t st = B.F.stream;
+    auto go = [&](auto d) {
+        constexpr int D = decltype(d)::value;
+        if (g.M <= 64)
+            dw_partial_small_bf16<D><<<B.nsplit, 512, 0, st>>>(B.dst, srec, B.part, g.M, g.BH, B.nsplit);
+        else
+            dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, st>>>(B.dst, srec, B.part, g.M, g.BH, B.nsplit,
+                                                                           ntj);
+    };
+    switch (g.D) {
+        case 32: go(std::integral_constant<int, 32>{}); break;
+        case 64: go(std::integral_constant<int, 64>{}); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t zero_f32(float* p, int n, hipStream_t stream) {
     if (n > 0) fill_zero<<<(n + 255) / 256, 256, 0, stream>>>(p, n);

@@ -75,6 +75,22 @@ struct BwdLaunch {
 // Summary and mixing kernels of the bf16 forward only (regions of F).
 hipError_t run_bf16_summaries(const Launch& L);
 hipError_t run_bwd_bf16(const BwdLaunch& B);
+// Pieces of the bf16 backward shared with the causal form: the mixing of
+// B.dst with W^T (B.wbt) into B.ds, B.dz, and the dW partial products of
+// B.dst with the summary records srec into B.part (g: one record per block).
+hipError_t launch_mix_transposed_bf16(const BwdLaunch& B, const Geo& g);
+hipError_t launch_dw_partial_bf16(const BwdLaunch& B, const Geo& g, const uint16_t* srec);
+
+// The bf16 causal backward (d = 32 or 64, chunks contiguous in raster order,
+// one sub-chunk per chunk).  B.F runs the recompute (path MHLA_PATH_CAUSAL,
+// summaries_only, wbt set); B.dst, B.ds, B.dz, B.wbt, B.part, B.nsplit as in
+// the non-causal backward; B.events: 5 events or nullptr.
+struct CausalBwdLaunch {
+    BwdLaunch B;
+    float* tsc;       // [B][N][H][2]: per token 1 / den and dden = -(g . num) / den^2
+    float* diag;      // [BH][M]: each pair's in-chunk terms of dW[i][i]
+};
+hipError_t run_causal_bwd_bf16(const CausalBwdLaunch& C);
 // The causal chunkwise apply (bf16, d = 32 or 64) after the summary and
 // mixing kernels have run with W restricted to earlier blocks.
 // The causal apply kernel on the workspace's St, zt; W's diagonal entry of

@@ -412,6 +412,28 @@ BwdLayout bwd_layout(const Shape& s) {
     return L;
 }
 
+// The bf16 causal backward on the matrix cores: d = 32 or 64 and chunks that
+// the forward runs whole (no sub-chunks).  Its workspace: the backward's
+// regions, then per-token 1 / den and dden (fp32 pairs), and the in-chunk dW terms.
+bool cbwd_supported(const Shape& s) {
+    return s.dtype == MHLA_BF16 && (s.D == 32 || s.D == 64) && chunks_contiguous(s) && causal_parts(s) == 1;
+}
+
+struct CbwdLayout {
+    BwdLayout b;
+    size_t tsc, diag, total;
+};
+
+CbwdLayout cbwd_layout(const Shape& s) {
+    CbwdLayout L;
+    L.b = bwd_layout(s);
+    const size_t toks = (size_t)s.B * (size_t)s.N * (size_t)s.H;
+    L.tsc = L.b.total;
+    L.diag = L.tsc + align_up(toks * 8);
+    L.total = L.diag + align_up((size_t)(s.B * s.H * s.M) * 4);
+    return L;
+}
+
 // The general backward path (fp32 inputs, or head_dim 128): fp32 records.
 struct GenLayout {
     size_t s, st, dst, ds, part, dnum, dden, diag, total;
@@ -457,6 +479,7 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
     if (variant & ~MHLA_VARIANT_NO_PAIR_HEADS) return MHLA_ERR_INVALID_ARG;
     if (causal && !causal_supported(s)) return MHLA_ERR_UNSUPPORTED;
     const bool fast = !causal && bwd_supported(s);
+    const bool cfast = causal && cbwd_supported(s);
     if (!dW) return MHLA_ERR_INVALID_ARG;
     if (!aligned16(dW)) return MHLA_ERR_MISALIGNED;
     const size_t wbytes = (size_t)(s.M * s.M) * 4;
@@ -485,7 +508,8 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
     }
     const BwdLayout lay = bwd_layout(s);
     const GenLayout glay = gen_layout(s, causal);
-    const size_t need = fast ? lay.total : glay.total;
+    const CbwdLayout clay = cbwd_layout(s);
+    const size_t need = fast ? lay.total : (cfast ? clay.total : glay.total);
     bool owned = false;
     if (ws) {
         if (ws_bytes < need) return MHLA_ERR_INVALID_ARG;
@@ -501,6 +525,51 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
         owned = true;
     }
     char* base = static_cast<char*>(ws);
+    if (cfast) {
+        mhla::CausalBwdLaunch C;
+        mhla::BwdLaunch& B = C.B;
+        mhla::Launch& L = B.F;
+        L.q = q; L.k = k; L.v = v; L.W = W; L.out = nullptr;
+        L.sz = base + lay.fwd.sz;
+        L.st = base + lay.fwd.st;
+        L.zt = reinterpret_cast<float*>(base + lay.fwd.zt);
+        L.wb = base + lay.fwd.wb;
+        L.wbt = base + lay.wbt;
+        L.g = make_geo(s, grid->eps);
+        L.g.RD = kCausalWParts;   // the causal mixtures take W as bf16 high and low parts
+        L.tune = choose_tuning(s);
+        apply_variant(L.tune, variant);
+        L.path = MHLA_PATH_CAUSAL;
+        L.summaries_only = 1;
+        L.events = nullptr;
+        L.stream = stream;
+        {
+            int dev = 0, cus = 0;
+            if (hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+                L.tune.num_cus = cus;
+            else
+                (void)hipGetLastError();
+        }
+        B.dout = dout;
+        B.dq = dq; B.dk = dk; B.dv = dv; B.dw = dW;
+        B.dst = reinterpret_cast<uint16_t*>(base + lay.dst);
+        B.ds = reinterpret_cast<uint16_t*>(base + lay.ds);
+        B.dz = reinterpret_cast<float*>(base + lay.dz);
+        B.wbt = reinterpret_cast<uint16_t*>(base + lay.wbt);
+        B.part = reinterpret_cast<float*>(base + lay.part);
+        B.nsplit = lay.nsplit;
+        B.kv_parts = 1;
+        B.q_parts = 1;
+        B.dpart = nullptr;
+        B.sfold = nullptr;
+        B.events = events;
+        C.tsc = reinterpret_cast<float*>(base + clay.tsc);
+        C.diag = reinterpret_cast<float*>(base + clay.diag);
+        const hipError_t err = mhla::run_causal_bwd_bf16(C);
+        if (owned) (void)hipFreeAsync(ws, stream);
+        return err == hipSuccess ? MHLA_OK : MHLA_ERR_HIP;
+    }
     if (!fast) {
         mhla::GenericBwd G;
         G.g = make_geo(s, grid->eps);
@@ -877,7 +946,7 @@ mhla_status mhla_backward_ex(const void* q, const void* k, const void* v, const 
 size_t mhla_causal_backward_workspace_bytes(const mhla_grid* grid, const mhla_block* block) {
     Shape s;
     if (check(grid, block, &s) != MHLA_OK || s.B == 0 || s.H == 0 || !causal_supported(s)) return 0;
-    return gen_layout(s, true).total;
+    return cbwd_supported(s) ? cbwd_layout(s).total : gen_layout(s, true).total;
 }
 
 mhla_status mhla_causal_backward(const void* q, const void* k, const void* v, const float* W, const void* dout,
