@@ -36,6 +36,9 @@ CASES = [
     ("cbwd-frames-3d", 1, 2, 64, (4, 6, 8), (1, 6, 8), BF, "gaussian"),
     ("cbwd-d128-T40", 2, 1, 128, (1, 200), (1, 40), BF, "gaussian"),
     ("cbwd-d128-T256", 1, 2, 128, (1, 1024), (1, 256), BF, "gaussian"),
+    # long chunks on the matrix-core path (129 chunks: no sub-chunks): five
+    # 128-token query tiles per chunk, the last one ragged
+    ("cbwd-d32-T520-M129", 1, 1, 32, (1, 129 * 520), (1, 520), BF, "gaussian"),
     ("cbwd-f32-d32-T16", 1, 2, 32, (1, 256), (1, 16), F32, "local"),
     ("cbwd-f32-d64-T100", 2, 1, 64, (1, 400), (1, 100), F32, "local"),
     ("cbwd-f32-d128-T33", 1, 1, 128, (1, 99), (1, 33), F32, "local"),

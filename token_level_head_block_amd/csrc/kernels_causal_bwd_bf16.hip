@@ -831,7 +831,11 @@ void launch_kv(const CausalBwdLaunch& C, const Geo& g) {
         static_cast<uint16_t*>(C.B.dv), g);
 }
 
-// Waves per workgroup: enough for two 16-token groups each, at most 8.
+// Waves per workgroup: enough for two 16-token groups each, at most 4.  Two
+// workgroups of 4 waves per compute unit overlap each other's staging and
+// barriers; one of 8 waves (the register file allows no second) does not
+// (dit-s2-256x256-causal-rows: query side 174 -> 167 us, key/value side
+// 149 -> 137 us; workgroups of 2 waves: 211 and 199 us).
 template <int D, bool KV>
 void launch_nw(const CausalBwdLaunch& C, const Geo& g) {
     const int nit = (g.T + 15) / 16;
@@ -840,8 +844,7 @@ void launch_nw(const CausalBwdLaunch& C, const Geo& g) {
         if constexpr (KV) launch_kv<D, NW>(C, g);
         else launch_pair<D, NW>(C, g);
     };
-    if (nit > 8) go(std::integral_constant<int, 8>{});
-    else if (nit > 4) go(std::integral_constant<int, 4>{});
+    if (nit > 4) go(std::integral_constant<int, 4>{});
     else if (nit > 2) go(std::integral_constant<int, 2>{});
     else go(std::integral_constant<int, 1>{});
 }
