@@ -118,8 +118,11 @@ enum {
                                              every query block (any M) */
     MHLA_VARIANT_NO_PAIR_HEADS = 1 << 10, /* bf16, head_dim 32, even head count: one head per wave
                                              in the summary kernel instead of head pairs */
-    MHLA_VARIANT_MIX_SPLIT = 1 << 11      /* bf16, at most 256 source records: mixing with one
+    MHLA_VARIANT_MIX_SPLIT = 1 << 11,     /* bf16, at most 256 source records: mixing with one
                                              workgroup per (pair, column tile, query-block tile) */
+    MHLA_VARIANT_APPLY_REGS = 1 << 12     /* bf16, head_dim 32 or 64: each apply wave holds St_i and
+                                             zt_i operands in registers instead of reading them from
+                                             the copy its head's waves stage in LDS */
 };
 
 /* Human-readable name of a status code (static storage, never NULL). */

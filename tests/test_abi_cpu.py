@@ -141,10 +141,11 @@ def test_variant_flags(L):
     g, b = cfg2()
     three = ["block_kv_summary", "mix_summaries", "query_apply"]
     for flag in (mh.MHLA_VARIANT_MIX_RESIDENT, mh.MHLA_VARIANT_MIX_TILED, mh.MHLA_VARIANT_MIX_SPLIT,
-                 mh.MHLA_VARIANT_NO_PAIR_HEADS, mh.MHLA_VARIANT_MIX_SPLIT | mh.MHLA_VARIANT_NO_PAIR_HEADS):
+                 mh.MHLA_VARIANT_NO_PAIR_HEADS, mh.MHLA_VARIANT_MIX_SPLIT | mh.MHLA_VARIANT_NO_PAIR_HEADS,
+                 mh.MHLA_VARIANT_APPLY_REGS):
         assert mh.mhla_launch_plan(g, b, mh.MHLA_PATH_3KERNEL | flag) == (mh.MHLA_OK, three)
     need = mh.mhla_workspace_bytes(g, b)
-    for bad in (1 << 12, 1 << 30, mh.MHLA_VARIANT_MIX_RESIDENT | mh.MHLA_VARIANT_MIX_TILED,
+    for bad in (1 << 13, 1 << 30, mh.MHLA_VARIANT_MIX_RESIDENT | mh.MHLA_VARIANT_MIX_TILED,
                 mh.MHLA_VARIANT_MIX_SPLIT | mh.MHLA_VARIANT_MIX_TILED):
         assert mh.mhla_launch_plan(g, b, bad)[0] == mh.MHLA_ERR_INVALID_ARG
         assert call_fwd(L, g, b, ws=6 * BIG, ws_bytes=need, path=bad) == mh.MHLA_ERR_INVALID_ARG

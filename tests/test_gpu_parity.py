@@ -157,6 +157,34 @@ def test_d32_head_pairs(case):
         assert np.array_equal(a, b)
 
 
+APPLY_CASES = [
+    ("apply-d64-T256-H3", 1, 3, 64, (64, 64), (16, 16), BF, 1.0),        # two heads per workgroup: one slot idle
+    ("apply-d32-T64-H5", 2, 5, 32, (32, 32), (8, 8), BF, 1.0),           # one wave per head, odd head count
+    ("apply-d64-T200", 1, 2, 64, (20, 40), (10, 20), BF, 1.0),           # ragged last token group
+    ("apply-d64-parts-empty", 1, 2, 64, (40, 52), (20, 26), BF, 1.0),    # 8 token parts, the last one empty
+]
+
+
+@pytest.mark.parametrize("case", APPLY_CASES, ids=lambda c: c[0])
+def test_apply_operand_kernels(case):
+    """query_apply with St_i, zt_i operands staged once per head in LDS (the
+    default at d <= 64 with several waves per head, and at d = 32) and with
+    each wave's own register copy (MHLA_VARIANT_APPLY_REGS): both against
+    the oracle, and equal bit for bit (same operands, same products)."""
+    p = small_problem(case)
+    q, k, v, W = synth.make_inputs(p, seed=27)
+    ref = oracle.forward(q, k, v, W, p.grid, p.block, eps=p.eps)
+    run = Run(p, q, k, v, W)
+    outs = []
+    for flag in (0, mh.MHLA_VARIANT_APPLY_REGS):
+        out = run.forward(mh.MHLA_PATH_3KERNEL | flag)
+        err = rel_err(to_host64(out), ref)
+        say(f"  {p.name} variant={flag:#x}: max|d|/max|ref| = {err:.3e}")
+        assert err <= TOL[p.dtype]
+        outs.append(out.clone())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
 def token_parts(B, H, M, T, limit_sources):
     """Token parts of the bf16 3-kernel forward (the rule documented with
     mhla_workspace_bytes): doubled while B*M*H*parts < 1536, parts of at least

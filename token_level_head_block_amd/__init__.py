@@ -37,6 +37,7 @@ MHLA_VARIANT_MIX_RESIDENT = 1 << 8
 MHLA_VARIANT_MIX_TILED = 1 << 9
 MHLA_VARIANT_NO_PAIR_HEADS = 1 << 10
 MHLA_VARIANT_MIX_SPLIT = 1 << 11
+MHLA_VARIANT_APPLY_REGS = 1 << 12
 
 MHLA_PHI_ELU1 = 0
 MHLA_PHI_RELU_EPS = 1

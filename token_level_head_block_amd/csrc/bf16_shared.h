@@ -298,11 +298,29 @@ __device__ __forceinline__ void mix_tile_bf16(uint32_t wg, const RecT* __restric
     }
 }
 
+// The apply's A operands: St_i^T row tiles and zt_i's high and low words.
+// ApplyA holds them in the wave's registers; ApplyL reads them from LDS
+// operand words laid out [RT][KS][lane], then zt's high [KS][lane] and low
+// [KS][lane] words (one 16-byte word per lane and operand: lane-linear,
+// conflict-free reads).
 template <int D>
 struct ApplyA {
     static constexpr int RT = D / 16, KS = D / 32;
+    static constexpr bool kShared = false;   // per wave: no workgroup barrier in its preparation
     u32x4 a[RT][KS];
     u32x4 zhi[KS], zlo[KS];
+    __device__ __forceinline__ u32x4 op(int r, int kk, int) const { return a[r][kk]; }
+    __device__ __forceinline__ u32x4 hi(int kk, int) const { return zhi[kk]; }
+    __device__ __forceinline__ u32x4 lo(int kk, int) const { return zlo[kk]; }
+};
+template <int D>
+struct ApplyL {
+    static constexpr int RT = D / 16, KS = D / 32, WORDS = (RT + 2) * KS * 64;
+    static constexpr bool kShared = true;    // staged by the workgroup: every wave reaches its barrier
+    const u32x4* w;
+    __device__ __forceinline__ u32x4 op(int r, int kk, int lane) const { return w[(r * KS + kk) * 64 + lane]; }
+    __device__ __forceinline__ u32x4 hi(int kk, int lane) const { return w[(RT * KS + kk) * 64 + lane]; }
+    __device__ __forceinline__ u32x4 lo(int kk, int lane) const { return w[((RT + 1) * KS + kk) * 64 + lane]; }
 };
 
 // zt (8 fp32 values of one k-slot group) -> hi/lo bf16 operand words.

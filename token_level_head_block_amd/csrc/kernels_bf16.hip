@@ -728,12 +728,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void m
 // (split into a bf16 high part and the bf16 rounding of the remainder), so
 // every lane receives its token's phi(q) . zt_i without cross-lane sums.
 // =====================================================================
-template <int D, int NWA, int PF, bool NTL, int MAXW, typename PrepLoad, typename PrepFinish>
-__device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFinish&& prep_finish,
+template <int D, int NWA, int PF, bool NTL, int MAXW, typename Ops, typename PrepLoad, typename PrepFinish>
+__device__ __forceinline__ void apply_tokens_bf16(Ops A, PrepLoad&& prep_load, PrepFinish&& prep_finish,
                                                   const uint16_t* __restrict__ Q,
                                                   uint16_t* __restrict__ O, const Geo& g, int bh,
-                                                  int i, int wave, int lane, int p0 = 0, int p1 = -1) {
-    // Tokens [p0, p1) of block i (p1 < 0: to the block's end).
+                                                  int i, int wave, int lane, int p0 = 0, int p1 = -1,
+                                                  bool active = true) {
+    // Tokens [p0, p1) of block i (p1 < 0: to the block's end).  A wave that is
+    // not active (a head past the last, an empty part) only takes part in the
+    // operands' preparation when that has a workgroup barrier (Ops::kShared).
     if (p1 < 0) p1 = g.T;
     constexpr int RT = D / 16, KS = D / 32;
     const int t = lane & 15, gq = lane >> 4;
@@ -769,7 +772,7 @@ __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFini
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) R.q[kk] = ld<NTL>(reinterpret_cast<const u32x4*>(qb + R.off + kk * 32));
     };
-    auto compute = [&](const ApplyA<D>& A, const Raw& R) {
+    auto compute = [&](const Ops& A, const Raw& R) {
         u32x4 bq[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
@@ -782,9 +785,9 @@ __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFini
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-            for (int r = 0; r < RT; ++r) acc[r] = mfma_bf16(A.a[r][kk], bq[kk], acc[r]);
-            accd = mfma_bf16(A.zhi[kk], bq[kk], accd);
-            accd = mfma_bf16(A.zlo[kk], bq[kk], accd);
+            for (int r = 0; r < RT; ++r) acc[r] = mfma_bf16(A.op(r, kk, lane), bq[kk], acc[r]);
+            accd = mfma_bf16(A.hi(kk, lane), bq[kk], accd);
+            accd = mfma_bf16(A.lo(kk, lane), bq[kk], accd);
         }
         const float inv = 1.f / (accd[0] + g.eps);
         uint32_t wv[2 * RT];
@@ -823,13 +826,16 @@ __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFini
     // Two batch buffers alternate: the next batch's loads are issued before the
     // current batch is computed and stored.  The first batch goes out before
     // the block's St / zt operands, the second right after them.
-    if (wave >= nit) return;
+    const bool work = active && wave < nit;
+    if (!Ops::kShared && !work) return;
     const int step = NWA * PF;
-    ApplyA<D> A;
     Raw ra[PF], rb[PF];
+    if (work) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) load(wave + u * NWA, ra[u]);
+        for (int u = 0; u < PF; ++u) load(wave + u * NWA, ra[u]);
+    }
     prep_load(A);
+    if (!work) return;
     int it0 = wave;
 #pragma unroll
     for (int u = 0; u < PF; ++u) load(it0 + step + u * NWA, rb[u]);
@@ -855,7 +861,13 @@ __device__ __forceinline__ void apply_tokens_bf16(PrepLoad&& prep_load, PrepFini
 
 // Workgroup = query block i of batch b for G consecutive heads x NWA waves
 // splitting the block's tokens, at most MAXW waves.
-template <int D, int NWA, int PF, bool NTL, int MAXW>
+// LDSA: the NWA waves of each head first stage the head's operands (St_i^T
+// row tiles and zt_i's high and low words) once in LDS and read them from
+// there for every token group; each wave then holds about 30 fewer
+// registers (d = 64: 97 -> 66, so 7 instead of 4 waves per SIMD) and St_i
+// leaves L2 once per head instead of once per wave.  Otherwise each wave
+// loads them into its own registers.
+template <int D, int NWA, int PF, bool NTL, int MAXW, bool LDSA>
 __global__ __launch_bounds__(64 * MAXW) void query_apply_bf16(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ St,
                                                         const float* __restrict__ Zt,
@@ -864,40 +876,75 @@ __global__ __launch_bounds__(64 * MAXW) void query_apply_bf16(const uint16_t* __
     const int wave = (threadIdx.x >> 6) % NWA, lane = threadIdx.x & 63;
     const int t = lane & 15, gq = lane >> 4;
     const WgCoordP wgc = wg_coord_parts(g, blockIdx.x, g.div_AP);
-    const int h = wgc.hg * g.G + (int)(threadIdx.x >> 6) / NWA;
-    if (h >= g.H) return;
+    const int hs = (int)(threadIdx.x >> 6) / NWA;   // the head's slot in the workgroup
+    const int h = wgc.hg * g.G + hs;
     const int i = wgc.j;
     // Part t of AP contiguous runs of the block's 16-token groups.
     const int ngr = (g.T + 15) >> 4, gper = (ngr + g.AP - 1) / g.AP;
     const int p0 = min(g.T, 16 * gper * wgc.t), p1 = min(g.T, p0 + 16 * gper);
-    if (p0 >= p1) return;
     const int bh = wgc.b * g.H + h;
     const int blk = bh * g.M + i;
     const uint16_t* sb = St + (size_t)blk * (D * D);
     const float* zb = Zt + (size_t)blk * D;
-    f32x4 zraw[KS][2];
-    auto prep_load = [&](ApplyA<D>& A) {
+    if constexpr (LDSA) {
+        constexpr int WORDS = ApplyL<D>::WORDS;
+        __shared__ u32x4 opw[(MAXW / NWA) * WORDS];
+        u32x4* w = opw + hs * WORDS;
+        const bool active = h < g.H && p0 < p1;
+        auto stage = [&](ApplyL<D>&) {
+            if (active) {
+                const int x0 = (int)threadIdx.x - hs * 64 * NWA;
+                for (int wi = x0; wi < WORDS; wi += 64 * NWA) {
+                    const int ln = wi & 63, tl = ln & 15, gl = ln >> 4;
+                    if (wi < RT * KS * 64) {
+                        const int r = wi / (KS * 64), kk = (wi >> 6) % KS;
+                        const int e = 4 * RT * (tl >> 2) + 4 * r + (tl & 3);
+                        w[wi] = *reinterpret_cast<const u32x4*>(sb + e * D + kk * 32 + gl * 8);
+                    } else {
+                        const int zi = wi - RT * KS * 64, part = zi / (KS * 64), kk = (zi >> 6) % KS;
+                        const f32x4 x = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gl * 8);
+                        const f32x4 y = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gl * 8 + 4);
+                        const float z[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+                        u32x4 hi, lo;
+                        split_zt(z, hi, lo);
+                        w[wi] = part == 0 ? hi : lo;
+                    }
+                }
+            }
+            __syncthreads();
+        };
+        auto none = [&](ApplyL<D>&) {};
+        // The first batch of Q loads is in flight while the operands are staged.
+        apply_tokens_bf16<D, NWA, PF, NTL, MAXW>(ApplyL<D>{w}, stage, none, Q, O, g, bh, i, wave, lane,
+                                                  active ? p0 : 0, active ? p1 : 1, active);
+    } else {
+        if (h >= g.H || p0 >= p1) return;
+        f32x4 zraw[KS][2];
+        auto prep_load = [&](ApplyA<D>& A) {
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
+            for (int r = 0; r < RT; ++r) {
+                const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) A.a[r][kk] = *reinterpret_cast<const u32x4*>(sb + e * D + kk * 32 + gq * 8);
-        }
+                for (int kk = 0; kk < KS; ++kk)
+                    A.a[r][kk] = *reinterpret_cast<const u32x4*>(sb + e * D + kk * 32 + gq * 8);
+            }
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            zraw[kk][0] = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8);
-            zraw[kk][1] = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8 + 4);
-        }
-    };
-    auto prep_finish = [&](ApplyA<D>& A) {
+            for (int kk = 0; kk < KS; ++kk) {
+                zraw[kk][0] = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8);
+                zraw[kk][1] = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8 + 4);
+            }
+        };
+        auto prep_finish = [&](ApplyA<D>& A) {
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const f32x4 x = zraw[kk][0], y = zraw[kk][1];
-            const float z[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-            split_zt(z, A.zhi[kk], A.zlo[kk]);
-        }
-    };
-    apply_tokens_bf16<D, NWA, PF, NTL, MAXW>(prep_load, prep_finish, Q, O, g, bh, i, wave, lane, p0, p1);
+            for (int kk = 0; kk < KS; ++kk) {
+                const f32x4 x = zraw[kk][0], y = zraw[kk][1];
+                const float z[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+                split_zt(z, A.zhi[kk], A.zlo[kk]);
+            }
+        };
+        apply_tokens_bf16<D, NWA, PF, NTL, MAXW>(ApplyA<D>{}, prep_load, prep_finish, Q, O, g, bh, i, wave, lane,
+                                                  p0, p1);
+    }
 }
 
 // =====================================================================
@@ -985,7 +1032,7 @@ __global__ __launch_bounds__(256) void query_apply_fused_bf16(const uint16_t* __
             split_zt(z, A.zhi[kk], A.zlo[kk]);
         }
     };
-    apply_tokens_bf16<D, 4, 2, false, 4>(prep_load, prep_finish, Q, O, g, bh, i, wave, lane);
+    apply_tokens_bf16<D, 4, 2, false, 4>(ApplyA<D>{}, prep_load, prep_finish, Q, O, g, bh, i, wave, lane);
 }
 
 // =====================================================================
@@ -1069,8 +1116,15 @@ template <int D, int NWA, int PF, int MAXW>
 void launch_apply_pf(const Launch& L, const uint16_t* q, const uint16_t* st, uint16_t* o) {
     const Geo g = with_head_groups(L.g, NWA, MAXW);
     const int grid = g.B * g.M * g.AP * g.HG, block = 64 * NWA * g.G;
-    if (L.tune.nt_apply) query_apply_bf16<D, NWA, PF, true, MAXW><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
-    else query_apply_bf16<D, NWA, PF, false, MAXW><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
+    if constexpr (D <= 64) {
+        if (L.tune.apply_lds) {
+            if (L.tune.nt_apply) query_apply_bf16<D, NWA, PF, true, MAXW, true><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
+            else query_apply_bf16<D, NWA, PF, false, MAXW, true><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
+            return;
+        }
+    }
+    if (L.tune.nt_apply) query_apply_bf16<D, NWA, PF, true, MAXW, false><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
+    else query_apply_bf16<D, NWA, PF, false, MAXW, false><<<grid, block, 0, L.stream>>>(q, st, L.zt, o, g);
 }
 
 template <int D, int NWA>

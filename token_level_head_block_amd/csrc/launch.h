@@ -17,6 +17,7 @@ struct Tuning {
     int pair_heads;      // bf16 path, head_dim 32 with an even head count: summaries of head pairs
     int bwdq_heads;      // bf16 backward: heads per bwd_query workgroup (0: the kernel's maximum)
     int apply_maxw;      // bf16 path: waves per query_apply workgroup (4 or 8; heads grouped up to it)
+    int apply_lds;       // bf16 path, d <= 64: query_apply reads St_i, zt_i operands from LDS (staged once per head)
     int nt_loads;        // bf16 path: non-temporal hint on the loads of k, v (summary kernel)
     int nt_apply;        // bf16 path: non-temporal hint on the loads of q (apply kernel)
     int nt_mix;          // bf16 persistent mixing kernel: 1 = non-temporal summary loads, 2 = non-temporal stores of St

@@ -221,6 +221,12 @@ mhla::Tuning choose_tuning(const Shape& s) {
     t.d128_shared = env_int("MHLA_D128_SHARED", 1);
     if (t.d128_shared < 0 || t.d128_shared > 2) t.d128_shared = 1;
     t.apply_maxw = 8;
+    // Apply operands staged once per head in LDS (d <= 64) when several waves
+    // share a head: dit-s2-256x256 apply 25.9 -> 23.9 us, sana-128x128 (d = 32)
+    // 75.1 -> 68.2 us; with one wave per head at d = 64 the 12 KB of operand
+    // words per wave leave room for too few waves (dit-s2-64x64 53 -> 78 us).
+    const int lds_default = s.D == 32 || (s.D == 64 && t.apply_waves >= 2);
+    t.apply_lds = env_int("MHLA_APPLY_LDS", lds_default) != 0;
     t.bwdq_heads = env_int("MHLA_BWDQ_HEADS", 0);
     if (t.bwdq_heads < 0 || t.bwdq_heads > 4) t.bwdq_heads = 0;
     const int am = env_int("MHLA_APPLY_MAXW", 0);
@@ -280,7 +286,7 @@ mhla::Geo make_geo(const Shape& s, float eps) {
 // The path argument of mhla_forward_ex: a MHLA_PATH_* value in the low 8 bits
 // and MHLA_VARIANT_* flags above them.
 constexpr int32_t kMixFlags = MHLA_VARIANT_MIX_RESIDENT | MHLA_VARIANT_MIX_TILED | MHLA_VARIANT_MIX_SPLIT;
-constexpr int32_t kVariantMask = kMixFlags | MHLA_VARIANT_NO_PAIR_HEADS;
+constexpr int32_t kVariantMask = kMixFlags | MHLA_VARIANT_NO_PAIR_HEADS | MHLA_VARIANT_APPLY_REGS;
 
 bool split_path(int32_t arg, int32_t* path, int32_t* variant) {
     *path = arg & 0xff;
@@ -296,6 +302,7 @@ void apply_variant(mhla::Tuning& t, int32_t variant) {
     if (variant & MHLA_VARIANT_MIX_TILED) t.mix_kind = 0;
     if (variant & MHLA_VARIANT_MIX_SPLIT) t.mix_kind = 2;
     if (variant & MHLA_VARIANT_NO_PAIR_HEADS) t.pair_heads = 0;
+    if (variant & MHLA_VARIANT_APPLY_REGS) t.apply_lds = 0;
 }
 
 mhla_status forward_impl(const void* q, const void* k, const void* v, const float* W,
