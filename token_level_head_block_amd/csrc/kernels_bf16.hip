@@ -1149,6 +1149,59 @@ void launch_apply(const Launch& L, const uint16_t* q, const uint16_t* st, uint16
     }
 }
 
+// The mixing product of records with W's operands: out[i] = sum_j w(i, j) rec[j]
+// over the M * TP * RD k-slots of g, for the forward's summaries (W) and the
+// backward's gradient records (W^T, TP = RD = 1); outputs St-style bf16
+// records and fp32 normalisers.  The kernel follows the problem: mix_split
+// with at most 256 source k-slots, the persistent kernel when so tuned (at
+// most 64 query blocks by default), the per-tile kernel otherwise.
+template <int D>
+void launch_mixing(const Launch& L, const uint16_t* src, const uint16_t* wops, uint16_t* dst, float* zdst,
+                   const Geo& g) {
+    const int IT = (g.M + 63) / 64, NK = (g.M * g.TP * g.RD + 31) / 32;
+    MixGeo mg;
+    mg.CT = (D * D + D + 63) / 64;
+    mg.IT = IT;
+    // Column tiles per workgroup: its 8 waves cover CPW tiles x IT query
+    // tiles x 2, and the A staging (one unit per thread) needs CPW * min(NK, 8) <= 8.
+    const int nkp = NK < 8 ? NK : 8;
+    mg.CPW = IT >= 4 ? 1 : 4 / IT;
+    if (mg.CPW * nkp > 8) mg.CPW = 8 / nkp;
+    mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
+    mg.Jpad = NK * 32;
+    mg.div_CTG = make_fastdiv(mg.CTG);
+    if (L.tune.mix_kind == 2 && NK <= 8) {
+        SplitGeo sg;
+        sg.CT = mg.CT;
+        sg.NC = g.BH * mg.CT;
+        sg.div_CT = make_fastdiv((uint32_t)mg.CT);
+        const int tr = (g.M <= 64 || L.tune.mix_rows == 1) ? 1 : 2;
+        const int ni = (g.M + 64 * tr - 1) / (64 * tr);
+        sg.div_NI = make_fastdiv((uint32_t)ni);
+        const int grid = 8 * ni * ((sg.NC + 7) / 8);
+        const bool nt = (L.tune.nt_mix & 2) != 0;
+        if (tr == 1) {
+            if (nt) mix_split_bf16<D, 1, 2><<<grid, 256, 0, L.stream>>>(src, wops, dst, zdst, g, sg);
+            else mix_split_bf16<D, 1, 0><<<grid, 256, 0, L.stream>>>(src, wops, dst, zdst, g, sg);
+        } else {
+            if (nt) mix_split_bf16<D, 2, 2><<<grid, 256, 0, L.stream>>>(src, wops, dst, zdst, g, sg);
+            else mix_split_bf16<D, 2, 0><<<grid, 256, 0, L.stream>>>(src, wops, dst, zdst, g, sg);
+        }
+    } else if (L.tune.mix_kind == 1 && IT <= 4 && NK <= 8) {
+        // NK <= 8: at most 256 source records (M <= 256, M * TP <= 256).
+        const int units = g.BH * mg.CTG;
+        const int grid = units < L.tune.num_cus ? units : L.tune.num_cus;
+        switch (L.tune.nt_mix) {
+            case 1: mix_resident_bf16<D, 1><<<grid, 512, 0, L.stream>>>(src, wops, dst, zdst, g, mg); break;
+            case 2: mix_resident_bf16<D, 2><<<grid, 512, 0, L.stream>>>(src, wops, dst, zdst, g, mg); break;
+            case 3: mix_resident_bf16<D, 3><<<grid, 512, 0, L.stream>>>(src, wops, dst, zdst, g, mg); break;
+            default: mix_resident_bf16<D, 0><<<grid, 512, 0, L.stream>>>(src, wops, dst, zdst, g, mg); break;
+        }
+    } else {
+        mix_summaries_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(src, wops, dst, zdst, g, mg);
+    }
+}
+
 template <int D>
 hipError_t run_d(const Launch& L0) {
     // Token parts apply to the 3-kernel forward and the backward's recompute
@@ -1204,49 +1257,7 @@ hipError_t run_d(const Launch& L0) {
         record(L, 2);
         query_apply_fused_bf16<D><<<nblk, 256, 0, L.stream>>>(q, sz, L.W, o, g);
     } else {
-        MixGeo mg;
-        mg.CT = (D * D + D + 63) / 64;
-        mg.IT = IT;
-        // Column tiles per workgroup: its 8 waves cover CPW tiles x IT query
-        // tiles x 2, and the A staging (one unit per thread) needs CPW * min(NK, 8) <= 8.
-        const int nkp = NK < 8 ? NK : 8;
-        mg.CPW = IT >= 4 ? 1 : 4 / IT;
-        if (mg.CPW * nkp > 8) mg.CPW = 8 / nkp;
-        mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
-        mg.Jpad = NK * 32;
-        mg.div_CTG = make_fastdiv(mg.CTG);
-        if (L.tune.mix_kind == 2 && NK <= 8) {
-            SplitGeo sg;
-            sg.CT = mg.CT;
-            sg.NC = g.BH * mg.CT;
-            sg.div_CT = make_fastdiv((uint32_t)mg.CT);
-            const int tr = (g.M <= 64 || L.tune.mix_rows == 1) ? 1 : 2;
-            const int ni = (g.M + 64 * tr - 1) / (64 * tr);
-            sg.div_NI = make_fastdiv((uint32_t)ni);
-            const int grid = 8 * ni * ((sg.NC + 7) / 8);
-            const auto* wbp = static_cast<const uint16_t*>(L.wb);
-            const bool nt = (L.tune.nt_mix & 2) != 0;
-            if (tr == 1) {
-                if (nt) mix_split_bf16<D, 1, 2><<<grid, 256, 0, L.stream>>>(sz, wbp, st, L.zt, g, sg);
-                else mix_split_bf16<D, 1, 0><<<grid, 256, 0, L.stream>>>(sz, wbp, st, L.zt, g, sg);
-            } else {
-                if (nt) mix_split_bf16<D, 2, 2><<<grid, 256, 0, L.stream>>>(sz, wbp, st, L.zt, g, sg);
-                else mix_split_bf16<D, 2, 0><<<grid, 256, 0, L.stream>>>(sz, wbp, st, L.zt, g, sg);
-            }
-        } else if (L.tune.mix_kind == 1 && IT <= 4 && NK <= 8) {
-            // NK <= 8: at most 256 source records (M <= 256, M * TP <= 256).
-            const int units = g.BH * mg.CTG;
-            const int grid = units < L.tune.num_cus ? units : L.tune.num_cus;
-            switch (L.tune.nt_mix) {
-                case 1: mix_resident_bf16<D, 1><<<grid, 512, 0, L.stream>>>(sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg); break;
-                case 2: mix_resident_bf16<D, 2><<<grid, 512, 0, L.stream>>>(sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg); break;
-                case 3: mix_resident_bf16<D, 3><<<grid, 512, 0, L.stream>>>(sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg); break;
-                default: mix_resident_bf16<D, 0><<<grid, 512, 0, L.stream>>>(sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg); break;
-            }
-        } else {
-            mix_summaries_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(
-                sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g, mg);
-        }
+        launch_mixing<D>(L, sz, static_cast<const uint16_t*>(L.wb), st, L.zt, g);
         record(L, 2);
         if (L.summaries_only) return hipGetLastError();
         if (causal) {
@@ -1272,6 +1283,17 @@ hipError_t run_bf16_summaries(const Launch& L) {
     S.path = MHLA_PATH_3KERNEL;
     S.events = nullptr;
     return run_bf16(S);
+}
+
+hipError_t launch_mix_records_bf16(const Launch& L, const uint16_t* src, const uint16_t* wops, uint16_t* dst,
+                                  float* zdst, const Geo& g) {
+    switch (g.D) {
+        case 32: launch_mixing<32>(L, src, wops, dst, zdst, g); break;
+        case 64: launch_mixing<64>(L, src, wops, dst, zdst, g); break;
+        case 128: launch_mixing<128>(L, src, wops, dst, zdst, g); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t run_bf16(const Launch& L) {

@@ -708,15 +708,6 @@ __global__ __launch_bounds__(256) void dw_reduce(const float* __restrict__ part,
     dW[x] = s;
 }
 
-// The mixing product with W^T over the gradient records.
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void mix_transposed_bf16(
-    const uint16_t* __restrict__ dSt, const uint16_t* __restrict__ WbT, uint16_t* __restrict__ dS,
-    float* __restrict__ dZ, const Geo g, const MixGeo mg) {
-    __shared__ u32x4 sA[MIX_LDS_UNITS];
-    mix_tile_bf16<D>(blockIdx.x, dSt, WbT, dS, dZ, g, mg, sA);
-}
-
 inline void rec(const BwdLaunch& B, int k) {
     if (B.events) (void)hipEventRecord(B.events[k], B.F.stream);
 }
@@ -743,7 +734,6 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
         srec = B.sfold;
     }
     rec(B, 1);
-    const int IT = (g.M + 63) / 64, NK = (g.M + 31) / 32;
     // Head groups: at most `maxw` heads (one wave each) per workgroup, balanced.
     auto heads = [&](int maxw) {
         Geo x = g;
@@ -781,14 +771,9 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     gh.div_AP = make_fastdiv((uint32_t)gh.AP);
     const int grid_tok = gh.B * gh.M * gh.AP * gh.HG, block_tok = 64 * gh.G;
     rec(B, 2);
-    MixGeo mg;
-    mg.CT = (D * D + D + 63) / 64;
-    mg.IT = IT;
-    mg.CPW = IT >= 4 ? 1 : 4 / IT;
-    mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
-    mg.Jpad = NK * 32;
-    mg.div_CTG = make_fastdiv(mg.CTG);
-    mix_transposed_bf16<D><<<g.BH * mg.CTG, 512, 0, L.stream>>>(B.dst, B.wbt, B.ds, B.dz, g, mg);
+    // the gradient records mixed with W^T on the forward's mixing kernels
+    err = launch_mix_records_bf16(L, B.dst, B.wbt, B.ds, B.dz, g);
+    if (err != hipSuccess) return err;
     const int ntj = (g.M + 127) / 128;
     if (g.M <= 64)
         dw_partial_small_bf16<D><<<B.nsplit, 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH, B.nsplit);
@@ -832,21 +817,7 @@ __global__ __launch_bounds__(256) void fill_zero(float* __restrict__ p, int n) {
 }  // namespace
 
 hipError_t launch_mix_transposed_bf16(const BwdLaunch& B, const Geo& g) {
-    const int IT = (g.M + 63) / 64, NK = (g.M + 31) / 32;
-    MixGeo mg;
-    mg.CT = (g.D * g.D + g.D + 63) / 64;
-    mg.IT = IT;
-    mg.CPW = IT >= 4 ? 1 : 4 / IT;
-    mg.CTG = (mg.CT + mg.CPW - 1) / mg.CPW;
-    mg.Jpad = NK * 32;
-    mg.div_CTG = make_fastdiv(mg.CTG);
-    const hipStream_t st = B.F.stream;
-    switch (g.D) {
-        case 32: mix_transposed_bf16<32><<<g.BH * mg.CTG, 512, 0, st>>>(B.dst, B.wbt, B.ds, B.dz, g, mg); break;
-        case 64: mix_transposed_bf16<64><<<g.BH * mg.CTG, 512, 0, st>>>(B.dst, B.wbt, B.ds, B.dz, g, mg); break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return launch_mix_records_bf16(B.F, B.dst, B.wbt, B.ds, B.dz, g);
 }
 
 hipError_t launch_dw_partial_bf16(const BwdLaunch& B, const Geo& g, const uint16_t* srec) {
