@@ -242,8 +242,11 @@ mhla::Tuning choose_tuning(const Shape& s) {
     // mhla_forward_ex select one per call).
     // With at most 64 query blocks the per-tile workgroups are small (8 KB
     // of W and 8 KB of records each) and the persistent kernel, which loads W
-    // once per compute unit, is faster (dit-s2-64x64 mixing 38.2 -> 33.7 us).
-    const int mix_default = s.M <= 64 ? 1 : 2;
+    // once per compute unit, is faster (dit-s2-64x64 mixing 38.2 -> 33.7 us);
+    // at head_dim 128 (258 column tiles per pair, each workgroup of the split
+    // kernel reading 64 KB of W for 32 KB of records) too: video-16x64x64
+    // step 254.4-255.5 -> 251.5-252.5 us over three alternating runs.
+    const int mix_default = (s.M <= 64 || s.D == 128) ? 1 : 2;
     t.mix_kind = env_int("MHLA_MIX", mix_default);
     if (t.mix_kind < 0 || t.mix_kind > 2) t.mix_kind = mix_default;
     t.mix_rows = env_int("MHLA_MIX_ROWS", 0);
