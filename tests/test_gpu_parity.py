@@ -95,6 +95,9 @@ MIX_CASES = [
     ("mix-d64-M16-units544", 4, 8, 64, (16, 16), (4, 4), BF, 1.0),     # 544 work units: several per workgroup
     ("mix-d32-M180", 1, 3, 32, (30, 24), (2, 2), BF, 1.0),              # 3 query-block tiles, ragged
     ("mix-d128-M96", 1, 2, 128, (24, 32), (2, 4), BF, 1.0),
+    # more than three units per persistent workgroup
+    ("mix-d64-M16-units1088", 8, 8, 64, (16, 16), (4, 4), BF, 1.0),
+    ("mix-d128-M256-units774", 1, 3, 128, (32, 32), (2, 2), BF, 1.0),
 ]
 
 
