@@ -39,6 +39,9 @@ SMALL = [
     ("bwd-d64-M4-parts", 1, 2, 64, (32, 32), (16, 16), 1.0),
     ("bwd-d32-M4-parts", 1, 4, 32, (32, 48), (16, 24), 1.0),
     ("bwd-d64-B2-parts", 2, 3, 64, (64, 64), (32, 32), 1.0),
+    # enough (b, block, head) tasks for whole blocks per wave on the query side
+    # (operand copies in LDS), 9 token groups with the last of 8 tokens
+    ("bwd-d64-T136-one-part", 4, 6, 64, (64, 136), (8, 17), 1.0),
 ]
 
 # the general path: name, B, H, d, grid, block, dtype

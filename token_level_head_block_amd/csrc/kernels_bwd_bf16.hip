@@ -41,6 +41,20 @@ __device__ __forceinline__ void rows_e_k_c(const uint16_t* __restrict__ m, int t
     }
 }
 
+// The same rows with the k-slots of lane group gq at c = 4 * RT * gq + 8 * kk + s:
+// the 4 * RT channels that lane group also holds as output rows of a product
+// whose A operand comes from rows_c_k_e.
+template <int D>
+__device__ __forceinline__ void rows_e_k_cl(const uint16_t* __restrict__ m, int t, int gq, u32x4 (&a)[D / 16][D / 32]) {
+    constexpr int RT = D / 16, KS = D / 32;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) a[r][kk] = *reinterpret_cast<const u32x4*>(m + e * D + 4 * RT * gq + 8 * kk);
+    }
+}
+
 // The transposed operand of the same matrix: row c, k-slot s of k-step kk at
 // e = ebase(gq) + 8 * kk + s, gathered element by element (once per block).
 template <int D>
@@ -117,7 +131,7 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
     const uint16_t* sb = St + (size_t)blk * (D * D);
     const float* zb = Zt + (size_t)blk * D;
     u32x4 a1[RT][KS], a2r[LOP ? 1 : RT][LOP ? 1 : KS], zhi[LOP ? 1 : KS], zlo[LOP ? 1 : KS];
-    rows_e_k_c<D>(sb, t, gq, a1);
+    rows_e_k_cl<D>(sb, t, gq, a1);
     u32x4* zl2 = a2l + A2U / 8;   // [hi/lo][kk][lane] operand words of zt
     float* zl = reinterpret_cast<float*>(zl2 + ZU / 8);   // zt
     float zc[LOP ? 1 : 4 * RT];   // zt at this lane's output channels 4*RT*gq + ..
@@ -133,8 +147,8 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
     }
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8);
-        const f32x4 y = *reinterpret_cast<const f32x4*>(zb + kk * 32 + gq * 8 + 4);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(zb + 4 * RT * gq + 8 * kk);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(zb + 4 * RT * gq + 8 * kk + 4);
         const float z[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
         if constexpr (LOP) {
             u32x4 hi, lo;
@@ -172,7 +186,7 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
     }
 
     struct Raw {
-        u32x4 qv[KS], go[RT / 2], qo[LOP ? 1 : RT / 2];
+        u32x4 qv[KS], go[RT / 2];
         int off;
         bool ok;
     };
@@ -181,27 +195,25 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
         R.ok = p < g.T;
         R.off = (origin + in_block(g, R.ok ? p : g.T - 1)) * row;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) R.qv[kk] = *reinterpret_cast<const u32x4*>(qb + R.off + kk * 32 + gq * 8);
+        for (int kk = 0; kk < KS; ++kk) R.qv[kk] = *reinterpret_cast<const u32x4*>(qb + R.off + 4 * RT * gq + 8 * kk);
 #pragma unroll
-        for (int u = 0; u < RT / 2; ++u) {
-            R.go[u] = *reinterpret_cast<const u32x4*>(gb + R.off + 4 * RT * gq + 8 * u);
-            if constexpr (!LOP) R.qo[u] = *reinterpret_cast<const u32x4*>(qb + R.off + 4 * RT * gq + 8 * u);
-        }
+        for (int u = 0; u < RT / 2; ++u) R.go[u] = *reinterpret_cast<const u32x4*>(gb + R.off + 4 * RT * gq + 8 * u);
     };
     auto compute = [&](const Raw& R) {
-        // q at this lane's output channels (for phi'); with LOP loaded here, from
-        // the lines qv already brought in
-        u32x4 qo[RT / 2];
-#pragma unroll
-        for (int u = 0; u < RT / 2; ++u)
-            qo[u] = LOP ? *reinterpret_cast<const u32x4*>(qb + R.off + 4 * RT * gq + 8 * u) : R.qo[LOP ? 0 : u];
-        // u = phi(q) as the B operand (k = channel kk*32 + gq*8 + s, column = token t)
+        // u = phi(q) as the B operand (k = channel 4*RT*gq + 8*kk + s, column =
+        // token t): the channels of this lane's dq, so phi'(q) there shares the exponential
         u32x4 bq[KS];
+        float pg[4 * RT];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                bq[kk][w] = pack_bf16(phi_fast(bf_lo(R.qv[kk][w])), phi_fast(bf_hi(R.qv[kk][w])));
+            for (int w = 0; w < 4; ++w) {
+                const float x0 = bf_lo(R.qv[kk][w]), x1 = bf_hi(R.qv[kk][w]);
+                const float e0 = __expf(x0), e1 = __expf(x1);
+                bq[kk][w] = pack_bf16(x0 > 0.f ? x0 + 1.f : e0, x1 > 0.f ? x1 + 1.f : e1);
+                pg[8 * kk + 2 * w] = x0 > 0.f ? 1.f : e0;
+                pg[8 * kk + 2 * w + 1] = x1 > 0.f ? 1.f : e1;
+            }
         f32x4 acc[RT], accd = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -251,9 +263,6 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
                 du[rt] = mfma_bf16(a2, b2h[kk], du[rt]);
                 du[rt] = mfma_bf16(a2, b2l[kk], du[rt]);
             }
-        float ql[4 * RT];
-#pragma unroll
-        for (int u = 0; u < RT / 2; ++u) unpack8(qo[u], ql + 8 * u);
         uint32_t wv[2 * RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -261,7 +270,7 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int cl = 4 * rt + v;
-                x[v] = (du[rt][v] + (LOP ? zl[4 * RT * gq + cl] : zc[LOP ? 0 : cl]) * dden) * phi_grad(ql[cl]);
+                x[v] = (du[rt][v] + (LOP ? zl[4 * RT * gq + cl] : zc[LOP ? 0 : cl]) * dden) * pg[cl];
             }
             wv[2 * rt] = pack_bf16(x[0], x[1]);
             wv[2 * rt + 1] = pack_bf16(x[2], x[3]);
@@ -276,7 +285,7 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const int c = kk * 32 + gq * 8 + 2 * w;
+                const int c = 4 * RT * gq + 8 * kk + 2 * w;
                 uT[c * TS + t] = (uint16_t)(bq[kk][w] & 0xffffu);
                 uT[(c + 1) * TS + t] = (uint16_t)(bq[kk][w] >> 16);
             }
