@@ -224,13 +224,13 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
             accd = mfma_bf16(LOP ? zl2[kk * 64 + lane] : zhi[LOP ? 0 : kk], bq[kk], accd);
             accd = mfma_bf16(LOP ? zl2[(KS + kk) * 64 + lane] : zlo[LOP ? 0 : kk], bq[kk], accd);
         }
-        const float inv = 1.f / (accd[0] + g.eps);
-        // Upstream gradient at this lane's channels e = 4*RT*gq + 4r + v (zero past the block).
+        // 1 / den; zero for a token past the block (its row is a clamped copy of
+        // a valid one), which zeroes its dnum, dden and so its dSt, dzt terms
+        const float inv = R.ok ? 1.f / (accd[0] + g.eps) : 0.f;
+        // Upstream gradient at this lane's channels e = 4*RT*gq + 4r + v.
         float gl[4 * RT];
 #pragma unroll
         for (int u = 0; u < RT / 2; ++u) unpack8(R.go[u], gl + 8 * u);
-#pragma unroll
-        for (int e = 0; e < 4 * RT; ++e) gl[e] = R.ok ? gl[e] : 0.f;
         float dot = 0.f;   // g . num over this lane's channels
 #pragma unroll
         for (int r = 0; r < RT; ++r)
@@ -251,6 +251,15 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
                 const uint32_t hw = pack_bf16(x0, x1);
                 b2h[kk][w] = hw;
                 b2l[kk][w] = pack_bf16(x0 - bf_lo(hw), x1 - bf_hi(hw));
+            }
+        // dnum in bf16 (the high parts of du's B operand), transposed for the dSt product
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int e = 4 * RT * gq + 8 * kk + 2 * w;
+                dnT[e * TS + t] = (uint16_t)(b2h[kk][w] & 0xffffu);
+                dnT[(e + 1) * TS + t] = (uint16_t)(b2h[kk][w] >> 16);
             }
         f32x4 du[RT];
 #pragma unroll
@@ -278,9 +287,6 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
         store_rows<D>(sout, wv, lane, R.off, R.ok, rsrc, olane);
 
         // ---- dSt += u dnum^T and dzt += u dden over these 16 tokens.
-#pragma unroll
-        for (int e = 0; e < 4 * RT; ++e)
-            dnT[(4 * RT * gq + e) * TS + t] = (uint16_t)(pack_bf16(gl[e] * inv, 0.f) & 0xffffu);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
