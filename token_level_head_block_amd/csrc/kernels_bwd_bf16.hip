@@ -78,9 +78,9 @@ __device__ __forceinline__ void rows_c_k_e(const uint16_t* __restrict__ m, int t
 // bwd_query: dq and the gradients of the mixed summaries, per query block.
 // Workgroup = (b, block i, group of <= 8 heads), one wave per head over all of
 // the block's tokens, 16 tokens per step (token t = lane % 16):
-//   num = St^T u and den (as in the forward apply), then dnum, dden;
-//   du  = St dnum (MFMA; k-slots of lane group gq are its own 4*RT channels)
-//         + zt dden, dq = du * phi'(q);
+//   num = St^T u and den (as in the forward apply), then dnum = g / den, dden;
+//   du  = (St g) / den (MFMA on the bf16 upstream gradient itself; k-slots of
+//         lane group gq are its own 4*RT channels) + zt dden, dq = du * phi'(q);
 //   dSt += u dnum^T, dzt += u dden on v_mfma_f32_16x16x16_bf16 with the 16
 //   tokens as k, both operands read transposed from the wave's LDS slice.
 // =====================================================================
@@ -201,7 +201,8 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
     };
     auto compute = [&](const Raw& R) {
         // u = phi(q) as the B operand (k = channel 4*RT*gq + 8*kk + s, column =
-        // token t): the channels of this lane's dq, so phi'(q) there shares the exponential
+        // token t): the channels of this lane's dq.  With e = exp(min(x, 0)),
+        // phi(x) = max(x, 0) + e and phi'(x) = e.
         u32x4 bq[KS];
         float pg[4 * RT];
 #pragma unroll
@@ -209,14 +210,17 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const float x0 = bf_lo(R.qv[kk][w]), x1 = bf_hi(R.qv[kk][w]);
-                const float e0 = __expf(x0), e1 = __expf(x1);
-                bq[kk][w] = pack_bf16(x0 > 0.f ? x0 + 1.f : e0, x1 > 0.f ? x1 + 1.f : e1);
-                pg[8 * kk + 2 * w] = x0 > 0.f ? 1.f : e0;
-                pg[8 * kk + 2 * w + 1] = x1 > 0.f ? 1.f : e1;
+                const float e0 = __expf(fminf(x0, 0.f)), e1 = __expf(fminf(x1, 0.f));
+                bq[kk][w] = pack_bf16(fmaxf(x0, 0.f) + e0, fmaxf(x1, 0.f) + e1);
+                pg[8 * kk + 2 * w] = e0;
+                pg[8 * kk + 2 * w + 1] = e1;
             }
-        f32x4 acc[RT], accd = f32x4{0.f, 0.f, 0.f, 0.f};
+        // num = St^T u, den, and du' = St g: dnum = g / den, so du = du' / den with
+        // the bf16 upstream gradient itself as the B operand (k-step kk of lane
+        // group gq: e = 4*RT*gq + 8*kk + s, the words the lane loaded).
+        f32x4 acc[RT], accd = f32x4{0.f, 0.f, 0.f, 0.f}, du[RT];
 #pragma unroll
-        for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < RT; ++r) acc[r] = du[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
@@ -224,6 +228,12 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
             accd = mfma_bf16(LOP ? zl2[kk * 64 + lane] : zhi[LOP ? 0 : kk], bq[kk], accd);
             accd = mfma_bf16(LOP ? zl2[(KS + kk) * 64 + lane] : zlo[LOP ? 0 : kk], bq[kk], accd);
         }
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                du[rt] = mfma_bf16(LOP ? a2l[(rt * KS + kk) * 64 + lane] : a2r[LOP ? 0 : rt][LOP ? 0 : kk], R.go[kk],
+                                   du[rt]);
         // 1 / den; zero for a token past the block (its row is a clamped copy of
         // a valid one), which zeroes its dnum, dden and so its dSt, dzt terms
         const float inv = R.ok ? 1.f / (accd[0] + g.eps) : 0.f;
@@ -239,38 +249,15 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
         dot += shfl_xor(dot, 16);
         dot += shfl_xor(dot, 32);
         const float dden = -dot * inv * inv;
-        // dnum as the B operand of du: k-step kk, slot s <-> e = 4*RT*gq + 8*kk + s,
-        // as a bf16 high part and the bf16 rounding of the remainder (du cancels
-        // along u, so dnum's own rounding would show in dq).
-        u32x4 b2h[KS], b2l[KS];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float x0 = gl[8 * kk + 2 * w] * inv, x1 = gl[8 * kk + 2 * w + 1] * inv;
-                const uint32_t hw = pack_bf16(x0, x1);
-                b2h[kk][w] = hw;
-                b2l[kk][w] = pack_bf16(x0 - bf_lo(hw), x1 - bf_hi(hw));
-            }
-        // dnum in bf16 (the high parts of du's B operand), transposed for the dSt product
+        // dnum in bf16, transposed for the dSt product
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const int e = 4 * RT * gq + 8 * kk + 2 * w;
-                dnT[e * TS + t] = (uint16_t)(b2h[kk][w] & 0xffffu);
-                dnT[(e + 1) * TS + t] = (uint16_t)(b2h[kk][w] >> 16);
-            }
-        f32x4 du[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) du[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const u32x4 a2 = LOP ? a2l[(rt * KS + kk) * 64 + lane] : a2r[LOP ? 0 : rt][LOP ? 0 : kk];
-                du[rt] = mfma_bf16(a2, b2h[kk], du[rt]);
-                du[rt] = mfma_bf16(a2, b2l[kk], du[rt]);
+                const uint32_t hw = pack_bf16(gl[8 * kk + 2 * w] * inv, gl[8 * kk + 2 * w + 1] * inv);
+                dnT[e * TS + t] = (uint16_t)(hw & 0xffffu);
+                dnT[(e + 1) * TS + t] = (uint16_t)(hw >> 16);
             }
         uint32_t wv[2 * RT];
 #pragma unroll
@@ -279,7 +266,7 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int cl = 4 * rt + v;
-                x[v] = (du[rt][v] + (LOP ? zl[4 * RT * gq + cl] : zc[LOP ? 0 : cl]) * dden) * pg[cl];
+                x[v] = (du[rt][v] * inv + (LOP ? zl[4 * RT * gq + cl] : zc[LOP ? 0 : cl]) * dden) * pg[cl];
             }
             wv[2 * rt] = pack_bf16(x[0], x[1]);
             wv[2 * rt + 1] = pack_bf16(x[2], x[3]);
