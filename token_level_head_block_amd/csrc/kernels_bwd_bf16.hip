@@ -622,64 +622,111 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
 // =====================================================================
 // dW = sum over (b, h) and record elements of dSt_i[x] S_j[x]: a GEMM whose
 // k runs over B*H*(d*d + d).  Workgroup = (split s of the k-steps, 128 x 128
-// tile of dW); split s is a contiguous run of k-steps, so consecutive steps
-// read consecutive 64-byte pieces of each record row (whole cache lines over
-// two steps), and blockIdx.x = s puts every tile of one split on the same XCD
-// (workgroups are dealt to the XCDs by linear index), where they share the
-// records in L2.  Wave (wi, wj) computes 32 i x 64 j; both operands come from
-// the bf16 records (rows i of dSt, rows j of S, 8 consecutive elements per
-// lane).  Partial sums go to part[s]; dw_reduce adds them in split order.
+// tile of dW); split s is a contiguous run of k-steps, and blockIdx.x = s puts
+// every tile of one split on the same XCD (workgroups are dealt to the XCDs by
+// linear index), where they share the records in L2.  The operands go through
+// LDS two k-steps (64 record elements) at a time: eight consecutive threads
+// load the 128 bytes of one record row, so the loads are whole lines that the
+// L1 serves four lanes per access (loaded straight into the MFMA layout,
+// consecutive lanes would read rows a record apart, one access per lane).  The
+// loads of the next two stages are in flight while one is multiplied.  Wave
+// (wi, wj) computes 32 i x 64 j.  Rows past M load a valid row; their outputs
+// are computed and not stored (each output element depends only on its own
+// rows).  Partial sums go to part[s]; dw_reduce adds them in split order.
 // =====================================================================
 template <int D>
 __global__ __launch_bounds__(512) void dw_partial_bf16(const uint16_t* __restrict__ dSt,
                                                        const uint16_t* __restrict__ SZ, float* __restrict__ part,
                                                        int M, int P, int nsplit, int ntj) {
     constexpr int REC = D * D + D, KPR = REC / 32;
+    constexpr int KST = 2;                // k-steps per stage
+    constexpr int SROW = 32 * KST + 8;    // LDS row: 64 elements + 8 padding (144 bytes)
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][128 * SROW];   // [buffer][dSt, S][row]: 72 KB
     const int s = blockIdx.x, tile = blockIdx.y;
     const int ti = tile / ntj, tj = tile - ti * ntj;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, gq = lane >> 4;
     const int i0 = ti * 128 + (wave >> 1) * 32, j0 = tj * 128 + (wave & 1) * 64;
-    int ri[2], rj[4];
-    uint32_t mi[2], mj[4];
+    // staging role: rows srow and srow + 64 of both tiles, 16-byte piece pc of the stage's 128 bytes
+    const int srow = tid >> 3, pc = tid & 7;
+    int ra[2], rb[2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        const int i = i0 + 16 * a + li;
-        ri[a] = i < M ? i : M - 1;
-        mi[a] = i < M ? 0xffffffffu : 0u;
+    for (int p = 0; p < 2; ++p) {
+        ra[p] = min(ti * 128 + srow + 64 * p, M - 1) * REC;
+        rb[p] = min(tj * 128 + srow + 64 * p, M - 1) * REC;
     }
+    const int nks = P * KPR, per = (nks + nsplit - 1) / nsplit;
+    const int k0 = min(nks, s * per), k1 = min(nks, k0 + per);
+    const int nst = (k1 - k0 + KST - 1) / KST;
+
+    struct Regs {
+        u32x4 a[2], b[2];
+    };
+    // Stage st: k-steps k0 + KST st + (pc >> 2); a k-step past k1 stages zeros.
+    auto load = [&](int st, Regs& r) {
+        const int ks = k0 + KST * st + (pc >> 2);
+        const bool ok = ks < k1;
+        const int kc = ok ? ks : k0;
+        const int bh = kc / KPR, col = (kc - bh * KPR) * 32 + (pc & 3) * 8;
+        const size_t base = (size_t)bh * M * REC + col;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int jj = j0 + 16 * c + li;
-        rj[c] = jj < M ? jj : M - 1;
-        mj[c] = jj < M ? 0xffffffffu : 0u;
-    }
+        for (int p = 0; p < 2; ++p) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(dSt + base + ra[p]);
+            const u32x4 y = *reinterpret_cast<const u32x4*>(SZ + base + rb[p]);
+            r.a[p] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+            r.b[p] = ok ? y : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store = [&](int buf, const Regs& r) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            *reinterpret_cast<u32x4*>(&lds[buf][0][(srow + 64 * p) * SROW + pc * 8]) = r.a[p];
+            *reinterpret_cast<u32x4*>(&lds[buf][1][(srow + 64 * p) * SROW + pc * 8]) = r.b[p];
+        }
+    };
     f32x4 acc[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    struct Ops {
-        u32x4 A[2], B[4];
+    auto compute = [&](int buf) {
+        const uint16_t* la = &lds[buf][0][((wave >> 1) * 32 + li) * SROW + gq * 8];
+        const uint16_t* lb = &lds[buf][1][((wave & 1) * 64 + li) * SROW + gq * 8];
+#pragma unroll
+        for (int kk = 0; kk < KST; ++kk) {
+            u32x4 A[2], B[4];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) A[a] = *reinterpret_cast<const u32x4*>(la + 16 * a * SROW + 32 * kk);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) B[c] = *reinterpret_cast<const u32x4*>(lb + 16 * c * SROW + 32 * kk);
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(A[a], B[c], acc[a][c]);
+        }
     };
-    auto load = [&](int ks, Ops& o) {
-        const int bh = ks / KPR, col = (ks - bh * KPR) * 32 + gq * 8;
-        const size_t rb = (size_t)bh * M;
-#pragma unroll
-        for (int a = 0; a < 2; ++a) o.A[a] = *reinterpret_cast<const u32x4*>(dSt + (rb + ri[a]) * REC + col);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o.B[c] = *reinterpret_cast<const u32x4*>(SZ + (rb + rj[c]) * REC + col);
-    };
-    auto compute = [&](const Ops& o) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(o.A[a] & mi[a], o.B[c] & mj[c], acc[a][c]);
-    };
-    // Steps [k0, k1) of this split; two later ones in flight while one is multiplied.
-    const int nks = P * KPR, per = (nks + nsplit - 1) / nsplit;
-    const int k0 = s * per, k1 = min(nks, k0 + per);
-    if (k0 < k1) pipelined<2, Ops>(k0, 1, k1, load, compute);
+    if (nst > 0) {
+        Regs r0, r1;
+        load(0, r0);
+        if (nst > 1) load(1, r1);
+        store(0, r0);
+        __syncthreads();
+        // Stage st is in buffer st & 1; the register set of stage st + 1 is
+        // stored after stage st is multiplied, and stage st + 2 loads into the
+        // set just freed.
+        for (int st = 0; st < nst; st += 2) {
+            if (st + 2 < nst) load(st + 2, r0);
+            compute(0);
+            if (st + 1 >= nst) break;
+            store(1, r1);
+            __syncthreads();
+            if (st + 3 < nst) load(st + 3, r1);
+            compute(1);
+            if (st + 2 >= nst) break;
+            store(0, r0);
+            __syncthreads();
+        }
+    }
     float* out = part + (size_t)s * M * M;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
