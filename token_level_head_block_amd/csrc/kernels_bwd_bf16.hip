@@ -341,59 +341,100 @@ __global__ __launch_bounds__(D == 64 ? 256 : 512) __attribute__((amdgpu_waves_pe
 }
 
 // dW for M <= 64: one 64 x 64 tile; the workgroup's eight waves are four
-// k-groups x two row halves (wave w: rows 32 (w & 1) .., all 64 columns,
-// k-steps k0 + (w >> 1), k0 + (w >> 1) + 4, ... of the split's run), and the
-// four k-groups' partial tiles are added in k-group order through LDS.
+// k-groups x two row halves (wave w: rows 32 (w & 1) .., all 64 columns), and
+// the four k-groups' partial tiles are added in k-group order through LDS.
+// The operands go through LDS four k-steps (128 record elements, two lines per
+// record row) at a time, loaded by sixteen consecutive threads per row; in
+// each stage k-group g multiplies its k-step g.  Rows past M load a valid row;
+// their outputs are computed and not stored.
 template <int D>
 __global__ __launch_bounds__(512) void dw_partial_small_bf16(const uint16_t* __restrict__ dSt,
                                                              const uint16_t* __restrict__ SZ, float* __restrict__ part,
                                                              int M, int P, int nsplit) {
     constexpr int REC = D * D + D, KPR = REC / 32;
+    constexpr int KST = 4;                 // k-steps per stage, one per k-group
+    constexpr int SROW = 32 * KST + 8;     // LDS row: 128 elements + 8 padding (272 bytes)
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][64 * SROW];   // [buffer][dSt, S][row]: 68 KB
     __shared__ f32x4 red[3][2][2][4][64];   // k-groups 1..3 x row half x acc[2][4] x lane: 48 KB
     const int s = blockIdx.x;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, gq = lane >> 4;
     const int half = wave & 1, kg = wave >> 1;
     const int i0 = 32 * half;
-    int ri[2], rj[4];
-    uint32_t mi[2], mj[4];
+    // staging role: rows srow and srow + 32 of both operands, 16-byte piece pc of the stage's 256 bytes
+    const int srow = tid >> 4, pc = tid & 15;
+    int rr[2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-        const int i = i0 + 16 * a + li;
-        ri[a] = i < M ? i : M - 1;
-        mi[a] = i < M ? 0xffffffffu : 0u;
-    }
+    for (int p = 0; p < 2; ++p) rr[p] = min(srow + 32 * p, M - 1) * REC;
+    const int nks = P * KPR, per = (nks + nsplit - 1) / nsplit;
+    const int k0 = min(nks, s * per), k1 = min(nks, k0 + per);
+    const int nst = (k1 - k0 + KST - 1) / KST;
+
+    struct Regs {
+        u32x4 a[2], b[2];
+    };
+    // Stage st: k-steps k0 + KST st + (pc >> 2); a k-step past k1 stages zeros.
+    auto load = [&](int st, Regs& r) {
+        const int ks = k0 + KST * st + (pc >> 2);
+        const bool ok = ks < k1;
+        const int kc = ok ? ks : k0;
+        const int bh = kc / KPR, col = (kc - bh * KPR) * 32 + (pc & 3) * 8;
+        const size_t base = (size_t)bh * M * REC + col;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int jj = 16 * c + li;
-        rj[c] = jj < M ? jj : M - 1;
-        mj[c] = jj < M ? 0xffffffffu : 0u;
-    }
+        for (int p = 0; p < 2; ++p) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(dSt + base + rr[p]);
+            const u32x4 y = *reinterpret_cast<const u32x4*>(SZ + base + rr[p]);
+            r.a[p] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+            r.b[p] = ok ? y : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store = [&](int buf, const Regs& r) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            *reinterpret_cast<u32x4*>(&lds[buf][0][(srow + 32 * p) * SROW + pc * 8]) = r.a[p];
+            *reinterpret_cast<u32x4*>(&lds[buf][1][(srow + 32 * p) * SROW + pc * 8]) = r.b[p];
+        }
+    };
     f32x4 acc[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    struct Ops {
+    auto compute = [&](int buf) {
+        const uint16_t* la = &lds[buf][0][(i0 + li) * SROW + 32 * kg + gq * 8];
+        const uint16_t* lb = &lds[buf][1][li * SROW + 32 * kg + gq * 8];
         u32x4 A[2], B[4];
-    };
-    auto load = [&](int ks, Ops& o) {
-        const int bh = ks / KPR, col = (ks - bh * KPR) * 32 + gq * 8;
-        const size_t rb = (size_t)bh * M;
 #pragma unroll
-        for (int a = 0; a < 2; ++a) o.A[a] = *reinterpret_cast<const u32x4*>(dSt + (rb + ri[a]) * REC + col);
+        for (int a = 0; a < 2; ++a) A[a] = *reinterpret_cast<const u32x4*>(la + 16 * a * SROW);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) o.B[c] = *reinterpret_cast<const u32x4*>(SZ + (rb + rj[c]) * REC + col);
-    };
-    auto compute = [&](const Ops& o) {
+        for (int c = 0; c < 4; ++c) B[c] = *reinterpret_cast<const u32x4*>(lb + 16 * c * SROW);
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(o.A[a] & mi[a], o.B[c] & mj[c], acc[a][c]);
+            for (int c = 0; c < 4; ++c) acc[a][c] = mfma_bf16(A[a], B[c], acc[a][c]);
     };
-    const int nks = P * KPR, per = (nks + nsplit - 1) / nsplit;
-    const int k0 = s * per, k1 = min(nks, k0 + per);
-    if (k0 + kg < k1) pipelined<2, Ops>(k0 + kg, 4, k1, load, compute);
+    if (nst > 0) {
+        Regs r0, r1;
+        load(0, r0);
+        if (nst > 1) load(1, r1);
+        store(0, r0);
+        __syncthreads();
+        // Stage st is in buffer st & 1; the register set of stage st + 1 is
+        // stored after stage st is multiplied, and stage st + 2 loads into the
+        // set just freed.
+        for (int st = 0; st < nst; st += 2) {
+            if (st + 2 < nst) load(st + 2, r0);
+            compute(0);
+            if (st + 1 >= nst) break;
+            store(1, r1);
+            __syncthreads();
+            if (st + 3 < nst) load(st + 3, r1);
+            compute(1);
+            if (st + 2 >= nst) break;
+            store(0, r0);
+            __syncthreads();
+        }
+    }
     if (kg > 0) {
 #pragma unroll
         for (int a = 0; a < 2; ++a)
