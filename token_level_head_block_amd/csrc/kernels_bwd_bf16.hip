@@ -28,22 +28,10 @@ namespace mhla {
 namespace {
 
 // A x B operand rows for a d x d matrix held as [e][c] (c fastest), the way
-// the summaries store S^T: row e, k = c (contiguous), lane (t, gq) rows in the
-// order that leaves each lane with 4*RT consecutive outputs.
-template <int D>
-__device__ __forceinline__ void rows_e_k_c(const uint16_t* __restrict__ m, int t, int gq, u32x4 (&a)[D / 16][D / 32]) {
-    constexpr int RT = D / 16, KS = D / 32;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-        const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) a[r][kk] = *reinterpret_cast<const u32x4*>(m + e * D + kk * 32 + gq * 8);
-    }
-}
-
-// The same rows with the k-slots of lane group gq at c = 4 * RT * gq + 8 * kk + s:
-// the 4 * RT channels that lane group also holds as output rows of a product
-// whose A operand comes from rows_c_k_e.
+// the summaries store S^T: row e, lane (t, gq) rows in the order that leaves
+// each lane with 4*RT consecutive outputs, and the k-slots of lane group gq at
+// c = 4 * RT * gq + 8 * kk + s: the 4 * RT channels that lane group also holds
+// as output rows of a product whose A operand comes from rows_c_k_e.
 template <int D>
 __device__ __forceinline__ void rows_e_k_cl(const uint16_t* __restrict__ m, int t, int gq, u32x4 (&a)[D / 16][D / 32]) {
     constexpr int RT = D / 16, KS = D / 32;
@@ -494,7 +482,9 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
                                                    const Geo g) {
     constexpr int RT = D / 16, KS = D / 32;
     constexpr int OSTR = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[8 * 16 * OSTR];
+    // per wave: the output staging of 16 token rows; first the summary tile [D][OSTR]
+    constexpr int SLICE = PAIR ? 16 * OSTR : D * OSTR;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[8 * SLICE];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = lane & 15, gq = lane >> 4;
     // Workgroup = (b, block j, token part, head group): part t takes a
@@ -511,7 +501,7 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
     const int gr1 = min(ngr, gr0 + gper);
     if (gr0 >= gr1) return;
     const int blk = (b * g.H + h) * g.M + j;
-    uint16_t* sout = lds + wave * (16 * OSTR);
+    uint16_t* sout = lds + wave * SLICE;
 
     static_assert(!PAIR || D == 64, "paired heads run the 64-channel layout");
     const uint16_t* mb = dS + (size_t)blk * (D * D);
@@ -564,7 +554,22 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
             dzc[4 * u] = x.x; dzc[4 * u + 1] = x.y; dzc[4 * u + 2] = x.z; dzc[4 * u + 3] = x.w;
         }
     } else {
-    rows_e_k_c<D>(mb, t, gq, a3);
+    // The D x D tile read with whole-line loads into the wave's slice, then
+    // gathered in both operand layouts (read straight in those layouts,
+    // consecutive lanes would address rows D elements apart).
+#pragma unroll
+    for (int p = 0; p < D * D / 512; ++p) {
+        const int x = p * 64 + lane, e = x / (D / 8), c8 = x % (D / 8);
+        *reinterpret_cast<u32x4*>(sout + e * OSTR + 8 * c8) = *reinterpret_cast<const u32x4*>(mb + e * D + 8 * c8);
+    }
+    // a3: row e = 4*RT*(t/4) + 4r + t%4, k = c = kk*32 + gq*8 + s
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            a3[r][kk] = *reinterpret_cast<const u32x4*>(sout + e * OSTR + kk * 32 + gq * 8);
+    }
     // a4: row c, k-slot s of k-step kk at e = kk*32 + gq*8 + s (the layout V is loaded in).
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -574,9 +579,10 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const int e0 = kk * 32 + gq * 8 + 2 * w;
-                a4[rt][kk][w] = (uint32_t)mb[e0 * D + c] | ((uint32_t)mb[(e0 + 1) * D + c] << 16);
+                a4[rt][kk][w] = (uint32_t)sout[e0 * OSTR + c] | ((uint32_t)sout[(e0 + 1) * OSTR + c] << 16);
             }
     }
+    // (the wave's LDS operations run in order: the tile is read before the output staging overwrites it)
     const float* zb = dZ + (size_t)blk * D;
 #pragma unroll
     for (int u = 0; u < RT; ++u) {
