@@ -25,6 +25,9 @@ CASES = [
     ("layer-c384-rows", 2, 6, 64, (40, 36), (8, 12), True, True, False, mh.MHLA_PHI_ELU1),
     # 4 blocks of 256 tokens: the core runs with token parts (4 summary and 4 apply parts)
     ("layer-c64-token-parts", 1, 2, 32, (32, 32), (16, 16), False, True, True, mh.MHLA_PHI_ELU1),
+    # relu feature map without q/k norm and 2C = 192: one projection tile holds
+    # columns on both sides of the preimage boundary
+    ("layer-c96-relu-split-tile", 1, 3, 32, (12, 16), (3, 4), False, True, True, mh.MHLA_PHI_RELU_EPS),
 ]
 
 

@@ -18,6 +18,8 @@
 // around 1e5 times the deviation.
 #include "launch.h"
 
+#include <type_traits>
+
 #include <mhla.h>
 
 namespace mhla {
@@ -30,10 +32,11 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // elu(y) + 1 = r for the feature map value r = relu(x) + eps > 0: the core
-// then evaluates the relu feature map through its elu + 1.
+// then evaluates the relu feature map through its elu + 1.  r >= eps is a
+// normal float, so the hardware log2 needs no denormal scaling.
 __device__ __forceinline__ float relu_phi_preimage(float x, float eps) {
     const float r = fmaxf(x, 0.f) + eps;
-    return r > 1.f ? r - 1.f : __logf(r);
+    return r > 1.f ? r - 1.f : __builtin_amdgcn_logf(r) * 0.693147180559945309f;
 }
 
 // ---------------------------------------------------------------- weight folding
@@ -128,8 +131,14 @@ struct GemmArgs {
 // they run on the same XCD and share its L2 copy of the token rows.
 template <bool LN, bool WHOLE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WHOLE ? 4 : 3))) void layer_gemm_bf16(const GemmArgs a) {
-    constexpr int TC = 128, TN = 128, KC = 64, STR = KC + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[TC * STR + TN * STR];   // 36 KB: four workgroups per CU
+    constexpr int TC = 128, TN = 128, KC = 64, STR = KC;
+    // Rows of 128 bytes, the 16-byte piece c of row r at piece c ^ ((r / 2) % 8):
+    // the sixteen rows of an operand read (and the two rows of eight pieces of a
+    // staging write) cover every bank once.
+    auto sw = [](int r, int c) { return r * STR + ((c ^ ((r >> 1) & 7)) << 3); };
+    constexpr int ESTR = TC + 8;   // epilogue rows of 272 bytes
+    constexpr int LDS_E = (TC * STR + TN * STR) > TN * ESTR ? (TC * STR + TN * STR) : TN * ESTR;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_E];   // 34 KB: four workgroups per CU
     uint16_t* const la = lds;
     uint16_t* const lb = lds + TC * STR;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -191,12 +200,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WHOLE ? 4 :
             }
         }
     };
+    const int soff = sw(tid >> 3, tid & 7);
     auto lstore = [&](int kc) {
         const bool partial = !WHOLE && (kc + 1) * KC > a.K;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int u = tid + 256 * s;
-            const int off = (u >> 3) * STR + (u & 7) * 8;
+            const int off = soff + 32 * STR * s;   // sw(u >> 3, u & 7): rows 32 s apart share the swizzle
             u32x4 x = ra[s], y = rb[s];
             if (partial) {
                 const uint32_t m = kc * KC + (u & 7) * 8 < a.K ? 0xffffffffu : 0u;
@@ -219,12 +229,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WHOLE ? 4 :
 #pragma unroll
         for (int ks = 0; ks < KC / 32; ++ks) {
             u32x4 fa[4], fb[4];
+            // sw(16 m + li, c) = (16 m + li) STR + ((c ^ (li / 2 % 8)) << 3)
+            const int po = ((ks * 4 + gq) ^ ((li >> 1) & 7)) << 3;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                fa[i] = *reinterpret_cast<const u32x4*>(&la[(64 * wc + 16 * i + li) * STR + ks * 32 + gq * 8]);
+                fa[i] = *reinterpret_cast<const u32x4*>(&la[(64 * wc + 16 * i + li) * STR + po]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                fb[j] = *reinterpret_cast<const u32x4*>(&lb[(64 * wn + 16 * j + li) * STR + ks * 32 + gq * 8]);
+                fb[j] = *reinterpret_cast<const u32x4*>(&lb[(64 * wn + 16 * j + li) * STR + po]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -250,36 +262,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WHOLE ? 4 :
     // finished values go to LDS as [token][feature] (the staging buffers are
     // free after the last barrier), then every lane stores 16 bytes so that
     // eight lanes write one token's 128 features as whole 128-byte lines.
-    constexpr int ESTR = TC + 8;   // 272-byte rows: the 16 tokens x 4 feature groups of a store hit distinct banks
-    static_assert(TN * ESTR <= TC * STR + TN * STR, "epilogue tile must fit the staging buffers");
-    uint16_t* et = lds;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int cl = 64 * wc + 16 * i + 4 * gq, c = c0 + cl;
-        const int cb = c < a.Nc ? c : a.Nc - 4;   // Nc is a multiple of 4; columns past it are never stored
-        const f32x4 bias = a.bias ? *reinterpret_cast<const f32x4*>(a.bias + cb) : f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 cs = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (LN) cs = *reinterpret_cast<const f32x4*>(a.colsum + cb);
-        const bool pre = c < a.phi_cols;
+    uint16_t* et = lds;   // [token][ESTR]
+    // PRE: 0 = no column of the tile takes the preimage, 1 = every column, 2 = per column
+    auto epilogue = [&](auto pre_kind) {
+        constexpr int PRE = decltype(pre_kind)::value;
+        float mu[4], rs[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int nl = 64 * wn + 16 * j + li, n = min(n0 + nl, a.R - 1);
-            float mu = 0.f, rs = 1.f;
-            if constexpr (LN) {
-                mu = a.mean[n];
-                rs = a.rstd[n];
-            }
-            float o[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float x = acc[i][j][v];
-                if constexpr (LN) x = rs * (x - mu * cs[v]);
-                x += bias[v];
-                o[v] = pre ? relu_phi_preimage(x, a.phi_eps) : x;
-            }
-            *reinterpret_cast<u32x2*>(&et[nl * ESTR + cl]) = u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+            const int n = min(n0 + 64 * wn + 16 * j + li, a.R - 1);
+            mu[j] = LN ? a.mean[n] : 0.f;
+            rs[j] = LN ? a.rstd[n] : 1.f;
         }
-    }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cl = 64 * wc + 16 * i + 4 * gq, c = c0 + cl;
+            const int cb = c < a.Nc ? c : a.Nc - 4;   // Nc is a multiple of 4; columns past it are never stored
+            const f32x4 bias = a.bias ? *reinterpret_cast<const f32x4*>(a.bias + cb) : f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 cs = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (LN) cs = *reinterpret_cast<const f32x4*>(a.colsum + cb);
+            const bool pre = PRE == 1 || (PRE == 2 && c < a.phi_cols);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int nl = 64 * wn + 16 * j + li;
+                float o[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float x = acc[i][j][v];
+                    if constexpr (LN) x = rs[j] * (x - mu[j] * cs[v]);
+                    x += bias[v];
+                    if constexpr (PRE == 1) o[v] = relu_phi_preimage(x, a.phi_eps);
+                    else if constexpr (PRE == 2) o[v] = pre ? relu_phi_preimage(x, a.phi_eps) : x;
+                    else o[v] = x;
+                }
+                *reinterpret_cast<u32x2*>(&et[nl * ESTR + cl]) = u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+            }
+        }
+    };
+    if (c0 + TC <= a.phi_cols) epilogue(std::integral_constant<int, 1>{});
+    else if (c0 >= a.phi_cols) epilogue(std::integral_constant<int, 0>{});
+    else epilogue(std::integral_constant<int, 2>{});
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < TN * TC / 8 / 256; ++s) {
