@@ -747,7 +747,7 @@ __device__ __forceinline__ void apply_tokens_bf16(Ops A, PrepLoad&& prep_load, P
     const int b = (int)fdiv(bh, g.div_H), h = bh - b * g.H;
     const int row = g.H * D;
     const int origin = block_origin(g, i);
-    const uint16_t* qb = Q + (b * g.N * row + h * D + gq * 8);
+    const uint16_t* qb = Q + (b * g.N * row + h * D);
     // Output of batch b as a raw buffer (at most 2^31 bytes: checked on the host);
     // the descriptor is wave-uniform, per-lane parts go in the offset.
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -760,6 +760,16 @@ __device__ __forceinline__ void apply_tokens_bf16(Ops A, PrepLoad&& prep_load, P
     __shared__ __attribute__((aligned(16))) uint16_t sout_all[MAXW * 16 * OSTR];
     uint16_t* sout = sout_all + (threadIdx.x >> 6) * (16 * OSTR);
 
+    // d <= 64: the group's q rows are loaded whole: load k brings tokens TPI k
+    // .. TPI k + TPI - 1, CPR lanes per row (consecutive lanes, consecutive 16
+    // bytes), and the rows go through the wave's LDS slice into the B-operand
+    // layout (lane (t, gq): token t, channels kk*32 + 8 gq ..); read straight in
+    // that layout, consecutive lanes would address different token rows
+    // (dit-s2-256x256 apply 23.5 -> 22.1 us, dit-s2-64x64 53.3 -> 50.7 us,
+    // sana-128x128 67.9 -> 65.2 us).  At d = 128 the direct loads stay
+    // (video-16x64x64 apply 101.9 against 102.6 us).
+    constexpr bool QROWS = D <= 64;
+    constexpr int TPI = 64 / CPR;   // token rows per load instruction; 16 / TPI == KS
     struct Raw {
         u32x4 q[KS];
         int off;
@@ -770,15 +780,34 @@ __device__ __forceinline__ void apply_tokens_bf16(Ops A, PrepLoad&& prep_load, P
         R.ok = p < p1;   // false for padding lanes and for groups past the end
         R.off = (origin + in_block(g, R.ok ? p : p1 - 1)) * row;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) R.q[kk] = ld<NTL>(reinterpret_cast<const u32x4*>(qb + R.off + kk * 32));
+        for (int k = 0; k < KS; ++k) {
+            if constexpr (QROWS) {
+                const int offk = __shfl(R.off, k * TPI + lane / CPR, 64);
+                R.q[k] = ld<NTL>(reinterpret_cast<const u32x4*>(qb + offk + (lane % CPR) * 8));
+            } else {
+                R.q[k] = ld<NTL>(reinterpret_cast<const u32x4*>(qb + R.off + k * 32 + gq * 8));
+            }
+        }
     };
     auto compute = [&](const Ops& A, const Raw& R) {
+        u32x4 qv[KS];
+        if constexpr (QROWS) {
+#pragma unroll
+            for (int k = 0; k < KS; ++k)
+                *reinterpret_cast<u32x4*>(sout + (k * TPI + lane / CPR) * OSTR + (lane % CPR) * 8) = R.q[k];
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+                qv[kk] = *reinterpret_cast<const u32x4*>(sout + t * OSTR + kk * 32 + gq * 8);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) qv[kk] = R.q[kk];
+        }
         u32x4 bq[KS];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
             for (int w = 0; w < 4; ++w)
-                bq[kk][w] = pack_bf16(phi_fast(bf_lo(R.q[kk][w])), phi_fast(bf_hi(R.q[kk][w])));
+                bq[kk][w] = pack_bf16(phi_fast(bf_lo(qv[kk][w])), phi_fast(bf_hi(qv[kk][w])));
         f32x4 acc[RT], accd = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
