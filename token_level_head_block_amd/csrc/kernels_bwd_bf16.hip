@@ -562,13 +562,13 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
         const int x = p * 64 + lane, e = x / (D / 8), c8 = x % (D / 8);
         *reinterpret_cast<u32x4*>(sout + e * OSTR + 8 * c8) = *reinterpret_cast<const u32x4*>(mb + e * D + 8 * c8);
     }
-    // a3: row e = 4*RT*(t/4) + 4r + t%4, k = c = kk*32 + gq*8 + s
+    // a3: row e = 4*RT*(t/4) + 4r + t%4, k = c = 4*RT*gq + 8*kk + s
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         const int e = 4 * RT * (t >> 2) + 4 * r + (t & 3);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
-            a3[r][kk] = *reinterpret_cast<const u32x4*>(sout + e * OSTR + kk * 32 + gq * 8);
+            a3[r][kk] = *reinterpret_cast<const u32x4*>(sout + e * OSTR + 4 * RT * gq + 8 * kk);
     }
     // a4: row c, k-slot s of k-step kk at e = kk*32 + gq*8 + s (the layout V is loaded in).
 #pragma unroll
@@ -602,8 +602,13 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
                                                                         g.N * row * 2, 0x00020000);
     const int olane = h * D * 2;
 
+    // Without head pairs phi(k) enters the dv product with k-slots c =
+    // 4*RT*gq + 8*kk + s, the channels of this lane's dk, so phi'(k) there
+    // shares its exponential and k is loaded once.  Head pairs keep k-slots
+    // kk*32 + 8*gq + s (one head per k-step, the same sums as one head per
+    // wave) and load k again at the dk channels.
     struct Raw {
-        u32x4 kv[KS], vv[KS], ko[RT / 2];
+        u32x4 kv[KS], vv[KS], ko[PAIR ? RT / 2 : 1];
         int off;
         bool ok;
     };
@@ -613,19 +618,36 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
         R.off = (origin + in_block(g, R.ok ? p : g.T - 1)) * row;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            R.kv[kk] = *reinterpret_cast<const u32x4*>(kb + R.off + kk * 32 + gq * 8);
+            R.kv[kk] = *reinterpret_cast<const u32x4*>(kb + R.off + (PAIR ? kk * 32 + gq * 8 : 4 * RT * gq + 8 * kk));
             R.vv[kk] = *reinterpret_cast<const u32x4*>(vb + R.off + kk * 32 + gq * 8);
         }
+        if constexpr (PAIR) {
 #pragma unroll
-        for (int u = 0; u < RT / 2; ++u) R.ko[u] = *reinterpret_cast<const u32x4*>(kb + R.off + 4 * RT * gq + 8 * u);
+            for (int u = 0; u < RT / 2; ++u)
+                R.ko[u] = *reinterpret_cast<const u32x4*>(kb + R.off + 4 * RT * gq + 8 * u);
+        }
     };
     auto compute = [&](const Raw& R) {
+        // with e = exp(min(x, 0)): phi(x) = max(x, 0) + e, phi'(x) = e
         u32x4 ba[KS];
+        float pg[4 * RT];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                ba[kk][w] = pack_bf16(phi_fast(bf_lo(R.kv[kk][w])), phi_fast(bf_hi(R.kv[kk][w])));
+            for (int w = 0; w < 4; ++w) {
+                const float x0 = bf_lo(R.kv[kk][w]), x1 = bf_hi(R.kv[kk][w]);
+                const float e0 = __expf(fminf(x0, 0.f)), e1 = __expf(fminf(x1, 0.f));
+                ba[kk][w] = pack_bf16(fmaxf(x0, 0.f) + e0, fmaxf(x1, 0.f) + e1);
+                pg[8 * kk + 2 * w] = e0;
+                pg[8 * kk + 2 * w + 1] = e1;
+            }
+        if constexpr (PAIR) {
+            float kl[4 * RT];
+#pragma unroll
+            for (int u = 0; u < RT / 2; ++u) unpack8(R.ko[u], kl + 8 * u);
+#pragma unroll
+            for (int cl = 0; cl < 4 * RT; ++cl) pg[cl] = phi_grad(kl[cl]);
+        }
         f32x4 accv[RT], acck[RT];
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
@@ -646,16 +668,13 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
             wv[2 * r + 1] = pack_bf16(accv[r][2], accv[r][3]);
         }
         store_rows<D>(sout, wv, lane, R.off, R.ok, rv, olane);
-        float kl[4 * RT];
-#pragma unroll
-        for (int u = 0; u < RT / 2; ++u) unpack8(R.ko[u], kl + 8 * u);
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             float x[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int cl = 4 * r + v;
-                x[v] = (acck[r][v] + dzc[cl]) * phi_grad(kl[cl]);
+                x[v] = (acck[r][v] + dzc[cl]) * pg[cl];
             }
             wv[2 * r] = pack_bf16(x[0], x[1]);
             wv[2 * r + 1] = pack_bf16(x[2], x[3]);
