@@ -40,14 +40,13 @@ __device__ __forceinline__ float relu_phi_preimage(float x, float eps) {
 }
 
 // ---------------------------------------------------------------- weight folding
-// One workgroup of 64 threads per output feature c of the QKV projection:
+// One wave per output feature c of the QKV projection:
 // W'[c][k] = bf16(Wt[c][k] gamma[k]), colsum'[c] = sum_k W'[c][k] (of the rounded
 // values), b'[c] = b[c] + sum_k Wt[c][k] beta[k].
-__global__ __launch_bounds__(64) void fold_ln_bf16(const uint16_t* __restrict__ Wt, const float* __restrict__ gamma,
-                                                   const float* __restrict__ beta, const float* __restrict__ bias,
-                                                   uint16_t* __restrict__ Wf, float* __restrict__ colsum,
-                                                   float* __restrict__ biasf, int K) {
-    const int c = blockIdx.x, lane = threadIdx.x;
+__device__ __forceinline__ void fold_ln_feature(const uint16_t* __restrict__ Wt, const float* __restrict__ gamma,
+                                                const float* __restrict__ beta, const float* __restrict__ bias,
+                                                uint16_t* __restrict__ Wf, float* __restrict__ colsum,
+                                                float* __restrict__ biasf, int K, int c, int lane) {
     const uint16_t* wr = Wt + (size_t)c * K;
     uint16_t* fr = Wf + (size_t)c * K;
     float s = 0.f, t = 0.f;
@@ -80,10 +79,10 @@ __global__ __launch_bounds__(64) void fold_ln_bf16(const uint16_t* __restrict__ 
 // K channels), once per token: eight lanes per row, one pass of shifted sums
 // (x - x0, x0 the row's first element, which keeps them accurate for a large
 // mean).  Workgroup = 32 rows.
-__global__ __launch_bounds__(256) void ln_stats_bf16(const uint16_t* __restrict__ X, float* __restrict__ mean,
-                                                     float* __restrict__ rstd, int R, int K, float eps) {
+__device__ __forceinline__ void ln_stats_rows(const uint16_t* __restrict__ X, float* __restrict__ mean,
+                                              float* __restrict__ rstd, int R, int K, float eps, int rg) {
     const int tid = threadIdx.x, part = tid & 7;
-    const int n = blockIdx.x * 32 + (tid >> 3);
+    const int n = rg * 32 + (tid >> 3);
     const int nc = n < R ? n : R - 1;
     const uint16_t* xr = X + (size_t)nc * K;
     const float x0 = bf_lo(*reinterpret_cast<const uint32_t*>(xr));
@@ -107,6 +106,23 @@ __global__ __launch_bounds__(256) void ln_stats_bf16(const uint16_t* __restrict_
         mean[n] = x0 + m1;
         rstd[n] = 1.f / sqrtf(fmaxf(s2 / (float)K - m1 * m1, 0.f) + eps);
     }
+}
+
+// The weight folding and the token statistics in one launch (they are
+// independent): workgroups [0, nfold) fold four features each (one per wave),
+// the rest take 32 token rows each.
+__global__ __launch_bounds__(256) void ln_prepare_bf16(const uint16_t* __restrict__ Wt, const float* __restrict__ gamma,
+                                                       const float* __restrict__ beta, const float* __restrict__ bias,
+                                                       uint16_t* __restrict__ Wf, float* __restrict__ colsum,
+                                                       float* __restrict__ biasf, int nfeat, int nfold,
+                                                       const uint16_t* __restrict__ X, float* __restrict__ mean,
+                                                       float* __restrict__ rstd, int R, int K, float eps) {
+    if ((int)blockIdx.x < nfold) {
+        const int c = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+        if (c < nfeat) fold_ln_feature(Wt, gamma, beta, bias, Wf, colsum, biasf, K, c, threadIdx.x & 63);
+        return;
+    }
+    ln_stats_rows(X, mean, rstd, R, K, eps, (int)blockIdx.x - nfold);
 }
 
 // ---------------------------------------------------------------- projection GEMM
@@ -447,7 +463,10 @@ hipError_t run_layer_bf16(const LayerLaunch& L) {
     };
     rec(0);
     // 1. LayerNorm folded into the QKV weights, then the projection
-    fold_ln_bf16<<<3 * C, 64, 0, L.stream>>>(L.w_qkv, L.ln_w, L.ln_b, L.b_qkv, L.wf, L.colsum, L.biasf, C);
+    const int nfold = (3 * C + 3) / 4;
+    ln_prepare_bf16<<<nfold + (R + 31) / 32, 256, 0, L.stream>>>(L.w_qkv, L.ln_w, L.ln_b, L.b_qkv, L.wf, L.colsum,
+                                                                   L.biasf, 3 * C, nfold, L.x, L.mean, L.rstd, R, C,
+                                                                   L.ln_eps);
     GemmArgs a;
     a.X = L.x;
     a.Wt = L.wf;
@@ -455,7 +474,6 @@ hipError_t run_layer_bf16(const LayerLaunch& L) {
     a.colsum = L.colsum;
     a.mean = L.mean;
     a.rstd = L.rstd;
-    ln_stats_bf16<<<(R + 31) / 32, 256, 0, L.stream>>>(L.x, L.mean, L.rstd, R, C, L.ln_eps);
     a.dst[0] = L.q; a.dst[1] = L.k; a.dst[2] = L.v;
     a.R = R; a.K = C; a.Nc = 3 * C; a.split = C;
     a.phi_cols = (L.relu_phi && !L.qn_w) ? 2 * C : 0;
