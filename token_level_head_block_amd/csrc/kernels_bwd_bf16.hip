@@ -700,15 +700,17 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
 // are computed and not stored (each output element depends only on its own
 // rows).  Partial sums go to part[s]; dw_reduce adds them in split order.
 // =====================================================================
+constexpr int DW_SROW = 72;                              // LDS row: 64 elements + 8 padding (144 bytes)
+constexpr int DW_LDS_BYTES = 2 * 2 * 128 * DW_SROW * 2;  // [buffer][dSt, S][row]: 72 KB
+
 template <int D>
-__global__ __launch_bounds__(512) void dw_partial_bf16(const uint16_t* __restrict__ dSt,
-                                                       const uint16_t* __restrict__ SZ, float* __restrict__ part,
-                                                       int M, int P, int nsplit, int ntj) {
+__device__ __forceinline__ void dw_tile(int s, int tile, uint16_t* __restrict__ lds_raw,
+                                        const uint16_t* __restrict__ dSt, const uint16_t* __restrict__ SZ,
+                                        float* __restrict__ part, int M, int P, int nsplit, int ntj) {
     constexpr int REC = D * D + D, KPR = REC / 32;
     constexpr int KST = 2;                // k-steps per stage
-    constexpr int SROW = 32 * KST + 8;    // LDS row: 64 elements + 8 padding (144 bytes)
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][128 * SROW];   // [buffer][dSt, S][row]: 72 KB
-    const int s = blockIdx.x, tile = blockIdx.y;
+    constexpr int SROW = DW_SROW;
+    auto lds = reinterpret_cast<uint16_t (*)[2][128 * SROW]>(lds_raw);
     const int ti = tile / ntj, tj = tile - ti * ntj;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, gq = lane >> 4;
@@ -805,6 +807,136 @@ __global__ __launch_bounds__(512) void dw_partial_bf16(const uint16_t* __restric
             }
 }
 
+template <int D>
+__global__ __launch_bounds__(512) void dw_partial_bf16(const uint16_t* __restrict__ dSt,
+                                                       const uint16_t* __restrict__ SZ, float* __restrict__ part,
+                                                       int M, int P, int nsplit, int ntj) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[DW_LDS_BYTES / 2];
+    dw_tile<D>(blockIdx.x, blockIdx.y, lds, dSt, SZ, part, M, P, nsplit, ntj);
+}
+
+// The gradient records mixed with W^T (dS, dz of every block) and dW's partial
+// products are independent, so one launch runs both: workgroups [0, ndw) are
+// dW tiles (as dw_partial), the rest mix one column tile of 64 record
+// elements of one (b, h) for all query blocks: wave w takes blocks 32 w ..
+// 32 w + 31 with its W operands in registers, the column tile of every source
+// record is staged once for the eight waves (the split mixing kernel's
+// operand packing and output mapping).  At most 256 blocks.
+template <int D, int NT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void mix_dw_bf16(
+    const uint16_t* __restrict__ dSt, const uint16_t* __restrict__ SZ, float* __restrict__ part, int nsplit, int ntj,
+    int ndw, const uint16_t* __restrict__ Wb, uint16_t* __restrict__ dS, float* __restrict__ dZ, const Geo g, int CT) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[DW_LDS_BYTES / 2];
+    const int id = blockIdx.x;
+    if (id < ndw) {
+        dw_tile<D>(id % nsplit, id / nsplit, lds, dSt, SZ, part, g.M, g.BH, nsplit, ntj);
+        return;
+    }
+    constexpr int REC = D * D + D, KMAX = 8, OROW = MIX_OROW, ROWS = 32;
+    u32x4* sA = reinterpret_cast<u32x4*>(lds);   // [r][kk][lane] operands, 32 KB; then output staging
+    const int c = id - ndw;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, gq = lane >> 4;
+    const int bh = c / CT, cp0 = (c - bh * CT) * 64;
+    const int M = g.M, NK = (M + 31) >> 5;
+    const int i0 = wave * ROWS;
+    const bool active = i0 < M;                  // then i0 + 32 <= roundup(M, 32): inside Wb's rows
+    const int rt0 = active ? i0 >> 4 : 0;
+    u32x4 bw[KMAX][2];
+#pragma unroll
+    for (int kk = 0; kk < KMAX; ++kk)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            bw[kk][t] = *reinterpret_cast<const u32x4*>(
+                Wb + ((size_t)((rt0 + t) * NK + (kk < NK ? kk : NK - 1)) * 64 + lane) * 8);
+    // stage A: unit (li', group of 8 source records) -> 4 packed operands, one per thread
+    const int units = 16 * 4 * NK;
+    const uint16_t* base = dSt + (size_t)bh * M * REC;
+    {
+        const int u = tid;
+        const int colp = cp0 + 4 * (u & 15);
+        const bool ok = u < units && colp < REC;
+        const int colc = ok ? colp : 0;
+        u32x2 raw[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int jj = 8 * (u >> 4) + s;
+            const u32x2 t = *reinterpret_cast<const u32x2*>(base + (size_t)(jj < M ? jj : M - 1) * REC + colc);
+            const uint32_t m = (ok && jj < M) ? 0xffffffffu : 0u;
+            raw[s] = u32x2{t.x & m, t.y & m};
+        }
+        if (u < units) {
+            const int jg = u >> 4, kk = jg >> 2, lanep = (jg & 3) * 16 + (u & 15);
+            u32x4 op[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                op[0][w] = pack_lo(raw[2 * w].x, raw[2 * w + 1].x);
+                op[1][w] = pack_hi(raw[2 * w].x, raw[2 * w + 1].x);
+                op[2][w] = pack_lo(raw[2 * w].y, raw[2 * w + 1].y);
+                op[3][w] = pack_hi(raw[2 * w].y, raw[2 * w + 1].y);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sA[(r * NK + kk) * 64 + lanep] = op[r];
+        }
+    }
+    __syncthreads();
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r][0] = acc[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (active) {
+#pragma unroll
+        for (int kk = 0; kk < KMAX; ++kk) {
+            if (kk >= NK) break;
+            u32x4 a[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = sA[(r * NK + kk) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc[r][t] = mfma_bf16(a[r], bw[kk][t], acc[r][t]);
+        }
+    }
+    __syncthreads();   // every wave is done with the A operands
+    if (!active) return;
+    // Lane holds C[col' = cp0 + 16*gq + 4*v + r][i = i0 + 16*t + li].
+    if (cp0 < D * D) {
+        uint16_t* stage = lds + wave * (ROWS * OROW);   // this wave's slice only
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            uint32_t wv[8];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                wv[2 * v] = pack_bf16(acc[0][t][v], acc[1][t][v]);
+                wv[2 * v + 1] = pack_bf16(acc[2][t][v], acc[3][t][v]);
+            }
+            uint16_t* dst = stage + (16 * t + li) * OROW + 16 * gq;
+            *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+        }
+#pragma unroll
+        for (int k = 0; k < ROWS / 8; ++k) {
+            const int rl = 8 * k + (lane >> 3), chunk = lane & 7;
+            const int i = i0 + rl;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rl * OROW + chunk * 8);
+            u32x4* dst = reinterpret_cast<u32x4*>(dS + ((size_t)bh * M + i) * (D * D) + cp0 + chunk * 8);
+            if (i < M) {
+                if constexpr ((NT & 2) != 0) __builtin_nontemporal_store(x, dst);
+                else *dst = x;
+            }
+        }
+    } else if (cp0 + 16 * gq < REC) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int i = i0 + 16 * t + li;
+            if (i >= M) continue;
+            float* dst = dZ + ((size_t)bh * M + i) * D + (cp0 + 16 * gq - D * D);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                *reinterpret_cast<f32x4*>(dst + 4 * v) = f32x4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
+        }
+    }
+}
+
 // dW[x] = sum over splits in split order; eight partial sums in flight per thread.
 __global__ __launch_bounds__(256) void dw_reduce(const float* __restrict__ part, float* __restrict__ dW, int MM,
                                                  int nsplit) {
@@ -886,15 +1018,27 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     gh.div_AP = make_fastdiv((uint32_t)gh.AP);
     const int grid_tok = gh.B * gh.M * gh.AP * gh.HG, block_tok = 64 * gh.G;
     rec(B, 2);
-    // the gradient records mixed with W^T on the forward's mixing kernels
-    err = launch_mix_records_bf16(L, B.dst, B.wbt, B.ds, B.dz, g);
-    if (err != hipSuccess) return err;
     const int ntj = (g.M + 127) / 128;
-    if (g.M <= 64)
-        dw_partial_small_bf16<D><<<B.nsplit, 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH, B.nsplit);
-    else
-        dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH,
-                                                                            B.nsplit, ntj);
+    if (g.M > 128 && g.M <= 256 && L.tune.mix_kind == 2 && L.tune.bwd_fuse) {
+        // the gradient records' W^T mixing and dW's partial products in one launch
+        const int CT = (D * D + D + 63) / 64, ndw = B.nsplit * ntj * ntj;
+        const int grid = ndw + g.BH * CT;
+        if (L.tune.nt_mix & 2)
+            mix_dw_bf16<D, 2><<<grid, 512, 0, L.stream>>>(B.dst, srec, B.part, B.nsplit, ntj, ndw, B.wbt, B.ds, B.dz,
+                                                           g, CT);
+        else
+            mix_dw_bf16<D, 0><<<grid, 512, 0, L.stream>>>(B.dst, srec, B.part, B.nsplit, ntj, ndw, B.wbt, B.ds, B.dz,
+                                                           g, CT);
+    } else {
+        // the gradient records mixed with W^T on the forward's mixing kernels
+        err = launch_mix_records_bf16(L, B.dst, B.wbt, B.ds, B.dz, g);
+        if (err != hipSuccess) return err;
+        if (g.M <= 64)
+            dw_partial_small_bf16<D><<<B.nsplit, 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH, B.nsplit);
+        else
+            dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH,
+                                                                                B.nsplit, ntj);
+    }
     dw_reduce<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, B.dw, g.M * g.M, B.nsplit);
     rec(B, 3);
     bool paired = false;

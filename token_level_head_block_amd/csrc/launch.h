@@ -24,6 +24,7 @@ struct Tuning {
     int mix_kind;        // bf16 path, M <= 256: 2 = mix_split (workgroup per tile), 1 = persistent
                          // mix_resident with W in registers, 0 = mix_summaries (any M)
     int mix_rows;        // mix_split: query blocks per wave / 16 (1 or 2; 0 = by M)
+    int bwd_fuse;        // backward: W^T mixing of the gradient records and dW partials in one launch
     int num_cus;         // compute units of the current device (persistent grid size)
 };
 

@@ -250,6 +250,7 @@ mhla::Tuning choose_tuning(const Shape& s) {
     t.mix_kind = env_int("MHLA_MIX", mix_default);
     if (t.mix_kind < 0 || t.mix_kind > 2) t.mix_kind = mix_default;
     t.mix_rows = env_int("MHLA_MIX_ROWS", 0);
+    t.bwd_fuse = env_int("MHLA_BWD_FUSE", 1) != 0;
     // Non-temporal stores of the mixed summaries: mixing 12.7 -> 11.7 us at
     // dit-s2-256x256 (T = 256, the apply unchanged), video-16x64x64 307 us
     // per step against 308; at T = 64 the apply waits longer for St (one
