@@ -394,7 +394,7 @@ struct BwdLayout {
 
 bool bwd_supported(const Shape& s) { return s.dtype == MHLA_BF16 && (s.D == 32 || s.D == 64); }
 
-BwdLayout bwd_layout(const Shape& s) {
+BwdLayout bwd_layout(const Shape& s, bool dw_with_mixing = true) {
     BwdLayout L;
     L.fwd = layout(s);
     const size_t recs = (size_t)(s.B * s.H * s.M);
@@ -405,10 +405,16 @@ BwdLayout bwd_layout(const Shape& s) {
     L.wbt = L.dz + align_up(recs * (size_t)s.D * 4);
     L.part = L.wbt + align_up(wpad);
     // dW: k-steps of 32 record elements over all (b, h), split so that about
-    // 256 workgroups share them.
+    // 256 workgroups share them.  Where the dW tiles run in one launch with
+    // the W^T mixing (129..256 blocks), at least DW_KSTEPS k-steps per
+    // workgroup: the mixing workgroups fill the rest of the GPU, and fewer
+    // splits mean fewer fp32 partial tiles to write and reduce
+    // (dit-s2-256x256: 64 -> 32 splits, the stage 31.0 -> 26.6 us).
+    constexpr int64_t DW_KSTEPS = 24;
     const int64_t tiles = ((s.M + 127) / 128) * ((s.M + 127) / 128);
     const int64_t ksteps = s.B * s.H * ((s.D * s.D + s.D) / 32);
     int64_t ns = 256 / tiles;
+    if (dw_with_mixing && s.M > 128 && s.M <= 256 && ns > ksteps / DW_KSTEPS) ns = ksteps / DW_KSTEPS;
     if (ns < 1) ns = 1;
     if (ns > ksteps) ns = ksteps > 0 ? ksteps : 1;
     L.nsplit = (int)ns;
@@ -437,7 +443,7 @@ struct CbwdLayout {
 
 CbwdLayout cbwd_layout(const Shape& s) {
     CbwdLayout L;
-    L.b = bwd_layout(s);
+    L.b = bwd_layout(s, false);   // its dW partials run in a launch of their own
     const size_t toks = (size_t)s.B * (size_t)s.N * (size_t)s.H;
     L.tsc = L.b.total;
     L.diag = L.tsc + align_up(toks * 8);
@@ -541,11 +547,11 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
         mhla::BwdLaunch& B = C.B;
         mhla::Launch& L = B.F;
         L.q = q; L.k = k; L.v = v; L.W = W; L.out = nullptr;
-        L.sz = base + lay.fwd.sz;
-        L.st = base + lay.fwd.st;
-        L.zt = reinterpret_cast<float*>(base + lay.fwd.zt);
-        L.wb = base + lay.fwd.wb;
-        L.wbt = base + lay.wbt;
+        L.sz = base + clay.b.fwd.sz;
+        L.st = base + clay.b.fwd.st;
+        L.zt = reinterpret_cast<float*>(base + clay.b.fwd.zt);
+        L.wb = base + clay.b.fwd.wb;
+        L.wbt = base + clay.b.wbt;
         L.g = make_geo(s, grid->eps);
         L.g.RD = kCausalWParts;   // the causal mixtures take W as bf16 high and low parts
         L.tune = choose_tuning(s);
@@ -564,12 +570,12 @@ mhla_status backward_impl(const void* q, const void* k, const void* v, const flo
         }
         B.dout = dout;
         B.dq = dq; B.dk = dk; B.dv = dv; B.dw = dW;
-        B.dst = reinterpret_cast<uint16_t*>(base + lay.dst);
-        B.ds = reinterpret_cast<uint16_t*>(base + lay.ds);
-        B.dz = reinterpret_cast<float*>(base + lay.dz);
-        B.wbt = reinterpret_cast<uint16_t*>(base + lay.wbt);
-        B.part = reinterpret_cast<float*>(base + lay.part);
-        B.nsplit = lay.nsplit;
+        B.dst = reinterpret_cast<uint16_t*>(base + clay.b.dst);
+        B.ds = reinterpret_cast<uint16_t*>(base + clay.b.ds);
+        B.dz = reinterpret_cast<float*>(base + clay.b.dz);
+        B.wbt = reinterpret_cast<uint16_t*>(base + clay.b.wbt);
+        B.part = reinterpret_cast<float*>(base + clay.b.part);
+        B.nsplit = clay.b.nsplit;
         B.kv_parts = 1;
         B.q_parts = 1;
         B.dpart = nullptr;
