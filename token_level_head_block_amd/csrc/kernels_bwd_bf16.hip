@@ -1018,27 +1018,8 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     gh.div_AP = make_fastdiv((uint32_t)gh.AP);
     const int grid_tok = gh.B * gh.M * gh.AP * gh.HG, block_tok = 64 * gh.G;
     rec(B, 2);
-    const int ntj = (g.M + 127) / 128;
-    if (g.M > 128 && g.M <= 256 && L.tune.mix_kind == 2 && L.tune.bwd_fuse) {
-        // the gradient records' W^T mixing and dW's partial products in one launch
-        const int CT = (D * D + D + 63) / 64, ndw = B.nsplit * ntj * ntj;
-        const int grid = ndw + g.BH * CT;
-        if (L.tune.nt_mix & 2)
-            mix_dw_bf16<D, 2><<<grid, 512, 0, L.stream>>>(B.dst, srec, B.part, B.nsplit, ntj, ndw, B.wbt, B.ds, B.dz,
-                                                           g, CT);
-        else
-            mix_dw_bf16<D, 0><<<grid, 512, 0, L.stream>>>(B.dst, srec, B.part, B.nsplit, ntj, ndw, B.wbt, B.ds, B.dz,
-                                                           g, CT);
-    } else {
-        // the gradient records mixed with W^T on the forward's mixing kernels
-        err = launch_mix_records_bf16(L, B.dst, B.wbt, B.ds, B.dz, g);
-        if (err != hipSuccess) return err;
-        if (g.M <= 64)
-            dw_partial_small_bf16<D><<<B.nsplit, 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH, B.nsplit);
-        else
-            dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH,
-                                                                                B.nsplit, ntj);
-    }
+    err = launch_mix_dw_bf16(B, g, srec);
+    if (err != hipSuccess) return err;
     dw_reduce<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, B.dw, g.M * g.M, B.nsplit);
     rec(B, 3);
     bool paired = false;
@@ -1075,20 +1056,39 @@ __global__ __launch_bounds__(256) void fill_zero(float* __restrict__ p, int n) {
 
 }  // namespace
 
-hipError_t launch_mix_transposed_bf16(const BwdLaunch& B, const Geo& g) {
-    return launch_mix_records_bf16(B.F, B.dst, B.wbt, B.ds, B.dz, g);
-}
-
-hipError_t launch_dw_partial_bf16(const BwdLaunch& B, const Geo& g, const uint16_t* srec) {
+hipError_t launch_mix_dw_bf16(const BwdLaunch& B, const Geo& g, const uint16_t* srec) {
+    const Launch& L = B.F;
     const int ntj = (g.M + 127) / 128;
-    const hipStream_t st = B.F.stream;
+    if (g.M > 128 && g.M <= 256 && L.tune.mix_kind == 2 && L.tune.bwd_fuse) {
+        // the gradient records' W^T mixing and dW's partial products in one launch
+        auto go = [&](auto d) {
+            constexpr int D = decltype(d)::value;
+            const int CT = (D * D + D + 63) / 64, ndw = B.nsplit * ntj * ntj;
+            const int grid = ndw + g.BH * CT;
+            if (L.tune.nt_mix & 2)
+                mix_dw_bf16<D, 2><<<grid, 512, 0, L.stream>>>(B.dst, srec, B.part, B.nsplit, ntj, ndw, B.wbt, B.ds,
+                                                               B.dz, g, CT);
+            else
+                mix_dw_bf16<D, 0><<<grid, 512, 0, L.stream>>>(B.dst, srec, B.part, B.nsplit, ntj, ndw, B.wbt, B.ds,
+                                                               B.dz, g, CT);
+        };
+        switch (g.D) {
+            case 32: go(std::integral_constant<int, 32>{}); break;
+            case 64: go(std::integral_constant<int, 64>{}); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    // the gradient records mixed with W^T on the forward's mixing kernels, then dW's partials
+    const hipError_t err = launch_mix_records_bf16(L, B.dst, B.wbt, B.ds, B.dz, g);
+    if (err != hipSuccess) return err;
     auto go = [&](auto d) {
         constexpr int D = decltype(d)::value;
         if (g.M <= 64)
-            dw_partial_small_bf16<D><<<B.nsplit, 512, 0, st>>>(B.dst, srec, B.part, g.M, g.BH, B.nsplit);
+            dw_partial_small_bf16<D><<<B.nsplit, 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH, B.nsplit);
         else
-            dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, st>>>(B.dst, srec, B.part, g.M, g.BH, B.nsplit,
-                                                                           ntj);
+            dw_partial_bf16<D><<<dim3(B.nsplit, ntj * ntj), 512, 0, L.stream>>>(B.dst, srec, B.part, g.M, g.BH,
+                                                                                B.nsplit, ntj);
     };
     switch (g.D) {
         case 32: go(std::integral_constant<int, 32>{}); break;

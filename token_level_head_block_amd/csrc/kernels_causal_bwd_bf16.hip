@@ -872,9 +872,7 @@ hipError_t run_cbwd_d(const CausalBwdLaunch& C) {
     g.RD = 1;
     launch_nw<D, false>(C, g);
     rec_event(C, 2);
-    err = launch_mix_transposed_bf16(B, g);
-    if (err != hipSuccess) return err;
-    err = launch_dw_partial_bf16(B, g, static_cast<const uint16_t*>(L.sz));
+    err = launch_mix_dw_bf16(B, g, static_cast<const uint16_t*>(L.sz));
     if (err != hipSuccess) return err;
     dw_reduce_causal<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, C.diag, B.dw, g.M, B.nsplit, g.BH);
     rec_event(C, 3);

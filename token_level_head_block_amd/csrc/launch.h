@@ -77,16 +77,16 @@ struct BwdLaunch {
 // Summary and mixing kernels of the bf16 forward only (regions of F).
 hipError_t run_bf16_summaries(const Launch& L);
 hipError_t run_bwd_bf16(const BwdLaunch& B);
-// Pieces of the bf16 backward shared with the causal form: the mixing of
-// B.dst with W^T (B.wbt) into B.ds, B.dz, and the dW partial products of
-// B.dst with the summary records srec into B.part (g: one record per block).
-hipError_t launch_mix_transposed_bf16(const BwdLaunch& B, const Geo& g);
 // The bf16 mixing product of records src (layout of the summaries) with W's
 // operands wops (as converted by the summary launch) into dst (bf16) and
 // zdst (fp32), on the kernel that suits g (L supplies tuning and stream).
 hipError_t launch_mix_records_bf16(const Launch& L, const uint16_t* src, const uint16_t* wops, uint16_t* dst,
                                   float* zdst, const Geo& g);
-hipError_t launch_dw_partial_bf16(const BwdLaunch& B, const Geo& g, const uint16_t* srec);
+// The piece of the bf16 backward shared with the causal form: the mixing of
+// B.dst with W^T (B.wbt) into B.ds, B.dz, and the dW partial products of
+// B.dst with the summary records srec into B.nsplit partial tiles at B.part
+// (g: one record per block); one launch for 129..256 blocks, two otherwise.
+hipError_t launch_mix_dw_bf16(const BwdLaunch& B, const Geo& g, const uint16_t* srec);
 
 // The bf16 causal backward (d = 32 or 64, chunks contiguous in raster order,
 // one sub-chunk per chunk).  B.F runs the recompute (path MHLA_PATH_CAUSAL,

@@ -394,7 +394,7 @@ struct BwdLayout {
 
 bool bwd_supported(const Shape& s) { return s.dtype == MHLA_BF16 && (s.D == 32 || s.D == 64); }
 
-BwdLayout bwd_layout(const Shape& s, bool dw_with_mixing = true) {
+BwdLayout bwd_layout(const Shape& s) {
     BwdLayout L;
     L.fwd = layout(s);
     const size_t recs = (size_t)(s.B * s.H * s.M);
@@ -414,7 +414,7 @@ BwdLayout bwd_layout(const Shape& s, bool dw_with_mixing = true) {
     const int64_t tiles = ((s.M + 127) / 128) * ((s.M + 127) / 128);
     const int64_t ksteps = s.B * s.H * ((s.D * s.D + s.D) / 32);
     int64_t ns = 256 / tiles;
-    if (dw_with_mixing && s.M > 128 && s.M <= 256 && ns > ksteps / DW_KSTEPS) ns = ksteps / DW_KSTEPS;
+    if (s.M > 128 && s.M <= 256 && ns > ksteps / DW_KSTEPS) ns = ksteps / DW_KSTEPS;
     if (ns < 1) ns = 1;
     if (ns > ksteps) ns = ksteps > 0 ? ksteps : 1;
     L.nsplit = (int)ns;
@@ -443,7 +443,7 @@ struct CbwdLayout {
 
 CbwdLayout cbwd_layout(const Shape& s) {
     CbwdLayout L;
-    L.b = bwd_layout(s, false);   // its dW partials run in a launch of their own
+    L.b = bwd_layout(s);
     const size_t toks = (size_t)s.B * (size_t)s.N * (size_t)s.H;
     L.tsc = L.b.total;
     L.diag = L.tsc + align_up(toks * 8);
