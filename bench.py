@@ -269,9 +269,9 @@ def backward_bytes(p, general=False, causal=False):
     return {
         "recompute (block_kv_summary + mix)": 2 * tensor + rec + rec + w + st + zt,
         "bwd_query": 2 * tensor + st + zt + tensor + rec,
-        "mix_transposed + dW": rec + w + st + zt + 2 * rec + w,
-        "bwd_kv": 2 * tensor + st + zt + 2 * tensor,
-    }
+        "mix_transposed + dW partials": rec + w + st + zt + 2 * rec,
+        "bwd_kv + dW reduce": 2 * tensor + st + zt + 2 * tensor + w,
+    }   # (the reduce runs in the dW stage instead when the partials are many)
 
 
 def bench_backward(args, p, torch, mh, synth):

@@ -10,7 +10,7 @@
 //   dq  = (St_i dnum + zt_i dden) * phi'(q)
 //   dSt_i = sum_{n in i} u dnum^T,  dzt_i = sum_{n in i} u dden        (bwd_query)
 //   dS_j = sum_i W[i,j] dSt_i,  dz_j = sum_i W[i,j] dzt_i              (mixing with W^T)
-//   dW[i,j] = sum over (b, h) of <dSt_i, S_j> + <dzt_i, z_j>          (dw_partial + dw_reduce)
+//   dW[i,j] = sum over (b, h) of <dSt_i, S_j> + <dzt_i, z_j>          (dw_partial, then the sum of its partials)
 //   dv = dS_j^T a,  dk = (dS_j v + dz_j) * phi'(k)                       (bwd_kv)
 //
 // with phi'(x) = 1 for x > 0 and exp(x) otherwise.  Products run on bf16
@@ -465,6 +465,22 @@ __global__ __launch_bounds__(256) void fold_parts_bf16(const T* __restrict__ par
     out[x] = (uint16_t)(pack_bf16(sum, 0.f) & 0xffffu);
 }
 
+// dW[x] = the sum of the split partials part[0..nsplit)[x] in split order,
+// eight loads in flight per thread.
+__device__ __forceinline__ float dw_sum(const float* __restrict__ part, int x, int MM, int nsplit) {
+    float s = 0.f;
+    int k = 0;
+    for (; k + 8 <= nsplit; k += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(k + u) * MM + x];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; k < nsplit; ++k) s += part[(size_t)k * MM + x];
+    return s;
+}
+
 // =====================================================================
 // bwd_kv: dv and dk per source block.  Workgroup = (b, block j, group of
 // <= 8 heads), one wave per head over the block's tokens, 16 per step:
@@ -479,7 +495,15 @@ template <int D, bool PAIR = false>
 __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                    const uint16_t* __restrict__ dS, const float* __restrict__ dZ,
                                                    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-                                                   const Geo g) {
+                                                   const Geo g, const float* __restrict__ part,
+                                                   float* __restrict__ dW, int MM, int nsplit, int nkv) {
+    // Workgroups from nkv on reduce dW's split partials (independent of the
+    // key/value gradients; they run beside them instead of in a launch of their own).
+    if ((int)blockIdx.x >= nkv) {
+        const int x = ((int)blockIdx.x - nkv) * (int)blockDim.x + (int)threadIdx.x;
+        if (x < MM) dW[x] = dw_sum(part, x, MM, nsplit);
+        return;
+    }
     constexpr int RT = D / 16, KS = D / 32;
     constexpr int OSTR = D + 8;
     // per wave: the output staging of 16 token rows; first the summary tile [D][OSTR]
@@ -698,7 +722,7 @@ __global__ __launch_bounds__(512) void bwd_kv_bf16(const uint16_t* __restrict__ 
 // loads of the next two stages are in flight while one is multiplied.  Wave
 // (wi, wj) computes 32 i x 64 j.  Rows past M load a valid row; their outputs
 // are computed and not stored (each output element depends only on its own
-// rows).  Partial sums go to part[s]; dw_reduce adds them in split order.
+// rows).  Partial sums go to part[s]; dw_sum adds them in split order.
 // =====================================================================
 constexpr int DW_SROW = 72;                              // LDS row: 64 elements + 8 padding (144 bytes)
 constexpr int DW_LDS_BYTES = 2 * 2 * 128 * DW_SROW * 2;  // [buffer][dSt, S][row]: 72 KB
@@ -937,22 +961,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
     }
 }
 
-// dW[x] = sum over splits in split order; eight partial sums in flight per thread.
 __global__ __launch_bounds__(256) void dw_reduce(const float* __restrict__ part, float* __restrict__ dW, int MM,
                                                  int nsplit) {
     const int x = blockIdx.x * blockDim.x + threadIdx.x;
-    if (x >= MM) return;
-    float s = 0.f;
-    int k = 0;
-    for (; k + 8 <= nsplit; k += 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(k + u) * MM + x];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) s += v[u];
-    }
-    for (; k < nsplit; ++k) s += part[(size_t)k * MM + x];
-    dW[x] = s;
+    if (x < MM) dW[x] = dw_sum(part, x, MM, nsplit);
 }
 
 inline void rec(const BwdLaunch& B, int k) {
@@ -1020,7 +1032,14 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     rec(B, 2);
     err = launch_mix_dw_bf16(B, g, srec);
     if (err != hipSuccess) return err;
-    dw_reduce<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, B.dw, g.M * g.M, B.nsplit);
+    // dW's split partials are summed by extra workgroups at the end of the
+    // key/value launch while each thread's chain of loads is short (dit-s2-256x256,
+    // 32 splits: 152.5 -> 150.1 us per step); a long chain (dit-s2-64x64, 256
+    // splits of 4096 entries) would start last and outlast the key/value
+    // workgroups, so it keeps a launch of its own.
+    const int MM = g.M * g.M;
+    const bool reduce_in_kv = B.nsplit <= 64;
+    if (!reduce_in_kv) dw_reduce<<<(MM + 255) / 256, 256, 0, L.stream>>>(B.part, B.dw, MM, B.nsplit);
     rec(B, 3);
     bool paired = false;
     if constexpr (D == 32) {
@@ -1035,16 +1054,17 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
             gp.div_HG = make_fastdiv((uint32_t)gp.HG);
             gp.AP = gh.AP;
             gp.div_AP = gh.div_AP;
-            bwd_kv_bf16<64, true><<<gp.B * gp.M * gp.AP * gp.HG, 64 * gp.G, 0, L.stream>>>(
+            const int nkv = gp.B * gp.M * gp.AP * gp.HG, blk = 64 * gp.G;
+            bwd_kv_bf16<64, true><<<nkv + (reduce_in_kv ? (MM + blk - 1) / blk : 0), blk, 0, L.stream>>>(
                 static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v), B.ds, B.dz,
-                static_cast<uint16_t*>(B.dk), static_cast<uint16_t*>(B.dv), gp);
+                static_cast<uint16_t*>(B.dk), static_cast<uint16_t*>(B.dv), gp, B.part, B.dw, MM, B.nsplit, nkv);
             paired = true;
         }
     }
     if (!paired)
-        bwd_kv_bf16<D><<<grid_tok, block_tok, 0, L.stream>>>(
+        bwd_kv_bf16<D><<<grid_tok + (reduce_in_kv ? (MM + block_tok - 1) / block_tok : 0), block_tok, 0, L.stream>>>(
             static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v), B.ds, B.dz,
-            static_cast<uint16_t*>(B.dk), static_cast<uint16_t*>(B.dv), gh);
+            static_cast<uint16_t*>(B.dk), static_cast<uint16_t*>(B.dv), gh, B.part, B.dw, MM, B.nsplit, grid_tok);
     rec(B, 4);
     return hipGetLastError();
 }
