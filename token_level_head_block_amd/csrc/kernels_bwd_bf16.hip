@@ -961,10 +961,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
     }
 }
 
-__global__ __launch_bounds__(256) void dw_reduce(const float* __restrict__ part, float* __restrict__ dW, int MM,
-                                                 int nsplit) {
-    const int x = blockIdx.x * blockDim.x + threadIdx.x;
-    if (x < MM) dW[x] = dw_sum(part, x, MM, nsplit);
+// dW from many split partials: a workgroup takes 16 entries, its 16 lane
+// groups a sixteenth of the splits each (in split order), and the 16 group
+// sums are added in group order, so each thread's chain of loads is nsplit / 16
+// long instead of nsplit.
+__global__ __launch_bounds__(256) void dw_reduce_wide(const float* __restrict__ part, float* __restrict__ dW, int MM,
+                                                      int nsplit) {
+    __shared__ float red[16][17];
+    const int xl = threadIdx.x & 15, grp = threadIdx.x >> 4;
+    const int x = blockIdx.x * 16 + xl;
+    const int per = (nsplit + 15) >> 4;
+    const int k0 = min(nsplit, grp * per), k1 = min(nsplit, k0 + per);
+    float s = 0.f;
+    if (x < MM) {
+        int k = k0;
+        for (; k + 8 <= k1; k += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(k + u) * MM + x];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; k < k1; ++k) s += part[(size_t)k * MM + x];
+    }
+    red[grp][xl] = s;
+    __syncthreads();
+    if (grp == 0 && x < MM) {
+        float t = red[0][xl];
+#pragma unroll
+        for (int q = 1; q < 16; ++q) t += red[q][xl];
+        dW[x] = t;
+    }
 }
 
 inline void rec(const BwdLaunch& B, int k) {
@@ -1039,7 +1066,7 @@ hipError_t run_bwd_d(const BwdLaunch& B) {
     // workgroups, so it keeps a launch of its own.
     const int MM = g.M * g.M;
     const bool reduce_in_kv = B.nsplit <= 64;
-    if (!reduce_in_kv) dw_reduce<<<(MM + 255) / 256, 256, 0, L.stream>>>(B.part, B.dw, MM, B.nsplit);
+    if (!reduce_in_kv) dw_reduce_wide<<<(MM + 15) / 16, 256, 0, L.stream>>>(B.part, B.dw, MM, B.nsplit);
     rec(B, 3);
     bool paired = false;
     if constexpr (D == 32) {
