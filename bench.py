@@ -250,8 +250,8 @@ def backward_bytes(p, general=False, causal=False):
         return {
             "recompute (summary + causal mix)": 2 * tensor + rec + rec + w + st + zt,
             "query side": 4 * tensor + st + zt + tensor + rec + tok + P * M * 4,
-            "mix_transposed + dW": rec + w + st + zt + 2 * rec + P * M * 4 + w,
-            "key/value side": 4 * tensor + tok + st + zt + 2 * tensor,
+            "mix_transposed + dW partials": rec + w + st + zt + 2 * rec,
+            "key/value side + dW reduce": 4 * tensor + tok + st + zt + 2 * tensor + P * M * 4 + w,
         }
     if general or causal:
         rec = P * M * (d * d + d) * 4

@@ -567,6 +567,36 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     }
 }
 
+// dW of the causal form: entries below the diagonal are sums over the
+// partial products (split order), the diagonal is the pairs' in-chunk terms
+// (pair order), entries above it are zero.
+__device__ __forceinline__ float dw_causal_entry(const float* __restrict__ part, const float* __restrict__ dg, int x,
+                                                 int M, int nsplit, int P) {
+    const int i = x / M, j = x - i * M;
+    const int MM = M * M;
+    float s = 0.f;
+    if (j < i) {
+        int k = 0;
+        for (; k + 8 <= nsplit; k += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(k + u) * MM + x];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; k < nsplit; ++k) s += part[(size_t)k * MM + x];
+    } else if (j == i) {
+        for (int p = 0; p < P; ++p) s += dg[(size_t)p * M + i];
+    }
+    return s;
+}
+
+__global__ __launch_bounds__(256) void dw_reduce_causal(const float* __restrict__ part, const float* __restrict__ dg,
+                                                        float* __restrict__ dW, int M, int nsplit, int P) {
+    const int x = blockIdx.x * blockDim.x + threadIdx.x;
+    if (x < M * M) dW[x] = dw_causal_entry(part, dg, x, M, nsplit, P);
+}
+
 // =====================================================================
 // Key/value side.  Workgroup = (b, chunk i, head h) with NW waves; per key
 // tile, wave w takes key groups w and 2 NW - 1 - w (phi(k) and v of its keys
@@ -587,7 +617,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ tsc, const uint16_t* __restrict__ dS,
     const float* __restrict__ dZ, const float* __restrict__ W, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    const Geo g) {
+    const Geo g, const float* __restrict__ part, const float* __restrict__ dg, float* __restrict__ dW, int nsplit,
+    int nkv) {
+    // Workgroups from nkv on form dW from its split partials and the in-chunk
+    // diagonal terms, beside the key/value gradients (which do not need it).
+    if ((int)blockIdx.x >= nkv) {
+        const int x = ((int)blockIdx.x - nkv) * (64 * NW) + (int)threadIdx.x;
+        if (x < g.M * g.M) dW[x] = dw_causal_entry(part, dg, x, g.M, nsplit, g.BH);
+        return;
+    }
     constexpr int RT = D / 16, KS = D / 32;
     constexpr int NT = 64 * NW, KT = 32 * NW, NKG = KT / 16;
     constexpr int KSTR = D + 8, VSTR = KT + 8;
@@ -785,32 +823,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     }
 }
 
-// dW of the causal form: entries below the diagonal are sums over the
-// partial products (split order), the diagonal is the pairs' in-chunk terms
-// (pair order), entries above it are zero.
-__global__ __launch_bounds__(256) void dw_reduce_causal(const float* __restrict__ part, const float* __restrict__ dg,
-                                                        float* __restrict__ dW, int M, int nsplit, int P) {
-    const int x = blockIdx.x * blockDim.x + threadIdx.x;
-    if (x >= M * M) return;
-    const int i = x / M, j = x - i * M;
-    const int MM = M * M;
-    float s = 0.f;
-    if (j < i) {
-        int k = 0;
-        for (; k + 8 <= nsplit; k += 8) {
-            float v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(k + u) * MM + x];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) s += v[u];
-        }
-        for (; k < nsplit; ++k) s += part[(size_t)k * MM + x];
-    } else if (j == i) {
-        for (int p = 0; p < P; ++p) s += dg[(size_t)p * M + i];
-    }
-    dW[x] = s;
-}
-
 template <int D, int NW>
 void launch_pair(const CausalBwdLaunch& C, const Geo& g) {
     const unsigned grid = (unsigned)(g.B * g.M * g.H);
@@ -822,13 +834,14 @@ void launch_pair(const CausalBwdLaunch& C, const Geo& g) {
 }
 
 template <int D, int NW>
-void launch_kv(const CausalBwdLaunch& C, const Geo& g) {
-    const unsigned grid = (unsigned)(g.B * g.M * g.H);
+void launch_kv(const CausalBwdLaunch& C, const Geo& g, bool with_reduce) {
+    const int nkv = g.B * g.M * g.H, MM = g.M * g.M;
+    const int nred = with_reduce ? (MM + 64 * NW - 1) / (64 * NW) : 0;
     const Launch& L = C.B.F;
-    causal_bwd_kv_bf16<D, NW><<<grid, 64 * NW, 0, L.stream>>>(
+    causal_bwd_kv_bf16<D, NW><<<(unsigned)(nkv + nred), 64 * NW, 0, L.stream>>>(
         static_cast<const uint16_t*>(L.q), static_cast<const uint16_t*>(L.k), static_cast<const uint16_t*>(L.v),
         static_cast<const uint16_t*>(C.B.dout), C.tsc, C.B.ds, C.B.dz, L.W, static_cast<uint16_t*>(C.B.dk),
-        static_cast<uint16_t*>(C.B.dv), g);
+        static_cast<uint16_t*>(C.B.dv), g, C.B.part, C.diag, C.B.dw, C.B.nsplit, nkv);
 }
 
 // Waves per workgroup: enough for two 16-token groups each, at most 4.  Two
@@ -837,11 +850,11 @@ void launch_kv(const CausalBwdLaunch& C, const Geo& g) {
 // (dit-s2-256x256-causal-rows: query side 174 -> 167 us, key/value side
 // 149 -> 137 us; workgroups of 2 waves: 211 and 199 us).
 template <int D, bool KV>
-void launch_nw(const CausalBwdLaunch& C, const Geo& g) {
+void launch_nw(const CausalBwdLaunch& C, const Geo& g, bool with_reduce = false) {
     const int nit = (g.T + 15) / 16;
     auto go = [&](auto nw) {
         constexpr int NW = decltype(nw)::value;
-        if constexpr (KV) launch_kv<D, NW>(C, g);
+        if constexpr (KV) launch_kv<D, NW>(C, g, with_reduce);
         else launch_pair<D, NW>(C, g);
     };
     if (nit > 4) go(std::integral_constant<int, 4>{});
@@ -874,9 +887,13 @@ hipError_t run_cbwd_d(const CausalBwdLaunch& C) {
     rec_event(C, 2);
     err = launch_mix_dw_bf16(B, g, static_cast<const uint16_t*>(L.sz));
     if (err != hipSuccess) return err;
-    dw_reduce_causal<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, C.diag, B.dw, g.M, B.nsplit, g.BH);
+    // dW's partials summed beside the key/value side while the chains are
+    // short (as in the non-causal backward), else in a launch of their own
+    const bool reduce_in_kv = B.nsplit <= 64;
+    if (!reduce_in_kv)
+        dw_reduce_causal<<<(g.M * g.M + 255) / 256, 256, 0, L.stream>>>(B.part, C.diag, B.dw, g.M, B.nsplit, g.BH);
     rec_event(C, 3);
-    launch_nw<D, true>(C, g);
+    launch_nw<D, true>(C, g, reduce_in_kv);
     rec_event(C, 4);
     return hipGetLastError();
 }
