@@ -392,20 +392,36 @@ __global__ __launch_bounds__(256) void lepe_add_bf16(const uint16_t* __restrict_
     const int y0 = ty * LP_TY, x0 = tx * LP_TX, ch0 = cg * LP_TCH;
     const int nch = min(LP_TCH, C - ch0);   // 64, or 32 for the last group when C % 64 == 32
     const size_t img = (size_t)b * Y * X;
-    // halo of v: unit = (position, 8 channels)
-    for (int u = tid; u < HY * HX * (LP_TCH / 8); u += 256) {
-        const int part = u % (LP_TCH / 8), pos = u / (LP_TCH / 8);
-        const int hy = pos / HX, hx = pos % HX;
-        const int yy = y0 + hy - 2, xx = x0 + hx - 2;
-        u32x4 val = u32x4{0u, 0u, 0u, 0u};
-        if (yy >= 0 && yy < Y && xx >= 0 && xx < X && part * 8 < nch)
-            val = *reinterpret_cast<const u32x4*>(V + (img + (size_t)yy * X + xx) * C + ch0 + part * 8);
-        *reinterpret_cast<u32x4*>(&vt[pos * PAIRS + part * 4]) = val;
-    }
     const int p = tid & (PAIRS - 1), xg = tid / PAIRS;   // channel pair, pair of output columns
     const int c = ch0 + 2 * p;
     const bool cok = 2 * p < nch;
     const int cw = cok ? c : ch0;
+    // halo of v: unit = (position, 8 channels).  Every load of the thread is
+    // in flight before the first LDS write: unconditional loads from addresses
+    // clamped inside the tensor, the units outside the image or the channels
+    // zeroed afterwards.
+    constexpr int NU = HY * HX * (LP_TCH / 8), NIT = (NU + 255) / 256;
+    u32x4 hv[NIT];
+    uint32_t inside = 0;
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        const int u = min(tid + 256 * k, NU - 1);
+        const int part = u % (LP_TCH / 8), pos = u / (LP_TCH / 8);
+        const int hy = pos / HX, hx = pos % HX;
+        const int yy = y0 + hy - 2, xx = x0 + hx - 2;
+        if (yy >= 0 && yy < Y && xx >= 0 && xx < X && part * 8 < nch) inside |= 1u << k;
+        const int yc = min(max(yy, 0), Y - 1), xc = min(max(xx, 0), X - 1), pc = min(part * 8, nch - 8);
+        hv[k] = *reinterpret_cast<const u32x4*>(V + (img + (size_t)yc * X + xc) * C + ch0 + pc);
+    }
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+        const int u = tid + 256 * k;
+        const int part = u % (LP_TCH / 8), pos = u / (LP_TCH / 8);
+        const uint32_t m = (inside >> k) & 1u ? 0xffffffffu : 0u;
+        if (u < NU)
+            *reinterpret_cast<u32x4*>(&vt[pos * PAIRS + part * 4]) =
+                u32x4{hv[k][0] & m, hv[k][1] & m, hv[k][2] & m, hv[k][3] & m};
+    }
     float w0[25], w1[25];
 #pragma unroll
     for (int t = 0; t < 25; ++t) {
@@ -442,6 +458,17 @@ __global__ __launch_bounds__(256) void lepe_add_bf16(const uint16_t* __restrict_
         }
     }
     if (!cok) return;
+    // o's values at this thread's outputs, all requested before the first
+    // store (O is read and written, so loads written between the stores
+    // would each wait for the one before; addresses clamped inside the image)
+    uint32_t prev[LP_TY][2];
+#pragma unroll
+    for (int oy = 0; oy < LP_TY; ++oy)
+#pragma unroll
+        for (int ox = 0; ox < 2; ++ox) {
+            const int yy = min(y0 + oy, Y - 1), xx = min(x0 + 2 * xg + ox, X - 1);
+            prev[oy][ox] = *reinterpret_cast<const uint32_t*>(O + (img + (size_t)yy * X + xx) * C + c);
+        }
 #pragma unroll
     for (int oy = 0; oy < LP_TY; ++oy)
 #pragma unroll
@@ -449,8 +476,8 @@ __global__ __launch_bounds__(256) void lepe_add_bf16(const uint16_t* __restrict_
             const int yy = y0 + oy, xx = x0 + 2 * xg + ox;
             if (yy >= Y || xx >= X) continue;
             uint32_t* op = reinterpret_cast<uint32_t*>(O + (img + (size_t)yy * X + xx) * C + c);
-            const uint32_t prev = *op;
-            *op = pack_bf16(bf_lo(prev) + acc[oy][ox][0] + b0, bf_hi(prev) + acc[oy][ox][1] + b1);
+            const uint32_t pv = prev[oy][ox];
+            *op = pack_bf16(bf_lo(pv) + acc[oy][ox][0] + b0, bf_hi(pv) + acc[oy][ox][1] + b1);
         }
 }
 
