@@ -85,15 +85,24 @@ __device__ __forceinline__ void ln_stats_rows(const uint16_t* __restrict__ X, fl
     const int n = rg * 32 + (tid >> 3);
     const int nc = n < R ? n : R - 1;
     const uint16_t* xr = X + (size_t)nc * K;
-    const float x0 = bf_lo(*reinterpret_cast<const uint32_t*>(xr));
-    float s1 = 0.f, s2 = 0.f;
-    for (int k0 = 8 * part; k0 < K; k0 += 64) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(xr + k0);
+    float x0 = 0.f, s1 = 0.f, s2 = 0.f;
+    // eight 16-byte pieces of the row per lane in flight at once (addresses
+    // clamped inside the row, pieces past it skipped when summed)
+    for (int kb = 0; kb < K; kb += 512) {
+        u32x4 x[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float d0 = bf_lo(x[j]) - x0, d1 = bf_hi(x[j]) - x0;
-            s1 += d0 + d1;
-            s2 += d0 * d0 + d1 * d1;
+        for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const u32x4*>(xr + min(kb + 64 * u + 8 * part, K - 8));
+        // the row's first element, from the lane with part 0 (the row's lanes are consecutive)
+        if (kb == 0) x0 = __shfl(bf_lo(x[0][0]), (tid & 63) & ~7, 64);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool in = kb + 64 * u + 8 * part < K;   // K is a multiple of 8
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float d0 = in ? bf_lo(x[u][j]) - x0 : 0.f, d1 = in ? bf_hi(x[u][j]) - x0 : 0.f;
+                s1 += d0 + d1;
+                s2 += d0 * d0 + d1 * d1;
+            }
         }
     }
 #pragma unroll
