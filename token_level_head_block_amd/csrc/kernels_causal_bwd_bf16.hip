@@ -61,55 +61,71 @@ __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, int off) {
 
 constexpr int kRF = 0x00020000;   // buffer descriptor flags (raw buffer, 32-bit offsets)
 
-// Stages one tile of KT tokens (positions kt KT ..) of a chunk in LDS:
-//   rows[key][channel] from the rows source, phi applied if PHI_R;
-//   tr[channel][key]   from the transposed source, phi applied if PHI_T.
-// Tokens at or past T read as the chunk's last token, or as zeros where
-// ZERO_R / ZERO_T ask for it (per-token gradients that must not count).
-template <int D, int NW, bool PHI_R, bool ZERO_R, bool PHI_T, bool ZERO_T>
-__device__ __forceinline__ void stage_tile(uint16_t* __restrict__ rows, uint16_t* __restrict__ tr,
-                                           __amdgpu_buffer_rsrc_t rr, __amdgpu_buffer_rsrc_t rt, int kt, int T,
-                                           int rowb) {
-    constexpr int NT = 64 * NW, KT = 32 * NW;
-    constexpr int KSTR = D + 8, VSTR = KT + 8;
-    constexpr int KU = KT * D / 8 / NT;
-    constexpr int VU = (KT / 4 * (D / 8) + NT - 1) / NT;
+// One tile's global loads, held in registers: the rows source in 16-byte
+// pieces of token rows, the transposed source as 4 tokens x 8 channels per
+// unit.  Loading the next tile into them before the current one is
+// multiplied keeps its loads in flight during the MFMAs.
+template <int D, int NW>
+struct TileRegs {
+    static constexpr int NT = 64 * NW, KT = 32 * NW;
+    static constexpr int KU = KT * D / 8 / NT;
+    static constexpr int VU = (KT / 4 * (D / 8) + NT - 1) / NT;
+    u32x4 kx[KU], vx[VU][4];
+};
+
+// Tokens at or past T read as the chunk's last token.
+template <int D, int NW>
+__device__ __forceinline__ void load_tile(TileRegs<D, NW>& R, __amdgpu_buffer_rsrc_t rr, __amdgpu_buffer_rsrc_t rt,
+                                          int kt, int T, int rowb) {
+    using TR = TileRegs<D, NW>;
     const int tid = threadIdx.x;
     auto tok = [&](int p) { return (p < T ? p : T - 1) * rowb; };
-    u32x4 kx[KU], vx[VU][4];
 #pragma unroll
-    for (int s = 0; s < KU; ++s) {
-        const int u = tid + NT * s;
-        kx[s] = ld16(rr, tok(kt * KT + u / (D / 8)) + (u % (D / 8)) * 16);
+    for (int s = 0; s < TR::KU; ++s) {
+        const int u = tid + TR::NT * s;
+        R.kx[s] = ld16(rr, tok(kt * TR::KT + u / (D / 8)) + (u % (D / 8)) * 16);
     }
 #pragma unroll
-    for (int s = 0; s < VU; ++s) {
-        const int u = tid + NT * s;
+    for (int s = 0; s < TR::VU; ++s) {
+        const int u = tid + TR::NT * s;
         const int kq = u / (D / 8), c8 = u % (D / 8);
-        if (u < KT / 4 * (D / 8)) {
+        if (u < TR::KT / 4 * (D / 8)) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vx[s][j] = ld16(rt, tok(kt * KT + 4 * kq + j) + c8 * 16);
+            for (int j = 0; j < 4; ++j) R.vx[s][j] = ld16(rt, tok(kt * TR::KT + 4 * kq + j) + c8 * 16);
         }
     }
+}
+
+// Writes a loaded tile of KT tokens (positions kt KT ..) of a chunk to LDS:
+//   rows[key][channel] from the rows source, phi applied if PHI_R;
+//   tr[channel][key]   from the transposed source, phi applied if PHI_T;
+// tokens past T as zeros where ZERO_R / ZERO_T ask for it (per-token
+// gradients that must not count).
+template <int D, int NW, bool PHI_R, bool ZERO_R, bool PHI_T, bool ZERO_T>
+__device__ __forceinline__ void store_tile(uint16_t* __restrict__ rows, uint16_t* __restrict__ tr,
+                                           const TileRegs<D, NW>& R, int kt, int T) {
+    using TR = TileRegs<D, NW>;
+    constexpr int KSTR = D + 8, VSTR = TR::KT + 8;
+    const int tid = threadIdx.x;
     const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int s = 0; s < KU; ++s) {
-        const int u = tid + NT * s;
+    for (int s = 0; s < TR::KU; ++s) {
+        const int u = tid + TR::NT * s;
         const int key = u / (D / 8);
-        u32x4 y = PHI_R ? phi_words(kx[s]) : kx[s];
-        if (ZERO_R && kt * KT + key >= T) y = zero;
+        u32x4 y = PHI_R ? phi_words(R.kx[s]) : R.kx[s];
+        if (ZERO_R && kt * TR::KT + key >= T) y = zero;
         *reinterpret_cast<u32x4*>(rows + key * KSTR + (u % (D / 8)) * 8) = y;
     }
 #pragma unroll
-    for (int s = 0; s < VU; ++s) {
-        const int u = tid + NT * s;
+    for (int s = 0; s < TR::VU; ++s) {
+        const int u = tid + TR::NT * s;
         const int kq = u / (D / 8), c8 = u % (D / 8);
-        if (u < KT / 4 * (D / 8)) {
+        if (u < TR::KT / 4 * (D / 8)) {
             u32x4 y[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                y[j] = PHI_T ? phi_words(vx[s][j]) : vx[s][j];
-                if (ZERO_T && kt * KT + 4 * kq + j >= T) y[j] = zero;
+                y[j] = PHI_T ? phi_words(R.vx[s][j]) : R.vx[s][j];
+                if (ZERO_T && kt * TR::KT + 4 * kq + j >= T) y[j] = zero;
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -119,6 +135,16 @@ __device__ __forceinline__ void stage_tile(uint16_t* __restrict__ rows, uint16_t
             }
         }
     }
+}
+
+// Loads and writes one tile (store_tile's layouts).
+template <int D, int NW, bool PHI_R, bool ZERO_R, bool PHI_T, bool ZERO_T>
+__device__ __forceinline__ void stage_tile(uint16_t* __restrict__ rows, uint16_t* __restrict__ tr,
+                                           __amdgpu_buffer_rsrc_t rr, __amdgpu_buffer_rsrc_t rt, int kt, int T,
+                                           int rowb) {
+    TileRegs<D, NW> R;
+    load_tile<D, NW>(R, rr, rt, kt, T, rowb);
+    store_tile<D, NW, PHI_R, ZERO_R, PHI_T, ZERO_T>(rows, tr, R, kt, T);
 }
 
 // A d x d record stored as [e][c] (element (c, e) at e d + c) -> LDS as
@@ -662,15 +688,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
         __builtin_amdgcn_make_buffer_rsrc((void*)(dS + (size_t)blk * (D * D)), 0, D * D * 2, kRF);
     const __amdgpu_buffer_rsrc_t rdz = __builtin_amdgcn_make_buffer_rsrc((void*)(dZ + (size_t)blk * D), 0, D * 4, kRF);
     auto tok = [&](int p) { return (p < T ? p : T - 1) * rowb; };
-    // 1 / den and dden of query tile qt into LDS (zeros past the chunk)
-    auto stage_scalars = [&](int qt) {
-        for (int x = tid; x < KT; x += NT) {
-            const int p = qt * KT + x;
-            const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rts, (p < T ? p : 0) * g.H * 8, 0, 0));
-            ivl[x] = p < T ? __uint_as_float(t[0]) : 0.f;
-            ddl[x] = p < T ? __uint_as_float(t[1]) : 0.f;
+    // 1 / den and dden of query tile qt (thread x < KT takes token x; zeros
+    // past the chunk), loaded with the tile and written to LDS with it
+    auto load_scalars = [&](int qt, u32x2& t) {
+        const int p = qt * KT + tid;
+        if (tid < KT)
+            t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rts, (p < T ? p : 0) * g.H * 8, 0, 0));
+    };
+    auto store_scalars = [&](int qt, const u32x2& t) {
+        const int p = qt * KT + tid;
+        if (tid < KT) {
+            ivl[tid] = p < T ? __uint_as_float(t[0]) : 0.f;
+            ddl[tid] = p < T ? __uint_as_float(t[1]) : 0.f;
         }
     };
+    // The stages run in the order (key tile kt: pass 1 over query tiles kt..,
+    // then pass 2 over the same); each stage's loads are issued while the
+    // stage before it is multiplied.  Pass 1 stages phi(Q) rows and g^T,
+    // pass 2 g rows and phi(Q)^T: the same tokens, other layouts.
+    TileRegs<D, NW> tr;
+    u32x2 tsr = u32x2{0u, 0u};
+    load_tile<D, NW>(tr, rq, rg, 0, T, rowb);
+    load_scalars(0, tsr);
 
     const int nit = (T + 15) >> 4;
     const int nqt = (T + KT - 1) / KT;
@@ -691,10 +730,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
         // ---- pass 1: dv
         for (int qt = kt; qt < nqt; ++qt) {
             __syncthreads();
-            stage_tile<D, NW, true, false, false, true>(kl, vl, rq, rg, qt, T, rowb);
-            stage_scalars(qt);
+            store_tile<D, NW, true, false, false, true>(kl, vl, tr, qt, T);
+            store_scalars(qt, tsr);
             if (kt == 0 && qt == 0) stage_transposed_record<D, NT>(gxt, rds);
             __syncthreads();
+            // next stage: this pass's next query tile, else pass 2's first
+            if (qt + 1 < nqt) {
+                load_tile<D, NW>(tr, rq, rg, qt + 1, T, rowb);
+                load_scalars(qt + 1, tsr);
+            } else {
+                load_tile<D, NW>(tr, rg, rq, kt, T, rowb);
+                load_scalars(kt, tsr);
+            }
             // local query groups [lq0, nlq) that either key group needs
             const int lq0 = qt == kt ? w : 0;
             const int nlq = min(NKG, nit - qt * NKG);
@@ -755,9 +802,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
         for (int r = 0; r < RT; ++r) acca[r] = accb[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int qt = kt; qt < nqt; ++qt) {
             __syncthreads();
-            stage_tile<D, NW, false, true, true, false>(kl, vl, rg, rq, qt, T, rowb);
-            stage_scalars(qt);
+            store_tile<D, NW, false, true, true, false>(kl, vl, tr, qt, T);
+            store_scalars(qt, tsr);
             __syncthreads();
+            // next stage: this pass's next query tile, else pass 1 of the next key tile
+            if (qt + 1 < nqt) {
+                load_tile<D, NW>(tr, rg, rq, qt + 1, T, rowb);
+                load_scalars(qt + 1, tsr);
+            } else if (kt + 1 < nqt) {
+                load_tile<D, NW>(tr, rq, rg, kt + 1, T, rowb);
+                load_scalars(kt + 1, tsr);
+            }
             const int lq0 = qt == kt ? w : 0;
             const int nlq = min(NKG, nit - qt * NKG);
             for (int lq = va ? lq0 : nlq; lq < nlq; ++lq) {
