@@ -44,7 +44,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4))) vo
     constexpr int KT = 32 * NW;        // tokens per query tile and per key tile
     constexpr int NKG = KT / 16;       // 16-key groups per key tile
     constexpr int KSTR = D + 8;        // row stride of phi(K) and St in LDS (bf16)
-    constexpr int VSTR = KT + 8;       // V^T row stride in LDS (bf16)
+    constexpr int VSTR = KT + 4;       // V^T row stride in LDS (bf16): 264 bytes at KT = 128, rows 8 bytes apart in the banks
     constexpr int KU = KT * D / 8 / NT;                 // phi(K) units (key, 8 channels) per thread
     constexpr int VU = (KT / 4 * (D / 8) + NT - 1) / NT;   // V^T units (4 keys, 8 channels) per thread
     constexpr int SU = (D * D / 8 + NT - 1) / NT;          // St units (row, 8 channels) per thread

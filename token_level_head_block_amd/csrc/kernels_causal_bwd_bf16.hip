@@ -98,14 +98,16 @@ __device__ __forceinline__ void load_tile(TileRegs<D, NW>& R, __amdgpu_buffer_rs
 
 // Writes a loaded tile of KT tokens (positions kt KT ..) of a chunk to LDS:
 //   rows[key][channel] from the rows source, phi applied if PHI_R;
-//   tr[channel][key]   from the transposed source, phi applied if PHI_T;
+//   tr[channel][key]   from the transposed source, phi applied if PHI_T (row
+//     stride KT + 4: the 8-byte pieces that the writes and the operand reads
+//     touch fall on fewer common banks than with KT + 8);
 // tokens past T as zeros where ZERO_R / ZERO_T ask for it (per-token
 // gradients that must not count).
 template <int D, int NW, bool PHI_R, bool ZERO_R, bool PHI_T, bool ZERO_T>
 __device__ __forceinline__ void store_tile(uint16_t* __restrict__ rows, uint16_t* __restrict__ tr,
                                            const TileRegs<D, NW>& R, int kt, int T) {
     using TR = TileRegs<D, NW>;
-    constexpr int KSTR = D + 8, VSTR = TR::KT + 8;
+    constexpr int KSTR = D + 8, VSTR = TR::KT + 4;
     const int tid = threadIdx.x;
     const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     float* __restrict__ diag, const Geo g) {
     constexpr int RT = D / 16, KS = D / 32, REC = D * D + D;
     constexpr int NT = 64 * NW, KT = 32 * NW, NKG = KT / 16;
-    constexpr int KSTR = D + 8, VSTR = KT + 8;
+    constexpr int KSTR = D + 8, VSTR = KT + 4;
     constexpr int STAGE_B = (KT * KSTR + D * VSTR) * 2;
     constexpr int SLOT = RT * RT * 4 * 64;   // floats of one wave's dSt partial
     constexpr int RED_B = ((NW / 2) * SLOT + NW * D) * 4;
@@ -654,7 +656,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     }
     constexpr int RT = D / 16, KS = D / 32;
     constexpr int NT = 64 * NW, KT = 32 * NW, NKG = KT / 16;
-    constexpr int KSTR = D + 8, VSTR = KT + 8;
+    constexpr int KSTR = D + 8, VSTR = KT + 4;
     __shared__ __attribute__((aligned(16))) uint16_t kl[KT * KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t vl[D * VSTR];
     __shared__ __attribute__((aligned(16))) uint16_t gxt[D * KSTR];   // Gx_i as [c][e]
