@@ -431,14 +431,25 @@ __global__ __launch_bounds__(256) void lepe_add_bf16(const uint16_t* __restrict_
             *reinterpret_cast<u32x4*>(&vt[pos * PAIRS + part * 4]) =
                 u32x4{hv[k][0] & m, hv[k][1] & m, hv[k][2] & m, hv[k][3] & m};
     }
-    float w0[25], w1[25];
+    // Weights as bf16 pairs per tap row dy: (w0, w1), (w2, w3), (w4, 0), (0, w4),
+    // for v_dot2_f32_bf16 (two products of bf16 values, exact in fp32, added
+    // to an fp32 accumulator): three per output row instead of five FMAs.
+    uint32_t wq[2][5][4];
 #pragma unroll
-    for (int t = 0; t < 25; ++t) {
-        w0[t] = w[(size_t)cw * 25 + t];
-        w1[t] = w[(size_t)(cw + 1) * 25 + t];
-    }
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int dy = 0; dy < 5; ++dy) {
+            const float* wr = w + (size_t)(cw + ch) * 25 + dy * 5;
+            wq[ch][dy][0] = pack_bf16(wr[0], wr[1]);
+            wq[ch][dy][1] = pack_bf16(wr[2], wr[3]);
+            wq[ch][dy][2] = pack_bf16(wr[4], 0.f);
+            wq[ch][dy][3] = pack_bf16(0.f, wr[4]);
+        }
     const float b0 = bias ? bias[cw] : 0.f, b1 = bias ? bias[cw + 1] : 0.f;
     __syncthreads();
+    auto dot2 = [](uint32_t a, uint32_t b, float c) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+    };
     float acc[LP_TY][2][2];
 #pragma unroll
     for (int oy = 0; oy < LP_TY; ++oy)
@@ -446,24 +457,33 @@ __global__ __launch_bounds__(256) void lepe_add_bf16(const uint16_t* __restrict_
         for (int ox = 0; ox < 2; ++ox) acc[oy][ox][0] = acc[oy][ox][1] = 0.f;
 #pragma unroll
     for (int iy = 0; iy < HY; ++iy) {
-        float in0[6], in1[6];
+        // the window's six columns hold channel pairs (c, c + 1); q[ch][s] pairs
+        // columns s and s + 1 of one channel
+        uint32_t r[6], q[2][5];
 #pragma unroll
-        for (int s = 0; s < 6; ++s) {
-            const uint32_t pr = vt[(iy * HX + 2 * xg + s) * PAIRS + p];
-            in0[s] = bf_lo(pr);
-            in1[s] = bf_hi(pr);
+        for (int s = 0; s < 6; ++s) r[s] = vt[(iy * HX + 2 * xg + s) * PAIRS + p];
+#pragma unroll
+        for (int s = 0; s < 5; ++s) {
+            q[0][s] = pack_lo(r[s], r[s + 1]);
+            q[1][s] = pack_hi(r[s], r[s + 1]);
         }
 #pragma unroll
         for (int dy = 0; dy < 5; ++dy) {
             const int oy = iy - dy;
             if (oy < 0 || oy >= LP_TY) continue;
 #pragma unroll
-            for (int ox = 0; ox < 2; ++ox)
-#pragma unroll
-                for (int dx = 0; dx < 5; ++dx) {
-                    acc[oy][ox][0] += w0[dy * 5 + dx] * in0[ox + dx];
-                    acc[oy][ox][1] += w1[dy * 5 + dx] * in1[ox + dx];
-                }
+            for (int ch = 0; ch < 2; ++ch) {
+                // column 0 of the pair: taps on columns 0..4; column 1: on columns 1..5
+                float a0 = acc[oy][0][ch], a1 = acc[oy][1][ch];
+                a0 = dot2(q[ch][0], wq[ch][dy][0], a0);
+                a0 = dot2(q[ch][2], wq[ch][dy][1], a0);
+                a0 = dot2(q[ch][4], wq[ch][dy][2], a0);
+                a1 = dot2(q[ch][1], wq[ch][dy][0], a1);
+                a1 = dot2(q[ch][3], wq[ch][dy][1], a1);
+                a1 = dot2(q[ch][4], wq[ch][dy][3], a1);
+                acc[oy][0][ch] = a0;
+                acc[oy][1][ch] = a1;
+            }
         }
     }
     if (!cok) return;
