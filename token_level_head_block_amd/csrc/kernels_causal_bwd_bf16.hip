@@ -42,6 +42,20 @@ __device__ __forceinline__ constexpr int och(int r, int rho) {
     return (r >> 1) * 32 + 8 * (rho >> 2) + 4 * (r & 1) + (rho & 3);
 }
 
+// XOR swizzle of the 8-byte pieces (4 tokens) in a row of a transposed tile:
+// piece p of row c sits at p ^ tsw(c).  The staging writes (eight lanes on
+// rows 8 apart) then fall on different banks, and the operand reads (rows
+// och(r, li)) keep their spread.
+__device__ __forceinline__ constexpr int tsw(int row) { return (row >> 3) & 7; }
+
+// Element offset in a transposed tile of the operand piece 4 k + gq of row
+// och(r, li) (k: 16-token group).  With d <= 64, tsw(och(r, li)) is
+// 4 (r / 2) + li / 4, so the swizzle splits into a per-lane part and
+// k ^ (r / 2).
+__device__ __forceinline__ int tr_piece(int r, int li, int gq, int k, int vstr) {
+    return och(r, li) * vstr + 4 * (gq ^ (li >> 2)) + 16 * (k ^ (r >> 1));
+}
+
 __device__ __forceinline__ u32x4 phi_words(const u32x4& x) {
     u32x4 y;
 #pragma unroll
@@ -99,8 +113,8 @@ __device__ __forceinline__ void load_tile(TileRegs<D, NW>& R, __amdgpu_buffer_rs
 // Writes a loaded tile of KT tokens (positions kt KT ..) of a chunk to LDS:
 //   rows[key][channel] from the rows source, phi applied if PHI_R;
 //   tr[channel][key]   from the transposed source, phi applied if PHI_T (row
-//     stride KT + 4: the 8-byte pieces that the writes and the operand reads
-//     touch fall on fewer common banks than with KT + 8);
+//     stride KT + 4 and the pieces swizzled by tsw: the writes and the
+//     operand reads share fewer banks);
 // tokens past T as zeros where ZERO_R / ZERO_T ask for it (per-token
 // gradients that must not count).
 template <int D, int NW, bool PHI_R, bool ZERO_R, bool PHI_T, bool ZERO_T>
@@ -131,7 +145,8 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ rows, uint16_t
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                uint16_t* d0 = tr + (c8 * 8 + 2 * j) * VSTR + 4 * kq;
+                const int row = c8 * 8 + 2 * j;   // rows row and row + 1 share tsw
+                uint16_t* d0 = tr + row * VSTR + 4 * (kq ^ tsw(row));
                 *reinterpret_cast<u32x2*>(d0) = u32x2{pack_lo(y[0][j], y[1][j]), pack_lo(y[2][j], y[3][j])};
                 *reinterpret_cast<u32x2*>(d0 + VSTR) = u32x2{pack_hi(y[0][j], y[1][j]), pack_hi(y[2][j], y[3][j])};
             }
@@ -203,6 +218,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     constexpr int RT = D / 16, KS = D / 32, REC = D * D + D;
     constexpr int NT = 64 * NW, KT = 32 * NW, NKG = KT / 16;
     constexpr int KSTR = D + 8, VSTR = KT + 4;
+    static_assert(D <= 64, "tr_piece assumes at most four row tiles");
     constexpr int STAGE_B = (KT * KSTR + D * VSTR) * 2;
     constexpr int SLOT = RT * RT * 4 * 64;   // floats of one wave's dSt partial
     constexpr int RED_B = ((NW / 2) * SLOT + NW * D) * 4;
@@ -296,7 +312,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
                     ak[kk] = *reinterpret_cast<const u32x4*>(kl + (16 * kg + li) * KSTR + kk * 32 + gq * 8);
 #pragma unroll
                 for (int r = 0; r < RT; ++r)
-                    av[r] = *reinterpret_cast<const u32x2*>(vl + och(r, li) * VSTR + 16 * kg + 4 * gq);
+                    av[r] = *reinterpret_cast<const u32x2*>(vl + tr_piece(r, li, gq, kg, VSTR));
                 const int kgg = kt * NKG + kg;
                 auto step = [&](const u32x4* bq, f32x4* acc, f32x4& ps, bool dg) {
                     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -432,7 +448,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
                     avr[kk] = *reinterpret_cast<const u32x4*>(kl + (16 * kg + li) * KSTR + kk * 32 + gq * 8);
 #pragma unroll
                 for (int r = 0; r < RT; ++r)
-                    akt[r] = *reinterpret_cast<const u32x2*>(vl + och(r, li) * VSTR + 16 * kg + 4 * gq);
+                    akt[r] = *reinterpret_cast<const u32x2*>(vl + tr_piece(r, li, gq, kg, VSTR));
                 const int kgg = kt * NKG + kg;
                 auto step = [&](const Grad& G, f32x4* du, bool dg) {
                     f32x4 xs = f32x4{0.f, 0.f, 0.f, 0.f};   // v . g
@@ -657,6 +673,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
     constexpr int RT = D / 16, KS = D / 32;
     constexpr int NT = 64 * NW, KT = 32 * NW, NKG = KT / 16;
     constexpr int KSTR = D + 8, VSTR = KT + 4;
+    static_assert(D <= 64, "tr_piece assumes at most four row tiles");
     __shared__ __attribute__((aligned(16))) uint16_t kl[KT * KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t vl[D * VSTR];
     __shared__ __attribute__((aligned(16))) uint16_t gxt[D * KSTR];   // Gx_i as [c][e]
@@ -755,7 +772,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
                     aq[kk] = *reinterpret_cast<const u32x4*>(kl + (16 * lq + li) * KSTR + kk * 32 + gq * 8);
 #pragma unroll
                 for (int r = 0; r < RT; ++r)
-                    adn[r] = *reinterpret_cast<const u32x2*>(vl + och(r, li) * VSTR + 16 * lq + 4 * gq);
+                    adn[r] = *reinterpret_cast<const u32x2*>(vl + tr_piece(r, li, gq, lq, VSTR));
                 const f32x4 iv = *reinterpret_cast<const f32x4*>(ivl + 16 * lq + 4 * gq);
                 const int qg = qt * NKG + lq;
                 auto step = [&](const u32x4* bk, f32x4* acc, bool dg) {
@@ -825,7 +842,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW == 1
                     adn[kk] = *reinterpret_cast<const u32x4*>(kl + (16 * lq + li) * KSTR + kk * 32 + gq * 8);
 #pragma unroll
                 for (int r = 0; r < RT; ++r)
-                    au[r] = *reinterpret_cast<const u32x2*>(vl + och(r, li) * VSTR + 16 * lq + 4 * gq);
+                    au[r] = *reinterpret_cast<const u32x2*>(vl + tr_piece(r, li, gq, lq, VSTR));
                 const f32x4 dd = *reinterpret_cast<const f32x4*>(ddl + 16 * lq + 4 * gq);
                 const f32x4 iv = *reinterpret_cast<const f32x4*>(ivl + 16 * lq + 4 * gq);
                 const int qg = qt * NKG + lq;
