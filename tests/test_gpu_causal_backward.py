@@ -39,6 +39,9 @@ CASES = [
     # long chunks on the matrix-core path (129 chunks: no sub-chunks): five
     # 128-token query tiles per chunk, the last one ragged
     ("cbwd-d32-T520-M129", 1, 1, 32, (1, 129 * 520), (1, 520), BF, "gaussian"),
+    # 144 chunks of one pair: the transposed mixing and a single dW split in one launch
+    ("cbwd-d32-M144-one-split", 1, 1, 32, (1, 144 * 8), (1, 8), BF, "gaussian"),
+    ("cbwd-d64-M144-T16", 1, 1, 64, (1, 144 * 16), (1, 16), BF, "gaussian"),
     ("cbwd-f32-d32-T16", 1, 2, 32, (1, 256), (1, 16), F32, "local"),
     ("cbwd-f32-d64-T100", 2, 1, 64, (1, 400), (1, 100), F32, "local"),
     ("cbwd-f32-d128-T33", 1, 1, 128, (1, 99), (1, 33), F32, "local"),
