@@ -38,6 +38,8 @@ SMALL = [
     ("bwd-d64-B2-M196", 2, 3, 64, (56, 56), (4, 4), 1.0),
     # one pair, 144 blocks: the dW product runs as a single split beside the mixing
     ("bwd-d32-M144-one-split", 1, 1, 32, (48, 48), (4, 4), 1.0),
+    # 64 pairs x 17 column tiles: two column tiles per mixing workgroup, the last one alone
+    ("bwd-d32-H64-M144-two-tiles", 1, 64, 32, (48, 48), (4, 4), 1.0),
     # few blocks of many tokens: the key/value side runs in token parts
     ("bwd-d64-M4-parts", 1, 2, 64, (32, 32), (16, 16), 1.0),
     ("bwd-d32-M4-parts", 1, 4, 32, (32, 48), (16, 24), 1.0),

@@ -22,6 +22,7 @@
 
 #include <mhla.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace mhla {
@@ -849,7 +850,8 @@ __global__ __launch_bounds__(512) void dw_partial_bf16(const uint16_t* __restric
 template <int D, int NT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void mix_dw_bf16(
     const uint16_t* __restrict__ dSt, const uint16_t* __restrict__ SZ, float* __restrict__ part, int nsplit, int ntj,
-    int ndw, const uint16_t* __restrict__ Wb, uint16_t* __restrict__ dS, float* __restrict__ dZ, const Geo g, int CT) {
+    int ndw, const uint16_t* __restrict__ Wb, uint16_t* __restrict__ dS, float* __restrict__ dZ, const Geo g, int CT,
+    int CW) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[DW_LDS_BYTES / 2];
     const int id = blockIdx.x;
     if (id < ndw) {
@@ -858,14 +860,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
     }
     constexpr int REC = D * D + D, KMAX = 8, OROW = MIX_OROW, ROWS = 32;
     u32x4* sA = reinterpret_cast<u32x4*>(lds);   // [r][kk][lane] operands, 32 KB; then output staging
-    const int c = id - ndw;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, gq = lane >> 4;
-    const int bh = c / CT, cp0 = (c - bh * CT) * 64;
+    // this workgroup: column tiles ct0 .. ct0 + CW - 1 (those below CT) of pair bh
+    const int CTP = (CT + CW - 1) / CW, c = id - ndw;
+    const int bh = c / CTP, ct0 = (c - bh * CTP) * CW;
     const int M = g.M, NK = (M + 31) >> 5;
     const int i0 = wave * ROWS;
     const bool active = i0 < M;                  // then i0 + 32 <= roundup(M, 32): inside Wb's rows
     const int rt0 = active ? i0 >> 4 : 0;
+    // W operands, loaded once for the workgroup's column tiles
     u32x4 bw[KMAX][2];
 #pragma unroll
     for (int kk = 0; kk < KMAX; ++kk)
@@ -873,15 +877,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
         for (int t = 0; t < 2; ++t)
             bw[kk][t] = *reinterpret_cast<const u32x4*>(
                 Wb + ((size_t)((rt0 + t) * NK + (kk < NK ? kk : NK - 1)) * 64 + lane) * 8);
-    // stage A: unit (li', group of 8 source records) -> 4 packed operands, one per thread
+    // staging of a column tile: unit (li', group of 8 source records) -> 4 packed operands, one per thread
     const int units = 16 * 4 * NK;
     const uint16_t* base = dSt + (size_t)bh * M * REC;
-    {
+    auto load_raw = [&](int cp0, u32x2* raw) {
         const int u = tid;
         const int colp = cp0 + 4 * (u & 15);
         const bool ok = u < units && colp < REC;
         const int colc = ok ? colp : 0;
-        u32x2 raw[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int jj = 8 * (u >> 4) + s;
@@ -889,6 +892,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
             const uint32_t m = (ok && jj < M) ? 0xffffffffu : 0u;
             raw[s] = u32x2{t.x & m, t.y & m};
         }
+    };
+    auto store_op = [&](const u32x2* raw) {
+        const int u = tid;
         if (u < units) {
             const int jg = u >> 4, kk = jg >> 2, lanep = (jg & 3) * 16 + (u & 15);
             u32x4 op[4];
@@ -902,61 +908,72 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void m
 #pragma unroll
             for (int r = 0; r < 4; ++r) sA[(r * NK + kk) * 64 + lanep] = op[r];
         }
-    }
-    __syncthreads();
-    f32x4 acc[4][2];
+    };
+    u32x2 raw[8];
+    load_raw(ct0 * 64, raw);
+    for (int q = 0; q < CW; ++q) {
+        const int ct = ct0 + q;
+        if (ct >= CT) break;                     // the same for the whole workgroup
+        const int cp0 = ct * 64;
+        if (q > 0) __syncthreads();              // the last tile's output staging (over sA) is done
+        store_op(raw);
+        if (q + 1 < CW && ct + 1 < CT) load_raw(cp0 + 64, raw);   // the next tile's records in flight
+        __syncthreads();
+        f32x4 acc[4][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r][0] = acc[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (active) {
+        for (int r = 0; r < 4; ++r) acc[r][0] = acc[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (active) {
 #pragma unroll
-        for (int kk = 0; kk < KMAX; ++kk) {
-            if (kk >= NK) break;
-            u32x4 a[4];
+            for (int kk = 0; kk < KMAX; ++kk) {
+                if (kk >= NK) break;
+                u32x4 a[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = sA[(r * NK + kk) * 64 + lane];
+                for (int r = 0; r < 4; ++r) a[r] = sA[(r * NK + kk) * 64 + lane];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int t = 0; t < 2; ++t) acc[r][t] = mfma_bf16(a[r], bw[kk][t], acc[r][t]);
-        }
-    }
-    __syncthreads();   // every wave is done with the A operands
-    if (!active) return;
-    // Lane holds C[col' = cp0 + 16*gq + 4*v + r][i = i0 + 16*t + li].
-    if (cp0 < D * D) {
-        uint16_t* stage = lds + wave * (ROWS * OROW);   // this wave's slice only
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            uint32_t wv[8];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                wv[2 * v] = pack_bf16(acc[0][t][v], acc[1][t][v]);
-                wv[2 * v + 1] = pack_bf16(acc[2][t][v], acc[3][t][v]);
-            }
-            uint16_t* dst = stage + (16 * t + li) * OROW + 16 * gq;
-            *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
-        }
-#pragma unroll
-        for (int k = 0; k < ROWS / 8; ++k) {
-            const int rl = 8 * k + (lane >> 3), chunk = lane & 7;
-            const int i = i0 + rl;
-            const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rl * OROW + chunk * 8);
-            u32x4* dst = reinterpret_cast<u32x4*>(dS + ((size_t)bh * M + i) * (D * D) + cp0 + chunk * 8);
-            if (i < M) {
-                if constexpr ((NT & 2) != 0) __builtin_nontemporal_store(x, dst);
-                else *dst = x;
+                    for (int t = 0; t < 2; ++t) acc[r][t] = mfma_bf16(a[r], bw[kk][t], acc[r][t]);
             }
         }
-    } else if (cp0 + 16 * gq < REC) {
+        __syncthreads();   // every wave is done with the A operands
+        if (!active) continue;
+        // Lane holds C[col' = cp0 + 16*gq + 4*v + r][i = i0 + 16*t + li].
+        if (cp0 < D * D) {
+            uint16_t* stage = lds + wave * (ROWS * OROW);   // this wave's slice only
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int i = i0 + 16 * t + li;
-            if (i >= M) continue;
-            float* dst = dZ + ((size_t)bh * M + i) * D + (cp0 + 16 * gq - D * D);
+            for (int t = 0; t < 2; ++t) {
+                uint32_t wv[8];
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                *reinterpret_cast<f32x4*>(dst + 4 * v) = f32x4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
+                for (int v = 0; v < 4; ++v) {
+                    wv[2 * v] = pack_bf16(acc[0][t][v], acc[1][t][v]);
+                    wv[2 * v + 1] = pack_bf16(acc[2][t][v], acc[3][t][v]);
+                }
+                uint16_t* dst = stage + (16 * t + li) * OROW + 16 * gq;
+                *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+                *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+            }
+#pragma unroll
+            for (int k = 0; k < ROWS / 8; ++k) {
+                const int rl = 8 * k + (lane >> 3), chunk = lane & 7;
+                const int i = i0 + rl;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(stage + rl * OROW + chunk * 8);
+                u32x4* dst = reinterpret_cast<u32x4*>(dS + ((size_t)bh * M + i) * (D * D) + cp0 + chunk * 8);
+                if (i < M) {
+                    if constexpr ((NT & 2) != 0) __builtin_nontemporal_store(x, dst);
+                    else *dst = x;
+                }
+            }
+        } else if (cp0 + 16 * gq < REC) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int i = i0 + 16 * t + li;
+                if (i >= M) continue;
+                float* dst = dZ + ((size_t)bh * M + i) * D + (cp0 + 16 * gq - D * D);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    *reinterpret_cast<f32x4*>(dst + 4 * v) =
+                        f32x4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
+            }
         }
     }
 }
@@ -1111,13 +1128,18 @@ hipError_t launch_mix_dw_bf16(const BwdLaunch& B, const Geo& g, const uint16_t* 
         auto go = [&](auto d) {
             constexpr int D = decltype(d)::value;
             const int CT = (D * D + D + 63) / 64, ndw = B.nsplit * ntj * ntj;
-            const int grid = ndw + g.BH * CT;
+            // Column tiles per mixing workgroup, which loads its W operands once for
+            // them: with many tiles, fewer and longer workgroups (sana-128x128,
+            // 2380 tiles: 1, 2, 3, 4, 6, 9 per workgroup 117.7, 116.0, 113.0,
+            // 111.9, 115.3, 125.7 us for the stage); dit-s2-256x256's 396 the same.
+            const int CW = std::max(1, std::min(4, g.BH * CT / 512));
+            const int grid = ndw + g.BH * ((CT + CW - 1) / CW);
             if (L.tune.nt_mix & 2)
                 mix_dw_bf16<D, 2><<<grid, 512, 0, L.stream>>>(B.dst, srec, B.part, B.nsplit, ntj, ndw, B.wbt, B.ds,
-                                                               B.dz, g, CT);
+                                                               B.dz, g, CT, CW);
             else
                 mix_dw_bf16<D, 0><<<grid, 512, 0, L.stream>>>(B.dst, srec, B.part, B.nsplit, ntj, ndw, B.wbt, B.ds,
-                                                               B.dz, g, CT);
+                                                               B.dz, g, CT, CW);
         };
         switch (g.D) {
             case 32: go(std::integral_constant<int, 32>{}); break;
