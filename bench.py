@@ -774,6 +774,11 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if p.dtype == synth.BF16 else "f32", "data": "synthetic",
+        "precision": (("q, k, v, out bf16; summaries [S|z] as bf16 records; fp32 accumulation; W (fp32 input) "
+                       + {"causal": "as bf16 high and low parts in the mixing, mixed S bf16 and z fp32",
+                          "fused": "applied in fp32 inside the apply, mixed S staged as bf16"}.get(
+                           args.path, "rounded to bf16 for the mixing product, mixed S bf16 and z fp32"))
+                      if p.dtype == synth.BF16 else "fp32 throughout"),
         "config": {"workload": f"{p.name}: B={p.batch} H={p.heads} d={p.head_dim} grid={list(p.grid)} "
                                f"blocks={list(p.block)} N={p.n_tokens} M={p.n_blocks}",
                    "path": args.path, "w": args.w, "input_sets": sets, "parallelism": "none (1 GPU)"},
