@@ -34,6 +34,10 @@ SMALL = [
     ("bf-d128-T200", 1, 1, 128, (20, 40), (10, 20), BF, 1.0),
     ("bf-d128-H3-full", 2, 3, 128, (16, 32), (8, 8), BF, 1.0),   # odd head count: a half-empty head group
     ("bf-d128-row8", 1, 2, 128, (24, 16), (3, 8), BF, 1.0),     # rows of 8 tokens, T = 24: ragged last step
+    # blocks of at most 64 tokens: summaries of four, two or one block per wave
+    ("bf-d64-T64-M10-two-blocks", 1, 3, 64, (40, 16), (8, 8), BF, 1.0),
+    ("bf-d64-T64-M5-one-block", 1, 2, 64, (40, 8), (8, 8), BF, 1.0),
+    ("bf-d32-T32-M12-pairs", 2, 4, 32, (16, 24), (4, 8), BF, 1.0),
     ("f32-d32-T15", 1, 2, 32, (12, 20), (3, 5), F, 1.0),
     ("f32-d64-3d", 2, 1, 64, (8, 16, 8), (2, 4, 4), F, 1.0),
     ("f32-d128", 1, 2, 128, (16, 16), (4, 8), F, 1.0),

@@ -19,6 +19,8 @@
 // Output layout of a 16x16 MFMA tile (f32x4 per lane): lane l holds rows
 // 4*(l/16) + v, v = 0..3, of column l % 16.
 #include "launch.h"
+
+#include <type_traits>
 #include "bf16_shared.h"
 
 #include <mhla.h>
@@ -45,13 +47,18 @@ namespace {
 // whose two diagonal 32 x 32 blocks are the two heads' S (the off-diagonal
 // blocks are discarded); the records written are those of head_dim 32.
 // =====================================================================
-template <int D, int PF, bool ROW8, bool FULL, bool NTL, bool PAIR = false>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 && D <= 64 && FULL ? 3 : 2)))
+
+// NBW > 1 (whole blocks of at most 64 tokens, TP = 1): a wave walks NBW
+// consecutive blocks as one pipeline, so the loads of the next block are in
+// flight while one block's last step is multiplied and its record stored.
+template <int D, int PF, bool ROW8, bool FULL, bool NTL, bool PAIR = false, int NBW = 1>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(PF == 1 && D <= 64 && FULL && NBW == 1 ? 3 : 2)))
 void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                            uint16_t* __restrict__ SZ, const Geo g, const float* __restrict__ W,
                            uint16_t* __restrict__ Wb, const WConv wc) {
     static_assert(!FULL || ROW8, "FULL implies ROW8");
     static_assert(!PAIR || D == 64, "paired heads run the 64-channel layout");
+    static_assert(NBW == 1 || (FULL && D <= 64), "several blocks per wave: whole blocks, d <= 64");
     constexpr int CPL = (D == 32) ? 2 : 4;   // channels per lane
     constexpr int CW = CPL / 2;              // 32-bit words per lane per token
     constexpr int NQ = (D == 128) ? 4 : 1;
@@ -62,15 +69,25 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int quad = wave % NQ;
     const int li = lane & 15, gq = lane >> 4;
-    const WgCoordP wgc = wg_coord_parts(g, blockIdx.x, g.div_TP);
+    WgCoordP wgc;
+    if constexpr (NBW > 1) {
+        // blocks NBW jg .. NBW jg + NBW - 1 (M is a multiple of NBW; TP = 1)
+        const uint32_t bj = fdiv(blockIdx.x, g.div_HG);
+        const int mg = g.M / NBW;
+        wgc.hg = (int)(blockIdx.x - bj * g.div_HG.d);
+        wgc.b = (int)bj / mg;
+        wgc.j = ((int)bj - wgc.b * mg) * NBW;
+        wgc.t = 0;
+    } else {
+        wgc = wg_coord_parts(g, blockIdx.x, g.div_TP);
+    }
     const int b = wgc.b, j = wgc.j, h = wgc.hg * g.G + wave / NQ;
     if (h >= g.H) return;
-    const int blk = ((b * g.H + h) * g.M + j) * g.TP + wgc.t;   // record index (b, h, j, part)
     const int rowbase = (D == 128) ? (quad >> 1) * 64 : 0;
     const int colbase = (D == 128) ? (quad & 1) * 64 : 0;
     const bool do_z = (quad & 1) == 0;        // one wave per row range forms z
     const int row = g.H * D;
-    const int origin = block_origin(g, j);
+    int origin = block_origin(g, j);
     const uint16_t* kb = K + (b * g.N * row + h * D + rowbase + CPL * li);
     const uint16_t* vb = V + (b * g.N * row + h * D + colbase + CPL * li);
     const u32x4 ones = u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0 pairs
@@ -86,8 +103,17 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
     struct Raw {
         uint32_t k[8][CW], v[8][CW];
         uint32_t valid;
+        int it;                               // NBW > 1: the pipeline iteration
     };
+    const int nks = (g.T + 31) >> 5;          // 32-token steps per block
     auto load = [&](int ks, Raw& R) {
+        if constexpr (NBW > 1) {
+            // iteration ks: step ks % nks of block j + ks / nks
+            R.it = ks;
+            const int jb = ks / nks;
+            origin = block_origin(g, j + jb);
+            ks -= jb * nks;
+        }
         int offs[8];
         if constexpr (ROW8) {
             const int p0 = ks * 32 + gq * 8;
@@ -154,11 +180,6 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
             if (do_z) accz[r] = mfma_bf16(aw, ones, accz[r]);
         }
     };
-    // This part's run of the block's 32-token steps (all of them when TP = 1).
-    const int nks = (g.T + 31) >> 5, per = (nks + g.TP - 1) / g.TP;
-    const int ks0 = wgc.t * per, ks1 = min(nks, ks0 + per);
-    if (ks0 < ks1) pipelined<PF, Raw>(ks0, 1, ks1, load, compute);
-
     // Record layout: S_j transposed ([e][c], c fastest), then z_j.
     // Lane holds S[c][e] for c = rowbase + 4*CPL*gq + CPL*v + r, e = colbase + CPL*li + c2,
     // and z[c] (every column of accz is the same) for the same c.  The tile
@@ -168,63 +189,87 @@ void block_kv_summary_bf16(const uint16_t* __restrict__ K, const uint16_t* __res
     constexpr int TS = TW + 8;            // padded LDS row
     __shared__ __attribute__((aligned(16))) uint16_t stile_all[8 * TW * TS];
     uint16_t* stile = stile_all + wave * (TW * TS);
+    // The record of block jr from acc, accz (through this wave's own LDS slice).
+    auto store_record = [&](int jr) {
 #pragma unroll
-    for (int c2 = 0; c2 < CPL; ++c2) {
-        uint32_t wv[2 * CPL];
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-            for (int rp = 0; rp < CPL / 2; ++rp)
-                wv[v * (CPL / 2) + rp] = pack_bf16(acc[2 * rp][c2][v], acc[2 * rp + 1][c2][v]);
-        uint16_t* dst = stile + (CPL * li + c2) * TS + 4 * CPL * gq;
-        *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-        if constexpr (CPL == 4) *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
-    }
-    if constexpr (PAIR) {
-        // Head 2h + s owns rows e and columns c in [32 s, 32 s + 32) of the
-        // tile: each record row is 64 bytes, four lanes x 16 bytes.
-        constexpr int DH = 32, RECH = DH * DH + DH;
-        const int Hr = 2 * g.H;
-#pragma unroll
-        for (int k = 0; k < TW / 16; ++k) {
-            const int er = k * 16 + (lane >> 2), chunk = lane & 3;
-            const int s = er >> 5;
-            const u32x4 x = *reinterpret_cast<const u32x4*>(stile + er * TS + DH * s + chunk * 8);
-            uint16_t* rech = SZ + (((size_t)(b * Hr + 2 * h + s) * g.M + j) * g.TP + wgc.t) * RECH;
-            *reinterpret_cast<u32x4*>(rech + (er - DH * s) * DH + chunk * 8) = x;
-        }
-        if (li == 0) {
-            // Lane group gq holds z for channels 16 gq .. 16 gq + 15 of the pair.
-            uint32_t wv[8];
+        for (int c2 = 0; c2 < CPL; ++c2) {
+            uint32_t wv[2 * CPL];
 #pragma unroll
             for (int v = 0; v < 4; ++v)
 #pragma unroll
-                for (int rp = 0; rp < 2; ++rp) wv[v * 2 + rp] = pack_bf16(accz[2 * rp][v], accz[2 * rp + 1][v]);
-            const int s = gq >> 1;
-            uint16_t* dst = SZ + (((size_t)(b * Hr + 2 * h + s) * g.M + j) * g.TP + wgc.t) * RECH + DH * DH + 16 * (gq & 1);
+                for (int rp = 0; rp < CPL / 2; ++rp)
+                    wv[v * (CPL / 2) + rp] = pack_bf16(acc[2 * rp][c2][v], acc[2 * rp + 1][c2][v]);
+            uint16_t* dst = stile + (CPL * li + c2) * TS + 4 * CPL * gq;
             *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-            *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+            if constexpr (CPL == 4) *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
         }
-        return;
-    }
-    uint16_t* rec = SZ + (size_t)blk * (D * D + D);
-    constexpr int LPR = TW / 8;           // lanes per tile row (16 bytes each)
+        if constexpr (PAIR) {
+            // Head 2h + s owns rows e and columns c in [32 s, 32 s + 32) of the
+            // tile: each record row is 64 bytes, four lanes x 16 bytes.
+            constexpr int DH = 32, RECH = DH * DH + DH;
+            const int Hr = 2 * g.H;
 #pragma unroll
-    for (int k = 0; k < TW / (64 / LPR); ++k) {
-        const int er = k * (64 / LPR) + lane / LPR, chunk = lane % LPR;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(stile + er * TS + chunk * 8);
-        *reinterpret_cast<u32x4*>(rec + (colbase + er) * D + rowbase + chunk * 8) = x;
-    }
-    if (do_z && li == 0) {
-        uint32_t wv[2 * CPL];
+            for (int k = 0; k < TW / 16; ++k) {
+                const int er = k * 16 + (lane >> 2), chunk = lane & 3;
+                const int s = er >> 5;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(stile + er * TS + DH * s + chunk * 8);
+                uint16_t* rech = SZ + (((size_t)(b * Hr + 2 * h + s) * g.M + jr) * g.TP + wgc.t) * RECH;
+                *reinterpret_cast<u32x4*>(rech + (er - DH * s) * DH + chunk * 8) = x;
+            }
+            if (li == 0) {
+                // Lane group gq holds z for channels 16 gq .. 16 gq + 15 of the pair.
+                uint32_t wv[8];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+                for (int v = 0; v < 4; ++v)
 #pragma unroll
-            for (int rp = 0; rp < CPL / 2; ++rp)
-                wv[v * (CPL / 2) + rp] = pack_bf16(accz[2 * rp][v], accz[2 * rp + 1][v]);
-        uint16_t* dst = rec + D * D + rowbase + 4 * CPL * gq;
-        *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-        if constexpr (CPL == 4) *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+                    for (int rp = 0; rp < 2; ++rp) wv[v * 2 + rp] = pack_bf16(accz[2 * rp][v], accz[2 * rp + 1][v]);
+                const int s = gq >> 1;
+                uint16_t* dst = SZ + (((size_t)(b * Hr + 2 * h + s) * g.M + jr) * g.TP + wgc.t) * RECH + DH * DH + 16 * (gq & 1);
+                *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+                *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+            }
+            return;
+        }
+        uint16_t* rec = SZ + (size_t)(((b * g.H + h) * g.M + jr) * g.TP + wgc.t) * (D * D + D);
+        constexpr int LPR = TW / 8;           // lanes per tile row (16 bytes each)
+#pragma unroll
+        for (int k = 0; k < TW / (64 / LPR); ++k) {
+            const int er = k * (64 / LPR) + lane / LPR, chunk = lane % LPR;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(stile + er * TS + chunk * 8);
+            *reinterpret_cast<u32x4*>(rec + (colbase + er) * D + rowbase + chunk * 8) = x;
+        }
+        if (do_z && li == 0) {
+            uint32_t wv[2 * CPL];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int rp = 0; rp < CPL / 2; ++rp)
+                    wv[v * (CPL / 2) + rp] = pack_bf16(accz[2 * rp][v], accz[2 * rp + 1][v]);
+            uint16_t* dst = rec + D * D + rowbase + 4 * CPL * gq;
+            *reinterpret_cast<u32x4*>(dst) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+            if constexpr (CPL == 4) *reinterpret_cast<u32x4*>(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+        }
+    };
+    if constexpr (NBW > 1) {
+        auto compute_nb = [&](const Raw& R) {
+            compute(R);
+            if (R.it % nks == nks - 1) {
+                store_record(j + R.it / nks);
+#pragma unroll
+                for (int r = 0; r < CPL; ++r) {
+                    accz[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        };
+        pipelined<PF, Raw>(0, 1, NBW * nks, load, compute_nb);
+    } else {
+        // This part's run of the block's 32-token steps (all of them when TP = 1).
+        const int per = (nks + g.TP - 1) / g.TP;
+        const int ks0 = wgc.t * per, ks1 = min(nks, ks0 + per);
+        if (ks0 < ks1) pipelined<PF, Raw>(ks0, 1, ks1, load, compute);
+        store_record(j);
     }
 }
 
@@ -1118,6 +1163,32 @@ void launch_summary(const Launch& L, const uint16_t* k, const uint16_t* v, uint1
                 else
                     block_kv_summary_d128_bf16<PF, ROW8, FULL, false, 2><<<ns1 + w1.nconv, th1, 0, L.stream>>>(k, v, sz, g1, L.W, wbp, w1);
             }
+            return;
+        }
+    }
+    if constexpr (FULL && D <= 64) {
+        // Blocks of at most 64 tokens (one or two 32-token steps): each wave
+        // walks four (else two) blocks, so the pipeline does not fill and
+        // drain once per block (dit-s2-64x64 summary 65.0 -> 60.8 us with two,
+        // 58.3 us with four; sana-128x128 80.8 -> 77.9 -> 77.5 us).
+        auto go = [&](auto nbw) {
+            constexpr int NBW = decltype(nbw)::value;
+            const int nsb = g.B * (g.M / NBW) * g.HG;
+            WConv wb = w;
+            wb.first_wg = nsb;
+            if (L.tune.nt_loads)
+                block_kv_summary_bf16<D, PF, ROW8, FULL, true, PAIR, NBW><<<nsb + nconv, threads, 0, L.stream>>>(
+                    k, v, sz, g, L.W, static_cast<uint16_t*>(L.wb), wb);
+            else
+                block_kv_summary_bf16<D, PF, ROW8, FULL, false, PAIR, NBW><<<nsb + nconv, threads, 0, L.stream>>>(
+                    k, v, sz, g, L.W, static_cast<uint16_t*>(L.wb), wb);
+        };
+        if (g.TP == 1 && g.T <= 64 && g.M % 4 == 0) {
+            go(std::integral_constant<int, 4>{});
+            return;
+        }
+        if (g.TP == 1 && g.T <= 64 && g.M % 2 == 0) {
+            go(std::integral_constant<int, 2>{});
             return;
         }
     }
