@@ -102,6 +102,8 @@ MIX_CASES = [
     # more than three units per persistent workgroup
     ("mix-d64-M16-units1088", 8, 8, 64, (16, 16), (4, 4), BF, 1.0),
     ("mix-d128-M256-units774", 1, 3, 128, (32, 32), (2, 2), BF, 1.0),
+    # 64 pairs, 144 blocks: 17 column tiles per pair, the last one ragged
+    ("mix-d32-M144-H64-ragged-tile", 1, 64, 32, (48, 48), (4, 4), BF, 1.0),
 ]
 
 
