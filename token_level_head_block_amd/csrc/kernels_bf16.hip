@@ -1254,7 +1254,8 @@ void launch_apply(const Launch& L, const uint16_t* q, const uint16_t* st, uint16
 // backward's gradient records (W^T, TP = RD = 1); outputs St-style bf16
 // records and fp32 normalisers.  The kernel follows the problem: mix_split
 // with at most 256 source k-slots, the persistent kernel when so tuned (at
-// most 64 query blocks by default), the per-tile kernel otherwise.
+// most 64 query blocks, head_dim 128, or head_dim 32 with many pairs by
+// default), the per-tile kernel otherwise.
 template <int D>
 void launch_mixing(const Launch& L, const uint16_t* src, const uint16_t* wops, uint16_t* dst, float* zdst,
                    const Geo& g) {

@@ -1123,7 +1123,7 @@ __global__ __launch_bounds__(256) void fill_zero(float* __restrict__ p, int n) {
 hipError_t launch_mix_dw_bf16(const BwdLaunch& B, const Geo& g, const uint16_t* srec) {
     const Launch& L = B.F;
     const int ntj = (g.M + 127) / 128;
-    if (g.M > 128 && g.M <= 256 && L.tune.mix_kind == 2 && L.tune.bwd_fuse) {
+    if (g.M > 128 && g.M <= 256 && L.tune.mix_kind != 0 && L.tune.bwd_fuse) {
         // the gradient records' W^T mixing and dW's partial products in one launch
         auto go = [&](auto d) {
             constexpr int D = decltype(d)::value;

@@ -246,7 +246,11 @@ mhla::Tuning choose_tuning(const Shape& s) {
     // at head_dim 128 (258 column tiles per pair, each workgroup of the split
     // kernel reading 64 KB of W for 32 KB of records) too: video-16x64x64
     // step 254.4-255.5 -> 251.5-252.5 us over three alternating runs.
-    const int mix_default = (s.M <= 64 || s.D == 128) ? 1 : 2;
+    // At head_dim 32 with many pairs (17 column tiles each; sana-128x128: 140
+    // pairs, 4760 split workgroups) the persistent kernel wins as well:
+    // mixing 38.0 -> 37.3 us, step 183.8 -> 180.7 us over two alternating runs.
+    const bool many_d32 = s.D == 32 && s.M <= 256 && s.B * s.H >= 64;
+    const int mix_default = (s.M <= 64 || s.D == 128 || many_d32) ? 1 : 2;
     t.mix_kind = env_int("MHLA_MIX", mix_default);
     if (t.mix_kind < 0 || t.mix_kind > 2) t.mix_kind = mix_default;
     t.mix_rows = env_int("MHLA_MIX_ROWS", 0);
